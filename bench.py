@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped MXFP4 GEMM hot path on one MI355X.
+
+One step = one training step of an MoE expert layer (FC1 of a gated FFN:
+32 experts, 4096 tokens x top-8 = 32768 routed rows, K = 4096, N = 3072,
+seeded Dirichlet(0.5) routing with empty experts) through every row of the
+hot path, all in the library's HIP kernels:
+
+  forward : quantize A row-wise, quantize W row-wise, grouped forward (TN)
+  dgrad   : quantize dY row-wise, quantize W along N (column-wise segment-
+            padded, splits N per expert), grouped input gradient (NN)
+  wgrad   : quantize dY and X column-wise segment-padded (pad 32), grouped
+            variable-K weight gradient (NT) accumulated in place into an
+            fp32 main_grad [32, 3072, 4096]
+
+value = GEMM flops of the step (3 x 2 * sum(m_g) * N * K) / step time, in
+TFLOPS. Every kernel is also timed alone with HIP events on the stream it is
+launched on; the dominant kernel's roofline is reported against MI355X's
+published peaks (MXFP4 dense MFMA 10.1 PFLOP/s, HBM3E 8 TB/s).
+
+cpu_baseline: the CPU oracle (NumPy fp64) timed on a bounded sample of the
+same step -- one expert with 1024 tokens at the full K and N, all three
+passes including quantization -- on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "grouped MXFP4 GEMM TFLOPS (fwd/dgrad/wgrad) and % of MFMA peak, 1 MI355X"
+PEAK_MXFP4_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--passes", default="all", help="profiling aid: fwd, dgrad, wgrad or all")
+    return ap.parse_args()
+
+
+def cpu_baseline(seconds_hint=20.0):
+    """The oracle on a bounded sample: one expert, 1024 tokens, K=4096,
+    N=3072; fwd + dgrad + wgrad including every quantization."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import grouped as og
+    from oracle import mx as omx
+    from synth import bf16_normal
+
+    m, K, N = 1024, 4096, 3072
+    a = bf16_normal((m, K), 1.0, seed=1)
+    w = bf16_normal((N, K), 0.02, seed=2)
+    dy = bf16_normal((m, N), 1.0, seed=3)
+    t0 = time.perf_counter()
+    aq, as_ = omx.quantize_rowwise(a, "mxfp4")
+    wq, ws = omx.quantize_rowwise(w, "mxfp4")
+    og.grouped_fwd(omx.dequantize_rowwise(aq, as_, "mxfp4"), omx.dequantize_rowwise(wq, ws, "mxfp4")[None], [m])
+    dq, ds = omx.quantize_rowwise(dy, "mxfp4")
+    wcq, wcs = omx.quantize_colwise_segpad(w, [N], "mxfp4")
+    og.grouped_dgrad(omx.dequantize_rowwise(dq, ds, "mxfp4"), omx.dequantize_rowwise(wcq, wcs, "mxfp4"), [m])
+    dcq, dcs = omx.quantize_colwise_segpad(dy, [m], "mxfp4")
+    xcq, xcs = omx.quantize_colwise_segpad(a, [m], "mxfp4")
+    og.grouped_wgrad(omx.dequantize_rowwise(dcq, dcs, "mxfp4"), omx.dequantize_rowwise(xcq, xcs, "mxfp4"), [m])
+    t = time.perf_counter() - t0
+    flops = 3 * 2.0 * m * N * K
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / t / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "seconds": round(t, 3),
+            "sample": f"one expert, {m} tokens, K={K}, N={N}: fwd+dgrad+wgrad incl. MX quantization, "
+                      f"NumPy fp64 oracle (OpenBLAS {threads} threads, host has {os.cpu_count()} cpus)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the path shards by expert "
+                                   "(see DESIGN.md) but no multi-GPU run is part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import moe_grouped_block_mx_amd as mxg
+    from synth import WORKLOADS, splits_for
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS["fc1"]
+    G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
+    sp = splits_for("fc1")
+    assert int(sp.sum()) == M
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    a = torch.randn((M, K), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    w = (torch.randn((G * N, K), generator=gen, device=dev, dtype=torch.float32) * wl["w_std"]).to(torch.bfloat16)
+    dy = torch.randn((M, N), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    main_grad = torch.randn((G, N, K), generator=gen, device=dev, dtype=torch.float32)
+    mpad = mxg.segpad_rows(sp, "mxfp4")
+
+    # outputs / quantized operands allocated once (the library allocates nothing)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    aq, as_ = torch.empty((M, K // 2), **u8), torch.empty((M, K // 32), **u8)
+    wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty((G * N, K // 32), **u8)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dq, ds = torch.empty((M, N // 2), **u8), torch.empty((M, N // 32), **u8)
+    wcq, wcs = torch.empty((K, G * N // 2), **u8), torch.empty((K, G * N // 32), **u8)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dcq, dcs = torch.empty((N, mpad // 2), **u8), torch.empty((N, mpad // 32), **u8)
+    xcq, xcs = torch.empty((K, mpad // 2), **u8), torch.empty((K, mpad // 32), **u8)
+
+    ops = [
+        ("quant_A_row", "quant", lambda: mxg.quantize_rowwise(a, "mxfp4", q=aq, scales=as_)),
+        ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, "mxfp4", q=wq, scales=ws)),
+        ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, out=y)),
+        ("quant_dY_row", "quant", lambda: mxg.quantize_rowwise(dy, "mxfp4", q=dq, scales=ds)),
+        ("quant_W_col", "quant", lambda: mxg.quantize_colwise_segpad(w, [N] * G, "mxfp4", q=wcq, scales=wcs)),
+        ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, dx=dx)),
+        ("quant_dY_col", "quant", lambda: mxg.quantize_colwise_segpad(dy, sp, "mxfp4", q=dcq, scales=dcs)),
+        ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "mxfp4", q=xcq, scales=xcs)),
+        ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, main_grad,
+                                                    accumulate=True)),
+    ]
+    if args.passes != "all":
+        keep = {"fwd": {"quant_A_row", "quant_W_row", "fwd"},
+                "dgrad": {"quant_dY_row", "quant_W_col", "dgrad"},
+                "wgrad": {"quant_dY_col", "quant_X_col", "wgrad"}}[args.passes]
+        ops = [o for o in ops if o[0] in keep]
+
+    gemm_flops = 2.0 * M * N * K
+    # algorithmic bytes per launch: what each kernel must move at least once
+    nz = int((sp > 0).sum())
+    bytes_alg = {
+        "quant_A_row": M * K * (2 + 0.5 + 1 / 32),
+        "quant_W_row": G * N * K * (2 + 0.5 + 1 / 32),
+        "fwd": M * K * (0.5 + 1 / 32) + nz * N * K * (0.5 + 1 / 32) + M * N * 2,
+        "quant_dY_row": M * N * (2 + 0.5 + 1 / 32),
+        "quant_W_col": G * N * K * (2 + 0.5 + 1 / 32),
+        "dgrad": M * N * (0.5 + 1 / 32) + nz * N * K * (0.5 + 1 / 32) + M * K * 2,
+        "quant_dY_col": M * N * 2 + mpad * N * (0.5 + 1 / 32),
+        "quant_X_col": M * K * 2 + mpad * K * (0.5 + 1 / 32),
+        "wgrad": mpad * (N + K) * (0.5 + 1 / 32) + nz * N * K * 4 * 2,
+    }
+
+    stream = torch.cuda.current_stream(dev)
+    ev = {name: [] for name, _, _ in ops}
+
+    def step(record):
+        for name, _, fn in ops:
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ev[name].append((e0, e1))
+            else:
+                fn()
+
+    # a leading kernel so the first timed launch does not absorb launch latency
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+
+    # per-kernel durations (separate timed steps, events around each launch)
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    per = {}
+    for name, kind, _ in ops:
+        ms = [e0.elapsed_time(e1) for e0, e1 in ev[name]]
+        d = float(np.mean(ms)) * 1e-3
+        entry = {"ms": round(d * 1e3, 4), "ms_min": round(float(np.min(ms)), 4)}
+        entry["GBs_alg"] = round(bytes_alg[name] / d / 1e9, 1)
+        entry["frac_hbm"] = round(bytes_alg[name] / d / 1e9 / PEAK_HBM_GBS, 4)
+        if kind == "gemm":
+            entry["TFLOPS"] = round(gemm_flops / d / 1e12, 1)
+            entry["pct_mxfp4_peak"] = round(100 * gemm_flops / d / 1e12 / PEAK_MXFP4_TFLOPS, 2)
+        per[name] = entry
+
+    n_gemm = sum(1 for _, k, _ in ops if k == "gemm")
+    value = n_gemm * gemm_flops / t_step / 1e12
+    dom = max(per, key=lambda k: per[k]["ms"])
+    dkind = dict((n, k) for n, k, _ in ops)[dom]
+    d = per[dom]["ms"] * 1e-3
+    if dkind == "gemm" and dom != "wgrad":
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(gemm_flops / d / 1e12, 1),
+                "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(bytes_alg[dom] / d / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["per_launch_algorithmic"] = (gemm_flops if roof["bound"] == "mfma" else bytes_alg[dom])
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "MoE FC1 a4w4 training step (fwd+dgrad+wgrad with MX quantization)",
+                   "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz,
+                   "max_split": int(sp.max()), "mpad": mpad, "routing": "Dirichlet(0.5), 3 zeroed, seed 0",
+                   "passes": args.passes},
+        "roofline": roof,
+        "kernels": per,
+        "pct_mxfp4_peak_step": round(100 * value / PEAK_MXFP4_TFLOPS, 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,234 @@
+/*
+ * mxgg.h -- C ABI of the grouped block-scaled (MX) GEMM library for MoE expert
+ * layers on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are the public pull-request pages this library is
+ * built from; each is named by its title):
+ *
+ *  - "Triton mxfp4 (and a8w4) grouped GEMM kernel": a persistent grouped MXFP4
+ *    GEMM in three passes -- forward (TN), input gradient (dgrad, NN) and
+ *    variable-K weight gradient (wgrad, NT) -- fed by a row operand
+ *    (data (N, K/2) + UE8M0 scales (N, K/32)) and, for wgrad, a column operand
+ *    whose expert segments are padded (the segment-padded layout below). The
+ *    same page requires split validation: no negative split, one split per
+ *    expert, splits summing to the row count of every row-split operand.
+ *  - "route te.GroupedLinear through #723; a8w4 fwd-only": the a8w4 forward
+ *    (E4M3 activations with UE8M0 block-32 scales x E2M1 weights), empty
+ *    batches that launch nothing, caller-provided output buffers, and the
+ *    tiny-scale rule (the shared exponent clamps at -127 and is applied before
+ *    rounding).
+ *  - "Grouped MXFP8 GEMMs with HipKittens": one launch over all experts with a
+ *    binary-search (upper_bound) tile-to-expert lookup, at most 512 experts,
+ *    contiguous packed expert weights.
+ *  - "Add ROCm Triton blockwise FP8 grouped GEMM": the blockwise FP8 variant
+ *    (1x128 activation scales, 128x128 weight scales, segment-padded 1x128
+ *    column scales, power-of-two scales), variable-K wgrad with in-place
+ *    accumulation, and the rule that every output element is owned by exactly
+ *    one tile (no wrapped tail tiles).
+ *
+ * Formats (OCP MX v1.0 and OCP FP8):
+ *   MXGG_MXFP4        E2M1 elements, 2 per byte (even element in bits 3:0),
+ *                     one UE8M0 scale byte per 32 elements along the
+ *                     contraction axis (value 2^(byte-127)).
+ *   MXGG_MXFP8        E4M3 ("FN", max 448) elements, one byte each, UE8M0
+ *                     scale per 32 elements.
+ *   MXGG_FP8_1x128    E4M3 elements, one fp32 scale per 128 elements along the
+ *                     contraction axis (activations, wgrad column operands).
+ *   MXGG_FP8_128x128  E4M3 elements, one fp32 scale per 128x128 block
+ *                     (weights).
+ *
+ * MX quantization rule (what mxgg_quantize_* produce): amax = max |x| over the
+ * block; e = clamp(floor(log2 amax) - emax, -127, 127) with emax = 2 (E2M1) or
+ * 8 (E4M3), e = -127 for an all-zero block; codes = round-to-nearest-even of
+ * x * 2^-e, saturating at +-6 / +-448, sign kept (so -0 stays -0); scale byte
+ * = e + 127. Blockwise FP8 with MXGG_POW2_SCALES: amax floored at fp32(1e-4),
+ * s = 2^-t with t the largest integer such that amax * 2^t <= 448, codes =
+ * RNE-saturating E4M3 of x * 2^t; without the flag: q = fp32(448/amax),
+ * codes from fp32(x*q), s = fp32(1/q).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument except m_splits is a DEVICE pointer on the device
+ *     that owns `stream` (NULL stream = the current device). m_splits is a
+ *     HOST array of G int64 values, read only during the call.
+ *   - bf16 tensors are row-major with a leading dimension (elements) and unit
+ *     inner stride; quantized tensors are dense row-major (row stride = the
+ *     row's byte count).
+ *   - The caller owns every buffer, outputs included; the library allocates
+ *     nothing per call and keeps no state beyond a cached per-device
+ *     architecture check.
+ *   - All work is enqueued on `stream` and is asynchronous: no host
+ *     synchronization and no device-to-host copy happen inside a call.
+ *   - Every argument check runs before anything is enqueued: an error return
+ *     means nothing was launched or written. A batch with no rows is checked
+ *     first and then returns MXGG_OK without a launch (except wgrad with
+ *     accumulate == 0, which zero-fills its output).
+ *   - Device pointers with a nonzero extent must be 16-byte aligned
+ *     (MXGG_ERR_ALIGN), bf16 leading dimensions multiples of 8 elements.
+ *   - Errors never abort and never throw; mxgg_last_error() returns a
+ *     thread-local text for the last failing call on the calling thread.
+ */
+#ifndef MXGG_H
+#define MXGG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream handle (the same declaration as the HIP runtime's). */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum mxgg_status {
+  MXGG_OK = 0,
+  MXGG_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  MXGG_ERR_SHAPE = 2,     /* bad G, dimension, multiple or leading dimension   */
+  MXGG_ERR_SPLITS = 3,    /* negative split or splits not summing to the rows  */
+  MXGG_ERR_FORMAT = 4,    /* unsupported format or format pair for this pass   */
+  MXGG_ERR_ALIGN = 5,     /* a device pointer / leading dimension misaligned   */
+  MXGG_ERR_WORKSPACE = 6, /* workspace smaller than mxgg_workspace_size()      */
+  MXGG_ERR_DEVICE = 7,    /* a pointer is not device memory of the stream's GPU */
+  MXGG_ERR_ARCH = 8,      /* the stream's GPU is not gfx950                     */
+  MXGG_ERR_HIP = 9        /* a HIP runtime call or kernel launch failed        */
+} mxgg_status;
+
+typedef enum mxgg_format {
+  MXGG_MXFP4 = 0,
+  MXGG_MXFP8 = 1,
+  MXGG_FP8_1x128 = 2,
+  MXGG_FP8_128x128 = 3
+} mxgg_format;
+
+/* flags for the quantizers (blockwise formats only) */
+#define MXGG_POW2_SCALES 1u
+
+/* largest expert count a single launch handles */
+#define MXGG_MAX_EXPERTS 512
+
+/*
+ * Row-wise quantization ("Triton mxfp4 (and a8w4) grouped GEMM kernel", the
+ * row operand; blockwise formats from "Add ROCm Triton blockwise FP8 grouped
+ * GEMM").
+ *   x       bf16 [rows, cols], leading dimension ldx (elements, >= cols,
+ *           multiple of 8).
+ *   fmt     MXGG_MXFP4 / MXGG_MXFP8: blocks of 32 along cols (cols % 32 == 0).
+ *           MXGG_FP8_1x128: blocks of 128 along cols (cols % 128 == 0).
+ *           MXGG_FP8_128x128: 128x128 blocks (rows % 128 == 0, cols % 128 == 0).
+ *   flags   MXGG_POW2_SCALES for the blockwise formats (ignored for MX).
+ *   q       MXFP4: u8 [rows, cols/2]; otherwise u8 [rows, cols] (E4M3 codes).
+ *   scales  MX: u8 [rows, cols/32]; FP8_1x128: f32 [rows, cols/128];
+ *           FP8_128x128: f32 [rows/128, cols/128].
+ * rows == 0 returns MXGG_OK with no launch. Errors: NULL, SHAPE, FORMAT,
+ * ALIGN, DEVICE, ARCH, HIP.
+ */
+mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                  mxgg_format fmt, uint32_t flags, void* q, void* scales,
+                                  hipStream_t stream);
+
+/*
+ * Column-wise, segment-padded quantization (the padded column operand of the
+ * variable-K weight gradient, "Triton mxfp4 (and a8w4) grouped GEMM kernel";
+ * the 1x128 blockwise form from "Add ROCm Triton blockwise FP8 grouped GEMM").
+ * The rows of expert g (m_splits[g] of them, consecutive) become columns
+ * [pad_offs[g], pad_offs[g] + m_splits[g]) of a transposed [cols, mpad]
+ * operand; each segment is padded with zeros to a multiple of P (P = 32 for
+ * MX formats, 128 for MXGG_FP8_1x128) and quantized along its padded length,
+ * so no scale block straddles two experts. Also used on weights for dgrad:
+ * W viewed as [G*N, K] with m_splits = {N, ..., N} gives W quantized along N.
+ *   x        bf16 [rows, cols], leading dimension ldx; rows == sum(m_splits).
+ *   m_splits host int64 [G], 1 <= G <= 512, each >= 0.
+ *   fmt      MXGG_MXFP4, MXGG_MXFP8 or MXGG_FP8_1x128; cols % 32 == 0.
+ *   q        MXFP4: u8 [cols, mpad/2]; otherwise u8 [cols, mpad].
+ *   scales   MX: u8 [cols, mpad/32]; FP8_1x128: f32 [cols, mpad/128].
+ *   mpad     must equal mxgg_segpad_rows(m_splits, G, fmt).
+ * Padding positions hold zero codes. rows == 0 returns MXGG_OK (no launch).
+ * Errors: NULL, SHAPE, SPLITS, FORMAT, ALIGN, DEVICE, ARCH, HIP.
+ */
+mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                         const int64_t* m_splits, int32_t G, mxgg_format fmt,
+                                         uint32_t flags, void* q, void* scales, int64_t mpad,
+                                         hipStream_t stream);
+
+/*
+ * Grouped forward, TN: out[r, n] = sum_k A[r, k] * W_g[n, k] for every row r
+ * of expert g (rows of expert g are consecutive, in expert order).
+ *   a_q, a_s  A quantized row-wise along K: (MXFP4: u8 [M, K/2] | MXFP8: u8 [M, K])
+ *             + u8 [M, K/32]; or MXGG_FP8_1x128: u8 [M, K] + f32 [M, K/128].
+ *   w_q, w_s  packed expert weights [G*N, K] quantized row-wise along K:
+ *             MXFP4 u8 [G*N, K/2] + u8 [G*N, K/32]; or MXGG_FP8_128x128:
+ *             u8 [G*N, K] + f32 [G*N/128, K/128].
+ *   format pairs (a_fmt, w_fmt): (MXFP4, MXFP4) a4w4, (MXFP8, MXFP4) a8w4,
+ *             (FP8_1x128, FP8_128x128) blockwise FP8.
+ *   m_splits  host int64 [G]; sum == M.
+ *   M, N, K   K % 32 == 0 and N % 32 == 0 (MX); K % 128 == 0 and N % 128 == 0
+ *             (blockwise); M < 2^31.
+ *   out       bf16 [M, N] (dense), written with round-to-nearest-even.
+ *   ws        workspace of at least mxgg_workspace_size(G) bytes (may be NULL
+ *             when that is 0).
+ * Errors: NULL, SHAPE, SPLITS, FORMAT, ALIGN, WORKSPACE, DEVICE, ARCH, HIP.
+ */
+mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt,
+                             const void* w_q, const void* w_s, mxgg_format w_fmt,
+                             const int64_t* m_splits, int32_t G, int64_t M, int64_t N,
+                             int64_t K, void* out, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * Grouped input gradient, NN: dx[r, k] = sum_n dY[r, n] * W_g[n, k].
+ *   dy_q, dy_s     dY quantized row-wise along N: u8 [M, N/2] + u8 [M, N/32].
+ *   wcol_q, wcol_s W quantized along N with mxgg_quantize_colwise_segpad on
+ *                  W as [G*N, K] with splits {N, ..., N}: u8 [K, G*N/2] +
+ *                  u8 [K, G*N/32] (expert g owns columns [g*N, (g+1)*N)).
+ *   fmt            MXGG_MXFP4 (the only dgrad format).
+ *   dx             bf16 [M, K].
+ * Shape rules as for the forward. Errors as for the forward.
+ */
+mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* wcol_q,
+                               const void* wcol_s, mxgg_format fmt, const int64_t* m_splits,
+                               int32_t G, int64_t M, int64_t N, int64_t K, void* dx,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Grouped variable-K weight gradient, NT: dW_g[n, k] = sum over the tokens t of
+ * expert g of dY[t, n] * X[t, k], contracted over the expert's padded segment
+ * (pad positions are zero codes, so they add nothing).
+ *   dycol_q/_s  dY from mxgg_quantize_colwise_segpad: [N, mpad] operand.
+ *   xcol_q/_s   X from mxgg_quantize_colwise_segpad: [K, mpad] operand.
+ *   fmt         MXGG_MXFP4 (pad 32) or MXGG_FP8_1x128 (pad 128).
+ *   mpad        mxgg_segpad_rows(m_splits, G, fmt).
+ *   main_grad   [G, N, K]: fp32 when out_is_bf16 == 0, else bf16.
+ *   accumulate  1: main_grad[g] += dW_g in place (experts with no tokens are
+ *               left untouched); 0: main_grad[g] = dW_g (experts with no
+ *               tokens are zero-filled). Every element is read/written by
+ *               exactly one thread, so in-place accumulation is race-free.
+ * Shape rules: N % 32 == 0 and K % 32 == 0 (MX), % 128 (blockwise).
+ * Errors: NULL, SHAPE, SPLITS, FORMAT, ALIGN, WORKSPACE, DEVICE, ARCH, HIP.
+ */
+mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const void* xcol_q,
+                               const void* xcol_s, mxgg_format fmt, const int64_t* m_splits,
+                               int32_t G, int64_t N, int64_t K, int64_t mpad, void* main_grad,
+                               int32_t out_is_bf16, int32_t accumulate, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes the GEMM entry points need for G experts (0 today: the
+ * per-expert tables travel as kernel arguments and are rebuilt in LDS). */
+size_t mxgg_workspace_size(int32_t G);
+
+/* Padded row count of the segment-padded operand: sum_g ceil(m_g/P)*P with
+ * P = 32 (MX formats) or 128 (MXGG_FP8_1x128). Returns -1 for invalid input
+ * (NULL, G outside [1, 512], a negative split, other formats). */
+int64_t mxgg_segpad_rows(const int64_t* m_splits, int32_t G, mxgg_format fmt);
+
+/* Static text for a status code. */
+const char* mxgg_status_string(mxgg_status status);
+
+/* Thread-local description of the last error returned on this thread
+ * ("" when the last call succeeded). Valid until the next call on the thread. */
+const char* mxgg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGG_H */

@@ -1,0 +1,13 @@
+"""Grouped block-scaled (MX) GEMM for MoE expert layers on AMD MI355X (gfx950).
+
+The compute path is libmxgg.so (hand-written HIP kernels behind the C ABI of
+include/mxgg.h); this package is its thin ctypes binding.
+"""
+from ._lib import (  # noqa: F401
+    FORMATS, FP8_1x128, FP8_128x128, LIB_PATH, MAX_EXPERTS, MXFP4, MXFP8, POW2_SCALES,
+    MxggError, header_functions, lib,
+    mxgg_grouped_dgrad, mxgg_grouped_fwd, mxgg_grouped_wgrad, mxgg_quantize_colwise_segpad,
+    mxgg_quantize_rowwise, mxgg_segpad_rows, mxgg_workspace_size,
+    grouped_dgrad, grouped_fwd, grouped_wgrad, quantize_colwise_segpad, quantize_rowwise,
+    segpad_rows, workspace_size,
+)

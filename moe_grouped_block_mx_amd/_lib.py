@@ -1,0 +1,214 @@
+"""ctypes binding of libmxgg.so (include/mxgg.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. torch supplies device memory and the current stream; output tensors
+are allocated here when the caller passes none. Importing this module fails
+loudly when the built library is missing -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB_PATH = os.path.join(PKG, "libmxgg.so")
+HEADER = os.path.join(ROOT, "include", "mxgg.h")
+
+# mxgg_format
+MXFP4, MXFP8, FP8_1x128, FP8_128x128 = 0, 1, 2, 3
+FORMATS = {"mxfp4": MXFP4, "mxfp8": MXFP8, "fp8_1x128": FP8_1x128, "fp8_128x128": FP8_128x128}
+POW2_SCALES = 1
+MAX_EXPERTS = 512
+
+STATUS = {
+    0: "MXGG_OK", 1: "MXGG_ERR_NULL", 2: "MXGG_ERR_SHAPE", 3: "MXGG_ERR_SPLITS",
+    4: "MXGG_ERR_FORMAT", 5: "MXGG_ERR_ALIGN", 6: "MXGG_ERR_WORKSPACE",
+    7: "MXGG_ERR_DEVICE", 8: "MXGG_ERR_ARCH", 9: "MXGG_ERR_HIP",
+}
+
+
+class MxggError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {message}")
+
+
+_vp, _i64, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+_SIGS = {
+    "mxgg_quantize_rowwise": [_vp, _i64, _i64, _i64, _i32, _u32, _vp, _vp, _vp],
+    "mxgg_quantize_colwise_segpad": [_vp, _i64, _i64, _i64, _i64p, _i32, _i32, _u32, _vp, _vp, _i64, _vp],
+    "mxgg_grouped_fwd": [_vp, _vp, _i32, _vp, _vp, _i32, _i64p, _i32, _i64, _i64, _i64, _vp, _vp, _sz, _vp],
+    "mxgg_grouped_dgrad": [_vp, _vp, _vp, _vp, _i32, _i64p, _i32, _i64, _i64, _i64, _vp, _vp, _sz, _vp],
+    "mxgg_grouped_wgrad": [_vp, _vp, _vp, _vp, _i32, _i64p, _i32, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _sz,
+                           _vp],
+}
+
+
+def _load():
+    # torch's HIP runtime must be the one in the process before the library
+    # binds to libamdhip64.so (it links that same runtime)
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m moe_grouped_block_mx_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.mxgg_workspace_size.argtypes = [_i32]
+    lib.mxgg_workspace_size.restype = _sz
+    lib.mxgg_segpad_rows.argtypes = [_i64p, _i32, _i32]
+    lib.mxgg_segpad_rows.restype = _i64
+    lib.mxgg_status_string.argtypes = [_i32]
+    lib.mxgg_status_string.restype = ctypes.c_char_p
+    lib.mxgg_last_error.argtypes = []
+    lib.mxgg_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/mxgg.h declares."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(mxgg_[a-z_0-9]+)\s*\(", txt)))
+
+
+def _check(status: int):
+    if status != 0:
+        raise MxggError(status, lib.mxgg_last_error().decode())
+
+
+def _splits(m_splits):
+    vals = [int(v) for v in m_splits]
+    arr = (ctypes.c_int64 * max(1, len(vals)))(*vals)
+    return arr, len(vals)
+
+
+def _fmt(f) -> int:
+    return FORMATS[f] if isinstance(f, str) else int(f)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def mxgg_workspace_size(G: int) -> int:
+    return int(lib.mxgg_workspace_size(G))
+
+
+def mxgg_segpad_rows(m_splits, fmt) -> int:
+    arr, G = _splits(m_splits)
+    r = int(lib.mxgg_segpad_rows(arr, G, _fmt(fmt)))
+    if r < 0:
+        raise MxggError(2, "invalid splits or format for mxgg_segpad_rows")
+    return r
+
+
+def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=0, q=None, scales=None):
+    """x: bf16 [rows, cols] (row stride may exceed cols). Returns (q, scales)."""
+    torch = _torch()
+    f = _fmt(fmt)
+    rows, cols = x.shape
+    if x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be bf16 with unit inner stride")
+    if q is None:
+        q = torch.empty((rows, cols // 2 if f == MXFP4 else cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        if f in (MXFP4, MXFP8):
+            scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+        elif f == FP8_1x128:
+            scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+        else:
+            scales = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=x.device)
+    _check(lib.mxgg_quantize_rowwise(_ptr(x), rows, cols, x.stride(0), f, flags, _ptr(q), _ptr(scales),
+                                     _stream(x)))
+    return q, scales
+
+
+def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=0, q=None, scales=None):
+    """x: bf16 [rows, cols]. Returns (q [cols, mpad(/2)], scales, mpad)."""
+    torch = _torch()
+    f = _fmt(fmt)
+    rows, cols = x.shape
+    if x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be bf16 with unit inner stride")
+    arr, G = _splits(m_splits)
+    mpad = int(lib.mxgg_segpad_rows(arr, G, f))
+    if mpad < 0:
+        mpad = 0
+    if q is None:
+        q = torch.empty((cols, mpad // 2 if f == MXFP4 else mpad), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        if f == FP8_1x128:
+            scales = torch.empty((cols, mpad // 128), dtype=torch.float32, device=x.device)
+        else:
+            scales = torch.empty((cols, mpad // 32), dtype=torch.uint8, device=x.device)
+    _check(lib.mxgg_quantize_colwise_segpad(_ptr(x), rows, cols, x.stride(0), arr, G, f, flags, _ptr(q),
+                                            _ptr(scales), mpad, _stream(x)))
+    return q, scales, mpad
+
+
+def mxgg_grouped_fwd(a_q, a_s, w_q, w_s, m_splits, N, K, a_fmt="mxfp4", w_fmt="mxfp4", out=None, ws=None):
+    """out[M, N] (bf16) = per-expert A . W_g^T; W packed [G*N, ...]."""
+    torch = _torch()
+    arr, G = _splits(m_splits)
+    M = a_q.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.mxgg_grouped_fwd(_ptr(a_q), _ptr(a_s), _fmt(a_fmt), _ptr(w_q), _ptr(w_s), _fmt(w_fmt), arr, G, M, N,
+                                K, _ptr(out), _ptr(ws), ws_bytes, _stream(a_q)))
+    return out
+
+
+def mxgg_grouped_dgrad(dy_q, dy_s, wcol_q, wcol_s, m_splits, N, K, fmt="mxfp4", dx=None, ws=None):
+    """dx[M, K] (bf16) = per-expert dY . W_g with W quantized along N."""
+    torch = _torch()
+    arr, G = _splits(m_splits)
+    M = dy_q.shape[0]
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy_q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.mxgg_grouped_dgrad(_ptr(dy_q), _ptr(dy_s), _ptr(wcol_q), _ptr(wcol_s), _fmt(fmt), arr, G, M, N, K,
+                                  _ptr(dx), _ptr(ws), ws_bytes, _stream(dy_q)))
+    return dx
+
+
+def mxgg_grouped_wgrad(dycol_q, dycol_s, xcol_q, xcol_s, m_splits, N, K, mpad, main_grad, accumulate=True,
+                       fmt="mxfp4", ws=None):
+    """main_grad [G, N, K] (fp32 or bf16) += / = per-expert dY_g^T . X_g."""
+    torch = _torch()
+    arr, G = _splits(m_splits)
+    out_bf16 = 1 if main_grad.dtype == torch.bfloat16 else 0
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.mxgg_grouped_wgrad(_ptr(dycol_q), _ptr(dycol_s), _ptr(xcol_q), _ptr(xcol_s), _fmt(fmt), arr, G, N, K,
+                                  mpad, _ptr(main_grad), out_bf16, 1 if accumulate else 0, _ptr(ws), ws_bytes,
+                                  _stream(main_grad)))
+    return main_grad
+
+
+# short names
+quantize_rowwise = mxgg_quantize_rowwise
+quantize_colwise_segpad = mxgg_quantize_colwise_segpad
+grouped_fwd = mxgg_grouped_fwd
+grouped_dgrad = mxgg_grouped_dgrad
+grouped_wgrad = mxgg_grouped_wgrad
+workspace_size = mxgg_workspace_size
+segpad_rows = mxgg_segpad_rows

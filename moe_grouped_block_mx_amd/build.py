@@ -1,0 +1,91 @@
+"""Build libmxgg.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+Usage: python -m moe_grouped_block_mx_amd.build [--jobs N] [--verbose]
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmxgg.so")
+
+SOURCES = ["api.cpp", "quant_mx.hip", "gemm_mx.hip"]
+
+# -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    f"-I{os.path.join(ROOT, 'include')}",
+]
+
+
+def _hipcc() -> str:
+    h = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(h):
+        raise RuntimeError("hipcc not found")
+    return h
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+    return out
+
+
+def torch_lib_dir() -> str:
+    """Directory of the HIP runtime torch loads. The library must link that
+    same runtime: a second HIP runtime in the process (e.g. /opt/rocm's) sees
+    none of torch's devices, streams or allocations."""
+    import torch
+    d = os.path.join(os.path.dirname(torch.__file__), "lib")
+    if not os.path.exists(os.path.join(d, "libamdhip64.so")):
+        raise RuntimeError(f"torch's HIP runtime not found in {d}")
+    return d
+
+
+def build(jobs: int = 4, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    hipcc = _hipcc()
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
+        objs.append(obj)
+        cmds.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    tl = torch_lib_dir()
+    cxx = shutil.which("g++") or "g++"
+    _run([cxx, "-shared", "-fPIC", "-o", tmp, *objs, f"-L{tl}", "-lamdhip64", f"-Wl,-rpath,{tl}",
+          "-Wl,--no-undefined"], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=4)
+    ap.add_argument("--verbose", action="store_true")
+    a = ap.parse_args(argv)
+    print(build(a.jobs, a.verbose))
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

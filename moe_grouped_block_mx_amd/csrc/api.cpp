@@ -1,0 +1,292 @@
+// C ABI of the grouped block-scaled GEMM library (include/mxgg.h).
+//
+// Order inside every entry point: (1) argument validation (validate.hpp, no
+// HIP calls), (2) the empty-batch return, (3) device checks -- the stream's
+// GPU must be gfx950 (the scaled FP4/FP8 MFMA exists only on CDNA4, as the
+// page "Triton mxfp4 (and a8w4) grouped GEMM kernel" states for its kernels)
+// and every pointer must be device memory of that GPU (the operand's device,
+// not merely the current one: "route te.GroupedLinear through #723; a8w4
+// fwd-only") -- (4) kernel launches on the caller's stream. Nothing is enqueued
+// before all checks pass.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <mutex>
+#include <numeric>
+#include <string>
+
+#include "../../include/mxgg.h"
+#include "launch.hpp"
+#include "validate.hpp"
+
+namespace mxgg {
+namespace {
+
+thread_local std::string g_last_error;
+
+mxgg_status finish(const Check& c) {
+  g_last_error = c.msg;
+  return c.st;
+}
+
+mxgg_status ok() {
+  g_last_error.clear();
+  return MXGG_OK;
+}
+
+// Per-device cache: 0 unknown, 1 gfx950, 2 other arch.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];
+
+Check stream_device(hipStream_t st, int* dev) {
+  hipError_t e = st ? hipStreamGetDevice(st, dev) : hipGetDevice(dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    Check r; r.st = MXGG_ERR_HIP; r.msg = std::string("cannot query the stream's device: ") + hipGetErrorString(e);
+    return r;
+  }
+  if (*dev < 0 || *dev >= kMaxDevices) return fail(MXGG_ERR_DEVICE, "device ordinal %lld out of range", *dev);
+  return Check{};
+}
+
+Check check_arch(int dev, int* num_cus) {
+  int a = g_arch[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      Check r; r.st = MXGG_ERR_HIP; r.msg = std::string("hipGetDeviceProperties: ") + hipGetErrorString(e);
+      return r;
+    }
+    a = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_arch[dev].store(a, std::memory_order_release);
+  }
+  if (a != 1) return fail(MXGG_ERR_ARCH, "device %lld is not gfx950 (CDNA4 scaled MFMA required)", dev);
+  *num_cus = g_cus[dev].load(std::memory_order_relaxed);
+  return Check{};
+}
+
+Check check_on_device(const void* p, int dev, const char* name) {
+  if (!p) return Check{};
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    Check r; r.st = MXGG_ERR_DEVICE; r.msg = std::string(name) + " is not HIP device memory";
+    return r;
+  }
+  const bool devmem = attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+  if (!devmem || attr.device != dev) {
+    Check r; r.st = MXGG_ERR_DEVICE;
+    r.msg = std::string(name) + " is not device memory of the stream's GPU " + std::to_string(dev);
+    return r;
+  }
+  return Check{};
+}
+
+// Arch + device membership of every pointer; returns the device's CU count.
+Check device_checks(hipStream_t st, std::initializer_list<std::pair<const void*, const char*>> ptrs, int* num_cus) {
+  int dev = 0;
+  MXGG_TRY(stream_device(st, &dev));
+  MXGG_TRY(check_arch(dev, num_cus));
+  for (auto& pr : ptrs) MXGG_TRY(check_on_device(pr.first, dev, pr.second));
+  return Check{};
+}
+
+Check hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return Check{};
+  (void)hipGetLastError();
+  Check r; r.st = MXGG_ERR_HIP; r.msg = std::string(what) + ": " + hipGetErrorString(e);
+  return r;
+}
+
+SplitArgs make_splits(const int64_t* m, int32_t G) {
+  SplitArgs s;
+  std::memset(&s, 0, sizeof(s));
+  s.G = G;
+  for (int32_t g = 0; g < G; ++g) s.m[g] = (int32_t)m[g];
+  return s;
+}
+
+}  // namespace
+}  // namespace mxgg
+
+using namespace mxgg;
+
+extern "C" {
+
+const char* mxgg_status_string(mxgg_status s) {
+  switch (s) {
+    case MXGG_OK: return "MXGG_OK";
+    case MXGG_ERR_NULL: return "MXGG_ERR_NULL: a required pointer is NULL";
+    case MXGG_ERR_SHAPE: return "MXGG_ERR_SHAPE: invalid expert count, dimension or leading dimension";
+    case MXGG_ERR_SPLITS: return "MXGG_ERR_SPLITS: negative split or splits do not sum to the rows";
+    case MXGG_ERR_FORMAT: return "MXGG_ERR_FORMAT: unsupported format or format pair";
+    case MXGG_ERR_ALIGN: return "MXGG_ERR_ALIGN: misaligned pointer or leading dimension";
+    case MXGG_ERR_WORKSPACE: return "MXGG_ERR_WORKSPACE: workspace too small";
+    case MXGG_ERR_DEVICE: return "MXGG_ERR_DEVICE: pointer is not device memory of the stream's GPU";
+    case MXGG_ERR_ARCH: return "MXGG_ERR_ARCH: the GPU is not gfx950";
+    case MXGG_ERR_HIP: return "MXGG_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "unknown mxgg_status";
+}
+
+const char* mxgg_last_error(void) { return g_last_error.c_str(); }
+
+size_t mxgg_workspace_size(int32_t G) {
+  (void)G;
+  return 0;
+}
+
+int64_t mxgg_segpad_rows(const int64_t* m_splits, int32_t G, mxgg_format fmt) {
+  if (!m_splits || G < 1 || G > MXGG_MAX_EXPERTS) return -1;
+  if (fmt != MXGG_MXFP4 && fmt != MXGG_MXFP8 && fmt != MXGG_FP8_1x128) return -1;
+  for (int32_t g = 0; g < G; ++g)
+    if (m_splits[g] < 0) return -1;
+  return segpad_rows(m_splits, G, segpad_multiple(fmt));
+}
+
+mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, mxgg_format fmt,
+                                  uint32_t flags, void* q, void* scales, hipStream_t stream) {
+  (void)flags;
+  Check c = validate_quantize_rowwise(x, rows, cols, ldx, (int)fmt, q, scales);
+  if (!c.ok()) return finish(c);
+  if (rows == 0) return ok();
+  if (!is_mx(fmt)) return finish(fail(MXGG_ERR_FORMAT, "blockwise FP8 quantization is not built in this library"));
+  int cus = 0;
+  c = device_checks(stream, {{x, "x"}, {q, "q"}, {scales, "scales"}}, &cus);
+  if (!c.ok()) return finish(c);
+  c = hip_status(launch_quant_rowwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, fmt == MXGG_MXFP8,
+                                         static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), cus, stream),
+                 "row-wise quantizer launch");
+  return c.ok() ? ok() : finish(c);
+}
+
+mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                         const int64_t* m_splits, int32_t G, mxgg_format fmt, uint32_t flags,
+                                         void* q, void* scales, int64_t mpad, hipStream_t stream) {
+  (void)flags;
+  Check c = validate_quantize_colwise(x, rows, cols, ldx, m_splits, G, (int)fmt, q, scales, mpad);
+  if (!c.ok()) return finish(c);
+  if (rows == 0) return ok();
+  if (!is_mx(fmt)) return finish(fail(MXGG_ERR_FORMAT, "blockwise FP8 quantization is not built in this library"));
+  int cus = 0;
+  c = device_checks(stream, {{x, "x"}, {q, "q"}, {scales, "scales"}}, &cus);
+  if (!c.ok()) return finish(c);
+  const SplitArgs sp = make_splits(m_splits, G);
+  c = hip_status(launch_quant_colwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8,
+                                         static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), mpad, stream),
+                 "column-wise quantizer launch");
+  return c.ok() ? ok() : finish(c);
+}
+
+mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt, const void* w_q, const void* w_s,
+                             mxgg_format w_fmt, const int64_t* m_splits, int32_t G, int64_t M, int64_t N, int64_t K,
+                             void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Check c = validate_fwd(a_q, a_s, (int)a_fmt, w_q, w_s, (int)w_fmt, m_splits, G, M, N, K, out, ws, ws_bytes,
+                         mxgg_workspace_size(G));
+  if (!c.ok()) return finish(c);
+  if (M == 0) return ok();
+  if (!is_mx(a_fmt)) return finish(fail(MXGG_ERR_FORMAT, "blockwise FP8 GEMMs are not built in this library"));
+  int cus = 0;
+  c = device_checks(stream, {{a_q, "a_q"}, {a_s, "a_s"}, {w_q, "w_q"}, {w_s, "w_s"}, {out, "out"}}, &cus);
+  if (!c.ok()) return finish(c);
+  RowsGemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  const bool a8 = a_fmt == MXGG_MXFP8;
+  p.a = static_cast<const uint8_t*>(a_q);
+  p.as = static_cast<const uint8_t*>(a_s);
+  p.b = static_cast<const uint8_t*>(w_q);
+  p.bs = static_cast<const uint8_t*>(w_s);
+  p.c = static_cast<uint16_t*>(out);
+  p.lda = a8 ? K : K / 2;
+  p.ldas = K / 32;
+  p.ldb = K / 2;
+  p.ldbs = K / 32;
+  p.b_gstride = N * (K / 2);
+  p.bs_gstride = N * (K / 32);
+  p.ldc = N;
+  p.n_out = (int32_t)N;
+  p.kc = (int32_t)K;
+  p.sp = make_splits(m_splits, G);
+  c = hip_status(launch_grouped_rows_mx(p, a8, cus, stream), "forward launch");
+  return c.ok() ? ok() : finish(c);
+}
+
+mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* wcol_q, const void* wcol_s,
+                               mxgg_format fmt, const int64_t* m_splits, int32_t G, int64_t M, int64_t N, int64_t K,
+                               void* dx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Check c = validate_dgrad(dy_q, dy_s, wcol_q, wcol_s, (int)fmt, m_splits, G, M, N, K, dx, ws, ws_bytes,
+                           mxgg_workspace_size(G));
+  if (!c.ok()) return finish(c);
+  if (M == 0) return ok();
+  int cus = 0;
+  c = device_checks(stream, {{dy_q, "dy_q"}, {dy_s, "dy_s"}, {wcol_q, "wcol_q"}, {wcol_s, "wcol_s"}, {dx, "dx"}},
+                    &cus);
+  if (!c.ok()) return finish(c);
+  RowsGemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.a = static_cast<const uint8_t*>(dy_q);
+  p.as = static_cast<const uint8_t*>(dy_s);
+  p.b = static_cast<const uint8_t*>(wcol_q);
+  p.bs = static_cast<const uint8_t*>(wcol_s);
+  p.c = static_cast<uint16_t*>(dx);
+  p.lda = N / 2;
+  p.ldas = N / 32;
+  p.ldb = (int64_t)G * N / 2;     // W column-wise: [K, G*N/2]
+  p.ldbs = (int64_t)G * N / 32;
+  p.b_gstride = N / 2;            // expert g owns columns [g*N, (g+1)*N)
+  p.bs_gstride = N / 32;
+  p.ldc = K;
+  p.n_out = (int32_t)K;
+  p.kc = (int32_t)N;
+  p.sp = make_splits(m_splits, G);
+  c = hip_status(launch_grouped_rows_mx(p, false, cus, stream), "dgrad launch");
+  return c.ok() ? ok() : finish(c);
+}
+
+mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const void* xcol_q, const void* xcol_s,
+                               mxgg_format fmt, const int64_t* m_splits, int32_t G, int64_t N, int64_t K,
+                               int64_t mpad, void* main_grad, int32_t out_is_bf16, int32_t accumulate, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  Check c = validate_wgrad(dycol_q, dycol_s, xcol_q, xcol_s, (int)fmt, m_splits, G, N, K, mpad, main_grad,
+                           out_is_bf16, accumulate, ws, ws_bytes, mxgg_workspace_size(G));
+  if (!c.ok()) return finish(c);
+  if (mpad == 0 && accumulate) return ok();
+  if (fmt != MXGG_MXFP4) return finish(fail(MXGG_ERR_FORMAT, "blockwise FP8 GEMMs are not built in this library"));
+  int cus = 0;
+  c = device_checks(stream, {{dycol_q, "dycol_q"}, {dycol_s, "dycol_s"}, {xcol_q, "xcol_q"}, {xcol_s, "xcol_s"},
+                             {main_grad, "main_grad"}},
+                    &cus);
+  if (!c.ok()) return finish(c);
+  WgradParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.a = static_cast<const uint8_t*>(dycol_q);
+  p.as = static_cast<const uint8_t*>(dycol_s);
+  p.b = static_cast<const uint8_t*>(xcol_q);
+  p.bs = static_cast<const uint8_t*>(xcol_s);
+  p.c = main_grad;
+  p.lda = mpad / 2;
+  p.ldas = mpad / 32;
+  p.ldb = mpad / 2;
+  p.ldbs = mpad / 32;
+  p.n_rows = (int32_t)N;
+  p.n_cols = (int32_t)K;
+  p.accumulate = accumulate;
+  p.out_bf16 = out_is_bf16;
+  p.sp = make_splits(m_splits, G);
+  // longest expert first: the variable-K tiles of big experts start early
+  int order[MXGG_MAX_EXPERTS];
+  std::iota(order, order + G, 0);
+  std::stable_sort(order, order + G, [&](int x, int y) { return m_splits[x] > m_splits[y]; });
+  for (int32_t j = 0; j < G; ++j) p.order[j] = (int16_t)order[j];
+  c = hip_status(launch_grouped_wgrad_mx(p, cus, stream), "wgrad launch");
+  return c.ok() ? ok() : finish(c);
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Device-side helpers shared by the quantizer and GEMM kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxgg {
+
+constexpr int kMaxExperts = 512;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Expert split counts travel as kernel arguments (int32, at most 512), so a
+// launch needs no device-side copy of the host array.
+struct SplitArgs {
+  int32_t G;
+  int32_t m[kMaxExperts];
+};
+
+// Block-wide exclusive prefix sum of 64-bit values v(g), g < G, into
+// out[0..G] (out[G] = total). Every thread of the block must call it.
+// Used on packed pairs (low and high 32-bit halves summed independently:
+// neither half's total may exceed 2^32 - 1).
+template <int THREADS, class F>
+__device__ inline void block_prefix64(int G, F v, int64_t* out, int64_t* wave_tot) {
+  static_assert(THREADS % 64 == 0 && THREADS >= 64, "threads");
+  constexpr int NW = THREADS / 64;
+  constexpr int PER = (kMaxExperts + THREADS - 1) / THREADS;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  int64_t local[PER];
+  int64_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = t * PER + i;
+    local[i] = (g < G) ? v(g) : 0;
+    sum += local[i];
+  }
+  // inclusive scan of per-thread sums inside the wave
+  int64_t inc = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int64_t o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  int64_t base = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+    if (w < wave) base += wave_tot[w];
+  int64_t run = base + inc - sum;  // exclusive prefix of this thread's first item
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = t * PER + i;
+    if (g < G) out[g] = run;
+    run += local[i];
+  }
+  if (t == THREADS - 1) out[G] = run;  // grand total (last thread's run covers all)
+  __syncthreads();
+}
+
+// Number of entries of the non-decreasing arr[0..n) that are <= val
+// (the upper_bound position). With arr = exclusive prefix offsets (arr[0] = 0)
+// the owning segment of item `val` is upper_bound - 1.
+__device__ inline int upper_bound_i32(const int32_t* arr, int n, int32_t val) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (arr[mid] <= val) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// The i-th 16-byte chunk position after an XOR swizzle that keeps the 16-byte
+// LDS accesses of 8 (or 16) consecutive rows in distinct banks.
+template <int CHUNKS_PER_ROW>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if constexpr (CHUNKS_PER_ROW == 8) {
+    return chunk ^ ((row ^ (row >> 3)) & 7);
+  } else if constexpr (CHUNKS_PER_ROW == 4) {
+    return chunk ^ (((row >> 1) ^ (row >> 3)) & 3);
+  } else if constexpr (CHUNKS_PER_ROW == 2) {
+    return chunk ^ ((row >> 2) & 1);
+  } else {
+    return chunk;
+  }
+}
+
+}  // namespace mxgg

@@ -1,0 +1,58 @@
+// Internal host-side launch interface between the C ABI (api.cpp) and the
+// kernels (*.hip). Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace mxgg {
+
+// Row-split grouped GEMM (forward and input gradient): out[r, :] for every row
+// r of expert g is A[r, :] . B_g^T, where B_g is the [n_out, kc] operand of
+// expert g starting at b + g * b_gstride with row stride ldb.
+struct RowsGemmParams {
+  const uint8_t* a;
+  const uint8_t* as;
+  const uint8_t* b;
+  const uint8_t* bs;
+  uint16_t* c;            // bf16 output
+  int64_t lda, ldas;      // A data / scale row strides (bytes)
+  int64_t ldb, ldbs;      // B data / scale row strides (bytes)
+  int64_t b_gstride;      // bytes between consecutive experts' B data
+  int64_t bs_gstride;     // bytes between consecutive experts' B scales
+  int64_t ldc;            // output row stride (elements)
+  int32_t n_out;          // output columns
+  int32_t kc;             // contraction length (elements), multiple of 32
+  SplitArgs sp;
+};
+
+// Variable-K grouped weight gradient: out[g] (rows n_rows, cols n_cols) =
+// A_g . B_g^T contracted over expert g's padded segment.
+struct WgradParams {
+  const uint8_t* a;       // [n_rows, mpad] operand (dY column-wise)
+  const uint8_t* as;
+  const uint8_t* b;       // [n_cols, mpad] operand (X column-wise)
+  const uint8_t* bs;
+  void* c;                // [G, n_rows, n_cols] fp32 (or bf16)
+  int64_t lda, ldas, ldb, ldbs;
+  int32_t n_rows, n_cols;
+  int32_t accumulate;
+  int32_t out_bf16;
+  SplitArgs sp;
+  int16_t order[kMaxExperts];  // experts by decreasing split (longest first)
+};
+
+struct DeviceInfo {
+  int num_cus;
+};
+
+hipError_t launch_quant_rowwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool fp8,
+                                   uint8_t* q, uint8_t* s, int num_cus, hipStream_t st);
+hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
+                                   bool fp8, uint8_t* q, uint8_t* s, int64_t mpad, hipStream_t st);
+
+hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, int num_cus, hipStream_t st);
+hipError_t launch_grouped_wgrad_mx(const WgradParams& p, int num_cus, hipStream_t st);
+
+}  // namespace mxgg

@@ -1,0 +1,217 @@
+// Host-side argument validation of the C ABI. Pure C++ (no HIP calls), so
+// every rule can be exercised on a machine without a GPU.
+//
+// Split rules follow the review of "Triton mxfp4 (and a8w4) grouped GEMM
+// kernel": splits are non-negative, there is one per expert, and they sum to
+// the row count of every row-split operand (unchecked offsets read or write out
+// of bounds, or leave part of a gradient unwritten). Empty experts are allowed.
+// The expert limit (512) and the rejection of unsupported shapes with a
+// status the caller can fall back on follow "Grouped MXFP8 GEMMs with
+// HipKittens"; validating before the empty-batch early return follows
+// "route te.GroupedLinear through #723; a8w4 fwd-only".
+#pragma once
+#include <stdint.h>
+
+#include <cstdio>
+#include <string>
+
+#include "../../include/mxgg.h"
+
+namespace mxgg {
+
+struct Check {
+  mxgg_status st = MXGG_OK;
+  std::string msg;
+  bool ok() const { return st == MXGG_OK; }
+};
+
+inline Check fail(mxgg_status st, const char* fmt, long long a = 0, long long b = 0, long long c = 0) {
+  Check r;
+  r.st = st;
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), fmt, a, b, c);
+  r.msg = buf;
+  return r;
+}
+
+inline bool is_mx(mxgg_format f) { return f == MXGG_MXFP4 || f == MXGG_MXFP8; }
+inline bool valid_format(int f) { return f >= MXGG_MXFP4 && f <= MXGG_FP8_128x128; }
+
+// Segment pad multiple of the column-wise operand of a format.
+inline int segpad_multiple(mxgg_format f) { return f == MXGG_FP8_1x128 ? 128 : 32; }
+
+// Splits: pointer, count, non-negativity and sum.
+inline Check check_splits(const int64_t* m, int32_t G, int64_t rows, const char* what) {
+  if (G < 1 || G > MXGG_MAX_EXPERTS) return fail(MXGG_ERR_SHAPE, "G=%lld outside [1, 512]", G);
+  if (!m) return fail(MXGG_ERR_NULL, "m_splits is NULL");
+  int64_t sum = 0;
+  for (int32_t g = 0; g < G; ++g) {
+    if (m[g] < 0) return fail(MXGG_ERR_SPLITS, "m_splits[%lld] = %lld is negative", g, m[g]);
+    sum += m[g];
+    if (sum > ((int64_t)1 << 40)) return fail(MXGG_ERR_SPLITS, "m_splits sum overflows");
+  }
+  if (sum != rows) {
+    Check r = fail(MXGG_ERR_SPLITS, "sum(m_splits) = %lld but %s has %lld rows", sum, 0, rows);
+    r.msg = "sum(m_splits) = " + std::to_string(sum) + " but " + what + " has " + std::to_string(rows) + " rows";
+    return r;
+  }
+  return Check{};
+}
+
+inline int64_t segpad_rows(const int64_t* m, int32_t G, int pad) {
+  int64_t s = 0;
+  for (int32_t g = 0; g < G; ++g) s += (m[g] + pad - 1) / pad * pad;
+  return s;
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A pointer that must be non-NULL and 16-byte aligned when the extent is
+// nonzero.
+inline Check check_ptr(const void* p, bool nonzero, const char* name) {
+  if (!nonzero) return Check{};
+  if (!p) {
+    Check r; r.st = MXGG_ERR_NULL; r.msg = std::string(name) + " is NULL"; return r;
+  }
+  if (!aligned16(p)) {
+    Check r; r.st = MXGG_ERR_ALIGN; r.msg = std::string(name) + " is not 16-byte aligned"; return r;
+  }
+  return Check{};
+}
+
+#define MXGG_TRY(expr)          \
+  do {                          \
+    ::mxgg::Check c_ = (expr);  \
+    if (!c_.ok()) return c_;    \
+  } while (0)
+
+// --- per entry point -------------------------------------------------------
+
+inline Check validate_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                       const void* q, const void* scales) {
+  if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
+  if (rows < 0 || cols <= 0) return fail(MXGG_ERR_SHAPE, "rows=%lld cols=%lld", rows, cols);
+  const mxgg_format f = (mxgg_format)fmt;
+  const int blk = is_mx(f) ? 32 : 128;
+  if (cols % blk) return fail(MXGG_ERR_SHAPE, "cols=%lld is not a multiple of %lld", cols, blk);
+  if (f == MXGG_FP8_128x128 && rows % 128) return fail(MXGG_ERR_SHAPE, "rows=%lld not a multiple of 128", rows);
+  if (ldx < cols) return fail(MXGG_ERR_SHAPE, "ldx=%lld < cols=%lld", ldx, cols);
+  if (ldx % 8) return fail(MXGG_ERR_ALIGN, "ldx=%lld not a multiple of 8 elements", ldx);
+  if (rows >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SHAPE, "rows=%lld >= 2^31", rows);
+  const bool nz = rows > 0;
+  MXGG_TRY(check_ptr(x, nz, "x"));
+  MXGG_TRY(check_ptr(q, nz, "q"));
+  MXGG_TRY(check_ptr(scales, nz, "scales"));
+  return Check{};
+}
+
+inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, const int64_t* m,
+                                       int32_t G, int fmt, const void* q, const void* scales, int64_t mpad) {
+  if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
+  const mxgg_format f = (mxgg_format)fmt;
+  if (f == MXGG_FP8_128x128) return fail(MXGG_ERR_FORMAT, "128x128 blocks have no column-wise form");
+  if (rows < 0 || cols <= 0) return fail(MXGG_ERR_SHAPE, "rows=%lld cols=%lld", rows, cols);
+  const int blk = is_mx(f) ? 32 : 128;
+  if (cols % 32) return fail(MXGG_ERR_SHAPE, "cols=%lld is not a multiple of 32", cols);
+  (void)blk;
+  if (ldx < cols) return fail(MXGG_ERR_SHAPE, "ldx=%lld < cols=%lld", ldx, cols);
+  if (ldx % 8) return fail(MXGG_ERR_ALIGN, "ldx=%lld not a multiple of 8 elements", ldx);
+  MXGG_TRY(check_splits(m, G, rows, "x"));
+  const int64_t need = segpad_rows(m, G, segpad_multiple(f));
+  if (mpad != need) return fail(MXGG_ERR_SHAPE, "mpad=%lld but the padded row count is %lld", mpad, need);
+  if (mpad >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SHAPE, "mpad=%lld >= 2^31", mpad);
+  const bool nz = rows > 0;
+  MXGG_TRY(check_ptr(x, nz, "x"));
+  MXGG_TRY(check_ptr(q, nz, "q"));
+  MXGG_TRY(check_ptr(scales, nz, "scales"));
+  return Check{};
+}
+
+inline Check validate_gemm_dims(int64_t M, int64_t N, int64_t K, int blk) {
+  if (M < 0 || N <= 0 || K <= 0) return fail(MXGG_ERR_SHAPE, "M=%lld N=%lld K=%lld", M, N, K);
+  if (N % blk || K % blk) return fail(MXGG_ERR_SHAPE, "N=%lld and K=%lld must be multiples of %lld", N, K, blk);
+  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 30))
+    return fail(MXGG_ERR_SHAPE, "M=%lld N=%lld K=%lld too large", M, N, K);
+  return Check{};
+}
+
+inline Check validate_fwd(const void* a_q, const void* a_s, int a_fmt, const void* w_q, const void* w_s, int w_fmt,
+                          const int64_t* m, int32_t G, int64_t M, int64_t N, int64_t K, const void* out,
+                          const void* ws, size_t ws_bytes, size_t ws_need) {
+  if (!valid_format(a_fmt) || !valid_format(w_fmt)) return fail(MXGG_ERR_FORMAT, "unknown format");
+  const bool a4w4 = a_fmt == MXGG_MXFP4 && w_fmt == MXGG_MXFP4;
+  const bool a8w4 = a_fmt == MXGG_MXFP8 && w_fmt == MXGG_MXFP4;
+  const bool blk = a_fmt == MXGG_FP8_1x128 && w_fmt == MXGG_FP8_128x128;
+  if (!(a4w4 || a8w4 || blk))
+    return fail(MXGG_ERR_FORMAT, "format pair (%lld, %lld) is not supported by the forward", a_fmt, w_fmt);
+  MXGG_TRY(validate_gemm_dims(M, N, K, blk ? 128 : 32));
+  MXGG_TRY(check_splits(m, G, M, "A"));
+  if (ws_bytes < ws_need) return fail(MXGG_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes,
+                                      (long long)ws_need);
+  if (ws_need) MXGG_TRY(check_ptr(ws, true, "ws"));
+  const bool nz = M > 0;
+  MXGG_TRY(check_ptr(a_q, nz, "a_q"));
+  MXGG_TRY(check_ptr(a_s, nz, "a_s"));
+  MXGG_TRY(check_ptr(w_q, nz, "w_q"));
+  MXGG_TRY(check_ptr(w_s, nz, "w_s"));
+  MXGG_TRY(check_ptr(out, nz, "out"));
+  return Check{};
+}
+
+inline Check validate_dgrad(const void* dy_q, const void* dy_s, const void* wc_q, const void* wc_s, int fmt,
+                            const int64_t* m, int32_t G, int64_t M, int64_t N, int64_t K, const void* dx,
+                            const void* ws, size_t ws_bytes, size_t ws_need) {
+  if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
+  if (fmt != MXGG_MXFP4) return fail(MXGG_ERR_FORMAT, "dgrad supports MXGG_MXFP4 only (got %lld)", fmt);
+  MXGG_TRY(validate_gemm_dims(M, N, K, 32));
+  MXGG_TRY(check_splits(m, G, M, "dY"));
+  if ((int64_t)G * N >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SHAPE, "G*N=%lld too large", (int64_t)G * N);
+  if (ws_bytes < ws_need) return fail(MXGG_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes,
+                                      (long long)ws_need);
+  if (ws_need) MXGG_TRY(check_ptr(ws, true, "ws"));
+  const bool nz = M > 0;
+  MXGG_TRY(check_ptr(dy_q, nz, "dy_q"));
+  MXGG_TRY(check_ptr(dy_s, nz, "dy_s"));
+  MXGG_TRY(check_ptr(wc_q, nz, "wcol_q"));
+  MXGG_TRY(check_ptr(wc_s, nz, "wcol_s"));
+  MXGG_TRY(check_ptr(dx, nz, "dx"));
+  return Check{};
+}
+
+inline Check validate_wgrad(const void* dy_q, const void* dy_s, const void* x_q, const void* x_s, int fmt,
+                            const int64_t* m, int32_t G, int64_t N, int64_t K, int64_t mpad, const void* main_grad,
+                            int32_t out_is_bf16, int32_t accumulate, const void* ws, size_t ws_bytes,
+                            size_t ws_need) {
+  if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
+  if (fmt != MXGG_MXFP4 && fmt != MXGG_FP8_1x128)
+    return fail(MXGG_ERR_FORMAT, "wgrad supports MXGG_MXFP4 and MXGG_FP8_1x128 (got %lld)", fmt);
+  if (out_is_bf16 != 0 && out_is_bf16 != 1) return fail(MXGG_ERR_SHAPE, "out_is_bf16=%lld", out_is_bf16);
+  if (accumulate != 0 && accumulate != 1) return fail(MXGG_ERR_SHAPE, "accumulate=%lld", accumulate);
+  const mxgg_format f = (mxgg_format)fmt;
+  const int blk = f == MXGG_FP8_1x128 ? 128 : 32;
+  if (N <= 0 || K <= 0 || N % blk || K % blk)
+    return fail(MXGG_ERR_SHAPE, "N=%lld and K=%lld must be positive multiples of %lld", N, K, blk);
+  if (N >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 30)) return fail(MXGG_ERR_SHAPE, "N or K too large");
+  if (G < 1 || G > MXGG_MAX_EXPERTS) return fail(MXGG_ERR_SHAPE, "G=%lld outside [1, 512]", G);
+  if (!m) return fail(MXGG_ERR_NULL, "m_splits is NULL");
+  int64_t rows = 0;
+  for (int32_t g = 0; g < G; ++g) {
+    if (m[g] < 0) return fail(MXGG_ERR_SPLITS, "m_splits[%lld] = %lld is negative", g, m[g]);
+    rows += m[g];
+  }
+  if (rows >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SPLITS, "sum(m_splits)=%lld >= 2^31", rows);
+  const int64_t need = segpad_rows(m, G, segpad_multiple(f));
+  if (mpad != need) return fail(MXGG_ERR_SHAPE, "mpad=%lld but the padded row count is %lld", mpad, need);
+  if (ws_bytes < ws_need) return fail(MXGG_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes,
+                                      (long long)ws_need);
+  if (ws_need) MXGG_TRY(check_ptr(ws, true, "ws"));
+  const bool nz = mpad > 0;
+  MXGG_TRY(check_ptr(dy_q, nz, "dycol_q"));
+  MXGG_TRY(check_ptr(dy_s, nz, "dycol_s"));
+  MXGG_TRY(check_ptr(x_q, nz, "xcol_q"));
+  MXGG_TRY(check_ptr(x_s, nz, "xcol_s"));
+  MXGG_TRY(check_ptr(main_grad, true, "main_grad"));
+  return Check{};
+}
+
+}  // namespace mxgg

@@ -1,0 +1,48 @@
+"""Helpers shared by the GPU tests: host <-> device copies and the GEMM
+tolerance. No arithmetic of the method lives here."""
+import numpy as np
+
+try:
+    import torch
+except ImportError:  # pragma: no cover
+    torch = None
+
+from oracle.formats import bf16_bits_to_f64
+
+
+def have_gpu() -> bool:
+    return torch is not None and torch.cuda.is_available()
+
+
+def dev_bf16(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def dev_f32(x: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda")
+
+
+def host(t) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def host_bf16_f64(t) -> np.ndarray:
+    return bf16_bits_to_f64(t.detach().view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def gemm_bound(ref: np.ndarray, rms=None) -> np.ndarray:
+    """|gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref): fp32 accumulation in any
+    order plus the bf16 rounding of the output stay well inside it, while a
+    wrong scale, a dropped block or a transposed operand do not."""
+    if rms is None:
+        rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    return 2.0 ** -7 * np.abs(ref) + 1e-3 * rms
+
+
+def assert_gemm_close(gpu: np.ndarray, ref: np.ndarray, rms=None, what=""):
+    b = gemm_bound(ref, rms)
+    err = np.abs(gpu - ref)
+    ratio = np.where(b > 0, err / np.where(b > 0, b, 1), np.where(err > 0, np.inf, 0))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    assert worst <= 1.0, f"{what}: max |gpu-ref|/bound = {worst:.3g} at {np.unravel_index(np.argmax(ratio), ratio.shape)}"
+    return worst

@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before any HIP call (so these run
+on a machine with no GPU). Pointers here are fake, aligned device addresses
+that validation never dereferences."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import moe_grouped_block_mx_amd as mx
+from oracle.mx import segpad_offsets
+
+L = mx.lib
+P = ctypes.c_void_p(0x100000)     # a fake 16-byte aligned device address
+BAD = ctypes.c_void_p(0x100008)   # misaligned
+NULL = None
+
+
+def splits(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def last():
+    return L.mxgg_last_error().decode()
+
+
+def test_exports_every_declared_function():
+    names = mx.header_functions()
+    assert {"mxgg_quantize_rowwise", "mxgg_quantize_colwise_segpad", "mxgg_grouped_fwd",
+            "mxgg_grouped_dgrad", "mxgg_grouped_wgrad", "mxgg_workspace_size",
+            "mxgg_segpad_rows", "mxgg_status_string", "mxgg_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(10):
+        assert L.mxgg_status_string(s).decode().startswith(mx._lib.STATUS[s])
+
+
+def fwd(m, G, M, N=64, K=64, a_fmt=0, w_fmt=0, a=P, out=P):
+    return L.mxgg_grouped_fwd(a, P, a_fmt, P, P, w_fmt, m, G, M, N, K, out, NULL, 0, NULL)
+
+
+def test_fwd_split_rules():
+    assert fwd(splits(3, -1), 2, 2) == 3 and "negative" in last()          # negative
+    assert fwd(splits(3, 4), 2, 8) == 3 and "sum" in last()                # sum != rows
+    assert fwd(splits(3, 4), 2, 6) == 3                                     # sum != rows
+    assert fwd(splits(3), 0, 3) == 2                                        # G = 0
+    big = (ctypes.c_int64 * 513)(*([0] * 513))
+    assert fwd(big, 513, 0) == 2                                            # G > 512
+    assert fwd(None, 2, 0) == 1                                             # NULL splits
+
+
+def test_fwd_shapes_formats_pointers():
+    m = splits(2, 0, 6)
+    assert fwd(m, 3, 8, K=48) == 2            # K % 32
+    assert fwd(m, 3, 8, N=40) == 2            # N % 32
+    assert fwd(m, 3, 8, a_fmt=1, w_fmt=1) == 4   # MXFP8 weights: not a supported pair
+    assert fwd(m, 3, 8, a_fmt=0, w_fmt=3) == 4
+    assert fwd(m, 3, 8, a_fmt=7) == 4
+    assert fwd(m, 3, 8, a=NULL) == 1
+    assert fwd(m, 3, 8, a=BAD) == 5
+    assert fwd(m, 3, 8, out=NULL) == 1
+    # blockwise pair needs multiples of 128
+    assert fwd(m, 3, 8, N=64, K=128, a_fmt=2, w_fmt=3) == 2
+
+
+def test_empty_batch_validated_then_ok_without_gpu():
+    # M == 0 with valid arguments returns OK before any device work
+    assert fwd(splits(0, 0), 2, 0, a=NULL, out=NULL) == 0
+    # ...but the splits are still validated first
+    assert fwd(splits(1, -1), 2, 0, a=NULL, out=NULL) == 3
+    assert L.mxgg_quantize_rowwise(NULL, 0, 64, 64, 0, 0, NULL, NULL, NULL) == 0
+    assert L.mxgg_grouped_dgrad(NULL, NULL, NULL, NULL, 0, splits(0, 0), 2, 0, 64, 64, NULL, NULL, 0, NULL) == 0
+
+
+def test_dgrad_rules():
+    m = splits(4, 4)
+    assert L.mxgg_grouped_dgrad(P, P, P, P, 1, m, 2, 8, 64, 64, P, NULL, 0, NULL) == 4   # a8w4 dgrad
+    assert L.mxgg_grouped_dgrad(P, P, P, P, 0, m, 2, 9, 64, 64, P, NULL, 0, NULL) == 3
+    assert L.mxgg_grouped_dgrad(P, P, P, P, 0, m, 2, 8, 64, 33, P, NULL, 0, NULL) == 2
+    assert L.mxgg_grouped_dgrad(P, P, NULL, P, 0, m, 2, 8, 64, 64, P, NULL, 0, NULL) == 1
+
+
+def test_quantizer_rules():
+    assert L.mxgg_quantize_rowwise(P, 4, 48, 48, 0, 0, P, P, NULL) == 2       # cols % 32
+    assert L.mxgg_quantize_rowwise(P, 4, 64, 32, 0, 0, P, P, NULL) == 2       # ldx < cols
+    assert L.mxgg_quantize_rowwise(P, 4, 64, 68, 0, 0, P, P, NULL) == 5       # ldx % 8
+    assert L.mxgg_quantize_rowwise(P, 4, 64, 64, 9, 0, P, P, NULL) == 4       # format
+    assert L.mxgg_quantize_rowwise(P, 4, 64, 64, 0, 0, BAD, P, NULL) == 5
+    assert L.mxgg_quantize_rowwise(P, 100, 128, 128, 3, 0, P, P, NULL) == 2   # 128x128 rows % 128
+    m = splits(5, 0, 40)
+    good = 32 + 64
+    assert L.mxgg_quantize_colwise_segpad(P, 45, 64, 64, m, 3, 0, 0, P, P, good + 32, NULL) == 2  # mpad
+    assert L.mxgg_quantize_colwise_segpad(P, 44, 64, 64, m, 3, 0, 0, P, P, good, NULL) == 3      # sum
+    assert L.mxgg_quantize_colwise_segpad(P, 45, 64, 64, m, 3, 3, 0, P, P, good, NULL) == 4      # 128x128
+    assert L.mxgg_quantize_colwise_segpad(P, 45, 64, 64, splits(5, -1, 41), 3, 0, 0, P, P, good, NULL) == 3
+
+
+def test_wgrad_rules():
+    m = splits(5, 0, 40)
+    mp = 96
+    w = lambda **k: L.mxgg_grouped_wgrad(k.get("dy", P), P, P, P, k.get("fmt", 0), k.get("m", m), 3, 64, 64,
+                                          k.get("mp", mp), k.get("out", P), k.get("bf16", 0), k.get("acc", 1),
+                                          NULL, 0, NULL)
+    assert w(mp=128) == 2
+    assert w(fmt=1) == 4
+    assert w(out=NULL) == 1
+    assert w(acc=2) == 2
+    assert w(m=splits(5, -3, 40)) == 3
+    assert w(dy=BAD) == 5
+    # all experts empty with accumulate: nothing to do, OK without a GPU
+    assert L.mxgg_grouped_wgrad(NULL, NULL, NULL, NULL, 0, splits(0, 0, 0), 3, 64, 64, 0, P, 0, 1,
+                                NULL, 0, NULL) == 0
+
+
+@pytest.mark.parametrize("fmt,pad", [(0, 32), (1, 32), (2, 128)])
+def test_segpad_rows_matches_oracle(fmt, pad):
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        G = int(rng.integers(1, 40))
+        v = rng.integers(0, 300, size=G)
+        v[rng.random(G) < 0.2] = 0
+        _, po = segpad_offsets(v, pad)
+        assert L.mxgg_segpad_rows(splits(*[int(x) for x in v]), G, fmt) == po[-1]
+    assert L.mxgg_segpad_rows(splits(1, -1), 2, 0) == -1
+    assert L.mxgg_segpad_rows(splits(1), 1, 3) == -1
+    assert L.mxgg_workspace_size(32) == 0
