@@ -19,7 +19,7 @@ launched on; the dominant kernel's roofline is reported against MI355X's
 published peaks (MXFP4 dense MFMA 10.1 PFLOP/s, HBM3E 8 TB/s).
 
 cpu_baseline: the CPU oracle (NumPy fp64) timed on a bounded sample of the
-same step -- one expert with 1024 tokens at the full K and N, all three
+same step -- one expert with 8192 tokens at the full K and N, all three
 passes including quantization -- on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -54,7 +54,7 @@ def parse():
 
 
 def cpu_baseline(seconds_hint=20.0):
-    """The oracle on a bounded sample: one expert, 1024 tokens, K=4096,
+    """The oracle on a bounded sample: one expert with 8192 tokens, K=4096,
     N=3072; fwd + dgrad + wgrad including every quantization."""
     from threadpoolctl import threadpool_info
 
@@ -62,7 +62,7 @@ def cpu_baseline(seconds_hint=20.0):
     from oracle import mx as omx
     from synth import bf16_normal
 
-    m, K, N = 1024, 4096, 3072
+    m, K, N = 8192, 4096, 3072
     a = bf16_normal((m, K), 1.0, seed=1)
     w = bf16_normal((N, K), 0.02, seed=2)
     dy = bf16_normal((m, N), 1.0, seed=3)

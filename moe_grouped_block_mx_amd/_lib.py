@@ -109,6 +109,19 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_bf16_2d(x):
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bf16 tensor")
+    if x.numel() and x.stride(1) != 1:
+        raise ValueError("x must have unit inner stride")
+
+
+def _ld(x):
+    """Leading dimension in elements (the column count for an empty tensor)."""
+    return x.stride(0) if x.numel() else x.shape[1]
+
+
 def mxgg_workspace_size(G: int) -> int:
     return int(lib.mxgg_workspace_size(G))
 
@@ -126,8 +139,7 @@ def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=0, q=None, scales=None):
     torch = _torch()
     f = _fmt(fmt)
     rows, cols = x.shape
-    if x.dtype != torch.bfloat16 or x.stride(1) != 1:
-        raise ValueError("x must be bf16 with unit inner stride")
+    _check_bf16_2d(x)
     if q is None:
         q = torch.empty((rows, cols // 2 if f == MXFP4 else cols), dtype=torch.uint8, device=x.device)
     if scales is None:
@@ -137,7 +149,7 @@ def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=0, q=None, scales=None):
             scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
         else:
             scales = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=x.device)
-    _check(lib.mxgg_quantize_rowwise(_ptr(x), rows, cols, x.stride(0), f, flags, _ptr(q), _ptr(scales),
+    _check(lib.mxgg_quantize_rowwise(_ptr(x), rows, cols, _ld(x), f, flags, _ptr(q), _ptr(scales),
                                      _stream(x)))
     return q, scales
 
@@ -147,8 +159,7 @@ def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=0, q=None, scal
     torch = _torch()
     f = _fmt(fmt)
     rows, cols = x.shape
-    if x.dtype != torch.bfloat16 or x.stride(1) != 1:
-        raise ValueError("x must be bf16 with unit inner stride")
+    _check_bf16_2d(x)
     arr, G = _splits(m_splits)
     mpad = int(lib.mxgg_segpad_rows(arr, G, f))
     if mpad < 0:
@@ -160,7 +171,7 @@ def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=0, q=None, scal
             scales = torch.empty((cols, mpad // 128), dtype=torch.float32, device=x.device)
         else:
             scales = torch.empty((cols, mpad // 32), dtype=torch.uint8, device=x.device)
-    _check(lib.mxgg_quantize_colwise_segpad(_ptr(x), rows, cols, x.stride(0), arr, G, f, flags, _ptr(q),
+    _check(lib.mxgg_quantize_colwise_segpad(_ptr(x), rows, cols, _ld(x), arr, G, f, flags, _ptr(q),
                                             _ptr(scales), mpad, _stream(x)))
     return q, scales, mpad
 
