@@ -1,41 +1,47 @@
 // Grouped block-scaled (MX) GEMMs for gfx950: forward, input gradient and
-// variable-K weight gradient in one launch each.
+// variable-K weight gradient, one launch each.
 //
-// Method (see the pages "Triton mxfp4 (and a8w4) grouped GEMM kernel" and
-// "Grouped MXFP8 GEMMs with HipKittens"): a persistent grid walks all output
-// tiles of all experts; a tile index maps to its expert with an upper_bound
-// search over the prefix sum of per-expert tile counts, built in LDS by every
-// workgroup from the split counts passed as kernel arguments. Every output
-// element belongs to exactly one tile and is stored under masks on
-// un-wrapped indices (the tail-tile rule of "Add ROCm Triton blockwise FP8
-// grouped GEMM").
+// Method (pages "Triton mxfp4 (and a8w4) grouped GEMM kernel" and "Grouped
+// MXFP8 GEMMs with HipKittens"): a persistent grid walks all output tiles of
+// all experts; a tile index maps to its expert with an upper_bound search over
+// the prefix sum of per-expert tile counts, built in LDS by every workgroup
+// from the split counts passed as kernel arguments. Every output element
+// belongs to exactly one tile and is stored under masks on un-wrapped indices
+// (the tail-tile rule of "Add ROCm Triton blockwise FP8 grouped GEMM").
 //
 // All three passes are "TN" on quantized data (MX scales run along the
-// contraction axis, so both operands are contraction-contiguous); only the
-// tile scheduler and the epilogue differ between them.
+// contraction axis, so both operands are contraction-contiguous); only the tile
+// source (which tile, which operand bases, how long the contraction) and the
+// epilogue differ between them.
 //
-// Tile: BM x BN outputs per workgroup, WM x WN waves, each wave owning a
-// (BM/WM) x (BN/WN) block of 32x32 fragments computed with the CDNA4
-// instruction v_mfma_scale_f32_32x32x64_f8f6f4. Measured operand layout of
-// that instruction (32x32x64): lane l holds row l % 32 of its operand; for
-// E2M1 the 16 bytes at byte offset 16*(l/32) of the row's 32-byte K chunk,
-// for E4M3 the 16 bytes at 16*(l/32) and at 32 + 16*(l/32) of the 64-byte
-// chunk; the scale byte (selected by op_sel) of lane l applies to row l % 32,
-// K-block l/32; result register i of lane l is row 8*(i/4) + 4*(l/32) + i%4,
-// column l % 32.
+// MFMA: v_mfma_scale_f32_32x32x64_f8f6f4. Measured operand layout (32x32x64):
+// lane l holds row l % 32 of its operand; for E2M1 the 16 bytes at byte offset
+// 16*(l/32) of the row's 32-byte K chunk, for E4M3 the 16 bytes at 16*(l/32)
+// and at 32 + 16*(l/32) of the 64-byte chunk; the op_sel-selected scale byte of
+// lane l applies to row l % 32, K-block l/32; result register i of lane l is
+// row 8*(i/4) + 4*(l/32) + i%4, column l % 32.
 //
-// Per K stage (BK elements) the workgroup copies the A and B tiles from HBM
-// into registers (16-byte coalesced loads), then into a double-buffered,
-// XOR-swizzled LDS tile, while each lane fetches its own scale bytes
-// (one per fragment per 32-element block) straight into registers and packs
-// the K stage's bytes so op_sel picks the right one.
+// Data movement: every load of the main loop is an LDS DMA
+// (global_load_lds_dwordx4 for operand chunks, global_load_lds_ubyte for scale
+// bytes, which land one per dword), so no VGPR is spent on staging and the
+// waits are explicit: a STAGES-deep LDS ring is kept full, a stage is consumed
+// after `s_waitcnt vmcnt` (counting only the DMAs issued after it) and a raw
+// s_barrier (no fence: a workgroup fence would drain every DMA in flight). The
+// ring runs across the tiles of a workgroup, so the next tile's first stages are
+// in flight during the current tile's epilogue. Operand chunks are placed with
+// an XOR swizzle of the 16-byte chunk index, chosen per lane on the global side
+// (the DMA writes lane-contiguous LDS). The epilogue goes through a per-wave LDS
+// scratch so global stores (and wgrad's fp32 read-modify-write) are 16-byte.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "device_common.hpp"
 #include "launch.hpp"
+
+#define MXGG_LDS __attribute__((address_space(3)))
 
 namespace mxgg {
 
@@ -51,314 +57,493 @@ __device__ __forceinline__ void unroll(F&& f) {
   unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, bool AFP8_>
+// s_waitcnt encodings (gfx9): vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits
+// 15:14, expcnt in 6:4, lgkmcnt in 11:8; a field at its maximum does not wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without a memory fence; the compiler may not move memory
+// operations across it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Source of the zero chunks / zero scale bytes read past the contraction end.
+static __device__ __attribute__((aligned(64))) uint32_t g_zero_page[16];
+
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (MXGG_LDS void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma1(const uint8_t* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (MXGG_LDS void*)lds, 1, 0, 0);
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool AFP8_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
   static constexpr bool AFP8 = AFP8_;
-  static constexpr int THREADS = 64 * WM * WN;
+  static constexpr int NW = WM * WN, THREADS = 64 * NW;
   static constexpr int RBA = AFP8 ? BK : BK / 2;  // A bytes per row per stage
   static constexpr int RBB = BK / 2;              // B (E2M1) bytes per row per stage
   static constexpr int CPA = RBA / 16, CPB = RBB / 16;
   static constexpr int KSTEPS = BK / 64;          // MFMA K steps per stage
+  static constexpr int SB = BK / 32;              // scale blocks per row per stage
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int NLA = BM * CPA / THREADS;  // 16-byte loads per thread per stage
-  static constexpr int NLB = BN * CPB / THREADS;
-  static constexpr int RSA = THREADS / CPA, RSB = THREADS / CPB;
-  static constexpr int LDS_A = BM * RBA, LDS_B = BN * RBB;
-  static_assert(BM * CPA % THREADS == 0 && BN * CPB % THREADS == 0, "load split");
-  static_assert(THREADS % CPA == 0 && THREADS % CPB == 0, "load rows");
-  static_assert(KSTEPS >= 1 && KSTEPS <= 4, "scale bytes per word");
-  static_assert(FM >= 1 && FN >= 1, "fragments");
+  // one ring stage: A chunks, B chunks, A scale dwords, B scale dwords
+  static constexpr int A_OFF = 0, A_BYTES = BM * RBA;
+  static constexpr int B_OFF = A_OFF + A_BYTES, B_BYTES = BN * RBB;
+  static constexpr int AS_OFF = B_OFF + B_BYTES, AS_BYTES = BM * SB * 4;
+  static constexpr int BS_OFF = AS_OFF + AS_BYTES, BS_BYTES = BN * SB * 4;
+  static constexpr int STAGE_BYTES = BS_OFF + BS_BYTES;
+  // LDS DMA instructions per wave per stage (1 KiB of chunks or 64 scale bytes each)
+  static constexpr int DA = A_BYTES / (NW * 1024), DB = B_BYTES / (NW * 1024);
+  static constexpr int DSA = AS_BYTES / (NW * 256), DSB = BS_BYTES / (NW * 256);
+  static constexpr int DPS = DA + DB + DSA + DSB;
+  static constexpr int EPI_BYTES = 16 * 33 * 4;  // per-wave epilogue scratch (16 rows x 32 fp32, padded)
+  static constexpr int EPI_OFF = STAGES * STAGE_BYTES;
+  static constexpr int SMEM_BYTES = EPI_OFF + NW * EPI_BYTES;
+  static_assert(A_BYTES % (NW * 1024) == 0 && B_BYTES % (NW * 1024) == 0, "chunk DMA split");
+  static_assert(AS_BYTES % (NW * 256) == 0 && BS_BYTES % (NW * 256) == 0, "scale DMA split");
+  static_assert(KSTEPS == 1 || KSTEPS == 2, "K steps per stage");
+  static_assert(FM >= 1 && FN >= 1 && STAGES >= 2 && STAGES <= 4, "shape");
+  static_assert(DPS * (STAGES - 2) < 64, "vmcnt range");
 };
 
-// Per-thread state of one tile's main loop.
+// Scale dword position p inside a row's stage -> K block. With two K steps per
+// stage the row is stored as blocks [0, 2, 1, 3], so the lane half h reads the
+// adjacent dwords (2h, 2h+1) = blocks (h, 2+h), i.e. K step 0 and 1.
 template <class C>
-struct LoopState {
-  uint32_t pa[C::NLA], pb[C::NLB];     // byte offsets of this thread's copy rows
-  uint32_t psa[C::FM], psb[C::FN];     // byte offsets of this lane's scale rows
-  v4i ra[C::NLA], rb[C::NLB];          // staged 16-byte chunks of the next stage
-  uint32_t sa_cur[C::FM], sb_cur[C::FN];           // packed scale words in use
-  uint32_t sa_raw[C::FM][C::KSTEPS], sb_raw[C::FN][C::KSTEPS];  // next stage, unpacked
+__device__ __forceinline__ int scale_block_of(int p) {
+  if constexpr (C::SB == 4) return (p & 1) * 2 + (p >> 1);
+  else return p;
+}
+
+// Operand bases and extents of one tile.
+struct TileOps {
+  const uint8_t* a;   // first row of the A tile (row stride lda)
+  const uint8_t* as;  // its scales (row stride ldas)
+  const uint8_t* b;
+  const uint8_t* bs;
+  int mrows, nrows;   // valid rows of A and B (>= 1)
+  int kc;             // contraction length (elements), multiple of 32
+};
+
+// Per-thread DMA offsets of the issuing tile (32-bit: a tile's rows span less
+// than 4 GiB, which the ABI's shape limits guarantee).
+template <class C>
+struct DmaPlan {
+  uint32_t offA[C::DA], offB[C::DB], offAS[C::DSA], offBS[C::DSB];
+  int kA[C::DA], kB[C::DB];       // byte offset of the chunk inside a stage row
+  int bAS[C::DSA], bBS[C::DSB];   // K block inside a stage
 };
 
 template <class C>
-__device__ __forceinline__ void stage_gload(LoopState<C>& st, const uint8_t* __restrict__ A,
-                                            const uint8_t* __restrict__ B, int s, int kca, int kcb) {
-  const int tid = threadIdx.x;
-  if ((s + 1) * C::RBA <= kca) {  // whole stage inside the contraction (uniform branch)
-#pragma unroll
-    for (int i = 0; i < C::NLA; ++i) st.ra[i] = *reinterpret_cast<const v4i*>(A + st.pa[i] + s * C::RBA);
-#pragma unroll
-    for (int i = 0; i < C::NLB; ++i) st.rb[i] = *reinterpret_cast<const v4i*>(B + st.pb[i] + s * C::RBB);
-    return;
-  }
-  const int ka = s * C::RBA + (tid % C::CPA) * 16;
-  const int kb = s * C::RBB + (tid % C::CPB) * 16;
-#pragma unroll
-  for (int i = 0; i < C::NLA; ++i)
-    st.ra[i] = (ka < kca) ? *reinterpret_cast<const v4i*>(A + st.pa[i] + s * C::RBA) : v4i{0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < C::NLB; ++i)
-    st.rb[i] = (kb < kcb) ? *reinterpret_cast<const v4i*>(B + st.pb[i] + s * C::RBB) : v4i{0, 0, 0, 0};
+__device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64_t lda, int64_t ldas, int64_t ldb,
+                                         int64_t ldbs, int w, int lane) {
+  unroll<C::DA>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int o = (i * C::NW + w) * 1024 + lane * 16;
+    const int r = o / C::RBA;
+    const int c = swz<C::CPA>(r, (o % C::RBA) / 16);
+    const int rr = r < t.mrows ? r : t.mrows - 1;
+    pl.offA[i] = (uint32_t)(rr * lda) + c * 16;
+    pl.kA[i] = c * 16;
+  });
+  unroll<C::DB>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int o = (i * C::NW + w) * 1024 + lane * 16;
+    const int r = o / C::RBB;
+    const int c = swz<C::CPB>(r, (o % C::RBB) / 16);
+    const int rr = r < t.nrows ? r : t.nrows - 1;
+    pl.offB[i] = (uint32_t)(rr * ldb) + c * 16;
+    pl.kB[i] = c * 16;
+  });
+  unroll<C::DSA>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int d = (i * C::NW + w) * 64 + lane;
+    const int r = d / C::SB;
+    const int blk = scale_block_of<C>(d % C::SB);
+    const int rr = r < t.mrows ? r : t.mrows - 1;
+    pl.offAS[i] = (uint32_t)(rr * ldas) + blk;
+    pl.bAS[i] = blk;
+  });
+  unroll<C::DSB>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int d = (i * C::NW + w) * 64 + lane;
+    const int r = d / C::SB;
+    const int blk = scale_block_of<C>(d % C::SB);
+    const int rr = r < t.nrows ? r : t.nrows - 1;
+    pl.offBS[i] = (uint32_t)(rr * ldbs) + blk;
+    pl.bBS[i] = blk;
+  });
 }
 
-// Scale bytes of stage s: for K step kk, lane half h uses block 2*kk + h of
-// the stage. Loads are branch-free (the block index is clamped into the row)
-// and stay unpacked until the stage is consumed, so waiting on them never
-// waits on the data prefetch issued alongside.
-template <class C, int NF>
-__device__ __forceinline__ void stage_sload(const uint32_t (&ps)[NF], const uint8_t* __restrict__ S,
-                                            uint32_t (&raw)[NF][C::KSTEPS], int s, int nblk) {
-  const int h = (threadIdx.x & 63) >> 5;
-  const int blk0 = s * (C::BK / 32) + h;
-#pragma unroll
-  for (int kk = 0; kk < C::KSTEPS; ++kk) {
-    int blk = blk0 + 2 * kk;
-    blk = blk < nblk ? blk : nblk - 1;
-#pragma unroll
-    for (int i = 0; i < NF; ++i) raw[i][kk] = S[ps[i] + blk];
-  }
-}
-
-// Packs stage s's scale bytes (byte kk = K step kk); blocks past the
-// contraction end get byte 127 (their data is zero).
-template <class C, int NF>
-__device__ __forceinline__ void stage_spack(const uint32_t (&raw)[NF][C::KSTEPS], uint32_t (&out)[NF], int s,
-                                            int nblk) {
-  const int h = (threadIdx.x & 63) >> 5;
-  const int blk0 = s * (C::BK / 32) + h;
-#pragma unroll
-  for (int i = 0; i < NF; ++i) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) w |= (blk0 + 2 * kk < nblk ? raw[i][kk] : 127u) << (8 * kk);
-    out[i] = w;
-  }
-}
-
+// Issue the DMAs of stage s of tile t into ring slot `st` (every wave issues
+// exactly DPS instructions, the count the waits rely on).
 template <class C>
-__device__ __forceinline__ void stage_lstore(const LoopState<C>& st, uint8_t* la, uint8_t* lb) {
-  const int tid = threadIdx.x;
-  const int ca = tid % C::CPA, ra0 = tid / C::CPA;
-  const int cb = tid % C::CPB, rb0 = tid / C::CPB;
-#pragma unroll
-  for (int i = 0; i < C::NLA; ++i) {
-    const int r = ra0 + i * C::RSA;
-    *reinterpret_cast<v4i*>(la + r * C::RBA + swz<C::CPA>(r, ca) * 16) = st.ra[i];
-  }
-#pragma unroll
-  for (int i = 0; i < C::NLB; ++i) {
-    const int r = rb0 + i * C::RSB;
-    *reinterpret_cast<v4i*>(lb + r * C::RBB + swz<C::CPB>(r, cb) * 16) = st.rb[i];
-  }
+__device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps& t, int s, uint8_t* st, int w) {
+  const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_zero_page);
+  const int kca = C::AFP8 ? t.kc : t.kc / 2;
+  const int kcb = t.kc / 2;
+  const int nblk = t.kc / 32;
+  const int ka0 = s * C::RBA, kb0 = s * C::RBB, blk0 = s * C::SB;
+  unroll<C::DA>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const uint8_t* src = (ka0 + pl.kA[i] < kca) ? t.a + pl.offA[i] + ka0 : zero;
+    dma16(src, st + C::A_OFF + (i * C::NW + w) * 1024);
+  });
+  unroll<C::DB>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const uint8_t* src = (kb0 + pl.kB[i] < kcb) ? t.b + pl.offB[i] + kb0 : zero;
+    dma16(src, st + C::B_OFF + (i * C::NW + w) * 1024);
+  });
+  unroll<C::DSA>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const uint8_t* src = (blk0 + pl.bAS[i] < nblk) ? t.as + pl.offAS[i] + blk0 : zero;
+    dma1(src, st + C::AS_OFF + (i * C::NW + w) * 256);
+  });
+  unroll<C::DSB>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const uint8_t* src = (blk0 + pl.bBS[i] < nblk) ? t.bs + pl.offBS[i] + blk0 : zero;
+    dma1(src, st + C::BS_OFF + (i * C::NW + w) * 256);
+  });
 }
 
-// One MFMA K step (64 contraction elements) of the wave's fragments.
-template <class C, int KK>
-__device__ __forceinline__ void kstep(const uint8_t* la, const uint8_t* lb, const uint32_t (&sa)[C::FM],
-                                      const uint32_t (&sb)[C::FN], v16f (&acc)[C::FM][C::FN]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int h = lane >> 5, l32 = lane & 31;
-  v8i af[C::FM], bf[C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int r = wm * C::WTM + i * 32 + l32;
-    if constexpr (C::AFP8) {
-      const v4i lo = *reinterpret_cast<const v4i*>(la + r * C::RBA + swz<C::CPA>(r, 4 * KK + h) * 16);
-      const v4i hi = *reinterpret_cast<const v4i*>(la + r * C::RBA + swz<C::CPA>(r, 4 * KK + 2 + h) * 16);
-      af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    } else {
-      const v4i lo = *reinterpret_cast<const v4i*>(la + r * C::RBA + swz<C::CPA>(r, 2 * KK + h) * 16);
-      af[i] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < C::FN; ++j) {
-    const int r = wn * C::WTN + j * 32 + l32;
-    const v4i lo = *reinterpret_cast<const v4i*>(lb + r * C::RBB + swz<C::CPB>(r, 2 * KK + h) * 16);
-    bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-  }
+// MFMAs of one ring stage for this wave's fragments.
+template <class C>
+__device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::FM][C::FN], int wm, int wn, int h,
+                                              int l32) {
+  uint32_t sa[C::FM], sb[C::FN];
   unroll<C::FM>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int r = wm * C::WTM + i * 32 + l32;
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(st + C::AS_OFF) + r * C::SB + h * C::KSTEPS;
+    if constexpr (C::KSTEPS == 2) sa[i] = p[0] | (p[1] << 8);
+    else sa[i] = p[0];
+  });
+  unroll<C::FN>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const int r = wn * C::WTN + j * 32 + l32;
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(st + C::BS_OFF) + r * C::SB + h * C::KSTEPS;
+    if constexpr (C::KSTEPS == 2) sb[j] = p[0] | (p[1] << 8);
+    else sb[j] = p[0];
+  });
+  unroll<C::KSTEPS>([&](auto kc_) {
+    constexpr int kk = decltype(kc_)::value;
+    v8i af[C::FM], bf[C::FN];
+    unroll<C::FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int r = wm * C::WTM + i * 32 + l32;
+      const uint8_t* row = st + C::A_OFF + r * C::RBA;
+      if constexpr (C::AFP8) {
+        const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r, 4 * kk + h) * 16);
+        const v4i hi = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r, 4 * kk + 2 + h) * 16);
+        af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r, 2 * kk + h) * 16);
+        af[i] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+      }
+    });
     unroll<C::FN>([&](auto jc) {
-      constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], C::AFP8 ? 0 : 4, 4, KK,
-                                                                  (int)sa[i], KK, (int)sb[j]);
+      constexpr int j = decltype(jc)::value;
+      const int r = wn * C::WTN + j * 32 + l32;
+      const uint8_t* row = st + C::B_OFF + r * C::RBB;
+      const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPB>(r, 2 * kk + h) * 16);
+      bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    });
+    unroll<C::FM>([&](auto ic) {
+      unroll<C::FN>([&](auto jc) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], C::AFP8 ? 0 : 4, 4, kk,
+                                                                    (int)sa[i], kk, (int)sb[j]);
+      });
     });
   });
 }
 
+// Wait until this wave's DMAs of the stage about to be consumed have landed,
+// given how many stages it issued after that one (DPS instructions each).
 template <class C>
-__device__ __forceinline__ void stage_compute(const uint8_t* la, const uint8_t* lb, const uint32_t (&sa)[C::FM],
-                                              const uint32_t (&sb)[C::FN], v16f (&acc)[C::FM][C::FN]) {
-  kstep<C, 0>(la, lb, sa, sb, acc);
-  if constexpr (C::KSTEPS > 1) kstep<C, 1>(la, lb, sa, sb, acc);
-  if constexpr (C::KSTEPS > 2) kstep<C, 2>(la, lb, sa, sb, acc);
-  if constexpr (C::KSTEPS > 3) kstep<C, 3>(la, lb, sa, sb, acc);
+__device__ __forceinline__ void wait_stage(int stages_after) {
+  if constexpr (C::STAGES >= 4) {
+    if (stages_after >= 2) { wait_vmcnt<2 * C::DPS>(); return; }
+  }
+  if constexpr (C::STAGES >= 3) {
+    if (stages_after >= 1) { wait_vmcnt<C::DPS>(); return; }
+  }
+  wait_vmcnt<0>();
 }
 
-// One output tile: acc += A_tile . B_tile^T over kc contraction elements.
-//   A rows [0, mrows) of A (row stride lda), scales AS (row stride ldas);
-//   B rows [0, nrows) likewise. Rows beyond mrows / nrows read the last valid
-//   row (their results are never stored). Contraction positions at or beyond
-//   kc read zeros (scale byte 127), so the tail adds nothing.
-//   Byte offsets inside a tile are 32-bit: the ABI bounds row strides so a
-//   tile's rows span less than 4 GiB.
-template <class C>
-__device__ __forceinline__ void tile_mainloop(const uint8_t* __restrict__ A, int64_t lda,
-                                              const uint8_t* __restrict__ AS, int64_t ldas, int mrows,
-                                              const uint8_t* __restrict__ B, int64_t ldb,
-                                              const uint8_t* __restrict__ BS, int64_t ldbs, int nrows, int kc,
-                                              uint8_t* lds_a, uint8_t* lds_b, v16f (&acc)[C::FM][C::FN]) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int l32 = lane & 31;
-  const int nstages = (kc + C::BK - 1) / C::BK;
-  if (nstages == 0) return;
-  const int kca = C::AFP8 ? kc : kc / 2;  // valid A bytes per row
-  const int kcb = kc / 2;                 // valid B bytes per row
-  const int nblk = kc / 32;               // valid scale blocks
-
-  LoopState<C> st;
-  {
-    const int ca = tid % C::CPA, ra0 = tid / C::CPA;
-    const int cb = tid % C::CPB, rb0 = tid / C::CPB;
-#pragma unroll
-    for (int i = 0; i < C::NLA; ++i) {
-      int r = ra0 + i * C::RSA;
-      r = r < mrows ? r : mrows - 1;
-      st.pa[i] = (uint32_t)(r * lda) + ca * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < C::NLB; ++i) {
-      int r = rb0 + i * C::RSB;
-      r = r < nrows ? r : nrows - 1;
-      st.pb[i] = (uint32_t)(r * ldb) + cb * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-      int r = wm * C::WTM + i * 32 + l32;
-      r = r < mrows ? r : mrows - 1;
-      st.psa[i] = (uint32_t)(r * ldas);
-    }
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      int r = wn * C::WTN + j * 32 + l32;
-      r = r < nrows ? r : nrows - 1;
-      st.psb[j] = (uint32_t)(r * ldbs);
-    }
-  }
-
-  stage_gload<C>(st, A, B, 0, kca, kcb);
-  stage_sload<C>(st.psa, AS, st.sa_raw, 0, nblk);
-  stage_sload<C>(st.psb, BS, st.sb_raw, 0, nblk);
-  stage_lstore<C>(st, lds_a, lds_b);
-  stage_spack<C>(st.sa_raw, st.sa_cur, 0, nblk);
-  stage_spack<C>(st.sb_raw, st.sb_cur, 0, nblk);
-  __syncthreads();
-  if (nstages > 1) {
-    stage_gload<C>(st, A, B, 1, kca, kcb);
-    stage_sload<C>(st.psa, AS, st.sa_raw, 1, nblk);
-    stage_sload<C>(st.psb, BS, st.sb_raw, 1, nblk);
-  }
-  for (int s = 0; s < nstages; ++s) {
-    const int buf = s & 1;
-    stage_compute<C>(lds_a + buf * C::LDS_A, lds_b + buf * C::LDS_B, st.sa_cur, st.sb_cur, acc);
-    if (s + 1 < nstages) {
-      stage_lstore<C>(st, lds_a + (buf ^ 1) * C::LDS_A, lds_b + (buf ^ 1) * C::LDS_B);
-      stage_spack<C>(st.sa_raw, st.sa_cur, s + 1, nblk);
-      stage_spack<C>(st.sb_raw, st.sb_cur, s + 1, nblk);
-    }
-    __syncthreads();
-    if (s + 2 < nstages) {
-      stage_gload<C>(st, A, B, s + 2, kca, kcb);
-      stage_sload<C>(st.psa, AS, st.sa_raw, s + 2, nblk);
-      stage_sload<C>(st.psb, BS, st.sb_raw, s + 2, nblk);
-    }
-  }
-}
-
-// Block index -> logical index so that the 32 workgroups resident on one XCD
-// (the hardware deals consecutive ids round-robin over the 8 XCDs) take
-// consecutive tile ids and share operands in that XCD's L2.
-__device__ __forceinline__ int xcd_logical_block() {
+// The pipelined persistent loop shared by all passes.
+//   src.count()       number of tiles
+//   src.ops(t)        TileOps of tile t
+//   src.epilogue(...) stores tile t
+// Tiles are visited t = first, first + gridDim.x, ...
+template <class C, class Src>
+__device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t lda, int64_t ldas, int64_t ldb,
+                                                int64_t ldbs) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / C::WN, wn = w % C::WN;
+  const int h = lane >> 5, l32 = lane & 31;
+  uint8_t* scratch = smem + C::EPI_OFF + w * C::EPI_BYTES;
+  const int total = src.count();
+  const int stride = gridDim.x;
   const int nb = gridDim.x, b = blockIdx.x;
-  return (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  // consecutive logical ids on one XCD (the hardware deals block ids
+  // round-robin over the 8 XCDs), so co-resident tiles share operands in L2
+  const int first = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+
+  // issuing side: the tile and stage whose DMAs go out next
+  int it = first, is = 0, ins = 0, slot_issue = 0;
+  TileOps iops{};
+  DmaPlan<C> plan;
+  auto load_issue_tile = [&]() {
+    while (it < total) {
+      iops = src.ops(it);
+      ins = (iops.kc + C::BK - 1) / C::BK;
+      if (ins > 0) break;
+      it += stride;  // tiles with an empty contraction issue nothing
+    }
+    if (it < total) plan_dma<C>(plan, iops, lda, ldas, ldb, ldbs, w, lane);
+  };
+  auto issue_one = [&]() -> int {
+    if (it >= total) return 0;
+    issue_stage<C>(plan, iops, is, smem + slot_issue * C::STAGE_BYTES, w);
+    slot_issue = slot_issue + 1 == C::STAGES ? 0 : slot_issue + 1;
+    if (++is == ins) {
+      is = 0;
+      it += stride;
+      load_issue_tile();
+    }
+    return 1;
+  };
+
+  load_issue_tile();
+  int ahead = 0;  // stages issued and not yet consumed
+  for (int q = 0; q < C::STAGES - 1; ++q) ahead += issue_one();
+
+  int slot_comp = 0;
+  for (int ct = first; ct < total; ct += stride) {
+    const TileOps cops = src.ops(ct);
+    const int cns = (cops.kc + C::BK - 1) / C::BK;
+    v16f acc[C::FM][C::FN];
+    unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
+    for (int s = 0; s < cns; ++s) {
+      wait_stage<C>(ahead - 1);
+      raw_barrier();
+      // the slot refilled now held the stage every wave consumed last step
+      ahead += issue_one();
+      compute_stage<C>(smem + slot_comp * C::STAGE_BYTES, acc, wm, wn, h, l32);
+      slot_comp = slot_comp + 1 == C::STAGES ? 0 : slot_comp + 1;
+      --ahead;
+    }
+    src.epilogue(ct, acc, scratch, w, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// epilogue: a 16-row half of one 32x32 fragment goes through the wave's
+// scratch (row pitch 33 floats), then each lane owns row l/4, columns
+// 8*(l%4) .. +8 of the half for 16-byte global accesses
+// ---------------------------------------------------------------------------
+template <int HF>
+__device__ __forceinline__ void frag_half_rows(const v16f& v, float* scr, int lane, float (&o)[8]) {
+  const int h = lane >> 5, l32 = lane & 31;
+  unroll<8>([&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    const int rr = 8 * (q / 4) + 4 * h + (q % 4);
+    scr[rr * 33 + l32] = v[HF * 8 + q];
+  });
+  const int rr = lane >> 2, cc = (lane & 3) * 8;
+  unroll<8>([&](auto ec) {
+    constexpr int e = decltype(ec)::value;
+    o[e] = scr[rr * 33 + cc + e];
+  });
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&o)[8]) {
+  uint4 pk;
+  pk.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+  pk.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+  pk.z = (uint32_t)f32_to_bf16_rne(o[4]) | ((uint32_t)f32_to_bf16_rne(o[5]) << 16);
+  pk.w = (uint32_t)f32_to_bf16_rne(o[6]) | ((uint32_t)f32_to_bf16_rne(o[7]) << 16);
+  return pk;
 }
 
 // ---------------------------------------------------------------------------
 // forward / input gradient
 // ---------------------------------------------------------------------------
 template <class C>
+struct RowsSource {
+  const RowsGemmParams& p;
+  const int64_t* pref;       // LDS: high = row offset, low = M-tile offset
+  const int32_t* tile_offs;  // LDS
+  int G, n_tiles, ntot;
+
+  __device__ __forceinline__ int count() const { return ntot; }
+
+  struct Pos { int g, mt, nt; };
+  __device__ __forceinline__ Pos pos(int t) const {
+    const int g = upper_bound_i32(tile_offs, G + 1, t) - 1;
+    const int local = t - tile_offs[g];
+    const int mt = local / n_tiles;
+    return Pos{g, mt, local - mt * n_tiles};
+  }
+  __device__ __forceinline__ TileOps ops(int t) const {
+    const Pos q = pos(t);
+    const int64_t row0 = (pref[q.g] >> 32) + (int64_t)q.mt * C::BM;
+    const int mleft = p.sp.m[q.g] - q.mt * C::BM;
+    const int col0 = q.nt * C::BN;
+    const int nleft = p.n_out - col0;
+    TileOps o;
+    o.a = p.a + row0 * p.lda;
+    o.as = p.as + row0 * p.ldas;
+    o.b = p.b + (int64_t)q.g * p.b_gstride + (int64_t)col0 * p.ldb;
+    o.bs = p.bs + (int64_t)q.g * p.bs_gstride + (int64_t)col0 * p.ldbs;
+    o.mrows = mleft < C::BM ? mleft : C::BM;
+    o.nrows = nleft < C::BN ? nleft : C::BN;
+    o.kc = p.kc;
+    return o;
+  }
+  __device__ __forceinline__ void epilogue(int t, v16f (&acc)[C::FM][C::FN], uint8_t* scratch, int w, int lane) {
+    const Pos q = pos(t);
+    const int64_t row0 = (pref[q.g] >> 32) + (int64_t)q.mt * C::BM;
+    const int mleft = p.sp.m[q.g] - q.mt * C::BM;
+    const int col0 = q.nt * C::BN;
+    const int ncols = p.n_out - col0;
+    const int wm = w / C::WN, wn = w % C::WN;
+    float* scr = reinterpret_cast<float*>(scratch);
+    const int rr = lane >> 2, cc = (lane & 3) * 8;
+    unroll<C::FM>([&](auto ic) {
+      unroll<C::FN>([&](auto jc) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        unroll<2>([&](auto hc) {
+          constexpr int hf = decltype(hc)::value;
+          float o[8];
+          frag_half_rows<hf>(acc[i][j], scr, lane, o);
+          const int row = wm * C::WTM + i * 32 + 16 * hf + rr;
+          const int col = wn * C::WTN + j * 32 + cc;
+          if (row < mleft && col < ncols)
+            *reinterpret_cast<uint4*>(p.c + (row0 + row) * p.ldc + col0 + col) = pack_bf16x8(o);
+        });
+      });
+    });
+  }
+};
+
+template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void grouped_rows_kernel(const RowsGemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * C::LDS_A];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2 * C::LDS_B];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int64_t pref[kMaxExperts + 1];
   __shared__ int64_t wtot[C::THREADS / 64];
   __shared__ int32_t tile_offs[kMaxExperts + 1];
 
   const int G = p.sp.G;
   const int n_tiles = (p.n_out + C::BN - 1) / C::BN;
-  // packed prefix: high half = row offset, low half = M-tile offset
   block_prefix64<C::THREADS>(G, [&](int g) {
     const int64_t m = p.sp.m[g];
     return (m << 32) | ((m + C::BM - 1) / C::BM);
   }, pref, wtot);
   for (int g = threadIdx.x; g <= G; g += C::THREADS) tile_offs[g] = (int32_t)(pref[g] & 0xffffffffll) * n_tiles;
   __syncthreads();
-  const int total = tile_offs[G];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int h = lane >> 5, l32 = lane & 31;
-
-  for (int t = xcd_logical_block(); t < total; t += gridDim.x) {
-    const int g = upper_bound_i32(tile_offs, G + 1, t) - 1;
-    const int local = t - tile_offs[g];
-    const int mt = local / n_tiles, nt = local - mt * n_tiles;
-    const int64_t row0 = (pref[g] >> 32) + (int64_t)mt * C::BM;
-    const int mleft = p.sp.m[g] - mt * C::BM;
-    const int mrows = mleft < C::BM ? mleft : C::BM;
-    const int col0 = nt * C::BN;
-    const int nleft = p.n_out - col0;
-    const int ncols = nleft < C::BN ? nleft : C::BN;
-
-    v16f acc[C::FM][C::FN];
-    unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
-
-    tile_mainloop<C>(p.a + row0 * p.lda, p.lda, p.as + row0 * p.ldas, p.ldas, mrows,
-                     p.b + (int64_t)g * p.b_gstride + (int64_t)col0 * p.ldb, p.ldb,
-                     p.bs + (int64_t)g * p.bs_gstride + (int64_t)col0 * p.ldbs, p.ldbs, ncols, p.kc, lds_a, lds_b,
-                     acc);
-
-    uint16_t* cbase = p.c + row0 * p.ldc + col0;
-    unroll<C::FM>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      unroll<C::FN>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        const int c = wn * C::WTN + j * 32 + l32;
-        const v16f v = acc[i][j];
-        unroll<16>([&](auto rc) {
-          constexpr int r = decltype(rc)::value;
-          const int row = wm * C::WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (row < mrows && c < ncols) cbase[(int64_t)row * p.ldc + c] = f32_to_bf16_rne(v[r]);
-        });
-      });
-    });
-  }
+  RowsSource<C> src{p, pref, tile_offs, G, n_tiles, tile_offs[G]};
+  persistent_loop<C>(src, smem, p.lda, p.ldas, p.ldb, p.ldbs);
 }
 
 // ---------------------------------------------------------------------------
 // variable-K weight gradient
 // ---------------------------------------------------------------------------
 template <class C>
+struct WgradSource {
+  const WgradParams& p;
+  const int64_t* pad_pref;   // LDS: padded segment offsets (natural expert order)
+  const int32_t* tile_offs;  // LDS: tile offsets in longest-first order
+  int G, tc, ntot;
+
+  __device__ __forceinline__ int count() const { return ntot; }
+
+  struct Pos { int g, row0, col0; int64_t p0; int kc; };
+  __device__ __forceinline__ Pos pos(int t) const {
+    const int j = upper_bound_i32(tile_offs, G + 1, t) - 1;
+    const int g = p.order[j];
+    const int local = t - tile_offs[j];
+    const int rt = local / tc;
+    const int64_t p0 = pad_pref[g];
+    return Pos{g, rt * C::BM, (local - rt * tc) * C::BN, p0, (int)(pad_pref[g + 1] - p0)};
+  }
+  __device__ __forceinline__ TileOps ops(int t) const {
+    const Pos q = pos(t);
+    TileOps o;
+    o.a = p.a + (int64_t)q.row0 * p.lda + q.p0 / 2;
+    o.as = p.as + (int64_t)q.row0 * p.ldas + q.p0 / 32;
+    o.b = p.b + (int64_t)q.col0 * p.ldb + q.p0 / 2;
+    o.bs = p.bs + (int64_t)q.col0 * p.ldbs + q.p0 / 32;
+    const int rl = p.n_rows - q.row0, cl = p.n_cols - q.col0;
+    o.mrows = rl < C::BM ? rl : C::BM;
+    o.nrows = cl < C::BN ? cl : C::BN;
+    o.kc = q.kc;
+    return o;
+  }
+  __device__ __forceinline__ void epilogue(int t, v16f (&acc)[C::FM][C::FN], uint8_t* scratch, int w, int lane) {
+    const Pos q = pos(t);
+    const int rl = p.n_rows - q.row0, cl = p.n_cols - q.col0;
+    const int wm = w / C::WN, wn = w % C::WN;
+    float* scr = reinterpret_cast<float*>(scratch);
+    const int rr = lane >> 2, cc = (lane & 3) * 8;
+    const int64_t obase = ((int64_t)q.g * p.n_rows + q.row0) * p.n_cols + q.col0;
+    unroll<C::FM>([&](auto ic) {
+      unroll<C::FN>([&](auto jc) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        unroll<2>([&](auto hc) {
+          constexpr int hf = decltype(hc)::value;
+          float o[8];
+          frag_half_rows<hf>(acc[i][j], scr, lane, o);
+          const int row = wm * C::WTM + i * 32 + 16 * hf + rr;
+          const int col = wn * C::WTN + j * 32 + cc;
+          if (row < rl && col < cl) {
+            const int64_t idx = obase + (int64_t)row * p.n_cols + col;
+            if (p.out_bf16) {
+              uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.c) + idx);
+              if (p.accumulate) {
+                const uint4 old = *dst;
+                const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
+                unroll<4>([&](auto ec) {
+                  constexpr int e = decltype(ec)::value;
+                  o[2 * e] += __uint_as_float(ow[e] << 16);
+                  o[2 * e + 1] += __uint_as_float(ow[e] & 0xffff0000u);
+                });
+              }
+              *dst = pack_bf16x8(o);
+            } else {
+              float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.c) + idx);
+              if (p.accumulate) {
+                const float4 a0 = dst[0], a1 = dst[1];
+                o[0] += a0.x; o[1] += a0.y; o[2] += a0.z; o[3] += a0.w;
+                o[4] += a1.x; o[5] += a1.y; o[6] += a1.z; o[7] += a1.w;
+              }
+              dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+              dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+            }
+          }
+        });
+      });
+    });
+  }
+};
+
+template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void grouped_wgrad_kernel(const WgradParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * C::LDS_A];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2 * C::LDS_B];
-  __shared__ int64_t pad_pref[kMaxExperts + 1];   // natural expert order: padded offsets
-  __shared__ int64_t tile_pref[kMaxExperts + 1];  // longest-first order: tile offsets
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int64_t pad_pref[kMaxExperts + 1];
+  __shared__ int64_t tile_pref[kMaxExperts + 1];
   __shared__ int64_t wtot[C::THREADS / 64];
   __shared__ int32_t tile_offs[kMaxExperts + 1];
 
@@ -371,72 +556,31 @@ __global__ __launch_bounds__(C::THREADS, 1) void grouped_wgrad_kernel(const Wgra
   }, tile_pref, wtot);
   for (int j = threadIdx.x; j <= G; j += C::THREADS) tile_offs[j] = (int32_t)tile_pref[j];
   __syncthreads();
-  const int total = tile_offs[G];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int h = lane >> 5, l32 = lane & 31;
-  constexpr int ABYTE_NUM = C::AFP8 ? 1 : 1, ABYTE_DEN = C::AFP8 ? 1 : 2;
-
-  for (int t = xcd_logical_block(); t < total; t += gridDim.x) {
-    const int j = upper_bound_i32(tile_offs, G + 1, t) - 1;
-    const int g = p.order[j];
-    const int local = t - tile_offs[j];
-    const int rt = local / tc, ct = local - rt * tc;
-    const int row0 = rt * C::BM, col0 = ct * C::BN;
-    const int rleft = p.n_rows - row0, cleft = p.n_cols - col0;
-    const int mrows = rleft < C::BM ? rleft : C::BM;
-    const int ncols = cleft < C::BN ? cleft : C::BN;
-    const int64_t p0 = pad_pref[g];                 // segment start (padded)
-    const int kc = (int)(pad_pref[g + 1] - p0);    // padded segment length
-
-    v16f acc[C::FM][C::FN];
-    unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
-
-    tile_mainloop<C>(p.a + (int64_t)row0 * p.lda + p0 * ABYTE_NUM / ABYTE_DEN, p.lda,
-                     p.as + (int64_t)row0 * p.ldas + p0 / 32, p.ldas, mrows,
-                     p.b + (int64_t)col0 * p.ldb + p0 / 2, p.ldb, p.bs + (int64_t)col0 * p.ldbs + p0 / 32, p.ldbs,
-                     ncols, kc, lds_a, lds_b, acc);
-
-    const int64_t obase = ((int64_t)g * p.n_rows + row0) * p.n_cols + col0;
-    unroll<C::FM>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      unroll<C::FN>([&](auto jc) {
-        constexpr int jj = decltype(jc)::value;
-        const int c = wn * C::WTN + jj * 32 + l32;
-        const v16f v = acc[i][jj];
-        unroll<16>([&](auto rc) {
-          constexpr int r = decltype(rc)::value;
-          const int row = wm * C::WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (row < mrows && c < ncols) {
-            const int64_t idx = obase + (int64_t)row * p.n_cols + c;
-            if (p.out_bf16) {
-              uint16_t* o = reinterpret_cast<uint16_t*>(p.c) + idx;
-              float x = v[r];
-              if (p.accumulate) x += __uint_as_float((uint32_t)(*o) << 16);
-              *o = f32_to_bf16_rne(x);
-            } else {
-              float* o = reinterpret_cast<float*>(p.c) + idx;
-              *o = p.accumulate ? *o + v[r] : v[r];
-            }
-          }
-        });
-      });
-    });
-  }
+  WgradSource<C> src{p, pad_pref, tile_offs, G, tc, tile_offs[G]};
+  persistent_loop<C>(src, smem, p.lda, p.ldas, p.ldb, p.ldbs);
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-using CfgFwd4 = TileCfg<256, 256, 2, 2, 128, false>;   // a4w4
-using CfgFwd8 = TileCfg<256, 256, 2, 2, 128, true>;    // a8w4
+using CfgA4 = TileCfg<256, 256, 2, 4, 128, 3, false>;   // a4w4: fwd, dgrad, wgrad
+using CfgA8 = TileCfg<256, 256, 2, 4, 64, 4, true>;     // a8w4 forward
 
-static int grid_for(int64_t tiles, int num_cus) {
-  int64_t g = num_cus;
-  if (tiles < g) g = tiles;
-  if (g < 1) g = 1;
-  return (int)g;
+template <class C, class K, class P>
+static hipError_t launch_persistent(K kernel, const P& p, int64_t tiles, int num_cus, hipStream_t st) {
+  static bool attr_set = false;  // raise the dynamic LDS limit once per kernel
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       C::SMEM_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int64_t grid = num_cus;
+  if (tiles < grid) grid = tiles;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::THREADS), C::SMEM_BYTES, st, p);
+  return hipGetLastError();
 }
 
 static int64_t rows_tiles(const RowsGemmParams& p, int BM, int BN) {
@@ -446,25 +590,19 @@ static int64_t rows_tiles(const RowsGemmParams& p, int BM, int BN) {
 }
 
 hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, int num_cus, hipStream_t st) {
-  if (a_fp8) {
-    const int grid = grid_for(rows_tiles(p, CfgFwd8::BM, CfgFwd8::BN), num_cus);
-    hipLaunchKernelGGL(grouped_rows_kernel<CfgFwd8>, dim3(grid), dim3(CfgFwd8::THREADS), 0, st, p);
-  } else {
-    const int grid = grid_for(rows_tiles(p, CfgFwd4::BM, CfgFwd4::BN), num_cus);
-    hipLaunchKernelGGL(grouped_rows_kernel<CfgFwd4>, dim3(grid), dim3(CfgFwd4::THREADS), 0, st, p);
-  }
-  return hipGetLastError();
+  if (a_fp8)
+    return launch_persistent<CfgA8>(grouped_rows_kernel<CfgA8>, p, rows_tiles(p, CfgA8::BM, CfgA8::BN), num_cus,
+                                    st);
+  return launch_persistent<CfgA4>(grouped_rows_kernel<CfgA4>, p, rows_tiles(p, CfgA4::BM, CfgA4::BN), num_cus, st);
 }
 
 hipError_t launch_grouped_wgrad_mx(const WgradParams& p, int num_cus, hipStream_t st) {
-  using C = CfgFwd4;
+  using C = CfgA4;
   int64_t tiles = 0;
   const int64_t per = (int64_t)((p.n_rows + C::BM - 1) / C::BM) * ((p.n_cols + C::BN - 1) / C::BN);
   for (int g = 0; g < p.sp.G; ++g) tiles += (p.sp.m[g] > 0 || !p.accumulate) ? per : 0;
   if (tiles == 0) return hipSuccess;
-  const int grid = grid_for(tiles, num_cus);
-  hipLaunchKernelGGL(grouped_wgrad_kernel<C>, dim3(grid), dim3(C::THREADS), 0, st, p);
-  return hipGetLastError();
+  return launch_persistent<C>(grouped_wgrad_kernel<C>, p, tiles, num_cus, st);
 }
 
 }  // namespace mxgg
