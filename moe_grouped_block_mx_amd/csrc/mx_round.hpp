@@ -1,4 +1,4 @@
-// MX element encoding on bf16 bit patterns, in integer arithmetic.
+// MX shared exponent and the operands of the hardware element conversion.
 //
 // The MX rule (OCP Microscaling v1.0; the tiny-scale clamp from the review
 // thread on the page "route te.GroupedLinear through #723; a8w4 fwd-only"):
@@ -6,11 +6,11 @@
 // an all-zero block; element code = round-to-nearest-even of |x| * 2^-e onto
 // the element grid, saturated at the largest finite magnitude; sign copied.
 //
-// Everything below works on integers, so the result does not depend on the
-// floating-point modes of the hardware (denormal flushing, conversion
-// rounding): a bf16 magnitude is sig * 2^ex with an integer significand, the
-// scaled value's binade L gives the grid quantum 2^Q, and the code is the
-// rounded multiple of that quantum laid out as (binade, mantissa) bits.
+// The shared exponent is computed exactly from the bf16 bits of amax. The
+// elements are encoded by gfx950's v_cvt_scalef32_pk_{fp4,fp8}_bf16, which were
+// checked against the rule on every finite bf16 pattern at every shared
+// exponent: E2M1 matches exactly; E4M3 matches except that scaled magnitudes
+// >= 464 become NaN instead of 448, which the clamp below removes.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -37,37 +37,26 @@ __host__ __device__ __forceinline__ int mx_shared_exp(uint32_t amax_mag) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// Magnitude code (no sign) of the bf16 magnitude `mag` scaled by 2^-e.
-template <class F>
-__host__ __device__ __forceinline__ uint32_t mx_encode_mag(uint32_t mag, int e) {
-  if (mag == 0) return 0;
-  const uint32_t E = mag >> 7;
-  const int sig = E ? (int)(0x80u | (mag & 0x7fu)) : (int)(mag & 0x7fu);
-  const int ex = E ? (int)E - 134 : -133;          // |x| = sig * 2^ex
-  const int L = (31 - __builtin_clz((uint32_t)sig)) + ex - e;         // floor(log2(|x| 2^-e))
-  const int Q = (L > F::EMIN ? L : F::EMIN) - F::MB;  // grid quantum exponent
-  const int sh = ex - e - Q;                        // n = sig * 2^sh
-  uint32_t n;
-  if (sh >= 0) {
-    n = (uint32_t)sig << sh;                        // exact (small values only)
-  } else {
-    int r = -sh;
-    r = r > 31 ? 31 : r;
-    const uint32_t us = (uint32_t)sig;
-    const uint32_t q = us >> r;
-    const uint32_t rem = us & ((1u << r) - 1u);
-    const uint32_t half = 1u << (r - 1);
-    n = q + ((rem > half) | ((rem == half) & (q & 1u)));
-  }
-  // grid position -> code: binade index above the subnormal binade, plus n
-  uint32_t code = ((uint32_t)(Q - (F::EMIN - F::MB)) << F::MB) + n;
-  return code > (uint32_t)F::MAXC ? (uint32_t)F::MAXC : code;
+// fp32 operand of the gfx950 scaled conversions: the UE8M0 scale 2^e carried
+// in the exponent field (e = -127 is exponent field 0, which the conversion
+// reads as 2^-127, not as a flushed denormal).
+__host__ __device__ __forceinline__ uint32_t mx_scale_operand_bits(int e) { return (uint32_t)(e + 127) << 23; }
+
+// bf16 bits of 448 * 2^e, the largest E4M3 magnitude at shared exponent e.
+// The hardware E4M3 conversion rounds magnitudes at or above 464 (after
+// scaling) to NaN instead of saturating, so inputs are first clamped to this
+// value; below it round-to-nearest-even already gives 448, so the clamp only
+// implements saturation. For e > 119 the bound exceeds every finite bf16.
+__host__ __device__ __forceinline__ uint32_t e4m3_sat_limit_bits(int e) {
+  return e > 119 ? 0x7f7fu : ((uint32_t)(e + 135) << 7) | 0x60u;
 }
 
-template <class F>
-__host__ __device__ __forceinline__ uint32_t mx_encode(uint32_t bits, int e) {
-  const uint32_t sign = (bits & 0x8000u) ? (uint32_t)F::SIGN : 0u;
-  return sign | mx_encode_mag<F>(bits & 0x7fffu, e);
+// Clamp both bf16 magnitudes of a packed pair to `limit` (sign kept).
+__host__ __device__ __forceinline__ uint32_t clamp_bf16x2_mag(uint32_t w, uint32_t limit) {
+  uint32_t lo = w & 0x7fffu, hi = (w >> 16) & 0x7fffu;
+  lo = lo < limit ? lo : limit;
+  hi = hi < limit ? hi : limit;
+  return (w & 0x80008000u) | lo | (hi << 16);
 }
 
 }  // namespace mxgg
