@@ -162,7 +162,7 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
  *             (FP8_1x128, FP8_128x128) blockwise FP8.
  *   m_splits  host int64 [G]; sum == M.
  *   M, N, K   K % 32 == 0 and N % 32 == 0 (MX); K % 128 == 0 and N % 128 == 0
- *             (blockwise); M < 2^31.
+ *             (blockwise); M < 2^31; N, K < 2^23.
  *   out       bf16 [M, N] (dense), written with round-to-nearest-even.
  *   ws        workspace of at least mxgg_workspace_size(G) bytes (may be NULL
  *             when that is 0).
@@ -182,7 +182,7 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
  *                  u8 [K, G*N/32] (expert g owns columns [g*N, (g+1)*N)).
  *   fmt            MXGG_MXFP4 (the only dgrad format).
  *   dx             bf16 [M, K].
- * Shape rules as for the forward. Errors as for the forward.
+ * Shape rules as for the forward, and G*N/2 < 2^23. Errors as for the forward.
  */
 mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* wcol_q,
                                const void* wcol_s, mxgg_format fmt, const int64_t* m_splits,
@@ -202,7 +202,8 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
  *               left untouched); 0: main_grad[g] = dW_g (experts with no
  *               tokens are zero-filled). Every element is read/written by
  *               exactly one thread, so in-place accumulation is race-free.
- * Shape rules: N % 32 == 0 and K % 32 == 0 (MX), % 128 (blockwise).
+ * Shape rules: N % 32 == 0 and K % 32 == 0 (MX), % 128 (blockwise); N, K and
+ * mpad < 2^23.
  * Errors: NULL, SHAPE, SPLITS, FORMAT, ALIGN, WORKSPACE, DEVICE, ARCH, HIP.
  */
 mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const void* xcol_q,

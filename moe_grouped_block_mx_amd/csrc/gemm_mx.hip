@@ -105,7 +105,7 @@ struct TileCfg {
   static constexpr int DA = A_BYTES / (NW * 1024), DB = B_BYTES / (NW * 1024);
   static constexpr int DSA = AS_BYTES / (NW * 256), DSB = BS_BYTES / (NW * 256);
   static constexpr int DPS = DA + DB + DSA + DSB;
-  static constexpr int EPI_BYTES = 16 * 33 * 4;  // per-wave epilogue scratch (16 rows x 32 fp32, padded)
+  static constexpr int EPI_BYTES = 16 * 36 * 4;  // per-wave epilogue scratch (16 rows x 32 fp32, padded)
   static constexpr int EPI_OFF = STAGES * STAGE_BYTES;
   static constexpr int SMEM_BYTES = EPI_OFF + NW * EPI_BYTES;
   static_assert(A_BYTES % (NW * 1024) == 0 && B_BYTES % (NW * 1024) == 0, "chunk DMA split");
@@ -350,31 +350,36 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
 
 // ---------------------------------------------------------------------------
 // epilogue: a 16-row half of one 32x32 fragment goes through the wave's
-// scratch (row pitch 33 floats), then each lane owns row l/4, columns
-// 8*(l%4) .. +8 of the half for 16-byte global accesses
+// scratch (row pitch 36 floats: 16-byte aligned rows, lane halves 16 banks
+// apart), then each lane owns row l/4, columns 8*(l%4) .. +8 of the half for
+// 16-byte global accesses
 // ---------------------------------------------------------------------------
+constexpr int kEpiPitch = 36;
+
 template <int HF>
 __device__ __forceinline__ void frag_half_rows(const v16f& v, float* scr, int lane, float (&o)[8]) {
   const int h = lane >> 5, l32 = lane & 31;
   unroll<8>([&](auto qc) {
     constexpr int q = decltype(qc)::value;
     const int rr = 8 * (q / 4) + 4 * h + (q % 4);
-    scr[rr * 33 + l32] = v[HF * 8 + q];
+    scr[rr * kEpiPitch + l32] = v[HF * 8 + q];
   });
   const int rr = lane >> 2, cc = (lane & 3) * 8;
-  unroll<8>([&](auto ec) {
-    constexpr int e = decltype(ec)::value;
-    o[e] = scr[rr * 33 + cc + e];
-  });
+  const v4f lo = *reinterpret_cast<const v4f*>(scr + rr * kEpiPitch + cc);
+  const v4f hi = *reinterpret_cast<const v4f*>(scr + rr * kEpiPitch + cc + 4);
+  o[0] = lo[0]; o[1] = lo[1]; o[2] = lo[2]; o[3] = lo[3];
+  o[4] = hi[0]; o[5] = hi[1]; o[6] = hi[2]; o[7] = hi[3];
 }
 
+typedef __bf16 v2bf16_t __attribute__((ext_vector_type(2)));
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32), 8 values -> 16 bytes
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_t{a, b}), v2bf16_t));
+}
 __device__ __forceinline__ uint4 pack_bf16x8(const float (&o)[8]) {
-  uint4 pk;
-  pk.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-  pk.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-  pk.z = (uint32_t)f32_to_bf16_rne(o[4]) | ((uint32_t)f32_to_bf16_rne(o[5]) << 16);
-  pk.w = (uint32_t)f32_to_bf16_rne(o[6]) | ((uint32_t)f32_to_bf16_rne(o[7]) << 16);
-  return pk;
+  return make_uint4(cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]), cvt_bf16x2(o[6], o[7]));
 }
 
 // ---------------------------------------------------------------------------
@@ -492,43 +497,60 @@ struct WgradSource {
     o.kc = q.kc;
     return o;
   }
-  __device__ __forceinline__ void epilogue(int t, v16f (&acc)[C::FM][C::FN], uint8_t* scratch, int w, int lane) {
-    const Pos q = pos(t);
+  // Per 32-row fragment row i, the old values of all its columns are loaded
+  // first (FN x 2 half fragments, 32 or 16 bytes per lane each), so a wave has
+  // that many read-modify-write loads in flight instead of one. The loads are
+  // unconditional from clamped (valid) addresses and masked afterwards, which
+  // keeps them in one straight-line group.
+  template <bool BF16, bool ACC>
+  __device__ __forceinline__ void store_tile(const Pos& q, v16f (&acc)[C::FM][C::FN], float* scr, int w, int lane) {
     const int rl = p.n_rows - q.row0, cl = p.n_cols - q.col0;
     const int wm = w / C::WN, wn = w % C::WN;
-    float* scr = reinterpret_cast<float*>(scratch);
     const int rr = lane >> 2, cc = (lane & 3) * 8;
     const int64_t obase = ((int64_t)q.g * p.n_rows + q.row0) * p.n_cols + q.col0;
     unroll<C::FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      float old[C::FN][2][8];
+      if constexpr (ACC) {
+        unroll<C::FN>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          unroll<2>([&](auto hc) {
+            constexpr int hf = decltype(hc)::value;
+            const int row = wm * C::WTM + i * 32 + 16 * hf + rr;
+            const int col = wn * C::WTN + j * 32 + cc;
+            const int64_t idx = obase + (int64_t)(row < rl ? row : rl - 1) * p.n_cols + (col < cl ? col : cl - 8);
+            if constexpr (BF16) {
+              const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.c) + idx);
+              const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+              unroll<4>([&](auto ec) {
+                constexpr int e = decltype(ec)::value;
+                old[j][hf][2 * e] = __uint_as_float(vw[e] << 16);
+                old[j][hf][2 * e + 1] = __uint_as_float(vw[e] & 0xffff0000u);
+              });
+            } else {
+              const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.c) + idx);
+              const float4 x0 = src[0], x1 = src[1];
+              old[j][hf][0] = x0.x; old[j][hf][1] = x0.y; old[j][hf][2] = x0.z; old[j][hf][3] = x0.w;
+              old[j][hf][4] = x1.x; old[j][hf][5] = x1.y; old[j][hf][6] = x1.z; old[j][hf][7] = x1.w;
+            }
+          });
+        });
+      }
       unroll<C::FN>([&](auto jc) {
-        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        constexpr int j = decltype(jc)::value;
         unroll<2>([&](auto hc) {
           constexpr int hf = decltype(hc)::value;
           float o[8];
           frag_half_rows<hf>(acc[i][j], scr, lane, o);
           const int row = wm * C::WTM + i * 32 + 16 * hf + rr;
           const int col = wn * C::WTN + j * 32 + cc;
+          if constexpr (ACC) unroll<8>([&](auto ec) { o[decltype(ec)::value] += old[j][hf][decltype(ec)::value]; });
           if (row < rl && col < cl) {
             const int64_t idx = obase + (int64_t)row * p.n_cols + col;
-            if (p.out_bf16) {
-              uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.c) + idx);
-              if (p.accumulate) {
-                const uint4 old = *dst;
-                const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
-                unroll<4>([&](auto ec) {
-                  constexpr int e = decltype(ec)::value;
-                  o[2 * e] += __uint_as_float(ow[e] << 16);
-                  o[2 * e + 1] += __uint_as_float(ow[e] & 0xffff0000u);
-                });
-              }
-              *dst = pack_bf16x8(o);
+            if constexpr (BF16) {
+              *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.c) + idx) = pack_bf16x8(o);
             } else {
               float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.c) + idx);
-              if (p.accumulate) {
-                const float4 a0 = dst[0], a1 = dst[1];
-                o[0] += a0.x; o[1] += a0.y; o[2] += a0.z; o[3] += a0.w;
-                o[4] += a1.x; o[5] += a1.y; o[6] += a1.z; o[7] += a1.w;
-              }
               dst[0] = make_float4(o[0], o[1], o[2], o[3]);
               dst[1] = make_float4(o[4], o[5], o[6], o[7]);
             }
@@ -536,6 +558,17 @@ struct WgradSource {
         });
       });
     });
+  }
+  __device__ __forceinline__ void epilogue(int t, v16f (&acc)[C::FM][C::FN], uint8_t* scratch, int w, int lane) {
+    const Pos q = pos(t);
+    float* scr = reinterpret_cast<float*>(scratch);
+    if (p.out_bf16) {
+      if (p.accumulate) store_tile<true, true>(q, acc, scr, w, lane);
+      else store_tile<true, false>(q, acc, scr, w, lane);
+    } else {
+      if (p.accumulate) store_tile<false, true>(q, acc, scr, w, lane);
+      else store_tile<false, false>(q, acc, scr, w, lane);
+    }
   }
 };
 

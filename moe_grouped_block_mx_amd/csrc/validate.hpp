@@ -127,11 +127,15 @@ inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols
   return Check{};
 }
 
+// The GEMM kernels address a 256-row tile with 32-bit byte offsets, so every
+// operand row stride is kept below 2^23 bytes (tile span < 2^31).
+constexpr int64_t kMaxRowStride = (int64_t)1 << 23;
+
 inline Check validate_gemm_dims(int64_t M, int64_t N, int64_t K, int blk) {
   if (M < 0 || N <= 0 || K <= 0) return fail(MXGG_ERR_SHAPE, "M=%lld N=%lld K=%lld", M, N, K);
   if (N % blk || K % blk) return fail(MXGG_ERR_SHAPE, "N=%lld and K=%lld must be multiples of %lld", N, K, blk);
-  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 30))
-    return fail(MXGG_ERR_SHAPE, "M=%lld N=%lld K=%lld too large", M, N, K);
+  if (M >= ((int64_t)1 << 31) || N >= kMaxRowStride || K >= kMaxRowStride)
+    return fail(MXGG_ERR_SHAPE, "M=%lld N=%lld K=%lld too large (N, K < 2^23)", M, N, K);
   return Check{};
 }
 
@@ -165,7 +169,8 @@ inline Check validate_dgrad(const void* dy_q, const void* dy_s, const void* wc_q
   if (fmt != MXGG_MXFP4) return fail(MXGG_ERR_FORMAT, "dgrad supports MXGG_MXFP4 only (got %lld)", fmt);
   MXGG_TRY(validate_gemm_dims(M, N, K, 32));
   MXGG_TRY(check_splits(m, G, M, "dY"));
-  if ((int64_t)G * N >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SHAPE, "G*N=%lld too large", (int64_t)G * N);
+  if ((int64_t)G * N / 2 >= kMaxRowStride)
+    return fail(MXGG_ERR_SHAPE, "G*N=%lld too large (G*N/2 < 2^23)", (int64_t)G * N);
   if (ws_bytes < ws_need) return fail(MXGG_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes,
                                       (long long)ws_need);
   if (ws_need) MXGG_TRY(check_ptr(ws, true, "ws"));
@@ -191,7 +196,7 @@ inline Check validate_wgrad(const void* dy_q, const void* dy_s, const void* x_q,
   const int blk = f == MXGG_FP8_1x128 ? 128 : 32;
   if (N <= 0 || K <= 0 || N % blk || K % blk)
     return fail(MXGG_ERR_SHAPE, "N=%lld and K=%lld must be positive multiples of %lld", N, K, blk);
-  if (N >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 30)) return fail(MXGG_ERR_SHAPE, "N or K too large");
+  if (N >= kMaxRowStride || K >= kMaxRowStride) return fail(MXGG_ERR_SHAPE, "N or K too large (< 2^23)");
   if (G < 1 || G > MXGG_MAX_EXPERTS) return fail(MXGG_ERR_SHAPE, "G=%lld outside [1, 512]", G);
   if (!m) return fail(MXGG_ERR_NULL, "m_splits is NULL");
   int64_t rows = 0;
@@ -202,6 +207,7 @@ inline Check validate_wgrad(const void* dy_q, const void* dy_s, const void* x_q,
   if (rows >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SPLITS, "sum(m_splits)=%lld >= 2^31", rows);
   const int64_t need = segpad_rows(m, G, segpad_multiple(f));
   if (mpad != need) return fail(MXGG_ERR_SHAPE, "mpad=%lld but the padded row count is %lld", mpad, need);
+  if (mpad >= kMaxRowStride) return fail(MXGG_ERR_SHAPE, "mpad=%lld too large (< 2^23)", mpad);
   if (ws_bytes < ws_need) return fail(MXGG_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes,
                                       (long long)ws_need);
   if (ws_need) MXGG_TRY(check_ptr(ws, true, "ws"));

@@ -64,6 +64,9 @@ def test_fwd_shapes_formats_pointers():
     assert fwd(m, 3, 8, out=NULL) == 1
     # blockwise pair needs multiples of 128
     assert fwd(m, 3, 8, N=64, K=128, a_fmt=2, w_fmt=3) == 2
+    # row strides of the tiles stay below 2^23 bytes
+    assert fwd(m, 3, 8, K=1 << 23) == 2 and "2^23" in last()
+    assert L.mxgg_grouped_dgrad(P, P, P, P, 0, splits(2, 2, 2, 2), 4, 8, 1 << 22, 64, P, NULL, 0, NULL) == 2
 
 
 def test_empty_batch_validated_then_ok_without_gpu():
