@@ -22,11 +22,21 @@ cpu_baseline: the CPU oracle (NumPy fp64) timed on a bounded sample of the
 same step -- one expert with 8192 tokens at the full K and N, all three
 passes including quantization -- on this host's cores.
 
+roofline.traffic: HBM bytes per launch of the dominant kernel, read from the
+committed rocprofv3 summary profiles/<kernel>_fc1_traffic.txt (FETCH_SIZE and
+WRITE_SIZE per dispatch, each scaled by the same counter's reading for a plain
+1 GiB copy); null when that summary was taken from a different kernel source.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-only            (calibration copy for --pmc runs)
+       python bench.py --summarize KERNEL STATS_CSV FETCH_CSV WRITE_CSV
+                       COPY_FETCH_CSV COPY_WRITE_CSV   (writes the summary text)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -50,7 +60,123 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--passes", default="all", help="profiling aid: fwd, dgrad, wgrad or all")
+    ap.add_argument("--copy-only", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize", nargs=6, metavar=("KERNEL", "STATS", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="print the profile summary of KERNEL from rocprofv3 csv outputs")
     return ap.parse_args()
+
+
+# --- profile summaries --------------------------------------------------------
+CSRC = os.path.join(ROOT, "moe_grouped_block_mx_amd", "csrc")
+KERNEL_SOURCES = {  # bench kernel name -> (profiled kernel name prefix, source files)
+    "fwd": ("void mxgg::grouped_rows_kernel", ["gemm_mx.hip", "device_common.hpp", "launch.hpp"]),
+    "dgrad": ("void mxgg::grouped_rows_kernel", ["gemm_mx.hip", "device_common.hpp", "launch.hpp"]),
+    "wgrad": ("void mxgg::grouped_wgrad_kernel", ["gemm_mx.hip", "device_common.hpp", "launch.hpp"]),
+}
+COPY_BYTES = 1 << 30
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel][1]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_summary_path(kernel):
+    return os.path.join(ROOT, "profiles", f"{kernel}_fc1_traffic.txt")
+
+
+def read_traffic(kernel):
+    """(fetch, write) HBM bytes per launch from the committed summary, or None."""
+    path = traffic_summary_path(kernel)
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return float(kv["hbm_fetch_bytes_per_launch"]), float(kv["hbm_write_bytes_per_launch"])
+
+
+def _counter_per_dispatch(path, name_prefix, counter, pick=None):
+    """Counter values (summed over the dispatch's entries) of every dispatch whose
+    kernel name starts with name_prefix, in dispatch order."""
+    per = {}
+    with open(path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            if not row["Kernel_Name"].startswith(name_prefix) or row["Counter_Name"] != counter:
+                continue
+            if pick is not None and not pick(row):
+                continue
+            d = int(row["Dispatch_Id"])
+            per[d] = per.get(d, 0.0) + float(row["Counter_Value"])
+    return [per[d] for d in sorted(per)]
+
+
+def summarize(kernel, stats_csv, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    prefix = KERNEL_SOURCES[kernel][0]
+    # the bench launches fwd and dgrad from the same template; dgrad is the
+    # second rows-kernel launch of each step
+    def nth(vals):
+        if kernel == "fwd":
+            return vals[0::2]
+        if kernel == "dgrad":
+            return vals[1::2]
+        return vals
+    stats = None
+    with open(stats_csv, newline="") as fh:
+        for row in csv.DictReader(fh):
+            if row["Name"].startswith(prefix):
+                stats = row if stats is None else stats
+    fetch = nth(_counter_per_dispatch(fetch_csv, prefix, "FETCH_SIZE"))
+    write = nth(_counter_per_dispatch(write_csv, prefix, "WRITE_SIZE"))
+    copy_pick = lambda r: "copy" in r["Kernel_Name"].lower()
+    cf = _counter_per_dispatch(copy_fetch_csv, "", "FETCH_SIZE", copy_pick)
+    cw = _counter_per_dispatch(copy_write_csv, "", "WRITE_SIZE", copy_pick)
+    kib = 1024.0
+    f_scale = COPY_BYTES / (float(np.median(cf)) * kib)
+    w_scale = COPY_BYTES / (float(np.median(cw)) * kib)
+    fetch_b = float(np.median(fetch)) * kib * f_scale
+    write_b = float(np.median(write)) * kib * w_scale
+    lines = [
+        f"kernel: {kernel}",
+        "workload: MoE FC1 a4w4, 32 experts, 32768 routed rows, K=4096, N=3072 (bench.py default step)",
+        f"source_sha256_16: {source_hash(kernel)}",
+        f"kernel_name_prefix: {prefix}",
+        f"stats_calls: {stats['Calls'] if stats else 'n/a'}",
+        f"stats_average_ns: {stats['AverageNs'] if stats else 'n/a'}",
+        f"stats_min_ns: {stats['MinNs'] if stats else 'n/a'}",
+        f"stats_max_ns: {stats['MaxNs'] if stats else 'n/a'}",
+        f"fetch_size_kib_per_dispatch_median: {float(np.median(fetch)):.1f}",
+        f"write_size_kib_per_dispatch_median: {float(np.median(write)):.1f}",
+        f"copy_calibration_bytes: {COPY_BYTES}",
+        f"copy_fetch_size_kib_median: {float(np.median(cf)):.1f}",
+        f"copy_write_size_kib_median: {float(np.median(cw)):.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"hbm_write_bytes_per_launch: {write_b:.0f}",
+        f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def copy_only():
+    import torch
+    dev = torch.device("cuda:0")
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}), flush=True)
 
 
 def cpu_baseline(seconds_hint=20.0):
@@ -87,6 +213,12 @@ def cpu_baseline(seconds_hint=20.0):
 
 def main():
     args = parse()
+    if args.summarize:
+        sys.stdout.write(summarize(*args.summarize))
+        return
+    if args.copy_only:
+        copy_only()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the path shards by expert "
                                    "(see DESIGN.md) but no multi-GPU run is part of it",
@@ -210,7 +342,8 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(bytes_alg[dom] / d / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    tr = read_traffic(dom) if args.passes == "all" else None
+    roof["traffic"] = None if tr is None else round(tr[0] + tr[1])
     roof["per_launch_algorithmic"] = (gemm_flops if roof["bound"] == "mfma" else bytes_alg[dom])
 
     out = {

@@ -83,9 +83,13 @@ __device__ __forceinline__ void dma1(const uint8_t* src, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds((const void*)src, (MXGG_LDS void*)lds, 1, 0, 0);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool AFP8_>
+// OCC workgroups share a CU (the grid is OCC per CU): while one waits at a
+// barrier or drains its epilogue, the other's MFMAs keep the SIMDs busy.
+// SCHED picks the instruction order inside a stage (see compute_stage).
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool AFP8_, int OCC_ = 1, int SCHED_ = 0>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
+  static constexpr int SCHED = SCHED_;
   static constexpr bool AFP8 = AFP8_;
   static constexpr int NW = WM * WN, THREADS = 64 * NW;
   static constexpr int RBA = AFP8 ? BK : BK / 2;  // A bytes per row per stage
@@ -265,6 +269,26 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::
       });
     });
   });
+  // Instruction order of the stage (one basic block):
+  //   0: the compiler's choice
+  //   1: every LDS read first, then every MFMA
+  //   2: the compiler's MFMA/LDS interleaving strategy 0
+  //   3: reads of K step 0, then K step 0's MFMAs each followed by one read of
+  //      K step 1, then the rest
+  constexpr int NR0 = C::FM + C::FN + (C::AFP8 ? C::FM : 0);  // fragment reads per K step
+  if constexpr (C::SCHED == 1) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 64, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);
+  } else if constexpr (C::SCHED == 2) {
+    __builtin_amdgcn_iglp_opt(0);
+  } else if constexpr (C::SCHED == 3) {
+    __builtin_amdgcn_sched_group_barrier(0x100, NR0 + C::FM + C::FN, 0);
+    unroll<NR0>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);
+  }
 }
 
 // Wait until this wave's DMAs of the stage about to be consumed have landed,
@@ -444,7 +468,7 @@ struct RowsSource {
 };
 
 template <class C>
-__global__ __launch_bounds__(C::THREADS, 1) void grouped_rows_kernel(const RowsGemmParams p) {
+__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_rows_kernel(const RowsGemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int64_t pref[kMaxExperts + 1];
   __shared__ int64_t wtot[C::THREADS / 64];
@@ -573,7 +597,7 @@ struct WgradSource {
 };
 
 template <class C>
-__global__ __launch_bounds__(C::THREADS, 1) void grouped_wgrad_kernel(const WgradParams p) {
+__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const WgradParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int64_t pad_pref[kMaxExperts + 1];
   __shared__ int64_t tile_pref[kMaxExperts + 1];
@@ -597,8 +621,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void grouped_wgrad_kernel(const Wgra
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-using CfgA4 = TileCfg<256, 256, 2, 4, 128, 3, false>;   // a4w4: fwd, dgrad, wgrad
-using CfgA8 = TileCfg<256, 256, 2, 4, 64, 4, true>;     // a8w4 forward
+using CfgA4 = TileCfg<256, 256, 2, 4, 128, 3, false, 1, 3>;   // a4w4: fwd, dgrad, wgrad
+using CfgA8 = TileCfg<256, 256, 2, 4, 64, 4, true, 1, 3>;     // a8w4 forward
 
 template <class C, class K, class P>
 static hipError_t launch_persistent(K kernel, const P& p, int64_t tiles, int num_cus, hipStream_t st) {
@@ -609,7 +633,7 @@ static hipError_t launch_persistent(K kernel, const P& p, int64_t tiles, int num
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  int64_t grid = num_cus;
+  int64_t grid = (int64_t)num_cus * C::OCC;
   if (tiles < grid) grid = tiles;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::THREADS), C::SMEM_BYTES, st, p);
