@@ -134,10 +134,19 @@ def mxgg_segpad_rows(m_splits, fmt) -> int:
     return r
 
 
-def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=0, q=None, scales=None):
-    """x: bf16 [rows, cols] (row stride may exceed cols). Returns (q, scales)."""
+def _flags(flags, f):
+    """Power-of-two scales are the blockwise default; MX formats take no flags."""
+    if flags is None:
+        return POW2_SCALES if f in (FP8_1x128, FP8_128x128) else 0
+    return int(flags)
+
+
+def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=None, q=None, scales=None):
+    """x: bf16 [rows, cols] (row stride may exceed cols). Returns (q, scales).
+    flags: None = default (MXGG_POW2_SCALES for the blockwise formats)."""
     torch = _torch()
     f = _fmt(fmt)
+    flags = _flags(flags, f)
     rows, cols = x.shape
     _check_bf16_2d(x)
     if q is None:
@@ -154,10 +163,11 @@ def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=0, q=None, scales=None):
     return q, scales
 
 
-def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=0, q=None, scales=None):
+def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=None, q=None, scales=None):
     """x: bf16 [rows, cols]. Returns (q [cols, mpad(/2)], scales, mpad)."""
     torch = _torch()
     f = _fmt(fmt)
+    flags = _flags(flags, f)
     rows, cols = x.shape
     _check_bf16_2d(x)
     arr, G = _splits(m_splits)

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxgg.so")
 
-SOURCES = ["api.cpp", "quant_mx.hip", "gemm_mx.hip"]
+SOURCES = ["api.cpp", "quant_mx.hip", "quant_blockwise.hip", "gemm_mx.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 HIP_FLAGS = [

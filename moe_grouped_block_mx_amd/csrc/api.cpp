@@ -153,35 +153,43 @@ int64_t mxgg_segpad_rows(const int64_t* m_splits, int32_t G, mxgg_format fmt) {
 
 mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, mxgg_format fmt,
                                   uint32_t flags, void* q, void* scales, hipStream_t stream) {
-  (void)flags;
   Check c = validate_quantize_rowwise(x, rows, cols, ldx, (int)fmt, q, scales);
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
-  if (!is_mx(fmt)) return finish(fail(MXGG_ERR_FORMAT, "blockwise FP8 quantization is not built in this library"));
   int cus = 0;
   c = device_checks(stream, {{x, "x"}, {q, "q"}, {scales, "scales"}}, &cus);
   if (!c.ok()) return finish(c);
-  c = hip_status(launch_quant_rowwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, fmt == MXGG_MXFP8,
-                                         static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), cus, stream),
-                 "row-wise quantizer launch");
+  if (is_mx(fmt))
+    c = hip_status(launch_quant_rowwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, fmt == MXGG_MXFP8,
+                                           static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), cus, stream),
+                   "row-wise quantizer launch");
+  else
+    c = hip_status(launch_quant_rowwise_blk(static_cast<const uint16_t*>(x), rows, cols, ldx,
+                                            fmt == MXGG_FP8_128x128, (flags & MXGG_POW2_SCALES) != 0,
+                                            static_cast<uint8_t*>(q), static_cast<float*>(scales), stream),
+                   "blockwise quantizer launch");
   return c.ok() ? ok() : finish(c);
 }
 
 mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t cols, int64_t ldx,
                                          const int64_t* m_splits, int32_t G, mxgg_format fmt, uint32_t flags,
                                          void* q, void* scales, int64_t mpad, hipStream_t stream) {
-  (void)flags;
   Check c = validate_quantize_colwise(x, rows, cols, ldx, m_splits, G, (int)fmt, q, scales, mpad);
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
-  if (!is_mx(fmt)) return finish(fail(MXGG_ERR_FORMAT, "blockwise FP8 quantization is not built in this library"));
   int cus = 0;
   c = device_checks(stream, {{x, "x"}, {q, "q"}, {scales, "scales"}}, &cus);
   if (!c.ok()) return finish(c);
   const SplitArgs sp = make_splits(m_splits, G);
-  c = hip_status(launch_quant_colwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8,
-                                         static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), mpad, stream),
-                 "column-wise quantizer launch");
+  if (is_mx(fmt))
+    c = hip_status(launch_quant_colwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8,
+                                           static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), mpad, stream),
+                   "column-wise quantizer launch");
+  else
+    c = hip_status(launch_quant_colwise_blk(static_cast<const uint16_t*>(x), cols, ldx, sp,
+                                            (flags & MXGG_POW2_SCALES) != 0, static_cast<uint8_t*>(q),
+                                            static_cast<float*>(scales), mpad, stream),
+                   "blockwise column-wise quantizer launch");
   return c.ok() ? ok() : finish(c);
 }
 
@@ -192,12 +200,31 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
                          mxgg_workspace_size(G));
   if (!c.ok()) return finish(c);
   if (M == 0) return ok();
-  if (!is_mx(a_fmt)) return finish(fail(MXGG_ERR_FORMAT, "blockwise FP8 GEMMs are not built in this library"));
   int cus = 0;
   c = device_checks(stream, {{a_q, "a_q"}, {a_s, "a_s"}, {w_q, "w_q"}, {w_s, "w_s"}, {out, "out"}}, &cus);
   if (!c.ok()) return finish(c);
   RowsGemmParams p;
   std::memset(&p, 0, sizeof(p));
+  if (a_fmt == MXGG_FP8_1x128) {
+    // E4M3 x E4M3; A scales f32 [M, K/128], W scales f32 [G*N/128, K/128]
+    p.a = static_cast<const uint8_t*>(a_q);
+    p.as = static_cast<const uint8_t*>(a_s);
+    p.b = static_cast<const uint8_t*>(w_q);
+    p.bs = static_cast<const uint8_t*>(w_s);
+    p.c = static_cast<uint16_t*>(out);
+    p.lda = K;
+    p.ldas = K / 128 * 4;
+    p.ldb = K;
+    p.ldbs = K / 128 * 4;
+    p.b_gstride = N * K;
+    p.bs_gstride = N / 128 * (K / 128 * 4);
+    p.ldc = N;
+    p.n_out = (int32_t)N;
+    p.kc = (int32_t)K;
+    p.sp = make_splits(m_splits, G);
+    c = hip_status(launch_grouped_rows_blk(p, cus, stream), "blockwise forward launch");
+    return c.ok() ? ok() : finish(c);
+  }
   const bool a8 = a_fmt == MXGG_MXFP8;
   p.a = static_cast<const uint8_t*>(a_q);
   p.as = static_cast<const uint8_t*>(a_s);
@@ -258,7 +285,7 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
                            out_is_bf16, accumulate, ws, ws_bytes, mxgg_workspace_size(G));
   if (!c.ok()) return finish(c);
   if (mpad == 0 && accumulate) return ok();
-  if (fmt != MXGG_MXFP4) return finish(fail(MXGG_ERR_FORMAT, "blockwise FP8 GEMMs are not built in this library"));
+  const bool blk = fmt == MXGG_FP8_1x128;
   int cus = 0;
   c = device_checks(stream, {{dycol_q, "dycol_q"}, {dycol_s, "dycol_s"}, {xcol_q, "xcol_q"}, {xcol_s, "xcol_s"},
                              {main_grad, "main_grad"}},
@@ -271,10 +298,10 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
   p.b = static_cast<const uint8_t*>(xcol_q);
   p.bs = static_cast<const uint8_t*>(xcol_s);
   p.c = main_grad;
-  p.lda = mpad / 2;
-  p.ldas = mpad / 32;
-  p.ldb = mpad / 2;
-  p.ldbs = mpad / 32;
+  p.lda = blk ? mpad : mpad / 2;               // E4M3 / E2M1 bytes
+  p.ldas = blk ? mpad / 128 * 4 : mpad / 32;    // f32 per 128 / UE8M0 per 32
+  p.ldb = p.lda;
+  p.ldbs = p.ldas;
   p.n_rows = (int32_t)N;
   p.n_cols = (int32_t)K;
   p.accumulate = accumulate;
@@ -285,7 +312,8 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
   std::iota(order, order + G, 0);
   std::stable_sort(order, order + G, [&](int x, int y) { return m_splits[x] > m_splits[y]; });
   for (int32_t j = 0; j < G; ++j) p.order[j] = (int16_t)order[j];
-  c = hip_status(launch_grouped_wgrad_mx(p, cus, stream), "wgrad launch");
+  c = hip_status(blk ? launch_grouped_wgrad_blk(p, cus, stream) : launch_grouped_wgrad_mx(p, cus, stream),
+                 "wgrad launch");
   return c.ok() ? ok() : finish(c);
 }
 

@@ -82,30 +82,46 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds) {
 __device__ __forceinline__ void dma1(const uint8_t* src, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds((const void*)src, (MXGG_LDS void*)lds, 1, 0, 0);
 }
+__device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (MXGG_LDS void*)lds, 4, 0, 0);
+}
+
+// Operand kinds: E2M1 x E2M1 and E4M3 x E2M1 with UE8M0 scales per 32 along
+// the contraction (applied by the MFMA), or E4M3 x E4M3 with one fp32 scale
+// per 128 along the contraction ("blockwise": the MFMA runs unscaled into a
+// per-128 partial that is then scaled and added, since fp32 scales are not
+// powers of two in general).
+enum : int { kA4W4 = 0, kA8W4 = 1, kBlkFp8 = 2 };
 
 // OCC workgroups share a CU (the grid is OCC per CU): while one waits at a
 // barrier or drains its epilogue, the other's MFMAs keep the SIMDs busy.
 // SCHED picks the instruction order inside a stage (see compute_stage).
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool AFP8_, int OCC_ = 1, int SCHED_ = 0>
+// BDIV: B rows sharing one scale row (128 for 128x128 weight blocks, else 1).
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, int KIND_, int OCC_ = 1, int SCHED_ = 0,
+          int BDIV_ = 1>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
-  static constexpr int SCHED = SCHED_;
-  static constexpr bool AFP8 = AFP8_;
+  static constexpr int SCHED = SCHED_, BDIV = BDIV_;
+  static constexpr bool AFP8 = KIND_ != kA4W4, BFP8 = KIND_ == kBlkFp8, BLK = KIND_ == kBlkFp8;
   static constexpr int NW = WM * WN, THREADS = 64 * NW;
   static constexpr int RBA = AFP8 ? BK : BK / 2;  // A bytes per row per stage
-  static constexpr int RBB = BK / 2;              // B (E2M1) bytes per row per stage
+  static constexpr int RBB = BFP8 ? BK : BK / 2;  // B bytes per row per stage
   static constexpr int CPA = RBA / 16, CPB = RBB / 16;
   static constexpr int KSTEPS = BK / 64;          // MFMA K steps per stage
-  static constexpr int SB = BK / 32;              // scale blocks per row per stage
+  static constexpr int SB = BLK ? 1 : BK / 32;    // scale dwords per row per stage
+  static constexpr int PROMO = BLK ? 128 / BK : 1;  // stages per 128-element scale block (blockwise)
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  // one ring stage: A chunks, B chunks, A scale dwords, B scale dwords
+  static constexpr int round_up(int v, int m) { return (v + m - 1) / m * m; }
+  // one ring stage: A chunks, B chunks, A scale dwords, B scale dwords (the
+  // scale regions are rounded up to whole DMA instructions; the extra dwords
+  // hold repeats of the last row)
   static constexpr int A_OFF = 0, A_BYTES = BM * RBA;
   static constexpr int B_OFF = A_OFF + A_BYTES, B_BYTES = BN * RBB;
-  static constexpr int AS_OFF = B_OFF + B_BYTES, AS_BYTES = BM * SB * 4;
-  static constexpr int BS_OFF = AS_OFF + AS_BYTES, BS_BYTES = BN * SB * 4;
+  static constexpr int AS_OFF = B_OFF + B_BYTES, AS_BYTES = round_up(BM * SB * 4, NW * 256);
+  static constexpr int BS_OFF = AS_OFF + AS_BYTES, BS_BYTES = round_up(BN * SB * 4, NW * 256);
   static constexpr int STAGE_BYTES = BS_OFF + BS_BYTES;
-  // LDS DMA instructions per wave per stage (1 KiB of chunks or 64 scale bytes each)
+  // LDS DMA instructions per wave per stage (1 KiB of chunks or 64 scale dwords each)
   static constexpr int DA = A_BYTES / (NW * 1024), DB = B_BYTES / (NW * 1024);
   static constexpr int DSA = AS_BYTES / (NW * 256), DSB = BS_BYTES / (NW * 256);
   static constexpr int DPS = DA + DB + DSA + DSB;
@@ -113,8 +129,8 @@ struct TileCfg {
   static constexpr int EPI_OFF = STAGES * STAGE_BYTES;
   static constexpr int SMEM_BYTES = EPI_OFF + NW * EPI_BYTES;
   static_assert(A_BYTES % (NW * 1024) == 0 && B_BYTES % (NW * 1024) == 0, "chunk DMA split");
-  static_assert(AS_BYTES % (NW * 256) == 0 && BS_BYTES % (NW * 256) == 0, "scale DMA split");
   static_assert(KSTEPS == 1 || KSTEPS == 2, "K steps per stage");
+  static_assert(!BLK || BK == 64 || BK == 128, "blockwise stages split a 128-element scale block");
   static_assert(FM >= 1 && FN >= 1 && STAGES >= 2 && STAGES <= 4, "shape");
   static_assert(DPS * (STAGES - 2) < 64, "vmcnt range");
 };
@@ -183,7 +199,7 @@ __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64
     const int r = d / C::SB;
     const int blk = scale_block_of<C>(d % C::SB);
     const int rr = r < t.nrows ? r : t.nrows - 1;
-    pl.offBS[i] = (uint32_t)(rr * ldbs) + blk;
+    pl.offBS[i] = (uint32_t)((rr / C::BDIV) * ldbs) + blk;
     pl.bBS[i] = blk;
   });
 }
@@ -194,9 +210,13 @@ template <class C>
 __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps& t, int s, uint8_t* st, int w) {
   const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_zero_page);
   const int kca = C::AFP8 ? t.kc : t.kc / 2;
-  const int kcb = t.kc / 2;
-  const int nblk = t.kc / 32;
-  const int ka0 = s * C::RBA, kb0 = s * C::RBB, blk0 = s * C::SB;
+  const int kcb = C::BFP8 ? t.kc : t.kc / 2;
+  const int ka0 = s * C::RBA, kb0 = s * C::RBB;
+  // scale bytes of this stage: MX, SB bytes per row from s * SB (blocks of 32
+  // past the contraction read zeros); blockwise, the fp32 of 128-block s*BK/128
+  const int nblk = C::BLK ? t.kc / 128 : t.kc / 32;
+  const int blk0 = C::BLK ? (s * C::BK / 128) * 4 : s * C::SB;
+  const int bidx0 = C::BLK ? s * C::BK / 128 : s * C::SB;
   unroll<C::DA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const uint8_t* src = (ka0 + pl.kA[i] < kca) ? t.a + pl.offA[i] + ka0 : zero;
@@ -209,14 +229,88 @@ __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps&
   });
   unroll<C::DSA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    const uint8_t* src = (blk0 + pl.bAS[i] < nblk) ? t.as + pl.offAS[i] + blk0 : zero;
-    dma1(src, st + C::AS_OFF + (i * C::NW + w) * 256);
+    const uint8_t* src = (bidx0 + pl.bAS[i] < nblk) ? t.as + pl.offAS[i] + blk0 : zero;
+    if constexpr (C::BLK) dma4(src, st + C::AS_OFF + (i * C::NW + w) * 256);
+    else dma1(src, st + C::AS_OFF + (i * C::NW + w) * 256);
   });
   unroll<C::DSB>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    const uint8_t* src = (blk0 + pl.bBS[i] < nblk) ? t.bs + pl.offBS[i] + blk0 : zero;
-    dma1(src, st + C::BS_OFF + (i * C::NW + w) * 256);
+    const uint8_t* src = (bidx0 + pl.bBS[i] < nblk) ? t.bs + pl.offBS[i] + blk0 : zero;
+    if constexpr (C::BLK) dma4(src, st + C::BS_OFF + (i * C::NW + w) * 256);
+    else dma1(src, st + C::BS_OFF + (i * C::NW + w) * 256);
   });
+}
+
+// B fragments of K step KK (E2M1: 16 bytes per lane; E4M3: 2 x 16 bytes).
+template <class C, int KK>
+__device__ __forceinline__ void load_b_frags(const uint8_t* st, v8i (&bf)[C::FN], int wn, int h, int l32) {
+  unroll<C::FN>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const int r = wn * C::WTN + j * 32 + l32;
+    const uint8_t* row = st + C::B_OFF + r * C::RBB;
+    if constexpr (C::BFP8) {
+      const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPB>(r, 4 * KK + h) * 16);
+      const v4i hi = *reinterpret_cast<const v4i*>(row + swz<C::CPB>(r, 4 * KK + 2 + h) * 16);
+      bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPB>(r, 2 * KK + h) * 16);
+      bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    }
+  });
+}
+
+// Blockwise FP8 stage: unscaled E4M3 x E4M3 MFMAs (scale bytes 127 = 2^0)
+// into the partial P of the current 128-element block (FIRST: the block's
+// first stage, P starts from zero); on its last stage (LAST) the partial is
+// scaled by the rows' A scale and the columns' B scale (fp32, from the stage's
+// scale region) and added to acc. Register r of a fragment holds row
+// 8*(r/4) + 4*(lane/32) + r%4, column lane%32, so a lane's 16 row scales of a
+// fragment are four runs of four consecutive dwords.
+template <class C, bool FIRST, bool LAST>
+__device__ __forceinline__ void compute_stage_blk(const uint8_t* st, v16f (&acc)[C::FM][C::FN],
+                                                  v16f (&P)[C::FM][C::FN], int wm, int wn, int h, int l32) {
+  constexpr int kUnit = 0x7F7F7F7F;
+  unroll<C::KSTEPS>([&](auto kc_) {
+    constexpr int kk = decltype(kc_)::value;
+    v8i af[C::FM], bf[C::FN];
+    unroll<C::FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int r = wm * C::WTM + i * 32 + l32;
+      const uint8_t* row = st + C::A_OFF + r * C::RBA;
+      const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r, 4 * kk + h) * 16);
+      const v4i hi = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r, 4 * kk + 2 + h) * 16);
+      af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    });
+    load_b_frags<C, kk>(st, bf, wn, h, l32);
+    unroll<C::FM>([&](auto ic) {
+      unroll<C::FN>([&](auto jc) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        const v16f c_in = (FIRST && kk == 0) ? v16f{} : P[i][j];
+        P[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], c_in, 0, 0, 0, kUnit, 0, kUnit);
+      });
+    });
+  });
+  if constexpr (LAST) {
+    const float* as = reinterpret_cast<const float*>(st + C::AS_OFF);
+    const float* bs = reinterpret_cast<const float*>(st + C::BS_OFF);
+    float sbv[C::FN];
+    unroll<C::FN>([&](auto jc) { sbv[decltype(jc)::value] = bs[wn * C::WTN + decltype(jc)::value * 32 + l32]; });
+    unroll<C::FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      v4f sa4[4];
+      unroll<4>([&](auto qc) {
+        sa4[decltype(qc)::value] =
+            *reinterpret_cast<const v4f*>(as + wm * C::WTM + i * 32 + 8 * decltype(qc)::value + 4 * h);
+      });
+      unroll<C::FN>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        unroll<16>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          acc[i][j][r] += P[i][j][r] * (sa4[r / 4][r % 4] * sbv[j]);
+        });
+      });
+    });
+  }
 }
 
 // MFMAs of one ring stage for this wave's fragments.
@@ -254,18 +348,13 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::
         af[i] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
       }
     });
-    unroll<C::FN>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const int r = wn * C::WTN + j * 32 + l32;
-      const uint8_t* row = st + C::B_OFF + r * C::RBB;
-      const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPB>(r, 2 * kk + h) * 16);
-      bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-    });
+    load_b_frags<C, kk>(st, bf, wn, h, l32);
     unroll<C::FM>([&](auto ic) {
       unroll<C::FN>([&](auto jc) {
         constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], C::AFP8 ? 0 : 4, 4, kk,
-                                                                    (int)sa[i], kk, (int)sb[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], C::AFP8 ? 0 : 4,
+                                                                    C::BFP8 ? 0 : 4, kk, (int)sa[i], kk,
+                                                                    (int)sb[j]);
       });
     });
   });
@@ -275,7 +364,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::
   //   2: the compiler's MFMA/LDS interleaving strategy 0
   //   3: reads of K step 0, then K step 0's MFMAs each followed by one read of
   //      K step 1, then the rest
-  constexpr int NR0 = C::FM + C::FN + (C::AFP8 ? C::FM : 0);  // fragment reads per K step
+  constexpr int NR0 = C::FM * (C::AFP8 ? 2 : 1) + C::FN * (C::BFP8 ? 2 : 1);  // fragment reads per K step
   if constexpr (C::SCHED == 1) {
     __builtin_amdgcn_sched_group_barrier(0x100, 64, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);
@@ -359,12 +448,23 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
     const int cns = (cops.kc + C::BK - 1) / C::BK;
     v16f acc[C::FM][C::FN];
     unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
+    v16f P[C::BLK ? C::FM : 1][C::BLK ? C::FN : 1];
     for (int s = 0; s < cns; ++s) {
       wait_stage<C>(ahead - 1);
       raw_barrier();
       // the slot refilled now held the stage every wave consumed last step
       ahead += issue_one();
-      compute_stage<C>(smem + slot_comp * C::STAGE_BYTES, acc, wm, wn, h, l32);
+      if constexpr (C::BLK) {
+        const uint8_t* st = smem + slot_comp * C::STAGE_BYTES;
+        if constexpr (C::PROMO == 1) {
+          compute_stage_blk<C, true, true>(st, acc, P, wm, wn, h, l32);
+        } else {
+          if ((s & 1) == 0) compute_stage_blk<C, true, false>(st, acc, P, wm, wn, h, l32);
+          else compute_stage_blk<C, false, true>(st, acc, P, wm, wn, h, l32);
+        }
+      } else {
+        compute_stage<C>(smem + slot_comp * C::STAGE_BYTES, acc, wm, wn, h, l32);
+      }
       slot_comp = slot_comp + 1 == C::STAGES ? 0 : slot_comp + 1;
       --ahead;
     }
@@ -435,7 +535,7 @@ struct RowsSource {
     o.a = p.a + row0 * p.lda;
     o.as = p.as + row0 * p.ldas;
     o.b = p.b + (int64_t)q.g * p.b_gstride + (int64_t)col0 * p.ldb;
-    o.bs = p.bs + (int64_t)q.g * p.bs_gstride + (int64_t)col0 * p.ldbs;
+    o.bs = p.bs + (int64_t)q.g * p.bs_gstride + (int64_t)(col0 / C::BDIV) * p.ldbs;
     o.mrows = mleft < C::BM ? mleft : C::BM;
     o.nrows = nleft < C::BN ? nleft : C::BN;
     o.kc = p.kc;
@@ -511,10 +611,13 @@ struct WgradSource {
   __device__ __forceinline__ TileOps ops(int t) const {
     const Pos q = pos(t);
     TileOps o;
-    o.a = p.a + (int64_t)q.row0 * p.lda + q.p0 / 2;
-    o.as = p.as + (int64_t)q.row0 * p.ldas + q.p0 / 32;
-    o.b = p.b + (int64_t)q.col0 * p.ldb + q.p0 / 2;
-    o.bs = p.bs + (int64_t)q.col0 * p.ldbs + q.p0 / 32;
+    // segment start: element bytes (E4M3: 1, E2M1: 1/2) and scale bytes
+    // (MX: one per 32; blockwise: one fp32 per 128)
+    const int64_t sc0 = C::BLK ? q.p0 / 128 * 4 : q.p0 / 32;
+    o.a = p.a + (int64_t)q.row0 * p.lda + (C::AFP8 ? q.p0 : q.p0 / 2);
+    o.as = p.as + (int64_t)q.row0 * p.ldas + sc0;
+    o.b = p.b + (int64_t)q.col0 * p.ldb + (C::BFP8 ? q.p0 : q.p0 / 2);
+    o.bs = p.bs + (int64_t)q.col0 * p.ldbs + sc0;
     const int rl = p.n_rows - q.row0, cl = p.n_cols - q.col0;
     o.mrows = rl < C::BM ? rl : C::BM;
     o.nrows = cl < C::BN ? cl : C::BN;
@@ -606,7 +709,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const
 
   const int G = p.sp.G;
   const int tr = (p.n_rows + C::BM - 1) / C::BM, tc = (p.n_cols + C::BN - 1) / C::BN;
-  block_prefix64<C::THREADS>(G, [&](int g) { return (int64_t)((p.sp.m[g] + 31) & ~31); }, pad_pref, wtot);
+  constexpr int PAD = C::BLK ? 128 : 32;  // segment pad multiple of the column-wise operands
+  block_prefix64<C::THREADS>(G, [&](int g) { return (int64_t)((p.sp.m[g] + PAD - 1) & ~(PAD - 1)); }, pad_pref,
+                             wtot);
   block_prefix64<C::THREADS>(G, [&](int j) {
     const int g = p.order[j];
     return (int64_t)((p.sp.m[g] > 0 || !p.accumulate) ? tr * tc : 0);
@@ -621,8 +726,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-using CfgA4 = TileCfg<256, 256, 2, 4, 128, 3, false, 1, 3>;   // a4w4: fwd, dgrad, wgrad
-using CfgA8 = TileCfg<256, 256, 2, 4, 64, 4, true, 1, 3>;     // a8w4 forward
+using CfgA4 = TileCfg<256, 256, 2, 4, 128, 3, kA4W4, 1, 3>;   // a4w4: fwd, dgrad, wgrad
+using CfgA8 = TileCfg<256, 256, 2, 4, 64, 4, kA8W4, 1, 3>;     // a8w4 forward
+// blockwise FP8: four waves (one per SIMD) each hold a 64x64 accumulator and
+// its per-128 partial; B scale rows are shared by 128 weight rows in the
+// forward, one per row in the weight gradient
+using CfgBlkF = TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 128>;
+using CfgBlkW = TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 1>;
 
 template <class C, class K, class P>
 static hipError_t launch_persistent(K kernel, const P& p, int64_t tiles, int num_cus, hipStream_t st) {
@@ -653,13 +763,26 @@ hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, int num_c
   return launch_persistent<CfgA4>(grouped_rows_kernel<CfgA4>, p, rows_tiles(p, CfgA4::BM, CfgA4::BN), num_cus, st);
 }
 
-hipError_t launch_grouped_wgrad_mx(const WgradParams& p, int num_cus, hipStream_t st) {
-  using C = CfgA4;
+hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, int num_cus, hipStream_t st) {
+  return launch_persistent<CfgBlkF>(grouped_rows_kernel<CfgBlkF>, p, rows_tiles(p, CfgBlkF::BM, CfgBlkF::BN),
+                                    num_cus, st);
+}
+
+template <class C>
+static hipError_t launch_wgrad(const WgradParams& p, int num_cus, hipStream_t st) {
   int64_t tiles = 0;
   const int64_t per = (int64_t)((p.n_rows + C::BM - 1) / C::BM) * ((p.n_cols + C::BN - 1) / C::BN);
   for (int g = 0; g < p.sp.G; ++g) tiles += (p.sp.m[g] > 0 || !p.accumulate) ? per : 0;
   if (tiles == 0) return hipSuccess;
   return launch_persistent<C>(grouped_wgrad_kernel<C>, p, tiles, num_cus, st);
+}
+
+hipError_t launch_grouped_wgrad_mx(const WgradParams& p, int num_cus, hipStream_t st) {
+  return launch_wgrad<CfgA4>(p, num_cus, st);
+}
+
+hipError_t launch_grouped_wgrad_blk(const WgradParams& p, int num_cus, hipStream_t st) {
+  return launch_wgrad<CfgBlkW>(p, num_cus, st);
 }
 
 }  // namespace mxgg

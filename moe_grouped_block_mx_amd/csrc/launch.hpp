@@ -55,4 +55,13 @@ hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols
 hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, int num_cus, hipStream_t st);
 hipError_t launch_grouped_wgrad_mx(const WgradParams& p, int num_cus, hipStream_t st);
 
+// Blockwise FP8 (E4M3 codes, fp32 scales per 128 along the contraction).
+// Scale row strides (ldas, ldbs) are in bytes.
+hipError_t launch_quant_rowwise_blk(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool blk128x128,
+                                    bool pow2, uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_quant_colwise_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
+                                    uint8_t* q, float* s, int64_t mpad, hipStream_t st);
+hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, int num_cus, hipStream_t st);
+hipError_t launch_grouped_wgrad_blk(const WgradParams& p, int num_cus, hipStream_t st);
+
 }  // namespace mxgg

@@ -1,0 +1,271 @@
+// Blockwise FP8 quantizers for gfx950 ("Add ROCm Triton blockwise FP8 grouped
+// GEMM"): E4M3 codes with one fp32 scale per block.
+//
+//   1x128 row-wise   activations: blocks of 128 along the row (the contraction
+//                    axis of the forward pass); scales f32 [rows, cols/128].
+//   128x128          weights: square blocks; scales f32 [rows/128, cols/128].
+//   1x128 column-wise, segment-padded: the wgrad operands; each expert's rows
+//                    transposed, padded with zeros to a multiple of 128, blocks
+//                    of 128 along the padded length; scales f32 [cols, mpad/128].
+//
+// Scale rule and encoder: blk_round.hpp. In power-of-two mode the codes come
+// from gfx950's scaled conversion with the stored scale 2^-t as its operand
+// (it divides by the scale: an exact multiplication by 2^t, and the rule keeps
+// every product at or below 448, where the conversion rounds to nearest even);
+// in fp32 mode the product x * q is rounded to fp32 first and encoded in
+// software. All three kernels are HBM-bound (2 B read, 1 B + 4/128 B written
+// per element) and read with 16-byte coalesced loads.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "blk_round.hpp"
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mxgg {
+
+namespace {
+
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v2bf16 as_bf16x2(uint32_t w) { return __builtin_bit_cast(v2bf16, w); }
+
+// Per-block encoding parameters from the block's bf16 amax magnitude.
+struct BlkScale {
+  float op;        // pow2: the conversion's scale operand 2^-t; fp32 mode: q
+  float stored;    // the scale written out (2^-t or fp32(1/q))
+};
+
+template <bool POW2>
+__device__ __forceinline__ BlkScale blk_scale(uint32_t amax_mag) {
+  const uint32_t a = blk_amax_floored_bits(amax_mag);
+  if constexpr (POW2) {
+    const float s = __uint_as_float(blk_pow2_scale_bits(blk_pow2_t(a)));
+    return BlkScale{s, s};
+  } else {
+    const float q = 448.0f / __uint_as_float(a);  // IEEE division (correctly rounded)
+    return BlkScale{q, 1.0f / q};
+  }
+}
+
+// 8 bf16 (4 packed words) -> 8 E4M3 codes (2 words, element 0 in byte 0).
+template <bool POW2>
+__device__ __forceinline__ uint2 encode8(const uint32_t (&wd)[4], const BlkScale& bs) {
+  if constexpr (POW2) {
+    v2s p0 = {0, 0}, p1 = {0, 0};
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(p0, as_bf16x2(wd[0]), bs.op, false);
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(p0, as_bf16x2(wd[1]), bs.op, true);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(p1, as_bf16x2(wd[2]), bs.op, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(p1, as_bf16x2(wd[3]), bs.op, true);
+    return make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+  } else {
+    uint32_t o[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(wd[i] << 16) * bs.op;
+      const float hi = __uint_as_float(wd[i] & 0xffff0000u) * bs.op;
+      const uint32_t pair = f32_to_e4m3_rne_sat(__float_as_uint(lo)) | (f32_to_e4m3_rne_sat(__float_as_uint(hi)) << 8);
+      o[i >> 1] |= pair << (16 * (i & 1));
+    }
+    return make_uint2(o[0], o[1]);
+  }
+}
+
+__device__ __forceinline__ uint32_t amax8(const uint32_t (&wd)[4]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(wd[i] & 0x7fffu, (wd[i] >> 16) & 0x7fffu));
+  return m;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// 1x128 row-wise. As the MX row-wise kernel: a wave owns 64 consecutive
+// 16-byte chunks of one row (four 128-element blocks, 16 lanes each, amax
+// reduced with four xor-shuffles); each thread keeps U rows' loads in flight.
+// ---------------------------------------------------------------------------
+template <bool POW2, int U>
+__global__ __launch_bounds__(256) void quant_rowwise_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                                  int rows, int cpr, uint8_t* __restrict__ q,
+                                                                  float* __restrict__ s) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;  // 8-element chunk inside the row
+  const bool cvalid = c < cpr;
+  const int64_t qrow = (int64_t)cpr * 8, srow = cpr / 16;
+  for (int rb = blockIdx.y * (4 * U); rb < rows; rb += gridDim.y * (4 * U)) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = rb + u * 4 + w;
+      v[u] = (cvalid && r < rows) ? *reinterpret_cast<const uint4*>(x + (int64_t)r * ldx + (int64_t)c * 8)
+                                  : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = rb + u * 4 + w;
+      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t amax = amax8(wd);
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, m, 64));
+      if (!(cvalid && r < rows)) continue;
+      const BlkScale bs = blk_scale<POW2>(amax);
+      *reinterpret_cast<uint2*>(q + (int64_t)r * qrow + (int64_t)c * 8) = encode8<POW2>(wd, bs);
+      if ((c & 15) == 0) s[(int64_t)r * srow + (c >> 4)] = bs.stored;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 blocks. One workgroup per block: thread t reads rows t/16 + 16 i
+// (i < 8), chunk t%16 (8 elements), i.e. every load instruction covers 16
+// full 256-byte row segments; amax is reduced in the wave, then across the
+// four waves through LDS.
+// ---------------------------------------------------------------------------
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t cols,
+                                                            uint8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ uint32_t wmax[4];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
+  const int rr = t >> 4, ch = t & 15;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + rr + 16 * i) * ldx + c0 + ch * 8);
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    amax = max(amax, amax8(wd));
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, m, 64));
+  if (lane == 0) wmax[w] = amax;
+  __syncthreads();
+  amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const BlkScale bs = blk_scale<POW2>(amax);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    *reinterpret_cast<uint2*>(q + (r0 + rr + 16 * i) * cols + c0 + ch * 8) = encode8<POW2>(wd, bs);
+  }
+  if (t == 0) s[(int64_t)blockIdx.y * (cols / 128) + blockIdx.x] = bs.stored;
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 column-wise, segment-padded. A workgroup transposes one 128-row block
+// of the padded row space (all of it inside one expert segment, zeros past the
+// segment end) by 64 columns through LDS; thread (column c, quarter b) holds
+// rows 32b .. 32b+31 of column c, the four quarters combine their amax through
+// LDS, and each thread writes its 32 codes (two 16-byte stores).
+// ---------------------------------------------------------------------------
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_colwise_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                                  int64_t cols, const SplitArgs sp, int64_t mpad,
+                                                                  uint8_t* __restrict__ q, float* __restrict__ s) {
+  constexpr int PITCH = 64 + 2;
+  __shared__ int64_t pref[kMaxExperts + 1];  // low: padded offsets, high: row offsets
+  __shared__ int64_t wtot[4];
+  __shared__ int32_t pad_offs[kMaxExperts + 1];
+  __shared__ uint16_t tile[128 * PITCH];
+  __shared__ uint32_t qmax[4][64];
+  __shared__ int64_t blk_row0;
+  __shared__ int32_t blk_valid;
+
+  const int G = sp.G;
+  block_prefix64<256>(G, [&](int g) {
+    const int64_t m = sp.m[g];
+    return (m << 32) | ((m + 127) & ~127ll);
+  }, pref, wtot);
+  for (int g = threadIdx.x; g <= G; g += 256) pad_offs[g] = (int32_t)(pref[g] & 0xffffffffll);
+  __syncthreads();
+
+  const int64_t p0 = (int64_t)blockIdx.x * 128;  // first padded row (< mpad by the grid)
+  if (threadIdx.x == 0) {
+    const int g = upper_bound_i32(pad_offs, G + 1, (int32_t)p0) - 1;
+    const int64_t local = p0 - pad_offs[g];
+    const int64_t nv = (int64_t)sp.m[g] - local;
+    blk_row0 = (pref[g] >> 32) + local;
+    blk_valid = nv > 128 ? 128 : (int)nv;
+  }
+  __syncthreads();
+
+  const int64_t c0 = (int64_t)blockIdx.y * 64;
+  const int ncol = cols - c0 < 64 ? (int)(cols - c0) : 64;  // multiple of 32
+  const int nvalid = blk_valid;
+  const int64_t row0 = blk_row0;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int idx = pass * 256 + threadIdx.x;
+    const int row = idx >> 3, ch = idx & 7;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < nvalid && ch * 8 < ncol) v = *reinterpret_cast<const uint4*>(x + (row0 + row) * ldx + c0 + ch * 8);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * PITCH + ch * 8);
+    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+  }
+  __syncthreads();
+
+  const int c = threadIdx.x & 63, b = threadIdx.x >> 6;
+  uint32_t vals[32];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    vals[r] = tile[(b * 32 + r) * PITCH + c];
+    amax = max(amax, vals[r] & 0x7fffu);
+  }
+  qmax[b][c] = amax;
+  __syncthreads();
+  amax = max(max(qmax[0][c], qmax[1][c]), max(qmax[2][c], qmax[3][c]));
+  if (c >= ncol) return;
+  const BlkScale bs = blk_scale<POW2>(amax);
+  uint8_t* qp = q + (c0 + c) * mpad + p0 + b * 32;
+  uint32_t o[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t wd[4] = {vals[8 * d] | (vals[8 * d + 1] << 16), vals[8 * d + 2] | (vals[8 * d + 3] << 16),
+                            vals[8 * d + 4] | (vals[8 * d + 5] << 16), vals[8 * d + 6] | (vals[8 * d + 7] << 16)};
+    const uint2 e = encode8<POW2>(wd, bs);
+    o[2 * d] = e.x;
+    o[2 * d + 1] = e.y;
+  }
+  reinterpret_cast<uint4*>(qp)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  reinterpret_cast<uint4*>(qp)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  if (b == 0) s[(c0 + c) * (mpad / 128) + p0 / 128] = bs.stored;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_quant_rowwise_blk(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool blk128x128,
+                                    bool pow2, uint8_t* q, float* s, hipStream_t st) {
+  if (blk128x128) {
+    const dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
+    if (pow2)
+      hipLaunchKernelGGL(quant_128x128_kernel<true>, grid, dim3(256), 0, st, x, ldx, cols, q, s);
+    else
+      hipLaunchKernelGGL(quant_128x128_kernel<false>, grid, dim3(256), 0, st, x, ldx, cols, q, s);
+    return hipGetLastError();
+  }
+  constexpr int U = 4;
+  const int cpr = (int)(cols / 8);
+  const int64_t gy_need = (rows + 4 * U - 1) / (4 * U);
+  const dim3 grid((unsigned)((cpr + 63) / 64), (unsigned)(gy_need < 65535 ? gy_need : 65535));
+  if (pow2)
+    hipLaunchKernelGGL((quant_rowwise_1x128_kernel<true, U>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q, s);
+  else
+    hipLaunchKernelGGL((quant_rowwise_1x128_kernel<false, U>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_colwise_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
+                                    uint8_t* q, float* s, int64_t mpad, hipStream_t st) {
+  const dim3 grid((unsigned)(mpad / 128), (unsigned)((cols + 63) / 64));
+  if (pow2)
+    hipLaunchKernelGGL(quant_colwise_1x128_kernel<true>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, q, s);
+  else
+    hipLaunchKernelGGL(quant_colwise_1x128_kernel<false>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, q, s);
+  return hipGetLastError();
+}
+
+}  // namespace mxgg

@@ -98,6 +98,9 @@ inline Check validate_quantize_rowwise(const void* x, int64_t rows, int64_t cols
   if (ldx < cols) return fail(MXGG_ERR_SHAPE, "ldx=%lld < cols=%lld", ldx, cols);
   if (ldx % 8) return fail(MXGG_ERR_ALIGN, "ldx=%lld not a multiple of 8 elements", ldx);
   if (rows >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SHAPE, "rows=%lld >= 2^31", rows);
+  // one 128x128 block per workgroup, block rows on the grid's y axis
+  if (f == MXGG_FP8_128x128 && rows / 128 > 65535)
+    return fail(MXGG_ERR_SHAPE, "rows=%lld too large for 128x128 blocks (<= 65535 block rows)", rows);
   const bool nz = rows > 0;
   MXGG_TRY(check_ptr(x, nz, "x"));
   MXGG_TRY(check_ptr(q, nz, "q"));
@@ -114,6 +117,8 @@ inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols
   const int blk = is_mx(f) ? 32 : 128;
   if (cols % 32) return fail(MXGG_ERR_SHAPE, "cols=%lld is not a multiple of 32", cols);
   (void)blk;
+  // 64 columns per workgroup on the grid's y axis
+  if ((cols + 63) / 64 > 65535) return fail(MXGG_ERR_SHAPE, "cols=%lld too large (<= 4194240)", cols);
   if (ldx < cols) return fail(MXGG_ERR_SHAPE, "ldx=%lld < cols=%lld", ldx, cols);
   if (ldx % 8) return fail(MXGG_ERR_ALIGN, "ldx=%lld not a multiple of 8 elements", ldx);
   MXGG_TRY(check_splits(m, G, rows, "x"));
