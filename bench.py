@@ -27,7 +27,7 @@ committed rocprofv3 summary profiles/<kernel>_fc1_traffic.txt (FETCH_SIZE and
 WRITE_SIZE per dispatch, each scaled by the same counter's reading for a plain
 1 GiB copy); null when that summary was taken from a different kernel source.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--workload fc1|a8w4|blockwise]
        python bench.py --copy-only            (calibration copy for --pmc runs)
        python bench.py --summarize KERNEL STATS_CSV FETCH_CSV WRITE_CSV
                        COPY_FETCH_CSV COPY_WRITE_CSV   (writes the summary text)
@@ -51,6 +51,7 @@ if ROOT not in sys.path:
 METRIC = "grouped MXFP4 GEMM TFLOPS (fwd/dgrad/wgrad) and % of MFMA peak, 1 MI355X"
 PEAK_MXFP4_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
 
 
 def parse():
@@ -60,6 +61,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--passes", default="all", help="profiling aid: fwd, dgrad, wgrad or all")
+    ap.add_argument("--workload", default="fc1", choices=["fc1", "a8w4", "blockwise"],
+                    help="fc1: the a4w4 training step (default, the headline); a8w4: the MXFP8 x MXFP4 forward; "
+                         "blockwise: the blockwise FP8 forward + weight gradient")
     ap.add_argument("--copy-only", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize", nargs=6, metavar=("KERNEL", "STATS", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="print the profile summary of KERNEL from rocprofv3 csv outputs")
@@ -211,6 +215,130 @@ def cpu_baseline(seconds_hint=20.0):
                       f"NumPy fp64 oracle (OpenBLAS {threads} threads, host has {os.cpu_count()} cpus)"}
 
 
+def build_workload(name, dev):
+    """Device inputs, the op list and the per-op algorithmic work of one step.
+
+    Returns dict(ops=[(name, kind, fn)], bytes_alg={op: bytes}, flops={op: flops},
+    config={...}, peak_tflops=..., dtype=...)."""
+    import torch
+
+    import moe_grouped_block_mx_amd as mxg
+    from synth import WORKLOADS, splits_for
+
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+
+    def normal(shape, std=1.0):
+        x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+        return (x * std).to(torch.bfloat16) if std != 1.0 else x.to(torch.bfloat16)
+
+    if name == "fc1":
+        wl = WORKLOADS["fc1"]
+        G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
+        sp = splits_for("fc1")
+        a, w, dy = normal((M, K)), normal((G * N, K), wl["w_std"]), normal((M, N))
+        main_grad = torch.randn((G, N, K), generator=gen, device=dev, dtype=torch.float32)
+        mpad = mxg.segpad_rows(sp, "mxfp4")
+        aq, as_ = torch.empty((M, K // 2), **u8), torch.empty((M, K // 32), **u8)
+        wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty((G * N, K // 32), **u8)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        dq, ds = torch.empty((M, N // 2), **u8), torch.empty((M, N // 32), **u8)
+        wcq, wcs = torch.empty((K, G * N // 2), **u8), torch.empty((K, G * N // 32), **u8)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        dcq, dcs = torch.empty((N, mpad // 2), **u8), torch.empty((N, mpad // 32), **u8)
+        xcq, xcs = torch.empty((K, mpad // 2), **u8), torch.empty((K, mpad // 32), **u8)
+        ops = [
+            ("quant_A_row", "quant", lambda: mxg.quantize_rowwise(a, "mxfp4", q=aq, scales=as_)),
+            ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, "mxfp4", q=wq, scales=ws)),
+            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, out=y)),
+            ("quant_dY_row", "quant", lambda: mxg.quantize_rowwise(dy, "mxfp4", q=dq, scales=ds)),
+            ("quant_W_col", "quant", lambda: mxg.quantize_colwise_segpad(w, [N] * G, "mxfp4", q=wcq, scales=wcs)),
+            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, dx=dx)),
+            ("quant_dY_col", "quant", lambda: mxg.quantize_colwise_segpad(dy, sp, "mxfp4", q=dcq, scales=dcs)),
+            ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "mxfp4", q=xcq, scales=xcs)),
+            ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, main_grad,
+                                                        accumulate=True)),
+        ]
+        nz = int((sp > 0).sum())
+        q4 = 0.5 + 1 / 32
+        bytes_alg = {
+            "quant_A_row": M * K * (2 + q4), "quant_W_row": G * N * K * (2 + q4),
+            "fwd": M * K * q4 + nz * N * K * q4 + M * N * 2,
+            "quant_dY_row": M * N * (2 + q4), "quant_W_col": G * N * K * (2 + q4),
+            "dgrad": M * N * q4 + nz * N * K * q4 + M * K * 2,
+            "quant_dY_col": M * N * 2 + mpad * N * q4, "quant_X_col": M * K * 2 + mpad * K * q4,
+            "wgrad": mpad * (N + K) * q4 + nz * N * K * 4 * 2,
+        }
+        config = {"workload": "MoE FC1 a4w4 training step (fwd+dgrad+wgrad with MX quantization)",
+                  "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz,
+                  "max_split": int(sp.max()), "mpad": mpad, "routing": "Dirichlet(0.5), 3 zeroed, seed 0"}
+        return dict(ops=ops, bytes_alg=bytes_alg, flops={"fwd": 2.0 * M * N * K, "dgrad": 2.0 * M * N * K,
+                                                          "wgrad": 2.0 * M * N * K},
+                    config=config, peak_tflops=PEAK_MXFP4_TFLOPS, dtype="mxfp4", hbm_gemms={"wgrad"},
+                    metric=METRIC)
+
+    if name == "a8w4":
+        wl = WORKLOADS["a8w4"]
+        G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
+        sp = splits_for("a8w4")
+        a, w = normal((M, K)), normal((G * N, K), wl["w_std"])
+        aq, as_ = torch.empty((M, K), **u8), torch.empty((M, K // 32), **u8)
+        wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty((G * N, K // 32), **u8)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ops = [
+            ("quant_A_row", "quant", lambda: mxg.quantize_rowwise(a, "mxfp8", q=aq, scales=as_)),
+            ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, "mxfp4", q=wq, scales=ws)),
+            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt="mxfp8", out=y)),
+        ]
+        nz = int((sp > 0).sum())
+        bytes_alg = {"quant_A_row": M * K * (2 + 1 + 1 / 32), "quant_W_row": G * N * K * (2 + 0.5 + 1 / 32),
+                     "fwd": M * K * (1 + 1 / 32) + nz * N * K * (0.5 + 1 / 32) + M * N * 2}
+        config = {"workload": "MoE a8w4 forward (MXFP8 activations x MXFP4 weights, with quantization)",
+                  "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz, "max_split": int(sp.max()),
+                  "routing": "Zipf(1.1), 8 zeroed, seed 0"}
+        return dict(ops=ops, bytes_alg=bytes_alg, flops={"fwd": 2.0 * M * N * K}, config=config,
+                    peak_tflops=PEAK_FP8_TFLOPS, dtype="mxfp8xmxfp4", hbm_gemms=set(),
+                    metric="grouped a8w4 GEMM TFLOPS (fwd) and % of FP8 MFMA peak, 1 MI355X")
+
+    if name == "blockwise":
+        wl = WORKLOADS["blockwise"]
+        G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
+        sp = splits_for("blockwise")
+        a, w, dy = normal((M, K)), normal((G * N, K), wl["w_std"]), normal((M, N))
+        mpad = mxg.segpad_rows(sp, "fp8_1x128")
+        aq, as_ = torch.empty((M, K), **u8), torch.empty((M, K // 128), **f32)
+        wq, ws = torch.empty((G * N, K), **u8), torch.empty((G * N // 128, K // 128), **f32)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        dcq, dcs = torch.empty((N, mpad), **u8), torch.empty((N, mpad // 128), **f32)
+        xcq, xcs = torch.empty((K, mpad), **u8), torch.empty((K, mpad // 128), **f32)
+        dw = torch.empty((G, N, K), dtype=torch.bfloat16, device=dev)
+        ops = [
+            ("quant_A_1x128", "quant", lambda: mxg.quantize_rowwise(a, "fp8_1x128", q=aq, scales=as_)),
+            ("quant_W_128x128", "quant", lambda: mxg.quantize_rowwise(w, "fp8_128x128", q=wq, scales=ws)),
+            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt="fp8_1x128",
+                                                    w_fmt="fp8_128x128", out=y)),
+            ("quant_dY_col", "quant", lambda: mxg.quantize_colwise_segpad(dy, sp, "fp8_1x128", q=dcq, scales=dcs)),
+            ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "fp8_1x128", q=xcq, scales=xcs)),
+            ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, dw, accumulate=False,
+                                                        fmt="fp8_1x128")),
+        ]
+        nz = int((sp > 0).sum())
+        q8 = 1 + 4 / 128
+        bytes_alg = {"quant_A_1x128": M * K * (2 + q8), "quant_W_128x128": G * N * K * (2 + 1),
+                     "fwd": M * K * q8 + nz * N * K * 1 + M * N * 2,
+                     "quant_dY_col": M * N * 2 + mpad * N * q8, "quant_X_col": M * K * 2 + mpad * K * q8,
+                     "wgrad": mpad * (N + K) * q8 + G * N * K * 2}
+        config = {"workload": "MoE blockwise FP8 forward + weight gradient (1x128 / 128x128 fp32 scales, "
+                              "power-of-two; bf16 weight gradient, overwrite)",
+                  "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz, "max_split": int(sp.max()),
+                  "mpad": mpad, "routing": "Dirichlet(1), seed 0"}
+        return dict(ops=ops, bytes_alg=bytes_alg, flops={"fwd": 2.0 * M * N * K, "wgrad": 2.0 * M * N * K},
+                    config=config, peak_tflops=PEAK_FP8_TFLOPS, dtype="fp8_e4m3", hbm_gemms={"wgrad"},
+                    metric="grouped blockwise FP8 GEMM TFLOPS (fwd/wgrad) and % of FP8 MFMA peak, 1 MI355X")
+    raise SystemExit(f"unknown workload {name!r}")
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -227,65 +355,15 @@ def main():
 
     import torch
 
-    import moe_grouped_block_mx_amd as mxg
-    from synth import WORKLOADS, splits_for
-
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = WORKLOADS["fc1"]
-    G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
-    sp = splits_for("fc1")
-    assert int(sp.sum()) == M
-    gen = torch.Generator(device=dev).manual_seed(1234)
-    a = torch.randn((M, K), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    w = (torch.randn((G * N, K), generator=gen, device=dev, dtype=torch.float32) * wl["w_std"]).to(torch.bfloat16)
-    dy = torch.randn((M, N), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    main_grad = torch.randn((G, N, K), generator=gen, device=dev, dtype=torch.float32)
-    mpad = mxg.segpad_rows(sp, "mxfp4")
-
-    # outputs / quantized operands allocated once (the library allocates nothing)
-    u8 = dict(dtype=torch.uint8, device=dev)
-    aq, as_ = torch.empty((M, K // 2), **u8), torch.empty((M, K // 32), **u8)
-    wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty((G * N, K // 32), **u8)
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    dq, ds = torch.empty((M, N // 2), **u8), torch.empty((M, N // 32), **u8)
-    wcq, wcs = torch.empty((K, G * N // 2), **u8), torch.empty((K, G * N // 32), **u8)
-    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    dcq, dcs = torch.empty((N, mpad // 2), **u8), torch.empty((N, mpad // 32), **u8)
-    xcq, xcs = torch.empty((K, mpad // 2), **u8), torch.empty((K, mpad // 32), **u8)
-
-    ops = [
-        ("quant_A_row", "quant", lambda: mxg.quantize_rowwise(a, "mxfp4", q=aq, scales=as_)),
-        ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, "mxfp4", q=wq, scales=ws)),
-        ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, out=y)),
-        ("quant_dY_row", "quant", lambda: mxg.quantize_rowwise(dy, "mxfp4", q=dq, scales=ds)),
-        ("quant_W_col", "quant", lambda: mxg.quantize_colwise_segpad(w, [N] * G, "mxfp4", q=wcq, scales=wcs)),
-        ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, dx=dx)),
-        ("quant_dY_col", "quant", lambda: mxg.quantize_colwise_segpad(dy, sp, "mxfp4", q=dcq, scales=dcs)),
-        ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "mxfp4", q=xcq, scales=xcs)),
-        ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, main_grad,
-                                                    accumulate=True)),
-    ]
+    W = build_workload(args.workload, dev)
+    ops, bytes_alg, flops = W["ops"], W["bytes_alg"], W["flops"]
     if args.passes != "all":
         keep = {"fwd": {"quant_A_row", "quant_W_row", "fwd"},
                 "dgrad": {"quant_dY_row", "quant_W_col", "dgrad"},
                 "wgrad": {"quant_dY_col", "quant_X_col", "wgrad"}}[args.passes]
         ops = [o for o in ops if o[0] in keep]
-
-    gemm_flops = 2.0 * M * N * K
-    # algorithmic bytes per launch: what each kernel must move at least once
-    nz = int((sp > 0).sum())
-    bytes_alg = {
-        "quant_A_row": M * K * (2 + 0.5 + 1 / 32),
-        "quant_W_row": G * N * K * (2 + 0.5 + 1 / 32),
-        "fwd": M * K * (0.5 + 1 / 32) + nz * N * K * (0.5 + 1 / 32) + M * N * 2,
-        "quant_dY_row": M * N * (2 + 0.5 + 1 / 32),
-        "quant_W_col": G * N * K * (2 + 0.5 + 1 / 32),
-        "dgrad": M * N * (0.5 + 1 / 32) + nz * N * K * (0.5 + 1 / 32) + M * K * 2,
-        "quant_dY_col": M * N * 2 + mpad * N * (0.5 + 1 / 32),
-        "quant_X_col": M * K * 2 + mpad * K * (0.5 + 1 / 32),
-        "wgrad": mpad * (N + K) * (0.5 + 1 / 32) + nz * N * K * 4 * 2,
-    }
 
     stream = torch.cuda.current_stream(dev)
     ev = {name: [] for name, _, _ in ops}
@@ -302,7 +380,6 @@ def main():
             else:
                 fn()
 
-    # a leading kernel so the first timed launch does not absorb launch latency
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(False)
@@ -314,7 +391,8 @@ def main():
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / args.steps
 
-    # per-kernel durations (separate timed steps, events around each launch)
+    # per-kernel durations (separate timed steps, HIP events around each
+    # launch on the stream the library launches on)
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
@@ -326,28 +404,32 @@ def main():
         entry["GBs_alg"] = round(bytes_alg[name] / d / 1e9, 1)
         entry["frac_hbm"] = round(bytes_alg[name] / d / 1e9 / PEAK_HBM_GBS, 4)
         if kind == "gemm":
-            entry["TFLOPS"] = round(gemm_flops / d / 1e12, 1)
-            entry["pct_mxfp4_peak"] = round(100 * gemm_flops / d / 1e12 / PEAK_MXFP4_TFLOPS, 2)
+            entry["TFLOPS"] = round(flops[name] / d / 1e12, 1)
+            entry["pct_mfma_peak"] = round(100 * flops[name] / d / 1e12 / W["peak_tflops"], 2)
         per[name] = entry
 
-    n_gemm = sum(1 for _, k, _ in ops if k == "gemm")
-    value = n_gemm * gemm_flops / t_step / 1e12
+    step_flops = sum(flops[n] for n, k, _ in ops if k == "gemm")
+    value = step_flops / t_step / 1e12
     dom = max(per, key=lambda k: per[k]["ms"])
     dkind = dict((n, k) for n, k, _ in ops)[dom]
     d = per[dom]["ms"] * 1e-3
-    if dkind == "gemm" and dom != "wgrad":
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(gemm_flops / d / 1e12, 1),
-                "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s"}
+    if dkind == "gemm" and dom not in W["hbm_gemms"]:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(flops[dom] / d / 1e12, 1),
+                "peak": W["peak_tflops"], "unit": "TFLOP/s"}
+        per_unit = flops[dom]
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(bytes_alg[dom] / d / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        per_unit = bytes_alg[dom]
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    tr = read_traffic(dom) if args.passes == "all" else None
+    tr = read_traffic(dom) if (args.passes == "all" and args.workload == "fc1") else None
     roof["traffic"] = None if tr is None else round(tr[0] + tr[1])
-    roof["per_launch_algorithmic"] = (gemm_flops if roof["bound"] == "mfma" else bytes_alg[dom])
+    roof["per_launch_algorithmic"] = per_unit
 
+    config = dict(W["config"])
+    config["passes"] = args.passes
     out = {
-        "metric": METRIC,
+        "metric": W["metric"],
         "value": round(value, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -357,17 +439,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4",
+        "dtype": W["dtype"],
         "data": "synthetic",
-        "config": {"workload": "MoE FC1 a4w4 training step (fwd+dgrad+wgrad with MX quantization)",
-                   "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz,
-                   "max_split": int(sp.max()), "mpad": mpad, "routing": "Dirichlet(0.5), 3 zeroed, seed 0",
-                   "passes": args.passes},
+        "config": config,
         "roofline": roof,
         "kernels": per,
-        "pct_mxfp4_peak_step": round(100 * value / PEAK_MXFP4_TFLOPS, 2),
+        "pct_mfma_peak_step": round(100 * value / W["peak_tflops"], 2),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "fc1":
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
