@@ -8,7 +8,7 @@
  *  - "Triton mxfp4 (and a8w4) grouped GEMM kernel": a persistent grouped MXFP4
  *    GEMM in three passes -- forward (TN), input gradient (dgrad, NN) and
  *    variable-K weight gradient (wgrad, NT) -- fed by a row operand
- *    (data (N, K/2) + UE8M0 scales (N, K/32)) and, for wgrad, a column operand
+ *    (data (N, K/2) + UE8M0 scales, one per 32 along K) and, for wgrad, a column operand
  *    whose expert segments are padded (the segment-padded layout below). The
  *    same page requires split validation: no negative split, one split per
  *    expert, splits summing to the row count of every row-split operand.
@@ -25,6 +25,13 @@
  *    column scales, power-of-two scales), variable-K wgrad with in-place
  *    accumulation, and the rule that every output element is owned by exactly
  *    one tile (no wrapped tail tiles).
+ *
+ * MX scale layout: block-major. The UE8M0 scales of an operand with R rows
+ * and B blocks of 32 along its contraction axis are stored as u8 [B, R]: the
+ * scale of row r, block b is byte b*R + r (the page on hipBLASLt MXFP4 support
+ * describes pre-arranged scale layouts; this one lets a GEMM stage read the
+ * scales of consecutive rows contiguously). Blockwise fp32 scales are
+ * row-major as listed below.
  *
  * Formats (OCP MX v1.0 and OCP FP8):
  *   MXGG_MXFP4        E2M1 elements, 2 per byte (even element in bits 3:0),
@@ -117,7 +124,7 @@ typedef enum mxgg_format {
  *           MXGG_FP8_128x128: 128x128 blocks (rows % 128 == 0, cols % 128 == 0).
  *   flags   MXGG_POW2_SCALES for the blockwise formats (ignored for MX).
  *   q       MXFP4: u8 [rows, cols/2]; otherwise u8 [rows, cols] (E4M3 codes).
- *   scales  MX: u8 [rows, cols/32]; FP8_1x128: f32 [rows, cols/128];
+ *   scales  MX: u8 [cols/32, rows] (block-major); FP8_1x128: f32 [rows, cols/128];
  *           FP8_128x128: f32 [rows/128, cols/128].
  * rows == 0 returns MXGG_OK with no launch. Errors: NULL, SHAPE, FORMAT,
  * ALIGN, DEVICE, ARCH, HIP.
@@ -140,7 +147,7 @@ mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int
  *   m_splits host int64 [G], 1 <= G <= 512, each >= 0.
  *   fmt      MXGG_MXFP4, MXGG_MXFP8 or MXGG_FP8_1x128; cols % 32 == 0.
  *   q        MXFP4: u8 [cols, mpad/2]; otherwise u8 [cols, mpad].
- *   scales   MX: u8 [cols, mpad/32]; FP8_1x128: f32 [cols, mpad/128].
+ *   scales   MX: u8 [mpad/32, cols] (block-major); FP8_1x128: f32 [cols, mpad/128].
  *   mpad     must equal mxgg_segpad_rows(m_splits, G, fmt).
  * Padding positions hold zero codes. rows == 0 returns MXGG_OK (no launch).
  * Errors: NULL, SHAPE, SPLITS, FORMAT, ALIGN, DEVICE, ARCH, HIP.
@@ -154,9 +161,9 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
  * Grouped forward, TN: out[r, n] = sum_k A[r, k] * W_g[n, k] for every row r
  * of expert g (rows of expert g are consecutive, in expert order).
  *   a_q, a_s  A quantized row-wise along K: (MXFP4: u8 [M, K/2] | MXFP8: u8 [M, K])
- *             + u8 [M, K/32]; or MXGG_FP8_1x128: u8 [M, K] + f32 [M, K/128].
+ *             + u8 [K/32, M]; or MXGG_FP8_1x128: u8 [M, K] + f32 [M, K/128].
  *   w_q, w_s  packed expert weights [G*N, K] quantized row-wise along K:
- *             MXFP4 u8 [G*N, K/2] + u8 [G*N, K/32]; or MXGG_FP8_128x128:
+ *             MXFP4 u8 [G*N, K/2] + u8 [K/32, G*N]; or MXGG_FP8_128x128:
  *             u8 [G*N, K] + f32 [G*N/128, K/128].
  *   format pairs (a_fmt, w_fmt): (MXFP4, MXFP4) a4w4, (MXFP8, MXFP4) a8w4,
  *             (FP8_1x128, FP8_128x128) blockwise FP8.
@@ -176,10 +183,11 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
 
 /*
  * Grouped input gradient, NN: dx[r, k] = sum_n dY[r, n] * W_g[n, k].
- *   dy_q, dy_s     dY quantized row-wise along N: u8 [M, N/2] + u8 [M, N/32].
+ *   dy_q, dy_s     dY quantized row-wise along N: u8 [M, N/2] + u8 [N/32, M].
  *   wcol_q, wcol_s W quantized along N with mxgg_quantize_colwise_segpad on
  *                  W as [G*N, K] with splits {N, ..., N}: u8 [K, G*N/2] +
- *                  u8 [K, G*N/32] (expert g owns columns [g*N, (g+1)*N)).
+ *                  u8 [G*N/32, K] (expert g owns columns [g*N, (g+1)*N) and
+ *                  scale blocks [g*N/32, (g+1)*N/32)).
  *   fmt            MXGG_MXFP4 (the only dgrad format).
  *   dx             bf16 [M, K].
  * Shape rules as for the forward, and G*N/2 < 2^23. Errors as for the forward.
@@ -193,8 +201,10 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
  * Grouped variable-K weight gradient, NT: dW_g[n, k] = sum over the tokens t of
  * expert g of dY[t, n] * X[t, k], contracted over the expert's padded segment
  * (pad positions are zero codes, so they add nothing).
- *   dycol_q/_s  dY from mxgg_quantize_colwise_segpad: [N, mpad] operand.
- *   xcol_q/_s   X from mxgg_quantize_colwise_segpad: [K, mpad] operand.
+ *   dycol_q/_s  dY from mxgg_quantize_colwise_segpad: [N, mpad] operand
+ *               (MX scales u8 [mpad/32, N]).
+ *   xcol_q/_s   X from mxgg_quantize_colwise_segpad: [K, mpad] operand
+ *               (MX scales u8 [mpad/32, K]).
  *   fmt         MXGG_MXFP4 (pad 32) or MXGG_FP8_1x128 (pad 128).
  *   mpad        mxgg_segpad_rows(m_splits, G, fmt).
  *   main_grad   [G, N, K]: fp32 when out_is_bf16 == 0, else bf16.

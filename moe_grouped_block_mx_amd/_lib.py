@@ -153,7 +153,7 @@ def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=None, q=None, scales=None):
         q = torch.empty((rows, cols // 2 if f == MXFP4 else cols), dtype=torch.uint8, device=x.device)
     if scales is None:
         if f in (MXFP4, MXFP8):
-            scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+            scales = torch.empty((cols // 32, rows), dtype=torch.uint8, device=x.device)  # block-major
         elif f == FP8_1x128:
             scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
         else:
@@ -180,7 +180,7 @@ def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=None, q=None, s
         if f == FP8_1x128:
             scales = torch.empty((cols, mpad // 128), dtype=torch.float32, device=x.device)
         else:
-            scales = torch.empty((cols, mpad // 32), dtype=torch.uint8, device=x.device)
+            scales = torch.empty((mpad // 32, cols), dtype=torch.uint8, device=x.device)  # block-major
     _check(lib.mxgg_quantize_colwise_segpad(_ptr(x), rows, cols, _ld(x), arr, G, f, flags, _ptr(q),
                                             _ptr(scales), mpad, _stream(x)))
     return q, scales, mpad

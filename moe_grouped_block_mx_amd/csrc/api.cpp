@@ -232,11 +232,11 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
   p.bs = static_cast<const uint8_t*>(w_s);
   p.c = static_cast<uint16_t*>(out);
   p.lda = a8 ? K : K / 2;
-  p.ldas = K / 32;
+  p.ldas = M;                     // A scales [K/32, M]
   p.ldb = K / 2;
-  p.ldbs = K / 32;
+  p.ldbs = (int64_t)G * N;        // W scales [K/32, G*N]
   p.b_gstride = N * (K / 2);
-  p.bs_gstride = N * (K / 32);
+  p.bs_gstride = N;               // expert g's rows start at g*N
   p.ldc = N;
   p.n_out = (int32_t)N;
   p.kc = (int32_t)K;
@@ -264,11 +264,11 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
   p.bs = static_cast<const uint8_t*>(wcol_s);
   p.c = static_cast<uint16_t*>(dx);
   p.lda = N / 2;
-  p.ldas = N / 32;
+  p.ldas = M;                     // dY scales [N/32, M]
   p.ldb = (int64_t)G * N / 2;     // W column-wise: [K, G*N/2]
-  p.ldbs = (int64_t)G * N / 32;
+  p.ldbs = K;                     // its scales [G*N/32, K]
   p.b_gstride = N / 2;            // expert g owns columns [g*N, (g+1)*N)
-  p.bs_gstride = N / 32;
+  p.bs_gstride = N / 32 * K;      // ... and scale blocks [g*N/32, (g+1)*N/32)
   p.ldc = K;
   p.n_out = (int32_t)K;
   p.kc = (int32_t)N;
@@ -298,10 +298,10 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
   p.b = static_cast<const uint8_t*>(xcol_q);
   p.bs = static_cast<const uint8_t*>(xcol_s);
   p.c = main_grad;
-  p.lda = blk ? mpad : mpad / 2;               // E4M3 / E2M1 bytes
-  p.ldas = blk ? mpad / 128 * 4 : mpad / 32;    // f32 per 128 / UE8M0 per 32
+  p.lda = blk ? mpad : mpad / 2;                // E4M3 / E2M1 bytes
   p.ldb = p.lda;
-  p.ldbs = p.ldas;
+  p.ldas = blk ? mpad / 128 * 4 : N;             // f32 [N, mpad/128] / u8 [mpad/32, N]
+  p.ldbs = blk ? mpad / 128 * 4 : K;             // f32 [K, mpad/128] / u8 [mpad/32, K]
   p.n_rows = (int32_t)N;
   p.n_cols = (int32_t)K;
   p.accumulate = accumulate;

@@ -135,19 +135,11 @@ struct TileCfg {
   static_assert(DPS * (STAGES - 2) < 64, "vmcnt range");
 };
 
-// Scale dword position p inside a row's stage -> K block. With two K steps per
-// stage the row is stored as blocks [0, 2, 1, 3], so the lane half h reads the
-// adjacent dwords (2h, 2h+1) = blocks (h, 2+h), i.e. K step 0 and 1.
-template <class C>
-__device__ __forceinline__ int scale_block_of(int p) {
-  if constexpr (C::SB == 4) return (p & 1) * 2 + (p >> 1);
-  else return p;
-}
-
 // Operand bases and extents of one tile.
 struct TileOps {
   const uint8_t* a;   // first row of the A tile (row stride lda)
-  const uint8_t* as;  // its scales (row stride ldas)
+  const uint8_t* as;  // its scales: MX, block-major (block stride ldas, row
+                      // stride 1); blockwise, row-major (row stride ldas)
   const uint8_t* b;
   const uint8_t* bs;
   int mrows, nrows;   // valid rows of A and B (>= 1)
@@ -160,7 +152,7 @@ template <class C>
 struct DmaPlan {
   uint32_t offA[C::DA], offB[C::DB], offAS[C::DSA], offBS[C::DSB];
   int kA[C::DA], kB[C::DB];       // byte offset of the chunk inside a stage row
-  int bAS[C::DSA], bBS[C::DSB];   // K block inside a stage
+  int bAS[C::DSA], bBS[C::DSB];   // K block inside a stage (MX: wave-uniform)
 };
 
 template <class C>
@@ -184,38 +176,50 @@ __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64
     pl.offB[i] = (uint32_t)(rr * ldb) + c * 16;
     pl.kB[i] = c * 16;
   });
+  // Scale dwords. MX: the stage's SB blocks x rows, block-major like the
+  // global layout, so one DMA instruction reads 64 consecutive scale bytes of
+  // one block (d < BM*SB, and 64 divides BM, so the block is wave-uniform).
+  // Blockwise: one fp32 per row of the stage's 128-element block.
   unroll<C::DSA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const int d = (i * C::NW + w) * 64 + lane;
-    const int r = d / C::SB;
-    const int blk = scale_block_of<C>(d % C::SB);
-    const int rr = r < t.mrows ? r : t.mrows - 1;
-    pl.offAS[i] = (uint32_t)(rr * ldas) + blk;
-    pl.bAS[i] = blk;
+    if constexpr (C::BLK) {
+      const int rr = d < t.mrows ? d : t.mrows - 1;
+      pl.offAS[i] = (uint32_t)(rr * ldas);
+      pl.bAS[i] = 0;
+    } else {
+      const int r = d % C::BM;
+      pl.offAS[i] = (uint32_t)(r < t.mrows ? r : t.mrows - 1);
+      pl.bAS[i] = __builtin_amdgcn_readfirstlane(d / C::BM);
+    }
   });
   unroll<C::DSB>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const int d = (i * C::NW + w) * 64 + lane;
-    const int r = d / C::SB;
-    const int blk = scale_block_of<C>(d % C::SB);
-    const int rr = r < t.nrows ? r : t.nrows - 1;
-    pl.offBS[i] = (uint32_t)((rr / C::BDIV) * ldbs) + blk;
-    pl.bBS[i] = blk;
+    if constexpr (C::BLK) {
+      const int rr = d < t.nrows ? d : t.nrows - 1;
+      pl.offBS[i] = (uint32_t)((rr / C::BDIV) * ldbs);
+      pl.bBS[i] = 0;
+    } else {
+      const int r = d % C::BN;
+      pl.offBS[i] = (uint32_t)(r < t.nrows ? r : t.nrows - 1);
+      pl.bBS[i] = __builtin_amdgcn_readfirstlane(d / C::BN);
+    }
   });
 }
 
 // Issue the DMAs of stage s of tile t into ring slot `st` (every wave issues
 // exactly DPS instructions, the count the waits rely on).
 template <class C>
-__device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps& t, int s, uint8_t* st, int w) {
+__device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps& t, int s, uint8_t* st, int w,
+                                            int64_t ldas, int64_t ldbs) {
   const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_zero_page);
   const int kca = C::AFP8 ? t.kc : t.kc / 2;
   const int kcb = C::BFP8 ? t.kc : t.kc / 2;
   const int ka0 = s * C::RBA, kb0 = s * C::RBB;
-  // scale bytes of this stage: MX, SB bytes per row from s * SB (blocks of 32
-  // past the contraction read zeros); blockwise, the fp32 of 128-block s*BK/128
+  // scales of this stage: MX, blocks s*SB .. s*SB+SB-1 (blocks past the
+  // contraction read zeros); blockwise, the fp32 of 128-block s*BK/128
   const int nblk = C::BLK ? t.kc / 128 : t.kc / 32;
-  const int blk0 = C::BLK ? (s * C::BK / 128) * 4 : s * C::SB;
   const int bidx0 = C::BLK ? s * C::BK / 128 : s * C::SB;
   unroll<C::DA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
@@ -229,15 +233,21 @@ __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps&
   });
   unroll<C::DSA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    const uint8_t* src = (bidx0 + pl.bAS[i] < nblk) ? t.as + pl.offAS[i] + blk0 : zero;
-    if constexpr (C::BLK) dma4(src, st + C::AS_OFF + (i * C::NW + w) * 256);
-    else dma1(src, st + C::AS_OFF + (i * C::NW + w) * 256);
+    const int b = bidx0 + pl.bAS[i];
+    if constexpr (C::BLK) {
+      dma4(b < nblk ? t.as + pl.offAS[i] + b * 4 : zero, st + C::AS_OFF + (i * C::NW + w) * 256);
+    } else {
+      dma1(b < nblk ? t.as + (int64_t)b * ldas + pl.offAS[i] : zero, st + C::AS_OFF + (i * C::NW + w) * 256);
+    }
   });
   unroll<C::DSB>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    const uint8_t* src = (bidx0 + pl.bBS[i] < nblk) ? t.bs + pl.offBS[i] + blk0 : zero;
-    if constexpr (C::BLK) dma4(src, st + C::BS_OFF + (i * C::NW + w) * 256);
-    else dma1(src, st + C::BS_OFF + (i * C::NW + w) * 256);
+    const int b = bidx0 + pl.bBS[i];
+    if constexpr (C::BLK) {
+      dma4(b < nblk ? t.bs + pl.offBS[i] + b * 4 : zero, st + C::BS_OFF + (i * C::NW + w) * 256);
+    } else {
+      dma1(b < nblk ? t.bs + (int64_t)b * ldbs + pl.offBS[i] : zero, st + C::BS_OFF + (i * C::NW + w) * 256);
+    }
   });
 }
 
@@ -321,15 +331,16 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::
   unroll<C::FM>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const int r = wm * C::WTM + i * 32 + l32;
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(st + C::AS_OFF) + r * C::SB + h * C::KSTEPS;
-    if constexpr (C::KSTEPS == 2) sa[i] = p[0] | (p[1] << 8);
+    // lane half h takes block h of K step 0 (op_sel 0) and block 2+h of K step 1 (op_sel 1)
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(st + C::AS_OFF) + h * C::BM + r;
+    if constexpr (C::KSTEPS == 2) sa[i] = p[0] | (p[2 * C::BM] << 8);
     else sa[i] = p[0];
   });
   unroll<C::FN>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     const int r = wn * C::WTN + j * 32 + l32;
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(st + C::BS_OFF) + r * C::SB + h * C::KSTEPS;
-    if constexpr (C::KSTEPS == 2) sb[j] = p[0] | (p[1] << 8);
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(st + C::BS_OFF) + h * C::BN + r;
+    if constexpr (C::KSTEPS == 2) sb[j] = p[0] | (p[2 * C::BN] << 8);
     else sb[j] = p[0];
   });
   unroll<C::KSTEPS>([&](auto kc_) {
@@ -428,7 +439,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
   };
   auto issue_one = [&]() -> int {
     if (it >= total) return 0;
-    issue_stage<C>(plan, iops, is, smem + slot_issue * C::STAGE_BYTES, w);
+    issue_stage<C>(plan, iops, is, smem + slot_issue * C::STAGE_BYTES, w, ldas, ldbs);
     slot_issue = slot_issue + 1 == C::STAGES ? 0 : slot_issue + 1;
     if (++is == ins) {
       is = 0;
@@ -533,9 +544,10 @@ struct RowsSource {
     const int nleft = p.n_out - col0;
     TileOps o;
     o.a = p.a + row0 * p.lda;
-    o.as = p.as + row0 * p.ldas;
+    // MX scales are block-major ([blocks, rows]); blockwise scales row-major
+    o.as = p.as + (C::BLK ? row0 * p.ldas : row0);
     o.b = p.b + (int64_t)q.g * p.b_gstride + (int64_t)col0 * p.ldb;
-    o.bs = p.bs + (int64_t)q.g * p.bs_gstride + (int64_t)(col0 / C::BDIV) * p.ldbs;
+    o.bs = p.bs + (int64_t)q.g * p.bs_gstride + (C::BLK ? (int64_t)(col0 / C::BDIV) * p.ldbs : (int64_t)col0);
     o.mrows = mleft < C::BM ? mleft : C::BM;
     o.nrows = nleft < C::BN ? nleft : C::BN;
     o.kc = p.kc;
@@ -611,13 +623,17 @@ struct WgradSource {
   __device__ __forceinline__ TileOps ops(int t) const {
     const Pos q = pos(t);
     TileOps o;
-    // segment start: element bytes (E4M3: 1, E2M1: 1/2) and scale bytes
-    // (MX: one per 32; blockwise: one fp32 per 128)
-    const int64_t sc0 = C::BLK ? q.p0 / 128 * 4 : q.p0 / 32;
+    // segment start: element bytes (E4M3: 1, E2M1: 1/2); scales, MX
+    // block-major (block p0/32, row row0), blockwise row-major (fp32 p0/128)
     o.a = p.a + (int64_t)q.row0 * p.lda + (C::AFP8 ? q.p0 : q.p0 / 2);
-    o.as = p.as + (int64_t)q.row0 * p.ldas + sc0;
     o.b = p.b + (int64_t)q.col0 * p.ldb + (C::BFP8 ? q.p0 : q.p0 / 2);
-    o.bs = p.bs + (int64_t)q.col0 * p.ldbs + sc0;
+    if constexpr (C::BLK) {
+      o.as = p.as + (int64_t)q.row0 * p.ldas + q.p0 / 128 * 4;
+      o.bs = p.bs + (int64_t)q.col0 * p.ldbs + q.p0 / 128 * 4;
+    } else {
+      o.as = p.as + q.p0 / 32 * p.ldas + q.row0;
+      o.bs = p.bs + q.p0 / 32 * p.ldbs + q.col0;
+    }
     const int rl = p.n_rows - q.row0, cl = p.n_cols - q.col0;
     o.mrows = rl < C::BM ? rl : C::BM;
     o.nrows = cl < C::BN ? cl : C::BN;

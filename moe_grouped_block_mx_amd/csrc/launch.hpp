@@ -17,8 +17,10 @@ struct RowsGemmParams {
   const uint8_t* b;
   const uint8_t* bs;
   uint16_t* c;            // bf16 output
-  int64_t lda, ldas;      // A data / scale row strides (bytes)
-  int64_t ldb, ldbs;      // B data / scale row strides (bytes)
+  int64_t lda, ldb;       // A / B data row strides (bytes)
+  int64_t ldas, ldbs;     // scale strides (bytes): MX scales are block-major
+                          // [blocks, rows] (ld = the block stride); blockwise
+                          // fp32 scales are row-major (ld = the row stride)
   int64_t b_gstride;      // bytes between consecutive experts' B data
   int64_t bs_gstride;     // bytes between consecutive experts' B scales
   int64_t ldc;            // output row stride (elements)
@@ -35,7 +37,7 @@ struct WgradParams {
   const uint8_t* b;       // [n_cols, mpad] operand (X column-wise)
   const uint8_t* bs;
   void* c;                // [G, n_rows, n_cols] fp32 (or bf16)
-  int64_t lda, ldas, ldb, ldbs;
+  int64_t lda, ldas, ldb, ldbs;  // as in RowsGemmParams
   int32_t n_rows, n_cols;
   int32_t accumulate;
   int32_t out_bf16;

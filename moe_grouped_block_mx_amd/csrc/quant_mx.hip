@@ -1,7 +1,8 @@
 // MX quantizers (E2M1 / E4M3 elements, UE8M0 scale per 32 elements) for gfx950.
 //
 // Row-wise: the row operand of "Triton mxfp4 (and a8w4) grouped GEMM kernel"
-// (data [rows, cols/2] or [rows, cols], scales [rows, cols/32]).
+// (data [rows, cols/2] or [rows, cols]; scales block-major [cols/32, rows], so
+// a GEMM stage reads the scales of consecutive rows contiguously).
 // Column-wise, segment-padded: the padded column operand of the variable-K
 // weight gradient on the same page (each expert's rows transposed, blocks of 32
 // starting at the segment start, zeros past the segment end).
@@ -41,7 +42,6 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
   const int c = blockIdx.x * 64 + lane;  // chunk inside the row
   const bool cvalid = c < cpr;
   const int64_t qrow_bytes = FP4 ? (int64_t)cpr * 4 : (int64_t)cpr * 8;
-  const int64_t srow_bytes = cpr / 4;
   for (int rb = blockIdx.y * (4 * U); rb < rows; rb += gridDim.y * (4 * U)) {
     uint4 v[U];
 #pragma unroll
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
         *reinterpret_cast<uint2*>(q + (int64_t)r * qrow_bytes + (int64_t)c * 8) =
             make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
       }
-      if ((c & 3) == 0) s[(int64_t)r * srow_bytes + (c >> 2)] = (uint8_t)(e + 127);
+      if ((c & 3) == 0) s[(int64_t)(c >> 2) * rows + r] = (uint8_t)(e + 127);  // block-major
     }
   }
 }
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void quant_colwise_segpad_kernel(const uint16_
     reinterpret_cast<uint4*>(qp)[0] = make_uint4(a[0], a[1], a[2], a[3]);
     reinterpret_cast<uint4*>(qp)[1] = make_uint4(a[4], a[5], a[6], a[7]);
   }
-  s[(c0 + c) * (mpad / 32) + p0 / 32] = (uint8_t)(e + 127);
+  s[(p0 / 32) * cols + c0 + c] = (uint8_t)(e + 127);  // block-major: [mpad/32, cols]
 }
 
 // ---------------------------------------------------------------------------

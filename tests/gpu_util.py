@@ -26,6 +26,12 @@ def host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+def mx_scales_rowmajor(t) -> np.ndarray:
+    """The library stores MX scales block-major, u8 [blocks, rows]; the oracle
+    row-major, [rows, blocks]. A pure layout permutation."""
+    return np.ascontiguousarray(host(t).T)
+
+
 def host_bf16_f64(t) -> np.ndarray:
     return bf16_bits_to_f64(t.detach().view(torch.int16).cpu().numpy().view(np.uint16))
 
