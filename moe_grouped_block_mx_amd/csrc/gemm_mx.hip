@@ -131,7 +131,7 @@ struct TileCfg {
   static_assert(A_BYTES % (NW * 1024) == 0 && B_BYTES % (NW * 1024) == 0, "chunk DMA split");
   static_assert(KSTEPS == 1 || KSTEPS == 2, "K steps per stage");
   static_assert(!BLK || BK == 64 || BK == 128, "blockwise stages split a 128-element scale block");
-  static_assert(FM >= 1 && FN >= 1 && STAGES >= 2 && STAGES <= 4, "shape");
+  static_assert(FM >= 1 && FN >= 1 && STAGES >= 2 && STAGES <= 8, "shape");
   static_assert(DPS * (STAGES - 2) < 64, "vmcnt range");
 };
 
@@ -393,15 +393,20 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::
 
 // Wait until this wave's DMAs of the stage about to be consumed have landed,
 // given how many stages it issued after that one (DPS instructions each).
+template <class C, int K>
+__device__ __forceinline__ bool wait_if_after(int stages_after) {
+  if (K > 0 && stages_after < K) return false;  // K = 0: wait for everything
+  wait_vmcnt<K * C::DPS>();
+  return true;
+}
+template <class C, int... Ks>
+__device__ __forceinline__ void wait_stage_impl(int stages_after, std::integer_sequence<int, Ks...>) {
+  // largest K first: at most STAGES-2 stages can follow the one awaited
+  (void)(wait_if_after<C, C::STAGES - 2 - Ks>(stages_after) || ...);
+}
 template <class C>
 __device__ __forceinline__ void wait_stage(int stages_after) {
-  if constexpr (C::STAGES >= 4) {
-    if (stages_after >= 2) { wait_vmcnt<2 * C::DPS>(); return; }
-  }
-  if constexpr (C::STAGES >= 3) {
-    if (stages_after >= 1) { wait_vmcnt<C::DPS>(); return; }
-  }
-  wait_vmcnt<0>();
+  wait_stage_impl<C>(stages_after, std::make_integer_sequence<int, C::STAGES - 1>{});
 }
 
 // The pipelined persistent loop shared by all passes.
@@ -481,6 +486,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
     }
     src.epilogue(ct, acc, scratch, w, lane);
   }
+  wait_vmcnt<0>();  // no DMA of this workgroup outlives it (every issued stage was waited for; kept explicit)
 }
 
 // ---------------------------------------------------------------------------

@@ -30,7 +30,9 @@ __device__ __forceinline__ v2bf16 as_bf16x2(uint32_t w) { return __builtin_bit_c
 // Row-wise. A wave owns 64 consecutive 16-byte chunks (8 elements each) of one
 // row, so every load instruction reads 1 KiB contiguous; 4 consecutive lanes
 // hold one 32-element block and reduce amax with two xor-shuffles. Each thread
-// keeps U rows' loads in flight before encoding (memory-level parallelism).
+// keeps U = 4 consecutive rows' loads in flight before encoding (memory-level
+// parallelism), so the four scale bytes of a block's rows are adjacent in the
+// block-major scale layout and go out as one 4-byte store.
 // Grid: x over 64-chunk column groups, y over 4*U-row groups (grid-strided).
 // ---------------------------------------------------------------------------
 template <class F, int U>
@@ -42,17 +44,19 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
   const int c = blockIdx.x * 64 + lane;  // chunk inside the row
   const bool cvalid = c < cpr;
   const int64_t qrow_bytes = FP4 ? (int64_t)cpr * 4 : (int64_t)cpr * 8;
+  static_assert(U == 4, "four rows per thread: one 4-byte scale store");
   for (int rb = blockIdx.y * (4 * U); rb < rows; rb += gridDim.y * (4 * U)) {
     uint4 v[U];
+    uint32_t sbytes = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = rb + u * 4 + w;
+      const int r = rb + w * U + u;
       v[u] = (cvalid && r < rows) ? *reinterpret_cast<const uint4*>(x + (int64_t)r * ldx + (int64_t)c * 8)
                                   : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = rb + u * 4 + w;
+      const int r = rb + w * U + u;
       const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       uint32_t amax = 0;
 #pragma unroll
@@ -79,8 +83,14 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
         *reinterpret_cast<uint2*>(q + (int64_t)r * qrow_bytes + (int64_t)c * 8) =
             make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
       }
-      if ((c & 3) == 0) s[(int64_t)(c >> 2) * rows + r] = (uint8_t)(e + 127);  // block-major
+      sbytes |= (uint32_t)(e + 127) << (8 * u);
+      if ((c & 3) == 0 && ((rows & 3) != 0 || rb + w * U + U > rows))
+        s[(int64_t)(c >> 2) * rows + r] = (uint8_t)(e + 127);  // ragged row count: one byte per row
     }
+    // block-major scales [cols/32, rows]: the thread's four rows are adjacent
+    const int r0 = rb + w * U;
+    if (cvalid && (c & 3) == 0 && (rows & 3) == 0 && r0 + U <= rows)
+      *reinterpret_cast<uint32_t*>(s + (int64_t)(c >> 2) * rows + r0) = sbytes;
   }
 }
 
