@@ -240,11 +240,13 @@ def build_workload(name, dev):
         a, w, dy = normal((M, K)), normal((G * N, K), wl["w_std"]), normal((M, N))
         main_grad = torch.randn((G, N, K), generator=gen, device=dev, dtype=torch.float32)
         mpad = mxg.segpad_rows(sp, "mxfp4")
-        # MX scales are block-major: [blocks of 32 along the contraction, rows]
-        aq, as_ = torch.empty((M, K // 2), **u8), torch.empty((K // 32, M), **u8)
+        # MX scales are block-major: [blocks of 32 along the contraction, rows
+        # rounded up to a multiple of 4]
+        R4 = mxg.mx_scale_stride(M)
+        aq, as_ = torch.empty((M, K // 2), **u8), torch.empty((K // 32, R4), **u8)
         wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty((K // 32, G * N), **u8)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        dq, ds = torch.empty((M, N // 2), **u8), torch.empty((N // 32, M), **u8)
+        dq, ds = torch.empty((M, N // 2), **u8), torch.empty((N // 32, R4), **u8)
         wcq, wcs = torch.empty((K, G * N // 2), **u8), torch.empty((G * N // 32, K), **u8)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         dcq, dcs = torch.empty((N, mpad // 2), **u8), torch.empty((mpad // 32, N), **u8)
@@ -284,7 +286,7 @@ def build_workload(name, dev):
         G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
         sp = splits_for("a8w4")
         a, w = normal((M, K)), normal((G * N, K), wl["w_std"])
-        aq, as_ = torch.empty((M, K), **u8), torch.empty((K // 32, M), **u8)
+        aq, as_ = torch.empty((M, K), **u8), torch.empty((K // 32, mxg.mx_scale_stride(M)), **u8)
         wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty((K // 32, G * N), **u8)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         ops = [

@@ -26,12 +26,14 @@
  *    accumulation, and the rule that every output element is owned by exactly
  *    one tile (no wrapped tail tiles).
  *
- * MX scale layout: block-major. The UE8M0 scales of an operand with R rows
- * and B blocks of 32 along its contraction axis are stored as u8 [B, R]: the
- * scale of row r, block b is byte b*R + r (the page on hipBLASLt MXFP4 support
- * describes pre-arranged scale layouts; this one lets a GEMM stage read the
- * scales of consecutive rows contiguously). Blockwise fp32 scales are
- * row-major as listed below.
+ * MX scale layout: block-major with a padded block stride. The UE8M0 scales
+ * of an operand with R rows and B blocks of 32 along its contraction axis are
+ * stored as u8 [B, R4], R4 = mxgg_mx_scale_stride(R) = R rounded up to a
+ * multiple of 4: the scale of row r, block b is byte b*R4 + r; the padding
+ * rows hold 0 as written by the quantizers and are never used (the page on
+ * hipBLASLt MXFP4 support describes pre-arranged scale layouts; this one lets
+ * a GEMM stage move the scales of four consecutive rows with one aligned
+ * 4-byte load). Blockwise fp32 scales are row-major as listed below.
  *
  * Formats (OCP MX v1.0 and OCP FP8):
  *   MXGG_MXFP4        E2M1 elements, 2 per byte (even element in bits 3:0),
@@ -114,6 +116,12 @@ typedef enum mxgg_format {
 #define MXGG_MAX_EXPERTS 512
 
 /*
+ * Block stride, in bytes, of the block-major MX scales of an operand with
+ * `rows` rows: rows rounded up to a multiple of 4 (0 for rows <= 0).
+ */
+int64_t mxgg_mx_scale_stride(int64_t rows);
+
+/*
  * Row-wise quantization ("Triton mxfp4 (and a8w4) grouped GEMM kernel", the
  * row operand; blockwise formats from "Add ROCm Triton blockwise FP8 grouped
  * GEMM").
@@ -124,7 +132,8 @@ typedef enum mxgg_format {
  *           MXGG_FP8_128x128: 128x128 blocks (rows % 128 == 0, cols % 128 == 0).
  *   flags   MXGG_POW2_SCALES for the blockwise formats (ignored for MX).
  *   q       MXFP4: u8 [rows, cols/2]; otherwise u8 [rows, cols] (E4M3 codes).
- *   scales  MX: u8 [cols/32, rows] (block-major); FP8_1x128: f32 [rows, cols/128];
+ *   scales  MX: u8 [cols/32, R4] (block-major, R4 = mxgg_mx_scale_stride(rows));
+ *           FP8_1x128: f32 [rows, cols/128];
  *           FP8_128x128: f32 [rows/128, cols/128].
  * rows == 0 returns MXGG_OK with no launch. Errors: NULL, SHAPE, FORMAT,
  * ALIGN, DEVICE, ARCH, HIP.
@@ -147,7 +156,8 @@ mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int
  *   m_splits host int64 [G], 1 <= G <= 512, each >= 0.
  *   fmt      MXGG_MXFP4, MXGG_MXFP8 or MXGG_FP8_1x128; cols % 32 == 0.
  *   q        MXFP4: u8 [cols, mpad/2]; otherwise u8 [cols, mpad].
- *   scales   MX: u8 [mpad/32, cols] (block-major); FP8_1x128: f32 [cols, mpad/128].
+ *   scales   MX: u8 [mpad/32, cols] (block-major; cols % 32 == 0, so R4 == cols);
+ *            FP8_1x128: f32 [cols, mpad/128].
  *   mpad     must equal mxgg_segpad_rows(m_splits, G, fmt).
  * Padding positions hold zero codes. rows == 0 returns MXGG_OK (no launch).
  * Errors: NULL, SHAPE, SPLITS, FORMAT, ALIGN, DEVICE, ARCH, HIP.
@@ -161,7 +171,8 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
  * Grouped forward, TN: out[r, n] = sum_k A[r, k] * W_g[n, k] for every row r
  * of expert g (rows of expert g are consecutive, in expert order).
  *   a_q, a_s  A quantized row-wise along K: (MXFP4: u8 [M, K/2] | MXFP8: u8 [M, K])
- *             + u8 [K/32, M]; or MXGG_FP8_1x128: u8 [M, K] + f32 [M, K/128].
+ *             + u8 [K/32, mxgg_mx_scale_stride(M)]; or MXGG_FP8_1x128: u8 [M, K]
+ *             + f32 [M, K/128].
  *   w_q, w_s  packed expert weights [G*N, K] quantized row-wise along K:
  *             MXFP4 u8 [G*N, K/2] + u8 [K/32, G*N]; or MXGG_FP8_128x128:
  *             u8 [G*N, K] + f32 [G*N/128, K/128].
@@ -183,7 +194,8 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
 
 /*
  * Grouped input gradient, NN: dx[r, k] = sum_n dY[r, n] * W_g[n, k].
- *   dy_q, dy_s     dY quantized row-wise along N: u8 [M, N/2] + u8 [N/32, M].
+ *   dy_q, dy_s     dY quantized row-wise along N: u8 [M, N/2] +
+ *                  u8 [N/32, mxgg_mx_scale_stride(M)].
  *   wcol_q, wcol_s W quantized along N with mxgg_quantize_colwise_segpad on
  *                  W as [G*N, K] with splits {N, ..., N}: u8 [K, G*N/2] +
  *                  u8 [G*N/32, K] (expert g owns columns [g*N, (g+1)*N) and

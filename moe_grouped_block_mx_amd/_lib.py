@@ -54,7 +54,7 @@ def _load():
     # binds to libamdhip64.so (it links that same runtime)
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m moe_grouped_block_mx_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python moe_grouped_block_mx_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, args in _SIGS.items():
         fn = getattr(lib, name)
@@ -64,6 +64,8 @@ def _load():
     lib.mxgg_workspace_size.restype = _sz
     lib.mxgg_segpad_rows.argtypes = [_i64p, _i32, _i32]
     lib.mxgg_segpad_rows.restype = _i64
+    lib.mxgg_mx_scale_stride.argtypes = [_i64]
+    lib.mxgg_mx_scale_stride.restype = _i64
     lib.mxgg_status_string.argtypes = [_i32]
     lib.mxgg_status_string.restype = ctypes.c_char_p
     lib.mxgg_last_error.argtypes = []
@@ -141,6 +143,11 @@ def _flags(flags, f):
     return int(flags)
 
 
+def mxgg_mx_scale_stride(rows):
+    """Block stride (bytes) of block-major MX scales of an operand with `rows` rows."""
+    return int(lib.mxgg_mx_scale_stride(int(rows)))
+
+
 def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=None, q=None, scales=None):
     """x: bf16 [rows, cols] (row stride may exceed cols). Returns (q, scales).
     flags: None = default (MXGG_POW2_SCALES for the blockwise formats)."""
@@ -153,7 +160,8 @@ def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=None, q=None, scales=None):
         q = torch.empty((rows, cols // 2 if f == MXFP4 else cols), dtype=torch.uint8, device=x.device)
     if scales is None:
         if f in (MXFP4, MXFP8):
-            scales = torch.empty((cols // 32, rows), dtype=torch.uint8, device=x.device)  # block-major
+            # block-major, block stride = rows rounded up to a multiple of 4
+            scales = torch.empty((cols // 32, mxgg_mx_scale_stride(rows)), dtype=torch.uint8, device=x.device)
         elif f == FP8_1x128:
             scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
         else:
@@ -233,3 +241,4 @@ grouped_dgrad = mxgg_grouped_dgrad
 grouped_wgrad = mxgg_grouped_wgrad
 workspace_size = mxgg_workspace_size
 segpad_rows = mxgg_segpad_rows
+mx_scale_stride = mxgg_mx_scale_stride

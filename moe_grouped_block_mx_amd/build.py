@@ -1,6 +1,7 @@
 """Build libmxgg.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Usage: python -m moe_grouped_block_mx_amd.build [--jobs N] [--verbose]
+Usage: python moe_grouped_block_mx_amd/build.py [--jobs N] [--verbose]
+(runs without importing the package, which loads the library)
 """
 from __future__ import annotations
 

@@ -151,6 +151,8 @@ int64_t mxgg_segpad_rows(const int64_t* m_splits, int32_t G, mxgg_format fmt) {
   return segpad_rows(m_splits, G, segpad_multiple(fmt));
 }
 
+int64_t mxgg_mx_scale_stride(int64_t rows) { return mx_scale_stride(rows); }
+
 mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, mxgg_format fmt,
                                   uint32_t flags, void* q, void* scales, hipStream_t stream) {
   Check c = validate_quantize_rowwise(x, rows, cols, ldx, (int)fmt, q, scales);
@@ -232,7 +234,7 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
   p.bs = static_cast<const uint8_t*>(w_s);
   p.c = static_cast<uint16_t*>(out);
   p.lda = a8 ? K : K / 2;
-  p.ldas = M;                     // A scales [K/32, M]
+  p.ldas = mx_scale_stride(M);    // A scales [K/32, R4(M)]
   p.ldb = K / 2;
   p.ldbs = (int64_t)G * N;        // W scales [K/32, G*N]
   p.b_gstride = N * (K / 2);
@@ -264,7 +266,7 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
   p.bs = static_cast<const uint8_t*>(wcol_s);
   p.c = static_cast<uint16_t*>(dx);
   p.lda = N / 2;
-  p.ldas = M;                     // dY scales [N/32, M]
+  p.ldas = mx_scale_stride(M);    // dY scales [N/32, R4(M)]
   p.ldb = (int64_t)G * N / 2;     // W column-wise: [K, G*N/2]
   p.ldbs = K;                     // its scales [G*N/32, K]
   p.b_gstride = N / 2;            // expert g owns columns [g*N, (g+1)*N)

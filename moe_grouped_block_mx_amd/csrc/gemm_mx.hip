@@ -108,22 +108,29 @@ struct TileCfg {
   static constexpr int RBB = BFP8 ? BK : BK / 2;  // B bytes per row per stage
   static constexpr int CPA = RBA / 16, CPB = RBB / 16;
   static constexpr int KSTEPS = BK / 64;          // MFMA K steps per stage
-  static constexpr int SB = BLK ? 1 : BK / 32;    // scale dwords per row per stage
+  static constexpr int SB = BLK ? 1 : BK / 32;    // scale values per row per stage
   static constexpr int PROMO = BLK ? 128 / BK : 1;  // stages per 128-element scale block (blockwise)
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int round_up(int v, int m) { return (v + m - 1) / m * m; }
-  // one ring stage: A chunks, B chunks, A scale dwords, B scale dwords (the
-  // scale regions are rounded up to whole DMA instructions; the extra dwords
-  // hold repeats of the last row)
+  // One ring stage: A chunks, B chunks, then the scales.
+  //   MX: bytes, block-major like the global layout: A [SB][BM], then B
+  //   [SB][BN]; one DMA lane moves four consecutive rows of one block, and the
+  //   region is rounded up to whole DMA instructions over all waves (the extra
+  //   lanes read the zero page into the padding).
+  //   Blockwise: one fp32 per row (A region, then B region, each rounded up to
+  //   whole instructions; the extra dwords hold repeats of the last row).
   static constexpr int A_OFF = 0, A_BYTES = BM * RBA;
   static constexpr int B_OFF = A_OFF + A_BYTES, B_BYTES = BN * RBB;
-  static constexpr int AS_OFF = B_OFF + B_BYTES, AS_BYTES = round_up(BM * SB * 4, NW * 256);
-  static constexpr int BS_OFF = AS_OFF + AS_BYTES, BS_BYTES = round_up(BN * SB * 4, NW * 256);
+  static constexpr int MXS_BYTES = round_up((BM + BN) * SB, NW * 256);
+  static constexpr int AS_OFF = B_OFF + B_BYTES, AS_BYTES = BLK ? round_up(BM * 4, NW * 256) : BM * SB;
+  static constexpr int BS_OFF = AS_OFF + AS_BYTES, BS_BYTES = BLK ? round_up(BN * 4, NW * 256) : MXS_BYTES - AS_BYTES;
   static constexpr int STAGE_BYTES = BS_OFF + BS_BYTES;
-  // LDS DMA instructions per wave per stage (1 KiB of chunks or 64 scale dwords each)
+  // LDS DMA instructions per wave per stage (1 KiB of chunks, or 256 bytes of
+  // scales: MX, both operands' in DSA; blockwise, A's in DSA and B's in DSB)
   static constexpr int DA = A_BYTES / (NW * 1024), DB = B_BYTES / (NW * 1024);
-  static constexpr int DSA = AS_BYTES / (NW * 256), DSB = BS_BYTES / (NW * 256);
+  static constexpr int DSA = BLK ? AS_BYTES / (NW * 256) : MXS_BYTES / (NW * 256);
+  static constexpr int DSB = BLK ? BS_BYTES / (NW * 256) : 0;
   static constexpr int DPS = DA + DB + DSA + DSB;
   static constexpr int EPI_BYTES = 16 * 36 * 4;  // per-wave epilogue scratch (16 rows x 32 fp32, padded)
   static constexpr int EPI_OFF = STAGES * STAGE_BYTES;
@@ -133,16 +140,21 @@ struct TileCfg {
   static_assert(!BLK || BK == 64 || BK == 128, "blockwise stages split a 128-element scale block");
   static_assert(FM >= 1 && FN >= 1 && STAGES >= 2 && STAGES <= 8, "shape");
   static_assert(DPS * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(BLK || (BM % 4 == 0 && BN % 4 == 0), "MX scale DMA moves four rows per lane");
+  static_assert(STAGE_BYTES % 16 == 0, "stage alignment");
 };
 
 // Operand bases and extents of one tile.
 struct TileOps {
   const uint8_t* a;   // first row of the A tile (row stride lda)
   const uint8_t* as;  // its scales: MX, block-major (block stride ldas, row
-                      // stride 1); blockwise, row-major (row stride ldas)
+                      // stride 1; the tile's first row a multiple of 4);
+                      // blockwise, row-major (row stride ldas)
   const uint8_t* b;
   const uint8_t* bs;
   int mrows, nrows;   // valid rows of A and B (>= 1)
+  int srows_a, srows_b;  // MX: scale rows readable from as / bs in every
+                         // block (a multiple of 4, >= 4)
   int kc;             // contraction length (elements), multiple of 32
 };
 
@@ -152,8 +164,13 @@ template <class C>
 struct DmaPlan {
   uint32_t offA[C::DA], offB[C::DB], offAS[C::DSA], offBS[C::DSB];
   int kA[C::DA], kB[C::DB];       // byte offset of the chunk inside a stage row
-  int bAS[C::DSA], bBS[C::DSB];   // K block inside a stage (MX: wave-uniform)
+  // MX scales: per lane, the row offset of its four rows and its block inside
+  // a stage (kNoBlock: padding); the operand of an instruction is
+  // wave-uniform (A's and B's regions are whole instructions)
+  uint32_t sOff[C::BLK ? 1 : C::DSA];
+  int sBlk[C::BLK ? 1 : C::DSA];
 };
+constexpr int kNoBlock = 1 << 24;
 
 template <class C>
 __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64_t lda, int64_t ldas, int64_t ldb,
@@ -176,79 +193,98 @@ __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64
     pl.offB[i] = (uint32_t)(rr * ldb) + c * 16;
     pl.kB[i] = c * 16;
   });
-  // Scale dwords. MX: the stage's SB blocks x rows, block-major like the
-  // global layout, so one DMA instruction reads 64 consecutive scale bytes of
-  // one block (d < BM*SB, and 64 divides BM, so the block is wave-uniform).
+  // Scales. MX: lane word d of the stage's scale region holds four rows of
+  // one block: A's [SB][BM] bytes, then B's [SB][BN], then padding. Rows past
+  // the readable scale rows (which only invalid tile rows reach) read the last
+  // readable group of four, so every read stays inside the buffer.
   // Blockwise: one fp32 per row of the stage's 128-element block.
-  unroll<C::DSA>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    const int d = (i * C::NW + w) * 64 + lane;
-    if constexpr (C::BLK) {
+  if constexpr (C::BLK) {
+    unroll<C::DSA>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int d = (i * C::NW + w) * 64 + lane;
       const int rr = d < t.mrows ? d : t.mrows - 1;
       pl.offAS[i] = (uint32_t)(rr * ldas);
-      pl.bAS[i] = 0;
-    } else {
-      const int r = d % C::BM;
-      pl.offAS[i] = (uint32_t)(r < t.mrows ? r : t.mrows - 1);
-      pl.bAS[i] = __builtin_amdgcn_readfirstlane(d / C::BM);
-    }
-  });
-  unroll<C::DSB>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    const int d = (i * C::NW + w) * 64 + lane;
-    if constexpr (C::BLK) {
+    });
+    unroll<C::DSB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int d = (i * C::NW + w) * 64 + lane;
       const int rr = d < t.nrows ? d : t.nrows - 1;
       pl.offBS[i] = (uint32_t)((rr / C::BDIV) * ldbs);
-      pl.bBS[i] = 0;
-    } else {
-      const int r = d % C::BN;
-      pl.offBS[i] = (uint32_t)(r < t.nrows ? r : t.nrows - 1);
-      pl.bBS[i] = __builtin_amdgcn_readfirstlane(d / C::BN);
-    }
-  });
+    });
+  } else {
+    unroll<C::DSA>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int byte = ((i * C::NW + w) * 64 + lane) * 4;
+      if (byte < C::BM * C::SB) {
+        const int r = byte % C::BM;
+        pl.sOff[i] = (uint32_t)(r < t.srows_a - 4 ? r : t.srows_a - 4);
+        pl.sBlk[i] = byte / C::BM;
+      } else if (byte < (C::BM + C::BN) * C::SB) {
+        const int bb = byte - C::BM * C::SB;
+        const int r = bb % C::BN;
+        pl.sOff[i] = (uint32_t)(r < t.srows_b - 4 ? r : t.srows_b - 4);
+        pl.sBlk[i] = bb / C::BN;
+      } else {
+        pl.sOff[i] = 0;
+        pl.sBlk[i] = kNoBlock;
+      }
+    });
+  }
 }
 
 // Issue the DMAs of stage s of tile t into ring slot `st` (every wave issues
 // exactly DPS instructions, the count the waits rely on).
+// Pointer select without a branch (the scale-block conditions are uniform,
+// and a uniform branch would split the stage's instruction block).
+__device__ __forceinline__ const uint8_t* select_ptr(bool c, const uint8_t* a, const uint8_t* b) {
+  const uint64_t m = 0 - (uint64_t)c;
+  return reinterpret_cast<const uint8_t*>((reinterpret_cast<uint64_t>(a) & m) | (reinterpret_cast<uint64_t>(b) & ~m));
+}
+
+// A dummy stage (no work left) issues the same instructions from the zero
+// page, so that every step issues exactly DPS DMAs.
 template <class C>
 __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps& t, int s, uint8_t* st, int w,
-                                            int64_t ldas, int64_t ldbs) {
+                                            int64_t ldas, int64_t ldbs, bool dummy = false) {
   const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_zero_page);
-  const int kca = C::AFP8 ? t.kc : t.kc / 2;
-  const int kcb = C::BFP8 ? t.kc : t.kc / 2;
+  const int kca = dummy ? 0 : (C::AFP8 ? t.kc : t.kc / 2);
+  const int kcb = dummy ? 0 : (C::BFP8 ? t.kc : t.kc / 2);
   const int ka0 = s * C::RBA, kb0 = s * C::RBB;
   // scales of this stage: MX, blocks s*SB .. s*SB+SB-1 (blocks past the
-  // contraction read zeros); blockwise, the fp32 of 128-block s*BK/128
-  const int nblk = C::BLK ? t.kc / 128 : t.kc / 32;
+  // contraction and padding lanes read zeros); blockwise, the fp32 of
+  // 128-block s*BK/128
+  const int nblk = dummy ? 0 : (C::BLK ? t.kc / 128 : t.kc / 32);
   const int bidx0 = C::BLK ? s * C::BK / 128 : s * C::SB;
   unroll<C::DA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    const uint8_t* src = (ka0 + pl.kA[i] < kca) ? t.a + pl.offA[i] + ka0 : zero;
+    const uint8_t* src = select_ptr(ka0 + pl.kA[i] < kca, t.a + pl.offA[i] + ka0, zero);
     dma16(src, st + C::A_OFF + (i * C::NW + w) * 1024);
   });
   unroll<C::DB>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    const uint8_t* src = (kb0 + pl.kB[i] < kcb) ? t.b + pl.offB[i] + kb0 : zero;
+    const uint8_t* src = select_ptr(kb0 + pl.kB[i] < kcb, t.b + pl.offB[i] + kb0, zero);
     dma16(src, st + C::B_OFF + (i * C::NW + w) * 1024);
   });
-  unroll<C::DSA>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    const int b = bidx0 + pl.bAS[i];
-    if constexpr (C::BLK) {
-      dma4(b < nblk ? t.as + pl.offAS[i] + b * 4 : zero, st + C::AS_OFF + (i * C::NW + w) * 256);
-    } else {
-      dma1(b < nblk ? t.as + (int64_t)b * ldas + pl.offAS[i] : zero, st + C::AS_OFF + (i * C::NW + w) * 256);
-    }
-  });
-  unroll<C::DSB>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    const int b = bidx0 + pl.bBS[i];
-    if constexpr (C::BLK) {
-      dma4(b < nblk ? t.bs + pl.offBS[i] + b * 4 : zero, st + C::BS_OFF + (i * C::NW + w) * 256);
-    } else {
-      dma1(b < nblk ? t.bs + (int64_t)b * ldbs + pl.offBS[i] : zero, st + C::BS_OFF + (i * C::NW + w) * 256);
-    }
-  });
+  if constexpr (C::BLK) {
+    unroll<C::DSA>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      dma4(select_ptr(bidx0 < nblk, t.as + pl.offAS[i] + bidx0 * 4, zero), st + C::AS_OFF + (i * C::NW + w) * 256);
+    });
+    unroll<C::DSB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      dma4(select_ptr(bidx0 < nblk, t.bs + pl.offBS[i] + bidx0 * 4, zero), st + C::BS_OFF + (i * C::NW + w) * 256);
+    });
+  } else {
+    static_assert((C::BM * C::SB) % 256 == 0 && (C::BN * C::SB) % 256 == 0, "operand regions: whole instructions");
+    unroll<C::DSA>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const bool on_b = (i * C::NW + w) * 256 >= C::BM * C::SB;  // wave-uniform
+      const uint8_t* base = on_b ? t.bs : t.as;
+      const int64_t ld = on_b ? ldbs : ldas;
+      const int b = bidx0 + pl.sBlk[i];
+      dma4(select_ptr(b < nblk, base + (int64_t)b * ld + pl.sOff[i], zero), st + C::AS_OFF + (i * C::NW + w) * 256);
+    });
+  }
 }
 
 // B fragments of K step KK (E2M1: 16 bytes per lane; E4M3: 2 x 16 bytes).
@@ -323,24 +359,28 @@ __device__ __forceinline__ void compute_stage_blk(const uint8_t* st, v16f (&acc)
   }
 }
 
-// MFMAs of one ring stage for this wave's fragments.
-template <class C>
+// MFMAs of one ring stage for this wave's fragments. `issue` issues the DMAs
+// of a later stage; with SCHED 5 they are spread over the last K step's MFMAs.
+struct NoIssue {
+  __device__ __forceinline__ void operator()() const {}
+};
+template <class C, class Issue = NoIssue>
 __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::FM][C::FN], int wm, int wn, int h,
-                                              int l32) {
+                                              int l32, Issue&& issue = Issue{}) {
   uint32_t sa[C::FM], sb[C::FN];
   unroll<C::FM>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const int r = wm * C::WTM + i * 32 + l32;
     // lane half h takes block h of K step 0 (op_sel 0) and block 2+h of K step 1 (op_sel 1)
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(st + C::AS_OFF) + h * C::BM + r;
-    if constexpr (C::KSTEPS == 2) sa[i] = p[0] | (p[2 * C::BM] << 8);
+    const uint8_t* p = st + C::AS_OFF + h * C::BM + r;
+    if constexpr (C::KSTEPS == 2) sa[i] = p[0] | ((uint32_t)p[2 * C::BM] << 8);
     else sa[i] = p[0];
   });
   unroll<C::FN>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     const int r = wn * C::WTN + j * 32 + l32;
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(st + C::BS_OFF) + h * C::BN + r;
-    if constexpr (C::KSTEPS == 2) sb[j] = p[0] | (p[2 * C::BN] << 8);
+    const uint8_t* p = st + C::BS_OFF + h * C::BN + r;
+    if constexpr (C::KSTEPS == 2) sb[j] = p[0] | ((uint32_t)p[2 * C::BN] << 8);
     else sb[j] = p[0];
   });
   unroll<C::KSTEPS>([&](auto kc_) {
@@ -369,25 +409,47 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::
       });
     });
   });
+  // after every LDS read of the stage in program order: the DMAs write LDS
+  // (another slot, which the compiler cannot prove), so reads may not pass them
+  issue();
   // Instruction order of the stage (one basic block):
   //   0: the compiler's choice
   //   1: every LDS read first, then every MFMA
   //   2: the compiler's MFMA/LDS interleaving strategy 0
   //   3: reads of K step 0, then K step 0's MFMAs each followed by one read of
   //      K step 1, then the rest
+  //   5: as 3, and the last K step's MFMAs each followed by one of the DMAs
+  //      issued for a later stage (the address unit drains them while the
+  //      MFMAs run instead of stalling the wave right after the barrier)
   constexpr int NR0 = C::FM * (C::AFP8 ? 2 : 1) + C::FN * (C::BFP8 ? 2 : 1);  // fragment reads per K step
+  constexpr int NSR = (C::FM + C::FN) * C::KSTEPS;                                // scale reads per stage
   if constexpr (C::SCHED == 1) {
     __builtin_amdgcn_sched_group_barrier(0x100, 64, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);
   } else if constexpr (C::SCHED == 2) {
     __builtin_amdgcn_iglp_opt(0);
   } else if constexpr (C::SCHED == 3) {
-    __builtin_amdgcn_sched_group_barrier(0x100, NR0 + C::FM + C::FN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR0 + NSR, 0);
     unroll<NR0>([&](auto) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     });
     __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);
+  } else if constexpr (C::SCHED == 5) {
+    constexpr int NMF = C::FM * C::FN;  // MFMAs per K step
+    __builtin_amdgcn_sched_group_barrier(0x100, NR0 + NSR, 0);
+    if constexpr (C::KSTEPS == 2) {
+      unroll<NMF>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      });
+    }
+    constexpr int PER = (C::DPS + NMF - 1) / NMF;  // DMAs after each MFMA of the last K step
+    unroll<NMF>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x060, PER, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x068, 64, 0);
   }
 }
 
@@ -456,9 +518,54 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
 
   load_issue_tile();
   int ahead = 0;  // stages issued and not yet consumed
+  int slot_comp = 0;
+  if constexpr (C::SCHED == 5) {
+    // Every step issues exactly one stage (a dummy from the zero page once no
+    // work is left), so STAGES-2 stages always follow the one awaited and the
+    // wait is a constant; the DMAs go out inside the stage's MFMA block.
+    auto advance_issue = [&](bool dummy) {
+      slot_issue = slot_issue + 1 == C::STAGES ? 0 : slot_issue + 1;
+      if (!dummy && ++is == ins) {
+        is = 0;
+        it += stride;
+        load_issue_tile();
+      }
+    };
+    for (int q = 0; q < C::STAGES - 1; ++q) {
+      const bool dummy = it >= total;
+      issue_stage<C>(plan, iops, is, smem + slot_issue * C::STAGE_BYTES, w, ldas, ldbs, dummy);
+      advance_issue(dummy);
+    }
+    bool pending = false, pending_dummy = false;
+    for (int ct = first; ct < total; ct += stride) {
+      const TileOps cops = src.ops(ct);
+      const int cns = (cops.kc + C::BK - 1) / C::BK;
+      v16f acc[C::FM][C::FN];
+      unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
+      for (int s = 0; s < cns; ++s) {
+        // the previous step's issue state advances here, ahead of the wait,
+        // so that its branches (a new tile's set-up) do not split this
+        // step's DMA + MFMA block
+        if (pending) advance_issue(pending_dummy);
+        const bool dummy = it >= total;
+        uint8_t* dst = smem + slot_issue * C::STAGE_BYTES;
+        wait_vmcnt<(C::STAGES - 2) * C::DPS>();
+        raw_barrier();
+        compute_stage<C>(smem + slot_comp * C::STAGE_BYTES, acc, wm, wn, h, l32,
+                         [&]() __attribute__((always_inline)) {
+                           issue_stage<C>(plan, iops, is, dst, w, ldas, ldbs, dummy);
+                         });
+        pending = true;
+        pending_dummy = dummy;
+        slot_comp = slot_comp + 1 == C::STAGES ? 0 : slot_comp + 1;
+      }
+      src.epilogue(ct, acc, scratch, w, lane);
+    }
+    wait_vmcnt<0>();
+    return;
+  }
   for (int q = 0; q < C::STAGES - 1; ++q) ahead += issue_one();
 
-  int slot_comp = 0;
   for (int ct = first; ct < total; ct += stride) {
     const TileOps cops = src.ops(ct);
     const int cns = (cops.kc + C::BK - 1) / C::BK;
@@ -526,10 +633,20 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&o)[8]) {
 // ---------------------------------------------------------------------------
 // forward / input gradient
 // ---------------------------------------------------------------------------
+// Row alignment mask of a rows-kernel tile start (MX: multiples of 4).
+template <class C>
+constexpr int kRowAlign = C::BLK ? 0 : 3;
+
+// Number of BM-row tiles of an expert with m rows starting at row `start`.
+template <class C>
+__host__ __device__ inline int64_t expert_row_tiles(int64_t start, int64_t m) {
+  return m > 0 ? (m + (start & kRowAlign<C>) + C::BM - 1) / C::BM : 0;
+}
+
 template <class C>
 struct RowsSource {
   const RowsGemmParams& p;
-  const int64_t* pref;       // LDS: high = row offset, low = M-tile offset
+  const int64_t* pref;       // LDS: first row of each expert's segment
   const int32_t* tile_offs;  // LDS
   int G, n_tiles, ntot;
 
@@ -542,27 +659,39 @@ struct RowsSource {
     const int mt = local / n_tiles;
     return Pos{g, mt, local - mt * n_tiles};
   }
+  // Tile rows: MX tiles start at a multiple of 4 (the scale DMA moves four
+  // rows per lane), so an expert's first tile may begin up to 3 rows before
+  // its segment; rows outside [lo, hi) belong to other experts and are
+  // computed but never stored.
+  struct Rows { int64_t row0; int lo, hi; };
+  __device__ __forceinline__ Rows rows(const Pos& q) const {
+    const int64_t start = pref[q.g];
+    const int64_t row0 = (start & ~(int64_t)kRowAlign<C>) + (int64_t)q.mt * C::BM;
+    return Rows{row0, (int)(start - row0), (int)(start + p.sp.m[q.g] - row0)};
+  }
   __device__ __forceinline__ TileOps ops(int t) const {
     const Pos q = pos(t);
-    const int64_t row0 = (pref[q.g] >> 32) + (int64_t)q.mt * C::BM;
-    const int mleft = p.sp.m[q.g] - q.mt * C::BM;
+    const Rows rw = rows(q);
     const int col0 = q.nt * C::BN;
     const int nleft = p.n_out - col0;
     TileOps o;
-    o.a = p.a + row0 * p.lda;
+    o.a = p.a + rw.row0 * p.lda;
     // MX scales are block-major ([blocks, rows]); blockwise scales row-major
-    o.as = p.as + (C::BLK ? row0 * p.ldas : row0);
+    o.as = p.as + (C::BLK ? rw.row0 * p.ldas : rw.row0);
     o.b = p.b + (int64_t)q.g * p.b_gstride + (int64_t)col0 * p.ldb;
     o.bs = p.bs + (int64_t)q.g * p.bs_gstride + (C::BLK ? (int64_t)(col0 / C::BDIV) * p.ldbs : (int64_t)col0);
-    o.mrows = mleft < C::BM ? mleft : C::BM;
+    o.mrows = rw.hi < C::BM ? rw.hi : C::BM;
     o.nrows = nleft < C::BN ? nleft : C::BN;
+    o.srows_a = (int)(p.ldas - rw.row0);  // MX: the padded row count is the block stride
+    o.srows_b = nleft;
     o.kc = p.kc;
     return o;
   }
   __device__ __forceinline__ void epilogue(int t, v16f (&acc)[C::FM][C::FN], uint8_t* scratch, int w, int lane) {
     const Pos q = pos(t);
-    const int64_t row0 = (pref[q.g] >> 32) + (int64_t)q.mt * C::BM;
-    const int mleft = p.sp.m[q.g] - q.mt * C::BM;
+    const Rows rw = rows(q);
+    const int64_t row0 = rw.row0;
+    const int mlo = rw.lo, mleft = rw.hi;
     const int col0 = q.nt * C::BN;
     const int ncols = p.n_out - col0;
     const int wm = w / C::WN, wn = w % C::WN;
@@ -577,7 +706,7 @@ struct RowsSource {
           frag_half_rows<hf>(acc[i][j], scr, lane, o);
           const int row = wm * C::WTM + i * 32 + 16 * hf + rr;
           const int col = wn * C::WTN + j * 32 + cc;
-          if (row < mleft && col < ncols)
+          if (row >= mlo && row < mleft && col < ncols)
             *reinterpret_cast<uint4*>(p.c + (row0 + row) * p.ldc + col0 + col) = pack_bf16x8(o);
         });
       });
@@ -589,16 +718,15 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_rows_kernel(const RowsGemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int64_t pref[kMaxExperts + 1];
+  __shared__ int64_t tpref[kMaxExperts + 1];
   __shared__ int64_t wtot[C::THREADS / 64];
   __shared__ int32_t tile_offs[kMaxExperts + 1];
 
   const int G = p.sp.G;
   const int n_tiles = (p.n_out + C::BN - 1) / C::BN;
-  block_prefix64<C::THREADS>(G, [&](int g) {
-    const int64_t m = p.sp.m[g];
-    return (m << 32) | ((m + C::BM - 1) / C::BM);
-  }, pref, wtot);
-  for (int g = threadIdx.x; g <= G; g += C::THREADS) tile_offs[g] = (int32_t)(pref[g] & 0xffffffffll) * n_tiles;
+  block_prefix64<C::THREADS>(G, [&](int g) { return (int64_t)p.sp.m[g]; }, pref, wtot);
+  block_prefix64<C::THREADS>(G, [&](int g) { return expert_row_tiles<C>(pref[g], p.sp.m[g]); }, tpref, wtot);
+  for (int g = threadIdx.x; g <= G; g += C::THREADS) tile_offs[g] = (int32_t)tpref[g] * n_tiles;
   __syncthreads();
 
   RowsSource<C> src{p, pref, tile_offs, G, n_tiles, tile_offs[G]};
@@ -643,6 +771,8 @@ struct WgradSource {
     const int rl = p.n_rows - q.row0, cl = p.n_cols - q.col0;
     o.mrows = rl < C::BM ? rl : C::BM;
     o.nrows = cl < C::BN ? cl : C::BN;
+    o.srows_a = rl;  // n_rows and n_cols are multiples of 32, the block strides
+    o.srows_b = cl;
     o.kc = q.kc;
     return o;
   }
@@ -748,8 +878,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-using CfgA4 = TileCfg<256, 256, 2, 4, 128, 3, kA4W4, 1, 3>;   // a4w4: fwd, dgrad, wgrad
-using CfgA8 = TileCfg<256, 256, 2, 4, 64, 4, kA8W4, 1, 3>;     // a8w4 forward
+// a4w4 (fwd, dgrad, wgrad): 8 waves, 3-stage ring, the next stage's DMAs
+// spread over the last K step's MFMAs
+using CfgA4 = TileCfg<256, 256, 2, 4, 128, 3, kA4W4, 1, 5>;
+// a8w4 forward: a 128-deep stage holds 32 KiB of E4M3 A rows, so the ring
+// has two stages (the DMAs go out right after the barrier)
+using CfgA8 = TileCfg<256, 256, 2, 4, 128, 2, kA8W4, 1, 3>;
 // blockwise FP8: four waves (one per SIMD) each hold a 64x64 accumulator and
 // its per-128 partial; B scale rows are shared by 128 weight rows in the
 // forward, one per row in the weight gradient
@@ -772,22 +906,24 @@ static hipError_t launch_persistent(K kernel, const P& p, int64_t tiles, int num
   return hipGetLastError();
 }
 
-static int64_t rows_tiles(const RowsGemmParams& p, int BM, int BN) {
-  int64_t mt = 0;
-  for (int g = 0; g < p.sp.G; ++g) mt += (p.sp.m[g] + BM - 1) / BM;
-  return mt * ((p.n_out + BN - 1) / BN);
+template <class C>
+static int64_t rows_tiles(const RowsGemmParams& p) {
+  int64_t mt = 0, start = 0;
+  for (int g = 0; g < p.sp.G; ++g) {
+    mt += expert_row_tiles<C>(start, p.sp.m[g]);
+    start += p.sp.m[g];
+  }
+  return mt * ((p.n_out + C::BN - 1) / C::BN);
 }
 
 hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, int num_cus, hipStream_t st) {
   if (a_fp8)
-    return launch_persistent<CfgA8>(grouped_rows_kernel<CfgA8>, p, rows_tiles(p, CfgA8::BM, CfgA8::BN), num_cus,
-                                    st);
-  return launch_persistent<CfgA4>(grouped_rows_kernel<CfgA4>, p, rows_tiles(p, CfgA4::BM, CfgA4::BN), num_cus, st);
+    return launch_persistent<CfgA8>(grouped_rows_kernel<CfgA8>, p, rows_tiles<CfgA8>(p), num_cus, st);
+  return launch_persistent<CfgA4>(grouped_rows_kernel<CfgA4>, p, rows_tiles<CfgA4>(p), num_cus, st);
 }
 
 hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, int num_cus, hipStream_t st) {
-  return launch_persistent<CfgBlkF>(grouped_rows_kernel<CfgBlkF>, p, rows_tiles(p, CfgBlkF::BM, CfgBlkF::BN),
-                                    num_cus, st);
+  return launch_persistent<CfgBlkF>(grouped_rows_kernel<CfgBlkF>, p, rows_tiles<CfgBlkF>(p), num_cus, st);
 }
 
 template <class C>

@@ -11,6 +11,9 @@ namespace mxgg {
 // Row-split grouped GEMM (forward and input gradient): out[r, :] for every row
 // r of expert g is A[r, :] . B_g^T, where B_g is the [n_out, kc] operand of
 // expert g starting at b + g * b_gstride with row stride ldb.
+// Block stride of block-major MX scales: rows rounded up to a multiple of 4.
+inline int64_t mx_scale_stride(int64_t rows) { return rows > 0 ? (rows + 3) & ~(int64_t)3 : 0; }
+
 struct RowsGemmParams {
   const uint8_t* a;
   const uint8_t* as;
@@ -19,7 +22,8 @@ struct RowsGemmParams {
   uint16_t* c;            // bf16 output
   int64_t lda, ldb;       // A / B data row strides (bytes)
   int64_t ldas, ldbs;     // scale strides (bytes): MX scales are block-major
-                          // [blocks, rows] (ld = the block stride); blockwise
+                          // [blocks, R4] (ld = the block stride R4, a
+                          // multiple of 4); blockwise
                           // fp32 scales are row-major (ld = the row stride)
   int64_t b_gstride;      // bytes between consecutive experts' B data
   int64_t bs_gstride;     // bytes between consecutive experts' B scales

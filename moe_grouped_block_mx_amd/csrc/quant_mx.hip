@@ -1,8 +1,9 @@
 // MX quantizers (E2M1 / E4M3 elements, UE8M0 scale per 32 elements) for gfx950.
 //
 // Row-wise: the row operand of "Triton mxfp4 (and a8w4) grouped GEMM kernel"
-// (data [rows, cols/2] or [rows, cols]; scales block-major [cols/32, rows], so
-// a GEMM stage reads the scales of consecutive rows contiguously).
+// (data [rows, cols/2] or [rows, cols]; scales block-major [cols/32, R4],
+// R4 = rows rounded up to a multiple of 4, so a GEMM stage reads the scales of
+// consecutive rows contiguously, four rows per aligned word).
 // Column-wise, segment-padded: the padded column operand of the variable-K
 // weight gradient on the same page (each expert's rows transposed, blocks of 32
 // starting at the segment start, zeros past the segment end).
@@ -38,7 +39,7 @@ __device__ __forceinline__ v2bf16 as_bf16x2(uint32_t w) { return __builtin_bit_c
 template <class F, int U>
 __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __restrict__ x, int64_t ldx, int rows,
                                                             int cpr, uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ s) {
+                                                            uint8_t* __restrict__ s, int64_t sld) {
   constexpr bool FP4 = F::MB == 1;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;  // chunk inside the row
@@ -84,13 +85,11 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
             make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
       }
       sbytes |= (uint32_t)(e + 127) << (8 * u);
-      if ((c & 3) == 0 && ((rows & 3) != 0 || rb + w * U + U > rows))
-        s[(int64_t)(c >> 2) * rows + r] = (uint8_t)(e + 127);  // ragged row count: one byte per row
     }
-    // block-major scales [cols/32, rows]: the thread's four rows are adjacent
+    // block-major scales [cols/32, sld], sld = rows rounded up to a multiple
+    // of 4: the thread's four rows are one aligned word (padding rows get 0)
     const int r0 = rb + w * U;
-    if (cvalid && (c & 3) == 0 && (rows & 3) == 0 && r0 + U <= rows)
-      *reinterpret_cast<uint32_t*>(s + (int64_t)(c >> 2) * rows + r0) = sbytes;
+    if (cvalid && (c & 3) == 0 && r0 < rows) *reinterpret_cast<uint32_t*>(s + (int64_t)(c >> 2) * sld + r0) = sbytes;
   }
 }
 
@@ -211,9 +210,11 @@ hipError_t launch_quant_rowwise_mx(const uint16_t* x, int64_t rows, int64_t cols
   const int64_t gy_need = (rows + 4 * U - 1) / (4 * U);
   const dim3 grid((unsigned)((cpr + 63) / 64), (unsigned)(gy_need < 65535 ? gy_need : 65535));
   if (fp8)
-    hipLaunchKernelGGL((quant_rowwise_kernel<E4M3Fmt, U>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q, s);
+    hipLaunchKernelGGL((quant_rowwise_kernel<E4M3Fmt, U>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q, s,
+                       mx_scale_stride(rows));
   else
-    hipLaunchKernelGGL((quant_rowwise_kernel<E2M1Fmt, U>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q, s);
+    hipLaunchKernelGGL((quant_rowwise_kernel<E2M1Fmt, U>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q, s,
+                       mx_scale_stride(rows));
   return hipGetLastError();
 }
 

@@ -26,10 +26,15 @@ def host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def mx_scales_rowmajor(t) -> np.ndarray:
-    """The library stores MX scales block-major, u8 [blocks, rows]; the oracle
-    row-major, [rows, blocks]. A pure layout permutation."""
-    return np.ascontiguousarray(host(t).T)
+def mx_scales_rowmajor(t, rows: int) -> np.ndarray:
+    """The library stores MX scales block-major, u8 [blocks, R4] with R4 = rows
+    rounded up to a multiple of 4 (padding rows hold 0); the oracle row-major,
+    [rows, blocks]. Checks the padding, then permutes the layout."""
+    a = host(t)
+    r4 = (rows + 3) // 4 * 4
+    assert a.shape[1] == r4, f"scale block stride {a.shape[1]} != {r4}"
+    assert not a[:, rows:].any(), "MX scale padding rows are not zero"
+    return np.ascontiguousarray(a[:, :rows].T)
 
 
 def host_bf16_f64(t) -> np.ndarray:

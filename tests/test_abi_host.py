@@ -28,9 +28,17 @@ def test_exports_every_declared_function():
     names = mx.header_functions()
     assert {"mxgg_quantize_rowwise", "mxgg_quantize_colwise_segpad", "mxgg_grouped_fwd",
             "mxgg_grouped_dgrad", "mxgg_grouped_wgrad", "mxgg_workspace_size",
-            "mxgg_segpad_rows", "mxgg_status_string", "mxgg_last_error"} <= set(names)
+            "mxgg_segpad_rows", "mxgg_mx_scale_stride", "mxgg_status_string",
+            "mxgg_last_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_mx_scale_stride():
+    # block stride of block-major MX scales: rows rounded up to a multiple of 4
+    for rows, want in ((0, 0), (-3, 0), (1, 4), (3, 4), (4, 4), (5, 8), (32768, 32768), (32769, 32772)):
+        assert L.mxgg_mx_scale_stride(rows) == want, rows
+    assert mx.mx_scale_stride(7) == 8
 
 
 def test_status_strings():

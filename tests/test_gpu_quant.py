@@ -1,8 +1,9 @@
 """GPU parity of the MX quantizers through the C ABI: bit-exact against the
 oracle on every finite bf16 pattern, special blocks, ragged shapes, strided
 inputs, segment-padded layouts and a full-size sampled check. The library's MX
-scales are block-major ([blocks, rows]); they are compared with the oracle's
-row-major scales after a transpose."""
+scales are block-major ([blocks, rows rounded up to a multiple of 4], padding
+rows zero); they are compared with the oracle's row-major scales after a
+transpose."""
 import numpy as np
 import pytest
 
@@ -20,7 +21,7 @@ def _check_rowwise(bits, fmt, what):
     x = dev_bf16(bits)
     q, s = mxg.quantize_rowwise(x, fmt)
     rq, rs = omx.quantize_rowwise(bits, fmt)
-    gq, gs = host(q), mx_scales_rowmajor(s)
+    gq, gs = host(q), mx_scales_rowmajor(s, bits.shape[0])
     bad_s = np.argwhere(gs != rs)
     assert bad_s.size == 0, f"{what}: scale mismatch at {bad_s[:4].tolist()}"
     bad_q = np.argwhere(gq != rq)
@@ -75,7 +76,7 @@ def test_rowwise_strided_input(fmt):
     x = dev_bf16(wide)[:, 8:168]                               # ldx = 200, cols = 160
     q, s = mxg.quantize_rowwise(x, fmt)
     rq, rs = omx.quantize_rowwise(np.ascontiguousarray(wide[:, 8:168]), fmt)
-    assert np.array_equal(host(q), rq) and np.array_equal(mx_scales_rowmajor(s), rs)
+    assert np.array_equal(host(q), rq) and np.array_equal(mx_scales_rowmajor(s, 100), rs)
 
 
 def _check_colwise(bits, splits, fmt, what):
@@ -83,7 +84,7 @@ def _check_colwise(bits, splits, fmt, what):
     q, s, mpad = mxg.quantize_colwise_segpad(x, splits, fmt)
     rq, rs = omx.quantize_colwise_segpad(bits, splits, fmt)
     assert mpad == rq.shape[1] * (2 if fmt == "mxfp4" else 1)
-    gq, gs = host(q), mx_scales_rowmajor(s)
+    gq, gs = host(q), mx_scales_rowmajor(s, bits.shape[1])
     assert np.array_equal(gs, rs), f"{what}: scales differ at {np.argwhere(gs != rs)[:4].tolist()}"
     assert np.array_equal(gq, rq), f"{what}: data differ at {np.argwhere(gq != rq)[:4].tolist()}"
 
@@ -125,7 +126,7 @@ def test_rowwise_full_size_fc1_sampled():
     q, s = mxg.quantize_rowwise(x, "mxfp4")
     rows = np.sort(np.random.default_rng(0).choice(32768, size=2048, replace=False))
     rq, rs = omx.quantize_rowwise(bits[rows], "mxfp4")
-    assert np.array_equal(host(q)[rows], rq) and np.array_equal(mx_scales_rowmajor(s)[rows], rs)
+    assert np.array_equal(host(q)[rows], rq) and np.array_equal(mx_scales_rowmajor(s, 32768)[rows], rs)
 
 
 def test_colwise_full_size_fc1_sampled_columns():
@@ -137,4 +138,4 @@ def test_colwise_full_size_fc1_sampled_columns():
     q, s, mpad = mxg.quantize_colwise_segpad(x, sp, "mxfp4")
     cols = np.sort(np.random.default_rng(1).choice(3072, size=64, replace=False))
     rq, rs = omx.quantize_colwise_segpad(np.ascontiguousarray(bits[:, cols]), sp, "mxfp4")
-    assert np.array_equal(host(q)[cols], rq) and np.array_equal(mx_scales_rowmajor(s)[cols], rs)
+    assert np.array_equal(host(q)[cols], rq) and np.array_equal(mx_scales_rowmajor(s, 3072)[cols], rs)
