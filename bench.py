@@ -6,12 +6,14 @@ One step = one training step of an MoE expert layer (FC1 of a gated FFN:
 seeded Dirichlet(0.5) routing with empty experts) through every row of the
 hot path, all in the library's HIP kernels:
 
-  forward : quantize A row-wise, quantize W row-wise, grouped forward (TN)
-  dgrad   : quantize dY row-wise, quantize W along N (column-wise segment-
-            padded, splits N per expert), grouped input gradient (NN)
-  wgrad   : quantize dY and X column-wise segment-padded (pad 32), grouped
-            variable-K weight gradient (NT) accumulated in place into an
-            fp32 main_grad [32, 3072, 4096]
+  quantize: X (= A), W and dY, each row-wise and column-wise segment-padded
+            in one read (the dual-output quantizer; W with splits N per
+            expert gives the forward's W and dgrad's W along N)
+  forward : grouped forward (TN)
+  dgrad   : grouped input gradient (NN)
+  wgrad   : grouped variable-K weight gradient (NT) accumulated in place into
+            an fp32 main_grad [32, 3072, 4096]
+(--separate-quant: the six single-output quantizer launches instead)
 
 value = GEMM flops of the step (3 x 2 * sum(m_g) * N * K) / step time, in
 TFLOPS. Every kernel is also timed alone with HIP events on the stream it is
@@ -28,6 +30,7 @@ WRITE_SIZE per dispatch, each scaled by the same counter's reading for a plain
 1 GiB copy); null when that summary was taken from a different kernel source.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--workload fc1|a8w4|blockwise]
+                       [--separate-quant]
        python bench.py --copy-only            (calibration copy for --pmc runs)
        python bench.py --summarize KERNEL STATS_CSV FETCH_CSV WRITE_CSV
                        COPY_FETCH_CSV COPY_WRITE_CSV   (writes the summary text)
@@ -65,6 +68,8 @@ def parse():
                     help="fc1: the a4w4 training step (default, the headline); a8w4: the MXFP8 x MXFP4 forward; "
                          "blockwise: the blockwise FP8 forward + weight gradient")
     ap.add_argument("--copy-only", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--separate-quant", action="store_true",
+                    help="fc1: single-output quantizers instead of the dual-output ones")
     ap.add_argument("--summarize", nargs=6, metavar=("KERNEL", "STATS", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="print the profile summary of KERNEL from rocprofv3 csv outputs")
     return ap.parse_args()
@@ -215,7 +220,7 @@ def cpu_baseline(seconds_hint=20.0):
                       f"NumPy fp64 oracle (OpenBLAS {threads} threads, host has {os.cpu_count()} cpus)"}
 
 
-def build_workload(name, dev):
+def build_workload(name, dev, separate_quant=False):
     """Device inputs, the op list and the per-op algorithmic work of one step.
 
     Returns dict(ops=[(name, kind, fn)], bytes_alg={op: bytes}, flops={op: flops},
@@ -251,6 +256,19 @@ def build_workload(name, dev):
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         dcq, dcs = torch.empty((N, mpad // 2), **u8), torch.empty((mpad // 32, N), **u8)
         xcq, xcs = torch.empty((K, mpad // 2), **u8), torch.empty((mpad // 32, K), **u8)
+        wsp = [N] * G
+        dual_ops = [
+            ("quant_X_dual", "quant", lambda: mxg.quantize_dual(a, sp, "mxfp4", q_row=aq, s_row=as_, q_col=xcq,
+                                                                s_col=xcs)),
+            ("quant_W_dual", "quant", lambda: mxg.quantize_dual(w, wsp, "mxfp4", q_row=wq, s_row=ws, q_col=wcq,
+                                                                s_col=wcs)),
+            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, out=y)),
+            ("quant_dY_dual", "quant", lambda: mxg.quantize_dual(dy, sp, "mxfp4", q_row=dq, s_row=ds, q_col=dcq,
+                                                                 s_col=dcs)),
+            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, dx=dx)),
+            ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, main_grad,
+                                                        accumulate=True)),
+        ]
         ops = [
             ("quant_A_row", "quant", lambda: mxg.quantize_rowwise(a, "mxfp4", q=aq, scales=as_)),
             ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, "mxfp4", q=wq, scales=ws)),
@@ -272,8 +290,13 @@ def build_workload(name, dev):
             "dgrad": M * N * q4 + nz * N * K * q4 + M * K * 2,
             "quant_dY_col": M * N * 2 + mpad * N * q4, "quant_X_col": M * K * 2 + mpad * K * q4,
             "wgrad": mpad * (N + K) * q4 + nz * N * K * 4 * 2,
+            "quant_X_dual": M * K * (2 + q4) + mpad * K * q4, "quant_W_dual": G * N * K * (2 + 2 * q4),
+            "quant_dY_dual": M * N * (2 + q4) + mpad * N * q4,
         }
+        if not separate_quant:
+            ops = dual_ops
         config = {"workload": "MoE FC1 a4w4 training step (fwd+dgrad+wgrad with MX quantization)",
+                  "quantizers": "separate" if separate_quant else "dual-output",
                   "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz,
                   "max_split": int(sp.max()), "mpad": mpad, "routing": "Dirichlet(0.5), 3 zeroed, seed 0"}
         return dict(ops=ops, bytes_alg=bytes_alg, flops={"fwd": 2.0 * M * N * K, "dgrad": 2.0 * M * N * K,
@@ -360,12 +383,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    W = build_workload(args.workload, dev)
+    W = build_workload(args.workload, dev, args.separate_quant)
     ops, bytes_alg, flops = W["ops"], W["bytes_alg"], W["flops"]
     if args.passes != "all":
-        keep = {"fwd": {"quant_A_row", "quant_W_row", "fwd"},
-                "dgrad": {"quant_dY_row", "quant_W_col", "dgrad"},
-                "wgrad": {"quant_dY_col", "quant_X_col", "wgrad"}}[args.passes]
+        keep = {"fwd": {"quant_A_row", "quant_W_row", "quant_X_dual", "quant_W_dual", "fwd"},
+                "dgrad": {"quant_dY_row", "quant_W_col", "quant_dY_dual", "quant_W_dual", "dgrad"},
+                "wgrad": {"quant_dY_col", "quant_X_col", "quant_X_dual", "quant_dY_dual", "wgrad"}}[args.passes]
         ops = [o for o in ops if o[0] in keep]
 
     stream = torch.cuda.current_stream(dev)

@@ -168,6 +168,28 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
                                          hipStream_t stream);
 
 /*
+ * Dual-output quantization: the row-wise and the column-wise segment-padded
+ * MX quantizations of one bf16 tensor from a single read of it (the "Changes"
+ * list of "Add ROCm Triton blockwise FP8 grouped GEMM" describes one kernel
+ * emitting both training operands in one pass; here for the MX formats).
+ * Bit-identical to mxgg_quantize_rowwise followed by
+ * mxgg_quantize_colwise_segpad on the same arguments.
+ *   x, rows, cols, ldx, m_splits, G, mpad  as for mxgg_quantize_colwise_segpad.
+ *   fmt     MXGG_MXFP4 or MXGG_MXFP8 (blockwise formats: MXGG_ERR_FORMAT).
+ *   flags   ignored (MX formats take none).
+ *   q_row, s_row  the row-wise outputs, as mxgg_quantize_rowwise.
+ *   q_col, s_col  the column-wise outputs, as mxgg_quantize_colwise_segpad.
+ * Weights for dgrad: W as [G*N, K] with m_splits = {N, ..., N} gives the
+ * forward's W_q/W_s and dgrad's wcol_q/wcol_s together.
+ * rows == 0 returns MXGG_OK (no launch). Errors: NULL, SHAPE, SPLITS, FORMAT,
+ * ALIGN, DEVICE, ARCH, HIP.
+ */
+mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                               const int64_t* m_splits, int32_t G, mxgg_format fmt,
+                               uint32_t flags, void* q_row, void* s_row, void* q_col,
+                               void* s_col, int64_t mpad, hipStream_t stream);
+
+/*
  * Grouped forward, TN: out[r, n] = sum_k A[r, k] * W_g[n, k] for every row r
  * of expert g (rows of expert g are consecutive, in expert order).
  *   a_q, a_s  A quantized row-wise along K: (MXFP4: u8 [M, K/2] | MXFP8: u8 [M, K])

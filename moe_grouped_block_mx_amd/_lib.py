@@ -42,6 +42,7 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 _SIGS = {
     "mxgg_quantize_rowwise": [_vp, _i64, _i64, _i64, _i32, _u32, _vp, _vp, _vp],
     "mxgg_quantize_colwise_segpad": [_vp, _i64, _i64, _i64, _i64p, _i32, _i32, _u32, _vp, _vp, _i64, _vp],
+    "mxgg_quantize_dual": [_vp, _i64, _i64, _i64, _i64p, _i32, _i32, _u32, _vp, _vp, _vp, _vp, _i64, _vp],
     "mxgg_grouped_fwd": [_vp, _vp, _i32, _vp, _vp, _i32, _i64p, _i32, _i64, _i64, _i64, _vp, _vp, _sz, _vp],
     "mxgg_grouped_dgrad": [_vp, _vp, _vp, _vp, _i32, _i64p, _i32, _i64, _i64, _i64, _vp, _vp, _sz, _vp],
     "mxgg_grouped_wgrad": [_vp, _vp, _vp, _vp, _i32, _i64p, _i32, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _sz,
@@ -194,6 +195,33 @@ def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=None, q=None, s
     return q, scales, mpad
 
 
+def mxgg_quantize_dual(x, m_splits, fmt="mxfp4", flags=None, q_row=None, s_row=None, q_col=None, s_col=None):
+    """x: bf16 [rows, cols]. Row-wise and column-wise segment-padded MX
+    quantization from one read. Returns (q_row, s_row, q_col, s_col, mpad)."""
+    torch = _torch()
+    f = _fmt(fmt)
+    flags = _flags(flags, f)
+    rows, cols = x.shape
+    _check_bf16_2d(x)
+    arr, G = _splits(m_splits)
+    mpad = int(lib.mxgg_segpad_rows(arr, G, f))
+    if mpad < 0:
+        mpad = 0
+    u8 = dict(dtype=torch.uint8, device=x.device)
+    fp4 = f == MXFP4
+    if q_row is None:
+        q_row = torch.empty((rows, cols // 2 if fp4 else cols), **u8)
+    if s_row is None:
+        s_row = torch.empty((cols // 32, mxgg_mx_scale_stride(rows)), **u8)
+    if q_col is None:
+        q_col = torch.empty((cols, mpad // 2 if fp4 else mpad), **u8)
+    if s_col is None:
+        s_col = torch.empty((mpad // 32, cols), **u8)
+    _check(lib.mxgg_quantize_dual(_ptr(x), rows, cols, _ld(x), arr, G, f, flags, _ptr(q_row), _ptr(s_row),
+                                  _ptr(q_col), _ptr(s_col), mpad, _stream(x)))
+    return q_row, s_row, q_col, s_col, mpad
+
+
 def mxgg_grouped_fwd(a_q, a_s, w_q, w_s, m_splits, N, K, a_fmt="mxfp4", w_fmt="mxfp4", out=None, ws=None):
     """out[M, N] (bf16) = per-expert A . W_g^T; W packed [G*N, ...]."""
     torch = _torch()
@@ -236,6 +264,7 @@ def mxgg_grouped_wgrad(dycol_q, dycol_s, xcol_q, xcol_s, m_splits, N, K, mpad, m
 # short names
 quantize_rowwise = mxgg_quantize_rowwise
 quantize_colwise_segpad = mxgg_quantize_colwise_segpad
+quantize_dual = mxgg_quantize_dual
 grouped_fwd = mxgg_grouped_fwd
 grouped_dgrad = mxgg_grouped_dgrad
 grouped_wgrad = mxgg_grouped_wgrad

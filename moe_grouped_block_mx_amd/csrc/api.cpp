@@ -195,6 +195,25 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
   return c.ok() ? ok() : finish(c);
 }
 
+mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, const int64_t* m_splits,
+                               int32_t G, mxgg_format fmt, uint32_t flags, void* q_row, void* s_row, void* q_col,
+                               void* s_col, int64_t mpad, hipStream_t stream) {
+  (void)flags;
+  Check c = validate_quantize_dual(x, rows, cols, ldx, m_splits, G, (int)fmt, q_row, s_row, q_col, s_col, mpad);
+  if (!c.ok()) return finish(c);
+  if (rows == 0) return ok();
+  int cus = 0;
+  c = device_checks(stream, {{x, "x"}, {q_row, "q_row"}, {s_row, "s_row"}, {q_col, "q_col"}, {s_col, "s_col"}}, &cus);
+  if (!c.ok()) return finish(c);
+  const SplitArgs sp = make_splits(m_splits, G);
+  c = hip_status(launch_quant_dual_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8,
+                                      static_cast<uint8_t*>(q_row), static_cast<uint8_t*>(s_row),
+                                      static_cast<uint8_t*>(q_col), static_cast<uint8_t*>(s_col), mpad, cus,
+                                      stream),
+                 "dual quantizer launch");
+  return c.ok() ? ok() : finish(c);
+}
+
 mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt, const void* w_q, const void* w_s,
                              mxgg_format w_fmt, const int64_t* m_splits, int32_t G, int64_t M, int64_t N, int64_t K,
                              void* out, void* ws, size_t ws_bytes, hipStream_t stream) {

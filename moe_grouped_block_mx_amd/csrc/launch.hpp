@@ -12,7 +12,7 @@ namespace mxgg {
 // r of expert g is A[r, :] . B_g^T, where B_g is the [n_out, kc] operand of
 // expert g starting at b + g * b_gstride with row stride ldb.
 // Block stride of block-major MX scales: rows rounded up to a multiple of 4.
-inline int64_t mx_scale_stride(int64_t rows) { return rows > 0 ? (rows + 3) & ~(int64_t)3 : 0; }
+__host__ __device__ inline int64_t mx_scale_stride(int64_t rows) { return rows > 0 ? (rows + 3) & ~(int64_t)3 : 0; }
 
 struct RowsGemmParams {
   const uint8_t* a;
@@ -55,6 +55,9 @@ struct DeviceInfo {
 
 hipError_t launch_quant_rowwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool fp8,
                                    uint8_t* q, uint8_t* s, int num_cus, hipStream_t st);
+hipError_t launch_quant_dual_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
+                                bool fp8, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc, int64_t mpad,
+                                int num_cus, hipStream_t st);
 hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
                                    bool fp8, uint8_t* q, uint8_t* s, int64_t mpad, hipStream_t st);
 

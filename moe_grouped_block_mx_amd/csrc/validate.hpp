@@ -132,6 +132,16 @@ inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols
   return Check{};
 }
 
+inline Check validate_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, const int64_t* m,
+                                    int32_t G, int fmt, const void* q_row, const void* s_row, const void* q_col,
+                                    const void* s_col, int64_t mpad) {
+  if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
+  if (!is_mx((mxgg_format)fmt)) return fail(MXGG_ERR_FORMAT, "the dual quantizer takes MX formats only");
+  MXGG_TRY(validate_quantize_rowwise(x, rows, cols, ldx, fmt, q_row, s_row));
+  MXGG_TRY(validate_quantize_colwise(x, rows, cols, ldx, m, G, fmt, q_col, s_col, mpad));
+  return Check{};
+}
+
 // The GEMM kernels address a 256-row tile with 32-bit byte offsets, so every
 // operand row stride is kept below 2^23 bytes (tile span < 2^31).
 constexpr int64_t kMaxRowStride = (int64_t)1 << 23;

@@ -28,7 +28,7 @@ def test_exports_every_declared_function():
     names = mx.header_functions()
     assert {"mxgg_quantize_rowwise", "mxgg_quantize_colwise_segpad", "mxgg_grouped_fwd",
             "mxgg_grouped_dgrad", "mxgg_grouped_wgrad", "mxgg_workspace_size",
-            "mxgg_segpad_rows", "mxgg_mx_scale_stride", "mxgg_status_string",
+            "mxgg_segpad_rows", "mxgg_mx_scale_stride", "mxgg_quantize_dual", "mxgg_status_string",
             "mxgg_last_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -39,6 +39,25 @@ def test_mx_scale_stride():
     for rows, want in ((0, 0), (-3, 0), (1, 4), (3, 4), (4, 4), (5, 8), (32768, 32768), (32769, 32772)):
         assert L.mxgg_mx_scale_stride(rows) == want, rows
     assert mx.mx_scale_stride(7) == 8
+
+
+def test_dual_quantizer_validation():
+    m = splits(40, 0, 24)
+    mpad = 96                                               # 64 + 0 + 32
+
+    def dual(fmt=0, mp=mpad, rows=64, cols=64, ldx=64, qr=P, qc=P, G=3):
+        return L.mxgg_quantize_dual(P, rows, cols, ldx, m, G, fmt, 0, qr, P, qc, P, mp, NULL)
+    assert dual(fmt=2) == 4 and "MX formats" in last()      # blockwise: not a dual format
+    assert dual(fmt=9) == 4
+    assert dual(mp=64) == 2 and "mpad" in last()            # wrong padded row count
+    assert dual(rows=63) == 3                               # splits do not sum to rows
+    assert dual(cols=48) == 2                               # cols % 32
+    assert dual(ldx=60) == 2                                # ldx < cols
+    assert dual(qr=NULL) == 1 and dual(qc=NULL) == 1        # NULL outputs
+    assert dual(qc=BAD) == 5                                # misaligned
+    assert dual(G=0) == 2
+    # an empty tensor is validated, then OK with no device work
+    assert L.mxgg_quantize_dual(NULL, 0, 64, 64, splits(0, 0), 2, 0, 0, NULL, NULL, NULL, NULL, 0, NULL) == 0
 
 
 def test_status_strings():
