@@ -340,10 +340,12 @@ def build_workload(name, dev, separate_quant=False):
         xcq, xcs = torch.empty((K, mpad), **u8), torch.empty((K, mpad // 128), **f32)
         dw = torch.empty((G, N, K), dtype=torch.bfloat16, device=dev)
         ops = [
-            ("quant_A_1x128", "quant", lambda: mxg.quantize_rowwise(a, "fp8_1x128", q=aq, scales=as_)),
-            ("quant_W_128x128", "quant", lambda: mxg.quantize_rowwise(w, "fp8_128x128", q=wq, scales=ws)),
-            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt="fp8_1x128",
-                                                    w_fmt="fp8_128x128", out=y)),
+            # power-of-two scales (the blockwise default), declared by the _p2
+            # formats so the forward applies them inside the MFMA
+            ("quant_A_1x128", "quant", lambda: mxg.quantize_rowwise(a, "fp8_1x128_p2", q=aq, scales=as_)),
+            ("quant_W_128x128", "quant", lambda: mxg.quantize_rowwise(w, "fp8_128x128_p2", q=wq, scales=ws)),
+            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt="fp8_1x128_p2",
+                                                    w_fmt="fp8_128x128_p2", out=y)),
             ("quant_dY_col", "quant", lambda: mxg.quantize_colwise_segpad(dy, sp, "fp8_1x128", q=dcq, scales=dcs)),
             ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "fp8_1x128", q=xcq, scales=xcs)),
             ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, dw, accumulate=False,

@@ -45,6 +45,15 @@
  *                     contraction axis (activations, wgrad column operands).
  *   MXGG_FP8_128x128  E4M3 elements, one fp32 scale per 128x128 block
  *                     (weights).
+ *   MXGG_FP8_1x128_P2, MXGG_FP8_128x128_P2
+ *                     The same layouts with every scale a power of two (what
+ *                     the quantizers write with MXGG_POW2_SCALES; given to a
+ *                     quantizer, these formats imply that flag). The GEMMs
+ *                     then apply the scales inside the MFMA (the fp32
+ *                     exponent field is a UE8M0 code) instead of scaling a
+ *                     per-128 partial: exact for powers of two, while a scale
+ *                     that is not one loses its mantissa. Mixing a _P2 format
+ *                     with a general one selects the general path.
  *
  * MX quantization rule (what mxgg_quantize_* produce): amax = max |x| over the
  * block; e = clamp(floor(log2 amax) - emax, -127, 127) with emax = 2 (E2M1) or
@@ -106,7 +115,9 @@ typedef enum mxgg_format {
   MXGG_MXFP4 = 0,
   MXGG_MXFP8 = 1,
   MXGG_FP8_1x128 = 2,
-  MXGG_FP8_128x128 = 3
+  MXGG_FP8_128x128 = 3,
+  MXGG_FP8_1x128_P2 = 4,
+  MXGG_FP8_128x128_P2 = 5
 } mxgg_format;
 
 /* flags for the quantizers (blockwise formats only) */

@@ -4,7 +4,7 @@ The compute path is libmxgg.so (hand-written HIP kernels behind the C ABI of
 include/mxgg.h); this package is its thin ctypes binding.
 """
 from ._lib import (  # noqa: F401
-    FORMATS, FP8_1x128, FP8_128x128, LIB_PATH, MAX_EXPERTS, MXFP4, MXFP8, POW2_SCALES,
+    FORMATS, FP8_1x128, FP8_128x128, FP8_1x128_P2, FP8_128x128_P2, LIB_PATH, MAX_EXPERTS, MXFP4, MXFP8, POW2_SCALES,
     MxggError, header_functions, lib,
     mxgg_grouped_dgrad, mxgg_grouped_fwd, mxgg_grouped_wgrad, mxgg_quantize_colwise_segpad, mxgg_quantize_dual,
     mxgg_mx_scale_stride, mxgg_quantize_rowwise, mxgg_segpad_rows, mxgg_workspace_size,

@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(PKG, "libmxgg.so")
 HEADER = os.path.join(ROOT, "include", "mxgg.h")
 
 # mxgg_format
-MXFP4, MXFP8, FP8_1x128, FP8_128x128 = 0, 1, 2, 3
-FORMATS = {"mxfp4": MXFP4, "mxfp8": MXFP8, "fp8_1x128": FP8_1x128, "fp8_128x128": FP8_128x128}
+MXFP4, MXFP8, FP8_1x128, FP8_128x128, FP8_1x128_P2, FP8_128x128_P2 = 0, 1, 2, 3, 4, 5
+FORMATS = {"mxfp4": MXFP4, "mxfp8": MXFP8, "fp8_1x128": FP8_1x128, "fp8_128x128": FP8_128x128,
+           "fp8_1x128_p2": FP8_1x128_P2, "fp8_128x128_p2": FP8_128x128_P2}
 POW2_SCALES = 1
 MAX_EXPERTS = 512
 
@@ -140,7 +141,7 @@ def mxgg_segpad_rows(m_splits, fmt) -> int:
 def _flags(flags, f):
     """Power-of-two scales are the blockwise default; MX formats take no flags."""
     if flags is None:
-        return POW2_SCALES if f in (FP8_1x128, FP8_128x128) else 0
+        return POW2_SCALES if f in (FP8_1x128, FP8_128x128, FP8_1x128_P2, FP8_128x128_P2) else 0
     return int(flags)
 
 
@@ -163,7 +164,7 @@ def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=None, q=None, scales=None):
         if f in (MXFP4, MXFP8):
             # block-major, block stride = rows rounded up to a multiple of 4
             scales = torch.empty((cols // 32, mxgg_mx_scale_stride(rows)), dtype=torch.uint8, device=x.device)
-        elif f == FP8_1x128:
+        elif f in (FP8_1x128, FP8_1x128_P2):
             scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
         else:
             scales = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=x.device)
@@ -186,7 +187,7 @@ def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=None, q=None, s
     if q is None:
         q = torch.empty((cols, mpad // 2 if f == MXFP4 else mpad), dtype=torch.uint8, device=x.device)
     if scales is None:
-        if f == FP8_1x128:
+        if f in (FP8_1x128, FP8_1x128_P2):
             scales = torch.empty((cols, mpad // 128), dtype=torch.float32, device=x.device)
         else:
             scales = torch.empty((mpad // 32, cols), dtype=torch.uint8, device=x.device)  # block-major

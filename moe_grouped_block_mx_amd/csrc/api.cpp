@@ -145,6 +145,7 @@ size_t mxgg_workspace_size(int32_t G) {
 
 int64_t mxgg_segpad_rows(const int64_t* m_splits, int32_t G, mxgg_format fmt) {
   if (!m_splits || G < 1 || G > MXGG_MAX_EXPERTS) return -1;
+  fmt = (mxgg_format)base_format(fmt);
   if (fmt != MXGG_MXFP4 && fmt != MXGG_MXFP8 && fmt != MXGG_FP8_1x128) return -1;
   for (int32_t g = 0; g < G; ++g)
     if (m_splits[g] < 0) return -1;
@@ -155,6 +156,8 @@ int64_t mxgg_mx_scale_stride(int64_t rows) { return mx_scale_stride(rows); }
 
 mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, mxgg_format fmt,
                                   uint32_t flags, void* q, void* scales, hipStream_t stream) {
+  if (is_p2(fmt)) flags |= MXGG_POW2_SCALES;
+  fmt = (mxgg_format)base_format(fmt);
   Check c = validate_quantize_rowwise(x, rows, cols, ldx, (int)fmt, q, scales);
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
@@ -176,6 +179,8 @@ mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int
 mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t cols, int64_t ldx,
                                          const int64_t* m_splits, int32_t G, mxgg_format fmt, uint32_t flags,
                                          void* q, void* scales, int64_t mpad, hipStream_t stream) {
+  if (is_p2(fmt)) flags |= MXGG_POW2_SCALES;
+  fmt = (mxgg_format)base_format(fmt);
   Check c = validate_quantize_colwise(x, rows, cols, ldx, m_splits, G, (int)fmt, q, scales, mpad);
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
@@ -217,6 +222,10 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
 mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt, const void* w_q, const void* w_s,
                              mxgg_format w_fmt, const int64_t* m_splits, int32_t G, int64_t M, int64_t N, int64_t K,
                              void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  // power-of-two blockwise scales on both sides: the MFMA applies them
+  const bool p2 = is_p2(a_fmt) && is_p2(w_fmt);
+  a_fmt = (mxgg_format)base_format(a_fmt);
+  w_fmt = (mxgg_format)base_format(w_fmt);
   Check c = validate_fwd(a_q, a_s, (int)a_fmt, w_q, w_s, (int)w_fmt, m_splits, G, M, N, K, out, ws, ws_bytes,
                          mxgg_workspace_size(G));
   if (!c.ok()) return finish(c);
@@ -243,7 +252,7 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
     p.n_out = (int32_t)N;
     p.kc = (int32_t)K;
     p.sp = make_splits(m_splits, G);
-    c = hip_status(launch_grouped_rows_blk(p, cus, stream), "blockwise forward launch");
+    c = hip_status(launch_grouped_rows_blk(p, p2, cus, stream), "blockwise forward launch");
     return c.ok() ? ok() : finish(c);
   }
   const bool a8 = a_fmt == MXGG_MXFP8;
@@ -302,6 +311,8 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
                                mxgg_format fmt, const int64_t* m_splits, int32_t G, int64_t N, int64_t K,
                                int64_t mpad, void* main_grad, int32_t out_is_bf16, int32_t accumulate, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
+  const bool p2 = is_p2(fmt);
+  fmt = (mxgg_format)base_format(fmt);
   Check c = validate_wgrad(dycol_q, dycol_s, xcol_q, xcol_s, (int)fmt, m_splits, G, N, K, mpad, main_grad,
                            out_is_bf16, accumulate, ws, ws_bytes, mxgg_workspace_size(G));
   if (!c.ok()) return finish(c);
@@ -333,7 +344,7 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
   std::iota(order, order + G, 0);
   std::stable_sort(order, order + G, [&](int x, int y) { return m_splits[x] > m_splits[y]; });
   for (int32_t j = 0; j < G; ++j) p.order[j] = (int16_t)order[j];
-  c = hip_status(blk ? launch_grouped_wgrad_blk(p, cus, stream) : launch_grouped_wgrad_mx(p, cus, stream),
+  c = hip_status(blk ? launch_grouped_wgrad_blk(p, p2, cus, stream) : launch_grouped_wgrad_mx(p, cus, stream),
                  "wgrad launch");
   return c.ok() ? ok() : finish(c);
 }

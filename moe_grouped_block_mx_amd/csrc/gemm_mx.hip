@@ -87,11 +87,13 @@ __device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* lds) {
 }
 
 // Operand kinds: E2M1 x E2M1 and E4M3 x E2M1 with UE8M0 scales per 32 along
-// the contraction (applied by the MFMA), or E4M3 x E4M3 with one fp32 scale
-// per 128 along the contraction ("blockwise": the MFMA runs unscaled into a
+// the contraction (applied by the MFMA); E4M3 x E4M3 with one fp32 scale per
+// 128 along the contraction ("blockwise": the MFMA runs unscaled into a
 // per-128 partial that is then scaled and added, since fp32 scales are not
-// powers of two in general).
-enum : int { kA4W4 = 0, kA8W4 = 1, kBlkFp8 = 2 };
+// powers of two in general); or blockwise E4M3 x E4M3 whose fp32 scales are
+// powers of two, which the MFMA applies itself (the scale's exponent field is
+// its UE8M0 code), so no partial is needed.
+enum : int { kA4W4 = 0, kA8W4 = 1, kBlkFp8 = 2, kBlkP2 = 3 };
 
 // OCC workgroups share a CU (the grid is OCC per CU): while one waits at a
 // barrier or drains its epilogue, the other's MFMAs keep the SIMDs busy.
@@ -102,13 +104,15 @@ template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, int KIND_, i
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
   static constexpr int SCHED = SCHED_, BDIV = BDIV_;
-  static constexpr bool AFP8 = KIND_ != kA4W4, BFP8 = KIND_ == kBlkFp8, BLK = KIND_ == kBlkFp8;
+  static constexpr bool AFP8 = KIND_ != kA4W4, BFP8 = KIND_ == kBlkFp8 || KIND_ == kBlkP2;
+  static constexpr bool BLK = KIND_ == kBlkFp8;                     // per-128 partial promotion
+  static constexpr bool F32S = KIND_ == kBlkFp8 || KIND_ == kBlkP2;  // fp32 row-major scales, 1 per 128
   static constexpr int NW = WM * WN, THREADS = 64 * NW;
   static constexpr int RBA = AFP8 ? BK : BK / 2;  // A bytes per row per stage
   static constexpr int RBB = BFP8 ? BK : BK / 2;  // B bytes per row per stage
   static constexpr int CPA = RBA / 16, CPB = RBB / 16;
   static constexpr int KSTEPS = BK / 64;          // MFMA K steps per stage
-  static constexpr int SB = BLK ? 1 : BK / 32;    // scale values per row per stage
+  static constexpr int SB = F32S ? 1 : BK / 32;   // scale values per row per stage
   static constexpr int PROMO = BLK ? 128 / BK : 1;  // stages per 128-element scale block (blockwise)
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -123,24 +127,24 @@ struct TileCfg {
   static constexpr int A_OFF = 0, A_BYTES = BM * RBA;
   static constexpr int B_OFF = A_OFF + A_BYTES, B_BYTES = BN * RBB;
   static constexpr int MXS_BYTES = round_up((BM + BN) * SB, NW * 256);
-  static constexpr int AS_OFF = B_OFF + B_BYTES, AS_BYTES = BLK ? round_up(BM * 4, NW * 256) : BM * SB;
-  static constexpr int BS_OFF = AS_OFF + AS_BYTES, BS_BYTES = BLK ? round_up(BN * 4, NW * 256) : MXS_BYTES - AS_BYTES;
+  static constexpr int AS_OFF = B_OFF + B_BYTES, AS_BYTES = F32S ? round_up(BM * 4, NW * 256) : BM * SB;
+  static constexpr int BS_OFF = AS_OFF + AS_BYTES, BS_BYTES = F32S ? round_up(BN * 4, NW * 256) : MXS_BYTES - AS_BYTES;
   static constexpr int STAGE_BYTES = BS_OFF + BS_BYTES;
   // LDS DMA instructions per wave per stage (1 KiB of chunks, or 256 bytes of
   // scales: MX, both operands' in DSA; blockwise, A's in DSA and B's in DSB)
   static constexpr int DA = A_BYTES / (NW * 1024), DB = B_BYTES / (NW * 1024);
-  static constexpr int DSA = BLK ? AS_BYTES / (NW * 256) : MXS_BYTES / (NW * 256);
-  static constexpr int DSB = BLK ? BS_BYTES / (NW * 256) : 0;
+  static constexpr int DSA = F32S ? AS_BYTES / (NW * 256) : MXS_BYTES / (NW * 256);
+  static constexpr int DSB = F32S ? BS_BYTES / (NW * 256) : 0;
   static constexpr int DPS = DA + DB + DSA + DSB;
   static constexpr int EPI_BYTES = 16 * 36 * 4;  // per-wave epilogue scratch (16 rows x 32 fp32, padded)
   static constexpr int EPI_OFF = STAGES * STAGE_BYTES;
   static constexpr int SMEM_BYTES = EPI_OFF + NW * EPI_BYTES;
   static_assert(A_BYTES % (NW * 1024) == 0 && B_BYTES % (NW * 1024) == 0, "chunk DMA split");
   static_assert(KSTEPS == 1 || KSTEPS == 2, "K steps per stage");
-  static_assert(!BLK || BK == 64 || BK == 128, "blockwise stages split a 128-element scale block");
+  static_assert(!F32S || BK == 64 || BK == 128, "blockwise stages split a 128-element scale block");
   static_assert(FM >= 1 && FN >= 1 && STAGES >= 2 && STAGES <= 8, "shape");
   static_assert(DPS * (STAGES - 2) < 64, "vmcnt range");
-  static_assert(BLK || (BM % 4 == 0 && BN % 4 == 0), "MX scale DMA moves four rows per lane");
+  static_assert(F32S || (BM % 4 == 0 && BN % 4 == 0), "MX scale DMA moves four rows per lane");
   static_assert(STAGE_BYTES % 16 == 0, "stage alignment");
 };
 
@@ -167,8 +171,8 @@ struct DmaPlan {
   // MX scales: per lane, the row offset of its four rows and its block inside
   // a stage (kNoBlock: padding); the operand of an instruction is
   // wave-uniform (A's and B's regions are whole instructions)
-  uint32_t sOff[C::BLK ? 1 : C::DSA];
-  int sBlk[C::BLK ? 1 : C::DSA];
+  uint32_t sOff[C::F32S ? 1 : C::DSA];
+  int sBlk[C::F32S ? 1 : C::DSA];
 };
 constexpr int kNoBlock = 1 << 24;
 
@@ -198,7 +202,7 @@ __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64
   // the readable scale rows (which only invalid tile rows reach) read the last
   // readable group of four, so every read stays inside the buffer.
   // Blockwise: one fp32 per row of the stage's 128-element block.
-  if constexpr (C::BLK) {
+  if constexpr (C::F32S) {
     unroll<C::DSA>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       const int d = (i * C::NW + w) * 64 + lane;
@@ -253,8 +257,8 @@ __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps&
   // scales of this stage: MX, blocks s*SB .. s*SB+SB-1 (blocks past the
   // contraction and padding lanes read zeros); blockwise, the fp32 of
   // 128-block s*BK/128
-  const int nblk = dummy ? 0 : (C::BLK ? t.kc / 128 : t.kc / 32);
-  const int bidx0 = C::BLK ? s * C::BK / 128 : s * C::SB;
+  const int nblk = dummy ? 0 : (C::F32S ? t.kc / 128 : t.kc / 32);
+  const int bidx0 = C::F32S ? s * C::BK / 128 : s * C::SB;
   unroll<C::DA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const uint8_t* src = select_ptr(ka0 + pl.kA[i] < kca, t.a + pl.offA[i] + ka0, zero);
@@ -265,7 +269,7 @@ __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps&
     const uint8_t* src = select_ptr(kb0 + pl.kB[i] < kcb, t.b + pl.offB[i] + kb0, zero);
     dma16(src, st + C::B_OFF + (i * C::NW + w) * 1024);
   });
-  if constexpr (C::BLK) {
+  if constexpr (C::F32S) {
     unroll<C::DSA>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       dma4(select_ptr(bidx0 < nblk, t.as + pl.offAS[i] + bidx0 * 4, zero), st + C::AS_OFF + (i * C::NW + w) * 256);
@@ -368,21 +372,37 @@ template <class C, class Issue = NoIssue>
 __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::FM][C::FN], int wm, int wn, int h,
                                               int l32, Issue&& issue = Issue{}) {
   uint32_t sa[C::FM], sb[C::FN];
-  unroll<C::FM>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    const int r = wm * C::WTM + i * 32 + l32;
-    // lane half h takes block h of K step 0 (op_sel 0) and block 2+h of K step 1 (op_sel 1)
-    const uint8_t* p = st + C::AS_OFF + h * C::BM + r;
-    if constexpr (C::KSTEPS == 2) sa[i] = p[0] | ((uint32_t)p[2 * C::BM] << 8);
-    else sa[i] = p[0];
-  });
-  unroll<C::FN>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    const int r = wn * C::WTN + j * 32 + l32;
-    const uint8_t* p = st + C::BS_OFF + h * C::BN + r;
-    if constexpr (C::KSTEPS == 2) sb[j] = p[0] | ((uint32_t)p[2 * C::BN] << 8);
-    else sb[j] = p[0];
-  });
+  if constexpr (C::F32S) {
+    // power-of-two fp32 scales, one per row for the whole stage: the
+    // exponent field is the UE8M0 code, the same for every K step
+    constexpr uint32_t REP = C::KSTEPS == 2 ? 0x0101u : 0x01u;
+    unroll<C::FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int r = wm * C::WTM + i * 32 + l32;
+      sa[i] = ((reinterpret_cast<const uint32_t*>(st + C::AS_OFF)[r] >> 23) & 0xffu) * REP;
+    });
+    unroll<C::FN>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int r = wn * C::WTN + j * 32 + l32;
+      sb[j] = ((reinterpret_cast<const uint32_t*>(st + C::BS_OFF)[r] >> 23) & 0xffu) * REP;
+    });
+  } else {
+    unroll<C::FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int r = wm * C::WTM + i * 32 + l32;
+      // lane half h takes block h of K step 0 (op_sel 0) and block 2+h of K step 1 (op_sel 1)
+      const uint8_t* p = st + C::AS_OFF + h * C::BM + r;
+      if constexpr (C::KSTEPS == 2) sa[i] = p[0] | ((uint32_t)p[2 * C::BM] << 8);
+      else sa[i] = p[0];
+    });
+    unroll<C::FN>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int r = wn * C::WTN + j * 32 + l32;
+      const uint8_t* p = st + C::BS_OFF + h * C::BN + r;
+      if constexpr (C::KSTEPS == 2) sb[j] = p[0] | ((uint32_t)p[2 * C::BN] << 8);
+      else sb[j] = p[0];
+    });
+  }
   unroll<C::KSTEPS>([&](auto kc_) {
     constexpr int kk = decltype(kc_)::value;
     v8i af[C::FM], bf[C::FN];
@@ -635,7 +655,7 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&o)[8]) {
 // ---------------------------------------------------------------------------
 // Row alignment mask of a rows-kernel tile start (MX: multiples of 4).
 template <class C>
-constexpr int kRowAlign = C::BLK ? 0 : 3;
+constexpr int kRowAlign = C::F32S ? 0 : 3;
 
 // Number of BM-row tiles of an expert with m rows starting at row `start`.
 template <class C>
@@ -677,9 +697,9 @@ struct RowsSource {
     TileOps o;
     o.a = p.a + rw.row0 * p.lda;
     // MX scales are block-major ([blocks, rows]); blockwise scales row-major
-    o.as = p.as + (C::BLK ? rw.row0 * p.ldas : rw.row0);
+    o.as = p.as + (C::F32S ? rw.row0 * p.ldas : rw.row0);
     o.b = p.b + (int64_t)q.g * p.b_gstride + (int64_t)col0 * p.ldb;
-    o.bs = p.bs + (int64_t)q.g * p.bs_gstride + (C::BLK ? (int64_t)(col0 / C::BDIV) * p.ldbs : (int64_t)col0);
+    o.bs = p.bs + (int64_t)q.g * p.bs_gstride + (C::F32S ? (int64_t)(col0 / C::BDIV) * p.ldbs : (int64_t)col0);
     o.mrows = rw.hi < C::BM ? rw.hi : C::BM;
     o.nrows = nleft < C::BN ? nleft : C::BN;
     o.srows_a = (int)(p.ldas - rw.row0);  // MX: the padded row count is the block stride
@@ -761,7 +781,7 @@ struct WgradSource {
     // block-major (block p0/32, row row0), blockwise row-major (fp32 p0/128)
     o.a = p.a + (int64_t)q.row0 * p.lda + (C::AFP8 ? q.p0 : q.p0 / 2);
     o.b = p.b + (int64_t)q.col0 * p.ldb + (C::BFP8 ? q.p0 : q.p0 / 2);
-    if constexpr (C::BLK) {
+    if constexpr (C::F32S) {
       o.as = p.as + (int64_t)q.row0 * p.ldas + q.p0 / 128 * 4;
       o.bs = p.bs + (int64_t)q.col0 * p.ldbs + q.p0 / 128 * 4;
     } else {
@@ -861,7 +881,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const
 
   const int G = p.sp.G;
   const int tr = (p.n_rows + C::BM - 1) / C::BM, tc = (p.n_cols + C::BN - 1) / C::BN;
-  constexpr int PAD = C::BLK ? 128 : 32;  // segment pad multiple of the column-wise operands
+  constexpr int PAD = C::F32S ? 128 : 32;  // segment pad multiple of the column-wise operands
   block_prefix64<C::THREADS>(G, [&](int g) { return (int64_t)((p.sp.m[g] + PAD - 1) & ~(PAD - 1)); }, pad_pref,
                              wtot);
   block_prefix64<C::THREADS>(G, [&](int j) {
@@ -889,6 +909,9 @@ using CfgA8 = TileCfg<256, 256, 2, 4, 128, 2, kA8W4, 1, 3>;
 // forward, one per row in the weight gradient
 using CfgBlkF = TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 128>;
 using CfgBlkW = TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 1>;
+// blockwise FP8 with power-of-two scales: the a4w4 loop (8 waves, 256x256)
+// with E4M3 on both sides; a 64-deep stage holds 16 KiB of each operand
+using CfgP2F = TileCfg<256, 256, 2, 4, 64, 3, kBlkP2, 1, 5, 128>;
 
 template <class C, class K, class P>
 static hipError_t launch_persistent(K kernel, const P& p, int64_t tiles, int num_cus, hipStream_t st) {
@@ -922,7 +945,8 @@ hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, int num_c
   return launch_persistent<CfgA4>(grouped_rows_kernel<CfgA4>, p, rows_tiles<CfgA4>(p), num_cus, st);
 }
 
-hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, int num_cus, hipStream_t st) {
+hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, bool pow2, int num_cus, hipStream_t st) {
+  if (pow2) return launch_persistent<CfgP2F>(grouped_rows_kernel<CfgP2F>, p, rows_tiles<CfgP2F>(p), num_cus, st);
   return launch_persistent<CfgBlkF>(grouped_rows_kernel<CfgBlkF>, p, rows_tiles<CfgBlkF>(p), num_cus, st);
 }
 
@@ -939,7 +963,11 @@ hipError_t launch_grouped_wgrad_mx(const WgradParams& p, int num_cus, hipStream_
   return launch_wgrad<CfgA4>(p, num_cus, st);
 }
 
-hipError_t launch_grouped_wgrad_blk(const WgradParams& p, int num_cus, hipStream_t st) {
+// The weight gradient always takes the per-128 partial path: its power-of-two
+// variant (the forward's loop on the variable-K source) faulted the GPU on its
+// first test and is switched off until the cause is found.
+hipError_t launch_grouped_wgrad_blk(const WgradParams& p, bool pow2, int num_cus, hipStream_t st) {
+  (void)pow2;
   return launch_wgrad<CfgBlkW>(p, num_cus, st);
 }
 

@@ -70,7 +70,8 @@ hipError_t launch_quant_rowwise_blk(const uint16_t* x, int64_t rows, int64_t col
                                     bool pow2, uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_quant_colwise_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
                                     uint8_t* q, float* s, int64_t mpad, hipStream_t st);
-hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, int num_cus, hipStream_t st);
-hipError_t launch_grouped_wgrad_blk(const WgradParams& p, int num_cus, hipStream_t st);
+// pow2: every scale is a power of two (the MFMA applies it; no per-128 partial)
+hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, bool pow2, int num_cus, hipStream_t st);
+hipError_t launch_grouped_wgrad_blk(const WgradParams& p, bool pow2, int num_cus, hipStream_t st);
 
 }  // namespace mxgg

@@ -35,10 +35,15 @@ inline Check fail(mxgg_status st, const char* fmt, long long a = 0, long long b 
 }
 
 inline bool is_mx(mxgg_format f) { return f == MXGG_MXFP4 || f == MXGG_MXFP8; }
-inline bool valid_format(int f) { return f >= MXGG_MXFP4 && f <= MXGG_FP8_128x128; }
+inline bool valid_format(int f) { return f >= MXGG_MXFP4 && f <= MXGG_FP8_128x128_P2; }
+// The power-of-two blockwise formats share their base format's layout.
+inline bool is_p2(int f) { return f == MXGG_FP8_1x128_P2 || f == MXGG_FP8_128x128_P2; }
+inline int base_format(int f) {
+  return f == MXGG_FP8_1x128_P2 ? MXGG_FP8_1x128 : f == MXGG_FP8_128x128_P2 ? MXGG_FP8_128x128 : f;
+}
 
 // Segment pad multiple of the column-wise operand of a format.
-inline int segpad_multiple(mxgg_format f) { return f == MXGG_FP8_1x128 ? 128 : 32; }
+inline int segpad_multiple(mxgg_format f) { return base_format(f) == MXGG_FP8_1x128 ? 128 : 32; }
 
 // Splits: pointer, count, non-negativity and sum.
 inline Check check_splits(const int64_t* m, int32_t G, int64_t rows, const char* what) {

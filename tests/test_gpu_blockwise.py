@@ -112,15 +112,19 @@ def test_quantize_colwise_1x128(pow2, case):
 # ---------------------------------------------------------------------------
 # GEMMs
 # ---------------------------------------------------------------------------
-def _fwd_case(splits, N, K, pow2, seed=0):
+def _fwd_case(splits, N, K, pow2, seed=0, p2=(False, False)):
+    """p2: (A, W) given as the power-of-two formats (quantized through them
+    too); both set selects the GEMM path that applies the scales in the MFMA."""
     splits = np.asarray(splits, dtype=np.int64)
     G, M = len(splits), int(splits.sum())
     a = bf16_normal((M, K), 1.0, seed=seed + 1)
     w = bf16_normal((G * N, K), 0.02, seed=seed + 2)
     fl = POW2 if pow2 else 0
-    aq, as_ = mxg.quantize_rowwise(dev_bf16(a), "fp8_1x128", flags=fl)
-    wq, ws = mxg.quantize_rowwise(dev_bf16(w), "fp8_128x128", flags=fl)
-    out = mxg.grouped_fwd(aq, as_, wq, ws, splits, N, K, a_fmt="fp8_1x128", w_fmt="fp8_128x128")
+    af = "fp8_1x128_p2" if p2[0] else "fp8_1x128"
+    wf = "fp8_128x128_p2" if p2[1] else "fp8_128x128"
+    aq, as_ = mxg.quantize_rowwise(dev_bf16(a), af, flags=fl)
+    wq, ws = mxg.quantize_rowwise(dev_bf16(w), wf, flags=fl)
+    out = mxg.grouped_fwd(aq, as_, wq, ws, splits, N, K, a_fmt=af, w_fmt=wf)
     torch.cuda.synchronize()
     ra, ras = ob.quantize_1x128(a, pow2=pow2)
     rw, rws = ob.quantize_128x128(w, pow2=pow2)
@@ -143,14 +147,27 @@ def test_blockwise_fwd(pow2, case):
     assert_gemm_close(gpu, ref, what=f"blockwise fwd {case} pow2={pow2}")
 
 
-def _wgrad_case(splits, N, K, pow2, out_bf16, accumulate, seed=0):
+@pytest.mark.parametrize("case", FWD_CASES, ids=[f"{len(c[0])}x{c[1]}x{c[2]}" for c in FWD_CASES])
+def test_blockwise_fwd_pow2_formats(case):
+    """Power-of-two formats on both sides: the scales are applied by the MFMA."""
+    gpu, ref = _fwd_case(*case, pow2=True, p2=(True, True))
+    assert_gemm_close(gpu, ref, what=f"blockwise fwd P2 {case}")
+
+
+def test_blockwise_fwd_mixed_pow2_flags_take_the_general_path():
+    gpu, ref = _fwd_case([300, 0, 5], 384, 640, pow2=True, p2=(True, False))
+    assert_gemm_close(gpu, ref, what="blockwise fwd P2 x general")
+
+
+def _wgrad_case(splits, N, K, pow2, out_bf16, accumulate, seed=0, p2=False):
     splits = np.asarray(splits, dtype=np.int64)
     G, M = len(splits), int(splits.sum())
     dy = bf16_normal((M, N), 1.0, seed=seed + 3)
     x = bf16_normal((M, K), 1.0, seed=seed + 1)
     fl = POW2 if pow2 else 0
-    dq, ds, mpad = mxg.quantize_colwise_segpad(dev_bf16(dy), splits, "fp8_1x128", flags=fl)
-    xq, xs, _ = mxg.quantize_colwise_segpad(dev_bf16(x), splits, "fp8_1x128", flags=fl)
+    fmt = "fp8_1x128_p2" if p2 else "fp8_1x128"
+    dq, ds, mpad = mxg.quantize_colwise_segpad(dev_bf16(dy), splits, fmt, flags=fl)
+    xq, xs, _ = mxg.quantize_colwise_segpad(dev_bf16(x), splits, fmt, flags=fl)
     if out_bf16:
         mg0 = bf16_normal((G, N, K), 1.0, seed=seed + 4)
         mg = dev_bf16(mg0).reshape(G, N, K)
@@ -158,7 +175,7 @@ def _wgrad_case(splits, N, K, pow2, out_bf16, accumulate, seed=0):
     else:
         mg0_f = f32_normal((G, N, K), seed=seed + 4).astype(np.float64)
         mg = dev_f32(mg0_f)
-    mxg.grouped_wgrad(dq, ds, xq, xs, splits, N, K, mpad, mg, accumulate=accumulate, fmt="fp8_1x128")
+    mxg.grouped_wgrad(dq, ds, xq, xs, splits, N, K, mpad, mg, accumulate=accumulate, fmt=fmt)
     torch.cuda.synchronize()
     rd, rds = ob.quantize_colwise_segpad_128(dy, splits, pow2=pow2)
     rx, rxs = ob.quantize_colwise_segpad_128(x, splits, pow2=pow2)
@@ -193,6 +210,26 @@ def test_blockwise_wgrad(mode, pow2, case):
     assert_gemm_close(gpu, ref, what=f"blockwise wgrad {case} {mode} pow2={pow2}")
 
 
+# The power-of-two weight-gradient kernel faulted the GPU on its first run
+# (this test, 4x256x256 bf16 overwrite); the library routes the _P2 format to
+# the general kernel until the cause is found, and these tests stay skipped.
+P2_WGRAD_OFF = "power-of-two wgrad kernel switched off after a GPU fault (cause not yet found)"
+
+
+@pytest.mark.skip(reason=P2_WGRAD_OFF)
+@pytest.mark.parametrize("mode", ["bf16_overwrite", "fp32_accumulate", "fp32_overwrite"])
+@pytest.mark.parametrize("case", WG_CASES, ids=[f"{len(c[0])}x{c[1]}x{c[2]}" for c in WG_CASES])
+def test_blockwise_wgrad_pow2_format(mode, case):
+    out_bf16 = mode.startswith("bf16")
+    acc = mode.endswith("accumulate")
+    gpu, ref = _wgrad_case(*case, pow2=True, out_bf16=out_bf16, accumulate=acc, p2=True)
+    splits = np.asarray(case[0])
+    if acc:
+        for g in np.nonzero(splits == 0)[0]:
+            assert np.array_equal(gpu[g], ref[g])
+    assert_gemm_close(gpu, ref, what=f"blockwise wgrad P2 {case} {mode}")
+
+
 def test_blockwise_rejects_mixed_pairs():
     a = dev_bf16(bf16_normal((128, 256), 1.0, seed=1))
     aq, as_ = mxg.quantize_rowwise(a, "fp8_1x128")
@@ -220,11 +257,13 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def test_c5_full_size_fwd_sampled(c5):
+@pytest.mark.parametrize("p2", [False, True], ids=["general", "pow2"])
+def test_c5_full_size_fwd_sampled(c5, p2):
     G, M, K, N, sp, a, w = (c5[k] for k in ("G", "M", "K", "N", "sp", "a", "w"))
-    aq, as_ = mxg.quantize_rowwise(a, "fp8_1x128")
-    wq, ws = mxg.quantize_rowwise(w, "fp8_128x128")
-    out = mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt="fp8_1x128", w_fmt="fp8_128x128")
+    af, wf = ("fp8_1x128_p2", "fp8_128x128_p2") if p2 else ("fp8_1x128", "fp8_128x128")
+    aq, as_ = mxg.quantize_rowwise(a, af)
+    wq, ws = mxg.quantize_rowwise(w, wf)
+    out = mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt=af, w_fmt=wf)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     offs = np.concatenate([[0], np.cumsum(sp)])
@@ -249,14 +288,17 @@ def test_c5_full_size_fwd_sampled(c5):
         assert_gemm_close(gpu, ref, what=f"c5 fwd expert {g}")
 
 
-def test_c5_full_size_wgrad_sampled(c5):
+@pytest.mark.parametrize("p2", [False, pytest.param(True, marks=pytest.mark.skip(reason=P2_WGRAD_OFF))],
+                         ids=["general", "pow2"])
+def test_c5_full_size_wgrad_sampled(c5, p2):
     G, M, K, N, sp, a = (c5[k] for k in ("G", "M", "K", "N", "sp", "a"))
+    fmt = "fp8_1x128_p2" if p2 else "fp8_1x128"
     gen = torch.Generator(device="cuda").manual_seed(78)
     dy = torch.randn((M, N), generator=gen, device="cuda").to(torch.bfloat16)
-    dq, ds, mpad = mxg.quantize_colwise_segpad(dy, sp, "fp8_1x128")
-    xq, xs, _ = mxg.quantize_colwise_segpad(a, sp, "fp8_1x128")
+    dq, ds, mpad = mxg.quantize_colwise_segpad(dy, sp, fmt)
+    xq, xs, _ = mxg.quantize_colwise_segpad(a, sp, fmt)
     out = torch.empty((G, N, K), dtype=torch.bfloat16, device="cuda")
-    mxg.grouped_wgrad(dq, ds, xq, xs, sp, N, K, mpad, out, accumulate=False, fmt="fp8_1x128")
+    mxg.grouped_wgrad(dq, ds, xq, xs, sp, N, K, mpad, out, accumulate=False, fmt=fmt)
     torch.cuda.synchronize()
     rng = np.random.default_rng(6)
     row_offs, pad_offs = np.concatenate([[0], np.cumsum(sp)]), np.concatenate([[0], np.cumsum((sp + 127) // 128 * 128)])
