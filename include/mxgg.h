@@ -252,7 +252,8 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
  *               (MX scales u8 [mpad/32, K]).
  *   fmt         MXGG_MXFP4 (pad 32) or MXGG_FP8_1x128 (pad 128).
  *   mpad        mxgg_segpad_rows(m_splits, G, fmt).
- *   main_grad   [G, N, K]: fp32 when out_is_bf16 == 0, else bf16.
+ *   main_grad   [G, N, K]: fp32 when out_is_bf16 == 0, else bf16 (blockwise
+ *               formats only; MXGG_MXFP4 with out_is_bf16 = 1 is MXGG_ERR_FORMAT).
  *   accumulate  1: main_grad[g] += dW_g in place (experts with no tokens are
  *               left untouched); 0: main_grad[g] = dW_g (experts with no
  *               tokens are zero-filled). Every element is read/written by

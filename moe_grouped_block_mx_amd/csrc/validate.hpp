@@ -211,6 +211,10 @@ inline Check validate_wgrad(const void* dy_q, const void* dy_s, const void* x_q,
   if (fmt != MXGG_MXFP4 && fmt != MXGG_FP8_1x128)
     return fail(MXGG_ERR_FORMAT, "wgrad supports MXGG_MXFP4 and MXGG_FP8_1x128 (got %lld)", fmt);
   if (out_is_bf16 != 0 && out_is_bf16 != 1) return fail(MXGG_ERR_SHAPE, "out_is_bf16=%lld", out_is_bf16);
+  // bf16 output is the blockwise workload's; the MX weight gradient writes
+  // the fp32 main_grad it accumulates into (its 256x256 bf16 epilogue is not
+  // covered by the GPU tests)
+  if (fmt == MXGG_MXFP4 && out_is_bf16) return fail(MXGG_ERR_FORMAT, "MXGG_MXFP4 wgrad writes fp32 main_grad only");
   if (accumulate != 0 && accumulate != 1) return fail(MXGG_ERR_SHAPE, "accumulate=%lld", accumulate);
   const mxgg_format f = (mxgg_format)fmt;
   const int blk = f == MXGG_FP8_1x128 ? 128 : 32;

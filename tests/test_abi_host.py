@@ -60,6 +60,12 @@ def test_dual_quantizer_validation():
     assert L.mxgg_quantize_dual(NULL, 0, 64, 64, splits(0, 0), 2, 0, 0, NULL, NULL, NULL, NULL, 0, NULL) == 0
 
 
+def test_wgrad_mx_bf16_output_rejected():
+    m = splits(32, 0)
+    st = L.mxgg_grouped_wgrad(P, P, P, P, 0, m, 2, 64, 64, 32, P, 1, 0, NULL, 0, NULL)
+    assert st == 4 and "fp32" in last()
+
+
 def test_status_strings():
     for s in range(10):
         assert L.mxgg_status_string(s).decode().startswith(mx._lib.STATUS[s])
