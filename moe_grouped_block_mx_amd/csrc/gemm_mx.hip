@@ -137,8 +137,11 @@ struct TileCfg {
   static constexpr int DSB = F32S ? BS_BYTES / (NW * 256) : 0;
   static constexpr int DPS = DA + DB + DSA + DSB;
   static constexpr int EPI_BYTES = 16 * 36 * 4;  // per-wave epilogue scratch (16 rows x 32 fp32, padded)
+  // SCHED 7 keeps the epilogue scratch in the ring slot of the tile's last
+  // stage (free until the next tile's first DMA into it); the others append it
+  static constexpr bool EPI_IN_RING = SCHED == 7;
   static constexpr int EPI_OFF = STAGES * STAGE_BYTES;
-  static constexpr int SMEM_BYTES = EPI_OFF + NW * EPI_BYTES;
+  static constexpr int SMEM_BYTES = EPI_OFF + (EPI_IN_RING ? 0 : NW * EPI_BYTES);
   static_assert(A_BYTES % (NW * 1024) == 0 && B_BYTES % (NW * 1024) == 0, "chunk DMA split");
   static_assert(KSTEPS == 1 || KSTEPS == 2, "K steps per stage");
   static_assert(!F32S || BK == 64 || BK == 128, "blockwise stages split a 128-element scale block");
@@ -146,6 +149,8 @@ struct TileCfg {
   static_assert(DPS * (STAGES - 2) < 64, "vmcnt range");
   static_assert(F32S || (BM % 4 == 0 && BN % 4 == 0), "MX scale DMA moves four rows per lane");
   static_assert(STAGE_BYTES % 16 == 0, "stage alignment");
+  static_assert(SCHED != 7 || (KSTEPS == 2 && !F32S && STAGES >= 4 && NW * EPI_BYTES <= STAGE_BYTES),
+                "read-ahead schedule: two K steps per stage, MX scales, a 4+ stage ring");
 };
 
 // Operand bases and extents of one tile.
@@ -247,10 +252,14 @@ __device__ __forceinline__ const uint8_t* select_ptr(bool c, const uint8_t* a, c
 
 // A dummy stage (no work left) issues the same instructions from the zero
 // page, so that every step issues exactly DPS DMAs.
-template <class C>
+// PART: -1 every DMA of the stage; 0 the A chunks and the scales; 1 the B chunks.
+// `zero`: the zero page's address (g_zero_page), which a caller may hold in
+// registers across its loop.
+template <class C, int PART = -1>
 __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps& t, int s, uint8_t* st, int w,
-                                            int64_t ldas, int64_t ldbs, bool dummy = false) {
-  const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_zero_page);
+                                            int64_t ldas, int64_t ldbs, bool dummy = false,
+                                            const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_zero_page)) {
+  constexpr bool DO_A = PART != 1, DO_B = PART != 0;
   const int kca = dummy ? 0 : (C::AFP8 ? t.kc : t.kc / 2);
   const int kcb = dummy ? 0 : (C::BFP8 ? t.kc : t.kc / 2);
   const int ka0 = s * C::RBA, kb0 = s * C::RBB;
@@ -259,17 +268,22 @@ __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps&
   // 128-block s*BK/128
   const int nblk = dummy ? 0 : (C::F32S ? t.kc / 128 : t.kc / 32);
   const int bidx0 = C::F32S ? s * C::BK / 128 : s * C::SB;
-  unroll<C::DA>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    const uint8_t* src = select_ptr(ka0 + pl.kA[i] < kca, t.a + pl.offA[i] + ka0, zero);
-    dma16(src, st + C::A_OFF + (i * C::NW + w) * 1024);
-  });
-  unroll<C::DB>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    const uint8_t* src = select_ptr(kb0 + pl.kB[i] < kcb, t.b + pl.offB[i] + kb0, zero);
-    dma16(src, st + C::B_OFF + (i * C::NW + w) * 1024);
-  });
-  if constexpr (C::F32S) {
+  if constexpr (DO_A) {
+    unroll<C::DA>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const uint8_t* src = select_ptr(ka0 + pl.kA[i] < kca, t.a + pl.offA[i] + ka0, zero);
+      dma16(src, st + C::A_OFF + (i * C::NW + w) * 1024);
+    });
+  }
+  if constexpr (DO_B) {
+    unroll<C::DB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const uint8_t* src = select_ptr(kb0 + pl.kB[i] < kcb, t.b + pl.offB[i] + kb0, zero);
+      dma16(src, st + C::B_OFF + (i * C::NW + w) * 1024);
+    });
+  }
+  if constexpr (!DO_A) {
+  } else if constexpr (C::F32S) {
     unroll<C::DSA>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       dma4(select_ptr(bidx0 < nblk, t.as + pl.offAS[i] + bidx0 * 4, zero), st + C::AS_OFF + (i * C::NW + w) * 256);
@@ -289,6 +303,26 @@ __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps&
       dma4(select_ptr(b < nblk, base + (int64_t)b * ld + pl.sOff[i], zero), st + C::AS_OFF + (i * C::NW + w) * 256);
     });
   }
+}
+
+// Sources of the B chunk DMAs of stage s (zero page past the contraction or
+// for a dummy stage), and their issue into ring slot st.
+template <class C>
+__device__ __forceinline__ void stage_b_srcs(const DmaPlan<C>& pl, const TileOps& t, int s, bool dummy,
+                                             const uint8_t* zero, const uint8_t* (&src)[C::DB]) {
+  const int kcb = dummy ? 0 : (C::BFP8 ? t.kc : t.kc / 2);
+  const int kb0 = s * C::RBB;
+  unroll<C::DB>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    src[i] = select_ptr(kb0 + pl.kB[i] < kcb, t.b + pl.offB[i] + kb0, zero);
+  });
+}
+template <class C>
+__device__ __forceinline__ void issue_b_srcs(const uint8_t* const (&src)[C::DB], uint8_t* st, int w) {
+  unroll<C::DB>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    dma16(src[i], st + C::B_OFF + (i * C::NW + w) * 1024);
+  });
 }
 
 // B fragments of K step KK (E2M1: 16 bytes per lane; E4M3: 2 x 16 bytes).
@@ -473,6 +507,82 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// SCHED 7 (read-ahead): a stage's two K steps are split by the workgroup
+// barrier. Before it, the wave runs the MFMAs of K step 0 (operands read
+// during the previous stage) and reads the operands of K step 1; after it,
+// the MFMAs of K step 1 run while the wave reads the next stage's K step 0
+// operands and issues the DMAs of a later stage. No LDS read sits between the
+// barrier and the first MFMA after it. The barrier before K step 1 of stage s
+// admits the reads of stage s+1 (its DMAs have landed) and the DMAs into the
+// slot of stage s-1 (every wave's reads of it were consumed by MFMAs issued
+// before the barrier). Each K step's operands (fragments and scale bytes) are
+// written in one half and read in the other, so no register is copied.
+// ---------------------------------------------------------------------------
+template <class C>
+struct KOps {
+  v8i a[C::FM], b[C::FN];
+  uint32_t sa[C::FM], sb[C::FN];  // scale byte in bits 0..7 (op_sel 0)
+};
+
+// lane half h takes block h of K step 0 and block 2+h of K step 1
+template <class C, int KK>
+__device__ __forceinline__ void read_kops(const uint8_t* st, KOps<C>& f, int wm, int wn, int h, int l32) {
+  unroll<C::FM>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int r = wm * C::WTM + i * 32 + l32;
+    const uint8_t* row = st + C::A_OFF + r * C::RBA;
+    if constexpr (C::AFP8) {
+      const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r, 4 * KK + h) * 16);
+      const v4i hi = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r, 4 * KK + 2 + h) * 16);
+      f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r, 2 * KK + h) * 16);
+      f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    }
+    f.sa[i] = st[C::AS_OFF + (2 * KK + h) * C::BM + r];
+  });
+  load_b_frags<C, KK>(st, f.b, wn, h, l32);
+  unroll<C::FN>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    f.sb[j] = st[C::BS_OFF + (2 * KK + h) * C::BN + wn * C::WTN + j * 32 + l32];
+  });
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_kops(const KOps<C>& f, v16f (&acc)[C::FM][C::FN]) {
+  unroll<C::FM>([&](auto ic) {
+    unroll<C::FN>([&](auto jc) {
+      constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], C::AFP8 ? 0 : 4,
+                                                                  C::BFP8 ? 0 : 4, 0, (int)f.sa[i], 0,
+                                                                  (int)f.sb[j]);
+    });
+  });
+}
+
+// One half: the MFMAs of `use`, each followed by a share of the reads into
+// `fill` (from stage slot st) and of the DMAs issued by `issue`.
+template <class C, int KK, int SYNC, int ND, class Issue>
+__device__ __forceinline__ void ra_half(const uint8_t* st, const KOps<C>& use, KOps<C>& fill,
+                                        v16f (&acc)[C::FM][C::FN], int wm, int wn, int h, int l32, Issue&& issue) {
+  read_kops<C, KK>(st, fill, wm, wn, h, l32);
+  mfma_kops<C>(use, acc);
+  issue();
+  constexpr int NMF = C::FM * C::FN;
+  constexpr int NR = C::FM * (C::AFP8 ? 2 : 1) + C::FN * (C::BFP8 ? 2 : 1) + C::FM + C::FN;
+  constexpr int PER = (NR + NMF - 1) / NMF;
+  // ND DMAs spread evenly: one after MFMA m when (m+1)*ND/NMF steps up
+  unroll<NMF>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, SYNC);
+    __builtin_amdgcn_sched_group_barrier(0x100, PER, SYNC);
+    constexpr int nd = (m + 1) * ND / NMF - m * ND / NMF;
+    if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x060, nd, SYNC);
+  });
+}
+
 // Wait until this wave's DMAs of the stage about to be consumed have landed,
 // given how many stages it issued after that one (DPS instructions each).
 template <class C, int K>
@@ -514,7 +624,11 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
   // issuing side: the tile and stage whose DMAs go out next
   int it = first, is = 0, ins = 0, slot_issue = 0;
   TileOps iops{};
-  DmaPlan<C> plan;
+  // Zero until the first tile with a contraction is planned: a workgroup
+  // whose tiles all have empty contractions issues only dummy stages, whose
+  // zero-page selection holds only while every chunk offset (kA, kB) and
+  // scale block (sBlk) of the plan is >= 0.
+  DmaPlan<C> plan{};
   auto load_issue_tile = [&]() {
     while (it < total) {
       iops = src.ops(it);
@@ -539,6 +653,85 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
   load_issue_tile();
   int ahead = 0;  // stages issued and not yet consumed
   int slot_comp = 0;
+  if constexpr (C::SCHED == 7) {
+    auto advance_issue = [&](bool dummy) {
+      slot_issue = slot_issue + 1 == C::STAGES ? 0 : slot_issue + 1;
+      if (!dummy && ++is == ins) {
+        is = 0;
+        it += stride;
+        load_issue_tile();
+      }
+    };
+    for (int q = 0; q < C::STAGES - 1; ++q) {
+      const bool dummy = it >= total;
+      issue_stage<C>(plan, iops, is, smem + slot_issue * C::STAGE_BYTES, w, ldas, ldbs, dummy);
+      advance_issue(dummy);
+    }
+    // stage 0 (of the first tile, or a dummy) has landed: its K step 0
+    // operands go to registers
+    KOps<C> f0, f1;
+    // the zero page's address, held in registers (otherwise the compiler
+    // reloads it from the GOT inside the loop, and that scalar load makes
+    // the wave wait for every LDS read in flight)
+    const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_zero_page);
+    asm volatile("" : "+s"(zero));
+    const uint8_t* bsrc[C::DB];
+    unroll<C::DB>([&](auto ic) { bsrc[decltype(ic)::value] = zero; });
+    uint8_t* bdst = smem + slot_issue * C::STAGE_BYTES;
+    wait_vmcnt<(C::STAGES - 2) * C::DPS>();
+    raw_barrier();
+    read_kops<C, 0>(smem, f0, wm, wn, h, l32);
+    bool pending = false, pending_dummy = false;
+    for (int ct = first; ct < total; ct += stride) {
+      const TileOps cops = src.ops(ct);
+      const int cns = (cops.kc + C::BK - 1) / C::BK;
+      v16f acc[C::FM][C::FN];
+      unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
+      for (int s = 0; s < cns; ++s) {
+        // the issue state advances here (its branches stay out of the
+        // step's straight-line block)
+        if (pending) advance_issue(pending_dummy);
+        const bool dummy = it >= total;
+        uint8_t* dst = smem + slot_issue * C::STAGE_BYTES;
+        const int slot_next = slot_comp + 1 == C::STAGES ? 0 : slot_comp + 1;
+        // first half: the B chunks of the stage whose A chunks and scales
+        // went out in the previous step's second half (same stage, same
+        // slot; in the first step, zero-page DMAs into the slot the prologue
+        // left empty, which that stage's own DMAs follow in issue order)
+        ra_half<C, 1, 1, C::DB>(smem + slot_comp * C::STAGE_BYTES, f0, f1, acc, wm, wn, h, l32,
+                                [&]() __attribute__((always_inline)) { issue_b_srcs<C>(bsrc, bdst, w); });
+        __builtin_amdgcn_sched_barrier(0);
+        // the next stage has landed (this wave's DMAs: STAGES-3 stages were
+        // issued after it; the barrier covers the other waves')
+        wait_vmcnt<(C::STAGES - 3) * C::DPS>();
+        raw_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        ra_half<C, 0, 2, C::DPS - C::DB>(smem + slot_next * C::STAGE_BYTES, f1, f0, acc, wm, wn, h, l32,
+                                         [&]() __attribute__((always_inline)) {
+                                           issue_stage<C, 0>(plan, iops, is, dst, w, ldas, ldbs, dummy, zero);
+                                         });
+        __builtin_amdgcn_sched_barrier(0);
+        stage_b_srcs<C>(plan, iops, is, dummy, zero, bsrc);
+        bdst = dst;
+        pending = true;
+        pending_dummy = dummy;
+        slot_comp = slot_next;
+      }
+      // The slot before slot_comp held the last stage consumed (before any,
+      // the one slot the prologue left empty); its next DMA goes out after
+      // the next barrier. Every wave's reads of it were consumed by MFMAs
+      // issued before this barrier, so it is free for the epilogue.
+      const int slot_free = slot_comp == 0 ? C::STAGES - 1 : slot_comp - 1;
+      raw_barrier();
+      src.epilogue(ct, acc, smem + slot_free * C::STAGE_BYTES + w * C::EPI_BYTES, w, lane);
+      // A tile with an empty contraction consumed no stage, so the next
+      // step's first-half DMAs may target the slot its epilogue used (the
+      // prologue's empty slot): every wave finishes the epilogue first.
+      if (cns == 0) raw_barrier();
+    }
+    wait_vmcnt<0>();
+    return;
+  }
   if constexpr (C::SCHED == 5) {
     // Every step issues exactly one stage (a dummy from the zero page once no
     // work is left), so STAGES-2 stages always follow the one awaited and the
@@ -898,9 +1091,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// a4w4 (fwd, dgrad, wgrad): 8 waves, 3-stage ring, the next stage's DMAs
-// spread over the last K step's MFMAs
-using CfgA4 = TileCfg<256, 256, 2, 4, 128, 3, kA4W4, 1, 5>;
+// a4w4 forward and input gradient: 8 waves (128x64 each), 4-stage ring,
+// read-ahead schedule; weight gradient: 4 waves (128x128 each), same ring
+using CfgA4 = TileCfg<256, 256, 2, 4, 128, 4, kA4W4, 1, 7>;
+using CfgA4W = TileCfg<256, 256, 2, 2, 128, 4, kA4W4, 1, 7>;
 // a8w4 forward: a 128-deep stage holds 32 KiB of E4M3 A rows, so the ring
 // has two stages (the DMAs go out right after the barrier)
 using CfgA8 = TileCfg<256, 256, 2, 4, 128, 2, kA8W4, 1, 3>;
@@ -960,7 +1154,7 @@ static hipError_t launch_wgrad(const WgradParams& p, int num_cus, hipStream_t st
 }
 
 hipError_t launch_grouped_wgrad_mx(const WgradParams& p, int num_cus, hipStream_t st) {
-  return launch_wgrad<CfgA4>(p, num_cus, st);
+  return launch_wgrad<CfgA4W>(p, num_cus, st);
 }
 
 // The weight gradient always takes the per-128 partial path: its power-of-two
