@@ -341,15 +341,16 @@ def build_workload(name, dev, separate_quant=False):
         dw = torch.empty((G, N, K), dtype=torch.bfloat16, device=dev)
         ops = [
             # power-of-two scales (the blockwise default), declared by the _p2
-            # formats so the forward applies them inside the MFMA
+            # formats so the forward and the weight gradient apply them inside
+            # the MFMA
             ("quant_A_1x128", "quant", lambda: mxg.quantize_rowwise(a, "fp8_1x128_p2", q=aq, scales=as_)),
             ("quant_W_128x128", "quant", lambda: mxg.quantize_rowwise(w, "fp8_128x128_p2", q=wq, scales=ws)),
             ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt="fp8_1x128_p2",
                                                     w_fmt="fp8_128x128_p2", out=y)),
-            ("quant_dY_col", "quant", lambda: mxg.quantize_colwise_segpad(dy, sp, "fp8_1x128", q=dcq, scales=dcs)),
-            ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "fp8_1x128", q=xcq, scales=xcs)),
+            ("quant_dY_col", "quant", lambda: mxg.quantize_colwise_segpad(dy, sp, "fp8_1x128_p2", q=dcq, scales=dcs)),
+            ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "fp8_1x128_p2", q=xcq, scales=xcs)),
             ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, dw, accumulate=False,
-                                                        fmt="fp8_1x128")),
+                                                        fmt="fp8_1x128_p2")),
         ]
         nz = int((sp > 0).sum())
         q8 = 1 + 4 / 128

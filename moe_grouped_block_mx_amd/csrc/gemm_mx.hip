@@ -1106,6 +1106,7 @@ using CfgBlkW = TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 1>;
 // blockwise FP8 with power-of-two scales: the a4w4 loop (8 waves, 256x256)
 // with E4M3 on both sides; a 64-deep stage holds 16 KiB of each operand
 using CfgP2F = TileCfg<256, 256, 2, 4, 64, 3, kBlkP2, 1, 5, 128>;
+using CfgP2W = TileCfg<256, 256, 2, 4, 64, 3, kBlkP2, 1, 5, 1>;
 
 template <class C, class K, class P>
 static hipError_t launch_persistent(K kernel, const P& p, int64_t tiles, int num_cus, hipStream_t st) {
@@ -1157,11 +1158,8 @@ hipError_t launch_grouped_wgrad_mx(const WgradParams& p, int num_cus, hipStream_
   return launch_wgrad<CfgA4W>(p, num_cus, st);
 }
 
-// The weight gradient always takes the per-128 partial path: its power-of-two
-// variant (the forward's loop on the variable-K source) faulted the GPU on its
-// first test and is switched off until the cause is found.
 hipError_t launch_grouped_wgrad_blk(const WgradParams& p, bool pow2, int num_cus, hipStream_t st) {
-  (void)pow2;
+  if (pow2) return launch_wgrad<CfgP2W>(p, num_cus, st);
   return launch_wgrad<CfgBlkW>(p, num_cus, st);
 }
 

@@ -210,13 +210,9 @@ def test_blockwise_wgrad(mode, pow2, case):
     assert_gemm_close(gpu, ref, what=f"blockwise wgrad {case} {mode} pow2={pow2}")
 
 
-# The power-of-two weight-gradient kernel faulted the GPU on its first run
-# (this test, 4x256x256 bf16 overwrite); the library routes the _P2 format to
-# the general kernel until the cause is found, and these tests stay skipped.
-P2_WGRAD_OFF = "power-of-two wgrad kernel switched off after a GPU fault (cause not yet found)"
-
-
-@pytest.mark.skip(reason=P2_WGRAD_OFF)
+# The _P2 formats take the power-of-two kernel (the MFMA applies the scales).
+# Its 4x256x256 overwrite case gives one workgroup a single empty-contraction
+# tile, the case that once read an uninitialised DMA plan.
 @pytest.mark.parametrize("mode", ["bf16_overwrite", "fp32_accumulate", "fp32_overwrite"])
 @pytest.mark.parametrize("case", WG_CASES, ids=[f"{len(c[0])}x{c[1]}x{c[2]}" for c in WG_CASES])
 def test_blockwise_wgrad_pow2_format(mode, case):
@@ -288,8 +284,7 @@ def test_c5_full_size_fwd_sampled(c5, p2):
         assert_gemm_close(gpu, ref, what=f"c5 fwd expert {g}")
 
 
-@pytest.mark.parametrize("p2", [False, pytest.param(True, marks=pytest.mark.skip(reason=P2_WGRAD_OFF))],
-                         ids=["general", "pow2"])
+@pytest.mark.parametrize("p2", [False, True], ids=["general", "pow2"])
 def test_c5_full_size_wgrad_sampled(c5, p2):
     G, M, K, N, sp, a = (c5[k] for k in ("G", "M", "K", "N", "sp", "a"))
     fmt = "fp8_1x128_p2" if p2 else "fp8_1x128"
