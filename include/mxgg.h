@@ -219,6 +219,21 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
  *             when that is 0).
  * Errors: NULL, SHAPE, SPLITS, FORMAT, ALIGN, WORKSPACE, DEVICE, ARCH, HIP.
  */
+/*
+ * 128x128-block FP8 weights transposed for the input gradient: the blocks are
+ * square, so the transpose's 128x128 quantization is the same codes and the
+ * same scale per block ("Add ROCm Triton blockwise FP8 grouped GEMM", weight
+ * blocks used in both passes).
+ *   w_q, w_s    from mxgg_quantize_rowwise(W as [G*N, K], MXGG_FP8_128x128):
+ *               E4M3 [G*N, K] + f32 [G*N/128, K/128].
+ *   wt_q, wt_s  written: E4M3 [G*K, N] (expert g's rows [g*K, (g+1)*K)) +
+ *               f32 [G*K/128, N/128]. Caller-owned; must not overlap w.
+ * N % 128 == 0, K % 128 == 0, N, K < 2^23, G in [1, 512].
+ * Errors: NULL, SHAPE, ALIGN, DEVICE, ARCH, HIP.
+ */
+mxgg_status mxgg_transpose_128x128(const void* w_q, const void* w_s, int32_t G, int64_t N,
+                                   int64_t K, void* wt_q, void* wt_s, hipStream_t stream);
+
 mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt,
                              const void* w_q, const void* w_s, mxgg_format w_fmt,
                              const int64_t* m_splits, int32_t G, int64_t M, int64_t N,
@@ -226,16 +241,26 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
                              hipStream_t stream);
 
 /*
- * Grouped input gradient, NN: dx[r, k] = sum_n dY[r, n] * W_g[n, k].
- *   dy_q, dy_s     dY quantized row-wise along N: u8 [M, N/2] +
- *                  u8 [N/32, mxgg_mx_scale_stride(M)].
- *   wcol_q, wcol_s W quantized along N with mxgg_quantize_colwise_segpad on
- *                  W as [G*N, K] with splits {N, ..., N}: u8 [K, G*N/2] +
+ * Grouped input gradient, NN: dx[r, k] = sum_n dY[r, n] * W_g[n, k]
+ * (the backward of the expert layers on "Triton mxfp4 (and a8w4) grouped GEMM
+ * kernel" and, for the blockwise formats, "Add ROCm Triton blockwise FP8
+ * grouped GEMM", whose 128x128 weight blocks serve both orientations).
+ *   fmt            dY's format, which fixes the weights':
+ *                  MXGG_MXFP4 (a4w4) and MXGG_MXFP8 (a8w4): W in MXFP4;
+ *                  MXGG_FP8_1x128 / _P2: W as transposed 128x128 blocks.
+ *   dy_q, dy_s     dY quantized row-wise along N: MX, u8 [M, N/2] (E2M1) or
+ *                  [M, N] (E4M3) + u8 [N/32, mxgg_mx_scale_stride(M)];
+ *                  blockwise, E4M3 [M, N] + f32 [M, N/128].
+ *   wcol_q, wcol_s MX: W quantized along N with mxgg_quantize_colwise_segpad
+ *                  on W as [G*N, K] with splits {N, ..., N}: u8 [K, G*N/2] +
  *                  u8 [G*N/32, K] (expert g owns columns [g*N, (g+1)*N) and
  *                  scale blocks [g*N/32, (g+1)*N/32)).
- *   fmt            MXGG_MXFP4 (the only dgrad format).
+ *                  Blockwise: W^T from mxgg_transpose_128x128, E4M3
+ *                  [G*K, N] + f32 [G*K/128, N/128]; with _P2 (power-of-two
+ *                  scales on both sides) the MFMA applies the scales.
  *   dx             bf16 [M, K].
- * Shape rules as for the forward, and G*N/2 < 2^23. Errors as for the forward.
+ * Shape rules as for the forward, and (MX) G*N/2 < 2^23. Errors as for the
+ * forward.
  */
 mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* wcol_q,
                                const void* wcol_s, mxgg_format fmt, const int64_t* m_splits,
@@ -250,10 +275,13 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
  *               (MX scales u8 [mpad/32, N]).
  *   xcol_q/_s   X from mxgg_quantize_colwise_segpad: [K, mpad] operand
  *               (MX scales u8 [mpad/32, K]).
- *   fmt         MXGG_MXFP4 (pad 32) or MXGG_FP8_1x128 (pad 128).
+ *   fmt         MXGG_MXFP4 or MXGG_MXFP8 (both operands in that format: the
+ *               a4w4 and a8w4 weight gradients; pad 32), or MXGG_FP8_1x128
+ *               (pad 128).
  *   mpad        mxgg_segpad_rows(m_splits, G, fmt).
  *   main_grad   [G, N, K]: fp32 when out_is_bf16 == 0, else bf16 (blockwise
- *               formats only; MXGG_MXFP4 with out_is_bf16 = 1 is MXGG_ERR_FORMAT).
+ *               formats only; an MX format with out_is_bf16 = 1 is
+ *               MXGG_ERR_FORMAT).
  *   accumulate  1: main_grad[g] += dW_g in place (experts with no tokens are
  *               left untouched); 0: main_grad[g] = dW_g (experts with no
  *               tokens are zero-filled). Every element is read/written by

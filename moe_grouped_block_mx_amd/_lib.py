@@ -46,6 +46,7 @@ _SIGS = {
     "mxgg_quantize_dual": [_vp, _i64, _i64, _i64, _i64p, _i32, _i32, _u32, _vp, _vp, _vp, _vp, _i64, _vp],
     "mxgg_grouped_fwd": [_vp, _vp, _i32, _vp, _vp, _i32, _i64p, _i32, _i64, _i64, _i64, _vp, _vp, _sz, _vp],
     "mxgg_grouped_dgrad": [_vp, _vp, _vp, _vp, _i32, _i64p, _i32, _i64, _i64, _i64, _vp, _vp, _sz, _vp],
+    "mxgg_transpose_128x128": [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp],
     "mxgg_grouped_wgrad": [_vp, _vp, _vp, _vp, _i32, _i64p, _i32, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _sz,
                            _vp],
 }
@@ -236,8 +237,22 @@ def mxgg_grouped_fwd(a_q, a_s, w_q, w_s, m_splits, N, K, a_fmt="mxfp4", w_fmt="m
     return out
 
 
+def mxgg_transpose_128x128(w_q, w_s, G, N, K, wt_q=None, wt_s=None):
+    """128x128-block FP8 weights [G*N, K] (+ f32 [G*N/128, K/128]) transposed
+    to [G*K, N] (+ f32 [G*K/128, N/128]): the input gradient's weights."""
+    torch = _torch()
+    if wt_q is None:
+        wt_q = torch.empty((G * K, N), dtype=torch.uint8, device=w_q.device)
+    if wt_s is None:
+        wt_s = torch.empty((G * K // 128, N // 128), dtype=torch.float32, device=w_q.device)
+    _check(lib.mxgg_transpose_128x128(_ptr(w_q), _ptr(w_s), G, N, K, _ptr(wt_q), _ptr(wt_s), _stream(w_q)))
+    return wt_q, wt_s
+
+
 def mxgg_grouped_dgrad(dy_q, dy_s, wcol_q, wcol_s, m_splits, N, K, fmt="mxfp4", dx=None, ws=None):
-    """dx[M, K] (bf16) = per-expert dY . W_g with W quantized along N."""
+    """dx[M, K] (bf16) = per-expert dY . W_g. fmt is dY's format: "mxfp4" /
+    "mxfp8" with W quantized along N in MXFP4, or "fp8_1x128" / "fp8_1x128_p2"
+    with W^T from mxgg_transpose_128x128."""
     torch = _torch()
     arr, G = _splits(m_splits)
     M = dy_q.shape[0]
@@ -268,6 +283,7 @@ quantize_colwise_segpad = mxgg_quantize_colwise_segpad
 quantize_dual = mxgg_quantize_dual
 grouped_fwd = mxgg_grouped_fwd
 grouped_dgrad = mxgg_grouped_dgrad
+transpose_128x128 = mxgg_transpose_128x128
 grouped_wgrad = mxgg_grouped_wgrad
 workspace_size = mxgg_workspace_size
 segpad_rows = mxgg_segpad_rows

@@ -219,6 +219,19 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
   return c.ok() ? ok() : finish(c);
 }
 
+mxgg_status mxgg_transpose_128x128(const void* w_q, const void* w_s, int32_t G, int64_t N, int64_t K, void* wt_q,
+                                   void* wt_s, hipStream_t stream) {
+  Check c = validate_transpose_128x128(w_q, w_s, G, N, K, wt_q, wt_s);
+  if (!c.ok()) return finish(c);
+  int cus = 0;
+  c = device_checks(stream, {{w_q, "w_q"}, {w_s, "w_s"}, {wt_q, "wt_q"}, {wt_s, "wt_s"}}, &cus);
+  if (!c.ok()) return finish(c);
+  c = hip_status(launch_transpose_128x128(static_cast<const uint8_t*>(w_q), static_cast<const float*>(w_s), G, N, K,
+                                          static_cast<uint8_t*>(wt_q), static_cast<float*>(wt_s), stream),
+                 "transpose launch");
+  return c.ok() ? ok() : finish(c);
+}
+
 mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt, const void* w_q, const void* w_s,
                              mxgg_format w_fmt, const int64_t* m_splits, int32_t G, int64_t M, int64_t N, int64_t K,
                              void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -278,6 +291,8 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
 mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* wcol_q, const void* wcol_s,
                                mxgg_format fmt, const int64_t* m_splits, int32_t G, int64_t M, int64_t N, int64_t K,
                                void* dx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const bool p2 = is_p2(fmt);
+  fmt = (mxgg_format)base_format(fmt);
   Check c = validate_dgrad(dy_q, dy_s, wcol_q, wcol_s, (int)fmt, m_splits, G, M, N, K, dx, ws, ws_bytes,
                            mxgg_workspace_size(G));
   if (!c.ok()) return finish(c);
@@ -293,17 +308,30 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
   p.b = static_cast<const uint8_t*>(wcol_q);
   p.bs = static_cast<const uint8_t*>(wcol_s);
   p.c = static_cast<uint16_t*>(dx);
-  p.lda = N / 2;
+  p.ldc = K;
+  p.n_out = (int32_t)K;
+  p.kc = (int32_t)N;
+  p.sp = make_splits(m_splits, G);
+  if (fmt == MXGG_FP8_1x128) {
+    // dY E4M3 [M, N] + f32 [M, N/128]; W^T E4M3 [G*K, N] + f32 [G*K/128, N/128]
+    // (the 128x128 blocks of W, transposed: same codes, same scales)
+    p.lda = N;
+    p.ldas = N / 128 * 4;
+    p.ldb = N;
+    p.ldbs = N / 128 * 4;
+    p.b_gstride = K * N;
+    p.bs_gstride = K / 128 * (N / 128 * 4);
+    c = hip_status(launch_grouped_rows_blk(p, p2, cus, stream), "blockwise dgrad launch");
+    return c.ok() ? ok() : finish(c);
+  }
+  const bool a8 = fmt == MXGG_MXFP8;  // a8w4: dY E4M3, W E2M1
+  p.lda = a8 ? N : N / 2;
   p.ldas = mx_scale_stride(M);    // dY scales [N/32, R4(M)]
   p.ldb = (int64_t)G * N / 2;     // W column-wise: [K, G*N/2]
   p.ldbs = K;                     // its scales [G*N/32, K]
   p.b_gstride = N / 2;            // expert g owns columns [g*N, (g+1)*N)
   p.bs_gstride = N / 32 * K;      // ... and scale blocks [g*N/32, (g+1)*N/32)
-  p.ldc = K;
-  p.n_out = (int32_t)K;
-  p.kc = (int32_t)N;
-  p.sp = make_splits(m_splits, G);
-  c = hip_status(launch_grouped_rows_mx(p, false, cus, stream), "dgrad launch");
+  c = hip_status(launch_grouped_rows_mx(p, a8, cus, stream), "dgrad launch");
   return c.ok() ? ok() : finish(c);
 }
 
@@ -318,6 +346,7 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
   if (!c.ok()) return finish(c);
   if (mpad == 0 && accumulate) return ok();
   const bool blk = fmt == MXGG_FP8_1x128;
+  const bool fp8 = fmt == MXGG_MXFP8;
   int cus = 0;
   c = device_checks(stream, {{dycol_q, "dycol_q"}, {dycol_s, "dycol_s"}, {xcol_q, "xcol_q"}, {xcol_s, "xcol_s"},
                              {main_grad, "main_grad"}},
@@ -330,7 +359,7 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
   p.b = static_cast<const uint8_t*>(xcol_q);
   p.bs = static_cast<const uint8_t*>(xcol_s);
   p.c = main_grad;
-  p.lda = blk ? mpad : mpad / 2;                // E4M3 / E2M1 bytes
+  p.lda = blk || fp8 ? mpad : mpad / 2;         // E4M3 / E2M1 bytes
   p.ldb = p.lda;
   p.ldas = blk ? mpad / 128 * 4 : N;             // f32 [N, mpad/128] / u8 [mpad/32, N]
   p.ldbs = blk ? mpad / 128 * 4 : K;             // f32 [K, mpad/128] / u8 [mpad/32, K]
@@ -344,7 +373,7 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
   std::iota(order, order + G, 0);
   std::stable_sort(order, order + G, [&](int x, int y) { return m_splits[x] > m_splits[y]; });
   for (int32_t j = 0; j < G; ++j) p.order[j] = (int16_t)order[j];
-  c = hip_status(blk ? launch_grouped_wgrad_blk(p, p2, cus, stream) : launch_grouped_wgrad_mx(p, cus, stream),
+  c = hip_status(blk ? launch_grouped_wgrad_blk(p, p2, cus, stream) : launch_grouped_wgrad_mx(p, fp8, cus, stream),
                  "wgrad launch");
   return c.ok() ? ok() : finish(c);
 }

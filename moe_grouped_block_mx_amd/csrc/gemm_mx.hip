@@ -92,8 +92,10 @@ __device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* lds) {
 // per-128 partial that is then scaled and added, since fp32 scales are not
 // powers of two in general); or blockwise E4M3 x E4M3 whose fp32 scales are
 // powers of two, which the MFMA applies itself (the scale's exponent field is
-// its UE8M0 code), so no partial is needed.
-enum : int { kA4W4 = 0, kA8W4 = 1, kBlkFp8 = 2, kBlkP2 = 3 };
+// its UE8M0 code), so no partial is needed; or E4M3 x E4M3 with UE8M0 scales
+// per 32 (the weight gradient of a8w4 training, whose operands are both
+// activations or their gradients).
+enum : int { kA4W4 = 0, kA8W4 = 1, kBlkFp8 = 2, kBlkP2 = 3, kA8A8 = 4 };
 
 // OCC workgroups share a CU (the grid is OCC per CU): while one waits at a
 // barrier or drains its epilogue, the other's MFMAs keep the SIMDs busy.
@@ -104,7 +106,7 @@ template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, int KIND_, i
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
   static constexpr int SCHED = SCHED_, BDIV = BDIV_;
-  static constexpr bool AFP8 = KIND_ != kA4W4, BFP8 = KIND_ == kBlkFp8 || KIND_ == kBlkP2;
+  static constexpr bool AFP8 = KIND_ != kA4W4, BFP8 = KIND_ == kBlkFp8 || KIND_ == kBlkP2 || KIND_ == kA8A8;
   static constexpr bool BLK = KIND_ == kBlkFp8;                     // per-128 partial promotion
   static constexpr bool F32S = KIND_ == kBlkFp8 || KIND_ == kBlkP2;  // fp32 row-major scales, 1 per 128
   static constexpr int NW = WM * WN, THREADS = 64 * NW;
@@ -1095,6 +1097,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const
 // read-ahead schedule; weight gradient: 4 waves (128x128 each), same ring
 using CfgA4 = TileCfg<256, 256, 2, 4, 128, 4, kA4W4, 1, 7>;
 using CfgA4W = TileCfg<256, 256, 2, 2, 128, 4, kA4W4, 1, 7>;
+// MXFP8 weight gradient (E4M3 x E4M3, UE8M0 per 32): 64-deep stages (16 KiB
+// per operand) in a 3-stage ring, DMAs between the MFMAs
+using CfgA8W = TileCfg<256, 256, 2, 4, 64, 3, kA8A8, 1, 5>;
 // a8w4 forward: a 128-deep stage holds 32 KiB of E4M3 A rows, so the ring
 // has two stages (the DMAs go out right after the barrier)
 using CfgA8 = TileCfg<256, 256, 2, 4, 128, 2, kA8W4, 1, 3>;
@@ -1154,7 +1159,8 @@ static hipError_t launch_wgrad(const WgradParams& p, int num_cus, hipStream_t st
   return launch_persistent<C>(grouped_wgrad_kernel<C>, p, tiles, num_cus, st);
 }
 
-hipError_t launch_grouped_wgrad_mx(const WgradParams& p, int num_cus, hipStream_t st) {
+hipError_t launch_grouped_wgrad_mx(const WgradParams& p, bool fp8, int num_cus, hipStream_t st) {
+  if (fp8) return launch_wgrad<CfgA8W>(p, num_cus, st);
   return launch_wgrad<CfgA4W>(p, num_cus, st);
 }
 

@@ -62,7 +62,8 @@ hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols
                                    bool fp8, uint8_t* q, uint8_t* s, int64_t mpad, hipStream_t st);
 
 hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, int num_cus, hipStream_t st);
-hipError_t launch_grouped_wgrad_mx(const WgradParams& p, int num_cus, hipStream_t st);
+// fp8: E4M3 operands on both sides (MXFP8), else E2M1 (MXFP4)
+hipError_t launch_grouped_wgrad_mx(const WgradParams& p, bool fp8, int num_cus, hipStream_t st);
 
 // Blockwise FP8 (E4M3 codes, fp32 scales per 128 along the contraction).
 // Scale row strides (ldas, ldbs) are in bytes.
@@ -70,6 +71,10 @@ hipError_t launch_quant_rowwise_blk(const uint16_t* x, int64_t rows, int64_t col
                                     bool pow2, uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_quant_colwise_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
                                     uint8_t* q, float* s, int64_t mpad, hipStream_t st);
+// 128x128-block weights [G*N, K] (+ f32 [G*N/128, K/128]) -> [G*K, N] (+ f32
+// [G*K/128, N/128]); N, K multiples of 128
+hipError_t launch_transpose_128x128(const uint8_t* wq, const float* ws, int32_t G, int64_t N, int64_t K, uint8_t* tq,
+                                    float* ts, hipStream_t st);
 // pow2: every scale is a power of two (the MFMA applies it; no per-128 partial)
 hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, bool pow2, int num_cus, hipStream_t st);
 hipError_t launch_grouped_wgrad_blk(const WgradParams& p, bool pow2, int num_cus, hipStream_t st);

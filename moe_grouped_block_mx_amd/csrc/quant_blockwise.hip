@@ -79,6 +79,50 @@ __device__ __forceinline__ uint32_t amax8(const uint32_t (&wd)[4]) {
   return m;
 }
 
+// 128x128-block weights transposed for the input gradient (which contracts
+// over the weights' rows): the blocks are square, so W^T's 128x128
+// quantization is W's, transposed: the same codes and the same scale per
+// block. One workgroup per block: the 128 rows x 128 bytes are read with
+// 16-byte loads into LDS (dword pitch 33), then each thread transposes 4x4
+// byte squares in registers and writes output rows with 4-byte stores, 32
+// threads per 128-byte output row. HBM-bound: 1 B read and 1 B written per
+// element.
+__global__ __launch_bounds__(256) void transpose_128x128_kernel(const uint8_t* __restrict__ wq,
+                                                                const float* __restrict__ ws, int64_t N,
+                                                                int64_t K, uint8_t* __restrict__ tq,
+                                                                float* __restrict__ ts) {
+  __shared__ uint32_t tile[128][33];
+  const int64_t nbs = N / 128, kbs = K / 128;
+  const int64_t b = blockIdx.x;
+  const int64_t g = b / (nbs * kbs);
+  const int64_t rem = b - g * nbs * kbs;
+  const int64_t nb = rem / kbs, kb = rem - nb * kbs;
+  const uint8_t* src = wq + (g * N + nb * 128) * K + kb * 128;
+  for (int c = threadIdx.x; c < 1024; c += 256) {
+    const int r = c >> 3, q = c & 7;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)r * K + q * 16);
+    tile[r][4 * q] = v.x;
+    tile[r][4 * q + 1] = v.y;
+    tile[r][4 * q + 2] = v.z;
+    tile[r][4 * q + 3] = v.w;
+  }
+  __syncthreads();
+  uint8_t* dst = tq + (g * K + kb * 128) * N + nb * 128;
+  for (int c = threadIdx.x; c < 1024; c += 256) {
+    const int kq = c >> 5, nq = c & 31;  // output rows 4kq..4kq+3, bytes 4nq..4nq+3
+    uint32_t d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = tile[4 * nq + i][kq];  // input row 4nq+i, bytes 4kq..4kq+3
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t o = ((d[0] >> (8 * j)) & 0xffu) | (((d[1] >> (8 * j)) & 0xffu) << 8) |
+                         (((d[2] >> (8 * j)) & 0xffu) << 16) | (((d[3] >> (8 * j)) & 0xffu) << 24);
+      *reinterpret_cast<uint32_t*>(dst + (int64_t)(4 * kq + j) * N + 4 * nq) = o;
+    }
+  }
+  if (threadIdx.x == 0) ts[(g * kbs + kb) * nbs + nb] = ws[(g * nbs + nb) * kbs + kb];
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -265,6 +309,14 @@ hipError_t launch_quant_colwise_blk(const uint16_t* x, int64_t cols, int64_t ldx
     hipLaunchKernelGGL(quant_colwise_1x128_kernel<true>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, q, s);
   else
     hipLaunchKernelGGL(quant_colwise_1x128_kernel<false>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_128x128(const uint8_t* wq, const float* ws, int32_t G, int64_t N, int64_t K, uint8_t* tq,
+                                    float* ts, hipStream_t st) {
+  const int64_t blocks = (int64_t)G * (N / 128) * (K / 128);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_128x128_kernel, dim3((unsigned)blocks), dim3(256), 0, st, wq, ws, N, K, tq, ts);
   return hipGetLastError();
 }
 

@@ -186,10 +186,14 @@ inline Check validate_dgrad(const void* dy_q, const void* dy_s, const void* wc_q
                             const int64_t* m, int32_t G, int64_t M, int64_t N, int64_t K, const void* dx,
                             const void* ws, size_t ws_bytes, size_t ws_need) {
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
-  if (fmt != MXGG_MXFP4) return fail(MXGG_ERR_FORMAT, "dgrad supports MXGG_MXFP4 only (got %lld)", fmt);
-  MXGG_TRY(validate_gemm_dims(M, N, K, 32));
+  // fmt is dY's format: MXFP4 (a4w4) or MXFP8 (a8w4) with W column-wise in
+  // MXFP4; FP8_1x128 with the transposed 128x128 weight blocks
+  if (fmt != MXGG_MXFP4 && fmt != MXGG_MXFP8 && fmt != MXGG_FP8_1x128)
+    return fail(MXGG_ERR_FORMAT, "dgrad supports MXGG_MXFP4, MXGG_MXFP8 and MXGG_FP8_1x128 (got %lld)", fmt);
+  const bool blk = fmt == MXGG_FP8_1x128;
+  MXGG_TRY(validate_gemm_dims(M, N, K, blk ? 128 : 32));
   MXGG_TRY(check_splits(m, G, M, "dY"));
-  if ((int64_t)G * N / 2 >= kMaxRowStride)
+  if (!blk && (int64_t)G * N / 2 >= kMaxRowStride)
     return fail(MXGG_ERR_SHAPE, "G*N=%lld too large (G*N/2 < 2^23)", (int64_t)G * N);
   if (ws_bytes < ws_need) return fail(MXGG_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes,
                                       (long long)ws_need);
@@ -203,18 +207,33 @@ inline Check validate_dgrad(const void* dy_q, const void* dy_s, const void* wc_q
   return Check{};
 }
 
+// 128x128-block weight transpose: w [G*N, K] codes + f32 [G*N/128, K/128]
+// scales -> [G*K, N] + [G*K/128, N/128].
+inline Check validate_transpose_128x128(const void* w_q, const void* w_s, int32_t G, int64_t N, int64_t K,
+                                        const void* wt_q, const void* wt_s) {
+  if (G < 1 || G > MXGG_MAX_EXPERTS) return fail(MXGG_ERR_SHAPE, "G=%lld outside [1, 512]", G);
+  if (N <= 0 || K <= 0 || N % 128 || K % 128)
+    return fail(MXGG_ERR_SHAPE, "N=%lld and K=%lld must be positive multiples of 128", N, K);
+  if (N >= kMaxRowStride || K >= kMaxRowStride) return fail(MXGG_ERR_SHAPE, "N or K too large (< 2^23)");
+  MXGG_TRY(check_ptr(w_q, true, "w_q"));
+  MXGG_TRY(check_ptr(w_s, true, "w_s"));
+  MXGG_TRY(check_ptr(wt_q, true, "wt_q"));
+  MXGG_TRY(check_ptr(wt_s, true, "wt_s"));
+  return Check{};
+}
+
 inline Check validate_wgrad(const void* dy_q, const void* dy_s, const void* x_q, const void* x_s, int fmt,
                             const int64_t* m, int32_t G, int64_t N, int64_t K, int64_t mpad, const void* main_grad,
                             int32_t out_is_bf16, int32_t accumulate, const void* ws, size_t ws_bytes,
                             size_t ws_need) {
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
-  if (fmt != MXGG_MXFP4 && fmt != MXGG_FP8_1x128)
-    return fail(MXGG_ERR_FORMAT, "wgrad supports MXGG_MXFP4 and MXGG_FP8_1x128 (got %lld)", fmt);
+  if (fmt != MXGG_MXFP4 && fmt != MXGG_MXFP8 && fmt != MXGG_FP8_1x128)
+    return fail(MXGG_ERR_FORMAT, "wgrad supports MXGG_MXFP4, MXGG_MXFP8 and MXGG_FP8_1x128 (got %lld)", fmt);
   if (out_is_bf16 != 0 && out_is_bf16 != 1) return fail(MXGG_ERR_SHAPE, "out_is_bf16=%lld", out_is_bf16);
   // bf16 output is the blockwise workload's; the MX weight gradient writes
   // the fp32 main_grad it accumulates into (its 256x256 bf16 epilogue is not
   // covered by the GPU tests)
-  if (fmt == MXGG_MXFP4 && out_is_bf16) return fail(MXGG_ERR_FORMAT, "MXGG_MXFP4 wgrad writes fp32 main_grad only");
+  if (fmt != MXGG_FP8_1x128 && out_is_bf16) return fail(MXGG_ERR_FORMAT, "MX wgrad writes fp32 main_grad only");
   if (accumulate != 0 && accumulate != 1) return fail(MXGG_ERR_SHAPE, "accumulate=%lld", accumulate);
   const mxgg_format f = (mxgg_format)fmt;
   const int blk = f == MXGG_FP8_1x128 ? 128 : 32;

@@ -28,8 +28,8 @@ def test_exports_every_declared_function():
     names = mx.header_functions()
     assert {"mxgg_quantize_rowwise", "mxgg_quantize_colwise_segpad", "mxgg_grouped_fwd",
             "mxgg_grouped_dgrad", "mxgg_grouped_wgrad", "mxgg_workspace_size",
-            "mxgg_segpad_rows", "mxgg_mx_scale_stride", "mxgg_quantize_dual", "mxgg_status_string",
-            "mxgg_last_error"} <= set(names)
+            "mxgg_segpad_rows", "mxgg_mx_scale_stride", "mxgg_quantize_dual", "mxgg_transpose_128x128",
+            "mxgg_status_string", "mxgg_last_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -113,10 +113,26 @@ def test_empty_batch_validated_then_ok_without_gpu():
 
 def test_dgrad_rules():
     m = splits(4, 4)
-    assert L.mxgg_grouped_dgrad(P, P, P, P, 1, m, 2, 8, 64, 64, P, NULL, 0, NULL) == 4   # a8w4 dgrad
+    # a8w4 (dY MXFP8) and blockwise (dY FP8_1x128) pass validation; without a
+    # GPU the stream's device query is what fails (HIP)
+    assert L.mxgg_grouped_dgrad(P, P, P, P, 1, m, 2, 8, 64, 64, P, NULL, 0, NULL) == 9
+    assert L.mxgg_grouped_dgrad(P, P, P, P, 2, m, 2, 8, 128, 128, P, NULL, 0, NULL) == 9
+    assert L.mxgg_grouped_dgrad(P, P, P, P, 4, m, 2, 8, 128, 128, P, NULL, 0, NULL) == 9   # _P2
+    assert L.mxgg_grouped_dgrad(P, P, P, P, 2, m, 2, 8, 64, 128, P, NULL, 0, NULL) == 2    # blockwise N % 128
+    assert L.mxgg_grouped_dgrad(P, P, P, P, 3, m, 2, 8, 128, 128, P, NULL, 0, NULL) == 4   # 128x128 is W's
     assert L.mxgg_grouped_dgrad(P, P, P, P, 0, m, 2, 9, 64, 64, P, NULL, 0, NULL) == 3
     assert L.mxgg_grouped_dgrad(P, P, P, P, 0, m, 2, 8, 64, 33, P, NULL, 0, NULL) == 2
     assert L.mxgg_grouped_dgrad(P, P, NULL, P, 0, m, 2, 8, 64, 64, P, NULL, 0, NULL) == 1
+
+
+def test_transpose_128x128_rules():
+    t = lambda G=2, N=128, K=256, w=P, ws=P, o=P, os=P: L.mxgg_transpose_128x128(w, ws, G, N, K, o, os, NULL)
+    assert t(N=64) == 2 and "128" in last()
+    assert t(K=200) == 2
+    assert t(G=0) == 2 and t(G=513) == 2
+    assert t(w=NULL) == 1 and t(os=NULL) == 1
+    assert t(o=BAD) == 5
+    assert t() == 9                          # valid; no GPU to run it on
 
 
 def test_quantizer_rules():
@@ -141,7 +157,9 @@ def test_wgrad_rules():
                                           k.get("mp", mp), k.get("out", P), k.get("bf16", 0), k.get("acc", 1),
                                           NULL, 0, NULL)
     assert w(mp=128) == 2
-    assert w(fmt=1) == 4
+    assert w(fmt=3) == 4                     # 128x128 is a weight format
+    assert w(fmt=1, bf16=1) == 4             # MXFP8: fp32 main_grad only
+    assert w(fmt=1) == 9                     # MXFP8 x MXFP8 passes validation (no GPU here)
     assert w(out=NULL) == 1
     assert w(acc=2) == 2
     assert w(m=splits(5, -3, 40)) == 3
