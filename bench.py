@@ -64,9 +64,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--passes", default="all", help="profiling aid: fwd, dgrad, wgrad or all")
-    ap.add_argument("--workload", default="fc1", choices=["fc1", "a8w4", "blockwise"],
+    ap.add_argument("--workload", default="fc1", choices=["fc1", "a8w4", "a8w4_bwd", "blockwise", "blockwise_dgrad"],
                     help="fc1: the a4w4 training step (default, the headline); a8w4: the MXFP8 x MXFP4 forward; "
-                         "blockwise: the blockwise FP8 forward + weight gradient")
+                         "a8w4_bwd: its input and weight gradients; blockwise: the blockwise FP8 forward + "
+                         "weight gradient; blockwise_dgrad: the blockwise input gradient")
     ap.add_argument("--copy-only", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--separate-quant", action="store_true",
                     help="fc1: single-output quantizers instead of the dual-output ones")
@@ -326,6 +327,74 @@ def build_workload(name, dev, separate_quant=False):
         return dict(ops=ops, bytes_alg=bytes_alg, flops={"fwd": 2.0 * M * N * K}, config=config,
                     peak_tflops=PEAK_FP8_TFLOPS, dtype="mxfp8xmxfp4", hbm_gemms=set(),
                     metric="grouped a8w4 GEMM TFLOPS (fwd) and % of FP8 MFMA peak, 1 MI355X")
+
+    if name == "a8w4_bwd":
+        # the backward of a8w4 training at the a8w4 shapes: dY quantized to
+        # MXFP8 both ways, W along N to MXFP4, X column-wise to MXFP8
+        wl = WORKLOADS["a8w4"]
+        G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
+        sp = splits_for("a8w4")
+        mpad = mxg.segpad_rows(sp, "mxfp8")
+        a, w, dy = normal((M, K)), normal((G * N, K), wl["w_std"]), normal((M, N))
+        main_grad = torch.randn((G, N, K), generator=torch.Generator(device=dev).manual_seed(4), device=dev,
+                                dtype=torch.float32)
+        R4 = mxg.mx_scale_stride(M)
+        dq, ds = torch.empty((M, N), **u8), torch.empty((N // 32, R4), **u8)
+        dcq, dcs = torch.empty((N, mpad), **u8), torch.empty((mpad // 32, N), **u8)
+        wcq, wcs = torch.empty((K, G * N // 2), **u8), torch.empty((G * N // 32, K), **u8)
+        xcq, xcs = torch.empty((K, mpad), **u8), torch.empty((mpad // 32, K), **u8)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        ops = [
+            ("quant_dY_dual", "quant", lambda: mxg.quantize_dual(dy, sp, "mxfp8", q_row=dq, s_row=ds, q_col=dcq,
+                                                                 s_col=dcs)),
+            ("quant_W_col", "quant", lambda: mxg.quantize_colwise_segpad(w, [N] * G, "mxfp4", q=wcq, scales=wcs)),
+            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, fmt="mxfp8", dx=dx)),
+            ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "mxfp8", q=xcq, scales=xcs)),
+            ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, main_grad,
+                                                        accumulate=True, fmt="mxfp8")),
+        ]
+        nz = int((sp > 0).sum())
+        q8, q4 = 1 + 1 / 32, 0.5 + 1 / 32
+        bytes_alg = {"quant_dY_dual": M * N * (2 + q8) + mpad * N * q8, "quant_W_col": G * N * K * (2 + q4),
+                     "dgrad": M * N * q8 + nz * N * K * q4 + M * K * 2,
+                     "quant_X_col": M * K * 2 + mpad * K * q8,
+                     "wgrad": mpad * (N + K) * q8 + nz * N * K * 4 * 2}
+        config = {"workload": "MoE a8w4 backward (input gradient MXFP8 x MXFP4, weight gradient MXFP8 x MXFP8 "
+                              "with fp32 main_grad accumulate, with quantization)",
+                  "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz, "max_split": int(sp.max()),
+                  "mpad": mpad, "routing": "Zipf(1.1), 8 zeroed, seed 0"}
+        return dict(ops=ops, bytes_alg=bytes_alg, flops={"dgrad": 2.0 * M * N * K, "wgrad": 2.0 * M * N * K},
+                    config=config, peak_tflops=PEAK_FP8_TFLOPS, dtype="mxfp8xmxfp4", hbm_gemms={"wgrad"},
+                    metric="grouped a8w4 backward GEMM TFLOPS (dgrad/wgrad) and % of FP8 MFMA peak, 1 MI355X")
+
+    if name == "blockwise_dgrad":
+        # the blockwise input gradient at the blockwise shapes: dY 1x128 along
+        # N, and the 128x128 weight blocks transposed (same codes and scales)
+        wl = WORKLOADS["blockwise"]
+        G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
+        sp = splits_for("blockwise")
+        w, dy = normal((G * N, K), wl["w_std"]), normal((M, N))
+        wq, ws = mxg.quantize_rowwise(w, "fp8_128x128_p2")
+        del w
+        dq, ds = torch.empty((M, N), **u8), torch.empty((M, N // 128), **f32)
+        tq, ts = torch.empty((G * K, N), **u8), torch.empty((G * K // 128, N // 128), **f32)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        ops = [
+            ("quant_dY_1x128", "quant", lambda: mxg.quantize_rowwise(dy, "fp8_1x128_p2", q=dq, scales=ds)),
+            ("transpose_W", "quant", lambda: mxg.transpose_128x128(wq, ws, G, N, K, wt_q=tq, wt_s=ts)),
+            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, tq, ts, sp, N, K, fmt="fp8_1x128_p2", dx=dx)),
+        ]
+        nz = int((sp > 0).sum())
+        q8 = 1 + 4 / 128
+        bytes_alg = {"quant_dY_1x128": M * N * (2 + q8), "transpose_W": G * N * K * 2 + G * N * K / 16384 * 8,
+                     "dgrad": M * N * q8 + nz * N * K + M * K * 2}
+        config = {"workload": "MoE blockwise FP8 input gradient (1x128 dY x transposed 128x128 weight blocks, "
+                              "power-of-two scales)",
+                  "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz, "max_split": int(sp.max()),
+                  "routing": "Dirichlet(1), seed 0"}
+        return dict(ops=ops, bytes_alg=bytes_alg, flops={"dgrad": 2.0 * M * N * K}, config=config,
+                    peak_tflops=PEAK_FP8_TFLOPS, dtype="fp8_e4m3", hbm_gemms=set(),
+                    metric="grouped blockwise FP8 input-gradient GEMM TFLOPS and % of FP8 MFMA peak, 1 MI355X")
 
     if name == "blockwise":
         wl = WORKLOADS["blockwise"]
