@@ -1,0 +1,150 @@
+"""GroupedLinear-style training wrapper over the C ABI: the expert layer whose
+forward is the grouped forward GEMM and whose backward is the grouped input
+gradient plus the variable-K weight gradient, with
+
+- the weights quantized once per weight version and reused by every
+  microbatch until the optimizer changes them (a cache keyed on the tensor's
+  storage and version counter);
+- the weight gradient accumulated in place into an fp32 ``main_grad`` (the
+  fused accumulation of the pages' GroupedLinear integration), so autograd
+  sees no weight gradient;
+- an optional delayed weight gradient: its quantized operands are kept and
+  ``backward_dw()`` launches them later (for pipeline schedules that split
+  the input and weight gradients).
+
+Pages: "Triton mxfp4 (and a8w4) grouped GEMM kernel" (the GroupedLinear
+integration, a4w4 and a8w4) and "Add ROCm Triton blockwise FP8 grouped GEMM"
+(blockwise FP8, the weight-quantization cache across microbatches, fused
+main_grad accumulation). Every step runs in libmxgg's kernels; this file only
+orders the calls and keeps the quantized operands between forward and
+backward. Tensors must live on the GPU: the library rejects anything else.
+
+Recipes (activation, weight, gradient formats):
+  "a4w4"      MXFP4 x MXFP4 everywhere;
+  "a8w4"      activations and output gradients MXFP8, weights MXFP4 (the
+              weight gradient contracts two MXFP8 operands);
+  "blockwise" 1x128 activations / gradients and 128x128 weights, E4M3 with
+              power-of-two scales (the input gradient reads the weights'
+              blocks transposed).
+"""
+import torch
+
+from . import _lib as L
+
+RECIPES = {
+    "a4w4": dict(act="mxfp4", wgt="mxfp4", grad="mxfp4"),
+    "a8w4": dict(act="mxfp8", wgt="mxfp4", grad="mxfp8"),
+    "blockwise": dict(act="fp8_1x128_p2", wgt="fp8_128x128_p2", grad="fp8_1x128_p2"),
+}
+
+
+class _WeightCache:
+    """Quantized weights of one parameter for the forward and for the input
+    gradient, rebuilt when the parameter's storage or version changes."""
+
+    def __init__(self):
+        self.key = None
+        self.fwd = None   # (q, s)
+        self.dgrad = None  # (q, s)
+
+    def get(self, weight, recipe, G, N, K):
+        key = (weight.data_ptr(), weight._version, recipe)
+        if key != self.key:
+            r = RECIPES[recipe]
+            if recipe == "blockwise":
+                q, s = L.mxgg_quantize_rowwise(weight, r["wgt"])
+                self.fwd = (q, s)
+                self.dgrad = L.mxgg_transpose_128x128(q, s, G, N, K)
+            else:
+                # row-wise along K for the forward, along N (segments of N
+                # rows per expert) for the input gradient, from one read
+                qr, sr, qc, sc, _ = L.mxgg_quantize_dual(weight, [N] * G, r["wgt"])
+                self.fwd, self.dgrad = (qr, sr), (qc, sc)
+            self.key = key
+        return self.fwd, self.dgrad
+
+
+def _quantize_act(x, m_splits, fmt, need_col):
+    """Row-wise (forward or input gradient) and, when needed, column-wise
+    segment-padded (weight gradient) quantization of an activation or a
+    gradient."""
+    if fmt.startswith("fp8"):
+        row = L.mxgg_quantize_rowwise(x, fmt)
+        col = L.mxgg_quantize_colwise_segpad(x, m_splits, fmt) if need_col else None
+        return row, col
+    if need_col:
+        qr, sr, qc, sc, mpad = L.mxgg_quantize_dual(x, m_splits, fmt)
+        return (qr, sr), (qc, sc, mpad)
+    return L.mxgg_quantize_rowwise(x, fmt), None
+
+
+class _GroupedLinearFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, weight, m_splits, module):
+        G, N, K, recipe = module.num_experts, module.out_features, module.in_features, module.recipe
+        r = RECIPES[recipe]
+        (wq, ws), wdgrad = module._cache.get(weight, recipe, G, N, K)
+        need_wgrad = ctx.needs_input_grad[1]
+        xrow, xcol = _quantize_act(x, m_splits, r["act"], need_wgrad)
+        y = L.mxgg_grouped_fwd(xrow[0], xrow[1], wq, ws, m_splits, N, K, a_fmt=r["act"], w_fmt=r["wgt"])
+        ctx.module, ctx.m_splits, ctx.wdgrad, ctx.xcol = module, m_splits, wdgrad, xcol
+        ctx.need_dx = ctx.needs_input_grad[0]
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        module, m_splits = ctx.module, ctx.m_splits
+        G, N, K, recipe = module.num_experts, module.out_features, module.in_features, module.recipe
+        r = RECIPES[recipe]
+        dy = dy.contiguous()
+        need_wgrad = ctx.xcol is not None
+        drow, dcol = _quantize_act(dy, m_splits, r["grad"], need_wgrad)
+        dx = None
+        if ctx.need_dx:
+            dx = L.mxgg_grouped_dgrad(drow[0], drow[1], ctx.wdgrad[0], ctx.wdgrad[1], m_splits, N, K,
+                                      fmt=r["grad"])
+        if need_wgrad:
+            job = (dcol[0], dcol[1], ctx.xcol[0], ctx.xcol[1], m_splits, dcol[2])
+            if module.delay_wgrad:
+                module._pending.append(job)
+            else:
+                module._run_wgrad(job)
+        ctx.xcol = ctx.wdgrad = None
+        return dx, None, None, None
+
+
+class GroupedLinear(torch.nn.Module):
+    """y[r] = x[r] . W_g^T for the rows r of expert g; weight bf16 [G*N, K]
+    (expert g owns rows [g*N, (g+1)*N)), main_grad fp32 [G, N, K]."""
+
+    def __init__(self, num_experts, in_features, out_features, recipe="a4w4", delay_wgrad=False, device=None,
+                 weight_std=0.02, generator=None):
+        super().__init__()
+        if recipe not in RECIPES:
+            raise ValueError(f"recipe {recipe!r} is not one of {sorted(RECIPES)}")
+        self.num_experts, self.in_features, self.out_features = num_experts, in_features, out_features
+        self.recipe, self.delay_wgrad = recipe, delay_wgrad
+        device = torch.device("cuda") if device is None else torch.device(device)
+        w = torch.randn((num_experts * out_features, in_features), device=device, generator=generator) * weight_std
+        self.weight = torch.nn.Parameter(w.to(torch.bfloat16))
+        self.weight.main_grad = torch.zeros((num_experts, out_features, in_features), dtype=torch.float32,
+                                            device=device)
+        self._cache = _WeightCache()
+        self._pending = []
+
+    def forward(self, x, m_splits):
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != self.in_features:
+            raise ValueError(f"x must be bf16 [M, {self.in_features}], got {tuple(x.shape)} {x.dtype}")
+        m_splits = [int(m) for m in m_splits]
+        return _GroupedLinearFn.apply(x, self.weight, m_splits, self)
+
+    def _run_wgrad(self, job):
+        dq, ds, xq, xs, m_splits, mpad = job
+        L.mxgg_grouped_wgrad(dq, ds, xq, xs, m_splits, self.out_features, self.in_features, mpad,
+                             self.weight.main_grad, accumulate=True, fmt=RECIPES[self.recipe]["grad"])
+
+    def backward_dw(self):
+        """Launch the delayed weight gradients, oldest first."""
+        jobs, self._pending = self._pending, []
+        for job in jobs:
+            self._run_wgrad(job)

@@ -181,3 +181,17 @@ def test_segpad_rows_matches_oracle(fmt, pad):
     assert L.mxgg_segpad_rows(splits(1, -1), 2, 0) == -1
     assert L.mxgg_segpad_rows(splits(1), 1, 3) == -1
     assert L.mxgg_workspace_size(32) == 0
+
+
+def test_grouped_linear_fails_loudly_off_gpu():
+    # the wrapper has no CPU path: CPU tensors are refused, never computed
+    import torch
+    from moe_grouped_block_mx_amd.grouped_linear import GroupedLinear
+    with pytest.raises(ValueError):
+        GroupedLinear(2, 64, 64, recipe="nope", device="cpu")
+    layer = GroupedLinear(2, 64, 64, device="cpu")
+    x = torch.zeros((8, 64), dtype=torch.bfloat16)
+    with pytest.raises(Exception):
+        layer(x, [4, 4])
+    with pytest.raises(ValueError):
+        layer(torch.zeros((8, 32), dtype=torch.bfloat16), [4, 4])
