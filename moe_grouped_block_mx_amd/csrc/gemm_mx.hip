@@ -845,6 +845,23 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&o)[8]) {
   return make_uint4(cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]), cvt_bf16x2(o[6], o[7]));
 }
 
+// Tile order inside an expert's R x Cn tile grid: groups of kTileGroup row
+// tiles walked column by column (the group's rows fastest). The tiles that
+// run at the same time (consecutive ids, 32 per XCD) then form a
+// kTileGroup x 32/kTileGroup block instead of a run along one row of tiles,
+// so an expert's weight tiles are re-read from beyond the XCD's L2 once per
+// kTileGroup row tiles rather than once per 32/Cn. Measured at the fc1
+// shapes: input gradient 342 -> 308 us (Cn = 16), forward and weight
+// gradient unchanged; groups of 2 and 8 were slower.
+constexpr int kTileGroup = 4;
+__device__ __forceinline__ void grouped_tile(int local, int R, int Cn, int& rt, int& ct) {
+  const int r0 = local / (kTileGroup * Cn) * kTileGroup;
+  const int h = R - r0 < kTileGroup ? R - r0 : kTileGroup;
+  const int in = local - r0 * Cn;
+  ct = in / h;
+  rt = r0 + (in - ct * h);
+}
+
 // ---------------------------------------------------------------------------
 // forward / input gradient
 // ---------------------------------------------------------------------------
@@ -871,8 +888,9 @@ struct RowsSource {
   __device__ __forceinline__ Pos pos(int t) const {
     const int g = upper_bound_i32(tile_offs, G + 1, t) - 1;
     const int local = t - tile_offs[g];
-    const int mt = local / n_tiles;
-    return Pos{g, mt, local - mt * n_tiles};
+    Pos q{g, 0, 0};
+    grouped_tile(local, (tile_offs[g + 1] - tile_offs[g]) / n_tiles, n_tiles, q.mt, q.nt);
+    return q;
   }
   // Tile rows: MX tiles start at a multiple of 4 (the scale DMA moves four
   // rows per lane), so an expert's first tile may begin up to 3 rows before
@@ -965,9 +983,10 @@ struct WgradSource {
     const int j = upper_bound_i32(tile_offs, G + 1, t) - 1;
     const int g = p.order[j];
     const int local = t - tile_offs[j];
-    const int rt = local / tc;
+    int rt, ct;
+    grouped_tile(local, (p.n_rows + C::BM - 1) / C::BM, tc, rt, ct);
     const int64_t p0 = pad_pref[g];
-    return Pos{g, rt * C::BM, (local - rt * tc) * C::BN, p0, (int)(pad_pref[g + 1] - p0)};
+    return Pos{g, rt * C::BM, ct * C::BN, p0, (int)(pad_pref[g + 1] - p0)};
   }
   __device__ __forceinline__ TileOps ops(int t) const {
     const Pos q = pos(t);
