@@ -18,8 +18,11 @@ Readings taken where the page gives no formula:
   such that amax' * 2^t <= 448 (no element overflows before saturation);
   codes = RNE-saturating E4M3 of x * 2^t (exact);
 * fp32 mode (flag off): q = fp32(448 / amax'), codes = RNE-saturating E4M3 of
-  fp32(x * q), s = fp32(1 / q). This mode is our own reading:
-  parity unpinned.
+  fp32(x * q), s = fp32(1 / q). This mode is our own reading; its pins are
+  what the arithmetic fixes (power-of-two amax makes every step exact; the
+  amax element lands on 448; half-step reconstruction bound), see
+  tests/test_oracle_blockwise.py. Whether the product x * q is rounded to
+  fp32 (as the kernels do) is not distinguishable by those pins.
 
 Dequantized value = value(code) * s. The grouped products reuse
 ``oracle.grouped`` on the dequantized operands (segment pad 128).

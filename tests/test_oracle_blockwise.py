@@ -1,5 +1,12 @@
-"""Pins for oracle.blockwise (power-of-two mode); the fp32-scale mode is our own
-reading and is only sanity-checked here (parity unpinned)."""
+"""Pins for oracle.blockwise. Power-of-two mode: brute force of the exponent
+rule, the amax floor, block sharing, the segment-pad mapping and an exact
+blockwise product. The fp32-scale mode (our reading of a step the page leaves
+open) is pinned by what the arithmetic fixes: blocks whose amax is a power of
+two make every fp32 step exact, so the codes must be the E4M3 round-to-nearest-
+even of the exact products (found here by a search over the E4M3 value table)
+and the scale the fp32 nearest to 1/q; for any block the amax element lands
+on 448 and every element reconstructs within half an E4M3 step of its scaled
+value (plus the fp32 rounding of q and x*q)."""
 from fractions import Fraction
 
 import numpy as np
@@ -122,3 +129,84 @@ def test_fp32_scale_mode_sanity():
     q, s = bw.quantize_1x128(x, pow2=False)
     assert int(q[0, -1]) == 0x7E          # amax * (448/amax) = 448 exactly
     assert s[0, 0] == np.float32(1.0) / (np.float32(448.0) / np.float32(3.0))
+
+
+# ---------------------------------------------------------------------------
+# fp32-scale mode pins
+# ---------------------------------------------------------------------------
+_E4M3_MAGS = [Fraction(float(v)) for v in E4M3.mag_values]   # increasing, code = index
+
+
+def _e4m3_rne_code(y: Fraction) -> int:
+    """Nearest E4M3 magnitude by search, ties to the even code, saturating at
+    448; the sign bit from y."""
+    a = abs(y)
+    if a >= _E4M3_MAGS[-1]:
+        c = len(_E4M3_MAGS) - 1
+    else:
+        hi = next(i for i, v in enumerate(_E4M3_MAGS) if v >= a)
+        lo = max(hi - 1, 0)
+        dl, dh = a - _E4M3_MAGS[lo], _E4M3_MAGS[hi] - a
+        c = lo if dl < dh else hi if dh < dl else (lo if lo % 2 == 0 else hi)
+    return c | (0x80 if y < 0 and c else 0)
+
+
+def _nearest_f32(r: Fraction) -> float:
+    """The fp32 nearest to the positive rational r, by comparing neighbours."""
+    f = np.float32(float(r))
+    best = None
+    for cand in (np.nextafter(f, np.float32(0)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(cand)) - r)
+        if best is None or d < best[0]:
+            best = (d, cand)
+    return float(best[1])
+
+
+def _bf16_block(rng, amax_exp):
+    """128 bf16 values below 2^amax_exp with one element exactly +-2^amax_exp."""
+    x = rng.uniform(-1, 1, size=128).astype(np.float32) * np.float32(2.0 ** amax_exp)
+    b = fp32_to_bf16_bits(x)
+    v = bf16_bits_to_f64(b)
+    b[np.abs(v) >= 2.0 ** amax_exp] = fp32_to_bf16_bits(np.float32(0.5 * 2.0 ** amax_exp))
+    b[int(rng.integers(0, 128))] = fp32_to_bf16_bits(np.float32((1 if rng.random() < 0.5 else -1) * 2.0 ** amax_exp))
+    return b
+
+
+@pytest.mark.parametrize("amax_exp", [-12, -3, 0, 1, 5, 9, 20])
+def test_fp32_mode_power_of_two_amax_is_exact_rne(amax_exp):
+    rng = np.random.default_rng(100 + amax_exp)
+    b = _bf16_block(rng, amax_exp)
+    q, s = bw.quantize_1x128(b[None, :], pow2=False)
+    x = bf16_bits_to_f64(b)
+    qv = Fraction(448) / Fraction(2) ** amax_exp          # exact in fp32 (7 * 2^k)
+    for i in range(128):
+        assert int(q[0, i]) == _e4m3_rne_code(Fraction(float(x[i])) * qv), i
+    assert float(s[0, 0]) == _nearest_f32(1 / qv)
+
+
+def test_fp32_mode_amax_to_448_and_half_step_bound():
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        scale = float(2.0 ** rng.uniform(-20, 20))
+        x = fp32_to_bf16_bits((rng.standard_normal(128) * scale).astype(np.float32))
+        q, s = bw.quantize_1x128(x[None, :], pow2=False)
+        xv = bf16_bits_to_f64(x)
+        codes = q[0].astype(np.int64)
+        i = int(np.argmax(np.abs(xv)))
+        floor = Fraction(float(bw.AMAX_FLOOR))
+        amax = max(Fraction(float(np.abs(xv).max())), floor)
+        if amax > floor:
+            assert codes[i] & 0x7F == 0x7E                   # the amax element lands on 448
+        assert np.all(codes & 0x7F <= 0x7E)                  # nothing beyond 448, no NaN code
+        sf = Fraction(float(s[0, 0]))
+        for k in range(128):
+            y = Fraction(float(xv[k])) * 448 / amax             # exact scaled value
+            c = int(codes[k]) & 0x7F
+            lo = _E4M3_MAGS[max(c - 1, 0)]
+            hi = _E4M3_MAGS[min(c + 1, len(_E4M3_MAGS) - 1)]
+            half_step = max(_E4M3_MAGS[c] - lo, hi - _E4M3_MAGS[c]) / 2
+            err = abs(Fraction(float(E4M3.values[int(codes[k])])) * sf - Fraction(float(xv[k])))
+            # half an E4M3 step of the scaled value, plus the fp32 roundings of q,
+            # x*q and 1/q (three relative 2^-24 terms of the scaled value)
+            bound = (half_step + 3 * abs(y) / 2 ** 23) * sf * (1 + Fraction(1, 2 ** 20))
+            assert err <= bound, (trial, k)
