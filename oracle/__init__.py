@@ -32,7 +32,10 @@ source pages; no line numbers):
   grouped GEMM").
 
 Parity status: every function is pinned by the ``-m "not gpu"`` tests in
-``tests/test_oracle_*.py`` except the non-power-of-two blockwise-FP8 scale
-mode (``blockwise.quantize_1x128(..., pow2=False)`` and friends), whose
-IEEE-fp32 definition is our own reading: parity unpinned.
+``tests/test_oracle_*.py``. The non-power-of-two blockwise-FP8 scale mode
+(``blockwise.quantize_1x128(..., pow2=False)`` and friends) is our own
+reading of a step the page leaves open; its pins are what the arithmetic
+fixes (exact power-of-two-amax blocks, the amax element at 448, a half-step
+reconstruction bound), which leave open only whether x * q is rounded to
+fp32 before encoding.
 """
