@@ -226,10 +226,18 @@ __global__ __launch_bounds__(256) void quant_colwise_segpad_kernel(const uint16_
 // Scale padding rows of the row-wise output (the last rows' word) are zeroed
 // by the workgroup holding the tensor's last row.
 // ---------------------------------------------------------------------------
-template <int TR_, int TC_, int NT_, int PH_, int OCC_>
+template <int TR_, int TC_, int NT_, int PH_, int OCC_, int CMAP_ = 0>
 struct DualCfg {
   static constexpr int TR = TR_, TC = TC_, NT = NT_, PH = PH_;
   static constexpr int OCC = OCC_;                          // workgroups per CU
+  // column-wise lane map: 0, a wave takes one 32-row block of 128 columns
+  // (a store instruction writes 16 bytes into each of 64 output rows);
+  // 1, a lane takes one column pair of one block, four lanes the four
+  // blocks of a pair (a store instruction writes 64 contiguous bytes into
+  // each of 16 output rows); the LDS tile's 16-byte chunks are then XOR
+  // swizzled by 4 x block so the four blocks' reads fall on distinct banks
+  static constexpr int CMAP = CMAP_;
+  static_assert(CMAP == 0 || (TR == 128 && TC / 2 * (TR / 32) == NT && TC / 8 >= 16), "column map 1 shape");
   static constexpr int PITCH = TC + 8;                      // bf16 per LDS row
   static constexpr int LDS_BYTES = TR * PITCH * 2;
   static constexpr int CPR = TC / 8;                        // 16-byte chunks per row
@@ -357,7 +365,8 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
       for (int k = 0; k < 4; ++k) amax = max(amax, max(wd[k] & 0x7fffu, (wd[k] >> 16) & 0x7fffu));
       amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
       amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
-      uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * D::PITCH + ch * 8);
+      const int pch = D::CMAP ? ch ^ (4 * (row >> 5)) : ch;  // physical 16-byte chunk
+      uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * D::PITCH + pch * 8);
       dst[0] = v[i].x; dst[1] = v[i].y; dst[2] = v[i].z; dst[3] = v[i].w;
       if (!(cvalid && rin < blk_valid[par][b])) continue;
       const int64_t r = blk_row0[par][b] + rin;
@@ -378,32 +387,61 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
     if (tn < total) issue_loads(tn, par ^ 1);
 
     // column-wise from LDS while the next tile's loads are in flight
-#pragma unroll
-    for (int it = 0; it < D::WITEMS / D::NW; ++it) {
-      const int item = wv + it * D::NW;
-      const int b = item % D::NB, cq = item / D::NB;
+    if constexpr (D::CMAP == 1) {
+      const int b = lane & 3, pr = wv * 16 + (lane >> 2);  // block, column pair
       const int64_t p0 = pt0 + b * 32;
-      const int c = cq * 128 + 2 * lane;
-      if (p0 >= mpad || c >= ncol) continue;
-      uint32_t w2[32];
-      uint32_t a0 = 0, a1 = 0;
+      const int c = 2 * pr;
+      if (p0 < mpad && c < ncol) {
+        uint32_t w2[32];
+        uint32_t a0 = 0, a1 = 0;
 #pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        w2[r] = *reinterpret_cast<const uint32_t*>(tile + (b * 32 + r) * D::PITCH + c);
-        a0 = max(a0, w2[r] & 0x7fffu);
-        a1 = max(a1, (w2[r] >> 16) & 0x7fffu);
+        for (int r = 0; r < 32; ++r) {
+          const int row = b * 32 + r;
+          w2[r] = *reinterpret_cast<const uint32_t*>(tile + row * D::PITCH + ((c >> 3) ^ (4 * b)) * 8 + (c & 7));
+          a0 = max(a0, w2[r] & 0x7fffu);
+          a1 = max(a1, (w2[r] >> 16) & 0x7fffu);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int e = mx_shared_exp<F>(j ? a1 : a0);
+          const float sc = __uint_as_float(mx_scale_operand_bits(e));
+          uint32_t pairs[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            pairs[i] = j ? (w2[2 * i] >> 16) | (w2[2 * i + 1] & 0xffff0000u)
+                         : (w2[2 * i] & 0xffffu) | (w2[2 * i + 1] << 16);
+          encode32_store<FP4>(pairs, e, sc, qc + (c0 + c + j) * qld + (FP4 ? p0 / 2 : p0));
+          sc_[(p0 / 32) * cols + c0 + c + j] = (uint8_t)(e + 127);
+        }
       }
+    } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int e = mx_shared_exp<F>(j ? a1 : a0);
-        const float sc = __uint_as_float(mx_scale_operand_bits(e));
-        uint32_t pairs[16];
+      for (int it = 0; it < D::WITEMS / D::NW; ++it) {
+        const int item = wv + it * D::NW;
+        const int b = item % D::NB, cq = item / D::NB;
+        const int64_t p0 = pt0 + b * 32;
+        const int c = cq * 128 + 2 * lane;
+        if (p0 >= mpad || c >= ncol) continue;
+        uint32_t w2[32];
+        uint32_t a0 = 0, a1 = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)  // rows 2i (low) and 2i+1 (high) of column c + j
-          pairs[i] = j ? (w2[2 * i] >> 16) | (w2[2 * i + 1] & 0xffff0000u)
-                       : (w2[2 * i] & 0xffffu) | (w2[2 * i + 1] << 16);
-        encode32_store<FP4>(pairs, e, sc, qc + (c0 + c + j) * qld + (FP4 ? p0 / 2 : p0));
-        sc_[(p0 / 32) * cols + c0 + c + j] = (uint8_t)(e + 127);
+        for (int r = 0; r < 32; ++r) {
+          w2[r] = *reinterpret_cast<const uint32_t*>(tile + (b * 32 + r) * D::PITCH + c);
+          a0 = max(a0, w2[r] & 0x7fffu);
+          a1 = max(a1, (w2[r] >> 16) & 0x7fffu);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int e = mx_shared_exp<F>(j ? a1 : a0);
+          const float sc = __uint_as_float(mx_scale_operand_bits(e));
+          uint32_t pairs[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i)  // rows 2i (low) and 2i+1 (high) of column c + j
+            pairs[i] = j ? (w2[2 * i] >> 16) | (w2[2 * i + 1] & 0xffff0000u)
+                         : (w2[2 * i] & 0xffffu) | (w2[2 * i + 1] << 16);
+          encode32_store<FP4>(pairs, e, sc, qc + (c0 + c + j) * qld + (FP4 ? p0 / 2 : p0));
+          sc_[(p0 / 32) * cols + c0 + c + j] = (uint8_t)(e + 127);
+        }
       }
     }
     if (tn >= total) break;
@@ -432,10 +470,11 @@ hipError_t launch_quant_dual_persistent(const uint16_t* x, int64_t rows, int64_t
 }
 
 // 128 padded rows x 256 columns, 512 threads (one load per thread per 16
-// rows), one workgroup per CU, column tiles fastest: measured at the fc1
-// sizes X 104 us, dY 85 us, W 274 us, against 168 / 96 / 484 us for the two
-// single-output kernels (and 136 / 95 / 342 us for one tile per workgroup).
-using DualCfgProduct = DualCfg<128, 256, 512, 1, 1>;
+// rows), one workgroup per CU, column tiles fastest, the column-pair lane map
+// of the column-wise pass: measured at the fc1 sizes X 99 us, dY 79 us, W
+// 260 us (103 / 82 / 277 us with a wave per 32-row block of 128 columns),
+// against 168 / 96 / 484 us for the two single-output kernels.
+using DualCfgProduct = DualCfg<128, 256, 512, 1, 1, 1>;
 
 // ---------------------------------------------------------------------------
 // launchers
