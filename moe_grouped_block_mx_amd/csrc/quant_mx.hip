@@ -237,7 +237,9 @@ struct DualCfg {
   // each of 16 output rows); the LDS tile's 16-byte chunks are then XOR
   // swizzled by 4 x block so the four blocks' reads fall on distinct banks
   static constexpr int CMAP = CMAP_;
-  static_assert(CMAP == 0 || (TR == 128 && TC / 2 * (TR / 32) == NT && TC / 8 >= 16), "column map 1 shape");
+  static constexpr int CIPT = TC / 2 * (TR / 32) / NT;  // column map 1: (pair, block) items per thread
+  static_assert(CMAP == 0 || (TR % 128 == 0 && TC / 2 == NT / 4 && CIPT * NT == TC / 2 * (TR / 32)),
+                "column map 1 shape");
   static constexpr int PITCH = TC + 8;                      // bf16 per LDS row
   static constexpr int LDS_BYTES = TR * PITCH * 2;
   static constexpr int CPR = TC / 8;                        // 16-byte chunks per row
@@ -365,7 +367,7 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
       for (int k = 0; k < 4; ++k) amax = max(amax, max(wd[k] & 0x7fffu, (wd[k] >> 16) & 0x7fffu));
       amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
       amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
-      const int pch = D::CMAP ? ch ^ (4 * (row >> 5)) : ch;  // physical 16-byte chunk
+      const int pch = D::CMAP ? ch ^ (4 * ((row >> 5) & 3)) : ch;  // physical 16-byte chunk
       uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * D::PITCH + pch * 8);
       dst[0] = v[i].x; dst[1] = v[i].y; dst[2] = v[i].z; dst[3] = v[i].w;
       if (!(cvalid && rin < blk_valid[par][b])) continue;
@@ -388,7 +390,9 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
 
     // column-wise from LDS while the next tile's loads are in flight
     if constexpr (D::CMAP == 1) {
-      const int b = lane & 3, pr = wv * 16 + (lane >> 2);  // block, column pair
+#pragma unroll
+      for (int it = 0; it < D::CIPT; ++it) {
+      const int b = (lane & 3) + 4 * it, pr = wv * 16 + (lane >> 2);  // block, column pair
       const int64_t p0 = pt0 + b * 32;
       const int c = 2 * pr;
       if (p0 < mpad && c < ncol) {
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
 #pragma unroll
         for (int r = 0; r < 32; ++r) {
           const int row = b * 32 + r;
-          w2[r] = *reinterpret_cast<const uint32_t*>(tile + row * D::PITCH + ((c >> 3) ^ (4 * b)) * 8 + (c & 7));
+          w2[r] = *reinterpret_cast<const uint32_t*>(tile + row * D::PITCH + ((c >> 3) ^ (4 * (b & 3))) * 8 + (c & 7));
           a0 = max(a0, w2[r] & 0x7fffu);
           a1 = max(a1, (w2[r] >> 16) & 0x7fffu);
         }
@@ -413,6 +417,7 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
           encode32_store<FP4>(pairs, e, sc, qc + (c0 + c + j) * qld + (FP4 ? p0 / 2 : p0));
           sc_[(p0 / 32) * cols + c0 + c + j] = (uint8_t)(e + 127);
         }
+      }
       }
     } else {
 #pragma unroll
