@@ -157,6 +157,20 @@ def summarize(kernel, stats_csv, fetch_csv, write_csv, copy_fetch_csv, copy_writ
     lines = [
         f"kernel: {kernel}",
         "workload: MoE FC1 a4w4, 32 experts, 32768 routed rows, K=4096, N=3072 (bench.py default step)",
+        "# commands (GPU run, R = repository root, each rocprofv3 pass in a process of its own):",
+        "#   cd /tmp && export TMPDIR=/tmp",
+        "#   rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_stats -o run"
+        " -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_fetch -o run"
+        " -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_write -o run"
+        " -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_cfetch -o run"
+        " -- python3 $R/bench.py --copy-only",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_cwrite -o run"
+        " -- python3 $R/bench.py --copy-only",
+        f"#   python3 $R/bench.py --summarize {kernel} <prof_stats kernel_stats.csv> <prof_fetch counter_collection.csv>"
+        " <prof_write ...> <prof_cfetch ...> <prof_cwrite ...>",
         f"source_sha256_16: {source_hash(kernel)}",
         f"kernel_name_prefix: {prefix}",
         f"stats_calls: {stats['Calls'] if stats else 'n/a'}",

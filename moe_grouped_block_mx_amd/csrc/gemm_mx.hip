@@ -974,6 +974,10 @@ struct WgradSource {
   const WgradParams& p;
   const int64_t* pad_pref;   // LDS: padded segment offsets (natural expert order)
   const int32_t* tile_offs;  // LDS: tile offsets in longest-first order
+  const int16_t* order;      // LDS: the expert at each position of that order
+                             // (a kernel-argument read with a lane-varying
+                             // index is a vector memory load, and its wait
+                             // would drain every DMA in flight)
   int G, tc, ntot;
 
   __device__ __forceinline__ int count() const { return ntot; }
@@ -981,7 +985,7 @@ struct WgradSource {
   struct Pos { int g, row0, col0; int64_t p0; int kc; };
   __device__ __forceinline__ Pos pos(int t) const {
     const int j = upper_bound_i32(tile_offs, G + 1, t) - 1;
-    const int g = p.order[j];
+    const int g = order[j];
     const int local = t - tile_offs[j];
     int rt, ct;
     grouped_tile(local, (p.n_rows + C::BM - 1) / C::BM, tc, rt, ct);
@@ -1092,8 +1096,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const
   __shared__ int64_t tile_pref[kMaxExperts + 1];
   __shared__ int64_t wtot[C::THREADS / 64];
   __shared__ int32_t tile_offs[kMaxExperts + 1];
+  __shared__ int16_t order[kMaxExperts];
 
   const int G = p.sp.G;
+  for (int j = threadIdx.x; j < G; j += C::THREADS) order[j] = p.order[j];
   const int tr = (p.n_rows + C::BM - 1) / C::BM, tc = (p.n_cols + C::BN - 1) / C::BN;
   constexpr int PAD = C::F32S ? 128 : 32;  // segment pad multiple of the column-wise operands
   block_prefix64<C::THREADS>(G, [&](int g) { return (int64_t)((p.sp.m[g] + PAD - 1) & ~(PAD - 1)); }, pad_pref,
@@ -1105,7 +1111,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const
   for (int j = threadIdx.x; j <= G; j += C::THREADS) tile_offs[j] = (int32_t)tile_pref[j];
   __syncthreads();
 
-  WgradSource<C> src{p, pad_pref, tile_offs, G, tc, tile_offs[G]};
+  WgradSource<C> src{p, pad_pref, tile_offs, order, G, tc, tile_offs[G]};
   persistent_loop<C>(src, smem, p.lda, p.ldas, p.ldb, p.ldbs);
 }
 
