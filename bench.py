@@ -28,12 +28,16 @@ roofline.traffic: HBM bytes per launch of the dominant kernel, read from the
 committed rocprofv3 summary profiles/<kernel>_fc1_traffic.txt (FETCH_SIZE and
 WRITE_SIZE per dispatch, each scaled by the same counter's reading for a plain
 1 GiB copy); null when that summary was taken from a different kernel source.
+kernels.<gemm>.rocprof_mfma_busy_pct (fc1): MFMA-busy of that GEMM from the
+committed summary profiles/gemm_fc1_mfma_busy.txt (SQ_VALU_MFMA_BUSY_CYCLES
+over GRBM_GUI_ACTIVE x SIMDs), null likewise.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--workload fc1|a8w4|blockwise]
                        [--separate-quant]
        python bench.py --copy-only            (calibration copy for --pmc runs)
        python bench.py --summarize KERNEL STATS_CSV FETCH_CSV WRITE_CSV
                        COPY_FETCH_CSV COPY_WRITE_CSV   (writes the summary text)
+       python bench.py --summarize-mfma PMC_CSV        (MFMA-busy summary of the fc1 GEMMs)
 """
 from __future__ import annotations
 
@@ -71,6 +75,8 @@ def parse():
     ap.add_argument("--copy-only", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--separate-quant", action="store_true",
                     help="fc1: single-output quantizers instead of the dual-output ones")
+    ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
+                    help="print the MFMA-busy summary of the fc1 GEMMs from a rocprofv3 counter csv")
     ap.add_argument("--summarize", nargs=6, metavar=("KERNEL", "STATS", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="print the profile summary of KERNEL from rocprofv3 csv outputs")
     return ap.parse_args()
@@ -189,6 +195,80 @@ def summarize(kernel, stats_csv, fetch_csv, write_csv, copy_fetch_csv, copy_writ
         f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
     ]
     return "\n".join(lines) + "\n"
+
+
+SIMDS = 256 * 4  # MI355X: 256 compute units x 4 SIMDs
+
+
+def mfma_summary_path():
+    return os.path.join(ROOT, "profiles", "gemm_fc1_mfma_busy.txt")
+
+
+def summarize_mfma(pmc_csv):
+    """MFMA-busy of the fc1 GEMMs from one rocprofv3 pass over
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: busy cycles summed over the
+    SIMDs / (GPU-active cycles x SIMDs), the MfmaUtil definition of
+    rocprofiler-sdk for gfx950, median over the dispatches. rocprofv3 reports
+    each counter summed over its instances, so GRBM_GUI_ACTIVE (one per XCD)
+    is divided by the XCD count; XCD and SIMD counts come from the run's
+    agent_info.csv."""
+    xcc, simds = 8, SIMDS
+    info = os.path.join(os.path.dirname(pmc_csv), os.path.basename(pmc_csv).replace("counter_collection", "agent_info"))
+    if os.path.exists(info):
+        with open(info, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Agent_Type") == "GPU":
+                    xcc, simds = int(row["Num_Xcc"]), int(row["Simd_Count"])
+    def per_dispatch(prefix, counter, reduce_fn):
+        vals = {}
+        with open(pmc_csv, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row["Kernel_Name"].startswith(prefix) and row["Counter_Name"] == counter:
+                    vals.setdefault(int(row["Dispatch_Id"]), []).append(float(row["Counter_Value"]))
+        return [reduce_fn(vals[d]) for d in sorted(vals)]
+    lines = [
+        "workload: MoE FC1 a4w4, 32 experts, 32768 routed rows, K=4096, N=3072 (bench.py default step)",
+        "# commands (GPU run, R = repository root):",
+        "#   cd /tmp && export TMPDIR=/tmp",
+        "#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof_mfma"
+        " -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        "#   python3 $R/bench.py --summarize-mfma <prof_mfma counter_collection.csv>",
+        f"# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcc} XCDs x {simds} SIMDs), median over dispatches",
+        "# (the busy count is 32 cycles per 32x32x64 FP4 MFMA issued, padding rows included; the active cycles run",
+        "#  at the shader clock under load, so busy x clock / 2.4 GHz is the fraction of the published peak's rate)",
+    ]
+    for kernel in ("fwd", "dgrad", "wgrad"):
+        prefix = KERNEL_SOURCES[kernel][0]
+        busy = per_dispatch(prefix, "SQ_VALU_MFMA_BUSY_CYCLES", sum)
+        active = per_dispatch(prefix, "GRBM_GUI_ACTIVE", max)
+        if kernel == "fwd":
+            busy, active = busy[0::2], active[0::2]
+        elif kernel == "dgrad":
+            busy, active = busy[1::2], active[1::2]
+        util = [100.0 * b / (a / xcc * simds) for b, a in zip(busy, active)]
+        lines += [f"{kernel}_source_sha256_16: {source_hash(kernel)}",
+                  f"{kernel}_dispatches: {len(util)}",
+                  f"{kernel}_mfma_busy_cycles_median: {float(np.median(busy)):.0f}",
+                  f"{kernel}_gpu_active_cycles_per_xcd_median: {float(np.median(active)) / xcc:.0f}",
+                  f"{kernel}_mfma_busy_pct_median: {float(np.median(util)):.2f}"]
+    return "\n".join(lines) + "\n"
+
+
+def read_mfma_busy(kernel):
+    """MFMA-busy percent of an fc1 GEMM from the committed summary, or None
+    when it was taken from a different kernel source."""
+    path = mfma_summary_path()
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get(f"{kernel}_source_sha256_16") != source_hash(kernel):
+        return None
+    return float(kv[f"{kernel}_mfma_busy_pct_median"])
 
 
 def copy_only():
@@ -456,6 +536,9 @@ def main():
     if args.summarize:
         sys.stdout.write(summarize(*args.summarize))
         return
+    if args.summarize_mfma:
+        sys.stdout.write(summarize_mfma(args.summarize_mfma))
+        return
     if args.copy_only:
         copy_only()
         return
@@ -518,6 +601,8 @@ def main():
         if kind == "gemm":
             entry["TFLOPS"] = round(flops[name] / d / 1e12, 1)
             entry["pct_mfma_peak"] = round(100 * flops[name] / d / 1e12 / W["peak_tflops"], 2)
+            if args.workload == "fc1" and args.passes == "all" and not args.separate_quant:
+                entry["rocprof_mfma_busy_pct"] = read_mfma_busy(name)
         per[name] = entry
 
     step_flops = sum(flops[n] for n, k, _ in ops if k == "gemm")
