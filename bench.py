@@ -76,7 +76,7 @@ def parse():
     ap.add_argument("--separate-quant", action="store_true",
                     help="fc1: single-output quantizers instead of the dual-output ones")
     ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
-                    help="print the MFMA-busy summary of the fc1 GEMMs from a rocprofv3 counter csv")
+                    help="print the MFMA-busy summary of the workload's GEMMs from a rocprofv3 counter csv")
     ap.add_argument("--summarize", nargs=6, metavar=("KERNEL", "STATS", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="print the profile summary of KERNEL from rocprofv3 csv outputs")
     return ap.parse_args()
@@ -198,13 +198,20 @@ def summarize(kernel, stats_csv, fetch_csv, write_csv, copy_fetch_csv, copy_writ
 
 
 SIMDS = 256 * 4  # MI355X: 256 compute units x 4 SIMDs
+WORKLOAD_TITLES = {
+    "fc1": "MoE FC1 a4w4, 32 experts, 32768 routed rows, K=4096, N=3072",
+    "a8w4": "a8w4 forward, 128 experts, 65536 routed rows, K=7168, N=2048",
+    "a8w4_bwd": "a8w4 backward (MXFP8 x MXFP4 input gradient, MXFP8 weight gradient), 128 experts, 65536 rows",
+    "blockwise": "blockwise FP8 forward and weight gradient, 64 experts, 32768 rows, K=7168, N=4096",
+    "blockwise_dgrad": "blockwise FP8 input gradient, 64 experts, 32768 rows, K=7168, N=4096",
+}
 
 
 def mfma_summary_path():
     return os.path.join(ROOT, "profiles", "gemm_fc1_mfma_busy.txt")
 
 
-def summarize_mfma(pmc_csv):
+def summarize_mfma(pmc_csv, workload="fc1"):
     """MFMA-busy of the fc1 GEMMs from one rocprofv3 pass over
     SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: busy cycles summed over the
     SIMDs / (GPU-active cycles x SIMDs), the MfmaUtil definition of
@@ -226,17 +233,35 @@ def summarize_mfma(pmc_csv):
                 if row["Kernel_Name"].startswith(prefix) and row["Counter_Name"] == counter:
                     vals.setdefault(int(row["Dispatch_Id"]), []).append(float(row["Counter_Value"]))
         return [reduce_fn(vals[d]) for d in sorted(vals)]
+    wl_flag = "" if workload == "fc1" else f" --workload {workload}"
+    prof_dir = "prof_mfma" if workload == "fc1" else f"prof_mfma_{workload}"
     lines = [
-        "workload: MoE FC1 a4w4, 32 experts, 32768 routed rows, K=4096, N=3072 (bench.py default step)",
+        f"workload: {WORKLOAD_TITLES[workload]} (bench.py{wl_flag or ' default step'})",
         "# commands (GPU run, R = repository root):",
         "#   cd /tmp && export TMPDIR=/tmp",
-        "#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof_mfma"
-        " -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-        "#   python3 $R/bench.py --summarize-mfma <prof_mfma counter_collection.csv>",
+        "#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/"
+        f"{prof_dir} -o run -- python3 $R/bench.py{wl_flag} --steps 3 --warmup 1 --no-cpu-baseline",
+        f"#   python3 $R/bench.py --summarize-mfma <{prof_dir} counter_collection.csv>{wl_flag}",
         f"# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcc} XCDs x {simds} SIMDs), median over dispatches",
-        "# (the busy count is 32 cycles per 32x32x64 FP4 MFMA issued, padding rows included; the active cycles run",
-        "#  at the shader clock under load, so busy x clock / 2.4 GHz is the fraction of the published peak's rate)",
+        "# (busy cycles accrue per MFMA issued, padding rows included: 32 for a 32x32x64 FP4 MFMA, 64 with an",
+        "#  E4M3 operand; the active cycles run at the shader clock under load, so busy x clock / 2.4 GHz is the",
+        "#  fraction of that format's peak rate)",
     ]
+    # every mxgg GEMM kernel of the run, by name
+    names = []
+    with open(pmc_csv, newline="") as fh:
+        for row in csv.DictReader(fh):
+            n = row["Kernel_Name"]
+            if n.startswith(("void mxgg::grouped_rows_kernel", "void mxgg::grouped_wgrad_kernel")) and n not in names:
+                names.append(n)
+    lines.append("# per kernel: dispatches, median mfma_busy %, kernel")
+    for n in names:
+        busy = per_dispatch(n, "SQ_VALU_MFMA_BUSY_CYCLES", sum)
+        active = per_dispatch(n, "GRBM_GUI_ACTIVE", max)
+        util = [100.0 * b / (a / xcc * simds) for b, a in zip(busy, active)]
+        lines.append(f"#   {len(util):3d} {float(np.median(util)):6.2f}  {n[:140]}")
+    if workload != "fc1":
+        return "\n".join(lines) + "\n"
     for kernel in ("fwd", "dgrad", "wgrad"):
         prefix = KERNEL_SOURCES[kernel][0]
         busy = per_dispatch(prefix, "SQ_VALU_MFMA_BUSY_CYCLES", sum)
@@ -537,7 +562,7 @@ def main():
         sys.stdout.write(summarize(*args.summarize))
         return
     if args.summarize_mfma:
-        sys.stdout.write(summarize_mfma(args.summarize_mfma))
+        sys.stdout.write(summarize_mfma(args.summarize_mfma, args.workload))
         return
     if args.copy_only:
         copy_only()
