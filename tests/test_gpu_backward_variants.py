@@ -8,8 +8,8 @@ the fp64 oracle on the oracle's own quantized operands (tolerance
   blocks (same codes, same scales), general and power-of-two (_P2) scales;
 - the 128x128 block transpose itself, bit-exact;
 - sampled full-size checks at the a8w4 shapes (128 experts, 65536 rows,
-  K=7168, N=2048) and the blockwise shapes (64 experts, 32768 rows, K=7168,
-  N=4096).
+  K=7168, N=2048; forward and input gradient) and the blockwise shapes (64
+  experts, 32768 rows, K=7168, N=4096).
 """
 import numpy as np
 import pytest
@@ -156,6 +156,36 @@ def test_dgrad_blockwise(case, fmt):
 # ---------------------------------------------------------------------------
 # full size, sampled
 # ---------------------------------------------------------------------------
+def test_a8w4_full_size_fwd_sampled():
+    """a8w4 forward at its workload's shapes and launch (128 experts, 65536
+    rows, Zipf splits with empty experts, K=7168, N=2048; activations MXFP8,
+    weights MXFP4): sampled rows of five random experts and the largest one,
+    16 sampled output columns each, against the oracle's quantize-dequantize
+    and fp64 contraction."""
+    from synth import WORKLOADS
+    wl = WORKLOADS["a8w4"]
+    G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
+    sp = splits_for("a8w4")
+    gen = torch.Generator(device="cuda").manual_seed(93)
+    a = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((G * N, K), generator=gen, device="cuda") * wl["w_std"]).to(torch.bfloat16)
+    aq, as_ = mxg.quantize_rowwise(a, "mxfp8")
+    wq, ws = mxg.quantize_rowwise(w, "mxfp4")
+    out = mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt="mxfp8", w_fmt="mxfp4")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(94)
+    offs = np.concatenate([[0], np.cumsum(sp)])
+    nz = np.nonzero(sp)[0]
+    for g in list(rng.choice(nz, size=5, replace=False)) + [int(np.argmax(sp))]:
+        rows = offs[g] + np.sort(rng.choice(sp[g], size=min(8, sp[g]), replace=False))
+        cols = np.sort(rng.choice(N, size=16, replace=False))
+        ra, ras = omx.quantize_rowwise(_bits(a[torch.as_tensor(rows, device="cuda")]), "mxfp8")
+        rw, rws = omx.quantize_rowwise(_bits(w[torch.as_tensor(g * N + cols, device="cuda")]), "mxfp4")
+        ref = omx.dequantize_rowwise(ra, ras, "mxfp8") @ omx.dequantize_rowwise(rw, rws, "mxfp4").T
+        gpu = host_bf16_f64(out[torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(cols, device="cuda")])
+        assert_gemm_close(gpu, ref, what=f"a8w4 fwd expert {g}")
+
+
 def test_a8w4_full_size_dgrad_sampled():
     """a8w4 input gradient at the a8w4 shapes (128 experts, 65536 rows, Zipf
     splits with empty experts; N=2048 contracted, K=7168 out)."""
@@ -184,6 +214,44 @@ def test_a8w4_full_size_dgrad_sampled():
         ref = omx.dequantize_rowwise(rd, rds, "mxfp8") @ omx.dequantize_rowwise(rw, rws, "mxfp4").T
         gpu = host_bf16_f64(dx[rt][:, torch.as_tensor(kcols, device="cuda")])
         assert_gemm_close(gpu, ref, what=f"a8w4 dgrad expert {g}")
+
+
+def test_a8w4_full_size_mxfp8_wgrad_sampled():
+    """MXFP8 weight gradient at the a8w4 shapes (128 experts, 65536 rows, Zipf
+    splits with empty experts; [128, 2048, 7168] fp32 main_grad accumulated in
+    place): 16 x 16 sampled entries of every eighth nonempty expert and the
+    largest, against the oracle's column-wise segment-padded quantization of
+    the expert's rows and an fp64 contraction plus the old values."""
+    from synth import WORKLOADS
+    wl = WORKLOADS["a8w4"]
+    G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
+    sp = splits_for("a8w4")
+    gen = torch.Generator(device="cuda").manual_seed(95)
+    x = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
+    dy = torch.randn((M, N), generator=gen, device="cuda").to(torch.bfloat16)
+    dq, ds, mpad = mxg.quantize_colwise_segpad(dy, sp, "mxfp8")
+    xq, xs, _ = mxg.quantize_colwise_segpad(x, sp, "mxfp8")
+    main0 = torch.randn((G, N, K), generator=gen, device="cuda", dtype=torch.float32)
+    rng = np.random.default_rng(96)
+    nz = [g for g in range(G) if sp[g] > 0]
+    picks = {g: (np.sort(rng.choice(N, 16, replace=False)), np.sort(rng.choice(K, 16, replace=False)))
+             for g in nz[::8] + [int(np.argmax(sp))]}
+    m0 = {g: host(main0[g][np.ix_(ns, ks)]).astype(np.float64) for g, (ns, ks) in picks.items()}
+    mxg.grouped_wgrad(dq, ds, xq, xs, sp, N, K, mpad, main0, fmt="mxfp8", accumulate=True)
+    torch.cuda.synchronize()
+    offs = np.concatenate([[0], np.cumsum(sp)])
+    gpu_all, ref_all = [], []
+    for g, (ns, ks) in picks.items():
+        seg = torch.arange(int(offs[g]), int(offs[g + 1]), device="cuda")
+        dyg = _bits(dy[seg][:, torch.as_tensor(ns, device="cuda")].contiguous())
+        xg = _bits(x[seg][:, torch.as_tensor(ks, device="cuda")].contiguous())
+        rd, rds = omx.quantize_colwise_segpad(dyg, [sp[g]], "mxfp8")
+        rx, rxs = omx.quantize_colwise_segpad(xg, [sp[g]], "mxfp8")
+        ref = og.grouped_wgrad(omx.dequantize_rowwise(rd, rds, "mxfp8"), omx.dequantize_rowwise(rx, rxs, "mxfp8"),
+                               [sp[g]], main_grad0=m0[g][None], accumulate=True)[0]
+        gpu_all.append(host(main0[g][np.ix_(ns, ks)]).astype(np.float64))
+        ref_all.append(ref)
+    assert_gemm_close(np.stack(gpu_all), np.stack(ref_all), what="a8w4 MXFP8 wgrad accumulate")
 
 
 @pytest.mark.parametrize("p2", [False, True], ids=["general", "pow2"])
