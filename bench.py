@@ -233,6 +233,14 @@ def summarize_mfma(pmc_csv, workload="fc1"):
                 if row["Kernel_Name"].startswith(prefix) and row["Counter_Name"] == counter:
                     vals.setdefault(int(row["Dispatch_Id"]), []).append(float(row["Counter_Value"]))
         return [reduce_fn(vals[d]) for d in sorted(vals)]
+
+    def durations_ns(prefix):
+        dur = {}
+        with open(pmc_csv, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row["Kernel_Name"].startswith(prefix):
+                    dur[int(row["Dispatch_Id"])] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+        return [dur[d] for d in sorted(dur)]
     wl_flag = "" if workload == "fc1" else f" --workload {workload}"
     prof_dir = "prof_mfma" if workload == "fc1" else f"prof_mfma_{workload}"
     lines = [
@@ -271,10 +279,16 @@ def summarize_mfma(pmc_csv, workload="fc1"):
         elif kernel == "dgrad":
             busy, active = busy[1::2], active[1::2]
         util = [100.0 * b / (a / xcc * simds) for b, a in zip(busy, active)]
+        dur = durations_ns(prefix)
+        dur = dur[0::2] if kernel == "fwd" else dur[1::2] if kernel == "dgrad" else dur
+        # shader clock while the kernel ran: active cycles per XCD over the
+        # dispatch's duration (under counter collection)
+        sclk = [a / xcc / d for a, d in zip(active, dur) if d > 0]
         lines += [f"{kernel}_source_sha256_16: {source_hash(kernel)}",
                   f"{kernel}_dispatches: {len(util)}",
                   f"{kernel}_mfma_busy_cycles_median: {float(np.median(busy)):.0f}",
                   f"{kernel}_gpu_active_cycles_per_xcd_median: {float(np.median(active)) / xcc:.0f}",
+                  f"{kernel}_sclk_ghz_median: {float(np.median(sclk)):.3f}",
                   f"{kernel}_mfma_busy_pct_median: {float(np.median(util)):.2f}"]
     return "\n".join(lines) + "\n"
 
@@ -620,7 +634,8 @@ def main():
     for name, kind, _ in ops:
         ms = [e0.elapsed_time(e1) for e0, e1 in ev[name]]
         d = float(np.mean(ms)) * 1e-3
-        entry = {"ms": round(d * 1e3, 4), "ms_min": round(float(np.min(ms)), 4)}
+        entry = {"ms": round(d * 1e3, 4), "ms_median": round(float(np.median(ms)), 4),
+                 "ms_min": round(float(np.min(ms)), 4)}
         entry["GBs_alg"] = round(bytes_alg[name] / d / 1e9, 1)
         entry["frac_hbm"] = round(bytes_alg[name] / d / 1e9 / PEAK_HBM_GBS, 4)
         if kind == "gemm":
