@@ -163,17 +163,17 @@ def summarize(kernel, stats_csv, fetch_csv, write_csv, copy_fetch_csv, copy_writ
     lines = [
         f"kernel: {kernel}",
         "workload: MoE FC1 a4w4, 32 experts, 32768 routed rows, K=4096, N=3072 (bench.py default step)",
-        "# commands (GPU run, R = repository root, each rocprofv3 pass in a process of its own):",
+        "# commands (GPU run, R = repository root, OUT = an output directory, each rocprofv3 pass in its own process):",
         "#   cd /tmp && export TMPDIR=/tmp",
-        "#   rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_stats -o run"
+        "#   rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_stats -o run"
         " -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
-        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_fetch -o run"
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/prof_fetch -o run"
         " -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_write -o run"
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/prof_write -o run"
         " -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_cfetch -o run"
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/prof_cfetch -o run"
         " -- python3 $R/bench.py --copy-only",
-        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_cwrite -o run"
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/prof_cwrite -o run"
         " -- python3 $R/bench.py --copy-only",
         f"#   python3 $R/bench.py --summarize {kernel} <prof_stats kernel_stats.csv> <prof_fetch counter_collection.csv>"
         " <prof_write ...> <prof_cfetch ...> <prof_cwrite ...>",
@@ -245,9 +245,9 @@ def summarize_mfma(pmc_csv, workload="fc1"):
     prof_dir = "prof_mfma" if workload == "fc1" else f"prof_mfma_{workload}"
     lines = [
         f"workload: {WORKLOAD_TITLES[workload]} (bench.py{wl_flag or ' default step'})",
-        "# commands (GPU run, R = repository root):",
+        "# commands (GPU run, R = repository root, OUT = an output directory):",
         "#   cd /tmp && export TMPDIR=/tmp",
-        "#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/"
+        "#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $OUT/"
         f"{prof_dir} -o run -- python3 $R/bench.py{wl_flag} --steps 3 --warmup 1 --no-cpu-baseline",
         f"#   python3 $R/bench.py --summarize-mfma <{prof_dir} counter_collection.csv>{wl_flag}",
         f"# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcc} XCDs x {simds} SIMDs), median over dispatches",
@@ -582,8 +582,8 @@ def main():
         copy_only()
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the path shards by expert "
-                                   "(see DESIGN.md) but no multi-GPU run is part of it",
+        print(json.dumps({"error": "one GPU only: the path would shard by expert (each GPU running these "
+                                   "kernels on its own experts), which is not implemented here",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
