@@ -1,0 +1,95 @@
+"""The GEMM stage loops wait only as designed (CPU: cross-compiled gfx950
+assembly, no GPU). The ring's correctness and speed rest on constant
+`s_waitcnt vmcnt(N)` waits; the compiler adds a full drain, `vmcnt(0)`,
+wherever it cannot prove an in-flight DMA or load is done (for instance
+before reusing a VGPR that an in-flight LDS DMA used as its address), and
+such a drain inside a stage loop stalls every step. For the forward / input
+gradient (a4w4 and power-of-two blockwise) and the a4w4 weight gradient, the
+innermost loop holding the MFMAs must carry exactly one vector-memory wait:
+(STAGES-3)*DPS for the read-ahead loop, (STAGES-2)*DPS for the other. The
+3-stage weight gradients (MXFP8, power-of-two blockwise) also carry the drain
+of their once-per-tile kernel-argument read of the expert order (measured
+faster than an LDS copy, whose build put a second drain at every step head);
+any further wait is a regression."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "moe_grouped_block_mx_amd", "csrc", "gemm_mx.hip")
+
+# kernel name fragment (TileCfg parameters) -> the waits its stage loop must carry
+EXPECTED = {
+    # a4w4 forward / input gradient: 8 waves, 128-deep stages, 4-stage read-ahead ring, DPS 5
+    "grouped_rows_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1E": [5],
+    # a4w4 weight gradient: 4 waves, same ring, DPS 10
+    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi2ELi128ELi4ELi0ELi1ELi7ELi1E": [10],
+    # power-of-two blockwise forward / input gradient: 64-deep stages, 3-stage ring, DPS 6
+    "grouped_rows_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128E": [6],
+    # MXFP8 weight gradient (DPS 5) and power-of-two blockwise weight gradient
+    # (DPS 6): the ring wait, then the tile switch's drain
+    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi4ELi1ELi5ELi1E": [5, 0],
+    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi1E": [6, 0],
+}
+
+
+def _hipcc():
+    h = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    return h if os.path.exists(h) else None
+
+
+def stage_loop_waits(asm_lines):
+    """{kernel label: [vmcnt values of the waits in the innermost loop holding
+    its MFMAs]}, from the block structure the compiler prints in comments."""
+    out, kern, blocks, cur = {}, None, {}, None
+
+    def finish():
+        if kern is None:
+            return
+        loops = {hdr for hdr, lines in blocks.values() if hdr and any("v_mfma" in l for l in lines)}
+        assert len(loops) == 1, (kern, loops)
+        h = loops.pop()
+        out[kern] = [int(m.group(1)) for hdr, lines in blocks.values() if hdr == h
+                     for l in lines for m in [re.search(r"s_waitcnt vmcnt\((\d+)\)", l)] if m]
+
+    for line in asm_lines:
+        m = re.match(r"^(_ZN4mxgg\S+):", line)
+        if m:
+            finish()
+            kern, blocks, cur = m.group(1), {}, "entry"
+            blocks[cur] = (None, [])
+            continue
+        if kern is None:
+            continue
+        if line.startswith(".LBB") or line.startswith("; %bb."):
+            name = line.split(":")[0].strip().lstrip(".").replace("; %", "")
+            if "This Loop Header" in line or "This Inner Loop Header" in line:
+                hdr = name.replace("LBB", "BB")
+            else:
+                mh = re.search(r"Header=(BB\d+_\d+)", line)
+                hdr = mh.group(1) if mh else None
+            cur = name
+            blocks[cur] = (hdr, [])
+            continue
+        blocks[cur][1].append(line)
+        if "s_endpgm" in line:
+            finish()
+            kern = None
+    return out
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_stage_loops_carry_only_the_ring_wait(tmp_path):
+    asm = tmp_path / "gemm.s"
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", f"-I{os.path.join(ROOT, 'include')}", "--cuda-device-only", "-S", SRC, "-o", str(asm)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    waits = stage_loop_waits(asm.read_text().splitlines())
+    for frag, want in EXPECTED.items():
+        found = [k for k in waits if frag in k]
+        assert len(found) == 1, (frag, list(waits))
+        assert waits[found[0]] == want, (frag, waits[found[0]])
