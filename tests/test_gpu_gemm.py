@@ -154,6 +154,32 @@ def test_wgrad(case, accumulate):
         assert_gemm_close(gpu, ref, what=f"wgrad acc={accumulate} {case}")
 
 
+def _max_g_splits(seed):
+    """512 experts (the ABI's maximum), about 30 % of them empty, the others
+    0..5 rows: every expert table in LDS is full and most tiles are partial."""
+    rng = np.random.default_rng(seed)
+    sp = rng.integers(0, 6, size=512)
+    sp[rng.random(512) < 0.3] = 0
+    return sp
+
+
+def test_dgrad_many_experts_max_G():
+    gpu, ref = _dgrad_case(_max_g_splits(10), 64, 96)
+    assert_gemm_close(gpu, ref, what="dgrad G=512")
+
+
+@pytest.mark.parametrize("accumulate", [True, False])
+def test_wgrad_many_experts_max_G(accumulate):
+    sp = _max_g_splits(11)
+    gpu, ref, main0 = _wgrad_case(sp, 64, 96, accumulate=accumulate)
+    empty = np.nonzero(sp == 0)[0]
+    if accumulate:
+        assert np.array_equal(gpu[empty], main0[empty].astype(np.float64)), "an empty expert was modified"
+    else:
+        assert np.all(gpu[empty] == 0), "an empty expert was not zero-filled"
+    assert_gemm_close(gpu, ref, what=f"wgrad G=512 acc={accumulate}")
+
+
 def test_error_paths_on_gpu():
     x = bf16_normal((32, 64), 1.0, seed=0)
     xd = dev_bf16(x)
