@@ -210,3 +210,84 @@ def test_fp32_mode_amax_to_448_and_half_step_bound():
             # x*q and 1/q (three relative 2^-24 terms of the scaled value)
             bound = (half_step + 3 * abs(y) / 2 ** 23) * sf * (1 + Fraction(1, 2 ** 20))
             assert err <= bound, (trial, k)
+
+
+# ---------------------------------------------------------------------------
+# dequantization pins ("Add ROCm Triton blockwise FP8 grouped GEMM": 1x128
+# activation scales along K, 128x128 weight blocks; dequantized = code * s)
+# ---------------------------------------------------------------------------
+def _e4m3_by_fields(code: int) -> Fraction:
+    """E4M3 "FN" value from its bit fields (sign, 4-bit exponent with bias 7,
+    3-bit mantissa; exponent field 0 is subnormal), written out here rather
+    than read from the oracle's table."""
+    sign = -1 if code & 0x80 else 1
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0:
+        return sign * Fraction(m, 8) * Fraction(1, 2 ** 6)
+    return sign * (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+
+
+def _finite_e4m3_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] ^= 0x01          # the two NaN codes become 448-adjacent finite ones
+    return c
+
+
+def test_dequantize_1x128_each_element_is_code_times_its_row_block_scale():
+    rng = np.random.default_rng(21)
+    R, C = 3, 384
+    codes = _finite_e4m3_codes(rng, (R, C))
+    # every (row, block) scale distinct, powers of two and general fp32
+    scales = np.array([[2.0 ** -7, 3.0, 0.15625], [1.7e-3, 2.0 ** 5, 0.9],
+                       [6.5e4, 2.0 ** -20, 1.1]], dtype=np.float32)
+    d = bw.dequantize_1x128(codes, scales)
+    assert d.shape == (R, C)
+    for r in range(R):
+        for c in range(C):
+            ref = _e4m3_by_fields(int(codes[r, c])) * Fraction(float(scales[r, c // 128]))
+            # a 4-bit significand times a 24-bit one: exact in fp64
+            assert Fraction(float(d[r, c])) == ref, (r, c)
+
+
+def test_dequantize_128x128_each_element_uses_its_block_scale():
+    rng = np.random.default_rng(22)
+    codes = _finite_e4m3_codes(rng, (256, 384))
+    scales = np.array([[2.0 ** -3, 5.0, 0.3], [7.0, 2.0 ** 9, 1e-3]], dtype=np.float32)
+    d = bw.dequantize_128x128(codes, scales)
+    for (r, c) in [(0, 0), (127, 127), (128, 0), (0, 128), (255, 383), (129, 260), (17, 300), (200, 131)]:
+        ref = _e4m3_by_fields(int(codes[r, c])) * Fraction(float(scales[r // 128, c // 128]))
+        assert Fraction(float(d[r, c])) == ref, (r, c)
+
+
+@pytest.mark.parametrize("t", [-20, -5, 0, 3, 17])
+def test_dequantize_1x128_round_trip_is_exact_on_the_scaled_e4m3_grid(t):
+    # x = E4M3 value * 2^-t with one element at 448 * 2^-t: the block's
+    # power-of-two exponent is t, every x * 2^t is an E4M3 value, so
+    # quantize-then-dequantize must give x back bit for bit
+    rng = np.random.default_rng(300 + t)
+    codes = _finite_e4m3_codes(rng, (2, 256))
+    codes[(codes & 0x7F) == 0x7E] -= 1                      # at most one amax element per block
+    codes[0, 5], codes[1, 200] = 0x7E, 0xFE               # +448 in block 0 of row 0, -448 in block 1 of row 1
+    codes[0, 130], codes[1, 64] = 0x7E, 0xFE
+    x = np.array([[float(_e4m3_by_fields(int(c)) * Fraction(2) ** -t) for c in row] for row in codes])
+    xb = fp32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f64(xb), x)        # 4-bit significands fit bf16
+    q, s = bw.quantize_1x128(xb)
+    assert np.all(s == np.float32(2.0 ** -t))
+    assert np.array_equal(bw.dequantize_1x128(q, s), x)
+
+
+def test_dequantize_1x128_reconstructs_within_half_an_e4m3_step():
+    rng = np.random.default_rng(23)
+    xb = fp32_to_bf16_bits((rng.standard_normal((4, 512)) * np.float32(2.0 ** 7)).astype(np.float32))
+    q, s = bw.quantize_1x128(xb)
+    d = bw.dequantize_1x128(q, s)
+    x = bf16_bits_to_f64(xb)
+    for r in range(4):
+        for c in range(512):
+            sc = Fraction(float(s[r, c // 128]))
+            mag = int(q[r, c]) & 0x7F
+            lo = _E4M3_MAGS[max(mag - 1, 0)]
+            hi = _E4M3_MAGS[min(mag + 1, len(_E4M3_MAGS) - 1)]
+            half_step = max(_E4M3_MAGS[mag] - lo, hi - _E4M3_MAGS[mag]) / 2
+            assert abs(Fraction(float(d[r, c])) - Fraction(float(x[r, c]))) <= half_step * sc, (r, c)
