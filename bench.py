@@ -85,8 +85,8 @@ def parse():
 # --- profile summaries --------------------------------------------------------
 CSRC = os.path.join(ROOT, "moe_grouped_block_mx_amd", "csrc")
 KERNEL_SOURCES = {  # bench kernel name -> (profiled kernel name prefix, source files)
-    "fwd": ("void mxgg::grouped_rows_kernel", ["gemm_mx.hip", "device_common.hpp", "launch.hpp"]),
-    "dgrad": ("void mxgg::grouped_rows_kernel", ["gemm_mx.hip", "device_common.hpp", "launch.hpp"]),
+    "fwd": ("void mxgg::grouped_fwd_kernel", ["gemm_mx.hip", "device_common.hpp", "launch.hpp"]),
+    "dgrad": ("void mxgg::grouped_dgrad_kernel", ["gemm_mx.hip", "device_common.hpp", "launch.hpp"]),
     "wgrad": ("void mxgg::grouped_wgrad_kernel", ["gemm_mx.hip", "device_common.hpp", "launch.hpp"]),
 }
 COPY_BYTES = 1 << 30
@@ -137,21 +137,13 @@ def _counter_per_dispatch(path, name_prefix, counter, pick=None):
 
 def summarize(kernel, stats_csv, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     prefix = KERNEL_SOURCES[kernel][0]
-    # the bench launches fwd and dgrad from the same template; dgrad is the
-    # second rows-kernel launch of each step
-    def nth(vals):
-        if kernel == "fwd":
-            return vals[0::2]
-        if kernel == "dgrad":
-            return vals[1::2]
-        return vals
     stats = None
     with open(stats_csv, newline="") as fh:
         for row in csv.DictReader(fh):
             if row["Name"].startswith(prefix):
                 stats = row if stats is None else stats
-    fetch = nth(_counter_per_dispatch(fetch_csv, prefix, "FETCH_SIZE"))
-    write = nth(_counter_per_dispatch(write_csv, prefix, "WRITE_SIZE"))
+    fetch = _counter_per_dispatch(fetch_csv, prefix, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_csv, prefix, "WRITE_SIZE")
     copy_pick = lambda r: "copy" in r["Kernel_Name"].lower()
     cf = _counter_per_dispatch(copy_fetch_csv, "", "FETCH_SIZE", copy_pick)
     cw = _counter_per_dispatch(copy_write_csv, "", "WRITE_SIZE", copy_pick)
@@ -260,7 +252,8 @@ def summarize_mfma(pmc_csv, workload="fc1"):
     with open(pmc_csv, newline="") as fh:
         for row in csv.DictReader(fh):
             n = row["Kernel_Name"]
-            if n.startswith(("void mxgg::grouped_rows_kernel", "void mxgg::grouped_wgrad_kernel")) and n not in names:
+            if n.startswith(("void mxgg::grouped_fwd_kernel", "void mxgg::grouped_dgrad_kernel",
+                             "void mxgg::grouped_wgrad_kernel")) and n not in names:
                 names.append(n)
     lines.append("# per kernel: dispatches, median mfma_busy %, kernel")
     for n in names:
@@ -274,13 +267,8 @@ def summarize_mfma(pmc_csv, workload="fc1"):
         prefix = KERNEL_SOURCES[kernel][0]
         busy = per_dispatch(prefix, "SQ_VALU_MFMA_BUSY_CYCLES", sum)
         active = per_dispatch(prefix, "GRBM_GUI_ACTIVE", max)
-        if kernel == "fwd":
-            busy, active = busy[0::2], active[0::2]
-        elif kernel == "dgrad":
-            busy, active = busy[1::2], active[1::2]
         util = [100.0 * b / (a / xcc * simds) for b, a in zip(busy, active)]
         dur = durations_ns(prefix)
-        dur = dur[0::2] if kernel == "fwd" else dur[1::2] if kernel == "dgrad" else dur
         # shader clock while the kernel ran: active cycles per XCD over the
         # dispatch's duration (under counter collection)
         sclk = [a / xcc / d for a, d in zip(active, dur) if d > 0]

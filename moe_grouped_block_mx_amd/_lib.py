@@ -127,6 +127,50 @@ def _ld(x):
     return x.stride(0) if x.numel() else x.shape[1]
 
 
+def _expect(t, name, shape, dtypes):
+    """The C ABI sees only pointers, so this is the one place where a buffer
+    of the wrong shape, dtype or layout is caught before the GPU reads or
+    writes past its end."""
+    torch = _torch()
+    shape = tuple(int(v) for v in shape)
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != shape or t.dtype not in dtypes or not t.is_contiguous():
+        want = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        got = f"{str(t.dtype).replace('torch.', '')} {tuple(t.shape)}" + ("" if t.is_contiguous() else " non-contiguous")
+        raise ValueError(f"{name} must be a contiguous {want} tensor of shape {shape}, got {got}")
+    return t
+
+
+def _is_mx(f):
+    return f in (MXFP4, MXFP8)
+
+
+def _q_shape(f, rows, cols):
+    """Quantized data of a [rows, cols] operand packed along cols."""
+    return (rows, cols // 2 if f == MXFP4 else cols)
+
+
+def _row_scale_shape(f, rows, cols):
+    """Scales of a [rows, cols] operand quantized along cols."""
+    if _is_mx(f):
+        return (cols // 32, mxgg_mx_scale_stride(rows))           # block-major
+    if f in (FP8_1x128, FP8_1x128_P2):
+        return (rows, cols // 128)
+    return (rows // 128, cols // 128)
+
+
+def _col_scale_shape(f, cols, mpad):
+    """Scales of the column-wise segment-padded [cols, mpad] operand."""
+    return (mpad // 32, cols) if _is_mx(f) else (cols, mpad // 128)
+
+
+def _sdtype(f):
+    torch = _torch()
+    return torch.uint8 if _is_mx(f) else torch.float32
+
+
 def mxgg_workspace_size(G: int) -> int:
     return int(lib.mxgg_workspace_size(G))
 
@@ -169,6 +213,8 @@ def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=None, q=None, scales=None):
             scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
         else:
             scales = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=x.device)
+    _expect(q, "q", _q_shape(f, rows, cols), torch.uint8)
+    _expect(scales, "scales", _row_scale_shape(f, rows, cols), _sdtype(f))
     _check(lib.mxgg_quantize_rowwise(_ptr(x), rows, cols, _ld(x), f, flags, _ptr(q), _ptr(scales),
                                      _stream(x)))
     return q, scales
@@ -192,6 +238,8 @@ def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=None, q=None, s
             scales = torch.empty((cols, mpad // 128), dtype=torch.float32, device=x.device)
         else:
             scales = torch.empty((mpad // 32, cols), dtype=torch.uint8, device=x.device)  # block-major
+    _expect(q, "q", _q_shape(f, cols, mpad), torch.uint8)
+    _expect(scales, "scales", _col_scale_shape(f, cols, mpad), _sdtype(f))
     _check(lib.mxgg_quantize_colwise_segpad(_ptr(x), rows, cols, _ld(x), arr, G, f, flags, _ptr(q),
                                             _ptr(scales), mpad, _stream(x)))
     return q, scales, mpad
@@ -219,6 +267,11 @@ def mxgg_quantize_dual(x, m_splits, fmt="mxfp4", flags=None, q_row=None, s_row=N
         q_col = torch.empty((cols, mpad // 2 if fp4 else mpad), **u8)
     if s_col is None:
         s_col = torch.empty((mpad // 32, cols), **u8)
+    if _is_mx(f):
+        _expect(q_row, "q_row", _q_shape(f, rows, cols), torch.uint8)
+        _expect(s_row, "s_row", _row_scale_shape(f, rows, cols), torch.uint8)
+        _expect(q_col, "q_col", _q_shape(f, cols, mpad), torch.uint8)
+        _expect(s_col, "s_col", _col_scale_shape(f, cols, mpad), torch.uint8)
     _check(lib.mxgg_quantize_dual(_ptr(x), rows, cols, _ld(x), arr, G, f, flags, _ptr(q_row), _ptr(s_row),
                                   _ptr(q_col), _ptr(s_col), mpad, _stream(x)))
     return q_row, s_row, q_col, s_col, mpad
@@ -229,8 +282,14 @@ def mxgg_grouped_fwd(a_q, a_s, w_q, w_s, m_splits, N, K, a_fmt="mxfp4", w_fmt="m
     torch = _torch()
     arr, G = _splits(m_splits)
     M = a_q.shape[0]
+    af, wf = _fmt(a_fmt), _fmt(w_fmt)
+    _expect(a_q, "a_q", _q_shape(af, M, K), torch.uint8)
+    _expect(a_s, "a_s", _row_scale_shape(af, M, K), _sdtype(af))
+    _expect(w_q, "w_q", _q_shape(wf, G * N, K), torch.uint8)
+    _expect(w_s, "w_s", _row_scale_shape(wf, G * N, K), _sdtype(wf))
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    _expect(out, "out", (M, N), torch.bfloat16)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.mxgg_grouped_fwd(_ptr(a_q), _ptr(a_s), _fmt(a_fmt), _ptr(w_q), _ptr(w_s), _fmt(w_fmt), arr, G, M, N,
                                 K, _ptr(out), _ptr(ws), ws_bytes, _stream(a_q)))
@@ -245,6 +304,10 @@ def mxgg_transpose_128x128(w_q, w_s, G, N, K, wt_q=None, wt_s=None):
         wt_q = torch.empty((G * K, N), dtype=torch.uint8, device=w_q.device)
     if wt_s is None:
         wt_s = torch.empty((G * K // 128, N // 128), dtype=torch.float32, device=w_q.device)
+    _expect(w_q, "w_q", (G * N, K), torch.uint8)
+    _expect(w_s, "w_s", (G * N // 128, K // 128), torch.float32)
+    _expect(wt_q, "wt_q", (G * K, N), torch.uint8)
+    _expect(wt_s, "wt_s", (G * K // 128, N // 128), torch.float32)
     _check(lib.mxgg_transpose_128x128(_ptr(w_q), _ptr(w_s), G, N, K, _ptr(wt_q), _ptr(wt_s), _stream(w_q)))
     return wt_q, wt_s
 
@@ -256,8 +319,18 @@ def mxgg_grouped_dgrad(dy_q, dy_s, wcol_q, wcol_s, m_splits, N, K, fmt="mxfp4", 
     torch = _torch()
     arr, G = _splits(m_splits)
     M = dy_q.shape[0]
+    f = _fmt(fmt)
+    _expect(dy_q, "dy_q", _q_shape(f, M, N), torch.uint8)
+    _expect(dy_s, "dy_s", _row_scale_shape(f, M, N), _sdtype(f))
+    if _is_mx(f):                       # W along N, MXFP4: [K, G*N/2] + [G*N/32, K]
+        _expect(wcol_q, "wcol_q", _q_shape(MXFP4, K, G * N), torch.uint8)
+        _expect(wcol_s, "wcol_s", _col_scale_shape(MXFP4, K, G * N), torch.uint8)
+    else:                               # transposed 128x128 blocks
+        _expect(wcol_q, "wcol_q", (G * K, N), torch.uint8)
+        _expect(wcol_s, "wcol_s", (G * K // 128, N // 128), torch.float32)
     if dx is None:
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy_q.device)
+    _expect(dx, "dx", (M, K), torch.bfloat16)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.mxgg_grouped_dgrad(_ptr(dy_q), _ptr(dy_s), _ptr(wcol_q), _ptr(wcol_s), _fmt(fmt), arr, G, M, N, K,
                                   _ptr(dx), _ptr(ws), ws_bytes, _stream(dy_q)))
@@ -269,6 +342,12 @@ def mxgg_grouped_wgrad(dycol_q, dycol_s, xcol_q, xcol_s, m_splits, N, K, mpad, m
     """main_grad [G, N, K] (fp32 or bf16) += / = per-expert dY_g^T . X_g."""
     torch = _torch()
     arr, G = _splits(m_splits)
+    f = _fmt(fmt)
+    _expect(dycol_q, "dycol_q", _q_shape(f, N, mpad), torch.uint8)
+    _expect(dycol_s, "dycol_s", _col_scale_shape(f, N, mpad), _sdtype(f))
+    _expect(xcol_q, "xcol_q", _q_shape(f, K, mpad), torch.uint8)
+    _expect(xcol_s, "xcol_s", _col_scale_shape(f, K, mpad), _sdtype(f))
+    _expect(main_grad, "main_grad", (G, N, K), (torch.float32, torch.bfloat16))
     out_bf16 = 1 if main_grad.dtype == torch.bfloat16 else 0
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.mxgg_grouped_wgrad(_ptr(dycol_q), _ptr(dycol_s), _ptr(xcol_q), _ptr(xcol_s), _fmt(fmt), arr, G, N, K,

@@ -148,7 +148,7 @@ int64_t mxgg_segpad_rows(const int64_t* m_splits, int32_t G, mxgg_format fmt) {
   fmt = (mxgg_format)base_format(fmt);
   if (fmt != MXGG_MXFP4 && fmt != MXGG_MXFP8 && fmt != MXGG_FP8_1x128) return -1;
   for (int32_t g = 0; g < G; ++g)
-    if (m_splits[g] < 0) return -1;
+    if (m_splits[g] < 0 || m_splits[g] > kMaxSplit) return -1;
   return segpad_rows(m_splits, G, segpad_multiple(fmt));
 }
 
@@ -265,7 +265,7 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
     p.n_out = (int32_t)N;
     p.kc = (int32_t)K;
     p.sp = make_splits(m_splits, G);
-    c = hip_status(launch_grouped_rows_blk(p, p2, cus, stream), "blockwise forward launch");
+    c = hip_status(launch_grouped_rows_blk(p, p2, false, cus, stream), "blockwise forward launch");
     return c.ok() ? ok() : finish(c);
   }
   const bool a8 = a_fmt == MXGG_MXFP8;
@@ -284,7 +284,7 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
   p.n_out = (int32_t)N;
   p.kc = (int32_t)K;
   p.sp = make_splits(m_splits, G);
-  c = hip_status(launch_grouped_rows_mx(p, a8, cus, stream), "forward launch");
+  c = hip_status(launch_grouped_rows_mx(p, a8, false, cus, stream), "forward launch");
   return c.ok() ? ok() : finish(c);
 }
 
@@ -321,7 +321,7 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
     p.ldbs = N / 128 * 4;
     p.b_gstride = K * N;
     p.bs_gstride = K / 128 * (N / 128 * 4);
-    c = hip_status(launch_grouped_rows_blk(p, p2, cus, stream), "blockwise dgrad launch");
+    c = hip_status(launch_grouped_rows_blk(p, p2, true, cus, stream), "blockwise dgrad launch");
     return c.ok() ? ok() : finish(c);
   }
   const bool a8 = fmt == MXGG_MXFP8;  // a8w4: dY E4M3, W E2M1
@@ -331,7 +331,7 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
   p.ldbs = K;                     // its scales [G*N/32, K]
   p.b_gstride = N / 2;            // expert g owns columns [g*N, (g+1)*N)
   p.bs_gstride = N / 32 * K;      // ... and scale blocks [g*N/32, (g+1)*N/32)
-  c = hip_status(launch_grouped_rows_mx(p, a8, cus, stream), "dgrad launch");
+  c = hip_status(launch_grouped_rows_mx(p, a8, true, cus, stream), "dgrad launch");
   return c.ok() ? ok() : finish(c);
 }
 

@@ -948,7 +948,7 @@ struct RowsSource {
 };
 
 template <class C>
-__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_rows_kernel(const RowsGemmParams p) {
+__device__ __forceinline__ void grouped_rows_body(const RowsGemmParams& p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int64_t pref[kMaxExperts + 1];
   __shared__ int64_t tpref[kMaxExperts + 1];
@@ -964,6 +964,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_rows_kernel(const 
 
   RowsSource<C> src{p, pref, tile_offs, G, n_tiles, tile_offs[G]};
   persistent_loop<C>(src, smem, p.lda, p.ldas, p.ldb, p.ldbs);
+}
+
+// The forward and the input gradient run the same body; each pass has its own
+// kernel symbol so that traces and profiles report the two passes apart.
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_fwd_kernel(const RowsGemmParams p) {
+  grouped_rows_body<C>(p);
+}
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_dgrad_kernel(const RowsGemmParams p) {
+  grouped_rows_body<C>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1142,13 +1153,8 @@ using CfgP2W = TileCfg<256, 256, 2, 4, 64, 3, kBlkP2, 1, 5, 1>;
 
 template <class C, class K, class P>
 static hipError_t launch_persistent(K kernel, const P& p, int64_t tiles, int num_cus, hipStream_t st) {
-  static bool attr_set = false;  // raise the dynamic LDS limit once per kernel
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::SMEM_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = ensure_dynamic_lds((const void*)kernel, C::SMEM_BYTES, st);
+  if (e != hipSuccess) return e;
   int64_t grid = (int64_t)num_cus * C::OCC;
   if (tiles < grid) grid = tiles;
   if (grid < 1) grid = 1;
@@ -1166,15 +1172,18 @@ static int64_t rows_tiles(const RowsGemmParams& p) {
   return mt * ((p.n_out + C::BN - 1) / C::BN);
 }
 
-hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, int num_cus, hipStream_t st) {
-  if (a_fp8)
-    return launch_persistent<CfgA8>(grouped_rows_kernel<CfgA8>, p, rows_tiles<CfgA8>(p), num_cus, st);
-  return launch_persistent<CfgA4>(grouped_rows_kernel<CfgA4>, p, rows_tiles<CfgA4>(p), num_cus, st);
+template <class C>
+static hipError_t launch_rows(const RowsGemmParams& p, bool dgrad, int num_cus, hipStream_t st) {
+  if (dgrad) return launch_persistent<C>(grouped_dgrad_kernel<C>, p, rows_tiles<C>(p), num_cus, st);
+  return launch_persistent<C>(grouped_fwd_kernel<C>, p, rows_tiles<C>(p), num_cus, st);
 }
 
-hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, bool pow2, int num_cus, hipStream_t st) {
-  if (pow2) return launch_persistent<CfgP2F>(grouped_rows_kernel<CfgP2F>, p, rows_tiles<CfgP2F>(p), num_cus, st);
-  return launch_persistent<CfgBlkF>(grouped_rows_kernel<CfgBlkF>, p, rows_tiles<CfgBlkF>(p), num_cus, st);
+hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, int num_cus, hipStream_t st) {
+  return a_fp8 ? launch_rows<CfgA8>(p, dgrad, num_cus, st) : launch_rows<CfgA4>(p, dgrad, num_cus, st);
+}
+
+hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, bool pow2, bool dgrad, int num_cus, hipStream_t st) {
+  return pow2 ? launch_rows<CfgP2F>(p, dgrad, num_cus, st) : launch_rows<CfgBlkF>(p, dgrad, num_cus, st);
 }
 
 template <class C>

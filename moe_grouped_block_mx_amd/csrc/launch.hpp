@@ -4,9 +4,37 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "device_common.hpp"
 
 namespace mxgg {
+
+// Raise a kernel's dynamic LDS limit on the stream's device before its first
+// launch there. The limit is an attribute of one kernel on one device, so it
+// is set once per (kernel, device) pair, with that device current; host
+// threads may launch concurrently, hence the lock.
+inline hipError_t ensure_dynamic_lds(const void* kernel, int bytes, hipStream_t st) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  int dev = 0;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return hipSuccess;
+  int cur = 0;
+  if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+  if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (cur != dev) {
+    const hipError_t e2 = hipSetDevice(cur);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e == hipSuccess) done.insert({kernel, dev});
+  return e;
+}
 
 // Row-split grouped GEMM (forward and input gradient): out[r, :] for every row
 // r of expert g is A[r, :] . B_g^T, where B_g is the [n_out, kc] operand of
@@ -61,7 +89,8 @@ hipError_t launch_quant_dual_mx(const uint16_t* x, int64_t rows, int64_t cols, i
 hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
                                    bool fp8, uint8_t* q, uint8_t* s, int64_t mpad, hipStream_t st);
 
-hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, int num_cus, hipStream_t st);
+// dgrad selects the input-gradient kernel symbol (same code as the forward's)
+hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, int num_cus, hipStream_t st);
 // fp8: E4M3 operands on both sides (MXFP8), else E2M1 (MXFP4)
 hipError_t launch_grouped_wgrad_mx(const WgradParams& p, bool fp8, int num_cus, hipStream_t st);
 
@@ -76,7 +105,7 @@ hipError_t launch_quant_colwise_blk(const uint16_t* x, int64_t cols, int64_t ldx
 hipError_t launch_transpose_128x128(const uint8_t* wq, const float* ws, int32_t G, int64_t N, int64_t K, uint8_t* tq,
                                     float* ts, hipStream_t st);
 // pow2: every scale is a power of two (the MFMA applies it; no per-128 partial)
-hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, bool pow2, int num_cus, hipStream_t st);
+hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, bool pow2, bool dgrad, int num_cus, hipStream_t st);
 hipError_t launch_grouped_wgrad_blk(const WgradParams& p, bool pow2, int num_cus, hipStream_t st);
 
 }  // namespace mxgg

@@ -459,13 +459,9 @@ template <class D, bool XCD, int ORDER>
 hipError_t launch_quant_dual_persistent(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                         const SplitArgs& sp, bool fp8, uint8_t* qr, uint8_t* sr, uint8_t* qc,
                                         uint8_t* sc, int64_t mpad, int num_cus, hipStream_t st) {
-  static bool attr_set[2] = {false, false};  // raise the dynamic LDS limit once per kernel
   auto kern = fp8 ? quant_dual_mx_persistent<E4M3Fmt, D, XCD, ORDER> : quant_dual_mx_persistent<E2M1Fmt, D, XCD, ORDER>;
-  if (!attr_set[fp8]) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, D::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set[fp8] = true;
-  }
+  const hipError_t e = ensure_dynamic_lds((const void*)kern, D::LDS_BYTES, st);
+  if (e != hipSuccess) return e;
   const int64_t tiles = ((mpad + D::TR - 1) / D::TR) * ((cols + D::TC - 1) / D::TC);
   int64_t grid = (int64_t)num_cus * D::OCC;
   if (tiles < grid) grid = tiles;

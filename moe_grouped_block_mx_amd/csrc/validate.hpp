@@ -49,11 +49,15 @@ inline int segpad_multiple(mxgg_format f) { return base_format(f) == MXGG_FP8_1x
 inline Check check_splits(const int64_t* m, int32_t G, int64_t rows, const char* what) {
   if (G < 1 || G > MXGG_MAX_EXPERTS) return fail(MXGG_ERR_SHAPE, "G=%lld outside [1, 512]", G);
   if (!m) return fail(MXGG_ERR_NULL, "m_splits is NULL");
+  // Each split is bounded before it is added (a split above the row count
+  // can never be part of a valid sum), so the int64 running sum cannot wrap:
+  // huge splits must not add up, modulo 2^64, to the right total.
+  for (int32_t g = 0; g < G; ++g)
+    if (m[g] < 0) return fail(MXGG_ERR_SPLITS, "m_splits[%lld] = %lld is negative", g, m[g]);
   int64_t sum = 0;
   for (int32_t g = 0; g < G; ++g) {
-    if (m[g] < 0) return fail(MXGG_ERR_SPLITS, "m_splits[%lld] = %lld is negative", g, m[g]);
-    sum += m[g];
-    if (sum > ((int64_t)1 << 40)) return fail(MXGG_ERR_SPLITS, "m_splits sum overflows");
+    if (m[g] > rows) return fail(MXGG_ERR_SPLITS, "m_splits[%lld] = %lld exceeds the %lld rows", g, m[g], rows);
+    if (__builtin_add_overflow(sum, m[g], &sum)) return fail(MXGG_ERR_SPLITS, "m_splits sum overflows");
   }
   if (sum != rows) {
     Check r = fail(MXGG_ERR_SPLITS, "sum(m_splits) = %lld but %s has %lld rows", sum, 0, rows);
@@ -63,6 +67,11 @@ inline Check check_splits(const int64_t* m, int32_t G, int64_t rows, const char*
   return Check{};
 }
 
+// Largest split any entry point accepts: row counts stay below 2^31.
+constexpr int64_t kMaxSplit = ((int64_t)1 << 31) - 1;
+
+// Padded row count; callers have checked 0 <= m[g] <= kMaxSplit, so neither
+// the rounding nor the sum (at most 512 terms) can overflow.
 inline int64_t segpad_rows(const int64_t* m, int32_t G, int pad) {
   int64_t s = 0;
   for (int32_t g = 0; g < G; ++g) s += (m[g] + pad - 1) / pad * pad;
@@ -126,6 +135,7 @@ inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols
   if ((cols + 63) / 64 > 65535) return fail(MXGG_ERR_SHAPE, "cols=%lld too large (<= 4194240)", cols);
   if (ldx < cols) return fail(MXGG_ERR_SHAPE, "ldx=%lld < cols=%lld", ldx, cols);
   if (ldx % 8) return fail(MXGG_ERR_ALIGN, "ldx=%lld not a multiple of 8 elements", ldx);
+  if (rows >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SHAPE, "rows=%lld >= 2^31", rows);
   MXGG_TRY(check_splits(m, G, rows, "x"));
   const int64_t need = segpad_rows(m, G, segpad_multiple(f));
   if (mpad != need) return fail(MXGG_ERR_SHAPE, "mpad=%lld but the padded row count is %lld", mpad, need);
@@ -242,9 +252,10 @@ inline Check validate_wgrad(const void* dy_q, const void* dy_s, const void* x_q,
   if (N >= kMaxRowStride || K >= kMaxRowStride) return fail(MXGG_ERR_SHAPE, "N or K too large (< 2^23)");
   if (G < 1 || G > MXGG_MAX_EXPERTS) return fail(MXGG_ERR_SHAPE, "G=%lld outside [1, 512]", G);
   if (!m) return fail(MXGG_ERR_NULL, "m_splits is NULL");
-  int64_t rows = 0;
+  int64_t rows = 0;  // at most 512 splits below 2^31 each: no overflow
   for (int32_t g = 0; g < G; ++g) {
     if (m[g] < 0) return fail(MXGG_ERR_SPLITS, "m_splits[%lld] = %lld is negative", g, m[g]);
+    if (m[g] > kMaxSplit) return fail(MXGG_ERR_SPLITS, "m_splits[%lld] = %lld >= 2^31", g, m[g]);
     rows += m[g];
   }
   if (rows >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SPLITS, "sum(m_splits)=%lld >= 2^31", rows);

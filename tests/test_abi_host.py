@@ -195,3 +195,30 @@ def test_grouped_linear_fails_loudly_off_gpu():
         layer(x, [4, 4])
     with pytest.raises(ValueError):
         layer(torch.zeros((8, 32), dtype=torch.bfloat16), [4, 4])
+
+
+I64_MAX = 2 ** 63 - 1
+
+
+def test_huge_splits_cannot_wrap_to_the_row_count():
+    # 1 + 2*(2^63-1) + 3 wraps to 2 modulo 2^64: must be rejected, not passed on
+    assert fwd(splits(1, I64_MAX, I64_MAX, 3), 4, 2) == 3 and "exceeds" in last()
+    assert L.mxgg_grouped_dgrad(P, P, P, P, 0, splits(1, I64_MAX, I64_MAX, 3), 4, 2, 64, 64, P, NULL, 0,
+                                NULL) == 3
+    assert L.mxgg_quantize_colwise_segpad(P, 2, 64, 64, splits(1, I64_MAX, I64_MAX, 3), 4, 0, 0, P, P, 64,
+                                          NULL) == 3
+    assert L.mxgg_quantize_dual(P, 2, 64, 64, splits(1, I64_MAX, I64_MAX, 3), 4, 0, 0, P, P, P, P, 64,
+                                NULL) == 3
+    # a split above the row count is rejected even when the others are 0
+    assert fwd(splits(0, 5), 2, 4) == 3 and "exceeds" in last()
+
+
+def test_wgrad_rejects_splits_at_or_above_2_31():
+    # wgrad takes no row count: each split is bounded below 2^31 before the sum
+    st = L.mxgg_grouped_wgrad(P, P, P, P, 0, splits(I64_MAX, I64_MAX, 2), 3, 64, 64, 96, P, 0, 1, NULL, 0, NULL)
+    assert st == 3 and "2^31" in last()
+    st = L.mxgg_grouped_wgrad(P, P, P, P, 0, splits(2 ** 31, 0), 2, 64, 64, 2 ** 31, P, 0, 1, NULL, 0, NULL)
+    assert st == 3
+    assert L.mxgg_segpad_rows(splits(I64_MAX, 1), 2, 0) == -1
+    assert L.mxgg_segpad_rows(splits(2 ** 31, 1), 2, 0) == -1
+    assert L.mxgg_segpad_rows(splits(2 ** 31 - 1, 1), 2, 0) == 2 ** 31 + 32

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
-ROWS = "void mxgg::grouped_rows_kernel<mxgg::TileCfg<256, 256, 2, 4, 128, 4, 0, 1, 7, 1> >(mxgg::RowsGemmParams)"
+FWD = "void mxgg::grouped_fwd_kernel<mxgg::TileCfg<256, 256, 2, 4, 128, 4, 0, 1, 7, 1> >(mxgg::RowsGemmParams)"
+DGRAD = "void mxgg::grouped_dgrad_kernel<mxgg::TileCfg<256, 256, 2, 4, 128, 4, 0, 1, 7, 1> >(mxgg::RowsGemmParams)"
 WGRAD = "void mxgg::grouped_wgrad_kernel<mxgg::TileCfg<256, 256, 2, 2, 128, 4, 0, 1, 7, 1> >(mxgg::WgradParams)"
 COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::bfloat16_copy_kernel_cuda>"
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
@@ -28,13 +29,13 @@ def _write(path, rows):
 
 
 def test_mfma_busy_and_clock(tmp_path):
-    # fwd (dispatch 1) and dgrad (dispatch 2) share the rows kernel; busy is one
-    # row per dispatch, GRBM_GUI_ACTIVE the sum over 8 XCDs
+    # fwd (dispatch 1) and dgrad (dispatch 2) are separate kernel symbols; busy
+    # is one row per dispatch, GRBM_GUI_ACTIVE the sum over 8 XCDs
     rows = [
-        (1, ROWS, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 400, 0, 500),
-        (1, ROWS, "GRBM_GUI_ACTIVE", 8 * 1000, 0, 500),
-        (2, ROWS, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 250, 1000, 2000),
-        (2, ROWS, "GRBM_GUI_ACTIVE", 8 * 2000, 1000, 2000),
+        (1, FWD, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 400, 0, 500),
+        (1, FWD, "GRBM_GUI_ACTIVE", 8 * 1000, 0, 500),
+        (2, DGRAD, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 250, 1000, 2000),
+        (2, DGRAD, "GRBM_GUI_ACTIVE", 8 * 2000, 1000, 2000),
         (3, WGRAD, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 100, 3000, 3400),
         (3, WGRAD, "GRBM_GUI_ACTIVE", 8 * 800, 3000, 3400),
     ]
@@ -96,3 +97,36 @@ def test_stale_summaries_read_as_absent(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "traffic_summary_path", lambda k: str(traffic))
     assert bench.read_traffic("wgrad") is None
 
+
+
+def test_fwd_and_dgrad_summaries_read_their_own_kernel(tmp_path):
+    # the two passes have their own kernel symbols: each summary takes its
+    # own stats row and its own dispatches' counters
+    kib = 1024
+    stats = tmp_path / "stats.csv"
+    with open(stats, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs"])
+        w.writeheader()
+        w.writerow({"Name": DGRAD, "Calls": 5, "AverageNs": 300000, "MinNs": 290000, "MaxNs": 310000})
+        w.writerow({"Name": FWD, "Calls": 5, "AverageNs": 270000, "MinNs": 260000, "MaxNs": 280000})
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    cfetch, cwrite = tmp_path / "cf.csv", tmp_path / "cw.csv"
+    _write(fetch, [(1, FWD, "FETCH_SIZE", 100, 0, 1), (2, DGRAD, "FETCH_SIZE", 900, 0, 1),
+                   (3, FWD, "FETCH_SIZE", 100, 0, 1), (4, DGRAD, "FETCH_SIZE", 900, 0, 1)])
+    _write(write, [(1, FWD, "WRITE_SIZE", 10, 0, 1), (2, DGRAD, "WRITE_SIZE", 90, 0, 1)])
+    _write(cfetch, [(1, COPY, "FETCH_SIZE", bench.COPY_BYTES / kib, 0, 1)])
+    _write(cwrite, [(1, COPY, "WRITE_SIZE", bench.COPY_BYTES / kib, 0, 1)])
+
+    def kv_of(kernel):
+        out = {}
+        for line in bench.summarize(kernel, str(stats), str(fetch), str(write), str(cfetch),
+                                    str(cwrite)).splitlines():
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                out[k.strip()] = v.strip()
+        return out
+    f, d = kv_of("fwd"), kv_of("dgrad")
+    assert f["stats_average_ns"] == "270000" and d["stats_average_ns"] == "300000"
+    assert float(f["hbm_fetch_bytes_per_launch"]) == pytest.approx(100 * kib)
+    assert float(d["hbm_fetch_bytes_per_launch"]) == pytest.approx(900 * kib)
+    assert float(d["hbm_write_bytes_per_launch"]) == pytest.approx(90 * kib)

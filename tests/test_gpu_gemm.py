@@ -62,10 +62,11 @@ def test_fwd_many_experts_max_G():
 
 def test_fwd_empty_batch_writes_nothing():
     out = torch.full((0, 64), 1.0, dtype=torch.bfloat16, device="cuda")
+    # block-major MX scales: [K/32 blocks, rows rounded up to a multiple of 4]
     aq = torch.empty((0, 32), dtype=torch.uint8, device="cuda")
-    as_ = torch.empty((0, 2), dtype=torch.uint8, device="cuda")
+    as_ = torch.empty((2, 0), dtype=torch.uint8, device="cuda")
     wq = torch.empty((128, 32), dtype=torch.uint8, device="cuda")
-    ws = torch.empty((128, 2), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((2, 128), dtype=torch.uint8, device="cuda")
     mxg.grouped_fwd(aq, as_, wq, ws, [0, 0], 64, 64, out=out)
     torch.cuda.synchronize()
 
@@ -189,11 +190,13 @@ def test_error_paths_on_gpu():
     st = mxg.lib.mxgg_quantize_rowwise(ctypes.c_void_p(xd.data_ptr()), 32, 64, 64, 0, 0,
                                        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(s.data_ptr()), None)
     assert st == 7, mxg.lib.mxgg_last_error()
-    with pytest.raises(mxg.MxggError):
+    # well-formed buffers (block-major scales), splits summing to 3 of 4 rows:
+    # the library's own split check refuses the call
+    with pytest.raises(mxg.MxggError, match="MXGG_ERR_SPLITS"):
         mxg.grouped_fwd(torch.empty((4, 32), dtype=torch.uint8, device="cuda"),
-                        torch.empty((4, 2), dtype=torch.uint8, device="cuda"),
+                        torch.empty((2, 4), dtype=torch.uint8, device="cuda"),
                         torch.empty((64, 32), dtype=torch.uint8, device="cuda"),
-                        torch.empty((64, 2), dtype=torch.uint8, device="cuda"), [2, 1], 32, 64)
+                        torch.empty((2, 64), dtype=torch.uint8, device="cuda"), [2, 1], 32, 64)
 
 
 # ---------------------------------------------------------------------------
