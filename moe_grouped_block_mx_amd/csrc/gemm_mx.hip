@@ -327,6 +327,84 @@ __device__ __forceinline__ void issue_b_srcs(const uint8_t* const (&src)[C::DB],
   });
 }
 
+// ---------------------------------------------------------------------------
+// DMA issue when every stage of a launch is full (the contraction a multiple
+// of BK, so no stage needs zero-page chunks): an address is a wave-uniform
+// base, advanced per stage with scalar adds, plus a per-lane 32-bit offset
+// fixed for the tile, so a DMA costs no vector ALU work. The general path
+// selects the zero page per lane and per stage with 64-bit vector address
+// arithmetic; measured with per-wave cycle counters at the fc1 shapes, that
+// work made the stage half issuing the A and scale DMAs take twice as long
+// as the other half (which issues the same number of MFMAs).
+// ---------------------------------------------------------------------------
+template <class C>
+struct FastPlan {
+  uint32_t vA[C::DA], vB[C::DB], vS[C::DSA];  // per lane
+  // wave-uniform: the tile's operand bases; per scale DMA instruction, the
+  // scale operand it reads (A's or B's) and that operand's bytes per stage
+  const uint8_t *a, *b, *s[C::DSA];
+  int64_t sstep[C::DSA];
+};
+
+// A wave-uniform pointer moved to scalar registers (the tile bases are
+// uniform but computed through LDS reads; without this the compiler keeps
+// them in vector registers and moves them back for every DMA).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// The offsets of plan_dma without the per-stage parts: chunks at row*ld +
+// swizzled chunk; scale words at block*ld + first row (padding lanes: 0,
+// which reads a valid word of the same operand into LDS padding). The
+// caller guarantees (SB-1)*ld + rows < 2^32 for both scale operands.
+template <class C>
+__device__ __forceinline__ void plan_fast(FastPlan<C>& fp, const DmaPlan<C>& pl, const TileOps& t, int64_t ldas,
+                                          int64_t ldbs, int w) {
+  static_assert(!C::F32S, "fast issue: MX scales");
+  w = __builtin_amdgcn_readfirstlane(w);
+  unroll<C::DA>([&](auto ic) { fp.vA[decltype(ic)::value] = pl.offA[decltype(ic)::value]; });
+  unroll<C::DB>([&](auto ic) { fp.vB[decltype(ic)::value] = pl.offB[decltype(ic)::value]; });
+  fp.a = uniform_ptr(t.a);
+  fp.b = uniform_ptr(t.b);
+  unroll<C::DSA>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const bool on_b = (i * C::NW + w) * 256 >= C::BM * C::SB;  // wave-uniform
+    const int64_t ld = on_b ? ldbs : ldas;
+    fp.vS[i] = pl.sBlk[i] < kNoBlock ? (uint32_t)pl.sBlk[i] * (uint32_t)ld + pl.sOff[i] : 0u;
+    fp.s[i] = uniform_ptr(on_b ? t.bs : t.as);
+    fp.sstep[i] = (int64_t)__builtin_amdgcn_readfirstlane((int)(C::SB * ld));
+  });
+}
+
+// Stage s of tile t into ring slot st (PART as for issue_stage). A dummy
+// stage re-reads stage 0 of the last planned tile (or the zero page before
+// any): its data is never consumed, the DMAs only keep the counts constant.
+template <class C, int PART = -1>
+__device__ __forceinline__ void issue_stage_fast(const FastPlan<C>& fp, int s, uint8_t* st, int w) {
+  constexpr bool DO_A = PART != 1, DO_B = PART != 0;
+  if constexpr (DO_A) {
+    const uint8_t* base = fp.a + s * C::RBA;
+    unroll<C::DA>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      dma16(base + fp.vA[i], st + C::A_OFF + (i * C::NW + w) * 1024);
+    });
+    unroll<C::DSA>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      dma4(fp.s[i] + s * fp.sstep[i] + fp.vS[i], st + C::AS_OFF + (i * C::NW + w) * 256);
+    });
+  }
+  if constexpr (DO_B) {
+    const uint8_t* base = fp.b + s * C::RBB;
+    unroll<C::DB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      dma16(base + fp.vB[i], st + C::B_OFF + (i * C::NW + w) * 1024);
+    });
+  }
+}
+
 // B fragments of K step KK (E2M1: 16 bytes per lane; E4M3: 2 x 16 bytes).
 template <class C, int KK>
 __device__ __forceinline__ void load_b_frags(const uint8_t* st, v8i (&bf)[C::FN], int wn, int h, int l32) {
@@ -608,9 +686,12 @@ __device__ __forceinline__ void wait_stage(int stages_after) {
 //   src.ops(t)        TileOps of tile t
 //   src.epilogue(...) stores tile t
 // Tiles are visited t = first, first + gridDim.x, ...
-template <class C, class Src>
+// FAST (read-ahead loop only): every tile's contraction is a multiple of BK
+// and the scale offsets fit 32 bits; the DMAs take the fast issue above.
+template <class C, bool FAST = false, class Src>
 __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t lda, int64_t ldas, int64_t ldb,
                                                 int64_t ldbs) {
+  static_assert(!FAST || C::SCHED == 7, "fast issue: read-ahead loop");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / C::WN, wn = w % C::WN;
@@ -631,6 +712,13 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
   // zero-page selection holds only while every chunk offset (kA, kB) and
   // scale block (sBlk) of the plan is >= 0.
   DmaPlan<C> plan{};
+  FastPlan<C> fplan{};
+  if constexpr (FAST) {
+    // dummy stages before any planned tile read the zero page at offset 0
+    const uint8_t* z = reinterpret_cast<const uint8_t*>(g_zero_page);
+    fplan.a = fplan.b = z;
+    unroll<C::DSA>([&](auto ic) { fplan.s[decltype(ic)::value] = z; });
+  }
   auto load_issue_tile = [&]() {
     while (it < total) {
       iops = src.ops(it);
@@ -638,7 +726,10 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
       if (ins > 0) break;
       it += stride;  // tiles with an empty contraction issue nothing
     }
-    if (it < total) plan_dma<C>(plan, iops, lda, ldas, ldb, ldbs, w, lane);
+    if (it < total) {
+      plan_dma<C>(plan, iops, lda, ldas, ldb, ldbs, w, lane);
+      if constexpr (FAST) plan_fast<C>(fplan, plan, iops, ldas, ldbs, w);
+    }
   };
   auto issue_one = [&]() -> int {
     if (it >= total) return 0;
@@ -666,7 +757,8 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
     };
     for (int q = 0; q < C::STAGES - 1; ++q) {
       const bool dummy = it >= total;
-      issue_stage<C>(plan, iops, is, smem + slot_issue * C::STAGE_BYTES, w, ldas, ldbs, dummy);
+      if constexpr (FAST) issue_stage_fast<C>(fplan, dummy ? 0 : is, smem + slot_issue * C::STAGE_BYTES, w);
+      else issue_stage<C>(plan, iops, is, smem + slot_issue * C::STAGE_BYTES, w, ldas, ldbs, dummy);
       advance_issue(dummy);
     }
     // stage 0 (of the first tile, or a dummy) has landed: its K step 0
@@ -679,6 +771,10 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
     asm volatile("" : "+s"(zero));
     const uint8_t* bsrc[C::DB];
     unroll<C::DB>([&](auto ic) { bsrc[decltype(ic)::value] = zero; });
+    // fast issue: the pending B chunks' base and lane offsets
+    const uint8_t* bbase = zero;
+    uint32_t bvoff[C::DB];
+    unroll<C::DB>([&](auto ic) { bvoff[decltype(ic)::value] = 0; });
     uint8_t* bdst = smem + slot_issue * C::STAGE_BYTES;
     wait_vmcnt<(C::STAGES - 2) * C::DPS>();
     raw_barrier();
@@ -701,7 +797,16 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
         // slot; in the first step, zero-page DMAs into the slot the prologue
         // left empty, which that stage's own DMAs follow in issue order)
         ra_half<C, 1, 1, C::DB>(smem + slot_comp * C::STAGE_BYTES, f0, f1, acc, wm, wn, h, l32,
-                                [&]() __attribute__((always_inline)) { issue_b_srcs<C>(bsrc, bdst, w); });
+                                [&]() __attribute__((always_inline)) {
+                                  if constexpr (FAST) {
+                                    unroll<C::DB>([&](auto ic) {
+                                      constexpr int i = decltype(ic)::value;
+                                      dma16(bbase + bvoff[i], bdst + C::B_OFF + (i * C::NW + w) * 1024);
+                                    });
+                                  } else {
+                                    issue_b_srcs<C>(bsrc, bdst, w);
+                                  }
+                                });
         __builtin_amdgcn_sched_barrier(0);
         // the next stage has landed (this wave's DMAs: STAGES-3 stages were
         // issued after it; the barrier covers the other waves')
@@ -710,10 +815,18 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
         __builtin_amdgcn_sched_barrier(0);
         ra_half<C, 0, 2, C::DPS - C::DB>(smem + slot_next * C::STAGE_BYTES, f1, f0, acc, wm, wn, h, l32,
                                          [&]() __attribute__((always_inline)) {
-                                           issue_stage<C, 0>(plan, iops, is, dst, w, ldas, ldbs, dummy, zero);
+                                           if constexpr (FAST)
+                                             issue_stage_fast<C, 0>(fplan, dummy ? 0 : is, dst, w);
+                                           else
+                                             issue_stage<C, 0>(plan, iops, is, dst, w, ldas, ldbs, dummy, zero);
                                          });
         __builtin_amdgcn_sched_barrier(0);
-        stage_b_srcs<C>(plan, iops, is, dummy, zero, bsrc);
+        if constexpr (FAST) {
+          bbase = fplan.b + (dummy ? 0 : is) * C::RBB;
+          unroll<C::DB>([&](auto ic) { bvoff[decltype(ic)::value] = fplan.vB[decltype(ic)::value]; });
+        } else {
+          stage_b_srcs<C>(plan, iops, is, dummy, zero, bsrc);
+        }
         bdst = dst;
         pending = true;
         pending_dummy = dummy;
@@ -947,7 +1060,7 @@ struct RowsSource {
   }
 };
 
-template <class C>
+template <class C, bool FAST>
 __device__ __forceinline__ void grouped_rows_body(const RowsGemmParams& p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int64_t pref[kMaxExperts + 1];
@@ -963,18 +1076,18 @@ __device__ __forceinline__ void grouped_rows_body(const RowsGemmParams& p) {
   __syncthreads();
 
   RowsSource<C> src{p, pref, tile_offs, G, n_tiles, tile_offs[G]};
-  persistent_loop<C>(src, smem, p.lda, p.ldas, p.ldb, p.ldbs);
+  persistent_loop<C, FAST>(src, smem, p.lda, p.ldas, p.ldb, p.ldbs);
 }
 
 // The forward and the input gradient run the same body; each pass has its own
 // kernel symbol so that traces and profiles report the two passes apart.
-template <class C>
+template <class C, bool FAST>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_fwd_kernel(const RowsGemmParams p) {
-  grouped_rows_body<C>(p);
+  grouped_rows_body<C, FAST>(p);
 }
-template <class C>
+template <class C, bool FAST>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_dgrad_kernel(const RowsGemmParams p) {
-  grouped_rows_body<C>(p);
+  grouped_rows_body<C, FAST>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1172,10 +1285,21 @@ static int64_t rows_tiles(const RowsGemmParams& p) {
   return mt * ((p.n_out + C::BN - 1) / C::BN);
 }
 
+template <class C, bool FAST>
+static hipError_t launch_rows_as(const RowsGemmParams& p, bool dgrad, int num_cus, hipStream_t st) {
+  if (dgrad) return launch_persistent<C>(grouped_dgrad_kernel<C, FAST>, p, rows_tiles<C>(p), num_cus, st);
+  return launch_persistent<C>(grouped_fwd_kernel<C, FAST>, p, rows_tiles<C>(p), num_cus, st);
+}
+
+// The read-ahead loop takes the fast DMA issue when every stage is full and
+// the per-lane scale offsets ((SB-1) blocks of ld bytes plus a row) fit 32 bits.
 template <class C>
 static hipError_t launch_rows(const RowsGemmParams& p, bool dgrad, int num_cus, hipStream_t st) {
-  if (dgrad) return launch_persistent<C>(grouped_dgrad_kernel<C>, p, rows_tiles<C>(p), num_cus, st);
-  return launch_persistent<C>(grouped_fwd_kernel<C>, p, rows_tiles<C>(p), num_cus, st);
+  if constexpr (C::SCHED == 7) {
+    constexpr int64_t kLim = (int64_t)1 << 30;
+    if (p.kc % C::BK == 0 && p.ldas < kLim && p.ldbs < kLim) return launch_rows_as<C, true>(p, dgrad, num_cus, st);
+  }
+  return launch_rows_as<C, false>(p, dgrad, num_cus, st);
 }
 
 hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, int num_cus, hipStream_t st) {

@@ -42,6 +42,9 @@ FWD_CASES = [
     ([0, 0, 7], 64, 1024),               # leading empty experts
     ([513, 255, 1, 0, 40], 320, 352),    # several M tiles, N tail, K tail
     ([700, 333], 512, 4096),             # long contraction
+    # every stage full (K % 128 == 0: the scalar-base DMA issue)
+    ([513, 255, 1, 0, 40], 320, 384),    # several M tiles, N tail
+    ([300, 0, 5], 192, 128),             # one stage, partial N tile
 ]
 
 
@@ -58,6 +61,8 @@ def test_fwd_many_experts_max_G():
     sp[rng.random(512) < 0.3] = 0
     gpu, ref = _fwd_case(sp, 64, 64, "mxfp4", seed=3)
     assert_gemm_close(gpu, ref, what="G=512")
+    gpu, ref = _fwd_case(sp, 64, 128, "mxfp4", seed=4)     # every stage full
+    assert_gemm_close(gpu, ref, what="G=512, K=128")
 
 
 def test_fwd_empty_batch_writes_nothing():

@@ -24,13 +24,16 @@ SRC = os.path.join(ROOT, "moe_grouped_block_mx_amd", "csrc", "gemm_mx.hip")
 # kernel name fragment (TileCfg parameters) -> the waits its stage loop must carry
 EXPECTED = {
     # a4w4 forward / input gradient: 8 waves, 128-deep stages, 4-stage read-ahead ring, DPS 5
-    "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1E": [5],
-    "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1E": [5],
+    # (Lb1: every stage full, scalar-base DMA issue; Lb0: the general issue)
+    "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb1E": [5],
+    "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb1E": [5],
+    "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [5],
+    "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [5],
     # a4w4 weight gradient: 4 waves, same ring, DPS 10
     "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi2ELi128ELi4ELi0ELi1ELi7ELi1E": [10],
     # power-of-two blockwise forward / input gradient: 64-deep stages, 3-stage ring, DPS 6
-    "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128E": [6],
-    "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128E": [6],
+    "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEELb0E": [6],
+    "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEELb0E": [6],
     # MXFP8 weight gradient (DPS 5) and power-of-two blockwise weight gradient
     # (DPS 6): the ring wait, then the tile switch's drain
     "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi4ELi1ELi5ELi1E": [5, 0],
