@@ -52,8 +52,10 @@
  *                     then apply the scales inside the MFMA (the fp32
  *                     exponent field is a UE8M0 code) instead of scaling a
  *                     per-128 partial: exact for powers of two, while a scale
- *                     that is not one loses its mantissa. Mixing a _P2 format
- *                     with a general one selects the general path.
+ *                     that is not one loses its mantissa. In the forward,
+ *                     mixing a _P2 format with a general one selects the
+ *                     general path; the input and weight gradients take one
+ *                     format for both operands, where _P2 asserts both.
  *
  * MX quantization rule (what mxgg_quantize_* produce): amax = max |x| over the
  * block; e = clamp(floor(log2 amax) - emax, -127, 127) with emax = 2 (E2M1) or
@@ -120,6 +122,28 @@ typedef enum mxgg_format {
   MXGG_FP8_128x128_P2 = 5
 } mxgg_format;
 
+/*
+ * MX scale layouts. An MX format argument may carry the layout of the scales
+ * it describes in its high bits: fmt = MXGG_MXFP4 | MXGG_LAYOUT_ROW_MAJOR.
+ * The layout is never inferred from shapes.
+ *   MXGG_LAYOUT_BLOCK_MAJOR (0, what a plain format means): the layout every
+ *     quantizer writes and every GEMM reads, u8 [blocks, R4] (see "MX scale
+ *     layout" above) -- the arrangement the GEMM stages load with one aligned
+ *     4-byte DMA per four rows of a block.
+ *   MXGG_LAYOUT_ROW_MAJOR: plain per-row scales, u8 [rows, blocks] (the
+ *     un-arranged scale layout of the page "Integrate MXFP4 hipblaslt GEMM
+ *     support"). The quantizers and GEMMs refuse it with MXGG_ERR_FORMAT; it
+ *     is never read as block-major. mxgg_mx_scales_relayout converts between
+ *     the two.
+ * Blockwise formats take no layout bits (their fp32 scales are row-major by
+ * definition); any layout bits on them are MXGG_ERR_FORMAT.
+ */
+typedef enum mxgg_scale_layout {
+  MXGG_LAYOUT_BLOCK_MAJOR = 0x000,
+  MXGG_LAYOUT_ROW_MAJOR = 0x100
+} mxgg_scale_layout;
+#define MXGG_LAYOUT_MASK 0xF00
+
 /* flags for the quantizers (blockwise formats only) */
 #define MXGG_POW2_SCALES 1u
 
@@ -131,6 +155,25 @@ typedef enum mxgg_format {
  * `rows` rows: rows rounded up to a multiple of 4 (0 for rows <= 0).
  */
 int64_t mxgg_mx_scale_stride(int64_t rows);
+
+/*
+ * MX scales from one layout into the other, on `stream`: row-major u8
+ * [rows, blocks] <-> block-major u8 [blocks, mxgg_mx_scale_stride(rows)]
+ * (padding rows written as 0). For callers that hold plain per-row UE8M0
+ * scales (the un-arranged layout the page "Integrate MXFP4 hipblaslt GEMM
+ * support" compares with pre-arranged ones) and want the GEMMs' layout, or
+ * back.
+ *   src, dst   device buffers in src_layout / dst_layout; must not overlap.
+ *   rows       rows of the operand (>= 0, < 2^31); blocks (> 0, <= 4194240):
+ *              scale blocks of 32 along the contraction (cols / 32).
+ * Layouts: MXGG_LAYOUT_ROW_MAJOR and MXGG_LAYOUT_BLOCK_MAJOR, different from
+ * each other (else MXGG_ERR_FORMAT). rows == 0 returns MXGG_OK (no launch).
+ * Errors: NULL, SHAPE, FORMAT, DEVICE, ARCH, HIP (no alignment requirement:
+ * byte data).
+ */
+mxgg_status mxgg_mx_scales_relayout(const void* src, mxgg_scale_layout src_layout, int64_t rows,
+                                    int64_t blocks, void* dst, mxgg_scale_layout dst_layout,
+                                    hipStream_t stream);
 
 /*
  * Row-wise quantization ("Triton mxfp4 (and a8w4) grouped GEMM kernel", the
@@ -201,8 +244,27 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
                                void* s_col, int64_t mpad, hipStream_t stream);
 
 /*
+ * 128x128-block FP8 weights transposed for the input gradient: the blocks are
+ * square, so the transpose's 128x128 quantization is the same codes and the
+ * same scale per block ("Add ROCm Triton blockwise FP8 grouped GEMM", weight
+ * blocks used in both passes).
+ *   w_q, w_s    from mxgg_quantize_rowwise(W as [G*N, K], MXGG_FP8_128x128):
+ *               E4M3 [G*N, K] + f32 [G*N/128, K/128].
+ *   wt_q, wt_s  written: E4M3 [G*K, N] (expert g's rows [g*K, (g+1)*K)) +
+ *               f32 [G*K/128, N/128]. Caller-owned; must not overlap w.
+ * N % 128 == 0, K % 128 == 0, N, K < 2^23, G in [1, 512].
+ * Errors: NULL, SHAPE, ALIGN, DEVICE, ARCH, HIP.
+ */
+mxgg_status mxgg_transpose_128x128(const void* w_q, const void* w_s, int32_t G, int64_t N,
+                                   int64_t K, void* wt_q, void* wt_s, hipStream_t stream);
+
+/*
  * Grouped forward, TN: out[r, n] = sum_k A[r, k] * W_g[n, k] for every row r
- * of expert g (rows of expert g are consecutive, in expert order).
+ * of expert g (rows of expert g are consecutive, in expert order). One launch
+ * covers every expert ("Triton mxfp4 (and a8w4) grouped GEMM kernel": the
+ * persistent grouped MXFP4 forward over the row operand and the packed expert
+ * weights; "route te.GroupedLinear through #723; a8w4 fwd-only": the a8w4
+ * pair; "Add ROCm Triton blockwise FP8 grouped GEMM": the blockwise pair).
  *   a_q, a_s  A quantized row-wise along K: (MXFP4: u8 [M, K/2] | MXFP8: u8 [M, K])
  *             + u8 [K/32, mxgg_mx_scale_stride(M)]; or MXGG_FP8_1x128: u8 [M, K]
  *             + f32 [M, K/128].
@@ -219,21 +281,6 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
  *             when that is 0).
  * Errors: NULL, SHAPE, SPLITS, FORMAT, ALIGN, WORKSPACE, DEVICE, ARCH, HIP.
  */
-/*
- * 128x128-block FP8 weights transposed for the input gradient: the blocks are
- * square, so the transpose's 128x128 quantization is the same codes and the
- * same scale per block ("Add ROCm Triton blockwise FP8 grouped GEMM", weight
- * blocks used in both passes).
- *   w_q, w_s    from mxgg_quantize_rowwise(W as [G*N, K], MXGG_FP8_128x128):
- *               E4M3 [G*N, K] + f32 [G*N/128, K/128].
- *   wt_q, wt_s  written: E4M3 [G*K, N] (expert g's rows [g*K, (g+1)*K)) +
- *               f32 [G*K/128, N/128]. Caller-owned; must not overlap w.
- * N % 128 == 0, K % 128 == 0, N, K < 2^23, G in [1, 512].
- * Errors: NULL, SHAPE, ALIGN, DEVICE, ARCH, HIP.
- */
-mxgg_status mxgg_transpose_128x128(const void* w_q, const void* w_s, int32_t G, int64_t N,
-                                   int64_t K, void* wt_q, void* wt_s, hipStream_t stream);
-
 mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt,
                              const void* w_q, const void* w_s, mxgg_format w_fmt,
                              const int64_t* m_splits, int32_t G, int64_t M, int64_t N,
@@ -256,8 +303,11 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
  *                  u8 [G*N/32, K] (expert g owns columns [g*N, (g+1)*N) and
  *                  scale blocks [g*N/32, (g+1)*N/32)).
  *                  Blockwise: W^T from mxgg_transpose_128x128, E4M3
- *                  [G*K, N] + f32 [G*K/128, N/128]; with _P2 (power-of-two
- *                  scales on both sides) the MFMA applies the scales.
+ *                  [G*K, N] + f32 [G*K/128, N/128]. MXGG_FP8_1x128_P2
+ *                  asserts that the scales of BOTH operands (dY's and the
+ *                  transposed weights') are powers of two, and the MFMA then
+ *                  applies them (a non-power-of-two scale would lose its
+ *                  mantissa); pass MXGG_FP8_1x128 when either is general.
  *   dx             bf16 [M, K].
  * Shape rules as for the forward, and (MX) G*N/2 < 2^23. Errors as for the
  * forward.
@@ -270,14 +320,21 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
 /*
  * Grouped variable-K weight gradient, NT: dW_g[n, k] = sum over the tokens t of
  * expert g of dY[t, n] * X[t, k], contracted over the expert's padded segment
- * (pad positions are zero codes, so they add nothing).
+ * (pad positions are zero codes, so they add nothing). One launch covers every
+ * expert, each with its own contraction length ("Triton mxfp4 (and a8w4)
+ * grouped GEMM kernel": the variable-K wgrad over the segment-padded column
+ * operands; "Add ROCm Triton blockwise FP8 grouped GEMM": its blockwise form
+ * and the in-place accumulation into the weight's main_grad).
  *   dycol_q/_s  dY from mxgg_quantize_colwise_segpad: [N, mpad] operand
  *               (MX scales u8 [mpad/32, N]).
  *   xcol_q/_s   X from mxgg_quantize_colwise_segpad: [K, mpad] operand
  *               (MX scales u8 [mpad/32, K]).
  *   fmt         MXGG_MXFP4 or MXGG_MXFP8 (both operands in that format: the
  *               a4w4 and a8w4 weight gradients; pad 32), or MXGG_FP8_1x128
- *               (pad 128).
+ *               (pad 128). MXGG_FP8_1x128_P2 asserts that the scales of BOTH
+ *               operands are powers of two (the MFMA then applies them and a
+ *               non-power-of-two scale would lose its mantissa); pass
+ *               MXGG_FP8_1x128 when either operand's scales are general.
  *   mpad        mxgg_segpad_rows(m_splits, G, fmt).
  *   main_grad   [G, N, K]: fp32 when out_is_bf16 == 0, else bf16 (blockwise
  *               formats only; an MX format with out_is_bf16 = 1 is

@@ -22,6 +22,8 @@ FORMATS = {"mxfp4": MXFP4, "mxfp8": MXFP8, "fp8_1x128": FP8_1x128, "fp8_128x128"
            "fp8_1x128_p2": FP8_1x128_P2, "fp8_128x128_p2": FP8_128x128_P2}
 POW2_SCALES = 1
 MAX_EXPERTS = 512
+# mxgg_scale_layout: OR-ed into an MX format to state the layout of its scales
+LAYOUT_BLOCK_MAJOR, LAYOUT_ROW_MAJOR, LAYOUT_MASK = 0x000, 0x100, 0xF00
 
 STATUS = {
     0: "MXGG_OK", 1: "MXGG_ERR_NULL", 2: "MXGG_ERR_SHAPE", 3: "MXGG_ERR_SPLITS",
@@ -49,6 +51,7 @@ _SIGS = {
     "mxgg_transpose_128x128": [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp],
     "mxgg_grouped_wgrad": [_vp, _vp, _vp, _vp, _i32, _i64p, _i32, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _sz,
                            _vp],
+    "mxgg_mx_scales_relayout": [_vp, _i32, _i64, _i64, _vp, _i32, _vp],
 }
 
 
@@ -144,26 +147,35 @@ def _expect(t, name, shape, dtypes):
 
 
 def _is_mx(f):
-    return f in (MXFP4, MXFP8)
+    return (f & 0xFF) in (MXFP4, MXFP8)
+
+
+def _row_major(f):
+    return (f & LAYOUT_MASK) == LAYOUT_ROW_MAJOR
 
 
 def _q_shape(f, rows, cols):
     """Quantized data of a [rows, cols] operand packed along cols."""
-    return (rows, cols // 2 if f == MXFP4 else cols)
+    return (rows, cols // 2 if (f & 0xFF) == MXFP4 else cols)
 
 
 def _row_scale_shape(f, rows, cols):
-    """Scales of a [rows, cols] operand quantized along cols."""
+    """Scales of a [rows, cols] operand quantized along cols (row-major scales
+    when the format says so: the library refuses them, never misreads them)."""
     if _is_mx(f):
+        if _row_major(f):
+            return (rows, cols // 32)
         return (cols // 32, mxgg_mx_scale_stride(rows))           # block-major
-    if f in (FP8_1x128, FP8_1x128_P2):
+    if (f & 0xFF) in (FP8_1x128, FP8_1x128_P2):
         return (rows, cols // 128)
     return (rows // 128, cols // 128)
 
 
 def _col_scale_shape(f, cols, mpad):
     """Scales of the column-wise segment-padded [cols, mpad] operand."""
-    return (mpad // 32, cols) if _is_mx(f) else (cols, mpad // 128)
+    if _is_mx(f):
+        return (cols, mpad // 32) if _row_major(f) else (mpad // 32, cols)
+    return (cols, mpad // 128)
 
 
 def _sdtype(f):
@@ -186,8 +198,23 @@ def mxgg_segpad_rows(m_splits, fmt) -> int:
 def _flags(flags, f):
     """Power-of-two scales are the blockwise default; MX formats take no flags."""
     if flags is None:
-        return POW2_SCALES if f in (FP8_1x128, FP8_128x128, FP8_1x128_P2, FP8_128x128_P2) else 0
+        return POW2_SCALES if (f & 0xFF) in (FP8_1x128, FP8_128x128, FP8_1x128_P2, FP8_128x128_P2) else 0
     return int(flags)
+
+
+def mxgg_mx_scales_relayout(src, rows, blocks, src_layout, dst_layout, dst=None):
+    """MX scales row-major u8 [rows, blocks] <-> block-major u8
+    [blocks, mx_scale_stride(rows)] (padding rows 0). Returns dst."""
+    torch = _torch()
+    src_shape = (rows, blocks) if src_layout == LAYOUT_ROW_MAJOR else (blocks, mxgg_mx_scale_stride(rows))
+    dst_shape = (rows, blocks) if dst_layout == LAYOUT_ROW_MAJOR else (blocks, mxgg_mx_scale_stride(rows))
+    _expect(src, "src", src_shape, torch.uint8)
+    if dst is None:
+        dst = torch.empty(dst_shape, dtype=torch.uint8, device=src.device)
+    _expect(dst, "dst", dst_shape, torch.uint8)
+    _check(lib.mxgg_mx_scales_relayout(_ptr(src), int(src_layout), int(rows), int(blocks), _ptr(dst),
+                                       int(dst_layout), _stream(src)))
+    return dst
 
 
 def mxgg_mx_scale_stride(rows):
@@ -204,15 +231,10 @@ def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=None, q=None, scales=None):
     rows, cols = x.shape
     _check_bf16_2d(x)
     if q is None:
-        q = torch.empty((rows, cols // 2 if f == MXFP4 else cols), dtype=torch.uint8, device=x.device)
+        q = torch.empty(_q_shape(f, rows, cols), dtype=torch.uint8, device=x.device)
     if scales is None:
-        if f in (MXFP4, MXFP8):
-            # block-major, block stride = rows rounded up to a multiple of 4
-            scales = torch.empty((cols // 32, mxgg_mx_scale_stride(rows)), dtype=torch.uint8, device=x.device)
-        elif f in (FP8_1x128, FP8_1x128_P2):
-            scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
-        else:
-            scales = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=x.device)
+        # MX: block-major, block stride = rows rounded up to a multiple of 4
+        scales = torch.empty(_row_scale_shape(f, rows, cols), dtype=_sdtype(f), device=x.device)
     _expect(q, "q", _q_shape(f, rows, cols), torch.uint8)
     _expect(scales, "scales", _row_scale_shape(f, rows, cols), _sdtype(f))
     _check(lib.mxgg_quantize_rowwise(_ptr(x), rows, cols, _ld(x), f, flags, _ptr(q), _ptr(scales),
@@ -232,12 +254,9 @@ def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=None, q=None, s
     if mpad < 0:
         mpad = 0
     if q is None:
-        q = torch.empty((cols, mpad // 2 if f == MXFP4 else mpad), dtype=torch.uint8, device=x.device)
+        q = torch.empty(_q_shape(f, cols, mpad), dtype=torch.uint8, device=x.device)
     if scales is None:
-        if f in (FP8_1x128, FP8_1x128_P2):
-            scales = torch.empty((cols, mpad // 128), dtype=torch.float32, device=x.device)
-        else:
-            scales = torch.empty((mpad // 32, cols), dtype=torch.uint8, device=x.device)  # block-major
+        scales = torch.empty(_col_scale_shape(f, cols, mpad), dtype=_sdtype(f), device=x.device)
     _expect(q, "q", _q_shape(f, cols, mpad), torch.uint8)
     _expect(scales, "scales", _col_scale_shape(f, cols, mpad), _sdtype(f))
     _check(lib.mxgg_quantize_colwise_segpad(_ptr(x), rows, cols, _ld(x), arr, G, f, flags, _ptr(q),
@@ -258,15 +277,14 @@ def mxgg_quantize_dual(x, m_splits, fmt="mxfp4", flags=None, q_row=None, s_row=N
     if mpad < 0:
         mpad = 0
     u8 = dict(dtype=torch.uint8, device=x.device)
-    fp4 = f == MXFP4
     if q_row is None:
-        q_row = torch.empty((rows, cols // 2 if fp4 else cols), **u8)
+        q_row = torch.empty(_q_shape(f, rows, cols), **u8)
     if s_row is None:
-        s_row = torch.empty((cols // 32, mxgg_mx_scale_stride(rows)), **u8)
+        s_row = torch.empty(_row_scale_shape(f, rows, cols), dtype=_sdtype(f), device=x.device)
     if q_col is None:
-        q_col = torch.empty((cols, mpad // 2 if fp4 else mpad), **u8)
+        q_col = torch.empty(_q_shape(f, cols, mpad), **u8)
     if s_col is None:
-        s_col = torch.empty((mpad // 32, cols), **u8)
+        s_col = torch.empty(_col_scale_shape(f, cols, mpad), dtype=_sdtype(f), device=x.device)
     if _is_mx(f):
         _expect(q_row, "q_row", _q_shape(f, rows, cols), torch.uint8)
         _expect(s_row, "s_row", _row_scale_shape(f, rows, cols), torch.uint8)
@@ -367,3 +385,4 @@ grouped_wgrad = mxgg_grouped_wgrad
 workspace_size = mxgg_workspace_size
 segpad_rows = mxgg_segpad_rows
 mx_scale_stride = mxgg_mx_scale_stride
+mx_scales_relayout = mxgg_mx_scales_relayout

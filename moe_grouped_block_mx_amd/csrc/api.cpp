@@ -154,6 +154,20 @@ int64_t mxgg_segpad_rows(const int64_t* m_splits, int32_t G, mxgg_format fmt) {
 
 int64_t mxgg_mx_scale_stride(int64_t rows) { return mx_scale_stride(rows); }
 
+mxgg_status mxgg_mx_scales_relayout(const void* src, mxgg_scale_layout src_layout, int64_t rows, int64_t blocks,
+                                    void* dst, mxgg_scale_layout dst_layout, hipStream_t stream) {
+  Check c = validate_relayout(src, (int)src_layout, rows, blocks, dst, (int)dst_layout);
+  if (!c.ok()) return finish(c);
+  if (rows == 0) return ok();
+  int cus = 0;
+  c = device_checks(stream, {{src, "src"}, {dst, "dst"}}, &cus);
+  if (!c.ok()) return finish(c);
+  c = hip_status(launch_relayout_scales(static_cast<const uint8_t*>(src), rows, blocks,
+                                        dst_layout == MXGG_LAYOUT_BLOCK_MAJOR, static_cast<uint8_t*>(dst), stream),
+                 "scale relayout launch");
+  return c.ok() ? ok() : finish(c);
+}
+
 mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, mxgg_format fmt,
                                   uint32_t flags, void* q, void* scales, hipStream_t stream) {
   if (is_p2(fmt)) flags |= MXGG_POW2_SCALES;

@@ -90,6 +90,10 @@ hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols
                                    bool fp8, uint8_t* q, uint8_t* s, int64_t mpad, hipStream_t st);
 
 // dgrad selects the input-gradient kernel symbol (same code as the forward's)
+// MX scales row-major [rows, blocks] -> block-major [blocks, R4] (or back)
+hipError_t launch_relayout_scales(const uint8_t* src, int64_t rows, int64_t blocks, bool to_block_major,
+                                  uint8_t* dst, hipStream_t st);
+
 hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, int num_cus, hipStream_t st);
 // fp8: E4M3 operands on both sides (MXFP8), else E2M1 (MXFP4)
 hipError_t launch_grouped_wgrad_mx(const WgradParams& p, bool fp8, int num_cus, hipStream_t st);

@@ -515,3 +515,54 @@ hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols
 }
 
 }  // namespace mxgg
+
+namespace mxgg {
+
+// ---------------------------------------------------------------------------
+// MX scale relayout: row-major u8 [rows, blocks] <-> block-major u8
+// [blocks, R4] (R4 = rows rounded up to 4, padding rows 0). A 64 x 64 byte
+// tile per workgroup goes through LDS so both sides are read and written
+// along their contiguous axis.
+// ---------------------------------------------------------------------------
+template <bool TO_BLOCK_MAJOR>
+__global__ __launch_bounds__(256) void relayout_scales_kernel(const uint8_t* __restrict__ src, int64_t rows,
+                                                              int64_t blocks, int64_t r4, uint8_t* __restrict__ dst) {
+  __shared__ uint8_t t[64][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, b0 = (int64_t)blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    if constexpr (TO_BLOCK_MAJOR) {  // read rows (blocks contiguous)
+      const int r = i >> 6, b = i & 63;
+      const int64_t rr = r0 + r, bb = b0 + b;
+      t[r][b] = (rr < rows && bb < blocks) ? src[rr * blocks + bb] : (uint8_t)0;
+    } else {                         // read blocks (rows contiguous)
+      const int b = i >> 6, r = i & 63;
+      const int64_t rr = r0 + r, bb = b0 + b;
+      t[r][b] = (rr < rows && bb < blocks) ? src[bb * r4 + rr] : (uint8_t)0;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    if constexpr (TO_BLOCK_MAJOR) {  // write blocks (rows contiguous, padding rows 0)
+      const int b = i >> 6, r = i & 63;
+      const int64_t rr = r0 + r, bb = b0 + b;
+      if (bb < blocks && rr < r4) dst[bb * r4 + rr] = t[r][b];
+    } else {
+      const int r = i >> 6, b = i & 63;
+      const int64_t rr = r0 + r, bb = b0 + b;
+      if (rr < rows && bb < blocks) dst[rr * blocks + bb] = t[r][b];
+    }
+  }
+}
+
+hipError_t launch_relayout_scales(const uint8_t* src, int64_t rows, int64_t blocks, bool to_block_major,
+                                  uint8_t* dst, hipStream_t st) {
+  const int64_t r4 = mx_scale_stride(rows);
+  const dim3 grid((unsigned)((r4 + 63) / 64), (unsigned)((blocks + 63) / 64));
+  if (to_block_major)
+    hipLaunchKernelGGL(relayout_scales_kernel<true>, grid, dim3(256), 0, st, src, rows, blocks, r4, dst);
+  else
+    hipLaunchKernelGGL(relayout_scales_kernel<false>, grid, dim3(256), 0, st, src, rows, blocks, r4, dst);
+  return hipGetLastError();
+}
+
+}  // namespace mxgg

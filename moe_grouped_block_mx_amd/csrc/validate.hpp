@@ -36,6 +36,11 @@ inline Check fail(mxgg_status st, const char* fmt, long long a = 0, long long b 
 
 inline bool is_mx(mxgg_format f) { return f == MXGG_MXFP4 || f == MXGG_MXFP8; }
 inline bool valid_format(int f) { return f >= MXGG_MXFP4 && f <= MXGG_FP8_128x128_P2; }
+
+// A format argument with layout bits: the scales it describes are not in the
+// block-major layout the kernels read (or the bits are unknown). Refused by
+// name, so a caller's row-major scales are never read as block-major.
+inline bool has_layout_bits(int f) { return (f & ~0xFF) != 0; }
 // The power-of-two blockwise formats share their base format's layout.
 inline bool is_p2(int f) { return f == MXGG_FP8_1x128_P2 || f == MXGG_FP8_128x128_P2; }
 inline int base_format(int f) {
@@ -72,6 +77,18 @@ constexpr int64_t kMaxSplit = ((int64_t)1 << 31) - 1;
 
 // Padded row count; callers have checked 0 <= m[g] <= kMaxSplit, so neither
 // the rounding nor the sum (at most 512 terms) can overflow.
+inline Check check_layout(int f, const char* what) {
+  if (!has_layout_bits(f)) return Check{};
+  if ((f & ~0xFF) == MXGG_LAYOUT_ROW_MAJOR && is_mx((mxgg_format)(f & 0xFF))) {
+    Check r;
+    r.st = MXGG_ERR_FORMAT;
+    r.msg = std::string(what) + ": row-major MX scales are not accepted (the kernels read block-major "
+            "scales); convert them with mxgg_mx_scales_relayout";
+    return r;
+  }
+  return fail(MXGG_ERR_FORMAT, "format 0x%llx: unknown layout bits or a layout on a blockwise format", f);
+}
+
 inline int64_t segpad_rows(const int64_t* m, int32_t G, int pad) {
   int64_t s = 0;
   for (int32_t g = 0; g < G; ++g) s += (m[g] + pad - 1) / pad * pad;
@@ -103,6 +120,7 @@ inline Check check_ptr(const void* p, bool nonzero, const char* name) {
 
 inline Check validate_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                        const void* q, const void* scales) {
+  MXGG_TRY(check_layout(fmt, "quantize_rowwise"));
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
   if (rows < 0 || cols <= 0) return fail(MXGG_ERR_SHAPE, "rows=%lld cols=%lld", rows, cols);
   const mxgg_format f = (mxgg_format)fmt;
@@ -124,6 +142,7 @@ inline Check validate_quantize_rowwise(const void* x, int64_t rows, int64_t cols
 
 inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, const int64_t* m,
                                        int32_t G, int fmt, const void* q, const void* scales, int64_t mpad) {
+  MXGG_TRY(check_layout(fmt, "quantize_colwise"));
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
   const mxgg_format f = (mxgg_format)fmt;
   if (f == MXGG_FP8_128x128) return fail(MXGG_ERR_FORMAT, "128x128 blocks have no column-wise form");
@@ -150,6 +169,7 @@ inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols
 inline Check validate_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, const int64_t* m,
                                     int32_t G, int fmt, const void* q_row, const void* s_row, const void* q_col,
                                     const void* s_col, int64_t mpad) {
+  MXGG_TRY(check_layout(fmt, "quantize_dual"));
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
   if (!is_mx((mxgg_format)fmt)) return fail(MXGG_ERR_FORMAT, "the dual quantizer takes MX formats only");
   MXGG_TRY(validate_quantize_rowwise(x, rows, cols, ldx, fmt, q_row, s_row));
@@ -172,6 +192,8 @@ inline Check validate_gemm_dims(int64_t M, int64_t N, int64_t K, int blk) {
 inline Check validate_fwd(const void* a_q, const void* a_s, int a_fmt, const void* w_q, const void* w_s, int w_fmt,
                           const int64_t* m, int32_t G, int64_t M, int64_t N, int64_t K, const void* out,
                           const void* ws, size_t ws_bytes, size_t ws_need) {
+  MXGG_TRY(check_layout(a_fmt, "fwd A"));
+  MXGG_TRY(check_layout(w_fmt, "fwd W"));
   if (!valid_format(a_fmt) || !valid_format(w_fmt)) return fail(MXGG_ERR_FORMAT, "unknown format");
   const bool a4w4 = a_fmt == MXGG_MXFP4 && w_fmt == MXGG_MXFP4;
   const bool a8w4 = a_fmt == MXGG_MXFP8 && w_fmt == MXGG_MXFP4;
@@ -195,6 +217,7 @@ inline Check validate_fwd(const void* a_q, const void* a_s, int a_fmt, const voi
 inline Check validate_dgrad(const void* dy_q, const void* dy_s, const void* wc_q, const void* wc_s, int fmt,
                             const int64_t* m, int32_t G, int64_t M, int64_t N, int64_t K, const void* dx,
                             const void* ws, size_t ws_bytes, size_t ws_need) {
+  MXGG_TRY(check_layout(fmt, "dgrad"));
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
   // fmt is dY's format: MXFP4 (a4w4) or MXFP8 (a8w4) with W column-wise in
   // MXFP4; FP8_1x128 with the transposed 128x128 weight blocks
@@ -236,6 +259,7 @@ inline Check validate_wgrad(const void* dy_q, const void* dy_s, const void* x_q,
                             const int64_t* m, int32_t G, int64_t N, int64_t K, int64_t mpad, const void* main_grad,
                             int32_t out_is_bf16, int32_t accumulate, const void* ws, size_t ws_bytes,
                             size_t ws_need) {
+  MXGG_TRY(check_layout(fmt, "wgrad"));
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
   if (fmt != MXGG_MXFP4 && fmt != MXGG_MXFP8 && fmt != MXGG_FP8_1x128)
     return fail(MXGG_ERR_FORMAT, "wgrad supports MXGG_MXFP4, MXGG_MXFP8 and MXGG_FP8_1x128 (got %lld)", fmt);
@@ -271,6 +295,21 @@ inline Check validate_wgrad(const void* dy_q, const void* dy_s, const void* x_q,
   MXGG_TRY(check_ptr(x_q, nz, "xcol_q"));
   MXGG_TRY(check_ptr(x_s, nz, "xcol_s"));
   MXGG_TRY(check_ptr(main_grad, true, "main_grad"));
+  return Check{};
+}
+
+// Scale relayout: row-major <-> block-major MX scales.
+inline Check validate_relayout(const void* src, int src_layout, int64_t rows, int64_t blocks, const void* dst,
+                               int dst_layout) {
+  const bool known = (src_layout == MXGG_LAYOUT_ROW_MAJOR || src_layout == MXGG_LAYOUT_BLOCK_MAJOR) &&
+                     (dst_layout == MXGG_LAYOUT_ROW_MAJOR || dst_layout == MXGG_LAYOUT_BLOCK_MAJOR);
+  if (!known || src_layout == dst_layout)
+    return fail(MXGG_ERR_FORMAT, "relayout from 0x%llx to 0x%llx: need one row-major and one block-major layout",
+                src_layout, dst_layout);
+  // 64 blocks per workgroup on the grid's y axis
+  if (rows < 0 || rows >= ((int64_t)1 << 31) || blocks <= 0 || blocks > (int64_t)65535 * 64)
+    return fail(MXGG_ERR_SHAPE, "rows=%lld blocks=%lld (0 <= rows < 2^31, 0 < blocks <= 4194240)", rows, blocks);
+  if (rows > 0 && (!src || !dst)) return fail(MXGG_ERR_NULL, "src or dst is NULL");
   return Check{};
 }
 

@@ -222,3 +222,54 @@ def test_wgrad_rejects_splits_at_or_above_2_31():
     assert L.mxgg_segpad_rows(splits(I64_MAX, 1), 2, 0) == -1
     assert L.mxgg_segpad_rows(splits(2 ** 31, 1), 2, 0) == -1
     assert L.mxgg_segpad_rows(splits(2 ** 31 - 1, 1), 2, 0) == 2 ** 31 + 32
+
+
+ROW_MAJOR = 0x100
+
+
+def _header_enum(name):
+    import re
+    txt = open(mx._lib.HEADER).read()
+    body = re.search(r"typedef enum " + name + r" \{(.*?)\}", txt, re.S).group(1)
+    return {k: int(v, 0) for k, v in re.findall(r"(MXGG_\w+)\s*=\s*(0x[0-9a-fA-F]+|\d+)", body)}
+
+
+def test_scale_layout_enum_declared():
+    assert _header_enum("mxgg_scale_layout") == {"MXGG_LAYOUT_BLOCK_MAJOR": 0, "MXGG_LAYOUT_ROW_MAJOR": ROW_MAJOR}
+    assert mx.LAYOUT_ROW_MAJOR == ROW_MAJOR and mx.LAYOUT_BLOCK_MAJOR == 0
+    # layout bits sit above every format value
+    assert max(_header_enum("mxgg_format").values()) < 0x100
+
+
+def test_row_major_scales_refused_by_every_entry_point():
+    m = splits(32, 0)
+    f = 0 | ROW_MAJOR
+    calls = {
+        "rowwise": lambda: L.mxgg_quantize_rowwise(P, 32, 64, 64, f, 0, P, P, NULL),
+        "colwise": lambda: L.mxgg_quantize_colwise_segpad(P, 32, 64, 64, m, 2, f, 0, P, P, 32, NULL),
+        "dual": lambda: L.mxgg_quantize_dual(P, 32, 64, 64, m, 2, f, 0, P, P, P, P, 32, NULL),
+        "fwd A": lambda: fwd(m, 2, 32, a_fmt=f),
+        "fwd W": lambda: fwd(m, 2, 32, w_fmt=f),
+        "dgrad": lambda: L.mxgg_grouped_dgrad(P, P, P, P, f, m, 2, 32, 64, 64, P, NULL, 0, NULL),
+        "wgrad": lambda: L.mxgg_grouped_wgrad(P, P, P, P, f, m, 2, 64, 64, 32, P, 0, 1, NULL, 0, NULL),
+    }
+    for name, call in calls.items():
+        assert call() == 4, name
+        assert "relayout" in last(), (name, last())
+    # MXFP8 with row-major scales too; unknown layout bits; a layout on a blockwise format
+    assert fwd(m, 2, 32, a_fmt=1 | ROW_MAJOR) == 4
+    assert fwd(m, 2, 32, a_fmt=0x200) == 4
+    assert L.mxgg_quantize_rowwise(P, 128, 128, 128, 2 | ROW_MAJOR, 0, P, P, NULL) == 4
+    # an empty batch is still refused: validation runs before the early return
+    assert fwd(splits(0, 0), 2, 0, a_fmt=f, a=NULL, out=NULL) == 4
+
+
+def test_relayout_validation():
+    R, B = 0x100, 0x000
+    assert L.mxgg_mx_scales_relayout(P, R, 10, 4, P, R, NULL) == 4          # same layout
+    assert L.mxgg_mx_scales_relayout(P, 0x300, 10, 4, P, B, NULL) == 4     # unknown layout
+    assert L.mxgg_mx_scales_relayout(P, R, -1, 4, P, B, NULL) == 2
+    assert L.mxgg_mx_scales_relayout(P, R, 10, 0, P, B, NULL) == 2
+    assert L.mxgg_mx_scales_relayout(P, R, 10, 65535 * 64 + 1, P, B, NULL) == 2
+    assert L.mxgg_mx_scales_relayout(NULL, R, 10, 4, P, B, NULL) == 1
+    assert L.mxgg_mx_scales_relayout(NULL, R, 0, 4, NULL, B, NULL) == 0     # nothing to do
