@@ -10,12 +10,22 @@ gradient plus the variable-K weight gradient, with
   sees no weight gradient;
 - an optional delayed weight gradient: its quantized operands are kept and
   ``backward_dw()`` launches them later (for pipeline schedules that split
-  the input and weight gradients).
+  the input and weight gradients);
+- ``is_first_microbatch`` (None: quantize whenever the weight changed; True:
+  quantize now; False: reuse the cached quantization, and fail loudly if
+  there is none or it does not fit the layer);
+- ``weight.overwrite_main_grad``: when True at a backward, that backward's
+  weight gradient overwrites ``main_grad`` (experts with no tokens become
+  zero) instead of adding to it -- the first microbatch of an accumulation;
+- caller-provided ``out`` (forward output) and ``dgrad_out`` (input gradient)
+  buffers, written in place and returned (aliased).
 
 Pages: "Triton mxfp4 (and a8w4) grouped GEMM kernel" (the GroupedLinear
-integration, a4w4 and a8w4) and "Add ROCm Triton blockwise FP8 grouped GEMM"
-(blockwise FP8, the weight-quantization cache across microbatches, fused
-main_grad accumulation). Every step runs in libmxgg's kernels; this file only
+integration, a4w4 and a8w4), "Add ROCm Triton blockwise FP8 grouped GEMM"
+(blockwise FP8, the weight-quantization cache across microbatches with
+is_first_microbatch, fused main_grad accumulation and the first-microbatch
+logic, overwrite_main_grad) and "route te.GroupedLinear through #723; a8w4
+fwd-only" (its review: preallocated out and dgrad_out buffers are honoured). Every step runs in libmxgg's kernels; this file only
 orders the calls and keeps the quantized operands between forward and
 backward. Tensors must live on the GPU: the library rejects anything else.
 
@@ -47,9 +57,17 @@ class _WeightCache:
         self.fwd = None   # (q, s)
         self.dgrad = None  # (q, s)
 
-    def get(self, weight, recipe, G, N, K):
+    def get(self, weight, recipe, G, N, K, is_first_microbatch=None):
         key = (weight.data_ptr(), weight._version, recipe)
-        if key != self.key:
+        if is_first_microbatch is False:
+            # reuse without checking the version (the caller promises the
+            # weight is unchanged); refuse a cache that cannot serve the layer
+            if self.fwd is None or self.key[2] != recipe or self.key[0] != weight.data_ptr() \
+                    or self.fwd[0].device != weight.device or self.fwd[0].shape[0] != G * N:
+                raise RuntimeError("is_first_microbatch=False but no compatible cached weight quantization exists "
+                                   "(run a microbatch with is_first_microbatch=True or None first)")
+            return self.fwd, self.dgrad
+        if is_first_microbatch or key != self.key:
             r = RECIPES[recipe]
             if recipe == "blockwise":
                 q, s = L.mxgg_quantize_rowwise(weight, r["wgt"])
@@ -80,15 +98,18 @@ def _quantize_act(x, m_splits, fmt, need_col):
 
 class _GroupedLinearFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, weight, m_splits, module):
+    def forward(ctx, x, weight, m_splits, module, is_first_microbatch, out, dgrad_out):
         G, N, K, recipe = module.num_experts, module.out_features, module.in_features, module.recipe
         r = RECIPES[recipe]
-        (wq, ws), wdgrad = module._cache.get(weight, recipe, G, N, K)
+        (wq, ws), wdgrad = module._cache.get(weight, recipe, G, N, K, is_first_microbatch)
         need_wgrad = ctx.needs_input_grad[1]
         xrow, xcol = _quantize_act(x, m_splits, r["act"], need_wgrad)
-        y = L.mxgg_grouped_fwd(xrow[0], xrow[1], wq, ws, m_splits, N, K, a_fmt=r["act"], w_fmt=r["wgt"])
+        y = L.mxgg_grouped_fwd(xrow[0], xrow[1], wq, ws, m_splits, N, K, a_fmt=r["act"], w_fmt=r["wgt"], out=out)
         ctx.module, ctx.m_splits, ctx.wdgrad, ctx.xcol = module, m_splits, wdgrad, xcol
         ctx.need_dx = ctx.needs_input_grad[0]
+        ctx.dgrad_out = dgrad_out
+        if out is not None:
+            ctx.mark_dirty(out)
         return y
 
     @staticmethod
@@ -102,15 +123,17 @@ class _GroupedLinearFn(torch.autograd.Function):
         dx = None
         if ctx.need_dx:
             dx = L.mxgg_grouped_dgrad(drow[0], drow[1], ctx.wdgrad[0], ctx.wdgrad[1], m_splits, N, K,
-                                      fmt=r["grad"])
+                                      fmt=r["grad"], dx=ctx.dgrad_out)
         if need_wgrad:
-            job = (dcol[0], dcol[1], ctx.xcol[0], ctx.xcol[1], m_splits, dcol[2])
+            # the accumulation mode is the one in force at this backward
+            accumulate = not getattr(module.weight, "overwrite_main_grad", False)
+            job = (dcol[0], dcol[1], ctx.xcol[0], ctx.xcol[1], m_splits, dcol[2], accumulate)
             if module.delay_wgrad:
                 module._pending.append(job)
             else:
                 module._run_wgrad(job)
-        ctx.xcol = ctx.wdgrad = None
-        return dx, None, None, None
+        ctx.xcol = ctx.wdgrad = ctx.dgrad_out = None
+        return dx, None, None, None, None, None, None
 
 
 class GroupedLinear(torch.nn.Module):
@@ -129,19 +152,27 @@ class GroupedLinear(torch.nn.Module):
         self.weight = torch.nn.Parameter(w.to(torch.bfloat16))
         self.weight.main_grad = torch.zeros((num_experts, out_features, in_features), dtype=torch.float32,
                                             device=device)
+        self.weight.overwrite_main_grad = False
         self._cache = _WeightCache()
         self._pending = []
 
-    def forward(self, x, m_splits):
+    def forward(self, x, m_splits, is_first_microbatch=None, out=None, dgrad_out=None):
+        """x bf16 [M, K]; out: optional bf16 [M, N] written and returned;
+        dgrad_out: optional bf16 [M, K] that receives the input gradient."""
         if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != self.in_features:
             raise ValueError(f"x must be bf16 [M, {self.in_features}], got {tuple(x.shape)} {x.dtype}")
+        M = x.shape[0]
+        for name, buf, shape in (("out", out, (M, self.out_features)), ("dgrad_out", dgrad_out, (M, self.in_features))):
+            if buf is not None and (buf.dtype != torch.bfloat16 or tuple(buf.shape) != shape
+                                    or not buf.is_contiguous() or buf.device != x.device):
+                raise ValueError(f"{name} must be a contiguous bf16 {shape} tensor on {x.device}")
         m_splits = [int(m) for m in m_splits]
-        return _GroupedLinearFn.apply(x, self.weight, m_splits, self)
+        return _GroupedLinearFn.apply(x, self.weight, m_splits, self, is_first_microbatch, out, dgrad_out)
 
     def _run_wgrad(self, job):
-        dq, ds, xq, xs, m_splits, mpad = job
+        dq, ds, xq, xs, m_splits, mpad, accumulate = job
         L.mxgg_grouped_wgrad(dq, ds, xq, xs, m_splits, self.out_features, self.in_features, mpad,
-                             self.weight.main_grad, accumulate=True, fmt=RECIPES[self.recipe]["grad"])
+                             self.weight.main_grad, accumulate=accumulate, fmt=RECIPES[self.recipe]["grad"])
 
     def backward_dw(self):
         """Launch the delayed weight gradients, oldest first."""

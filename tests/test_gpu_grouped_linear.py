@@ -2,8 +2,11 @@
 a4w4, a8w4 and blockwise recipes: forward, input gradient and the weight
 gradient accumulated into fp32 main_grad match the fp64 oracle on the oracle's
 quantized operands (tolerance 2^-7 |ref| + 1e-3 rms(ref)); two microbatches
-accumulate; the weight quantization is reused until the weight changes; a
-delayed weight gradient equals the immediate one bit for bit."""
+accumulate; the weight quantization is reused until the weight changes and
+follows is_first_microbatch; overwrite_main_grad makes the first microbatch
+overwrite main_grad (immediate and delayed); preallocated out / dgrad_out are
+written and returned; a delayed weight gradient equals the immediate one bit
+for bit."""
 import numpy as np
 import pytest
 
@@ -128,3 +131,65 @@ def test_frozen_input_and_empty_batch():
     e.sum().backward()
     torch.cuda.synchronize()
     assert e.shape == (0, N)
+
+
+def test_overwrite_main_grad_on_the_first_microbatch():
+    # overwrite_main_grad set for the first microbatch: its weight gradient
+    # replaces whatever main_grad held (experts with no tokens become zero);
+    # cleared afterwards: later microbatches add ("Add ROCm Triton blockwise
+    # FP8 grouped GEMM", first-microbatch accumulation logic)
+    M = sum(SPLITS)
+    xs = [bf16_normal((M, K), 1.0, seed=40 + i) for i in range(2)]
+    dys = [bf16_normal((M, N), 1.0, seed=50 + i) for i in range(2)]
+    for delay in (False, True):
+        layer = _layer("a4w4", delay=delay)
+        layer.weight.main_grad.fill_(7.0)                       # stale contents
+        layer.weight.overwrite_main_grad = True
+        layer(dev_bf16(xs[0]), SPLITS).backward(dev_bf16(dys[0]))
+        layer.weight.overwrite_main_grad = False                 # the mode of each backward is kept
+        layer(dev_bf16(xs[1]), SPLITS).backward(dev_bf16(dys[1]))
+        if delay:
+            layer.backward_dw()
+        torch.cuda.synchronize()
+        w_bits = _bits(layer.weight)
+        rdw = [_oracle("a4w4", xs[i], w_bits, dys[i], SPLITS)[2] for i in range(2)]
+        got = host(layer.weight.main_grad).astype(np.float64)
+        assert not got[1].any(), "the empty expert was not zero-filled"
+        assert_gemm_close(got, rdw[0] + rdw[1], what=f"overwrite then accumulate (delay={delay})")
+
+
+def test_preallocated_out_and_dgrad_out_are_written_and_returned():
+    layer = _layer("a4w4")
+    M = sum(SPLITS)
+    x_bits, dy_bits = bf16_normal((M, K), 1.0, seed=60), bf16_normal((M, N), 1.0, seed=61)
+    x = dev_bf16(x_bits).requires_grad_(True)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dgrad_out = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    y = layer(x, SPLITS, out=out, dgrad_out=dgrad_out)
+    (gx,) = torch.autograd.grad(y, x, dev_bf16(dy_bits))
+    torch.cuda.synchronize()
+    assert y.data_ptr() == out.data_ptr() and gx.data_ptr() == dgrad_out.data_ptr()
+    ry, rdx, _ = _oracle("a4w4", x_bits, _bits(layer.weight), dy_bits, SPLITS)
+    assert_gemm_close(host_bf16_f64(out), ry, what="forward into out")
+    assert_gemm_close(host_bf16_f64(dgrad_out), rdx, what="input gradient into dgrad_out")
+    with pytest.raises(ValueError, match="dgrad_out"):
+        layer(x, SPLITS, dgrad_out=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
+
+
+def test_is_first_microbatch_controls_weight_quantization():
+    layer = _layer("a4w4")
+    M = sum(SPLITS)
+    x = dev_bf16(bf16_normal((M, K), 1.0, seed=70))
+    with pytest.raises(RuntimeError, match="is_first_microbatch=False"):
+        layer(x, SPLITS, is_first_microbatch=False)           # nothing cached yet
+    y0 = layer(x, SPLITS, is_first_microbatch=True)
+    q0 = layer._cache.fwd[0]
+    with torch.no_grad():
+        layer.weight.data.mul_(0.5)                            # not seen by the version counter
+    y1 = layer(x, SPLITS, is_first_microbatch=False)          # cached quantization reused
+    assert layer._cache.fwd[0] is q0 and torch.equal(y0, y1)
+    y2 = layer(x, SPLITS, is_first_microbatch=True)           # quantized again
+    torch.cuda.synchronize()
+    assert layer._cache.fwd[0] is not q0
+    ry = _oracle("a4w4", _bits(x), _bits(layer.weight), bf16_normal((M, N), 1.0, seed=1), SPLITS)[0]
+    assert_gemm_close(host_bf16_f64(y2), ry, what="forward after is_first_microbatch=True")
