@@ -20,6 +20,16 @@ TFLOPS. Every kernel is also timed alone with HIP events on the stream it is
 launched on; the dominant kernel's roofline is reported against MI355X's
 published peaks (MXFP4 dense MFMA 10.1 PFLOP/s, HBM3E 8 TB/s).
 
+workloads: on the default run, the a8w4 forward (128 experts, 65536 routed
+rows, K=7168, N=2048, MXFP8 x MXFP4) and the blockwise FP8 forward + weight
+gradient (64 experts, 32768 rows, K=7168, N=4096) are timed the same way after
+the headline and reported under this key, each with its own metric (TFLOPS,
+% of the FP8 MFMA peak) and per-kernel times (--no-extra skips them).
+
+Inputs are drawn on the device from one seeded generator per tensor, with
+synth's per-tensor seeds (A 1, W 2, dY 3, main_grad 4) and the routing splits
+of synth (seed 0).
+
 cpu_baseline: the CPU oracle (NumPy fp64) timed on a bounded sample of the
 same step -- one expert with 8192 tokens at the full K and N, all three
 passes including quantization -- on this host's cores.
@@ -32,8 +42,8 @@ kernels.<gemm>.rocprof_mfma_busy_pct (fc1): MFMA-busy of that GEMM from the
 committed summary profiles/gemm_fc1_mfma_busy.txt (SQ_VALU_MFMA_BUSY_CYCLES
 over GRBM_GUI_ACTIVE x SIMDs), null likewise.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--workload fc1|a8w4|blockwise]
-                       [--separate-quant]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+                       [--workload fc1|a8w4|a8w4_bwd|blockwise|blockwise_dgrad] [--separate-quant]
        python bench.py --copy-only            (calibration copy for --pmc runs)
        python bench.py --summarize KERNEL STATS_CSV FETCH_CSV WRITE_CSV
                        COPY_FETCH_CSV COPY_WRITE_CSV   (writes the summary text)
@@ -67,6 +77,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="fc1: skip the a8w4 and blockwise workloads timed beside the headline")
     ap.add_argument("--passes", default="all", help="profiling aid: fwd, dgrad, wgrad or all")
     ap.add_argument("--workload", default="fc1", choices=["fc1", "a8w4", "a8w4_bwd", "blockwise", "blockwise_dgrad"],
                     help="fc1: the a4w4 training step (default, the headline); a8w4: the MXFP8 x MXFP4 forward; "
@@ -350,22 +362,30 @@ def build_workload(name, dev, separate_quant=False):
     import torch
 
     import moe_grouped_block_mx_amd as mxg
-    from synth import WORKLOADS, splits_for
+    from synth import SEED_A, SEED_DY, SEED_MAIN_GRAD, SEED_W, WORKLOADS, splits_for
 
-    gen = torch.Generator(device=dev).manual_seed(1234)
     u8 = dict(dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
 
-    def normal(shape, std=1.0):
-        x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    def gen_for(seed):
+        # one seeded generator per tensor, with the per-tensor seeds of synth
+        # (drawn on the device: the host PCG64 streams of the tests would take
+        # minutes at these sizes)
+        return torch.Generator(device=dev).manual_seed(seed)
+
+    def normal(shape, std=1.0, seed=SEED_A):
+        x = torch.randn(shape, generator=gen_for(seed), device=dev, dtype=torch.float32)
         return (x * std).to(torch.bfloat16) if std != 1.0 else x.to(torch.bfloat16)
+
+    def fp32_normal(shape, seed=SEED_MAIN_GRAD):
+        return torch.randn(shape, generator=gen_for(seed), device=dev, dtype=torch.float32)
 
     if name == "fc1":
         wl = WORKLOADS["fc1"]
         G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
         sp = splits_for("fc1")
-        a, w, dy = normal((M, K)), normal((G * N, K), wl["w_std"]), normal((M, N))
-        main_grad = torch.randn((G, N, K), generator=gen, device=dev, dtype=torch.float32)
+        a, w = normal((M, K), seed=SEED_A), normal((G * N, K), wl["w_std"], seed=SEED_W)
+        dy, main_grad = normal((M, N), seed=SEED_DY), fp32_normal((G, N, K))
         mpad = mxg.segpad_rows(sp, "mxfp4")
         # MX scales are block-major: [blocks of 32 along the contraction, rows
         # rounded up to a multiple of 4]
@@ -430,7 +450,7 @@ def build_workload(name, dev, separate_quant=False):
         wl = WORKLOADS["a8w4"]
         G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
         sp = splits_for("a8w4")
-        a, w = normal((M, K)), normal((G * N, K), wl["w_std"])
+        a, w = normal((M, K), seed=SEED_A), normal((G * N, K), wl["w_std"], seed=SEED_W)
         aq, as_ = torch.empty((M, K), **u8), torch.empty((K // 32, mxg.mx_scale_stride(M)), **u8)
         wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty((K // 32, G * N), **u8)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -456,9 +476,8 @@ def build_workload(name, dev, separate_quant=False):
         G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
         sp = splits_for("a8w4")
         mpad = mxg.segpad_rows(sp, "mxfp8")
-        a, w, dy = normal((M, K)), normal((G * N, K), wl["w_std"]), normal((M, N))
-        main_grad = torch.randn((G, N, K), generator=torch.Generator(device=dev).manual_seed(4), device=dev,
-                                dtype=torch.float32)
+        a, w = normal((M, K), seed=SEED_A), normal((G * N, K), wl["w_std"], seed=SEED_W)
+        dy, main_grad = normal((M, N), seed=SEED_DY), fp32_normal((G, N, K))
         R4 = mxg.mx_scale_stride(M)
         dq, ds = torch.empty((M, N), **u8), torch.empty((N // 32, R4), **u8)
         dcq, dcs = torch.empty((N, mpad), **u8), torch.empty((mpad // 32, N), **u8)
@@ -494,7 +513,7 @@ def build_workload(name, dev, separate_quant=False):
         wl = WORKLOADS["blockwise"]
         G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
         sp = splits_for("blockwise")
-        w, dy = normal((G * N, K), wl["w_std"]), normal((M, N))
+        w, dy = normal((G * N, K), wl["w_std"], seed=SEED_W), normal((M, N), seed=SEED_DY)
         wq, ws = mxg.quantize_rowwise(w, "fp8_128x128_p2")
         del w
         dq, ds = torch.empty((M, N), **u8), torch.empty((M, N // 128), **f32)
@@ -521,7 +540,8 @@ def build_workload(name, dev, separate_quant=False):
         wl = WORKLOADS["blockwise"]
         G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
         sp = splits_for("blockwise")
-        a, w, dy = normal((M, K)), normal((G * N, K), wl["w_std"]), normal((M, N))
+        a, w = normal((M, K), seed=SEED_A), normal((G * N, K), wl["w_std"], seed=SEED_W)
+        dy = normal((M, N), seed=SEED_DY)
         mpad = mxg.segpad_rows(sp, "fp8_1x128")
         aq, as_ = torch.empty((M, K), **u8), torch.empty((M, K // 128), **f32)
         wq, ws = torch.empty((G * N, K), **u8), torch.empty((G * N // 128, K // 128), **f32)
@@ -533,20 +553,21 @@ def build_workload(name, dev, separate_quant=False):
             # power-of-two scales (the blockwise default), declared by the _p2
             # formats so the forward and the weight gradient apply them inside
             # the MFMA
-            ("quant_A_1x128", "quant", lambda: mxg.quantize_rowwise(a, "fp8_1x128_p2", q=aq, scales=as_)),
+            # X both ways from one read (the blockwise dual quantizer)
+            ("quant_X_dual", "quant", lambda: mxg.quantize_dual(a, sp, "fp8_1x128_p2", q_row=aq, s_row=as_, q_col=xcq,
+                                                                s_col=xcs)),
             ("quant_W_128x128", "quant", lambda: mxg.quantize_rowwise(w, "fp8_128x128_p2", q=wq, scales=ws)),
             ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt="fp8_1x128_p2",
                                                     w_fmt="fp8_128x128_p2", out=y)),
             ("quant_dY_col", "quant", lambda: mxg.quantize_colwise_segpad(dy, sp, "fp8_1x128_p2", q=dcq, scales=dcs)),
-            ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "fp8_1x128_p2", q=xcq, scales=xcs)),
             ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, dw, accumulate=False,
                                                         fmt="fp8_1x128_p2")),
         ]
         nz = int((sp > 0).sum())
         q8 = 1 + 4 / 128
-        bytes_alg = {"quant_A_1x128": M * K * (2 + q8), "quant_W_128x128": G * N * K * (2 + 1),
+        bytes_alg = {"quant_X_dual": M * K * (2 + q8) + mpad * K * q8, "quant_W_128x128": G * N * K * (2 + 1),
                      "fwd": M * K * q8 + nz * N * K * 1 + M * N * 2,
-                     "quant_dY_col": M * N * 2 + mpad * N * q8, "quant_X_col": M * K * 2 + mpad * K * q8,
+                     "quant_dY_col": M * N * 2 + mpad * N * q8,
                      "wgrad": mpad * (N + K) * q8 + G * N * K * 2}
         config = {"workload": "MoE blockwise FP8 forward + weight gradient (1x128 / 128x128 fp32 scales, "
                               "power-of-two; bf16 weight gradient, overwrite)",
@@ -556,6 +577,76 @@ def build_workload(name, dev, separate_quant=False):
                     config=config, peak_tflops=PEAK_FP8_TFLOPS, dtype="fp8_e4m3", hbm_gemms={"wgrad"},
                     metric="grouped blockwise FP8 GEMM TFLOPS (fwd/wgrad) and % of FP8 MFMA peak, 1 MI355X")
     raise SystemExit(f"unknown workload {name!r}")
+
+
+def measure(W, args, dev):
+    """Warm-up, then `steps` timed steps of the workload's ops between device
+    synchronizations, then `steps` more with HIP events around every launch on
+    the stream it is launched on. Returns (seconds per step, per-kernel dict,
+    roofline dict of the kernel with the largest time)."""
+    import torch
+
+    ops, bytes_alg, flops = W["ops"], W["bytes_alg"], W["flops"]
+    stream = torch.cuda.current_stream(dev)
+    ev = {name: [] for name, _, _ in ops}
+
+    def step(record):
+        for name, _, fn in ops:
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ev[name].append((e0, e1))
+            else:
+                fn()
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+
+    per = {}
+    for name, kind, _ in ops:
+        ms = [e0.elapsed_time(e1) for e0, e1 in ev[name]]
+        d = float(np.mean(ms)) * 1e-3
+        entry = {"ms": round(d * 1e3, 4), "ms_median": round(float(np.median(ms)), 4),
+                 "ms_min": round(float(np.min(ms)), 4)}
+        entry["GBs_alg"] = round(bytes_alg[name] / d / 1e9, 1)
+        entry["frac_hbm"] = round(bytes_alg[name] / d / 1e9 / PEAK_HBM_GBS, 4)
+        if kind == "gemm":
+            entry["TFLOPS"] = round(flops[name] / d / 1e12, 1)
+            entry["pct_mfma_peak"] = round(100 * flops[name] / d / 1e12 / W["peak_tflops"], 2)
+        per[name] = entry
+
+    dom = max(per, key=lambda k: per[k]["ms"])
+    dkind = dict((n, k) for n, k, _ in ops)[dom]
+    d = per[dom]["ms"] * 1e-3
+    if dkind == "gemm" and dom not in W["hbm_gemms"]:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(flops[dom] / d / 1e12, 1),
+                "peak": W["peak_tflops"], "unit": "TFLOP/s"}
+        per_unit = flops[dom]
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(bytes_alg[dom] / d / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        per_unit = bytes_alg[dom]
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["per_launch_algorithmic"] = per_unit
+    return t_step, per, roof
+
+
+# workloads timed beside the headline one on the default run (their own
+# metrics, on the same JSON line)
+EXTRA_WORKLOADS = ("a8w4", "blockwise")
 
 
 def main():
@@ -580,75 +671,22 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     W = build_workload(args.workload, dev, args.separate_quant)
-    ops, bytes_alg, flops = W["ops"], W["bytes_alg"], W["flops"]
     if args.passes != "all":
         keep = {"fwd": {"quant_A_row", "quant_W_row", "quant_X_dual", "quant_W_dual", "fwd"},
                 "dgrad": {"quant_dY_row", "quant_W_col", "quant_dY_dual", "quant_W_dual", "dgrad"},
                 "wgrad": {"quant_dY_col", "quant_X_col", "quant_X_dual", "quant_dY_dual", "wgrad"}}[args.passes]
-        ops = [o for o in ops if o[0] in keep]
-
-    stream = torch.cuda.current_stream(dev)
-    ev = {name: [] for name, _, _ in ops}
-
-    def step(record):
-        for name, _, fn in ops:
-            if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                ev[name].append((e0, e1))
-            else:
-                fn()
-
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(False)
-    torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / args.steps
-
-    # per-kernel durations (separate timed steps, HIP events around each
-    # launch on the stream the library launches on)
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    per = {}
-    for name, kind, _ in ops:
-        ms = [e0.elapsed_time(e1) for e0, e1 in ev[name]]
-        d = float(np.mean(ms)) * 1e-3
-        entry = {"ms": round(d * 1e3, 4), "ms_median": round(float(np.median(ms)), 4),
-                 "ms_min": round(float(np.min(ms)), 4)}
-        entry["GBs_alg"] = round(bytes_alg[name] / d / 1e9, 1)
-        entry["frac_hbm"] = round(bytes_alg[name] / d / 1e9 / PEAK_HBM_GBS, 4)
-        if kind == "gemm":
-            entry["TFLOPS"] = round(flops[name] / d / 1e12, 1)
-            entry["pct_mfma_peak"] = round(100 * flops[name] / d / 1e12 / W["peak_tflops"], 2)
-            if args.workload == "fc1" and args.passes == "all" and not args.separate_quant:
-                entry["rocprof_mfma_busy_pct"] = read_mfma_busy(name)
-        per[name] = entry
-
-    step_flops = sum(flops[n] for n, k, _ in ops if k == "gemm")
+        W["ops"] = [o for o in W["ops"] if o[0] in keep]
+    flops = W["flops"]
+    t_step, per, roof = measure(W, args, dev)
+    if args.workload == "fc1" and args.passes == "all" and not args.separate_quant:
+        for name in per:
+            if "TFLOPS" in per[name]:
+                per[name]["rocprof_mfma_busy_pct"] = read_mfma_busy(name)
+    step_flops = sum(flops[n] for n, k, _ in W["ops"] if k == "gemm")
     value = step_flops / t_step / 1e12
-    dom = max(per, key=lambda k: per[k]["ms"])
-    dkind = dict((n, k) for n, k, _ in ops)[dom]
-    d = per[dom]["ms"] * 1e-3
-    if dkind == "gemm" and dom not in W["hbm_gemms"]:
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(flops[dom] / d / 1e12, 1),
-                "peak": W["peak_tflops"], "unit": "TFLOP/s"}
-        per_unit = flops[dom]
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(bytes_alg[dom] / d / 1e9, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-        per_unit = bytes_alg[dom]
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    tr = read_traffic(dom) if (args.passes == "all" and args.workload == "fc1") else None
+    tr = read_traffic(roof["kernel"]) if (args.passes == "all" and args.workload == "fc1") else None
     roof["traffic"] = None if tr is None else round(tr[0] + tr[1])
+    per_unit = roof.pop("per_launch_algorithmic")
     roof["per_launch_algorithmic"] = per_unit
 
     config = dict(W["config"])
@@ -671,6 +709,23 @@ def main():
         "kernels": per,
         "pct_mfma_peak_step": round(100 * value / W["peak_tflops"], 2),
     }
+    if args.workload == "fc1" and args.passes == "all" and not args.separate_quant and not args.no_extra:
+        # the a8w4 forward and the blockwise FP8 forward + weight gradient at
+        # their own workload sizes, against the FP8 MFMA peak
+        del W
+        torch.cuda.empty_cache()
+        extra = {}
+        for name in EXTRA_WORKLOADS:
+            X = build_workload(name, dev)
+            t_x, per_x, roof_x = measure(X, args, dev)
+            fl = sum(X["flops"][n] for n, k, _ in X["ops"] if k == "gemm")
+            extra[name] = {"metric": X["metric"], "value": round(fl / t_x / 1e12, 2), "unit": "TFLOPS",
+                           "ms_per_step": round(t_x * 1e3, 4), "dtype": X["dtype"], "config": X["config"],
+                           "pct_mfma_peak_step": round(100 * fl / t_x / 1e12 / X["peak_tflops"], 2),
+                           "roofline": roof_x, "kernels": per_x}
+            del X
+            torch.cuda.empty_cache()
+        out["workloads"] = extra
     if not args.no_cpu_baseline and args.workload == "fc1":
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -223,17 +223,20 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
 
 /*
  * Dual-output quantization: the row-wise and the column-wise segment-padded
- * MX quantizations of one bf16 tensor from a single read of it (the "Changes"
- * list of "Add ROCm Triton blockwise FP8 grouped GEMM" describes one kernel
- * emitting both training operands in one pass; here for the MX formats).
- * Bit-identical to mxgg_quantize_rowwise followed by
- * mxgg_quantize_colwise_segpad on the same arguments.
+ * quantizations of one bf16 tensor from a single read of it (the "Changes"
+ * list of "Add ROCm Triton blockwise FP8 grouped GEMM" describes one grouped
+ * kernel emitting both training operands in one pass). Bit-identical to
+ * mxgg_quantize_rowwise followed by mxgg_quantize_colwise_segpad on the same
+ * arguments.
  *   x, rows, cols, ldx, m_splits, G, mpad  as for mxgg_quantize_colwise_segpad.
- *   fmt     MXGG_MXFP4 or MXGG_MXFP8 (blockwise formats: MXGG_ERR_FORMAT).
- *   flags   ignored (MX formats take none).
+ *   fmt     MXGG_MXFP4, MXGG_MXFP8, or MXGG_FP8_1x128 / MXGG_FP8_1x128_P2
+ *           (1x128 blocks along cols row-wise, along each expert's padded
+ *           segment column-wise; cols % 128 == 0).
+ *   flags   MXGG_POW2_SCALES for MXGG_FP8_1x128 (implied by the _P2 format);
+ *           ignored for MX formats.
  *   q_row, s_row  the row-wise outputs, as mxgg_quantize_rowwise.
  *   q_col, s_col  the column-wise outputs, as mxgg_quantize_colwise_segpad.
- * Weights for dgrad: W as [G*N, K] with m_splits = {N, ..., N} gives the
+ * Weights for dgrad (MX): W as [G*N, K] with m_splits = {N, ..., N} gives the
  * forward's W_q/W_s and dgrad's wcol_q/wcol_s together.
  * rows == 0 returns MXGG_OK (no launch). Errors: NULL, SHAPE, SPLITS, FORMAT,
  * ALIGN, DEVICE, ARCH, HIP.

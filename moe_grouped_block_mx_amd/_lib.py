@@ -265,8 +265,9 @@ def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=None, q=None, s
 
 
 def mxgg_quantize_dual(x, m_splits, fmt="mxfp4", flags=None, q_row=None, s_row=None, q_col=None, s_col=None):
-    """x: bf16 [rows, cols]. Row-wise and column-wise segment-padded MX
-    quantization from one read. Returns (q_row, s_row, q_col, s_col, mpad)."""
+    """x: bf16 [rows, cols]. Row-wise and column-wise segment-padded
+    quantization (MX, or blockwise 1x128) from one read.
+    Returns (q_row, s_row, q_col, s_col, mpad)."""
     torch = _torch()
     f = _fmt(fmt)
     flags = _flags(flags, f)
@@ -285,11 +286,10 @@ def mxgg_quantize_dual(x, m_splits, fmt="mxfp4", flags=None, q_row=None, s_row=N
         q_col = torch.empty(_q_shape(f, cols, mpad), **u8)
     if s_col is None:
         s_col = torch.empty(_col_scale_shape(f, cols, mpad), dtype=_sdtype(f), device=x.device)
-    if _is_mx(f):
-        _expect(q_row, "q_row", _q_shape(f, rows, cols), torch.uint8)
-        _expect(s_row, "s_row", _row_scale_shape(f, rows, cols), torch.uint8)
-        _expect(q_col, "q_col", _q_shape(f, cols, mpad), torch.uint8)
-        _expect(s_col, "s_col", _col_scale_shape(f, cols, mpad), torch.uint8)
+    _expect(q_row, "q_row", _q_shape(f, rows, cols), torch.uint8)
+    _expect(s_row, "s_row", _row_scale_shape(f, rows, cols), _sdtype(f))
+    _expect(q_col, "q_col", _q_shape(f, cols, mpad), torch.uint8)
+    _expect(s_col, "s_col", _col_scale_shape(f, cols, mpad), _sdtype(f))
     _check(lib.mxgg_quantize_dual(_ptr(x), rows, cols, _ld(x), arr, G, f, flags, _ptr(q_row), _ptr(s_row),
                                   _ptr(q_col), _ptr(s_col), mpad, _stream(x)))
     return q_row, s_row, q_col, s_col, mpad

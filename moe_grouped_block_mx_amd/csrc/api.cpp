@@ -217,7 +217,8 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
 mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, const int64_t* m_splits,
                                int32_t G, mxgg_format fmt, uint32_t flags, void* q_row, void* s_row, void* q_col,
                                void* s_col, int64_t mpad, hipStream_t stream) {
-  (void)flags;
+  if (is_p2(fmt)) flags |= MXGG_POW2_SCALES;
+  fmt = (mxgg_format)base_format(fmt);
   Check c = validate_quantize_dual(x, rows, cols, ldx, m_splits, G, (int)fmt, q_row, s_row, q_col, s_col, mpad);
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
@@ -225,11 +226,18 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
   c = device_checks(stream, {{x, "x"}, {q_row, "q_row"}, {s_row, "s_row"}, {q_col, "q_col"}, {s_col, "s_col"}}, &cus);
   if (!c.ok()) return finish(c);
   const SplitArgs sp = make_splits(m_splits, G);
-  c = hip_status(launch_quant_dual_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8,
-                                      static_cast<uint8_t*>(q_row), static_cast<uint8_t*>(s_row),
-                                      static_cast<uint8_t*>(q_col), static_cast<uint8_t*>(s_col), mpad, cus,
-                                      stream),
-                 "dual quantizer launch");
+  if (is_mx(fmt))
+    c = hip_status(launch_quant_dual_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8,
+                                        static_cast<uint8_t*>(q_row), static_cast<uint8_t*>(s_row),
+                                        static_cast<uint8_t*>(q_col), static_cast<uint8_t*>(s_col), mpad, cus,
+                                        stream),
+                   "dual quantizer launch");
+  else
+    c = hip_status(launch_quant_dual_blk(static_cast<const uint16_t*>(x), cols, ldx, sp,
+                                         (flags & MXGG_POW2_SCALES) != 0, static_cast<uint8_t*>(q_row),
+                                         static_cast<float*>(s_row), static_cast<uint8_t*>(q_col),
+                                         static_cast<float*>(s_col), mpad, stream),
+                   "blockwise dual quantizer launch");
   return c.ok() ? ok() : finish(c);
 }
 

@@ -102,6 +102,10 @@ hipError_t launch_grouped_wgrad_mx(const WgradParams& p, bool fp8, int num_cus, 
 // Scale row strides (ldas, ldbs) are in bytes.
 hipError_t launch_quant_rowwise_blk(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool blk128x128,
                                     bool pow2, uint8_t* q, float* s, hipStream_t st);
+// both of the above (1x128 row-wise and column-wise segment-padded) from one
+// read; cols a multiple of 128
+hipError_t launch_quant_dual_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
+                                 uint8_t* qr, float* sr, uint8_t* qc, float* sc, int64_t mpad, hipStream_t st);
 hipError_t launch_quant_colwise_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
                                     uint8_t* q, float* s, int64_t mpad, hipStream_t st);
 // 128x128-block weights [G*N, K] (+ f32 [G*N/128, K/128]) -> [G*K, N] (+ f32

@@ -279,8 +279,130 @@ __global__ __launch_bounds__(256) void quant_colwise_1x128_kernel(const uint16_t
 }
 
 // ---------------------------------------------------------------------------
+// Dual output: the 1x128 row-wise and the 1x128 column-wise segment-padded
+// quantizations of one bf16 tensor from a single read of it (the page's
+// unified grouped kernel that emits both the row-wise activation operand and
+// the segment-padded column-wise wgrad operand in one pass). A workgroup takes
+// one 128-row block of the padded row space (inside one expert segment, zeros
+// past its end) by 128 columns:
+//   rows  thread t loads chunk t%16 (8 elements) of rows t/16 + 16 i, so the
+//         16 lanes of a row hold its whole 128-element block: amax by four
+//         xor-shuffles, encode from registers, one 8-byte store per lane;
+//   tile  the bf16 values go to LDS;
+//   cols  four threads per column (32 rows each) combine their amax through
+//         LDS and write 32 codes each (two 16-byte stores).
+// Identical output to the two single-output kernels (same scale rule and
+// encoder on the same values).
+// ---------------------------------------------------------------------------
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_dual_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                               int64_t cols, const SplitArgs sp, int64_t mpad,
+                                                               uint8_t* __restrict__ qr, float* __restrict__ sr,
+                                                               uint8_t* __restrict__ qc, float* __restrict__ sc) {
+  constexpr int PITCH = 128 + 8;  // bf16 per LDS row: 16-byte aligned rows
+  __shared__ int64_t pref[kMaxExperts + 1];  // low: padded offsets, high: row offsets
+  __shared__ int64_t wtot[4];
+  __shared__ int32_t pad_offs[kMaxExperts + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * PITCH];
+  __shared__ uint32_t qmax[4][128];
+  __shared__ int64_t blk_row0;
+  __shared__ int32_t blk_valid;
+
+  const int G = sp.G;
+  block_prefix64<256>(G, [&](int g) {
+    const int64_t m = sp.m[g];
+    return (m << 32) | ((m + 127) & ~127ll);
+  }, pref, wtot);
+  for (int g = threadIdx.x; g <= G; g += 256) pad_offs[g] = (int32_t)(pref[g] & 0xffffffffll);
+  __syncthreads();
+
+  const int64_t p0 = (int64_t)blockIdx.x * 128;  // first padded row (< mpad by the grid)
+  if (threadIdx.x == 0) {
+    const int g = upper_bound_i32(pad_offs, G + 1, (int32_t)p0) - 1;
+    const int64_t local = p0 - pad_offs[g];
+    const int64_t nv = (int64_t)sp.m[g] - local;
+    blk_row0 = (pref[g] >> 32) + local;
+    blk_valid = nv > 128 ? 128 : (int)nv;
+  }
+  __syncthreads();
+  const int nvalid = blk_valid;
+  const int64_t row0 = blk_row0;
+  const int64_t c0 = (int64_t)blockIdx.y * 128;  // cols is a multiple of 128
+  const int ch = threadIdx.x & 15, rg = threadIdx.x >> 4;
+
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = rg + 16 * i;
+    v[i] = row < nvalid ? *reinterpret_cast<const uint4*>(x + (row0 + row) * ldx + c0 + ch * 8)
+                        : make_uint4(0, 0, 0, 0);
+  }
+  const int64_t srow = cols / 128;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = rg + 16 * i;
+    const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t amax = amax8(wd);
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, m, 64));
+    *reinterpret_cast<uint4*>(tile + row * PITCH + ch * 8) = v[i];
+    if (row >= nvalid) continue;
+    const BlkScale bs = blk_scale<POW2>(amax);
+    const int64_t r = row0 + row;
+    *reinterpret_cast<uint2*>(qr + r * cols + c0 + ch * 8) = encode8<POW2>(wd, bs);
+    if (ch == 0) sr[r * srow + c0 / 128] = bs.stored;
+  }
+  __syncthreads();
+
+  // column-wise: item (column c, quarter b), two per thread; the quarters'
+  // amax meet in LDS, then each item re-reads its 32 values and encodes them
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int item = threadIdx.x + 256 * j, c = item & 127, b = item >> 7;
+    uint32_t amax = 0;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) amax = max(amax, (uint32_t)tile[(b * 32 + r) * PITCH + c] & 0x7fffu);
+    qmax[b][c] = amax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int item = threadIdx.x + 256 * j, c = item & 127, b = item >> 7;
+    const uint32_t amax = max(max(qmax[0][c], qmax[1][c]), max(qmax[2][c], qmax[3][c]));
+    const BlkScale bs = blk_scale<POW2>(amax);
+    uint32_t o[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t vv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) vv[k] = tile[(b * 32 + 8 * d + k) * PITCH + c];
+      const uint32_t wd[4] = {vv[0] | (vv[1] << 16), vv[2] | (vv[3] << 16), vv[4] | (vv[5] << 16),
+                              vv[6] | (vv[7] << 16)};
+      const uint2 e = encode8<POW2>(wd, bs);
+      o[2 * d] = e.x;
+      o[2 * d + 1] = e.y;
+    }
+    uint8_t* qp = qc + (c0 + c) * mpad + p0 + b * 32;
+    reinterpret_cast<uint4*>(qp)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<uint4*>(qp)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    if (b == 0) sc[(c0 + c) * (mpad / 128) + p0 / 128] = bs.stored;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_quant_dual_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
+                                 uint8_t* qr, float* sr, uint8_t* qc, float* sc, int64_t mpad, hipStream_t st) {
+  const dim3 grid((unsigned)(mpad / 128), (unsigned)(cols / 128));
+  if (pow2)
+    hipLaunchKernelGGL(quant_dual_1x128_kernel<true>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, qr, sr, qc, sc);
+  else
+    hipLaunchKernelGGL(quant_dual_1x128_kernel<false>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, qr, sr, qc,
+                       sc);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_rowwise_blk(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool blk128x128,
                                     bool pow2, uint8_t* q, float* s, hipStream_t st) {
   if (blk128x128) {

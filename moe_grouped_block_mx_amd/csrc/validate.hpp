@@ -171,7 +171,8 @@ inline Check validate_quantize_dual(const void* x, int64_t rows, int64_t cols, i
                                     const void* s_col, int64_t mpad) {
   MXGG_TRY(check_layout(fmt, "quantize_dual"));
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
-  if (!is_mx((mxgg_format)fmt)) return fail(MXGG_ERR_FORMAT, "the dual quantizer takes MX formats only");
+  if (!is_mx((mxgg_format)fmt) && fmt != MXGG_FP8_1x128)
+    return fail(MXGG_ERR_FORMAT, "the dual quantizer takes MX formats and MXGG_FP8_1x128 (got %lld)", fmt);
   MXGG_TRY(validate_quantize_rowwise(x, rows, cols, ldx, fmt, q_row, s_row));
   MXGG_TRY(validate_quantize_colwise(x, rows, cols, ldx, m, G, fmt, q_col, s_col, mpad));
   return Check{};

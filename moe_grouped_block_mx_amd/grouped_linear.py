@@ -85,11 +85,7 @@ class _WeightCache:
 def _quantize_act(x, m_splits, fmt, need_col):
     """Row-wise (forward or input gradient) and, when needed, column-wise
     segment-padded (weight gradient) quantization of an activation or a
-    gradient."""
-    if fmt.startswith("fp8"):
-        row = L.mxgg_quantize_rowwise(x, fmt)
-        col = L.mxgg_quantize_colwise_segpad(x, m_splits, fmt) if need_col else None
-        return row, col
+    gradient; both from one read when both are needed (MX and blockwise)."""
     if need_col:
         qr, sr, qc, sc, mpad = L.mxgg_quantize_dual(x, m_splits, fmt)
         return (qr, sr), (qc, sc, mpad)

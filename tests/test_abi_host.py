@@ -47,7 +47,11 @@ def test_dual_quantizer_validation():
 
     def dual(fmt=0, mp=mpad, rows=64, cols=64, ldx=64, qr=P, qc=P, G=3):
         return L.mxgg_quantize_dual(P, rows, cols, ldx, m, G, fmt, 0, qr, P, qc, P, mp, NULL)
-    assert dual(fmt=2) == 4 and "MX formats" in last()      # blockwise: not a dual format
+    assert dual(fmt=3) == 4 and "MX formats" in last()      # 128x128 blocks: no column-wise form
+    assert dual(fmt=5) == 4                                  # ... nor with power-of-two scales
+    assert dual(fmt=2) == 2 and "128" in last()              # 1x128: cols must be a multiple of 128
+    assert dual(fmt=2, cols=128, ldx=128) == 2 and "mpad" in last()   # 1x128 pads segments to 128
+    assert L.mxgg_quantize_dual(P, 64, 128, 128, m, 3, 4, 0, P, P, P, P, 256, NULL) != 4   # _P2 accepted
     assert dual(fmt=9) == 4
     assert dual(mp=64) == 2 and "mpad" in last()            # wrong padded row count
     assert dual(rows=63) == 3                               # splits do not sum to rows

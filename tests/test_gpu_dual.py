@@ -1,9 +1,10 @@
-"""GPU parity of the dual-output MX quantizer (row-wise and column-wise
-segment-padded outputs from one read) through the C ABI: bit-exact against the
-oracle's two quantizations and against the library's separate row-wise and
-column-wise kernels, on ragged and unaligned expert segments, column tails,
-strided inputs, empty experts, the largest expert count, and the full-size
-fc1 activations and weights (equality with the separate kernels everywhere,
+"""GPU parity of the dual-output quantizers (row-wise and column-wise
+segment-padded outputs from one read) through the C ABI, MX and blockwise
+1x128: bit-exact against the oracle's two quantizations and against the
+library's separate row-wise and column-wise kernels, on ragged and unaligned
+expert segments, column tails, strided inputs, empty experts, the largest
+expert count, special blocks, and the full-size fc1 and blockwise-workload
+activations and fc1 weights (equality with the separate kernels everywhere,
 the oracle on sampled rows and columns)."""
 import numpy as np
 import pytest
@@ -123,3 +124,74 @@ def test_dual_full_size_fc1_weights_equal_separate():
     assert got[4] == ref[4] == G * N
     for a, b in zip(got[:4], ref[:4]):
         assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# blockwise FP8 dual (1x128 row-wise + 1x128 column-wise segment-padded to 128)
+# ---------------------------------------------------------------------------
+from oracle import blockwise as ob  # noqa: E402
+
+BLK_CASES = [
+    ([64, 0, 96, 96], 256),             # segments shorter than a 128-row block
+    ([300, 0, 5], 128),                 # one column tile; a block straddled by nothing
+    ([513, 255, 1, 0, 40], 384),        # unaligned segment starts, three column tiles
+    ([0, 0, 7], 128),                   # leading empty experts
+    ([129, 127, 128], 256),             # a segment one row past / one short of a block
+]
+
+
+def _check_blk(bits, splits, fmt, what, x=None):
+    x = dev_bf16(bits) if x is None else x
+    pow2 = fmt.endswith("_p2")
+    qr, sr, qc, sc, mpad = mxg.quantize_dual(x, splits, fmt, flags=1 if pow2 else 0)
+    q2, s2 = mxg.quantize_rowwise(x, fmt, flags=1 if pow2 else 0)
+    qc2, sc2, mpad2 = mxg.quantize_colwise_segpad(x, splits, fmt, flags=1 if pow2 else 0)
+    torch.cuda.synchronize()
+    assert mpad == mpad2
+    for name, a, b in (("q_row", qr, q2), ("s_row", sr, s2), ("q_col", qc, qc2), ("s_col", sc, sc2)):
+        assert torch.equal(a, b), f"{what}: {name} differs from the separate kernel"
+    rq, rs = ob.quantize_1x128(bits, pow2=pow2)
+    assert np.array_equal(host(qr), rq) and np.array_equal(host(sr), rs), f"{what}: row-wise vs oracle"
+    cq, cs = ob.quantize_colwise_segpad_128(bits, splits, pow2=pow2)
+    assert np.array_equal(host(qc), cq) and np.array_equal(host(sc), cs), f"{what}: column-wise vs oracle"
+
+
+@pytest.mark.parametrize("fmt", ["fp8_1x128_p2", "fp8_1x128"])
+@pytest.mark.parametrize("case", BLK_CASES, ids=[f"{len(c[0])}x{c[1]}" for c in BLK_CASES])
+def test_blockwise_dual_matches_oracle_and_separate_kernels(fmt, case):
+    splits, cols = case
+    bits = bf16_normal((int(np.sum(splits)), cols), 1.0, seed=13)
+    _check_blk(bits, splits, fmt, f"{fmt} {case}")
+
+
+def test_blockwise_dual_special_and_strided():
+    bits = bf16_normal((200, 256), 1.0, seed=4)
+    bits[7, :] = 0                       # an all-zero row block: the amax floor
+    bits[:, 130:140] = 0x0080            # tiny values
+    bits[150, 3] = 0x7F00                # a huge outlier
+    _check_blk(bits, [90, 0, 110], "fp8_1x128_p2", "special")
+    _check_blk(bits, [90, 0, 110], "fp8_1x128", "special fp32 scales")
+    wide = bf16_normal((160, 512), 1.0, seed=6)
+    x = dev_bf16(wide)[:, 128:384]
+    _check_blk(np.ascontiguousarray(wide[:, 128:384]), [100, 60], "fp8_1x128_p2", "strided", x=x)
+
+
+def test_blockwise_dual_full_size_sampled():
+    """X at the blockwise workload's size (32768 x 7168, uniform-random
+    routing over 64 experts): equal to the separate kernels everywhere; the
+    oracle on 256 sampled rows and 16 sampled columns."""
+    sp = splits_for("blockwise")
+    bits = bf16_normal((32768, 7168), 1.0, seed=1)
+    x = dev_bf16(bits)
+    qr, sr, qc, sc, mpad = mxg.quantize_dual(x, sp, "fp8_1x128_p2")
+    q2, s2 = mxg.quantize_rowwise(x, "fp8_1x128_p2")
+    qc2, sc2, _ = mxg.quantize_colwise_segpad(x, sp, "fp8_1x128_p2")
+    torch.cuda.synchronize()
+    assert torch.equal(qr, q2) and torch.equal(sr, s2) and torch.equal(qc, qc2) and torch.equal(sc, sc2)
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(32768, size=256, replace=False))
+    rq, rs = ob.quantize_1x128(bits[rows])
+    assert np.array_equal(host(qr)[rows], rq) and np.array_equal(host(sr)[rows], rs)
+    cols = np.sort(rng.choice(7168, size=16, replace=False))
+    cq, cs = ob.quantize_colwise_segpad_128(np.ascontiguousarray(bits[:, cols]), sp)
+    assert np.array_equal(host(qc)[cols], cq) and np.array_equal(host(sc)[cols], cs)
