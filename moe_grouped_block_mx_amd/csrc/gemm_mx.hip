@@ -155,6 +155,21 @@ struct TileCfg {
                 "read-ahead schedule: two K steps per stage, MX scales, a 4+ stage ring");
 };
 
+// The segment owning item t of a non-decreasing prefix offs[0..n] (offs[0] =
+// 0), from a cursor: a workgroup visits its tiles in increasing order (the
+// issuing side and the computing side each with its own cursor), so the
+// cursor's segment usually still owns t and one LDS read confirms it; else a
+// binary search over the segments after it.
+__device__ __forceinline__ int seek_segment(const int32_t* offs, int n, int t, int& cursor) {
+  int j = cursor;
+  if (j < 0 || offs[j + 1] <= t) {
+    const int lo = j < 0 ? 0 : j + 1;
+    j = lo + upper_bound_i32(offs + lo, n - lo, t) - 1;
+  }
+  cursor = j;
+  return j;
+}
+
 // Operand bases and extents of one tile.
 struct TileOps {
   const uint8_t* a;   // first row of the A tile (row stride lda)
@@ -339,10 +354,12 @@ __device__ __forceinline__ void issue_b_srcs(const uint8_t* const (&src)[C::DB],
 // ---------------------------------------------------------------------------
 template <class C>
 struct FastPlan {
-  uint32_t vA[C::DA], vB[C::DB], vS[C::DSA];  // per lane
+  // per lane: chunk offsets; scale offsets (MX: DSA words of either operand;
+  // fp32 row scales: DSA of A's rows, then DSB of B's)
+  uint32_t vA[C::DA], vB[C::DB], vS[C::DSA], vSB[C::DSB > 0 ? C::DSB : 1];
   // wave-uniform: the tile's operand bases; per scale DMA instruction, the
-  // scale operand it reads (A's or B's) and that operand's bytes per stage
-  const uint8_t *a, *b, *s[C::DSA];
+  // scale operand it reads and that operand's bytes per stage
+  const uint8_t *a, *b, *s[C::DSA], *sb;
   int64_t sstep[C::DSA];
 };
 
@@ -363,12 +380,23 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 template <class C>
 __device__ __forceinline__ void plan_fast(FastPlan<C>& fp, const DmaPlan<C>& pl, const TileOps& t, int64_t ldas,
                                           int64_t ldbs, int w) {
-  static_assert(!C::F32S, "fast issue: MX scales");
   w = __builtin_amdgcn_readfirstlane(w);
   unroll<C::DA>([&](auto ic) { fp.vA[decltype(ic)::value] = pl.offA[decltype(ic)::value]; });
   unroll<C::DB>([&](auto ic) { fp.vB[decltype(ic)::value] = pl.offB[decltype(ic)::value]; });
   fp.a = uniform_ptr(t.a);
   fp.b = uniform_ptr(t.b);
+  if constexpr (C::F32S) {
+    // one fp32 per row and 128-element block: row offsets; the stage adds its
+    // block's 4 bytes
+    unroll<C::DSA>([&](auto ic) {
+      fp.vS[decltype(ic)::value] = pl.offAS[decltype(ic)::value];
+      fp.s[decltype(ic)::value] = uniform_ptr(t.as);
+      fp.sstep[decltype(ic)::value] = 0;
+    });
+    unroll<C::DSB>([&](auto ic) { fp.vSB[decltype(ic)::value] = pl.offBS[decltype(ic)::value]; });
+    fp.sb = uniform_ptr(t.bs);
+    return;
+  }
   unroll<C::DSA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const bool on_b = (i * C::NW + w) * 256 >= C::BM * C::SB;  // wave-uniform
@@ -391,10 +419,22 @@ __device__ __forceinline__ void issue_stage_fast(const FastPlan<C>& fp, int s, u
       constexpr int i = decltype(ic)::value;
       dma16(base + fp.vA[i], st + C::A_OFF + (i * C::NW + w) * 1024);
     });
-    unroll<C::DSA>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      dma4(fp.s[i] + s * fp.sstep[i] + fp.vS[i], st + C::AS_OFF + (i * C::NW + w) * 256);
-    });
+    if constexpr (C::F32S) {
+      const int boff = (s * C::BK / 128) * 4;  // the stage's 128-element block
+      unroll<C::DSA>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        dma4(fp.s[i] + boff + fp.vS[i], st + C::AS_OFF + (i * C::NW + w) * 256);
+      });
+      unroll<C::DSB>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        dma4(fp.sb + boff + fp.vSB[i], st + C::BS_OFF + (i * C::NW + w) * 256);
+      });
+    } else {
+      unroll<C::DSA>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        dma4(fp.s[i] + s * fp.sstep[i] + fp.vS[i], st + C::AS_OFF + (i * C::NW + w) * 256);
+      });
+    }
   }
   if constexpr (DO_B) {
     const uint8_t* base = fp.b + s * C::RBB;
@@ -683,15 +723,17 @@ __device__ __forceinline__ void wait_stage(int stages_after) {
 
 // The pipelined persistent loop shared by all passes.
 //   src.count()       number of tiles
-//   src.ops(t)        TileOps of tile t
-//   src.epilogue(...) stores tile t
+//   src.ops(t, side)  TileOps of tile t; side 0 the issuing side, 1 the
+//                     computing side (each keeps its own segment cursor)
+//   src.epilogue(...) stores tile t (the last tile ops(t, 1) was asked for)
 // Tiles are visited t = first, first + gridDim.x, ...
 // FAST (read-ahead loop only): every tile's contraction is a multiple of BK
 // and the scale offsets fit 32 bits; the DMAs take the fast issue above.
 template <class C, bool FAST = false, class Src>
 __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t lda, int64_t ldas, int64_t ldb,
                                                 int64_t ldbs) {
-  static_assert(!FAST || C::SCHED == 7, "fast issue: read-ahead loop");
+  static_assert(!FAST || C::SCHED == 7 || C::SCHED == 5, "fast issue: read-ahead or 3-stage loop");
+  static_assert(!FAST || !C::BLK, "fast issue: scales applied by the MFMA");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / C::WN, wn = w % C::WN;
@@ -716,12 +758,12 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
   if constexpr (FAST) {
     // dummy stages before any planned tile read the zero page at offset 0
     const uint8_t* z = reinterpret_cast<const uint8_t*>(g_zero_page);
-    fplan.a = fplan.b = z;
+    fplan.a = fplan.b = fplan.sb = z;
     unroll<C::DSA>([&](auto ic) { fplan.s[decltype(ic)::value] = z; });
   }
   auto load_issue_tile = [&]() {
     while (it < total) {
-      iops = src.ops(it);
+      iops = src.ops(it, 0);
       ins = (iops.kc + C::BK - 1) / C::BK;
       if (ins > 0) break;
       it += stride;  // tiles with an empty contraction issue nothing
@@ -781,7 +823,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
     read_kops<C, 0>(smem, f0, wm, wn, h, l32);
     bool pending = false, pending_dummy = false;
     for (int ct = first; ct < total; ct += stride) {
-      const TileOps cops = src.ops(ct);
+      const TileOps cops = src.ops(ct, 1);
       const int cns = (cops.kc + C::BK - 1) / C::BK;
       v16f acc[C::FM][C::FN];
       unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
@@ -861,12 +903,13 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
     };
     for (int q = 0; q < C::STAGES - 1; ++q) {
       const bool dummy = it >= total;
-      issue_stage<C>(plan, iops, is, smem + slot_issue * C::STAGE_BYTES, w, ldas, ldbs, dummy);
+      if constexpr (FAST) issue_stage_fast<C>(fplan, dummy ? 0 : is, smem + slot_issue * C::STAGE_BYTES, w);
+      else issue_stage<C>(plan, iops, is, smem + slot_issue * C::STAGE_BYTES, w, ldas, ldbs, dummy);
       advance_issue(dummy);
     }
     bool pending = false, pending_dummy = false;
     for (int ct = first; ct < total; ct += stride) {
-      const TileOps cops = src.ops(ct);
+      const TileOps cops = src.ops(ct, 1);
       const int cns = (cops.kc + C::BK - 1) / C::BK;
       v16f acc[C::FM][C::FN];
       unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
@@ -881,7 +924,8 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
         raw_barrier();
         compute_stage<C>(smem + slot_comp * C::STAGE_BYTES, acc, wm, wn, h, l32,
                          [&]() __attribute__((always_inline)) {
-                           issue_stage<C>(plan, iops, is, dst, w, ldas, ldbs, dummy);
+                           if constexpr (FAST) issue_stage_fast<C>(fplan, dummy ? 0 : is, dst, w);
+                           else issue_stage<C>(plan, iops, is, dst, w, ldas, ldbs, dummy);
                          });
         pending = true;
         pending_dummy = dummy;
@@ -895,7 +939,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
   for (int q = 0; q < C::STAGES - 1; ++q) ahead += issue_one();
 
   for (int ct = first; ct < total; ct += stride) {
-    const TileOps cops = src.ops(ct);
+    const TileOps cops = src.ops(ct, 1);
     const int cns = (cops.kc + C::BK - 1) / C::BK;
     v16f acc[C::FM][C::FN];
     unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
@@ -994,15 +1038,18 @@ struct RowsSource {
   const int64_t* pref;       // LDS: first row of each expert's segment
   const int32_t* tile_offs;  // LDS
   int G, n_tiles, ntot;
+  int cursor[2] = {-1, -1};  // segment cursors of the issuing and computing sides
 
   __device__ __forceinline__ int count() const { return ntot; }
 
   struct Pos { int g, mt, nt; };
-  __device__ __forceinline__ Pos pos(int t) const {
-    const int g = upper_bound_i32(tile_offs, G + 1, t) - 1;
+  Pos cur{};                 // the computing side's last tile
+  __device__ __forceinline__ Pos pos(int t, int side) {
+    const int g = seek_segment(tile_offs, G + 1, t, cursor[side]);
     const int local = t - tile_offs[g];
     Pos q{g, 0, 0};
     grouped_tile(local, (tile_offs[g + 1] - tile_offs[g]) / n_tiles, n_tiles, q.mt, q.nt);
+    if (side) cur = q;
     return q;
   }
   // Tile rows: MX tiles start at a multiple of 4 (the scale DMA moves four
@@ -1015,8 +1062,8 @@ struct RowsSource {
     const int64_t row0 = (start & ~(int64_t)kRowAlign<C>) + (int64_t)q.mt * C::BM;
     return Rows{row0, (int)(start - row0), (int)(start + p.sp.m[q.g] - row0)};
   }
-  __device__ __forceinline__ TileOps ops(int t) const {
-    const Pos q = pos(t);
+  __device__ __forceinline__ TileOps ops(int t, int side) {
+    const Pos q = pos(t, side);
     const Rows rw = rows(q);
     const int col0 = q.nt * C::BN;
     const int nleft = p.n_out - col0;
@@ -1034,7 +1081,8 @@ struct RowsSource {
     return o;
   }
   __device__ __forceinline__ void epilogue(int t, v16f (&acc)[C::FM][C::FN], uint8_t* scratch, int w, int lane) {
-    const Pos q = pos(t);
+    (void)t;
+    const Pos q = cur;
     const Rows rw = rows(q);
     const int64_t row0 = rw.row0;
     const int mlo = rw.lo, mleft = rw.hi;
@@ -1093,33 +1141,40 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_dgrad_kernel(const
 // ---------------------------------------------------------------------------
 // variable-K weight gradient
 // ---------------------------------------------------------------------------
-template <class C>
+// Output mode of the weight gradient, a template parameter so a kernel holds
+// only its own epilogue (the accumulating epilogues' loads into registers
+// otherwise make the compiler drain the DMA ring at every stage head).
+enum : int { kEpiF32Acc = 0, kEpiF32Set = 1, kEpiBf16Set = 2, kEpiBf16Acc = 3 };
+
+template <class C, bool FAST, int EPI>
 struct WgradSource {
   const WgradParams& p;
   const int64_t* pad_pref;   // LDS: padded segment offsets (natural expert order)
   const int32_t* tile_offs;  // LDS: tile offsets in longest-first order
   const int16_t* order;      // LDS: the expert at each position of that order
   int G, tc, ntot;
+  int cursor[2] = {-1, -1};  // segment cursors of the issuing and computing sides
 
   __device__ __forceinline__ int count() const { return ntot; }
 
   struct Pos { int g, row0, col0; int64_t p0; int kc; };
-  __device__ __forceinline__ Pos pos(int t) const {
-    const int j = upper_bound_i32(tile_offs, G + 1, t) - 1;
-    // Read-ahead loop: from the LDS copy. A kernel-argument read with a
-    // lane-varying index is a vector memory load, and its wait drains every
-    // DMA in flight once per tile: that costs the 4-stage read-ahead loop
-    // (fc1 795 -> 783 us without it) but measured 9-13 % faster in the
-    // 3-stage loops (MXFP8 3.81 vs 4.17 ms, blockwise 2.20 vs 2.48 ms).
-    const int g = C::SCHED == 7 ? order[j] : p.order[j];
+  Pos cur{};                 // the computing side's last tile
+  __device__ __forceinline__ Pos pos(int t, int side) {
+    const int j = seek_segment(tile_offs, G + 1, t, cursor[side]);
+    // the expert order from its LDS copy: a kernel-argument read with a
+    // lane-varying index is a vector memory load whose wait drains every DMA
+    // in flight once per tile
+    const int g = order[j];
     const int local = t - tile_offs[j];
     int rt, ct;
     grouped_tile(local, (p.n_rows + C::BM - 1) / C::BM, tc, rt, ct);
     const int64_t p0 = pad_pref[g];
-    return Pos{g, rt * C::BM, ct * C::BN, p0, (int)(pad_pref[g + 1] - p0)};
+    const Pos q{g, rt * C::BM, ct * C::BN, p0, (int)(pad_pref[g + 1] - p0)};
+    if (side) cur = q;
+    return q;
   }
-  __device__ __forceinline__ TileOps ops(int t) const {
-    const Pos q = pos(t);
+  __device__ __forceinline__ TileOps ops(int t, int side) {
+    const Pos q = pos(t, side);
     TileOps o;
     // segment start: element bytes (E4M3: 1, E2M1: 1/2); scales, MX
     // block-major (block p0/32, row row0), blockwise row-major (fp32 p0/128)
@@ -1203,19 +1258,15 @@ struct WgradSource {
     });
   }
   __device__ __forceinline__ void epilogue(int t, v16f (&acc)[C::FM][C::FN], uint8_t* scratch, int w, int lane) {
-    const Pos q = pos(t);
+    (void)t;
+    const Pos q = cur;
     float* scr = reinterpret_cast<float*>(scratch);
-    if (p.out_bf16) {
-      if (p.accumulate) store_tile<true, true>(q, acc, scr, w, lane);
-      else store_tile<true, false>(q, acc, scr, w, lane);
-    } else {
-      if (p.accumulate) store_tile<false, true>(q, acc, scr, w, lane);
-      else store_tile<false, false>(q, acc, scr, w, lane);
-    }
+    store_tile<EPI == kEpiBf16Set || EPI == kEpiBf16Acc, EPI == kEpiF32Acc || EPI == kEpiBf16Acc>(q, acc, scr, w,
+                                                                                                  lane);
   }
 };
 
-template <class C>
+template <class C, bool FAST, int EPI>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const WgradParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int64_t pad_pref[kMaxExperts + 1];
@@ -1237,8 +1288,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_wgrad_kernel(const
   for (int j = threadIdx.x; j <= G; j += C::THREADS) tile_offs[j] = (int32_t)tile_pref[j];
   __syncthreads();
 
-  WgradSource<C> src{p, pad_pref, tile_offs, order, G, tc, tile_offs[G]};
-  persistent_loop<C>(src, smem, p.lda, p.ldas, p.ldb, p.ldbs);
+  WgradSource<C, FAST, EPI> src{p, pad_pref, tile_offs, order, G, tc, tile_offs[G]};
+  persistent_loop<C, FAST>(src, smem, p.lda, p.ldas, p.ldb, p.ldbs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1295,7 +1346,7 @@ static hipError_t launch_rows_as(const RowsGemmParams& p, bool dgrad, int num_cu
 // the per-lane scale offsets ((SB-1) blocks of ld bytes plus a row) fit 32 bits.
 template <class C>
 static hipError_t launch_rows(const RowsGemmParams& p, bool dgrad, int num_cus, hipStream_t st) {
-  if constexpr (C::SCHED == 7) {
+  if constexpr ((C::SCHED == 7 || C::SCHED == 5) && !C::BLK) {
     constexpr int64_t kLim = (int64_t)1 << 30;
     if (p.kc % C::BK == 0 && p.ldas < kLim && p.ldbs < kLim) return launch_rows_as<C, true>(p, dgrad, num_cus, st);
   }
@@ -1316,7 +1367,15 @@ static hipError_t launch_wgrad(const WgradParams& p, int num_cus, hipStream_t st
   const int64_t per = (int64_t)((p.n_rows + C::BM - 1) / C::BM) * ((p.n_cols + C::BN - 1) / C::BN);
   for (int g = 0; g < p.sp.G; ++g) tiles += (p.sp.m[g] > 0 || !p.accumulate) ? per : 0;
   if (tiles == 0) return hipSuccess;
-  return launch_persistent<C>(grouped_wgrad_kernel<C>, p, tiles, num_cus, st);
+  // fp32 row scales: segments are padded to 128, so with BK dividing 128
+  // every stage is full and the fast issue applies
+  constexpr bool FAST = C::F32S && !C::BLK && 128 % C::BK == 0;
+  if (p.out_bf16) {
+    if (p.accumulate) return launch_persistent<C>(grouped_wgrad_kernel<C, FAST, kEpiBf16Acc>, p, tiles, num_cus, st);
+    return launch_persistent<C>(grouped_wgrad_kernel<C, FAST, kEpiBf16Set>, p, tiles, num_cus, st);
+  }
+  if (p.accumulate) return launch_persistent<C>(grouped_wgrad_kernel<C, FAST, kEpiF32Acc>, p, tiles, num_cus, st);
+  return launch_persistent<C>(grouped_wgrad_kernel<C, FAST, kEpiF32Set>, p, tiles, num_cus, st);
 }
 
 hipError_t launch_grouped_wgrad_mx(const WgradParams& p, bool fp8, int num_cus, hipStream_t st) {

@@ -1,16 +1,15 @@
 """The GEMM stage loops wait only as designed (CPU: cross-compiled gfx950
 assembly, no GPU). The ring's correctness and speed rest on constant
 `s_waitcnt vmcnt(N)` waits; the compiler adds a full drain, `vmcnt(0)`,
-wherever it cannot prove an in-flight DMA or load is done (for instance
-before reusing a VGPR that an in-flight LDS DMA used as its address), and
-such a drain inside a stage loop stalls every step. For the forward / input
-gradient (a4w4 and power-of-two blockwise) and the a4w4 weight gradient, the
-innermost loop holding the MFMAs must carry exactly one vector-memory wait:
-(STAGES-3)*DPS for the read-ahead loop, (STAGES-2)*DPS for the other. The
-3-stage weight gradients (MXFP8, power-of-two blockwise) also carry the drain
-of their once-per-tile kernel-argument read of the expert order (measured
-faster than an LDS copy, whose build put a second drain at every step head);
-any further wait is a regression."""
+wherever it cannot prove an in-flight DMA or load is done, and such a drain
+inside a stage loop stalls every step. The innermost loop holding the MFMAs
+must carry exactly one vector-memory wait: (STAGES-3)*DPS for the read-ahead
+loop, (STAGES-2)*DPS for the 3-stage loops. Two things once put extra drains
+there and are kept out: reading the expert order from the kernel arguments
+with a lane-varying index (a vector load; the order now comes from an LDS
+copy), and weight-gradient kernels holding every output mode's epilogue (the
+accumulating epilogues' loads into registers; each mode is now its own
+kernel). Any further wait is a regression."""
 import os
 import re
 import shutil
@@ -23,21 +22,24 @@ SRC = os.path.join(ROOT, "moe_grouped_block_mx_amd", "csrc", "gemm_mx.hip")
 
 # kernel name fragment (TileCfg parameters) -> the waits its stage loop must carry
 EXPECTED = {
-    # a4w4 forward / input gradient: 8 waves, 128-deep stages, 4-stage read-ahead ring, DPS 5
-    # (Lb1: every stage full, scalar-base DMA issue; Lb0: the general issue)
+    # a4w4 forward / input gradient: 8 waves, 128-deep stages, 4-stage
+    # read-ahead ring, DPS 5 (Lb1: every stage full, scalar-base DMA issue;
+    # Lb0: the general issue)
     "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb1E": [5],
     "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb1E": [5],
     "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [5],
     "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [5],
-    # a4w4 weight gradient: 4 waves, same ring, DPS 10
-    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi2ELi128ELi4ELi0ELi1ELi7ELi1E": [10],
+    # a4w4 weight gradient: 4 waves, same ring, DPS 10 (every output mode)
+    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi2ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [10],
     # power-of-two blockwise forward / input gradient: 64-deep stages, 3-stage ring, DPS 6
+    "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEELb1E": [6],
+    "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEELb1E": [6],
     "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEELb0E": [6],
     "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEELb0E": [6],
-    # MXFP8 weight gradient (DPS 5) and power-of-two blockwise weight gradient
-    # (DPS 6): the ring wait, then the tile switch's drain
-    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi4ELi1ELi5ELi1E": [5, 0],
-    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi1E": [6, 0],
+    # MXFP8 weight gradient (DPS 5, general issue) and power-of-two blockwise
+    # weight gradient (DPS 6, scalar-base issue), every output mode
+    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi4ELi1ELi5ELi1EEELb0E": [5],
+    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi1EEELb1E": [6],
 }
 
 
@@ -96,5 +98,6 @@ def test_stage_loops_carry_only_the_ring_wait(tmp_path):
     waits = stage_loop_waits(asm.read_text().splitlines())
     for frag, want in EXPECTED.items():
         found = [k for k in waits if frag in k]
-        assert len(found) == 1, (frag, list(waits))
-        assert waits[found[0]] == want, (frag, waits[found[0]])
+        assert found, (frag, list(waits))
+        for k in found:
+            assert waits[k] == want, (k, waits[k])
