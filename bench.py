@@ -35,7 +35,7 @@ same step -- one expert with 8192 tokens at the full K and N, all three
 passes including quantization -- on this host's cores.
 
 roofline.traffic: HBM bytes per launch of the dominant kernel, read from the
-committed rocprofv3 summary profiles/<kernel>_fc1_traffic.txt (FETCH_SIZE and
+committed rocprofv3 summary profiles/<kernel>_<workload>_traffic.txt (FETCH_SIZE and
 WRITE_SIZE per dispatch, each scaled by the same counter's reading for a plain
 1 GiB copy); null when that summary was taken from a different kernel source.
 kernels.<gemm>.rocprof_mfma_busy_pct (fc1): MFMA-busy of that GEMM from the
@@ -112,13 +112,13 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def traffic_summary_path(kernel):
-    return os.path.join(ROOT, "profiles", f"{kernel}_fc1_traffic.txt")
+def traffic_summary_path(kernel, workload="fc1"):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
 
 
-def read_traffic(kernel):
+def read_traffic(kernel, workload="fc1"):
     """(fetch, write) HBM bytes per launch from the committed summary, or None."""
-    path = traffic_summary_path(kernel)
+    path = traffic_summary_path(kernel, workload)
     if kernel not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     kv = {}
@@ -147,8 +147,10 @@ def _counter_per_dispatch(path, name_prefix, counter, pick=None):
     return [per[d] for d in sorted(per)]
 
 
-def summarize(kernel, stats_csv, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+def summarize(kernel, stats_csv, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload="fc1"):
     prefix = KERNEL_SOURCES[kernel][0]
+    wl = "" if workload == "fc1" else f" --workload {workload}"
+    sfx = "" if workload == "fc1" else f"_{workload}"
     stats = None
     with open(stats_csv, newline="") as fh:
         for row in csv.DictReader(fh):
@@ -166,21 +168,21 @@ def summarize(kernel, stats_csv, fetch_csv, write_csv, copy_fetch_csv, copy_writ
     write_b = float(np.median(write)) * kib * w_scale
     lines = [
         f"kernel: {kernel}",
-        "workload: MoE FC1 a4w4, 32 experts, 32768 routed rows, K=4096, N=3072 (bench.py default step)",
+        f"workload: {WORKLOAD_TITLES[workload]} (bench.py{wl or ' default step'})",
         "# commands (GPU run, R = repository root, OUT = an output directory, each rocprofv3 pass in its own process):",
         "#   cd /tmp && export TMPDIR=/tmp",
-        "#   rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_stats -o run"
-        " -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
-        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/prof_fetch -o run"
-        " -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/prof_write -o run"
-        " -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        f"#   rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_stats{sfx} -o run"
+        f" -- python3 $R/bench.py{wl} --steps 5 --warmup 2 --no-cpu-baseline",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/prof_fetch{sfx} -o run"
+        f" -- python3 $R/bench.py{wl} --steps 3 --warmup 1 --no-cpu-baseline",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/prof_write{sfx} -o run"
+        f" -- python3 $R/bench.py{wl} --steps 3 --warmup 1 --no-cpu-baseline",
         "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/prof_cfetch -o run"
         " -- python3 $R/bench.py --copy-only",
         "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/prof_cwrite -o run"
         " -- python3 $R/bench.py --copy-only",
-        f"#   python3 $R/bench.py --summarize {kernel} <prof_stats kernel_stats.csv> <prof_fetch counter_collection.csv>"
-        " <prof_write ...> <prof_cfetch ...> <prof_cwrite ...>",
+        f"#   python3 $R/bench.py --summarize {kernel} <prof_stats{sfx} kernel_stats.csv> <prof_fetch{sfx}"
+        f" counter_collection.csv> <prof_write{sfx} ...> <prof_cfetch ...> <prof_cwrite ...>{wl}",
         f"source_sha256_16: {source_hash(kernel)}",
         f"kernel_name_prefix: {prefix}",
         f"stats_calls: {stats['Calls'] if stats else 'n/a'}",
@@ -652,7 +654,7 @@ EXTRA_WORKLOADS = ("a8w4", "blockwise")
 def main():
     args = parse()
     if args.summarize:
-        sys.stdout.write(summarize(*args.summarize))
+        sys.stdout.write(summarize(*args.summarize, workload=args.workload))
         return
     if args.summarize_mfma:
         sys.stdout.write(summarize_mfma(args.summarize_mfma, args.workload))
@@ -718,6 +720,8 @@ def main():
         for name in EXTRA_WORKLOADS:
             X = build_workload(name, dev)
             t_x, per_x, roof_x = measure(X, args, dev)
+            tr_x = read_traffic(roof_x["kernel"], name)
+            roof_x["traffic"] = None if tr_x is None else round(tr_x[0] + tr_x[1])
             fl = sum(X["flops"][n] for n, k, _ in X["ops"] if k == "gemm")
             extra[name] = {"metric": X["metric"], "value": round(fl / t_x / 1e12, 2), "unit": "TFLOPS",
                            "ms_per_step": round(t_x * 1e3, 4), "dtype": X["dtype"], "config": X["config"],

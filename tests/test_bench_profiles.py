@@ -94,8 +94,30 @@ def test_stale_summaries_read_as_absent(tmp_path, monkeypatch):
     traffic = tmp_path / "wgrad_fc1_traffic.txt"
     traffic.write_text("source_sha256_16: 0000000000000000\nhbm_fetch_bytes_per_launch: 1\n"
                        "hbm_write_bytes_per_launch: 2\n")
-    monkeypatch.setattr(bench, "traffic_summary_path", lambda k: str(traffic))
+    monkeypatch.setattr(bench, "traffic_summary_path", lambda k, w="fc1": str(traffic))
     assert bench.read_traffic("wgrad") is None
+
+
+def test_traffic_summary_names_its_workload(tmp_path):
+    # a summary of another workload's kernel carries that workload's title and
+    # commands, and is found under its own file name
+    kib = 1024
+    stats = tmp_path / "stats.csv"
+    with open(stats, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs"])
+        w.writeheader()
+        w.writerow({"Name": WGRAD, "Calls": 1, "AverageNs": 2000000, "MinNs": 1, "MaxNs": 2})
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    cfetch, cwrite = tmp_path / "cf.csv", tmp_path / "cw.csv"
+    _write(fetch, [(7, WGRAD, "FETCH_SIZE", 10, 0, 1)])
+    _write(write, [(7, WGRAD, "WRITE_SIZE", 20, 0, 1)])
+    _write(cfetch, [(1, COPY, "FETCH_SIZE", bench.COPY_BYTES / kib, 0, 1)])
+    _write(cwrite, [(1, COPY, "WRITE_SIZE", bench.COPY_BYTES / kib, 0, 1)])
+    text = bench.summarize("wgrad", str(stats), str(fetch), str(write), str(cfetch), str(cwrite),
+                           workload="blockwise")
+    assert bench.WORKLOAD_TITLES["blockwise"] in text
+    assert "bench.py --workload blockwise --steps 3" in text
+    assert bench.traffic_summary_path("wgrad", "blockwise").endswith("wgrad_blockwise_traffic.txt")
 
 
 
