@@ -124,23 +124,39 @@ typedef enum mxgg_format {
 
 /*
  * MX scale layouts. An MX format argument may carry the layout of the scales
- * it describes in its high bits: fmt = MXGG_MXFP4 | MXGG_LAYOUT_ROW_MAJOR.
+ * it describes in its high bits: fmt = MXGG_MXFP4 | MXGG_LAYOUT_MFMA.
  * The layout is never inferred from shapes.
- *   MXGG_LAYOUT_BLOCK_MAJOR (0, what a plain format means): the layout every
- *     quantizer writes and every GEMM reads, u8 [blocks, R4] (see "MX scale
- *     layout" above) -- the arrangement the GEMM stages load with one aligned
- *     4-byte DMA per four rows of a block.
+ *   MXGG_LAYOUT_BLOCK_MAJOR (0, what a plain format means): u8 [blocks, R4]
+ *     (see "MX scale layout" above) -- what the quantizers write by default
+ *     and every GEMM reads for every operand: a GEMM stage loads four rows of
+ *     a block with one aligned 4-byte DMA.
  *   MXGG_LAYOUT_ROW_MAJOR: plain per-row scales, u8 [rows, blocks] (the
  *     un-arranged scale layout of the page "Integrate MXFP4 hipblaslt GEMM
  *     support"). The quantizers and GEMMs refuse it with MXGG_ERR_FORMAT; it
- *     is never read as block-major. mxgg_mx_scales_relayout converts between
- *     the two.
+ *     is never read as another layout. mxgg_mx_scales_relayout converts it.
+ *   MXGG_LAYOUT_MFMA: the pre-arranged layout of the scaled 32x32x64 MFMA
+ *     (the page above compares plain scales with pre-swizzled ones packed in
+ *     units of 32 rows by a run of blocks; this is such a packing, defined
+ *     here). With R32 = rows rounded up to a multiple of 32 and blocks a
+ *     multiple of 4, it is u8 [blocks/4, R32/32, 64, 2]: unit (g, u) holds
+ *     rows 32u..32u+31 and blocks 4g..4g+3, and byte (g, u, L, j) is the
+ *     scale of row 32u + L%32, block 4g + 2j + L/32 -- the two scale operands
+ *     lane L of one 32-row MFMA fragment takes for the two 64-deep K steps of
+ *     a 128-element chunk, side by side (padding rows 0). Total bytes:
+ *     blocks * R32. Written by the quantizers (rows of cols % 128 == 0;
+ *     column-wise only when every split is a multiple of 128, so each
+ *     expert's segment starts a unit) and read for the weights' scales: the
+ *     forward's w_s (N % 32 == 0, K % 128 == 0) and the input gradient's
+ *     wcol_s (N % 128 == 0). Activation and gradient scales stay block-major
+ *     (a_s, dy_s and both weight-gradient operands refuse it with
+ *     MXGG_ERR_FORMAT).
  * Blockwise formats take no layout bits (their fp32 scales are row-major by
  * definition); any layout bits on them are MXGG_ERR_FORMAT.
  */
 typedef enum mxgg_scale_layout {
   MXGG_LAYOUT_BLOCK_MAJOR = 0x000,
-  MXGG_LAYOUT_ROW_MAJOR = 0x100
+  MXGG_LAYOUT_ROW_MAJOR = 0x100,
+  MXGG_LAYOUT_MFMA = 0x200
 } mxgg_scale_layout;
 #define MXGG_LAYOUT_MASK 0xF00
 
@@ -157,19 +173,19 @@ typedef enum mxgg_scale_layout {
 int64_t mxgg_mx_scale_stride(int64_t rows);
 
 /*
- * MX scales from one layout into the other, on `stream`: row-major u8
- * [rows, blocks] <-> block-major u8 [blocks, mxgg_mx_scale_stride(rows)]
- * (padding rows written as 0). For callers that hold plain per-row UE8M0
+ * MX scales from one layout into another, on `stream`: any two different
+ * layouts among row-major u8 [rows, blocks], block-major u8 [blocks,
+ * mxgg_mx_scale_stride(rows)] and the MFMA layout u8 [blocks/4, R32/32, 64,
+ * 2] (padding rows written as 0). For callers that hold plain per-row UE8M0
  * scales (the un-arranged layout the page "Integrate MXFP4 hipblaslt GEMM
- * support" compares with pre-arranged ones) and want the GEMMs' layout, or
- * back.
+ * support" compares with pre-arranged ones) and want a GEMM's layout, or back.
  *   src, dst   device buffers in src_layout / dst_layout; must not overlap.
  *   rows       rows of the operand (>= 0, < 2^31); blocks (> 0, <= 4194240):
- *              scale blocks of 32 along the contraction (cols / 32).
- * Layouts: MXGG_LAYOUT_ROW_MAJOR and MXGG_LAYOUT_BLOCK_MAJOR, different from
- * each other (else MXGG_ERR_FORMAT). rows == 0 returns MXGG_OK (no launch).
- * Errors: NULL, SHAPE, FORMAT, DEVICE, ARCH, HIP (no alignment requirement:
- * byte data).
+ *              scale blocks of 32 along the contraction (cols / 32), a
+ *              multiple of 4 when either side is MXGG_LAYOUT_MFMA.
+ * Equal or unknown layouts are MXGG_ERR_FORMAT. rows == 0 returns MXGG_OK (no
+ * launch). Errors: NULL, SHAPE, FORMAT, DEVICE, ARCH, HIP (no alignment
+ * requirement: byte data).
  */
 mxgg_status mxgg_mx_scales_relayout(const void* src, mxgg_scale_layout src_layout, int64_t rows,
                                     int64_t blocks, void* dst, mxgg_scale_layout dst_layout,
@@ -181,12 +197,14 @@ mxgg_status mxgg_mx_scales_relayout(const void* src, mxgg_scale_layout src_layou
  * GEMM").
  *   x       bf16 [rows, cols], leading dimension ldx (elements, >= cols,
  *           multiple of 8).
- *   fmt     MXGG_MXFP4 / MXGG_MXFP8: blocks of 32 along cols (cols % 32 == 0).
+ *   fmt     MXGG_MXFP4 / MXGG_MXFP8: blocks of 32 along cols (cols % 32 == 0),
+ *           optionally | MXGG_LAYOUT_MFMA (cols % 128 == 0).
  *           MXGG_FP8_1x128: blocks of 128 along cols (cols % 128 == 0).
  *           MXGG_FP8_128x128: 128x128 blocks (rows % 128 == 0, cols % 128 == 0).
  *   flags   MXGG_POW2_SCALES for the blockwise formats (ignored for MX).
  *   q       MXFP4: u8 [rows, cols/2]; otherwise u8 [rows, cols] (E4M3 codes).
- *   scales  MX: u8 [cols/32, R4] (block-major, R4 = mxgg_mx_scale_stride(rows));
+ *   scales  MX: u8 [cols/32, R4] (block-major, R4 = mxgg_mx_scale_stride(rows)),
+ *           or with MXGG_LAYOUT_MFMA u8 [cols/128, R32/32, 64, 2];
  *           FP8_1x128: f32 [rows, cols/128];
  *           FP8_128x128: f32 [rows/128, cols/128].
  * rows == 0 returns MXGG_OK with no launch. Errors: NULL, SHAPE, FORMAT,
@@ -208,9 +226,12 @@ mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int
  * W viewed as [G*N, K] with m_splits = {N, ..., N} gives W quantized along N.
  *   x        bf16 [rows, cols], leading dimension ldx; rows == sum(m_splits).
  *   m_splits host int64 [G], 1 <= G <= 512, each >= 0.
- *   fmt      MXGG_MXFP4, MXGG_MXFP8 or MXGG_FP8_1x128; cols % 32 == 0.
+ *   fmt      MXGG_MXFP4, MXGG_MXFP8 or MXGG_FP8_1x128; cols % 32 == 0. MX
+ *            formats | MXGG_LAYOUT_MFMA need every split to be a multiple of
+ *            128 (else MXGG_ERR_SPLITS).
  *   q        MXFP4: u8 [cols, mpad/2]; otherwise u8 [cols, mpad].
- *   scales   MX: u8 [mpad/32, cols] (block-major; cols % 32 == 0, so R4 == cols);
+ *   scales   MX: u8 [mpad/32, cols] (block-major; cols % 32 == 0, so R4 == cols),
+ *            or with MXGG_LAYOUT_MFMA u8 [mpad/128, cols/32, 64, 2];
  *            FP8_1x128: f32 [cols, mpad/128].
  *   mpad     must equal mxgg_segpad_rows(m_splits, G, fmt).
  * Padding positions hold zero codes. rows == 0 returns MXGG_OK (no launch).
@@ -231,13 +252,16 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
  *   x, rows, cols, ldx, m_splits, G, mpad  as for mxgg_quantize_colwise_segpad.
  *   fmt     MXGG_MXFP4, MXGG_MXFP8, or MXGG_FP8_1x128 / MXGG_FP8_1x128_P2
  *           (1x128 blocks along cols row-wise, along each expert's padded
- *           segment column-wise; cols % 128 == 0).
+ *           segment column-wise; cols % 128 == 0). An MX format may carry
+ *           MXGG_LAYOUT_MFMA, which then applies to both scale outputs (the
+ *           rules of the two quantizers above apply).
  *   flags   MXGG_POW2_SCALES for MXGG_FP8_1x128 (implied by the _P2 format);
  *           ignored for MX formats.
  *   q_row, s_row  the row-wise outputs, as mxgg_quantize_rowwise.
  *   q_col, s_col  the column-wise outputs, as mxgg_quantize_colwise_segpad.
  * Weights for dgrad (MX): W as [G*N, K] with m_splits = {N, ..., N} gives the
- * forward's W_q/W_s and dgrad's wcol_q/wcol_s together.
+ * forward's W_q/W_s and dgrad's wcol_q/wcol_s together (in MXGG_LAYOUT_MFMA
+ * too when N % 128 == 0 and K % 128 == 0).
  * rows == 0 returns MXGG_OK (no launch). Errors: NULL, SHAPE, SPLITS, FORMAT,
  * ALIGN, DEVICE, ARCH, HIP.
  */
@@ -272,10 +296,13 @@ mxgg_status mxgg_transpose_128x128(const void* w_q, const void* w_s, int32_t G, 
  *             + u8 [K/32, mxgg_mx_scale_stride(M)]; or MXGG_FP8_1x128: u8 [M, K]
  *             + f32 [M, K/128].
  *   w_q, w_s  packed expert weights [G*N, K] quantized row-wise along K:
- *             MXFP4 u8 [G*N, K/2] + u8 [K/32, G*N]; or MXGG_FP8_128x128:
- *             u8 [G*N, K] + f32 [G*N/128, K/128].
+ *             MXFP4 u8 [G*N, K/2] + u8 [K/32, G*N], or with w_fmt =
+ *             MXGG_MXFP4 | MXGG_LAYOUT_MFMA the scales u8 [K/128, G*N/32,
+ *             64, 2] (K % 128 == 0); or MXGG_FP8_128x128: u8 [G*N, K] + f32
+ *             [G*N/128, K/128].
  *   format pairs (a_fmt, w_fmt): (MXFP4, MXFP4) a4w4, (MXFP8, MXFP4) a8w4,
- *             (FP8_1x128, FP8_128x128) blockwise FP8.
+ *             (FP8_1x128, FP8_128x128) blockwise FP8. a_fmt takes no layout
+ *             bits other than block-major.
  *   m_splits  host int64 [G]; sum == M.
  *   M, N, K   K % 32 == 0 and N % 32 == 0 (MX); K % 128 == 0 and N % 128 == 0
  *             (blockwise); M < 2^31; N, K < 2^23.
@@ -298,6 +325,9 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
  *   fmt            dY's format, which fixes the weights':
  *                  MXGG_MXFP4 (a4w4) and MXGG_MXFP8 (a8w4): W in MXFP4;
  *                  MXGG_FP8_1x128 / _P2: W as transposed 128x128 blocks.
+ *                  MXGG_LAYOUT_MFMA on an MX fmt says that wcol_s is in the
+ *                  MFMA layout, u8 [G*N/128, K/32, 64, 2] (N % 128 == 0);
+ *                  dy_s stays block-major.
  *   dy_q, dy_s     dY quantized row-wise along N: MX, u8 [M, N/2] (E2M1) or
  *                  [M, N] (E4M3) + u8 [N/32, mxgg_mx_scale_stride(M)];
  *                  blockwise, E4M3 [M, N] + f32 [M, N/128].
@@ -333,7 +363,8 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
  *   xcol_q/_s   X from mxgg_quantize_colwise_segpad: [K, mpad] operand
  *               (MX scales u8 [mpad/32, K]).
  *   fmt         MXGG_MXFP4 or MXGG_MXFP8 (both operands in that format: the
- *               a4w4 and a8w4 weight gradients; pad 32), or MXGG_FP8_1x128
+ *               a4w4 and a8w4 weight gradients; pad 32; block-major scales
+ *               only), or MXGG_FP8_1x128
  *               (pad 128). MXGG_FP8_1x128_P2 asserts that the scales of BOTH
  *               operands are powers of two (the MFMA then applies them and a
  *               non-power-of-two scale would lose its mantissa); pass
@@ -361,8 +392,9 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
 size_t mxgg_workspace_size(int32_t G);
 
 /* Padded row count of the segment-padded operand: sum_g ceil(m_g/P)*P with
- * P = 32 (MX formats) or 128 (MXGG_FP8_1x128). Returns -1 for invalid input
- * (NULL, G outside [1, 512], a negative split, other formats). */
+ * P = 32 (MX formats, any scale layout bits) or 128 (MXGG_FP8_1x128). Returns
+ * -1 for invalid input (NULL, G outside [1, 512], a negative split or one of
+ * 2^31 or more, other formats). */
 int64_t mxgg_segpad_rows(const int64_t* m_splits, int32_t G, mxgg_format fmt);
 
 /* Static text for a status code. */

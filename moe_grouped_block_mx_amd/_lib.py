@@ -23,7 +23,7 @@ FORMATS = {"mxfp4": MXFP4, "mxfp8": MXFP8, "fp8_1x128": FP8_1x128, "fp8_128x128"
 POW2_SCALES = 1
 MAX_EXPERTS = 512
 # mxgg_scale_layout: OR-ed into an MX format to state the layout of its scales
-LAYOUT_BLOCK_MAJOR, LAYOUT_ROW_MAJOR, LAYOUT_MASK = 0x000, 0x100, 0xF00
+LAYOUT_BLOCK_MAJOR, LAYOUT_ROW_MAJOR, LAYOUT_MFMA, LAYOUT_MASK = 0x000, 0x100, 0x200, 0xF00
 
 STATUS = {
     0: "MXGG_OK", 1: "MXGG_ERR_NULL", 2: "MXGG_ERR_SHAPE", 3: "MXGG_ERR_SPLITS",
@@ -154,6 +154,24 @@ def _row_major(f):
     return (f & LAYOUT_MASK) == LAYOUT_ROW_MAJOR
 
 
+def _mfma(f):
+    return (f & LAYOUT_MASK) == LAYOUT_MFMA
+
+
+def _rows32(rows):
+    return (rows + 31) // 32 * 32 if rows > 0 else 0
+
+
+def _layout_shape(layout, rows, blocks):
+    """u8 scales of an operand with `rows` rows and `blocks` blocks of 32 along
+    its contraction, in one of the three MX scale layouts."""
+    if layout == LAYOUT_ROW_MAJOR:
+        return (rows, blocks)
+    if layout == LAYOUT_MFMA:                                     # [blocks/4, R32/32, 64, 2]
+        return (blocks // 4, _rows32(rows) * 4)
+    return (blocks, mxgg_mx_scale_stride(rows))                   # block-major
+
+
 def _q_shape(f, rows, cols):
     """Quantized data of a [rows, cols] operand packed along cols."""
     return (rows, cols // 2 if (f & 0xFF) == MXFP4 else cols)
@@ -163,9 +181,7 @@ def _row_scale_shape(f, rows, cols):
     """Scales of a [rows, cols] operand quantized along cols (row-major scales
     when the format says so: the library refuses them, never misreads them)."""
     if _is_mx(f):
-        if _row_major(f):
-            return (rows, cols // 32)
-        return (cols // 32, mxgg_mx_scale_stride(rows))           # block-major
+        return _layout_shape(f & LAYOUT_MASK, rows, cols // 32)
     if (f & 0xFF) in (FP8_1x128, FP8_1x128_P2):
         return (rows, cols // 128)
     return (rows // 128, cols // 128)
@@ -174,7 +190,7 @@ def _row_scale_shape(f, rows, cols):
 def _col_scale_shape(f, cols, mpad):
     """Scales of the column-wise segment-padded [cols, mpad] operand."""
     if _is_mx(f):
-        return (cols, mpad // 32) if _row_major(f) else (mpad // 32, cols)
+        return _layout_shape(f & LAYOUT_MASK, cols, mpad // 32)
     return (cols, mpad // 128)
 
 
@@ -189,7 +205,7 @@ def mxgg_workspace_size(G: int) -> int:
 
 def mxgg_segpad_rows(m_splits, fmt) -> int:
     arr, G = _splits(m_splits)
-    r = int(lib.mxgg_segpad_rows(arr, G, _fmt(fmt)))
+    r = int(lib.mxgg_segpad_rows(arr, G, _fmt(fmt) & 0xFF))
     if r < 0:
         raise MxggError(2, "invalid splits or format for mxgg_segpad_rows")
     return r
@@ -203,11 +219,12 @@ def _flags(flags, f):
 
 
 def mxgg_mx_scales_relayout(src, rows, blocks, src_layout, dst_layout, dst=None):
-    """MX scales row-major u8 [rows, blocks] <-> block-major u8
-    [blocks, mx_scale_stride(rows)] (padding rows 0). Returns dst."""
+    """MX scales from one layout into another: row-major u8 [rows, blocks],
+    block-major u8 [blocks, mx_scale_stride(rows)], MFMA u8 [blocks/4,
+    R32*4] (R32 = rows rounded up to 32; padding rows 0). Returns dst."""
     torch = _torch()
-    src_shape = (rows, blocks) if src_layout == LAYOUT_ROW_MAJOR else (blocks, mxgg_mx_scale_stride(rows))
-    dst_shape = (rows, blocks) if dst_layout == LAYOUT_ROW_MAJOR else (blocks, mxgg_mx_scale_stride(rows))
+    src_shape = _layout_shape(src_layout, rows, blocks)
+    dst_shape = _layout_shape(dst_layout, rows, blocks)
     _expect(src, "src", src_shape, torch.uint8)
     if dst is None:
         dst = torch.empty(dst_shape, dtype=torch.uint8, device=src.device)
@@ -250,7 +267,7 @@ def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=None, q=None, s
     rows, cols = x.shape
     _check_bf16_2d(x)
     arr, G = _splits(m_splits)
-    mpad = int(lib.mxgg_segpad_rows(arr, G, f))
+    mpad = int(lib.mxgg_segpad_rows(arr, G, f & 0xFF))
     if mpad < 0:
         mpad = 0
     if q is None:
@@ -274,7 +291,7 @@ def mxgg_quantize_dual(x, m_splits, fmt="mxfp4", flags=None, q_row=None, s_row=N
     rows, cols = x.shape
     _check_bf16_2d(x)
     arr, G = _splits(m_splits)
-    mpad = int(lib.mxgg_segpad_rows(arr, G, f))
+    mpad = int(lib.mxgg_segpad_rows(arr, G, f & 0xFF))
     if mpad < 0:
         mpad = 0
     u8 = dict(dtype=torch.uint8, device=x.device)
@@ -338,11 +355,12 @@ def mxgg_grouped_dgrad(dy_q, dy_s, wcol_q, wcol_s, m_splits, N, K, fmt="mxfp4", 
     arr, G = _splits(m_splits)
     M = dy_q.shape[0]
     f = _fmt(fmt)
+    # layout bits of fmt describe wcol_s; dY's scales are block-major
     _expect(dy_q, "dy_q", _q_shape(f, M, N), torch.uint8)
-    _expect(dy_s, "dy_s", _row_scale_shape(f, M, N), _sdtype(f))
+    _expect(dy_s, "dy_s", _row_scale_shape(f & 0xFF, M, N), _sdtype(f))
     if _is_mx(f):                       # W along N, MXFP4: [K, G*N/2] + [G*N/32, K]
         _expect(wcol_q, "wcol_q", _q_shape(MXFP4, K, G * N), torch.uint8)
-        _expect(wcol_s, "wcol_s", _col_scale_shape(MXFP4, K, G * N), torch.uint8)
+        _expect(wcol_s, "wcol_s", _col_scale_shape(MXFP4 | (f & LAYOUT_MASK), K, G * N), torch.uint8)
     else:                               # transposed 128x128 blocks
         _expect(wcol_q, "wcol_q", (G * K, N), torch.uint8)
         _expect(wcol_s, "wcol_s", (G * K // 128, N // 128), torch.float32)

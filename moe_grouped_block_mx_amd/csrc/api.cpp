@@ -145,7 +145,7 @@ size_t mxgg_workspace_size(int32_t G) {
 
 int64_t mxgg_segpad_rows(const int64_t* m_splits, int32_t G, mxgg_format fmt) {
   if (!m_splits || G < 1 || G > MXGG_MAX_EXPERTS) return -1;
-  fmt = (mxgg_format)base_format(fmt);
+  fmt = (mxgg_format)base_format(format_bits(fmt));  // the scale layout does not change the padding
   if (fmt != MXGG_MXFP4 && fmt != MXGG_MXFP8 && fmt != MXGG_FP8_1x128) return -1;
   for (int32_t g = 0; g < G; ++g)
     if (m_splits[g] < 0 || m_splits[g] > kMaxSplit) return -1;
@@ -162,8 +162,8 @@ mxgg_status mxgg_mx_scales_relayout(const void* src, mxgg_scale_layout src_layou
   int cus = 0;
   c = device_checks(stream, {{src, "src"}, {dst, "dst"}}, &cus);
   if (!c.ok()) return finish(c);
-  c = hip_status(launch_relayout_scales(static_cast<const uint8_t*>(src), rows, blocks,
-                                        dst_layout == MXGG_LAYOUT_BLOCK_MAJOR, static_cast<uint8_t*>(dst), stream),
+  c = hip_status(launch_relayout_scales(static_cast<const uint8_t*>(src), (int)src_layout, rows, blocks,
+                                        (int)dst_layout, static_cast<uint8_t*>(dst), stream),
                  "scale relayout launch");
   return c.ok() ? ok() : finish(c);
 }
@@ -175,11 +175,13 @@ mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int
   Check c = validate_quantize_rowwise(x, rows, cols, ldx, (int)fmt, q, scales);
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
+  const bool mfma = is_mfma_layout(fmt);
+  fmt = (mxgg_format)format_bits(fmt);
   int cus = 0;
   c = device_checks(stream, {{x, "x"}, {q, "q"}, {scales, "scales"}}, &cus);
   if (!c.ok()) return finish(c);
   if (is_mx(fmt))
-    c = hip_status(launch_quant_rowwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, fmt == MXGG_MXFP8,
+    c = hip_status(launch_quant_rowwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, fmt == MXGG_MXFP8, mfma,
                                            static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), cus, stream),
                    "row-wise quantizer launch");
   else
@@ -198,13 +200,16 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
   Check c = validate_quantize_colwise(x, rows, cols, ldx, m_splits, G, (int)fmt, q, scales, mpad);
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
+  const bool mfma = is_mfma_layout(fmt);
+  fmt = (mxgg_format)format_bits(fmt);
   int cus = 0;
   c = device_checks(stream, {{x, "x"}, {q, "q"}, {scales, "scales"}}, &cus);
   if (!c.ok()) return finish(c);
   const SplitArgs sp = make_splits(m_splits, G);
   if (is_mx(fmt))
     c = hip_status(launch_quant_colwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8,
-                                           static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), mpad, stream),
+                                           mfma, static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), mpad,
+                                           stream),
                    "column-wise quantizer launch");
   else
     c = hip_status(launch_quant_colwise_blk(static_cast<const uint16_t*>(x), cols, ldx, sp,
@@ -222,12 +227,14 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
   Check c = validate_quantize_dual(x, rows, cols, ldx, m_splits, G, (int)fmt, q_row, s_row, q_col, s_col, mpad);
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
+  const bool mfma = is_mfma_layout(fmt);
+  fmt = (mxgg_format)format_bits(fmt);
   int cus = 0;
   c = device_checks(stream, {{x, "x"}, {q_row, "q_row"}, {s_row, "s_row"}, {q_col, "q_col"}, {s_col, "s_col"}}, &cus);
   if (!c.ok()) return finish(c);
   const SplitArgs sp = make_splits(m_splits, G);
   if (is_mx(fmt))
-    c = hip_status(launch_quant_dual_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8,
+    c = hip_status(launch_quant_dual_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8, mfma,
                                         static_cast<uint8_t*>(q_row), static_cast<uint8_t*>(s_row),
                                         static_cast<uint8_t*>(q_col), static_cast<uint8_t*>(s_col), mpad, cus,
                                         stream),
@@ -265,6 +272,8 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
                          mxgg_workspace_size(G));
   if (!c.ok()) return finish(c);
   if (M == 0) return ok();
+  const bool w_mfma = is_mfma_layout(w_fmt);
+  w_fmt = (mxgg_format)format_bits(w_fmt);
   int cus = 0;
   c = device_checks(stream, {{a_q, "a_q"}, {a_s, "a_s"}, {w_q, "w_q"}, {w_s, "w_s"}, {out, "out"}}, &cus);
   if (!c.ok()) return finish(c);
@@ -299,14 +308,15 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
   p.lda = a8 ? K : K / 2;
   p.ldas = mx_scale_stride(M);    // A scales [K/32, R4(M)]
   p.ldb = K / 2;
-  p.ldbs = (int64_t)G * N;        // W scales [K/32, G*N]
+  p.ldbs = (int64_t)G * N;        // W scales [K/32, G*N] (MFMA layout: a 128-element
+                                  // group is 4 blocks of G*N bytes, N % 32 == 0)
   p.b_gstride = N * (K / 2);
-  p.bs_gstride = N;               // expert g's rows start at g*N
+  p.bs_gstride = w_mfma ? N * 4 : N;  // expert g's rows start at g*N (its units at byte g*N*4)
   p.ldc = N;
   p.n_out = (int32_t)N;
   p.kc = (int32_t)K;
   p.sp = make_splits(m_splits, G);
-  c = hip_status(launch_grouped_rows_mx(p, a8, false, cus, stream), "forward launch");
+  c = hip_status(launch_grouped_rows_mx(p, a8, false, w_mfma, cus, stream), "forward launch");
   return c.ok() ? ok() : finish(c);
 }
 
@@ -319,6 +329,8 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
                            mxgg_workspace_size(G));
   if (!c.ok()) return finish(c);
   if (M == 0) return ok();
+  const bool w_mfma = is_mfma_layout(fmt);
+  fmt = (mxgg_format)format_bits(fmt);
   int cus = 0;
   c = device_checks(stream, {{dy_q, "dy_q"}, {dy_s, "dy_s"}, {wcol_q, "wcol_q"}, {wcol_s, "wcol_s"}, {dx, "dx"}},
                     &cus);
@@ -350,10 +362,12 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
   p.lda = a8 ? N : N / 2;
   p.ldas = mx_scale_stride(M);    // dY scales [N/32, R4(M)]
   p.ldb = (int64_t)G * N / 2;     // W column-wise: [K, G*N/2]
-  p.ldbs = K;                     // its scales [G*N/32, K]
+  p.ldbs = K;                     // its scales [G*N/32, K] (MFMA layout: 4 blocks of K
+                                  // bytes per 128-element group)
   p.b_gstride = N / 2;            // expert g owns columns [g*N, (g+1)*N)
-  p.bs_gstride = N / 32 * K;      // ... and scale blocks [g*N/32, (g+1)*N/32)
-  c = hip_status(launch_grouped_rows_mx(p, a8, true, cus, stream), "dgrad launch");
+  p.bs_gstride = N / 32 * K;      // ... and scale blocks [g*N/32, (g+1)*N/32) (MFMA: the
+                                  // same byte offset, groups [g*N/128, (g+1)*N/128))
+  c = hip_status(launch_grouped_rows_mx(p, a8, true, w_mfma, cus, stream), "dgrad launch");
   return c.ok() ? ok() : finish(c);
 }
 

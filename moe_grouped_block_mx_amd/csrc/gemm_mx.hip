@@ -106,6 +106,7 @@ template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, int KIND_, i
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
   static constexpr int SCHED = SCHED_, BDIV = BDIV_;
+  static constexpr bool MFB = false;  // B's MX scales in the MFMA layout (MfmaB)
   static constexpr bool AFP8 = KIND_ != kA4W4, BFP8 = KIND_ == kBlkFp8 || KIND_ == kBlkP2 || KIND_ == kA8A8;
   static constexpr bool BLK = KIND_ == kBlkFp8;                     // per-128 partial promotion
   static constexpr bool F32S = KIND_ == kBlkFp8 || KIND_ == kBlkP2;  // fp32 row-major scales, 1 per 128
@@ -155,6 +156,18 @@ struct TileCfg {
                 "read-ahead schedule: two K steps per stage, MX scales, a 4+ stage ring");
 };
 
+// A configuration whose B operand (the weights) carries its MX scales in the
+// MFMA layout: 128-byte units of 32 rows x 4 blocks in which lane L of a
+// fragment finds its two K steps' scale bytes at 2L and 2L+1. A stage's B
+// scales are then (BN/32) whole units, contiguous in memory and copied as one
+// run (the block-major layout needs four runs of BN bytes), and a lane reads
+// both K steps' bytes with one 2-byte LDS read.
+template <class C>
+struct MfmaB : C {
+  static constexpr bool MFB = true;
+  static_assert(!C::F32S && C::BK == 128 && C::BN % 32 == 0, "MFMA-layout scales: 128-deep MX stages");
+};
+
 // The segment owning item t of a non-decreasing prefix offs[0..n] (offs[0] =
 // 0), from a cursor: a workgroup visits its tiles in increasing order (the
 // issuing side and the computing side each with its own cursor), so the
@@ -180,7 +193,9 @@ struct TileOps {
   const uint8_t* bs;
   int mrows, nrows;   // valid rows of A and B (>= 1)
   int srows_a, srows_b;  // MX: scale rows readable from as / bs in every
-                         // block (a multiple of 4, >= 4)
+                         // block (a multiple of 4, >= 4); MFMA-layout B:
+                         // bytes readable in every 128-element group (a
+                         // multiple of 128)
   int kc;             // contraction length (elements), multiple of 32
 };
 
@@ -247,9 +262,17 @@ __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64
         pl.sBlk[i] = byte / C::BM;
       } else if (byte < (C::BM + C::BN) * C::SB) {
         const int bb = byte - C::BM * C::SB;
-        const int r = bb % C::BN;
-        pl.sOff[i] = (uint32_t)(r < t.srows_b - 4 ? r : t.srows_b - 4);
-        pl.sBlk[i] = bb / C::BN;
+        if constexpr (C::MFB) {
+          // byte bb of the tile's contiguous run in the stage's group (the
+          // stage's first block, sBlk 0, addresses the group: ldbs is a
+          // block's share of the group stride)
+          pl.sOff[i] = (uint32_t)(bb < t.srows_b - 4 ? bb : t.srows_b - 4);
+          pl.sBlk[i] = 0;
+        } else {
+          const int r = bb % C::BN;
+          pl.sOff[i] = (uint32_t)(r < t.srows_b - 4 ? r : t.srows_b - 4);
+          pl.sBlk[i] = bb / C::BN;
+        }
       } else {
         pl.sOff[i] = 0;
         pl.sBlk[i] = kNoBlock;
@@ -551,10 +574,14 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[C::
     });
     unroll<C::FN>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      const int r = wn * C::WTN + j * 32 + l32;
-      const uint8_t* p = st + C::BS_OFF + h * C::BN + r;
-      if constexpr (C::KSTEPS == 2) sb[j] = p[0] | ((uint32_t)p[2 * C::BN] << 8);
-      else sb[j] = p[0];
+      if constexpr (C::MFB) {
+        sb[j] = *reinterpret_cast<const uint16_t*>(st + C::BS_OFF + (wn * C::FN + j) * 128 + (l32 + 32 * h) * 2);
+      } else {
+        const int r = wn * C::WTN + j * 32 + l32;
+        const uint8_t* p = st + C::BS_OFF + h * C::BN + r;
+        if constexpr (C::KSTEPS == 2) sb[j] = p[0] | ((uint32_t)p[2 * C::BN] << 8);
+        else sb[j] = p[0];
+      }
     });
   }
   unroll<C::KSTEPS>([&](auto kc_) {
@@ -666,7 +693,8 @@ __device__ __forceinline__ void read_kops(const uint8_t* st, KOps<C>& f, int wm,
   load_b_frags<C, KK>(st, f.b, wn, h, l32);
   unroll<C::FN>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    f.sb[j] = st[C::BS_OFF + (2 * KK + h) * C::BN + wn * C::WTN + j * 32 + l32];
+    if constexpr (C::MFB) f.sb[j] = st[C::BS_OFF + (wn * C::FN + j) * 128 + (l32 + 32 * h) * 2 + KK];
+    else f.sb[j] = st[C::BS_OFF + (2 * KK + h) * C::BN + wn * C::WTN + j * 32 + l32];
   });
 }
 
@@ -1072,11 +1100,13 @@ struct RowsSource {
     // MX scales are block-major ([blocks, rows]); blockwise scales row-major
     o.as = p.as + (C::F32S ? rw.row0 * p.ldas : rw.row0);
     o.b = p.b + (int64_t)q.g * p.b_gstride + (int64_t)col0 * p.ldb;
-    o.bs = p.bs + (int64_t)q.g * p.bs_gstride + (C::F32S ? (int64_t)(col0 / C::BDIV) * p.ldbs : (int64_t)col0);
+    o.bs = p.bs + (int64_t)q.g * p.bs_gstride +
+           (C::F32S ? (int64_t)(col0 / C::BDIV) * p.ldbs : C::MFB ? (int64_t)col0 * 4 : (int64_t)col0);
     o.mrows = rw.hi < C::BM ? rw.hi : C::BM;
     o.nrows = nleft < C::BN ? nleft : C::BN;
     o.srows_a = (int)(p.ldas - rw.row0);  // MX: the padded row count is the block stride
-    o.srows_b = nleft;
+    // MFMA layout: B's rows are padded to 32 (N and K are multiples of 32)
+    o.srows_b = C::MFB ? (nleft + 31) / 32 * 128 : nleft;
     o.kc = p.kc;
     return o;
   }
@@ -1353,7 +1383,10 @@ static hipError_t launch_rows(const RowsGemmParams& p, bool dgrad, int num_cus, 
   return launch_rows_as<C, false>(p, dgrad, num_cus, st);
 }
 
-hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, int num_cus, hipStream_t st) {
+hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, bool mfma_b, int num_cus,
+                                  hipStream_t st) {
+  if (mfma_b)
+    return a_fp8 ? launch_rows<MfmaB<CfgA8>>(p, dgrad, num_cus, st) : launch_rows<MfmaB<CfgA4>>(p, dgrad, num_cus, st);
   return a_fp8 ? launch_rows<CfgA8>(p, dgrad, num_cus, st) : launch_rows<CfgA4>(p, dgrad, num_cus, st);
 }
 

@@ -42,6 +42,15 @@ inline hipError_t ensure_dynamic_lds(const void* kernel, int bytes, hipStream_t 
 // Block stride of block-major MX scales: rows rounded up to a multiple of 4.
 __host__ __device__ inline int64_t mx_scale_stride(int64_t rows) { return rows > 0 ? (rows + 3) & ~(int64_t)3 : 0; }
 
+// MFMA layout of MX scales: rows padded to a multiple of 32 (r32), blocks in
+// groups of 4; unit (b/4, r/32) holds 128 bytes, and lane L = r%32 + 32*(b%2)
+// of a 32x32x64 scaled MFMA fragment finds the scales of its two 64-deep K
+// steps at bytes 2L and 2L+1 (j = (b%4)/2). Byte offset of row r, block b.
+__host__ __device__ inline int64_t mx_rows32(int64_t rows) { return rows > 0 ? (rows + 31) & ~(int64_t)31 : 0; }
+__host__ __device__ inline int64_t mfma_scale_offset(int64_t r, int64_t b, int64_t r32) {
+  return (b >> 2) * (r32 * 4) + (r >> 5) * 128 + ((r & 31) + 32 * (b & 1)) * 2 + ((b >> 1) & 1);
+}
+
 struct RowsGemmParams {
   const uint8_t* a;
   const uint8_t* as;
@@ -81,20 +90,24 @@ struct DeviceInfo {
   int num_cus;
 };
 
-hipError_t launch_quant_rowwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool fp8,
+// MX quantizers; mfma: scales in the MFMA layout (column-wise: every split a
+// multiple of 128), else block-major
+hipError_t launch_quant_rowwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool fp8, bool mfma,
                                    uint8_t* q, uint8_t* s, int num_cus, hipStream_t st);
 hipError_t launch_quant_dual_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
-                                bool fp8, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc, int64_t mpad,
+                                bool fp8, bool mfma, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc, int64_t mpad,
                                 int num_cus, hipStream_t st);
 hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
-                                   bool fp8, uint8_t* q, uint8_t* s, int64_t mpad, hipStream_t st);
+                                   bool fp8, bool mfma, uint8_t* q, uint8_t* s, int64_t mpad, hipStream_t st);
 
-// dgrad selects the input-gradient kernel symbol (same code as the forward's)
-// MX scales row-major [rows, blocks] -> block-major [blocks, R4] (or back)
-hipError_t launch_relayout_scales(const uint8_t* src, int64_t rows, int64_t blocks, bool to_block_major,
+// MX scales from one layout (mxgg_scale_layout value) into another
+hipError_t launch_relayout_scales(const uint8_t* src, int src_layout, int64_t rows, int64_t blocks, int dst_layout,
                                   uint8_t* dst, hipStream_t st);
 
-hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, int num_cus, hipStream_t st);
+// dgrad selects the input-gradient kernel symbol (same code as the forward's);
+// mfma_b: B's scales in the MFMA layout (bs_gstride then in bytes of it)
+hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, bool mfma_b, int num_cus,
+                                  hipStream_t st);
 // fp8: E4M3 operands on both sides (MXFP8), else E2M1 (MXFP4)
 hipError_t launch_grouped_wgrad_mx(const WgradParams& p, bool fp8, int num_cus, hipStream_t st);
 

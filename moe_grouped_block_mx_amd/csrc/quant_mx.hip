@@ -81,10 +81,22 @@ __device__ __forceinline__ void encode32_store(const uint32_t (&pairs)[16], int 
 // hold one 32-element block and reduce amax with two xor-shuffles. Each thread
 // keeps U = 4 consecutive rows' loads in flight before encoding (memory-level
 // parallelism), so the four scale bytes of a block's rows are adjacent in the
-// block-major scale layout and go out as one 4-byte store.
+// block-major scale layout and go out as one 4-byte store. In the MFMA layout
+// the lane of a 128-element group's first block collects the other three
+// blocks' words (lanes +4, +8, +12) and writes the group's 16 bytes of its
+// four rows as two 8-byte runs (K step pairs of fragment lanes r%32 and
+// r%32 + 32); the row groups then run to the 32-row padding, whose scales
+// are 0.
 // Grid: x over 64-chunk column groups, y over 4*U-row groups (grid-strided).
 // ---------------------------------------------------------------------------
-template <class F, int U>
+// bytes (a0 b0 a1 b1 | a2 b2 a3 b3) of two words
+__device__ __forceinline__ uint2 interleave_bytes(uint32_t a, uint32_t b) {
+  const uint32_t lo = (a & 0xffu) | (b & 0xffu) << 8 | (a & 0xff00u) << 8 | (b & 0xff00u) << 16;
+  const uint32_t hi = (a >> 16 & 0xffu) | (b >> 16 & 0xffu) << 8 | (a >> 24) << 16 | (b >> 24) << 24;
+  return make_uint2(lo, hi);
+}
+
+template <class F, int U, bool MFMA>
 __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __restrict__ x, int64_t ldx, int rows,
                                                             int cpr, uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ s, int64_t sld) {
@@ -94,7 +106,9 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
   const bool cvalid = c < cpr;
   const int64_t qrow_bytes = FP4 ? (int64_t)cpr * 4 : (int64_t)cpr * 8;
   static_assert(U == 4, "four rows per thread: one 4-byte scale store");
-  for (int rb = blockIdx.y * (4 * U); rb < rows; rb += gridDim.y * (4 * U)) {
+  // MFMA: sld is the 128-element group stride (padded rows x 4 bytes)
+  const int row_end = MFMA ? (int)(sld / 4) : rows;
+  for (int rb = blockIdx.y * (4 * U); rb < row_end; rb += gridDim.y * (4 * U)) {
     uint4 v[U];
     uint32_t sbytes = 0;
 #pragma unroll
@@ -121,10 +135,21 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
         *reinterpret_cast<uint2*>(q + (int64_t)r * qrow_bytes + (int64_t)c * 8) = encode8_fp8(wd, e, sc);
       sbytes |= (uint32_t)(e + 127) << (8 * u);
     }
-    // block-major scales [cols/32, sld], sld = rows rounded up to a multiple
-    // of 4: the thread's four rows are one aligned word (padding rows get 0)
     const int r0 = rb + w * U;
-    if (cvalid && (c & 3) == 0 && r0 < rows) *reinterpret_cast<uint32_t*>(s + (int64_t)(c >> 2) * sld + r0) = sbytes;
+    if constexpr (MFMA) {
+      const uint32_t s1 = (uint32_t)__shfl_down((int)sbytes, 4, 64);
+      const uint32_t s2 = (uint32_t)__shfl_down((int)sbytes, 8, 64);
+      const uint32_t s3 = (uint32_t)__shfl_down((int)sbytes, 12, 64);
+      if (cvalid && (c & 15) == 0 && r0 < row_end) {
+        uint8_t* u = s + (int64_t)(c >> 4) * sld + (r0 >> 5) * 128 + (r0 & 31) * 2;
+        *reinterpret_cast<uint2*>(u) = interleave_bytes(sbytes, s2);    // blocks 0, 2 (lane r%32)
+        *reinterpret_cast<uint2*>(u + 64) = interleave_bytes(s1, s3);   // blocks 1, 3 (lane r%32 + 32)
+      }
+    } else {
+      // block-major scales [cols/32, sld], sld = rows rounded up to a multiple
+      // of 4: the thread's four rows are one aligned word (padding rows get 0)
+      if (cvalid && (c & 3) == 0 && r0 < rows) *reinterpret_cast<uint32_t*>(s + (int64_t)(c >> 2) * sld + r0) = sbytes;
+    }
   }
 }
 
@@ -137,7 +162,7 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
 // a column's 64 (E2M1) or 128 (E4M3) bytes are written by the four waves
 // together.
 // ---------------------------------------------------------------------------
-template <class F>
+template <class F, bool MFMA>
 __global__ __launch_bounds__(256) void quant_colwise_segpad_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                    int64_t cols, const SplitArgs sp, int64_t mpad,
                                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
@@ -207,7 +232,10 @@ __global__ __launch_bounds__(256) void quant_colwise_segpad_kernel(const uint16_
 #pragma unroll
   for (int i = 0; i < 16; ++i) pairs[i] = vals[2 * i] | (vals[2 * i + 1] << 16);
   encode32_store<FP4>(pairs, e, sc, q + (c0 + c) * qld + (FP4 ? p0 / 2 : p0));
-  s[(p0 / 32) * cols + c0 + c] = (uint8_t)(e + 127);  // block-major: [mpad/32, cols]
+  if constexpr (MFMA)  // cols % 32 == 0: no padding rows
+    s[mfma_scale_offset(c0 + c, p0 / 32, cols)] = (uint8_t)(e + 127);
+  else
+    s[(p0 / 32) * cols + c0 + c] = (uint8_t)(e + 127);  // block-major: [mpad/32, cols]
 }
 
 // ---------------------------------------------------------------------------
@@ -258,7 +286,7 @@ struct DualCfg {
 // one XCD). The expert scan runs once per workgroup, and the loads of the next
 // tile are issued before the column-wise pass of the current one, so they
 // overlap it.
-template <class F, class D, bool XCD, int ORDER>
+template <class F, class D, bool XCD, int ORDER, bool MFMA>
 __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persistent(const uint16_t* __restrict__ x, int64_t ldx,
                                                                     int rows, int64_t cols, const SplitArgs sp,
                                                                     int64_t mpad, uint8_t* __restrict__ qr,
@@ -328,7 +356,7 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
   if (threadIdx.x < D::NB) map_blocks(t, 0);
   __syncthreads();
 
-  const int64_t srow_ld = mx_scale_stride(rows);
+  const int64_t srow_ld = MFMA ? mx_rows32(rows) : mx_scale_stride(rows);
   const int ch = threadIdx.x % D::CPR, rg = threadIdx.x / D::CPR;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t qld = FP4 ? mpad / 2 : mpad;
@@ -379,10 +407,17 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
       else
         *reinterpret_cast<uint2*>(qr + r * cols + c0 + ch * 8) = encode8_fp8(wd, e, sc);
       if ((ch & 3) == 0) {
-        uint8_t* sp_ = sr + ((c0 + ch * 8) >> 5) * srow_ld + r;
-        sp_[0] = (uint8_t)(e + 127);
-        if (r == rows - 1)  // the padding rows of the last word
-          for (int64_t k = 1; r + k < srow_ld; ++k) sp_[k] = 0;
+        const int64_t blk = (c0 + ch * 8) >> 5;
+        if constexpr (MFMA) {
+          sr[mfma_scale_offset(r, blk, srow_ld)] = (uint8_t)(e + 127);
+          if (r == rows - 1)  // the 32-row padding
+            for (int64_t k = r + 1; k < srow_ld; ++k) sr[mfma_scale_offset(k, blk, srow_ld)] = 0;
+        } else {
+          uint8_t* sp_ = sr + blk * srow_ld + r;
+          sp_[0] = (uint8_t)(e + 127);
+          if (r == rows - 1)  // the padding rows of the last word
+            for (int64_t k = 1; r + k < srow_ld; ++k) sp_[k] = 0;
+        }
       }
     }
     __syncthreads();  // tile in LDS; the next tile's block map visible
@@ -415,7 +450,10 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
             pairs[i] = j ? (w2[2 * i] >> 16) | (w2[2 * i + 1] & 0xffff0000u)
                          : (w2[2 * i] & 0xffffu) | (w2[2 * i + 1] << 16);
           encode32_store<FP4>(pairs, e, sc, qc + (c0 + c + j) * qld + (FP4 ? p0 / 2 : p0));
-          sc_[(p0 / 32) * cols + c0 + c + j] = (uint8_t)(e + 127);
+          if constexpr (MFMA)
+            sc_[mfma_scale_offset(c0 + c + j, p0 / 32, cols)] = (uint8_t)(e + 127);
+          else
+            sc_[(p0 / 32) * cols + c0 + c + j] = (uint8_t)(e + 127);
         }
       }
       }
@@ -445,7 +483,10 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
             pairs[i] = j ? (w2[2 * i] >> 16) | (w2[2 * i + 1] & 0xffff0000u)
                          : (w2[2 * i] & 0xffffu) | (w2[2 * i + 1] << 16);
           encode32_store<FP4>(pairs, e, sc, qc + (c0 + c + j) * qld + (FP4 ? p0 / 2 : p0));
-          sc_[(p0 / 32) * cols + c0 + c + j] = (uint8_t)(e + 127);
+          if constexpr (MFMA)
+            sc_[mfma_scale_offset(c0 + c + j, p0 / 32, cols)] = (uint8_t)(e + 127);
+          else
+            sc_[(p0 / 32) * cols + c0 + c + j] = (uint8_t)(e + 127);
         }
       }
     }
@@ -455,11 +496,12 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
   }
 }
 
-template <class D, bool XCD, int ORDER>
+template <class D, bool XCD, int ORDER, bool MFMA>
 hipError_t launch_quant_dual_persistent(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                         const SplitArgs& sp, bool fp8, uint8_t* qr, uint8_t* sr, uint8_t* qc,
                                         uint8_t* sc, int64_t mpad, int num_cus, hipStream_t st) {
-  auto kern = fp8 ? quant_dual_mx_persistent<E4M3Fmt, D, XCD, ORDER> : quant_dual_mx_persistent<E2M1Fmt, D, XCD, ORDER>;
+  auto kern = fp8 ? quant_dual_mx_persistent<E4M3Fmt, D, XCD, ORDER, MFMA>
+                  : quant_dual_mx_persistent<E2M1Fmt, D, XCD, ORDER, MFMA>;
   const hipError_t e = ensure_dynamic_lds((const void*)kern, D::LDS_BYTES, st);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((mpad + D::TR - 1) / D::TR) * ((cols + D::TC - 1) / D::TC);
@@ -480,37 +522,59 @@ using DualCfgProduct = DualCfg<128, 256, 512, 1, 1, 1>;
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_quant_rowwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool fp8,
-                                   uint8_t* q, uint8_t* s, int num_cus, hipStream_t st) {
-  (void)num_cus;
+template <bool MFMA>
+static void launch_rowwise_as(const uint16_t* x, int64_t rows, int64_t ldx, int cpr, bool fp8, uint8_t* q,
+                              uint8_t* s, int64_t sld, hipStream_t st) {
   constexpr int U = 4;
-  const int cpr = (int)(cols / 8);
-  const int64_t gy_need = (rows + 4 * U - 1) / (4 * U);
+  const int64_t row_end = MFMA ? sld / 4 : rows;
+  const int64_t gy_need = (row_end + 4 * U - 1) / (4 * U);
   const dim3 grid((unsigned)((cpr + 63) / 64), (unsigned)(gy_need < 65535 ? gy_need : 65535));
   if (fp8)
-    hipLaunchKernelGGL((quant_rowwise_kernel<E4M3Fmt, U>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q, s,
-                       mx_scale_stride(rows));
+    hipLaunchKernelGGL((quant_rowwise_kernel<E4M3Fmt, U, MFMA>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q,
+                       s, sld);
   else
-    hipLaunchKernelGGL((quant_rowwise_kernel<E2M1Fmt, U>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q, s,
-                       mx_scale_stride(rows));
+    hipLaunchKernelGGL((quant_rowwise_kernel<E2M1Fmt, U, MFMA>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q,
+                       s, sld);
+}
+
+hipError_t launch_quant_rowwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool fp8, bool mfma,
+                                   uint8_t* q, uint8_t* s, int num_cus, hipStream_t st) {
+  (void)num_cus;
+  const int cpr = (int)(cols / 8);
+  if (mfma) launch_rowwise_as<true>(x, rows, ldx, cpr, fp8, q, s, mx_rows32(rows) * 4, st);
+  else launch_rowwise_as<false>(x, rows, ldx, cpr, fp8, q, s, mx_scale_stride(rows), st);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_dual_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
-                                bool fp8, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc, int64_t mpad,
+                                bool fp8, bool mfma, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc, int64_t mpad,
                                 int num_cus, hipStream_t st) {
-  return launch_quant_dual_persistent<DualCfgProduct, false, 1>(x, rows, cols, ldx, sp, fp8, qr, sr, qc, sc, mpad,
-                                                                num_cus, st);
+  if (mfma)
+    return launch_quant_dual_persistent<DualCfgProduct, false, 1, true>(x, rows, cols, ldx, sp, fp8, qr, sr, qc, sc,
+                                                                        mpad, num_cus, st);
+  return launch_quant_dual_persistent<DualCfgProduct, false, 1, false>(x, rows, cols, ldx, sp, fp8, qr, sr, qc, sc,
+                                                                       mpad, num_cus, st);
 }
 
 hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
-                                   bool fp8, uint8_t* q, uint8_t* s, int64_t mpad, hipStream_t st) {
+                                   bool fp8, bool mfma, uint8_t* q, uint8_t* s, int64_t mpad, hipStream_t st) {
   (void)rows;
   const dim3 grid((unsigned)((mpad + 127) / 128), (unsigned)((cols + 63) / 64));
-  if (fp8)
-    hipLaunchKernelGGL(quant_colwise_segpad_kernel<E4M3Fmt>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, q, s);
-  else
-    hipLaunchKernelGGL(quant_colwise_segpad_kernel<E2M1Fmt>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, q, s);
+  if (mfma) {
+    if (fp8)
+      hipLaunchKernelGGL((quant_colwise_segpad_kernel<E4M3Fmt, true>), grid, dim3(256), 0, st, x, ldx, cols, sp, mpad,
+                         q, s);
+    else
+      hipLaunchKernelGGL((quant_colwise_segpad_kernel<E2M1Fmt, true>), grid, dim3(256), 0, st, x, ldx, cols, sp, mpad,
+                         q, s);
+  } else {
+    if (fp8)
+      hipLaunchKernelGGL((quant_colwise_segpad_kernel<E4M3Fmt, false>), grid, dim3(256), 0, st, x, ldx, cols, sp,
+                         mpad, q, s);
+    else
+      hipLaunchKernelGGL((quant_colwise_segpad_kernel<E2M1Fmt, false>), grid, dim3(256), 0, st, x, ldx, cols, sp,
+                         mpad, q, s);
+  }
   return hipGetLastError();
 }
 
@@ -519,49 +583,63 @@ hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols
 namespace mxgg {
 
 // ---------------------------------------------------------------------------
-// MX scale relayout: row-major u8 [rows, blocks] <-> block-major u8
-// [blocks, R4] (R4 = rows rounded up to 4, padding rows 0). A 64 x 64 byte
-// tile per workgroup goes through LDS so both sides are read and written
-// along their contiguous axis.
+// MX scale relayout between the three layouts: row-major u8 [rows, blocks],
+// block-major u8 [blocks, R4] and the MFMA layout u8 [blocks/4, R32/32, 64,
+// 2] (padding rows 0). A 64 x 64 (row, block) byte tile per workgroup goes
+// through LDS; the row-major side is read and written along blocks, the other
+// two along rows.
 // ---------------------------------------------------------------------------
-template <bool TO_BLOCK_MAJOR>
+enum { kLayBlock = 0, kLayRow = 1, kLayMfma = 2 };
+
+template <int L>
+__device__ __forceinline__ int64_t scale_offset(int64_t r, int64_t b, int64_t blocks, int64_t r4, int64_t r32) {
+  if constexpr (L == kLayRow) return r * blocks + b;
+  else if constexpr (L == kLayBlock) return b * r4 + r;
+  else return mfma_scale_offset(r, b, r32);
+}
+
+template <int SRC, int DST>
 __global__ __launch_bounds__(256) void relayout_scales_kernel(const uint8_t* __restrict__ src, int64_t rows,
-                                                              int64_t blocks, int64_t r4, uint8_t* __restrict__ dst) {
+                                                              int64_t blocks, int64_t r4, int64_t r32,
+                                                              uint8_t* __restrict__ dst) {
   __shared__ uint8_t t[64][65];
   const int64_t r0 = (int64_t)blockIdx.x * 64, b0 = (int64_t)blockIdx.y * 64;
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    if constexpr (TO_BLOCK_MAJOR) {  // read rows (blocks contiguous)
-      const int r = i >> 6, b = i & 63;
-      const int64_t rr = r0 + r, bb = b0 + b;
-      t[r][b] = (rr < rows && bb < blocks) ? src[rr * blocks + bb] : (uint8_t)0;
-    } else {                         // read blocks (rows contiguous)
-      const int b = i >> 6, r = i & 63;
-      const int64_t rr = r0 + r, bb = b0 + b;
-      t[r][b] = (rr < rows && bb < blocks) ? src[bb * r4 + rr] : (uint8_t)0;
-    }
+    const int r = SRC == kLayRow ? i >> 6 : i & 63, b = SRC == kLayRow ? i & 63 : i >> 6;
+    const int64_t rr = r0 + r, bb = b0 + b;
+    t[r][b] = (rr < rows && bb < blocks) ? src[scale_offset<SRC>(rr, bb, blocks, r4, r32)] : (uint8_t)0;
   }
   __syncthreads();
+  // rows written: the destination's padded row count (padding rows get 0)
+  const int64_t rend = DST == kLayRow ? rows : DST == kLayBlock ? r4 : r32;
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    if constexpr (TO_BLOCK_MAJOR) {  // write blocks (rows contiguous, padding rows 0)
-      const int b = i >> 6, r = i & 63;
-      const int64_t rr = r0 + r, bb = b0 + b;
-      if (bb < blocks && rr < r4) dst[bb * r4 + rr] = t[r][b];
-    } else {
-      const int r = i >> 6, b = i & 63;
-      const int64_t rr = r0 + r, bb = b0 + b;
-      if (rr < rows && bb < blocks) dst[rr * blocks + bb] = t[r][b];
-    }
+    const int r = DST == kLayRow ? i >> 6 : i & 63, b = DST == kLayRow ? i & 63 : i >> 6;
+    const int64_t rr = r0 + r, bb = b0 + b;
+    if (rr < rend && bb < blocks) dst[scale_offset<DST>(rr, bb, blocks, r4, r32)] = t[r][b];
   }
 }
 
-hipError_t launch_relayout_scales(const uint8_t* src, int64_t rows, int64_t blocks, bool to_block_major,
+static int layout_id(int mxgg_layout) {
+  return mxgg_layout == 0x100 ? kLayRow : mxgg_layout == 0x200 ? kLayMfma : kLayBlock;
+}
+
+template <int SRC, int DST>
+static void launch_relayout_as(const uint8_t* src, int64_t rows, int64_t blocks, uint8_t* dst, hipStream_t st) {
+  const int64_t r4 = mx_scale_stride(rows), r32 = mx_rows32(rows);
+  const dim3 grid((unsigned)((r32 + 63) / 64), (unsigned)((blocks + 63) / 64));
+  hipLaunchKernelGGL((relayout_scales_kernel<SRC, DST>), grid, dim3(256), 0, st, src, rows, blocks, r4, r32, dst);
+}
+
+hipError_t launch_relayout_scales(const uint8_t* src, int src_layout, int64_t rows, int64_t blocks, int dst_layout,
                                   uint8_t* dst, hipStream_t st) {
-  const int64_t r4 = mx_scale_stride(rows);
-  const dim3 grid((unsigned)((r4 + 63) / 64), (unsigned)((blocks + 63) / 64));
-  if (to_block_major)
-    hipLaunchKernelGGL(relayout_scales_kernel<true>, grid, dim3(256), 0, st, src, rows, blocks, r4, dst);
-  else
-    hipLaunchKernelGGL(relayout_scales_kernel<false>, grid, dim3(256), 0, st, src, rows, blocks, r4, dst);
+  const int s = layout_id(src_layout), d = layout_id(dst_layout);
+  if (s == kLayRow && d == kLayBlock) launch_relayout_as<kLayRow, kLayBlock>(src, rows, blocks, dst, st);
+  else if (s == kLayRow && d == kLayMfma) launch_relayout_as<kLayRow, kLayMfma>(src, rows, blocks, dst, st);
+  else if (s == kLayBlock && d == kLayRow) launch_relayout_as<kLayBlock, kLayRow>(src, rows, blocks, dst, st);
+  else if (s == kLayBlock && d == kLayMfma) launch_relayout_as<kLayBlock, kLayMfma>(src, rows, blocks, dst, st);
+  else if (s == kLayMfma && d == kLayRow) launch_relayout_as<kLayMfma, kLayRow>(src, rows, blocks, dst, st);
+  else if (s == kLayMfma && d == kLayBlock) launch_relayout_as<kLayMfma, kLayBlock>(src, rows, blocks, dst, st);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -37,10 +37,14 @@ inline Check fail(mxgg_status st, const char* fmt, long long a = 0, long long b 
 inline bool is_mx(mxgg_format f) { return f == MXGG_MXFP4 || f == MXGG_MXFP8; }
 inline bool valid_format(int f) { return f >= MXGG_MXFP4 && f <= MXGG_FP8_128x128_P2; }
 
-// A format argument with layout bits: the scales it describes are not in the
-// block-major layout the kernels read (or the bits are unknown). Refused by
-// name, so a caller's row-major scales are never read as block-major.
+// A format argument with layout bits: the scales it describes are not
+// block-major. Each entry point accepts the MFMA layout where it reads or
+// writes it and refuses every other layout by name, so a caller's scales are
+// never read in a layout they are not in.
 inline bool has_layout_bits(int f) { return (f & ~0xFF) != 0; }
+inline int layout_bits(int f) { return f & ~0xFF; }
+inline int format_bits(int f) { return f & 0xFF; }
+inline bool is_mfma_layout(int f) { return layout_bits(f) == MXGG_LAYOUT_MFMA; }
 // The power-of-two blockwise formats share their base format's layout.
 inline bool is_p2(int f) { return f == MXGG_FP8_1x128_P2 || f == MXGG_FP8_128x128_P2; }
 inline int base_format(int f) {
@@ -77,16 +81,37 @@ constexpr int64_t kMaxSplit = ((int64_t)1 << 31) - 1;
 
 // Padded row count; callers have checked 0 <= m[g] <= kMaxSplit, so neither
 // the rounding nor the sum (at most 512 terms) can overflow.
-inline Check check_layout(int f, const char* what) {
+// mfma_ok: the operand's MX scales may be in the MFMA layout.
+inline Check check_layout(int f, const char* what, bool mfma_ok = false) {
   if (!has_layout_bits(f)) return Check{};
-  if ((f & ~0xFF) == MXGG_LAYOUT_ROW_MAJOR && is_mx((mxgg_format)(f & 0xFF))) {
+  const bool mx = is_mx((mxgg_format)format_bits(f));
+  if (mx && layout_bits(f) == MXGG_LAYOUT_MFMA) {
+    if (mfma_ok) return Check{};
     Check r;
     r.st = MXGG_ERR_FORMAT;
-    r.msg = std::string(what) + ": row-major MX scales are not accepted (the kernels read block-major "
-            "scales); convert them with mxgg_mx_scales_relayout";
+    r.msg = std::string(what) + ": MFMA-layout scales are read only for the weights (the forward's w_s and "
+            "the input gradient's wcol_s); this operand's scales must be block-major";
+    return r;
+  }
+  if (mx && layout_bits(f) == MXGG_LAYOUT_ROW_MAJOR) {
+    Check r;
+    r.st = MXGG_ERR_FORMAT;
+    r.msg = std::string(what) + ": row-major MX scales are not accepted (the kernels read block-major or "
+            "MFMA-layout scales); convert them with mxgg_mx_scales_relayout";
     return r;
   }
   return fail(MXGG_ERR_FORMAT, "format 0x%llx: unknown layout bits or a layout on a blockwise format", f);
+}
+
+// MFMA-layout column scales: every expert segment starts a 128-element unit.
+inline Check check_mfma_splits(const int64_t* m, int32_t G, const char* what) {
+  for (int32_t g = 0; g < G; ++g)
+    if (m[g] % 128) {
+      Check r = fail(MXGG_ERR_SPLITS, "m_splits[%lld] = %lld is not a multiple of 128", g, m[g]);
+      r.msg = std::string(what) + ": MFMA-layout column scales need every split a multiple of 128; " + r.msg;
+      return r;
+    }
+  return Check{};
 }
 
 inline int64_t segpad_rows(const int64_t* m, int32_t G, int pad) {
@@ -120,8 +145,11 @@ inline Check check_ptr(const void* p, bool nonzero, const char* name) {
 
 inline Check validate_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                        const void* q, const void* scales) {
-  MXGG_TRY(check_layout(fmt, "quantize_rowwise"));
+  MXGG_TRY(check_layout(fmt, "quantize_rowwise", true));
+  const bool mfma = is_mfma_layout(fmt);
+  fmt = format_bits(fmt);
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
+  if (mfma && cols % 128) return fail(MXGG_ERR_SHAPE, "cols=%lld: MFMA-layout scales need cols %% 128 == 0", cols);
   if (rows < 0 || cols <= 0) return fail(MXGG_ERR_SHAPE, "rows=%lld cols=%lld", rows, cols);
   const mxgg_format f = (mxgg_format)fmt;
   const int blk = is_mx(f) ? 32 : 128;
@@ -142,7 +170,9 @@ inline Check validate_quantize_rowwise(const void* x, int64_t rows, int64_t cols
 
 inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, const int64_t* m,
                                        int32_t G, int fmt, const void* q, const void* scales, int64_t mpad) {
-  MXGG_TRY(check_layout(fmt, "quantize_colwise"));
+  MXGG_TRY(check_layout(fmt, "quantize_colwise", true));
+  const bool mfma = is_mfma_layout(fmt);
+  fmt = format_bits(fmt);
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
   const mxgg_format f = (mxgg_format)fmt;
   if (f == MXGG_FP8_128x128) return fail(MXGG_ERR_FORMAT, "128x128 blocks have no column-wise form");
@@ -156,6 +186,7 @@ inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols
   if (ldx % 8) return fail(MXGG_ERR_ALIGN, "ldx=%lld not a multiple of 8 elements", ldx);
   if (rows >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SHAPE, "rows=%lld >= 2^31", rows);
   MXGG_TRY(check_splits(m, G, rows, "x"));
+  if (mfma) MXGG_TRY(check_mfma_splits(m, G, "quantize_colwise"));
   const int64_t need = segpad_rows(m, G, segpad_multiple(f));
   if (mpad != need) return fail(MXGG_ERR_SHAPE, "mpad=%lld but the padded row count is %lld", mpad, need);
   if (mpad >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SHAPE, "mpad=%lld >= 2^31", mpad);
@@ -169,9 +200,10 @@ inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols
 inline Check validate_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, const int64_t* m,
                                     int32_t G, int fmt, const void* q_row, const void* s_row, const void* q_col,
                                     const void* s_col, int64_t mpad) {
-  MXGG_TRY(check_layout(fmt, "quantize_dual"));
-  if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
-  if (!is_mx((mxgg_format)fmt) && fmt != MXGG_FP8_1x128)
+  MXGG_TRY(check_layout(fmt, "quantize_dual", true));
+  const int f0 = format_bits(fmt);
+  if (!valid_format(f0)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
+  if (!is_mx((mxgg_format)f0) && f0 != MXGG_FP8_1x128)
     return fail(MXGG_ERR_FORMAT, "the dual quantizer takes MX formats and MXGG_FP8_1x128 (got %lld)", fmt);
   MXGG_TRY(validate_quantize_rowwise(x, rows, cols, ldx, fmt, q_row, s_row));
   MXGG_TRY(validate_quantize_colwise(x, rows, cols, ldx, m, G, fmt, q_col, s_col, mpad));
@@ -194,8 +226,11 @@ inline Check validate_fwd(const void* a_q, const void* a_s, int a_fmt, const voi
                           const int64_t* m, int32_t G, int64_t M, int64_t N, int64_t K, const void* out,
                           const void* ws, size_t ws_bytes, size_t ws_need) {
   MXGG_TRY(check_layout(a_fmt, "fwd A"));
-  MXGG_TRY(check_layout(w_fmt, "fwd W"));
+  MXGG_TRY(check_layout(w_fmt, "fwd W", true));
+  const bool w_mfma = is_mfma_layout(w_fmt);
+  w_fmt = format_bits(w_fmt);
   if (!valid_format(a_fmt) || !valid_format(w_fmt)) return fail(MXGG_ERR_FORMAT, "unknown format");
+  if (w_mfma && K % 128) return fail(MXGG_ERR_SHAPE, "K=%lld: MFMA-layout weight scales need K %% 128 == 0", K);
   const bool a4w4 = a_fmt == MXGG_MXFP4 && w_fmt == MXGG_MXFP4;
   const bool a8w4 = a_fmt == MXGG_MXFP8 && w_fmt == MXGG_MXFP4;
   const bool blk = a_fmt == MXGG_FP8_1x128 && w_fmt == MXGG_FP8_128x128;
@@ -218,8 +253,11 @@ inline Check validate_fwd(const void* a_q, const void* a_s, int a_fmt, const voi
 inline Check validate_dgrad(const void* dy_q, const void* dy_s, const void* wc_q, const void* wc_s, int fmt,
                             const int64_t* m, int32_t G, int64_t M, int64_t N, int64_t K, const void* dx,
                             const void* ws, size_t ws_bytes, size_t ws_need) {
-  MXGG_TRY(check_layout(fmt, "dgrad"));
+  MXGG_TRY(check_layout(fmt, "dgrad", true));
+  const bool w_mfma = is_mfma_layout(fmt);
+  fmt = format_bits(fmt);
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
+  if (w_mfma && N % 128) return fail(MXGG_ERR_SHAPE, "N=%lld: MFMA-layout weight scales need N %% 128 == 0", N);
   // fmt is dY's format: MXFP4 (a4w4) or MXFP8 (a8w4) with W column-wise in
   // MXFP4; FP8_1x128 with the transposed 128x128 weight blocks
   if (fmt != MXGG_MXFP4 && fmt != MXGG_MXFP8 && fmt != MXGG_FP8_1x128)
@@ -299,14 +337,17 @@ inline Check validate_wgrad(const void* dy_q, const void* dy_s, const void* x_q,
   return Check{};
 }
 
-// Scale relayout: row-major <-> block-major MX scales.
+// Scale relayout between any two of the MX scale layouts.
+inline bool known_layout(int l) {
+  return l == MXGG_LAYOUT_ROW_MAJOR || l == MXGG_LAYOUT_BLOCK_MAJOR || l == MXGG_LAYOUT_MFMA;
+}
 inline Check validate_relayout(const void* src, int src_layout, int64_t rows, int64_t blocks, const void* dst,
                                int dst_layout) {
-  const bool known = (src_layout == MXGG_LAYOUT_ROW_MAJOR || src_layout == MXGG_LAYOUT_BLOCK_MAJOR) &&
-                     (dst_layout == MXGG_LAYOUT_ROW_MAJOR || dst_layout == MXGG_LAYOUT_BLOCK_MAJOR);
-  if (!known || src_layout == dst_layout)
-    return fail(MXGG_ERR_FORMAT, "relayout from 0x%llx to 0x%llx: need one row-major and one block-major layout",
-                src_layout, dst_layout);
+  if (!known_layout(src_layout) || !known_layout(dst_layout) || src_layout == dst_layout)
+    return fail(MXGG_ERR_FORMAT, "relayout from 0x%llx to 0x%llx: need two different known layouts", src_layout,
+                dst_layout);
+  if ((src_layout == MXGG_LAYOUT_MFMA || dst_layout == MXGG_LAYOUT_MFMA) && blocks % 4)
+    return fail(MXGG_ERR_SHAPE, "blocks=%lld: the MFMA layout needs a multiple of 4 blocks", blocks);
   // 64 blocks per workgroup on the grid's y axis
   if (rows < 0 || rows >= ((int64_t)1 << 31) || blocks <= 0 || blocks > (int64_t)65535 * 64)
     return fail(MXGG_ERR_SHAPE, "rows=%lld blocks=%lld (0 <= rows < 2^31, 0 < blocks <= 4194240)", rows, blocks);

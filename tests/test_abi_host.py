@@ -229,6 +229,7 @@ def test_wgrad_rejects_splits_at_or_above_2_31():
 
 
 ROW_MAJOR = 0x100
+MFMA = 0x200
 
 
 def _header_enum(name):
@@ -239,8 +240,9 @@ def _header_enum(name):
 
 
 def test_scale_layout_enum_declared():
-    assert _header_enum("mxgg_scale_layout") == {"MXGG_LAYOUT_BLOCK_MAJOR": 0, "MXGG_LAYOUT_ROW_MAJOR": ROW_MAJOR}
-    assert mx.LAYOUT_ROW_MAJOR == ROW_MAJOR and mx.LAYOUT_BLOCK_MAJOR == 0
+    assert _header_enum("mxgg_scale_layout") == {"MXGG_LAYOUT_BLOCK_MAJOR": 0, "MXGG_LAYOUT_ROW_MAJOR": ROW_MAJOR,
+                                                 "MXGG_LAYOUT_MFMA": MFMA}
+    assert mx.LAYOUT_ROW_MAJOR == ROW_MAJOR and mx.LAYOUT_BLOCK_MAJOR == 0 and mx.LAYOUT_MFMA == MFMA
     # layout bits sit above every format value
     assert max(_header_enum("mxgg_format").values()) < 0x100
 
@@ -262,16 +264,56 @@ def test_row_major_scales_refused_by_every_entry_point():
         assert "relayout" in last(), (name, last())
     # MXFP8 with row-major scales too; unknown layout bits; a layout on a blockwise format
     assert fwd(m, 2, 32, a_fmt=1 | ROW_MAJOR) == 4
-    assert fwd(m, 2, 32, a_fmt=0x200) == 4
+    assert fwd(m, 2, 32, a_fmt=0x300) == 4
     assert L.mxgg_quantize_rowwise(P, 128, 128, 128, 2 | ROW_MAJOR, 0, P, P, NULL) == 4
     # an empty batch is still refused: validation runs before the early return
     assert fwd(splits(0, 0), 2, 0, a_fmt=f, a=NULL, out=NULL) == 4
 
 
+def test_mfma_layout_accepted_only_for_weight_scales():
+    # the MFMA layout is read for the weights' scales (forward w_s, input
+    # gradient wcol_s) and written by the MX quantizers; activation and
+    # gradient scales and both weight-gradient operands refuse it
+    m = splits(32, 0)
+    refused = {
+        "fwd A": lambda: fwd(m, 2, 32, K=128, a_fmt=MFMA),
+        "fwd A a8w4": lambda: fwd(m, 2, 32, K=128, a_fmt=1 | MFMA),
+        "wgrad": lambda: L.mxgg_grouped_wgrad(P, P, P, P, MFMA, m, 2, 64, 64, 32, P, 0, 1, NULL, 0, NULL),
+        "wgrad fp8": lambda: L.mxgg_grouped_wgrad(P, P, P, P, 1 | MFMA, m, 2, 64, 64, 32, P, 0, 1, NULL, 0, NULL),
+    }
+    for name, call in refused.items():
+        assert call() == 4, name
+        assert "block-major" in last(), (name, last())
+    # a layout on a blockwise format stays unknown
+    assert fwd(m, 2, 32, K=128, N=128, a_fmt=2, w_fmt=3 | MFMA) == 4
+    assert L.mxgg_quantize_rowwise(P, 128, 128, 128, 2 | MFMA, 0, P, P, NULL) == 4
+    # accepted: validation passes (no GPU here, so the device check fails)
+    assert fwd(m, 2, 32, K=128, w_fmt=MFMA) == 9
+    assert fwd(m, 2, 32, K=128, a_fmt=1, w_fmt=MFMA) == 9                  # a8w4
+    assert L.mxgg_grouped_dgrad(P, P, P, P, MFMA, m, 2, 32, 128, 64, P, NULL, 0, NULL) == 9
+    assert L.mxgg_quantize_rowwise(P, 32, 128, 128, MFMA, 0, P, P, NULL) == 9
+    assert L.mxgg_quantize_colwise_segpad(P, 256, 64, 64, splits(128, 0, 128), 3, 1 | MFMA, 0, P, P, 256,
+                                          NULL) == 9
+    assert L.mxgg_quantize_dual(P, 256, 128, 128, splits(128, 128), 2, MFMA, 0, P, P, P, P, 256, NULL) == 9
+    # the shapes it needs: K % 128 (forward), N % 128 (input gradient), cols
+    # % 128 (row-wise), every split a multiple of 128 (column-wise)
+    assert fwd(m, 2, 32, K=96, w_fmt=MFMA) == 2 and "128" in last()
+    assert L.mxgg_grouped_dgrad(P, P, P, P, MFMA, m, 2, 32, 96, 64, P, NULL, 0, NULL) == 2
+    assert L.mxgg_quantize_rowwise(P, 32, 96, 96, MFMA, 0, P, P, NULL) == 2
+    assert L.mxgg_quantize_colwise_segpad(P, 160, 64, 64, splits(128, 32), 2, MFMA, 0, P, P, 160, NULL) == 3
+    assert "multiple of 128" in last()
+    assert L.mxgg_quantize_dual(P, 160, 128, 128, splits(32, 128), 2, MFMA, 0, P, P, P, P, 160, NULL) == 3
+
+
 def test_relayout_validation():
     R, B = 0x100, 0x000
     assert L.mxgg_mx_scales_relayout(P, R, 10, 4, P, R, NULL) == 4          # same layout
+    assert L.mxgg_mx_scales_relayout(P, MFMA, 10, 4, P, MFMA, NULL) == 4
     assert L.mxgg_mx_scales_relayout(P, 0x300, 10, 4, P, B, NULL) == 4     # unknown layout
+    assert L.mxgg_mx_scales_relayout(P, MFMA, 10, 6, P, B, NULL) == 2      # MFMA: blocks % 4
+    assert L.mxgg_mx_scales_relayout(P, R, 10, 6, P, MFMA, NULL) == 2
+    for src, dst in ((R, MFMA), (MFMA, R), (B, MFMA), (MFMA, B)):
+        assert L.mxgg_mx_scales_relayout(P, src, 10, 8, P, dst, NULL) == 9  # valid; no GPU here
     assert L.mxgg_mx_scales_relayout(P, R, -1, 4, P, B, NULL) == 2
     assert L.mxgg_mx_scales_relayout(P, R, 10, 0, P, B, NULL) == 2
     assert L.mxgg_mx_scales_relayout(P, R, 10, 65535 * 64 + 1, P, B, NULL) == 2

@@ -29,6 +29,11 @@ EXPECTED = {
     "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb1E": [5],
     "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [5],
     "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [5],
+    # the same with the weights' scales in the MFMA layout
+    "grouped_fwd_kernelINS_5MfmaBINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEELb1E": [5],
+    "grouped_dgrad_kernelINS_5MfmaBINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEELb1E": [5],
+    "grouped_fwd_kernelINS_5MfmaBINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEELb0E": [5],
+    "grouped_dgrad_kernelINS_5MfmaBINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEELb0E": [5],
     # a4w4 weight gradient: 4 waves, same ring, DPS 10 (every output mode)
     "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi2ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [10],
     # power-of-two blockwise forward / input gradient: 64-deep stages, 3-stage ring, DPS 6
