@@ -85,6 +85,8 @@ def parse():
                          "a8w4_bwd: its input and weight gradients; blockwise: the blockwise FP8 forward + "
                          "weight gradient; blockwise_dgrad: the blockwise input gradient")
     ap.add_argument("--copy-only", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--weight-scales", default="block", choices=["block", "mfma"],
+                    help="fc1: the weights' MX scales block-major or in the MFMA layout")
     ap.add_argument("--separate-quant", action="store_true",
                     help="fc1: single-output quantizers instead of the dual-output ones")
     ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
@@ -356,7 +358,7 @@ def cpu_baseline(seconds_hint=20.0):
                       f"NumPy fp64 oracle (OpenBLAS {threads} threads, host has {os.cpu_count()} cpus)"}
 
 
-def build_workload(name, dev, separate_quant=False):
+def build_workload(name, dev, separate_quant=False, weight_scales="block"):
     """Device inputs, the op list and the per-op algorithmic work of one step.
 
     Returns dict(ops=[(name, kind, fn)], bytes_alg={op: bytes}, flops={op: flops},
@@ -393,10 +395,16 @@ def build_workload(name, dev, separate_quant=False):
         # rounded up to a multiple of 4]
         R4 = mxg.mx_scale_stride(M)
         aq, as_ = torch.empty((M, K // 2), **u8), torch.empty((K // 32, R4), **u8)
-        wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty((K // 32, G * N), **u8)
+        # the weights' scales block-major, or in the MFMA layout ([K/128,
+        # G*N*4] row-wise, [G*N/128, K*4] column-wise)
+        lay = mxg.LAYOUT_MFMA if weight_scales == "mfma" else mxg.LAYOUT_BLOCK_MAJOR
+        wfmt = mxg.MXFP4 | lay
+        ws_shape = (K // 128, G * N * 4) if lay else (K // 32, G * N)
+        wcs_shape = (G * N // 128, K * 4) if lay else (G * N // 32, K)
+        wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty(ws_shape, **u8)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         dq, ds = torch.empty((M, N // 2), **u8), torch.empty((N // 32, R4), **u8)
-        wcq, wcs = torch.empty((K, G * N // 2), **u8), torch.empty((G * N // 32, K), **u8)
+        wcq, wcs = torch.empty((K, G * N // 2), **u8), torch.empty(wcs_shape, **u8)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         dcq, dcs = torch.empty((N, mpad // 2), **u8), torch.empty((mpad // 32, N), **u8)
         xcq, xcs = torch.empty((K, mpad // 2), **u8), torch.empty((mpad // 32, K), **u8)
@@ -404,22 +412,22 @@ def build_workload(name, dev, separate_quant=False):
         dual_ops = [
             ("quant_X_dual", "quant", lambda: mxg.quantize_dual(a, sp, "mxfp4", q_row=aq, s_row=as_, q_col=xcq,
                                                                 s_col=xcs)),
-            ("quant_W_dual", "quant", lambda: mxg.quantize_dual(w, wsp, "mxfp4", q_row=wq, s_row=ws, q_col=wcq,
+            ("quant_W_dual", "quant", lambda: mxg.quantize_dual(w, wsp, wfmt, q_row=wq, s_row=ws, q_col=wcq,
                                                                 s_col=wcs)),
-            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, out=y)),
+            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, w_fmt=wfmt, out=y)),
             ("quant_dY_dual", "quant", lambda: mxg.quantize_dual(dy, sp, "mxfp4", q_row=dq, s_row=ds, q_col=dcq,
                                                                  s_col=dcs)),
-            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, dx=dx)),
+            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, fmt=wfmt, dx=dx)),
             ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, main_grad,
                                                         accumulate=True)),
         ]
         ops = [
             ("quant_A_row", "quant", lambda: mxg.quantize_rowwise(a, "mxfp4", q=aq, scales=as_)),
-            ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, "mxfp4", q=wq, scales=ws)),
-            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, out=y)),
+            ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, wfmt, q=wq, scales=ws)),
+            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, w_fmt=wfmt, out=y)),
             ("quant_dY_row", "quant", lambda: mxg.quantize_rowwise(dy, "mxfp4", q=dq, scales=ds)),
-            ("quant_W_col", "quant", lambda: mxg.quantize_colwise_segpad(w, [N] * G, "mxfp4", q=wcq, scales=wcs)),
-            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, dx=dx)),
+            ("quant_W_col", "quant", lambda: mxg.quantize_colwise_segpad(w, [N] * G, wfmt, q=wcq, scales=wcs)),
+            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, fmt=wfmt, dx=dx)),
             ("quant_dY_col", "quant", lambda: mxg.quantize_colwise_segpad(dy, sp, "mxfp4", q=dcq, scales=dcs)),
             ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "mxfp4", q=xcq, scales=xcs)),
             ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, main_grad,
@@ -441,6 +449,7 @@ def build_workload(name, dev, separate_quant=False):
             ops = dual_ops
         config = {"workload": "MoE FC1 a4w4 training step (fwd+dgrad+wgrad with MX quantization)",
                   "quantizers": "separate" if separate_quant else "dual-output",
+                  "weight_scales": "MFMA layout" if lay else "block-major",
                   "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz,
                   "max_split": int(sp.max()), "mpad": mpad, "routing": "Dirichlet(0.5), 3 zeroed, seed 0"}
         return dict(ops=ops, bytes_alg=bytes_alg, flops={"fwd": 2.0 * M * N * K, "dgrad": 2.0 * M * N * K,
@@ -672,7 +681,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    W = build_workload(args.workload, dev, args.separate_quant)
+    W = build_workload(args.workload, dev, args.separate_quant, args.weight_scales)
     if args.passes != "all":
         keep = {"fwd": {"quant_A_row", "quant_W_row", "quant_X_dual", "quant_W_dual", "fwd"},
                 "dgrad": {"quant_dY_row", "quant_W_col", "quant_dY_dual", "quant_W_dual", "dgrad"},

@@ -140,9 +140,10 @@ struct TileCfg {
   static constexpr int DSB = F32S ? BS_BYTES / (NW * 256) : 0;
   static constexpr int DPS = DA + DB + DSA + DSB;
   static constexpr int EPI_BYTES = 16 * 36 * 4;  // per-wave epilogue scratch (16 rows x 32 fp32, padded)
-  // SCHED 7 keeps the epilogue scratch in the ring slot of the tile's last
-  // stage (free until the next tile's first DMA into it); the others append it
-  static constexpr bool EPI_IN_RING = SCHED == 7;
+  // SCHED 7 and 8 keep the epilogue scratch in the ring slot of the tile's
+  // last stage (free until the next tile's first DMA into it); the others
+  // append it
+  static constexpr bool EPI_IN_RING = SCHED == 7 || SCHED == 8;
   static constexpr int EPI_OFF = STAGES * STAGE_BYTES;
   static constexpr int SMEM_BYTES = EPI_OFF + (EPI_IN_RING ? 0 : NW * EPI_BYTES);
   static_assert(A_BYTES % (NW * 1024) == 0 && B_BYTES % (NW * 1024) == 0, "chunk DMA split");
@@ -154,6 +155,8 @@ struct TileCfg {
   static_assert(STAGE_BYTES % 16 == 0, "stage alignment");
   static_assert(SCHED != 7 || (KSTEPS == 2 && !F32S && STAGES >= 4 && NW * EPI_BYTES <= STAGE_BYTES),
                 "read-ahead schedule: two K steps per stage, MX scales, a 4+ stage ring");
+  static_assert(SCHED != 8 || (KSTEPS == 1 && !BLK && STAGES >= 4 && NW * EPI_BYTES <= STAGE_BYTES),
+                "stage read-ahead schedule: one K step per stage, scales applied by the MFMA, a 4+ stage ring");
 };
 
 // A configuration whose B operand (the weights) carries its MX scales in the
@@ -430,6 +433,81 @@ __device__ __forceinline__ void plan_fast(FastPlan<C>& fp, const DmaPlan<C>& pl,
   });
 }
 
+// The same issue with no per-lane state kept across the loop: every stage
+// recomputes the lane offsets from the lane index and the tile's uniform
+// extents (a few vector ALU operations per DMA, beside 16 MFMAs of 64
+// cycles), for the stage read-ahead loop, whose accumulators and operand
+// sets leave no registers for ten offsets (fp32 row scales only).
+template <class C>
+struct LeanPlan {
+  const uint8_t *a, *b, *as, *bs;  // the tile's bases (wave-uniform)
+  int mlast, nlast;                // last valid row of the A / B tile
+};
+
+template <class C>
+__device__ __forceinline__ void plan_lean(LeanPlan<C>& lp, const TileOps& t) {
+  static_assert(C::F32S, "lean issue: fp32 row scales");
+  lp.a = uniform_ptr(t.a);
+  lp.b = uniform_ptr(t.b);
+  lp.as = uniform_ptr(t.as);
+  lp.bs = uniform_ptr(t.bs);
+  lp.mlast = __builtin_amdgcn_readfirstlane(t.mrows - 1);
+  lp.nlast = __builtin_amdgcn_readfirstlane(t.nrows - 1);
+}
+
+// DMAs [Q0, Q1) of stage s in the order: A chunks, A scales, B scales, B
+// chunks (all of them for Q0 = 0, Q1 = DPS).
+template <class C, int Q0 = 0, int Q1 = C::DPS>
+__device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, uint8_t* st, int w, int lane, int lda,
+                                                 int ldb, int ldas, int ldbs) {
+  // rows per chunk DMA instruction over all waves: the swizzle of a lane's
+  // chunk is the same in every instruction
+  static_assert((C::NW * 1024 / C::RBA) % 16 == 0 && (C::NW * 1024 / C::RBB) % 16 == 0, "uniform swizzle");
+  constexpr int QSA = C::DA, QSB = QSA + C::DSA, QB = QSB + C::DSB;
+  uint32_t ln = (uint32_t)lane;
+  asm volatile("" : "+v"(ln));  // recomputed here, not hoisted out of the loop
+  const uint32_t wu = (uint32_t)w;
+  const uint8_t* abase = lp.a + s * C::RBA;
+  unroll<C::DA>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i >= Q0 && i < Q1) {
+      const uint32_t o = (i * C::NW + wu) * 1024 + ln * 16;
+      const int r = (int)(o / C::RBA);
+      const int c = swz<C::CPA>(r, (int)(o % C::RBA) / 16);
+      const int rr = r < lp.mlast ? r : lp.mlast;
+      dma16(abase + (uint32_t)(rr * lda + c * 16), st + C::A_OFF + (i * C::NW + w) * 1024);
+    }
+  });
+  const int boff = (s * C::BK / 128) * 4;  // the stage's 128-element block
+  unroll<C::DSA>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (QSA + i >= Q0 && QSA + i < Q1) {
+      const int d = (int)((i * C::NW + wu) * 64 + ln);
+      const int rr = d < lp.mlast ? d : lp.mlast;
+      dma4(lp.as + boff + (uint32_t)(rr * ldas), st + C::AS_OFF + (i * C::NW + w) * 256);
+    }
+  });
+  unroll<C::DSB>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (QSB + i >= Q0 && QSB + i < Q1) {
+      const int d = (int)((i * C::NW + wu) * 64 + ln);
+      const int rr = d < lp.nlast ? d : lp.nlast;
+      dma4(lp.bs + boff + (uint32_t)((rr / C::BDIV) * ldbs), st + C::BS_OFF + (i * C::NW + w) * 256);
+    }
+  });
+  const uint8_t* bbase = lp.b + s * C::RBB;
+  unroll<C::DB>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (QB + i >= Q0 && QB + i < Q1) {
+      const uint32_t o = (i * C::NW + wu) * 1024 + ln * 16;
+      const int r = (int)(o / C::RBB);
+      const int c = swz<C::CPB>(r, (int)(o % C::RBB) / 16);
+      const int rr = r < lp.nlast ? r : lp.nlast;
+      dma16(bbase + (uint32_t)(rr * ldb + c * 16), st + C::B_OFF + (i * C::NW + w) * 1024);
+    }
+  });
+}
+
 // Stage s of tile t into ring slot st (PART as for issue_stage). A dummy
 // stage re-reads stage 0 of the last planned tile (or the zero page before
 // any): its data is never consumed, the DMAs only keep the counts constant.
@@ -688,13 +766,20 @@ __device__ __forceinline__ void read_kops(const uint8_t* st, KOps<C>& f, int wm,
       const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r, 2 * KK + h) * 16);
       f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
     }
-    f.sa[i] = st[C::AS_OFF + (2 * KK + h) * C::BM + r];
+    if constexpr (C::F32S)  // power-of-two fp32 row scale: its exponent field is the UE8M0 code
+      f.sa[i] = (reinterpret_cast<const uint32_t*>(st + C::AS_OFF)[r] >> 23) & 0xffu;
+    else
+      f.sa[i] = st[C::AS_OFF + (2 * KK + h) * C::BM + r];
   });
   load_b_frags<C, KK>(st, f.b, wn, h, l32);
   unroll<C::FN>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    if constexpr (C::MFB) f.sb[j] = st[C::BS_OFF + (wn * C::FN + j) * 128 + (l32 + 32 * h) * 2 + KK];
-    else f.sb[j] = st[C::BS_OFF + (2 * KK + h) * C::BN + wn * C::WTN + j * 32 + l32];
+    if constexpr (C::F32S)
+      f.sb[j] = (reinterpret_cast<const uint32_t*>(st + C::BS_OFF)[wn * C::WTN + j * 32 + l32] >> 23) & 0xffu;
+    else if constexpr (C::MFB)
+      f.sb[j] = st[C::BS_OFF + (wn * C::FN + j) * 128 + (l32 + 32 * h) * 2 + KK];
+    else
+      f.sb[j] = st[C::BS_OFF + (2 * KK + h) * C::BN + wn * C::WTN + j * 32 + l32];
   });
 }
 
@@ -731,6 +816,116 @@ __device__ __forceinline__ void ra_half(const uint8_t* st, const KOps<C>& use, K
   });
 }
 
+// ---------------------------------------------------------------------------
+// SCHED 8 (stage read-ahead, one K step per stage): the operands of the next
+// stage are read while the current stage's MFMAs run. The B fragments come in
+// two sets (current, next); the A fragments of a row are replaced by the next
+// stage's as soon as that row's MFMAs have issued, so one set suffices. The
+// B scale bytes are packed in one register (byte j for column fragment j,
+// picked by the MFMA's op_sel).
+// ---------------------------------------------------------------------------
+template <class C>
+struct ROps {
+  v8i a[C::FM];
+  uint32_t sa[C::FM];
+  v8i b[2][C::FN];
+  uint32_t sb[2];
+};
+
+// Fragment rows 32 apart share their swizzle (it depends on row bits below
+// 5), so every fragment's address is the first fragment's plus a constant:
+// one lane offset serves them all (through the read's offset field).
+template <class C>
+__device__ __forceinline__ void read_a_frag(const uint8_t* st, int i, v8i& a, uint32_t& sa, int wm, int h,
+                                            int l32) {
+  const int r0 = wm * C::WTM + l32, r = r0 + i * 32;
+  const uint8_t* row = st + C::A_OFF + r0 * C::RBA + i * 32 * C::RBA;
+  if constexpr (C::AFP8) {
+    const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r0, h) * 16);
+    const v4i hi = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r0, 2 + h) * 16);
+    a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPA>(r0, h) * 16);
+    a = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+  }
+  if constexpr (C::F32S)  // power-of-two fp32 row scale: its exponent field is the UE8M0 code
+    sa = (reinterpret_cast<const uint32_t*>(st + C::AS_OFF)[r] >> 23) & 0xffu;
+  else
+    sa = st[C::AS_OFF + h * C::BM + r];
+}
+
+// B fragments [J0, J1) of a stage; with SCALES, every column fragment's scale
+// byte packed into sb
+template <class C, int J0, int J1, bool SCALES>
+__device__ __forceinline__ void read_b_part(const uint8_t* st, v8i (&b)[C::FN], uint32_t& sb, int wn, int h, int l32) {
+  unroll<C::FN>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j >= J0 && j < J1) {
+      const int r0 = wn * C::WTN + l32;
+      const uint8_t* row = st + C::B_OFF + r0 * C::RBB + j * 32 * C::RBB;
+      if constexpr (C::BFP8) {
+        const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPB>(r0, h) * 16);
+        const v4i hi = *reinterpret_cast<const v4i*>(row + swz<C::CPB>(r0, 2 + h) * 16);
+        b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const v4i lo = *reinterpret_cast<const v4i*>(row + swz<C::CPB>(r0, h) * 16);
+        b[j] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+      }
+    }
+  });
+  if constexpr (SCALES) {
+    uint32_t packed = 0;
+    unroll<C::FN>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int r = wn * C::WTN + j * 32 + l32;
+      uint32_t byte;
+      if constexpr (C::F32S) byte = (reinterpret_cast<const uint32_t*>(st + C::BS_OFF)[r] >> 23) & 0xffu;
+      else byte = st[C::BS_OFF + h * C::BN + r];
+      packed |= byte << (8 * j);
+    });
+    sb = packed;
+  }
+}
+
+// One step: the MFMAs of the current stage (B set P), row by row. Each row's
+// segment carries a share of the next stage's B reads and of the DMAs
+// (issue_part<Q0, Q1>: DMAs [Q0, Q1) of the stage) and ends with the next
+// stage's A fragment of that row, read into the registers the row's MFMAs
+// have just consumed (the fences keep those reads behind the MFMAs, so one A
+// set suffices).
+template <class C, int P, class IssuePart>
+__device__ __forceinline__ void ra_step(const uint8_t* nxt, ROps<C>& f, v16f (&acc)[C::FM][C::FN], int wm, int wn,
+                                        int h, int l32, IssuePart&& issue_part) {
+  static_assert(C::FN <= 4 && C::FM >= 2, "B scale bytes packed in one register; B reads over two rows");
+  constexpr int Q = 1 - P;
+  unroll<C::FM>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    // the next stage's B fragments over the first two rows, their scales with the second half
+    if constexpr (i == 0) read_b_part<C, 0, C::FN / 2, false>(nxt, f.b[Q], f.sb[Q], wn, h, l32);
+    if constexpr (i == 1) read_b_part<C, C::FN / 2, C::FN, true>(nxt, f.b[Q], f.sb[Q], wn, h, l32);
+    unroll<C::FN>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[P][j], acc[i][j], C::AFP8 ? 0 : 4,
+                                                                  C::BFP8 ? 0 : 4, 0, (int)f.sa[i], j,
+                                                                  (int)f.sb[P]);
+    });
+    constexpr int q0 = i * C::DPS / C::FM, q1 = (i + 1) * C::DPS / C::FM;
+    issue_part(std::integral_constant<int, q0>{}, std::integral_constant<int, q1>{});
+    constexpr int NRB = i < 2 ? (C::FN / 2) * (C::BFP8 ? 2 : 1) + (i == 1 ? C::FN : 0) : 0;  // B reads here
+    constexpr int PER = (NRB + C::FN - 1) / C::FN;
+    unroll<C::FN>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if constexpr (PER > 0) __builtin_amdgcn_sched_group_barrier(0x100, PER, 1);
+      constexpr int nd = (m + 1) * (q1 - q0) / C::FN - m * (q1 - q0) / C::FN;
+      if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x060, nd, 1);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    read_a_frag<C>(nxt, i, f.a[i], f.sa[i], wm, h, l32);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // Wait until this wave's DMAs of the stage about to be consumed have landed,
 // given how many stages it issued after that one (DPS instructions each).
 template <class C, int K>
@@ -760,7 +955,7 @@ __device__ __forceinline__ void wait_stage(int stages_after) {
 template <class C, bool FAST = false, class Src>
 __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t lda, int64_t ldas, int64_t ldb,
                                                 int64_t ldbs) {
-  static_assert(!FAST || C::SCHED == 7 || C::SCHED == 5, "fast issue: read-ahead or 3-stage loop");
+  static_assert(!FAST || C::SCHED == 7 || C::SCHED == 8 || C::SCHED == 5, "fast issue: read-ahead or 3-stage loop");
   static_assert(!FAST || !C::BLK, "fast issue: scales applied by the MFMA");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -783,7 +978,13 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
   // scale block (sBlk) of the plan is >= 0.
   DmaPlan<C> plan{};
   FastPlan<C> fplan{};
-  if constexpr (FAST) {
+  // the stage read-ahead loop issues with recomputed lane offsets
+  constexpr bool LEAN = FAST && C::SCHED == 8;
+  LeanPlan<C> lplan{};
+  if constexpr (LEAN) {
+    const uint8_t* z = reinterpret_cast<const uint8_t*>(g_zero_page);
+    lplan.a = lplan.b = lplan.as = lplan.bs = z;  // rows clamp to 0: offsets below 64 bytes
+  } else if constexpr (FAST) {
     // dummy stages before any planned tile read the zero page at offset 0
     const uint8_t* z = reinterpret_cast<const uint8_t*>(g_zero_page);
     fplan.a = fplan.b = fplan.sb = z;
@@ -797,8 +998,12 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
       it += stride;  // tiles with an empty contraction issue nothing
     }
     if (it < total) {
-      plan_dma<C>(plan, iops, lda, ldas, ldb, ldbs, w, lane);
-      if constexpr (FAST) plan_fast<C>(fplan, plan, iops, ldas, ldbs, w);
+      if constexpr (LEAN) {
+        plan_lean<C>(lplan, iops);
+      } else {
+        plan_dma<C>(plan, iops, lda, ldas, ldb, ldbs, w, lane);
+        if constexpr (FAST) plan_fast<C>(fplan, plan, iops, ldas, ldbs, w);
+      }
     }
   };
   auto issue_one = [&]() -> int {
@@ -917,6 +1122,97 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
     wait_vmcnt<0>();
     return;
   }
+  if constexpr (C::SCHED == 8) {
+    // Stage read-ahead with one K step per stage: every step waits for the
+    // NEXT stage (STAGES-3 stages were issued after it), passes the barrier,
+    // and then runs the MFMAs of the current stage (operands read during the
+    // previous step) interleaved with the reads of the next stage and the
+    // DMAs of a later stage into the slot of the previous one. The barrier
+    // admits the reads (every wave's DMAs of the next stage have landed) and
+    // frees that slot (every wave's reads of it were consumed by MFMAs issued
+    // before the barrier). No LDS read sits between the barrier and the first
+    // MFMA after it, and fragments alternate between two register sets.
+    auto advance_issue = [&](bool dummy) {
+      slot_issue = slot_issue + 1 == C::STAGES ? 0 : slot_issue + 1;
+      if (!dummy && ++is == ins) {
+        is = 0;
+        it += stride;
+        load_issue_tile();
+      }
+    };
+    // uniform strides for the lean issue (the ABI keeps a tile's span below 2^31)
+    const int ilda = __builtin_amdgcn_readfirstlane((int)lda), ildb = __builtin_amdgcn_readfirstlane((int)ldb);
+    const int ildas = __builtin_amdgcn_readfirstlane((int)ldas), ildbs = __builtin_amdgcn_readfirstlane((int)ldbs);
+    for (int q = 0; q < C::STAGES - 1; ++q) {
+      const bool dummy = it >= total;
+      if constexpr (LEAN)
+        issue_stage_lean<C>(lplan, dummy ? 0 : is, smem + slot_issue * C::STAGE_BYTES, w, lane, ilda, ildb, ildas,
+                            ildbs);
+      else if constexpr (FAST) issue_stage_fast<C>(fplan, dummy ? 0 : is, smem + slot_issue * C::STAGE_BYTES, w);
+      else issue_stage<C>(plan, iops, is, smem + slot_issue * C::STAGE_BYTES, w, ldas, ldbs, dummy);
+      advance_issue(dummy);
+    }
+    const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_zero_page);
+    asm volatile("" : "+s"(zero));
+    ROps<C> f;
+    wait_vmcnt<(C::STAGES - 2) * C::DPS>();
+    raw_barrier();
+    read_b_part<C, 0, C::FN, true>(smem, f.b[0], f.sb[0], wn, h, l32);
+    unroll<C::FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      read_a_frag<C>(smem, i, f.a[i], f.sa[i], wm, h, l32);
+    });
+    bool pending = false, pending_dummy = false;
+    v16f acc[C::FM][C::FN];
+    auto step = [&](auto pc) __attribute__((always_inline)) {
+      constexpr int P = decltype(pc)::value;
+      if (pending) advance_issue(pending_dummy);
+      const bool dummy = it >= total;
+      uint8_t* dst = smem + slot_issue * C::STAGE_BYTES;
+      const int slot_next = slot_comp + 1 == C::STAGES ? 0 : slot_comp + 1;
+      wait_vmcnt<(C::STAGES - 3) * C::DPS>();
+      raw_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      ra_step<C, P>(smem + slot_next * C::STAGE_BYTES, f, acc, wm, wn, h, l32,
+                    [&](auto q0c, auto q1c) __attribute__((always_inline)) {
+                      constexpr int q0 = decltype(q0c)::value, q1 = decltype(q1c)::value;
+                      if constexpr (LEAN) {
+                        issue_stage_lean<C, q0, q1>(lplan, dummy ? 0 : is, dst, w, lane, ilda, ildb, ildas, ildbs);
+                      } else if constexpr (q0 == 0) {
+                        issue_stage<C>(plan, iops, is, dst, w, ldas, ldbs, dummy, zero);
+                      }
+                    });
+      __builtin_amdgcn_sched_barrier(0);
+      pending = true;
+      pending_dummy = dummy;
+      slot_comp = slot_next;
+    };
+    for (int ct = first; ct < total; ct += stride) {
+      const TileOps cops = src.ops(ct, 1);
+      const int cns = (cops.kc + C::BK - 1) / C::BK;
+      unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
+      int s = 0;
+      for (; s + 2 <= cns; s += 2) {
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+      }
+      if (s < cns) {
+        step(std::integral_constant<int, 0>{});
+        // the next stage's B fragments go back to the first set
+        unroll<C::FN>([&](auto jc) { f.b[0][decltype(jc)::value] = f.b[1][decltype(jc)::value]; });
+        f.sb[0] = f.sb[1];
+      }
+      // the slot of the last stage consumed (before any, the one the prologue
+      // left empty) takes its next DMA after the next barrier: free for the
+      // epilogue once every wave has issued its last MFMAs
+      const int slot_free = slot_comp == 0 ? C::STAGES - 1 : slot_comp - 1;
+      raw_barrier();
+      src.epilogue(ct, acc, smem + slot_free * C::STAGE_BYTES + w * C::EPI_BYTES, w, lane);
+      if (cns == 0) raw_barrier();
+    }
+    wait_vmcnt<0>();
+    return;
+  }
   if constexpr (C::SCHED == 5) {
     // Every step issues exactly one stage (a dummy from the zero page once no
     // work is left), so STAGES-2 stages always follow the one awaited and the
@@ -1003,6 +1299,17 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
 // 16-byte global accesses
 // ---------------------------------------------------------------------------
 constexpr int kEpiPitch = 36;
+
+// Keeps an accumulator fragment in accumulation registers up to its use in
+// an epilogue, for wave tiles of 256 accumulators per lane (128x128): without
+// it the compiler copies every fragment into vector registers at the end of
+// the stage loop, which needs as many vector registers as there are
+// accumulators and spills the loop's state. Smaller wave tiles keep the
+// compiler's placement (measured faster there).
+template <class C>
+__device__ __forceinline__ void pin_acc(v16f& v) {
+  if constexpr (C::FM * C::FN * 16 > 128) asm volatile("" : "+a"(v));
+}
 
 template <int HF>
 __device__ __forceinline__ void frag_half_rows(const v16f& v, float* scr, int lane, float (&o)[8]) {
@@ -1127,6 +1434,7 @@ struct RowsSource {
         unroll<2>([&](auto hc) {
           constexpr int hf = decltype(hc)::value;
           float o[8];
+          pin_acc<C>(acc[i][j]);
           frag_half_rows<hf>(acc[i][j], scr, lane, o);
           const int row = wm * C::WTM + i * 32 + 16 * hf + rr;
           const int col = wn * C::WTN + j * 32 + cc;
@@ -1269,6 +1577,7 @@ struct WgradSource {
         unroll<2>([&](auto hc) {
           constexpr int hf = decltype(hc)::value;
           float o[8];
+          pin_acc<C>(acc[i][j]);
           frag_half_rows<hf>(acc[i][j], scr, lane, o);
           const int row = wm * C::WTM + i * 32 + 16 * hf + rr;
           const int col = wn * C::WTN + j * 32 + cc;
@@ -1343,7 +1652,7 @@ using CfgBlkW = TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 1>;
 // blockwise FP8 with power-of-two scales: the a4w4 loop (8 waves, 256x256)
 // with E4M3 on both sides; a 64-deep stage holds 16 KiB of each operand
 using CfgP2F = TileCfg<256, 256, 2, 4, 64, 3, kBlkP2, 1, 5, 128>;
-using CfgP2W = TileCfg<256, 256, 2, 4, 64, 3, kBlkP2, 1, 5, 1>;
+using CfgP2W = TileCfg<256, 256, 2, 2, 64, 4, kBlkP2, 1, 8, 1>;
 
 template <class C, class K, class P>
 static hipError_t launch_persistent(K kernel, const P& p, int64_t tiles, int num_cus, hipStream_t st) {
@@ -1376,7 +1685,7 @@ static hipError_t launch_rows_as(const RowsGemmParams& p, bool dgrad, int num_cu
 // the per-lane scale offsets ((SB-1) blocks of ld bytes plus a row) fit 32 bits.
 template <class C>
 static hipError_t launch_rows(const RowsGemmParams& p, bool dgrad, int num_cus, hipStream_t st) {
-  if constexpr ((C::SCHED == 7 || C::SCHED == 5) && !C::BLK) {
+  if constexpr ((C::SCHED == 7 || C::SCHED == 8 || C::SCHED == 5) && !C::BLK) {
     constexpr int64_t kLim = (int64_t)1 << 30;
     if (p.kc % C::BK == 0 && p.ldas < kLim && p.ldbs < kLim) return launch_rows_as<C, true>(p, dgrad, num_cus, st);
   }

@@ -44,7 +44,10 @@ EXPECTED = {
     # MXFP8 weight gradient (DPS 5, general issue) and power-of-two blockwise
     # weight gradient (DPS 6, scalar-base issue), every output mode
     "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi4ELi1ELi5ELi1EEELb0E": [5],
-    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi1EEELb1E": [6],
+    # blockwise FP8 weight gradient, power-of-two scales: 4 waves, stage
+    # read-ahead, 4-stage ring, DPS 10, two steps per loop iteration (every
+    # output mode)
+    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi2ELi64ELi4ELi3ELi1ELi8ELi1EEELb1E": [10, 10],
 }
 
 
@@ -61,9 +64,15 @@ def stage_loop_waits(asm_lines):
     def finish():
         if kern is None:
             return
-        loops = {hdr for hdr, lines in blocks.values() if hdr and any("v_mfma" in l for l in lines)}
-        assert len(loops) == 1, (kern, loops)
-        h = loops.pop()
+        # the loop whose blocks hold the most MFMAs (a stage loop unrolled by
+        # two leaves a one-stage tail in the enclosing tile loop)
+        count = {}
+        for hdr, lines in blocks.values():
+            if hdr:
+                count[hdr] = count.get(hdr, 0) + sum("v_mfma" in l for l in lines)
+        loops = [hdr for hdr, n in count.items() if n > 0]
+        assert loops, kern
+        h = max(loops, key=lambda x: count[x])
         out[kern] = [int(m.group(1)) for hdr, lines in blocks.values() if hdr == h
                      for l in lines for m in [re.search(r"s_waitcnt vmcnt\((\d+)\)", l)] if m]
 
@@ -85,6 +94,10 @@ def stage_loop_waits(asm_lines):
                 hdr = mh.group(1) if mh else None
             cur = name
             blocks[cur] = (hdr, [])
+            continue
+        if ("This Loop Header" in line or "This Inner Loop Header" in line) and not blocks[cur][1]:
+            # a header comment wrapped onto the line after the label
+            blocks[cur] = (cur.replace("LBB", "BB"), [])
             continue
         blocks[cur][1].append(line)
         if "s_endpgm" in line:
