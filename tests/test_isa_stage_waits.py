@@ -77,7 +77,7 @@ def stage_loop_waits(asm_lines):
                      for l in lines for m in [re.search(r"s_waitcnt vmcnt\((\d+)\)", l)] if m]
 
     for line in asm_lines:
-        m = re.match(r"^(_ZN4mxgg\S+):", line)
+        m = re.match(r"^(_ZN4mxgg\S*_kernel\S*):", line)  # kernel entry labels only
         if m:
             finish()
             kern, blocks, cur = m.group(1), {}, "entry"
