@@ -1322,6 +1322,9 @@ constexpr uint32_t kBufferOutside = 0x80000000u;  // an offset past every buffer
 // 752 -> 675 us accumulating, 604 -> 443 us overwriting; blockwise
 // 2.05 -> 1.92 ms.
 constexpr int kStreamAux = 2;
+// Accumulating weight-gradient epilogue: 16-row halves whose old output
+// values are in flight while a half is stored.
+constexpr int kEpiLoadAhead = 2;
 
 // Keeps an accumulator fragment in accumulation registers up to its use in
 // an epilogue, for wave tiles of 256 accumulators per lane (128x128): without
@@ -1565,7 +1568,8 @@ struct WgradSource {
   // half's valid rows, with columns past the output sent past its end: no
   // branches, so the compiler counts the outstanding memory operations
   // exactly; both are non-temporal. Accumulate: the old values of the next
-  // half are loaded before this half's stores, so loads and stores overlap.
+  // kEpiLoadAhead halves are loaded before this half's stores, so loads and
+  // stores overlap.
   template <bool BF16, bool ACC>
   __device__ __forceinline__ void store_tile(const Pos& q, v16f (&acc)[C::FM][C::FN], float* scr, int w, int lane) {
     constexpr int CPL = BF16 ? 8 : 4;   // columns per lane
@@ -1595,24 +1599,21 @@ struct WgradSource {
       return uniform_buffer(tile + (int64_t)r0 * row_bytes, (uint32_t)n * row_bytes);  // <= 2^29 bytes
     };
     auto off = [&](int t) { return (uint32_t)(t * RPI + lr) * row_bytes + coff; };
-    v4i old[2][ACC ? NI : 1];
-    if constexpr (ACC) {
-      const __amdgpu_buffer_rsrc_t b0 = half_buffer(0);
+    constexpr int D = kEpiLoadAhead < NH ? kEpiLoadAhead : NH;
+    v4i old[D + 1][ACC ? NI : 1];
+    auto load_half = [&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const __amdgpu_buffer_rsrc_t bk = half_buffer(k);
       unroll<NI>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
-        old[0][t] = __builtin_amdgcn_raw_buffer_load_b128(b0, off(t), 0, kStreamAux);
+        old[k % (D + 1)][t] = __builtin_amdgcn_raw_buffer_load_b128(bk, off(t), 0, kStreamAux);
       });
-    }
+    };
+    if constexpr (ACC) unroll<D>([&](auto kc) { load_half(kc); });
     unroll<NH>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       constexpr int i = k / 2, hf = k % 2;
-      if constexpr (ACC && k + 1 < NH) {
-        const __amdgpu_buffer_rsrc_t bn = half_buffer(k + 1);
-        unroll<NI>([&](auto tc) {
-          constexpr int t = decltype(tc)::value;
-          old[(k + 1) % 2][t] = __builtin_amdgcn_raw_buffer_load_b128(bn, off(t), 0, kStreamAux);
-        });
-      }
+      if constexpr (ACC && k + D < NH) load_half(std::integral_constant<int, k + D>{});
       // register q of a fragment is row 8*(q/4) + 4*(lane/32) + q%4, column lane%32
       unroll<C::FN>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
@@ -1636,7 +1637,7 @@ struct WgradSource {
         v4i d;
         if constexpr (BF16) {
           if constexpr (ACC) {
-            const v4i ov = old[k % 2][t];
+            const v4i ov = old[k % (D + 1)][t];
             unroll<4>([&](auto ec) {
               constexpr int e = decltype(ec)::value;
               o[2 * e] += __uint_as_float((uint32_t)ov[e] << 16);
@@ -1647,7 +1648,7 @@ struct WgradSource {
           d = v4i{(int)pk.x, (int)pk.y, (int)pk.z, (int)pk.w};
         } else {
           if constexpr (ACC) {
-            const v4i ov = old[k % 2][t];
+            const v4i ov = old[k % (D + 1)][t];
             unroll<4>([&](auto ec) { o[decltype(ec)::value] += __int_as_float(ov[decltype(ec)::value]); });
           }
           d = v4i{__float_as_int(o[0]), __float_as_int(o[1]), __float_as_int(o[2]), __float_as_int(o[3])};
