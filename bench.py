@@ -527,7 +527,7 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
         w, dy = normal((G * N, K), wl["w_std"], seed=SEED_W), normal((M, N), seed=SEED_DY)
         wq, ws = mxg.quantize_rowwise(w, "fp8_128x128_p2")
         del w
-        dq, ds = torch.empty((M, N), **u8), torch.empty((M, N // 128), **f32)
+        dq, ds = torch.empty((M, N), **u8), torch.empty((N // 128, M), **f32)  # 1x128 scales block-major
         tq, ts = torch.empty((G * K, N), **u8), torch.empty((G * K // 128, N // 128), **f32)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         ops = [
@@ -554,11 +554,11 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
         a, w = normal((M, K), seed=SEED_A), normal((G * N, K), wl["w_std"], seed=SEED_W)
         dy = normal((M, N), seed=SEED_DY)
         mpad = mxg.segpad_rows(sp, "fp8_1x128")
-        aq, as_ = torch.empty((M, K), **u8), torch.empty((M, K // 128), **f32)
+        aq, as_ = torch.empty((M, K), **u8), torch.empty((K // 128, M), **f32)  # 1x128 scales block-major
         wq, ws = torch.empty((G * N, K), **u8), torch.empty((G * N // 128, K // 128), **f32)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        dcq, dcs = torch.empty((N, mpad), **u8), torch.empty((N, mpad // 128), **f32)
-        xcq, xcs = torch.empty((K, mpad), **u8), torch.empty((K, mpad // 128), **f32)
+        dcq, dcs = torch.empty((N, mpad), **u8), torch.empty((mpad // 128, N), **f32)
+        xcq, xcs = torch.empty((K, mpad), **u8), torch.empty((mpad // 128, K), **f32)
         dw = torch.empty((G, N, K), dtype=torch.bfloat16, device=dev)
         ops = [
             # power-of-two scales (the blockwise default), declared by the _p2

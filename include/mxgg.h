@@ -42,7 +42,10 @@
  *   MXGG_MXFP8        E4M3 ("FN", max 448) elements, one byte each, UE8M0
  *                     scale per 32 elements.
  *   MXGG_FP8_1x128    E4M3 elements, one fp32 scale per 128 elements along the
- *                     contraction axis (activations, wgrad column operands).
+ *                     contraction axis (activations, wgrad column operands);
+ *                     the scales block-major like MX ones: f32 [blocks, rows],
+ *                     so a GEMM tile's rows of one block are one contiguous
+ *                     run.
  *   MXGG_FP8_128x128  E4M3 elements, one fp32 scale per 128x128 block
  *                     (weights).
  *   MXGG_FP8_1x128_P2, MXGG_FP8_128x128_P2
@@ -205,7 +208,7 @@ mxgg_status mxgg_mx_scales_relayout(const void* src, mxgg_scale_layout src_layou
  *   q       MXFP4: u8 [rows, cols/2]; otherwise u8 [rows, cols] (E4M3 codes).
  *   scales  MX: u8 [cols/32, R4] (block-major, R4 = mxgg_mx_scale_stride(rows)),
  *           or with MXGG_LAYOUT_MFMA u8 [cols/128, R32/32, 64, 2];
- *           FP8_1x128: f32 [rows, cols/128];
+ *           FP8_1x128: f32 [cols/128, rows] (block-major);
  *           FP8_128x128: f32 [rows/128, cols/128].
  * rows == 0 returns MXGG_OK with no launch. Errors: NULL, SHAPE, FORMAT,
  * ALIGN, DEVICE, ARCH, HIP.
@@ -232,7 +235,7 @@ mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int
  *   q        MXFP4: u8 [cols, mpad/2]; otherwise u8 [cols, mpad].
  *   scales   MX: u8 [mpad/32, cols] (block-major; cols % 32 == 0, so R4 == cols),
  *            or with MXGG_LAYOUT_MFMA u8 [mpad/128, cols/32, 64, 2];
- *            FP8_1x128: f32 [cols, mpad/128].
+ *            FP8_1x128: f32 [mpad/128, cols] (block-major).
  *   mpad     must equal mxgg_segpad_rows(m_splits, G, fmt).
  * Padding positions hold zero codes. rows == 0 returns MXGG_OK (no launch).
  * Errors: NULL, SHAPE, SPLITS, FORMAT, ALIGN, DEVICE, ARCH, HIP.
@@ -294,7 +297,7 @@ mxgg_status mxgg_transpose_128x128(const void* w_q, const void* w_s, int32_t G, 
  * pair; "Add ROCm Triton blockwise FP8 grouped GEMM": the blockwise pair).
  *   a_q, a_s  A quantized row-wise along K: (MXFP4: u8 [M, K/2] | MXFP8: u8 [M, K])
  *             + u8 [K/32, mxgg_mx_scale_stride(M)]; or MXGG_FP8_1x128: u8 [M, K]
- *             + f32 [M, K/128].
+ *             + f32 [K/128, M].
  *   w_q, w_s  packed expert weights [G*N, K] quantized row-wise along K:
  *             MXFP4 u8 [G*N, K/2] + u8 [K/32, G*N], or with w_fmt =
  *             MXGG_MXFP4 | MXGG_LAYOUT_MFMA the scales u8 [K/128, G*N/32,
@@ -330,7 +333,7 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
  *                  dy_s stays block-major.
  *   dy_q, dy_s     dY quantized row-wise along N: MX, u8 [M, N/2] (E2M1) or
  *                  [M, N] (E4M3) + u8 [N/32, mxgg_mx_scale_stride(M)];
- *                  blockwise, E4M3 [M, N] + f32 [M, N/128].
+ *                  blockwise, E4M3 [M, N] + f32 [N/128, M].
  *   wcol_q, wcol_s MX: W quantized along N with mxgg_quantize_colwise_segpad
  *                  on W as [G*N, K] with splits {N, ..., N}: u8 [K, G*N/2] +
  *                  u8 [G*N/32, K] (expert g owns columns [g*N, (g+1)*N) and
@@ -359,9 +362,9 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
  * operands; "Add ROCm Triton blockwise FP8 grouped GEMM": its blockwise form
  * and the in-place accumulation into the weight's main_grad).
  *   dycol_q/_s  dY from mxgg_quantize_colwise_segpad: [N, mpad] operand
- *               (MX scales u8 [mpad/32, N]).
+ *               (MX scales u8 [mpad/32, N]; 1x128 f32 [mpad/128, N]).
  *   xcol_q/_s   X from mxgg_quantize_colwise_segpad: [K, mpad] operand
- *               (MX scales u8 [mpad/32, K]).
+ *               (MX scales u8 [mpad/32, K]; 1x128 f32 [mpad/128, K]).
  *   fmt         MXGG_MXFP4 or MXGG_MXFP8 (both operands in that format: the
  *               a4w4 and a8w4 weight gradients; pad 32; block-major scales
  *               only), or MXGG_FP8_1x128

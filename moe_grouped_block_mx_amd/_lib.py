@@ -179,19 +179,21 @@ def _q_shape(f, rows, cols):
 
 def _row_scale_shape(f, rows, cols):
     """Scales of a [rows, cols] operand quantized along cols (row-major scales
-    when the format says so: the library refuses them, never misreads them)."""
+    when the format says so: the library refuses them, never misreads them).
+    1x128 fp32 scales are block-major [cols/128, rows]."""
     if _is_mx(f):
         return _layout_shape(f & LAYOUT_MASK, rows, cols // 32)
     if (f & 0xFF) in (FP8_1x128, FP8_1x128_P2):
-        return (rows, cols // 128)
+        return (cols // 128, rows)
     return (rows // 128, cols // 128)
 
 
 def _col_scale_shape(f, cols, mpad):
-    """Scales of the column-wise segment-padded [cols, mpad] operand."""
+    """Scales of the column-wise segment-padded [cols, mpad] operand (1x128:
+    block-major f32 [mpad/128, cols])."""
     if _is_mx(f):
         return _layout_shape(f & LAYOUT_MASK, cols, mpad // 32)
-    return (cols, mpad // 128)
+    return (mpad // 128, cols)
 
 
 def _sdtype(f):

@@ -240,7 +240,7 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
                                         stream),
                    "dual quantizer launch");
   else
-    c = hip_status(launch_quant_dual_blk(static_cast<const uint16_t*>(x), cols, ldx, sp,
+    c = hip_status(launch_quant_dual_blk(static_cast<const uint16_t*>(x), rows, cols, ldx, sp,
                                          (flags & MXGG_POW2_SCALES) != 0, static_cast<uint8_t*>(q_row),
                                          static_cast<float*>(s_row), static_cast<uint8_t*>(q_col),
                                          static_cast<float*>(s_col), mpad, stream),
@@ -280,14 +280,15 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
   RowsGemmParams p;
   std::memset(&p, 0, sizeof(p));
   if (a_fmt == MXGG_FP8_1x128) {
-    // E4M3 x E4M3; A scales f32 [M, K/128], W scales f32 [G*N/128, K/128]
+    // E4M3 x E4M3; A scales f32 [K/128, M] (block-major), W scales f32
+    // [G*N/128, K/128]
     p.a = static_cast<const uint8_t*>(a_q);
     p.as = static_cast<const uint8_t*>(a_s);
     p.b = static_cast<const uint8_t*>(w_q);
     p.bs = static_cast<const uint8_t*>(w_s);
     p.c = static_cast<uint16_t*>(out);
     p.lda = K;
-    p.ldas = K / 128 * 4;
+    p.ldas = M * 4;
     p.ldb = K;
     p.ldbs = K / 128 * 4;
     p.b_gstride = N * K;
@@ -347,10 +348,10 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
   p.kc = (int32_t)N;
   p.sp = make_splits(m_splits, G);
   if (fmt == MXGG_FP8_1x128) {
-    // dY E4M3 [M, N] + f32 [M, N/128]; W^T E4M3 [G*K, N] + f32 [G*K/128, N/128]
+    // dY E4M3 [M, N] + f32 [N/128, M]; W^T E4M3 [G*K, N] + f32 [G*K/128, N/128]
     // (the 128x128 blocks of W, transposed: same codes, same scales)
     p.lda = N;
-    p.ldas = N / 128 * 4;
+    p.ldas = M * 4;
     p.ldb = N;
     p.ldbs = N / 128 * 4;
     p.b_gstride = K * N;
@@ -397,8 +398,8 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
   p.c = main_grad;
   p.lda = blk || fp8 ? mpad : mpad / 2;         // E4M3 / E2M1 bytes
   p.ldb = p.lda;
-  p.ldas = blk ? mpad / 128 * 4 : N;             // f32 [N, mpad/128] / u8 [mpad/32, N]
-  p.ldbs = blk ? mpad / 128 * 4 : K;             // f32 [K, mpad/128] / u8 [mpad/32, K]
+  p.ldas = blk ? N * 4 : N;                      // f32 [mpad/128, N] / u8 [mpad/32, N]
+  p.ldbs = blk ? K * 4 : K;                      // f32 [mpad/128, K] / u8 [mpad/32, K]
   p.n_rows = (int32_t)N;
   p.n_cols = (int32_t)K;
   p.accumulate = accumulate;

@@ -109,7 +109,10 @@ struct TileCfg {
   static constexpr bool MFB = false;  // B's MX scales in the MFMA layout (MfmaB)
   static constexpr bool AFP8 = KIND_ != kA4W4, BFP8 = KIND_ == kBlkFp8 || KIND_ == kBlkP2 || KIND_ == kA8A8;
   static constexpr bool BLK = KIND_ == kBlkFp8;                     // per-128 partial promotion
-  static constexpr bool F32S = KIND_ == kBlkFp8 || KIND_ == kBlkP2;  // fp32 row-major scales, 1 per 128
+  // fp32 scales, one per 128 elements: A's (1x128) block-major [blocks][rows];
+  // B's block-major too for 1x128 operands (BDIV 1), or one per 128x128
+  // weight block ([row blocks][blocks], BDIV 128)
+  static constexpr bool F32S = KIND_ == kBlkFp8 || KIND_ == kBlkP2;
   static constexpr int NW = WM * WN, THREADS = 64 * NW;
   static constexpr int RBA = AFP8 ? BK : BK / 2;  // A bytes per row per stage
   static constexpr int RBB = BFP8 ? BK : BK / 2;  // B bytes per row per stage
@@ -221,6 +224,15 @@ struct DmaPlan {
 };
 constexpr int kNoBlock = 1 << 24;
 
+// Blockwise fp32 scales: byte offset of 128-element block `blk` inside a
+// tile's scale run. Block-major operands (A, and B with BDIV 1) step a whole
+// block row of ld bytes; 128x128 weight scales are row-major over blocks.
+template <class C, bool ON_B>
+__device__ __forceinline__ int64_t blk_off(int blk, int64_t ld) {
+  if constexpr (ON_B && C::BDIV != 1) return (int64_t)blk * 4;
+  return (int64_t)blk * ld;
+}
+
 template <class C>
 __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64_t lda, int64_t ldas, int64_t ldb,
                                          int64_t ldbs, int w, int lane) {
@@ -246,19 +258,20 @@ __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64
   // one block: A's [SB][BM] bytes, then B's [SB][BN], then padding. Rows past
   // the readable scale rows (which only invalid tile rows reach) read the last
   // readable group of four, so every read stays inside the buffer.
-  // Blockwise: one fp32 per row of the stage's 128-element block.
+  // Blockwise: one fp32 per row of the stage's 128-element block (per-lane
+  // row offsets here; the stage adds its block's offset, blk_off).
   if constexpr (C::F32S) {
     unroll<C::DSA>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       const int d = (i * C::NW + w) * 64 + lane;
       const int rr = d < t.mrows ? d : t.mrows - 1;
-      pl.offAS[i] = (uint32_t)(rr * ldas);
+      pl.offAS[i] = (uint32_t)(rr * 4);
     });
     unroll<C::DSB>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       const int d = (i * C::NW + w) * 64 + lane;
       const int rr = d < t.nrows ? d : t.nrows - 1;
-      pl.offBS[i] = (uint32_t)((rr / C::BDIV) * ldbs);
+      pl.offBS[i] = C::BDIV == 1 ? (uint32_t)(rr * 4) : (uint32_t)((rr / C::BDIV) * ldbs);
     });
   } else {
     unroll<C::DSA>([&](auto ic) {
@@ -334,11 +347,13 @@ __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps&
   } else if constexpr (C::F32S) {
     unroll<C::DSA>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      dma4(select_ptr(bidx0 < nblk, t.as + pl.offAS[i] + bidx0 * 4, zero), st + C::AS_OFF + (i * C::NW + w) * 256);
+      dma4(select_ptr(bidx0 < nblk, t.as + blk_off<C, false>(bidx0, ldas) + pl.offAS[i], zero),
+           st + C::AS_OFF + (i * C::NW + w) * 256);
     });
     unroll<C::DSB>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      dma4(select_ptr(bidx0 < nblk, t.bs + pl.offBS[i] + bidx0 * 4, zero), st + C::BS_OFF + (i * C::NW + w) * 256);
+      dma4(select_ptr(bidx0 < nblk, t.bs + blk_off<C, true>(bidx0, ldbs) + pl.offBS[i], zero),
+           st + C::BS_OFF + (i * C::NW + w) * 256);
     });
   } else {
     static_assert((C::BM * C::SB) % 256 == 0 && (C::BN * C::SB) % 256 == 0, "operand regions: whole instructions");
@@ -391,7 +406,7 @@ struct FastPlan {
   // wave-uniform: the tile's operand bases; per scale DMA instruction, the
   // scale operand it reads and that operand's bytes per stage
   const uint8_t *a, *b, *s[C::DSA], *sb;
-  int64_t sstep[C::DSA];
+  int64_t sstep[C::DSA], sbstep;
 };
 
 // A wave-uniform pointer moved to scalar registers (the tile bases are
@@ -418,14 +433,15 @@ __device__ __forceinline__ void plan_fast(FastPlan<C>& fp, const DmaPlan<C>& pl,
   fp.b = uniform_ptr(t.b);
   if constexpr (C::F32S) {
     // one fp32 per row and 128-element block: row offsets; the stage adds its
-    // block's 4 bytes
+    // block's offset (sstep / sbstep bytes per block)
     unroll<C::DSA>([&](auto ic) {
       fp.vS[decltype(ic)::value] = pl.offAS[decltype(ic)::value];
       fp.s[decltype(ic)::value] = uniform_ptr(t.as);
-      fp.sstep[decltype(ic)::value] = 0;
+      fp.sstep[decltype(ic)::value] = blk_off<C, false>(1, ldas);
     });
     unroll<C::DSB>([&](auto ic) { fp.vSB[decltype(ic)::value] = pl.offBS[decltype(ic)::value]; });
     fp.sb = uniform_ptr(t.bs);
+    fp.sbstep = blk_off<C, true>(1, ldbs);
     return;
   }
   unroll<C::DSA>([&](auto ic) {
@@ -483,13 +499,15 @@ __device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, u
       dma16(abase + (uint32_t)(rr * lda + c * 16), st + C::A_OFF + (i * C::NW + w) * 1024);
     }
   });
-  const int boff = (s * C::BK / 128) * 4;  // the stage's 128-element block
+  const int blk = s * C::BK / 128;  // the stage's 128-element block
+  const uint8_t* asb = lp.as + blk_off<C, false>(blk, ldas);
+  const uint8_t* bsb = lp.bs + blk_off<C, true>(blk, ldbs);
   unroll<C::DSA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     if constexpr (QSA + i >= Q0 && QSA + i < Q1) {
       const int d = (int)((i * C::NW + wu) * 64 + ln);
       const int rr = d < lp.mlast ? d : lp.mlast;
-      dma4(lp.as + boff + (uint32_t)(rr * ldas), st + C::AS_OFF + (i * C::NW + w) * 256);
+      dma4(asb + (uint32_t)(rr * 4), st + C::AS_OFF + (i * C::NW + w) * 256);
     }
   });
   unroll<C::DSB>([&](auto ic) {
@@ -497,7 +515,8 @@ __device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, u
     if constexpr (QSB + i >= Q0 && QSB + i < Q1) {
       const int d = (int)((i * C::NW + wu) * 64 + ln);
       const int rr = d < lp.nlast ? d : lp.nlast;
-      dma4(lp.bs + boff + (uint32_t)((rr / C::BDIV) * ldbs), st + C::BS_OFF + (i * C::NW + w) * 256);
+      const uint32_t ro = C::BDIV == 1 ? (uint32_t)(rr * 4) : (uint32_t)((rr / C::BDIV) * ldbs);
+      dma4(bsb + ro, st + C::BS_OFF + (i * C::NW + w) * 256);
     }
   });
   const uint8_t* bbase = lp.b + s * C::RBB;
@@ -526,14 +545,14 @@ __device__ __forceinline__ void issue_stage_fast(const FastPlan<C>& fp, int s, u
       dma16(base + fp.vA[i], st + C::A_OFF + (i * C::NW + w) * 1024);
     });
     if constexpr (C::F32S) {
-      const int boff = (s * C::BK / 128) * 4;  // the stage's 128-element block
+      const int blk = s * C::BK / 128;  // the stage's 128-element block
       unroll<C::DSA>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        dma4(fp.s[i] + boff + fp.vS[i], st + C::AS_OFF + (i * C::NW + w) * 256);
+        dma4(fp.s[i] + blk * fp.sstep[i] + fp.vS[i], st + C::AS_OFF + (i * C::NW + w) * 256);
       });
       unroll<C::DSB>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        dma4(fp.sb + boff + fp.vSB[i], st + C::BS_OFF + (i * C::NW + w) * 256);
+        dma4(fp.sb + blk * fp.sbstep + fp.vSB[i], st + C::BS_OFF + (i * C::NW + w) * 256);
       });
     } else {
       unroll<C::DSA>([&](auto ic) {
@@ -1430,8 +1449,8 @@ struct RowsSource {
     const int nleft = p.n_out - col0;
     TileOps o;
     o.a = p.a + rw.row0 * p.lda;
-    // MX scales are block-major ([blocks, rows]); blockwise scales row-major
-    o.as = p.as + (C::F32S ? rw.row0 * p.ldas : rw.row0);
+    // A's scales are block-major ([blocks, rows]: u8, or fp32 for 1x128)
+    o.as = p.as + (C::F32S ? rw.row0 * 4 : rw.row0);
     o.b = p.b + (int64_t)q.g * p.b_gstride + (int64_t)col0 * p.ldb;
     o.bs = p.bs + (int64_t)q.g * p.bs_gstride +
            (C::F32S ? (int64_t)(col0 / C::BDIV) * p.ldbs : C::MFB ? (int64_t)col0 * 4 : (int64_t)col0);
@@ -1541,12 +1560,13 @@ struct WgradSource {
     const Pos q = pos(t, side);
     TileOps o;
     // segment start: element bytes (E4M3: 1, E2M1: 1/2); scales, MX
-    // block-major (block p0/32, row row0), blockwise row-major (fp32 p0/128)
+    // block-major (block p0/32, row row0), blockwise block-major too (fp32,
+    // block p0/128, row row0)
     o.a = p.a + (int64_t)q.row0 * p.lda + (C::AFP8 ? q.p0 : q.p0 / 2);
     o.b = p.b + (int64_t)q.col0 * p.ldb + (C::BFP8 ? q.p0 : q.p0 / 2);
     if constexpr (C::F32S) {
-      o.as = p.as + (int64_t)q.row0 * p.ldas + q.p0 / 128 * 4;
-      o.bs = p.bs + (int64_t)q.col0 * p.ldbs + q.p0 / 128 * 4;
+      o.as = p.as + q.p0 / 128 * p.ldas + (int64_t)q.row0 * 4;
+      o.bs = p.bs + q.p0 / 128 * p.ldbs + (int64_t)q.col0 * 4;
     } else {
       o.as = p.as + q.p0 / 32 * p.ldas + q.row0;
       o.bs = p.bs + q.p0 / 32 * p.ldbs + q.col0;

@@ -60,8 +60,9 @@ struct RowsGemmParams {
   int64_t lda, ldb;       // A / B data row strides (bytes)
   int64_t ldas, ldbs;     // scale strides (bytes): MX scales are block-major
                           // [blocks, R4] (ld = the block stride R4, a
-                          // multiple of 4); blockwise
-                          // fp32 scales are row-major (ld = the row stride)
+                          // multiple of 4); 1x128 fp32 scales block-major
+                          // [blocks, rows] (ld = rows * 4); 128x128 weight
+                          // scales row-major over blocks (ld = the row stride)
   int64_t b_gstride;      // bytes between consecutive experts' B data
   int64_t bs_gstride;     // bytes between consecutive experts' B scales
   int64_t ldc;            // output row stride (elements)
@@ -111,14 +112,16 @@ hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgra
 // fp8: E4M3 operands on both sides (MXFP8), else E2M1 (MXFP4)
 hipError_t launch_grouped_wgrad_mx(const WgradParams& p, bool fp8, int num_cus, hipStream_t st);
 
-// Blockwise FP8 (E4M3 codes, fp32 scales per 128 along the contraction).
-// Scale row strides (ldas, ldbs) are in bytes.
+// Blockwise FP8 (E4M3 codes, fp32 scales per 128 along the contraction;
+// 1x128 scales block-major: [blocks, rows] row-wise, [mpad/128, cols]
+// column-wise).
 hipError_t launch_quant_rowwise_blk(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool blk128x128,
                                     bool pow2, uint8_t* q, float* s, hipStream_t st);
 // both of the above (1x128 row-wise and column-wise segment-padded) from one
 // read; cols a multiple of 128
-hipError_t launch_quant_dual_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
-                                 uint8_t* qr, float* sr, uint8_t* qc, float* sc, int64_t mpad, hipStream_t st);
+hipError_t launch_quant_dual_blk(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
+                                 bool pow2, uint8_t* qr, float* sr, uint8_t* qc, float* sc, int64_t mpad,
+                                 hipStream_t st);
 hipError_t launch_quant_colwise_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
                                     uint8_t* q, float* s, int64_t mpad, hipStream_t st);
 // 128x128-block weights [G*N, K] (+ f32 [G*N/128, K/128]) -> [G*K, N] (+ f32

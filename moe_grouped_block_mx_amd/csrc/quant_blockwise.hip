@@ -2,11 +2,14 @@
 // GEMM"): E4M3 codes with one fp32 scale per block.
 //
 //   1x128 row-wise   activations: blocks of 128 along the row (the contraction
-//                    axis of the forward pass); scales f32 [rows, cols/128].
+//                    axis of the forward pass); scales f32 [cols/128, rows]
+//                    (block-major, as the GEMM's DMA reads them: a tile's rows
+//                    of one block are contiguous).
 //   128x128          weights: square blocks; scales f32 [rows/128, cols/128].
 //   1x128 column-wise, segment-padded: the wgrad operands; each expert's rows
 //                    transposed, padded with zeros to a multiple of 128, blocks
-//                    of 128 along the padded length; scales f32 [cols, mpad/128].
+//                    of 128 along the padded length; scales f32 [mpad/128, cols]
+//                    (block-major).
 //
 // Scale rule and encoder: blk_round.hpp. In power-of-two mode the codes come
 // from gfx950's scaled conversion with the stored scale 2^-t as its operand
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void quant_rowwise_1x128_kernel(const uint16_t
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;  // 8-element chunk inside the row
   const bool cvalid = c < cpr;
-  const int64_t qrow = (int64_t)cpr * 8, srow = cpr / 16;
+  const int64_t qrow = (int64_t)cpr * 8;
   for (int rb = blockIdx.y * (4 * U); rb < rows; rb += gridDim.y * (4 * U)) {
     uint4 v[U];
 #pragma unroll
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(256) void quant_rowwise_1x128_kernel(const uint16_t
       if (!(cvalid && r < rows)) continue;
       const BlkScale bs = blk_scale<POW2>(amax);
       *reinterpret_cast<uint2*>(q + (int64_t)r * qrow + (int64_t)c * 8) = encode8<POW2>(wd, bs);
-      if ((c & 15) == 0) s[(int64_t)r * srow + (c >> 4)] = bs.stored;
+      if ((c & 15) == 0) s[(int64_t)(c >> 4) * rows + r] = bs.stored;
     }
   }
 }
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(256) void quant_colwise_1x128_kernel(const uint16_t
   }
   reinterpret_cast<uint4*>(qp)[0] = make_uint4(o[0], o[1], o[2], o[3]);
   reinterpret_cast<uint4*>(qp)[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  if (b == 0) s[(c0 + c) * (mpad / 128) + p0 / 128] = bs.stored;
+  if (b == 0) s[p0 / 128 * cols + c0 + c] = bs.stored;
 }
 
 // ---------------------------------------------------------------------------
@@ -296,7 +299,8 @@ __global__ __launch_bounds__(256) void quant_colwise_1x128_kernel(const uint16_t
 // ---------------------------------------------------------------------------
 template <bool POW2>
 __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
-                                                               int64_t cols, const SplitArgs sp, int64_t mpad,
+                                                               int64_t rows, int64_t cols, const SplitArgs sp,
+                                                               int64_t mpad,
                                                                uint8_t* __restrict__ qr, float* __restrict__ sr,
                                                                uint8_t* __restrict__ qc, float* __restrict__ sc) {
   constexpr int PITCH = 128 + 8;  // bf16 per LDS row: 16-byte aligned rows
@@ -337,7 +341,6 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(const uint16_t* _
     v[i] = row < nvalid ? *reinterpret_cast<const uint4*>(x + (row0 + row) * ldx + c0 + ch * 8)
                         : make_uint4(0, 0, 0, 0);
   }
-  const int64_t srow = cols / 128;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = rg + 16 * i;
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(const uint16_t* _
     const BlkScale bs = blk_scale<POW2>(amax);
     const int64_t r = row0 + row;
     *reinterpret_cast<uint2*>(qr + r * cols + c0 + ch * 8) = encode8<POW2>(wd, bs);
-    if (ch == 0) sr[r * srow + c0 / 128] = bs.stored;
+    if (ch == 0) sr[c0 / 128 * rows + r] = bs.stored;
   }
   __syncthreads();
 
@@ -385,21 +388,23 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(const uint16_t* _
     uint8_t* qp = qc + (c0 + c) * mpad + p0 + b * 32;
     reinterpret_cast<uint4*>(qp)[0] = make_uint4(o[0], o[1], o[2], o[3]);
     reinterpret_cast<uint4*>(qp)[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    if (b == 0) sc[(c0 + c) * (mpad / 128) + p0 / 128] = bs.stored;
+    if (b == 0) sc[p0 / 128 * cols + c0 + c] = bs.stored;
   }
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_quant_dual_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
-                                 uint8_t* qr, float* sr, uint8_t* qc, float* sc, int64_t mpad, hipStream_t st) {
+hipError_t launch_quant_dual_blk(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
+                                 bool pow2, uint8_t* qr, float* sr, uint8_t* qc, float* sc, int64_t mpad,
+                                 hipStream_t st) {
   const dim3 grid((unsigned)(mpad / 128), (unsigned)(cols / 128));
   if (pow2)
-    hipLaunchKernelGGL(quant_dual_1x128_kernel<true>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, qr, sr, qc, sc);
+    hipLaunchKernelGGL(quant_dual_1x128_kernel<true>, grid, dim3(256), 0, st, x, ldx, rows, cols, sp, mpad, qr, sr,
+                       qc, sc);
   else
-    hipLaunchKernelGGL(quant_dual_1x128_kernel<false>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, qr, sr, qc,
-                       sc);
+    hipLaunchKernelGGL(quant_dual_1x128_kernel<false>, grid, dim3(256), 0, st, x, ldx, rows, cols, sp, mpad, qr, sr,
+                       qc, sc);
   return hipGetLastError();
 }
 

@@ -80,7 +80,9 @@ def test_quantizer_outputs():
     with pytest.raises(ValueError, match="q"):
         mxg.quantize_rowwise(x, "mxfp8", q=z((M, K // 2), u8))
     with pytest.raises(ValueError, match="scales"):
-        mxg.quantize_rowwise(x, "fp8_1x128", scales=z((M, K // 128), u8))   # fp32 scales expected
+        mxg.quantize_rowwise(x, "fp8_1x128", scales=z((K // 128, M), u8))   # fp32 scales expected
+    with pytest.raises(ValueError, match="scales"):
+        mxg.quantize_rowwise(x, "fp8_1x128", scales=z((M, K // 128), f32))  # 1x128 scales are block-major
     with pytest.raises(ValueError, match="q_col"):
         mxg.quantize_dual(x, SPLITS, "mxfp4", q_col=z((K, MPAD), u8))
     with pytest.raises(ValueError, match="q"):

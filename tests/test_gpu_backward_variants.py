@@ -146,7 +146,7 @@ def test_dgrad_blockwise(case, fmt):
     torch.cuda.synchronize()
     rd, rds = ob.quantize_1x128(dy, pow2=p2)
     rw, rws = ob.quantize_128x128(w, pow2=p2)
-    assert np.array_equal(host(dq), rd.astype(np.uint8)) and np.array_equal(host(ds), rds.astype(np.float32))
+    assert np.array_equal(host(dq), rd.astype(np.uint8)) and np.array_equal(host(ds).T, rds.astype(np.float32))
     W = ob.dequantize_128x128(rw, rws).reshape(G, N, K)
     # dx = dY_g . W_g: the forward's contraction with W_g^T as the weight
     ref = og.grouped_fwd(ob.dequantize_1x128(rd, rds), np.ascontiguousarray(W.transpose(0, 2, 1)), splits)

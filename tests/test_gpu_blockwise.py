@@ -49,8 +49,9 @@ def test_quantize_1x128_rowwise(pow2, shape):
     q, s = mxg.quantize_rowwise(dev_bf16(x), "fp8_1x128", flags=POW2 if pow2 else 0)
     torch.cuda.synchronize()
     rq, rs = ob.quantize_1x128(x, pow2=pow2)
+    assert s.shape == (shape[1] // 128, shape[0])  # block-major
     assert np.array_equal(host(q), rq.astype(np.uint8))
-    assert np.array_equal(host(s).view(np.uint32), rs.astype(np.float32).view(np.uint32))
+    assert np.array_equal(host(s).T.copy().view(np.uint32), rs.astype(np.float32).view(np.uint32))
 
 
 def test_quantize_1x128_strided_input():
@@ -60,7 +61,7 @@ def test_quantize_1x128_strided_input():
     torch.cuda.synchronize()
     rq, rs = ob.quantize_1x128(np.ascontiguousarray(full[:, 128:384]))
     assert np.array_equal(host(q), rq.astype(np.uint8))
-    assert np.array_equal(host(s), rs.astype(np.float32))
+    assert np.array_equal(host(s).T, rs.astype(np.float32))
 
 
 @pytest.mark.parametrize("pow2", [True, False])
@@ -105,8 +106,9 @@ def test_quantize_colwise_1x128(pow2, case):
     torch.cuda.synchronize()
     rq, rs = ob.quantize_colwise_segpad_128(x, splits, pow2=pow2)
     assert mpad == rq.shape[1]
+    assert s.shape == (mpad // 128, cols)  # block-major
     assert np.array_equal(host(q), rq.astype(np.uint8))
-    assert np.array_equal(host(s).view(np.uint32), rs.astype(np.float32).view(np.uint32))
+    assert np.array_equal(host(s).T.copy().view(np.uint32), rs.astype(np.float32).view(np.uint32))
 
 
 # ---------------------------------------------------------------------------
@@ -272,7 +274,7 @@ def test_c5_full_size_fwd_sampled(c5, p2):
         # quantized by the oracle, must equal the library's bytes
         ra, ras = ob.quantize_1x128(_bits(a[torch.as_tensor(rows, device="cuda")]))
         assert np.array_equal(host(aq[torch.as_tensor(rows, device="cuda")]), ra.astype(np.uint8))
-        assert np.array_equal(host(as_[torch.as_tensor(rows, device="cuda")]), ras.astype(np.float32))
+        assert np.array_equal(host(as_[:, torch.as_tensor(rows, device="cuda")]).T, ras.astype(np.float32))
         r0 = g * N + blk * 128
         rw, rws = ob.quantize_128x128(_bits(w[r0:r0 + 128]))
         assert np.array_equal(host(wq[r0:r0 + 128]), rw.astype(np.uint8))
@@ -306,7 +308,7 @@ def test_c5_full_size_wgrad_sampled(c5, p2):
         rd, rds = ob.quantize_colwise_segpad_128(_bits(dy[r0:r1][:, torch.as_tensor(ns, device="cuda")]), [r1 - r0])
         rx, rxs = ob.quantize_colwise_segpad_128(_bits(a[r0:r1][:, torch.as_tensor(ks, device="cuda")]), [r1 - r0])
         assert np.array_equal(host(dq[torch.as_tensor(ns, device="cuda")][:, p0:p1]), rd.astype(np.uint8))
-        assert np.array_equal(host(xs[torch.as_tensor(ks, device="cuda")][:, p0 // 128:p1 // 128]),
+        assert np.array_equal(host(xs[p0 // 128:p1 // 128][:, torch.as_tensor(ks, device="cuda")]).T,
                               rxs.astype(np.float32))
         ref = ob.dequantize_1x128(rd, rds) @ ob.dequantize_1x128(rx, rxs).T
         gpu = host_bf16_f64(out[g][torch.as_tensor(ns, device="cuda")][:, torch.as_tensor(ks, device="cuda")])

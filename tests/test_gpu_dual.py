@@ -151,9 +151,10 @@ def _check_blk(bits, splits, fmt, what, x=None):
     for name, a, b in (("q_row", qr, q2), ("s_row", sr, s2), ("q_col", qc, qc2), ("s_col", sc, sc2)):
         assert torch.equal(a, b), f"{what}: {name} differs from the separate kernel"
     rq, rs = ob.quantize_1x128(bits, pow2=pow2)
-    assert np.array_equal(host(qr), rq) and np.array_equal(host(sr), rs), f"{what}: row-wise vs oracle"
+    # 1x128 scales are block-major: the oracle's [rows, blocks] transposed
+    assert np.array_equal(host(qr), rq) and np.array_equal(host(sr).T, rs), f"{what}: row-wise vs oracle"
     cq, cs = ob.quantize_colwise_segpad_128(bits, splits, pow2=pow2)
-    assert np.array_equal(host(qc), cq) and np.array_equal(host(sc), cs), f"{what}: column-wise vs oracle"
+    assert np.array_equal(host(qc), cq) and np.array_equal(host(sc).T, cs), f"{what}: column-wise vs oracle"
 
 
 @pytest.mark.parametrize("fmt", ["fp8_1x128_p2", "fp8_1x128"])
@@ -191,7 +192,7 @@ def test_blockwise_dual_full_size_sampled():
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(32768, size=256, replace=False))
     rq, rs = ob.quantize_1x128(bits[rows])
-    assert np.array_equal(host(qr)[rows], rq) and np.array_equal(host(sr)[rows], rs)
+    assert np.array_equal(host(qr)[rows], rq) and np.array_equal(host(sr)[:, rows].T, rs)
     cols = np.sort(rng.choice(7168, size=16, replace=False))
     cq, cs = ob.quantize_colwise_segpad_128(np.ascontiguousarray(bits[:, cols]), sp)
-    assert np.array_equal(host(qc)[cols], cq) and np.array_equal(host(sc)[cols], cs)
+    assert np.array_equal(host(qc)[cols], cq) and np.array_equal(host(sc)[:, cols].T, cs)
