@@ -186,7 +186,9 @@ struct MfmaB : C {
 // binary search over the segments after it.
 __device__ __forceinline__ int seek_segment(const int32_t* offs, int n, int t, int& cursor) {
   int j = cursor;
-  if (j < 0 || offs[j + 1] <= t) {
+  if (j >= 0 && t < offs[j]) {
+    j = upper_bound_i32(offs, j + 1, t) - 1;  // a workgroup walking its tiles backwards
+  } else if (j < 0 || offs[j + 1] <= t) {
     const int lo = j < 0 ? 0 : j + 1;
     j = lo + upper_bound_i32(offs + lo, n - lo, t) - 1;
   }
@@ -199,7 +201,7 @@ struct TileOps {
   const uint8_t* a;   // first row of the A tile (row stride lda)
   const uint8_t* as;  // its scales: MX, block-major (block stride ldas, row
                       // stride 1; the tile's first row a multiple of 4);
-                      // blockwise, row-major (row stride ldas)
+                      // blockwise 1x128, block-major fp32 (block stride ldas)
   const uint8_t* b;
   const uint8_t* bs;
   int mrows, nrows;   // valid rows of A and B (>= 1)
@@ -973,7 +975,8 @@ __device__ __forceinline__ void wait_stage(int stages_after) {
 //   src.ops(t, side)  TileOps of tile t; side 0 the issuing side, 1 the
 //                     computing side (each keeps its own segment cursor)
 //   src.epilogue(...) stores tile t (the last tile ops(t, 1) was asked for)
-// Tiles are visited t = first, first + gridDim.x, ...
+// Tiles are visited t = first, first + gridDim.x, ... (last to first on the
+// odd XCDs when Src::kDesync).
 // FAST (read-ahead loop only): every tile's contraction is a multiple of BK
 // and the scale offsets fit 32 bits; the DMAs take the fast issue above.
 template <class C, bool FAST = false, class Src>
@@ -992,6 +995,13 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
   // consecutive logical ids on one XCD (the hardware deals block ids
   // round-robin over the 8 XCDs), so co-resident tiles share operands in L2
   const int first = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  // Src::kDesync: the workgroups of odd XCDs take their tiles in reverse.
+  // Each still computes the same tiles, but neighbouring XCDs no longer run
+  // tiles of one expert (one contraction length) in lockstep, so their
+  // HBM-bound epilogues do not all fall on the same moments.
+  const int nmine = first < total ? (total - 1 - first) / stride + 1 : 0;
+  const bool rev = Src::kDesync && (b & 1) != 0;
+  auto tile_at = [&](int x) { return rev ? first + (nmine - 1 - (x - first) / stride) * stride : x; };
 
   // issuing side: the tile and stage whose DMAs go out next
   int it = first, is = 0, ins = 0, slot_issue = 0;
@@ -1016,7 +1026,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
   }
   auto load_issue_tile = [&]() {
     while (it < total) {
-      iops = src.ops(it, 0);
+      iops = src.ops(tile_at(it), 0);
       ins = (iops.kc + C::BK - 1) / C::BK;
       if (ins > 0) break;
       it += stride;  // tiles with an empty contraction issue nothing
@@ -1080,7 +1090,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
     read_kops<C, 0>(smem, f0, wm, wn, h, l32);
     bool pending = false, pending_dummy = false;
     for (int ct = first; ct < total; ct += stride) {
-      const TileOps cops = src.ops(ct, 1);
+      const TileOps cops = src.ops(tile_at(ct), 1);
       const int cns = (cops.kc + C::BK - 1) / C::BK;
       v16f acc[C::FM][C::FN];
       unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
@@ -1137,7 +1147,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
       // issued before this barrier, so it is free for the epilogue.
       const int slot_free = slot_comp == 0 ? C::STAGES - 1 : slot_comp - 1;
       raw_barrier();
-      src.epilogue(ct, acc, smem + slot_free * C::STAGE_BYTES + w * C::EPI_BYTES, w, lane);
+      src.epilogue(tile_at(ct), acc, smem + slot_free * C::STAGE_BYTES + w * C::EPI_BYTES, w, lane);
       // A tile with an empty contraction consumed no stage, so the next
       // step's first-half DMAs may target the slot its epilogue used (the
       // prologue's empty slot): every wave finishes the epilogue first.
@@ -1212,7 +1222,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
       slot_comp = slot_next;
     };
     for (int ct = first; ct < total; ct += stride) {
-      const TileOps cops = src.ops(ct, 1);
+      const TileOps cops = src.ops(tile_at(ct), 1);
       const int cns = (cops.kc + C::BK - 1) / C::BK;
       unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
       int s = 0;
@@ -1231,7 +1241,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
       // epilogue once every wave has issued its last MFMAs
       const int slot_free = slot_comp == 0 ? C::STAGES - 1 : slot_comp - 1;
       raw_barrier();
-      src.epilogue(ct, acc, smem + slot_free * C::STAGE_BYTES + w * C::EPI_BYTES, w, lane);
+      src.epilogue(tile_at(ct), acc, smem + slot_free * C::STAGE_BYTES + w * C::EPI_BYTES, w, lane);
       if (cns == 0) raw_barrier();
     }
     wait_vmcnt<0>();
@@ -1257,7 +1267,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
     }
     bool pending = false, pending_dummy = false;
     for (int ct = first; ct < total; ct += stride) {
-      const TileOps cops = src.ops(ct, 1);
+      const TileOps cops = src.ops(tile_at(ct), 1);
       const int cns = (cops.kc + C::BK - 1) / C::BK;
       v16f acc[C::FM][C::FN];
       unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
@@ -1279,7 +1289,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
         pending_dummy = dummy;
         slot_comp = slot_comp + 1 == C::STAGES ? 0 : slot_comp + 1;
       }
-      src.epilogue(ct, acc, scratch, w, lane);
+      src.epilogue(tile_at(ct), acc, scratch, w, lane);
     }
     wait_vmcnt<0>();
     return;
@@ -1287,7 +1297,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
   for (int q = 0; q < C::STAGES - 1; ++q) ahead += issue_one();
 
   for (int ct = first; ct < total; ct += stride) {
-    const TileOps cops = src.ops(ct, 1);
+    const TileOps cops = src.ops(tile_at(ct), 1);
     const int cns = (cops.kc + C::BK - 1) / C::BK;
     v16f acc[C::FM][C::FN];
     unroll<C::FM>([&](auto ic) { unroll<C::FN>([&](auto jc) { acc[ic][jc] = v16f{}; }); });
@@ -1311,7 +1321,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
       slot_comp = slot_comp + 1 == C::STAGES ? 0 : slot_comp + 1;
       --ahead;
     }
-    src.epilogue(ct, acc, scratch, w, lane);
+    src.epilogue(tile_at(ct), acc, scratch, w, lane);
   }
   wait_vmcnt<0>();  // no DMA of this workgroup outlives it (every issued stage was waited for; kept explicit)
 }
@@ -1414,6 +1424,7 @@ __host__ __device__ inline int64_t expert_row_tiles(int64_t start, int64_t m) {
 
 template <class C>
 struct RowsSource {
+  static constexpr bool kDesync = false;
   const RowsGemmParams& p;
   const int64_t* pref;       // LDS: first row of each expert's segment
   const int32_t* tile_offs;  // LDS
@@ -1531,6 +1542,11 @@ enum : int { kEpiF32Acc = 0, kEpiF32Set = 1, kEpiBf16Set = 2, kEpiBf16Acc = 3 };
 
 template <class C, bool FAST, int EPI>
 struct WgradSource {
+  // Accumulating epilogues read and write the output (HBM-bound): desync the
+  // XCDs (persistent_loop). Measured at the fc1 shapes, fp32 accumulate:
+  // 700 -> 668 us; the overwriting blockwise weight gradient was slower
+  // (1.71 -> 1.79 ms), so the other modes keep one order.
+  static constexpr bool kDesync = EPI == kEpiF32Acc || EPI == kEpiBf16Acc;
   const WgradParams& p;
   const int64_t* pad_pref;   // LDS: padded segment offsets (natural expert order)
   const int32_t* tile_offs;  // LDS: tile offsets in longest-first order

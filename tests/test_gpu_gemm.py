@@ -143,6 +143,10 @@ WGRAD_CASES = [
     ([33, 0, 1, 300], 96, 192),        # variable K incl. 32 and 320 (not a multiple of 128)
     ([0, 0, 0], 64, 64),               # all experts empty
     ([640, 40], 320, 288),             # N and K tails
+    # 384 tiles: a quarter of the workgroups take two, those of odd XCDs in
+    # reverse when accumulating (their segment cursor moves back)
+    ([37, 250, 0, 128, 5, 299, 64, 1, 190, 33, 0, 256, 77, 140, 12, 288, 96, 0, 45, 210, 160, 3, 31, 129],
+     1024, 1024),
 ]
 
 
