@@ -557,8 +557,9 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
         aq, as_ = torch.empty((M, K), **u8), torch.empty((K // 128, M), **f32)  # 1x128 scales block-major
         wq, ws = torch.empty((G * N, K), **u8), torch.empty((G * N // 128, K // 128), **f32)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        dcq, dcs = torch.empty((N, mpad), **u8), torch.empty((mpad // 128, N), **f32)
-        xcq, xcs = torch.empty((K, mpad), **u8), torch.empty((mpad // 128, K), **f32)
+        # column-wise 1x128 codes in 64-byte K blocks, scales block-major
+        dcq, dcs = torch.empty((mpad // 64, N, 64), **u8), torch.empty((mpad // 128, N), **f32)
+        xcq, xcs = torch.empty((mpad // 64, K, 64), **u8), torch.empty((mpad // 128, K), **f32)
         dw = torch.empty((G, N, K), dtype=torch.bfloat16, device=dev)
         ops = [
             # power-of-two scales (the blockwise default), declared by the _p2

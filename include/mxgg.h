@@ -232,7 +232,11 @@ mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int
  *   fmt      MXGG_MXFP4, MXGG_MXFP8 or MXGG_FP8_1x128; cols % 32 == 0. MX
  *            formats | MXGG_LAYOUT_MFMA need every split to be a multiple of
  *            128 (else MXGG_ERR_SPLITS).
- *   q        MXFP4: u8 [cols, mpad/2]; otherwise u8 [cols, mpad].
+ *   q        MXFP4: u8 [cols, mpad/2]; MXFP8: u8 [cols, mpad]; FP8_1x128: u8
+ *            [mpad/64, cols, 64], 64-byte blocks along the padded length
+ *            (byte p of column c at ((p/64)*cols + c)*64 + p%64: a weight-
+ *            gradient stage reads each tile row's 64 bytes of one block as
+ *            one contiguous run).
  *   scales   MX: u8 [mpad/32, cols] (block-major; cols % 32 == 0, so R4 == cols),
  *            or with MXGG_LAYOUT_MFMA u8 [mpad/128, cols/32, 64, 2];
  *            FP8_1x128: f32 [mpad/128, cols] (block-major).
@@ -362,9 +366,11 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
  * operands; "Add ROCm Triton blockwise FP8 grouped GEMM": its blockwise form
  * and the in-place accumulation into the weight's main_grad).
  *   dycol_q/_s  dY from mxgg_quantize_colwise_segpad: [N, mpad] operand
- *               (MX scales u8 [mpad/32, N]; 1x128 f32 [mpad/128, N]).
+ *               (MX scales u8 [mpad/32, N]; 1x128 codes u8 [mpad/64, N, 64]
+ *               and scales f32 [mpad/128, N]).
  *   xcol_q/_s   X from mxgg_quantize_colwise_segpad: [K, mpad] operand
- *               (MX scales u8 [mpad/32, K]; 1x128 f32 [mpad/128, K]).
+ *               (MX scales u8 [mpad/32, K]; 1x128 codes u8 [mpad/64, K, 64]
+ *               and scales f32 [mpad/128, K]).
  *   fmt         MXGG_MXFP4 or MXGG_MXFP8 (both operands in that format: the
  *               a4w4 and a8w4 weight gradients; pad 32; block-major scales
  *               only), or MXGG_FP8_1x128

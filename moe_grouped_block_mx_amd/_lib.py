@@ -177,6 +177,15 @@ def _q_shape(f, rows, cols):
     return (rows, cols // 2 if (f & 0xFF) == MXFP4 else cols)
 
 
+def _col_q_shape(f, cols, mpad):
+    """Codes of the column-wise segment-padded [cols, mpad] operand: rows of
+    codes, or for 1x128 64-byte blocks along the padded length, u8 [mpad/64,
+    cols, 64]."""
+    if (f & 0xFF) in (FP8_1x128, FP8_1x128_P2):
+        return (mpad // 64, cols, 64)
+    return _q_shape(f, cols, mpad)
+
+
 def _row_scale_shape(f, rows, cols):
     """Scales of a [rows, cols] operand quantized along cols (row-major scales
     when the format says so: the library refuses them, never misreads them).
@@ -262,7 +271,8 @@ def mxgg_quantize_rowwise(x, fmt="mxfp4", flags=None, q=None, scales=None):
 
 
 def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=None, q=None, scales=None):
-    """x: bf16 [rows, cols]. Returns (q [cols, mpad(/2)], scales, mpad)."""
+    """x: bf16 [rows, cols]. Returns (q, scales, mpad): q [cols, mpad(/2)],
+    or for the 1x128 formats u8 [mpad/64, cols, 64] (64-byte K blocks)."""
     torch = _torch()
     f = _fmt(fmt)
     flags = _flags(flags, f)
@@ -273,10 +283,10 @@ def mxgg_quantize_colwise_segpad(x, m_splits, fmt="mxfp4", flags=None, q=None, s
     if mpad < 0:
         mpad = 0
     if q is None:
-        q = torch.empty(_q_shape(f, cols, mpad), dtype=torch.uint8, device=x.device)
+        q = torch.empty(_col_q_shape(f, cols, mpad), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(_col_scale_shape(f, cols, mpad), dtype=_sdtype(f), device=x.device)
-    _expect(q, "q", _q_shape(f, cols, mpad), torch.uint8)
+    _expect(q, "q", _col_q_shape(f, cols, mpad), torch.uint8)
     _expect(scales, "scales", _col_scale_shape(f, cols, mpad), _sdtype(f))
     _check(lib.mxgg_quantize_colwise_segpad(_ptr(x), rows, cols, _ld(x), arr, G, f, flags, _ptr(q),
                                             _ptr(scales), mpad, _stream(x)))
@@ -302,12 +312,12 @@ def mxgg_quantize_dual(x, m_splits, fmt="mxfp4", flags=None, q_row=None, s_row=N
     if s_row is None:
         s_row = torch.empty(_row_scale_shape(f, rows, cols), dtype=_sdtype(f), device=x.device)
     if q_col is None:
-        q_col = torch.empty(_q_shape(f, cols, mpad), **u8)
+        q_col = torch.empty(_col_q_shape(f, cols, mpad), **u8)
     if s_col is None:
         s_col = torch.empty(_col_scale_shape(f, cols, mpad), dtype=_sdtype(f), device=x.device)
     _expect(q_row, "q_row", _q_shape(f, rows, cols), torch.uint8)
     _expect(s_row, "s_row", _row_scale_shape(f, rows, cols), _sdtype(f))
-    _expect(q_col, "q_col", _q_shape(f, cols, mpad), torch.uint8)
+    _expect(q_col, "q_col", _col_q_shape(f, cols, mpad), torch.uint8)
     _expect(s_col, "s_col", _col_scale_shape(f, cols, mpad), _sdtype(f))
     _check(lib.mxgg_quantize_dual(_ptr(x), rows, cols, _ld(x), arr, G, f, flags, _ptr(q_row), _ptr(s_row),
                                   _ptr(q_col), _ptr(s_col), mpad, _stream(x)))
@@ -381,9 +391,9 @@ def mxgg_grouped_wgrad(dycol_q, dycol_s, xcol_q, xcol_s, m_splits, N, K, mpad, m
     torch = _torch()
     arr, G = _splits(m_splits)
     f = _fmt(fmt)
-    _expect(dycol_q, "dycol_q", _q_shape(f, N, mpad), torch.uint8)
+    _expect(dycol_q, "dycol_q", _col_q_shape(f, N, mpad), torch.uint8)
     _expect(dycol_s, "dycol_s", _col_scale_shape(f, N, mpad), _sdtype(f))
-    _expect(xcol_q, "xcol_q", _q_shape(f, K, mpad), torch.uint8)
+    _expect(xcol_q, "xcol_q", _col_q_shape(f, K, mpad), torch.uint8)
     _expect(xcol_s, "xcol_s", _col_scale_shape(f, K, mpad), _sdtype(f))
     _expect(main_grad, "main_grad", (G, N, K), (torch.float32, torch.bfloat16))
     out_bf16 = 1 if main_grad.dtype == torch.bfloat16 else 0

@@ -396,8 +396,10 @@ mxgg_status mxgg_grouped_wgrad(const void* dycol_q, const void* dycol_s, const v
   p.b = static_cast<const uint8_t*>(xcol_q);
   p.bs = static_cast<const uint8_t*>(xcol_s);
   p.c = main_grad;
-  p.lda = blk || fp8 ? mpad : mpad / 2;         // E4M3 / E2M1 bytes
-  p.ldb = p.lda;
+  // row strides of the [N, mpad] / [K, mpad] codes (E4M3 / E2M1 bytes);
+  // blockwise: bytes per 64-byte K block, u8 [mpad/64, N or K, 64]
+  p.lda = blk ? N * 64 : fp8 ? mpad : mpad / 2;
+  p.ldb = blk ? K * 64 : p.lda;
   p.ldas = blk ? N * 4 : N;                      // f32 [mpad/128, N] / u8 [mpad/32, N]
   p.ldbs = blk ? K * 4 : K;                      // f32 [mpad/128, K] / u8 [mpad/32, K]
   p.n_rows = (int32_t)N;

@@ -107,6 +107,7 @@ struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
   static constexpr int SCHED = SCHED_, BDIV = BDIV_;
   static constexpr bool MFB = false;  // B's MX scales in the MFMA layout (MfmaB)
+  static constexpr bool KBLK = false;  // operand data in 64-byte K blocks (KBlocked)
   static constexpr bool AFP8 = KIND_ != kA4W4, BFP8 = KIND_ == kBlkFp8 || KIND_ == kBlkP2 || KIND_ == kA8A8;
   static constexpr bool BLK = KIND_ == kBlkFp8;                     // per-128 partial promotion
   // fp32 scales, one per 128 elements: A's (1x128) block-major [blocks][rows];
@@ -179,11 +180,31 @@ struct MfmaB : C {
   static_assert(!C::F32S && C::BK == 128 && C::BN % 32 == 0, "MFMA-layout scales: 128-deep MX stages");
 };
 
+// A configuration whose A and B data are stored in 64-byte blocks along the
+// contraction, u8 [L/64, rows, 64] for rows of L bytes (the blockwise
+// column-wise operands of the weight gradient, segments padded to 128): byte
+// j of row r sits at (j/64)*ld + r*64 + j%64 with ld = rows*64, so the 64
+// bytes a stage needs from each of a tile's rows form one contiguous run per
+// 64-byte block (one 1 KiB run per DMA instruction instead of 16 row pieces).
+template <class C>
+struct KBlocked : C {
+  static constexpr bool KBLK = true;
+  static_assert(C::AFP8 && C::BFP8 && C::RBA % 64 == 0 && C::RBB % 64 == 0, "64-byte K blocks of E4M3 stages");
+};
+
+// Byte offset of data byte j (along the contraction) of row r: row-major
+// rows of ld bytes, or 64-byte K blocks of ld bytes each (KBLK).
+template <class C>
+__host__ __device__ constexpr int64_t data_off(int64_t r, int64_t j, int64_t ld) {
+  return C::KBLK ? (j / 64) * ld + r * 64 + j % 64 : r * ld + j;
+}
+
 // The segment owning item t of a non-decreasing prefix offs[0..n] (offs[0] =
-// 0), from a cursor: a workgroup visits its tiles in increasing order (the
-// issuing side and the computing side each with its own cursor), so the
-// cursor's segment usually still owns t and one LDS read confirms it; else a
-// binary search over the segments after it.
+// 0), from a cursor: a workgroup visits its tiles in increasing order (or,
+// reversed, in decreasing order; the issuing side and the computing side
+// each with its own cursor), so the cursor's segment usually still owns t and
+// one LDS read confirms it; else a binary search over the segments after it
+// (before it, walking backwards).
 __device__ __forceinline__ int seek_segment(const int32_t* offs, int n, int t, int& cursor) {
   int j = cursor;
   if (j >= 0 && t < offs[j]) {
@@ -223,6 +244,7 @@ struct DmaPlan {
   // wave-uniform (A's and B's regions are whole instructions)
   uint32_t sOff[C::F32S ? 1 : C::DSA];
   int sBlk[C::F32S ? 1 : C::DSA];
+  int64_t astep, bstep;  // data bytes from one stage to the next (KBLK: whole blocks)
 };
 constexpr int kNoBlock = 1 << 24;
 
@@ -244,7 +266,7 @@ __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64
     const int r = o / C::RBA;
     const int c = swz<C::CPA>(r, (o % C::RBA) / 16);
     const int rr = r < t.mrows ? r : t.mrows - 1;
-    pl.offA[i] = (uint32_t)(rr * lda) + c * 16;
+    pl.offA[i] = (uint32_t)data_off<C>(rr, c * 16, lda);
     pl.kA[i] = c * 16;
   });
   unroll<C::DB>([&](auto ic) {
@@ -253,9 +275,11 @@ __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64
     const int r = o / C::RBB;
     const int c = swz<C::CPB>(r, (o % C::RBB) / 16);
     const int rr = r < t.nrows ? r : t.nrows - 1;
-    pl.offB[i] = (uint32_t)(rr * ldb) + c * 16;
+    pl.offB[i] = (uint32_t)data_off<C>(rr, c * 16, ldb);
     pl.kB[i] = c * 16;
   });
+  pl.astep = data_off<C>(0, C::RBA, lda);
+  pl.bstep = data_off<C>(0, C::RBB, ldb);
   // Scales. MX: lane word d of the stage's scale region holds four rows of
   // one block: A's [SB][BM] bytes, then B's [SB][BN], then padding. Rows past
   // the readable scale rows (which only invalid tile rows reach) read the last
@@ -334,14 +358,14 @@ __device__ __forceinline__ void issue_stage(const DmaPlan<C>& pl, const TileOps&
   if constexpr (DO_A) {
     unroll<C::DA>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      const uint8_t* src = select_ptr(ka0 + pl.kA[i] < kca, t.a + pl.offA[i] + ka0, zero);
+      const uint8_t* src = select_ptr(ka0 + pl.kA[i] < kca, t.a + s * pl.astep + pl.offA[i], zero);
       dma16(src, st + C::A_OFF + (i * C::NW + w) * 1024);
     });
   }
   if constexpr (DO_B) {
     unroll<C::DB>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      const uint8_t* src = select_ptr(kb0 + pl.kB[i] < kcb, t.b + pl.offB[i] + kb0, zero);
+      const uint8_t* src = select_ptr(kb0 + pl.kB[i] < kcb, t.b + s * pl.bstep + pl.offB[i], zero);
       dma16(src, st + C::B_OFF + (i * C::NW + w) * 1024);
     });
   }
@@ -379,7 +403,7 @@ __device__ __forceinline__ void stage_b_srcs(const DmaPlan<C>& pl, const TileOps
   const int kb0 = s * C::RBB;
   unroll<C::DB>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    src[i] = select_ptr(kb0 + pl.kB[i] < kcb, t.b + pl.offB[i] + kb0, zero);
+    src[i] = select_ptr(kb0 + pl.kB[i] < kcb, t.b + s * pl.bstep + pl.offB[i], zero);
   });
 }
 template <class C>
@@ -409,6 +433,7 @@ struct FastPlan {
   // scale operand it reads and that operand's bytes per stage
   const uint8_t *a, *b, *s[C::DSA], *sb;
   int64_t sstep[C::DSA], sbstep;
+  int64_t astep, bstep;  // data bytes per stage (as in DmaPlan)
 };
 
 // A wave-uniform pointer moved to scalar registers (the tile bases are
@@ -433,6 +458,8 @@ __device__ __forceinline__ void plan_fast(FastPlan<C>& fp, const DmaPlan<C>& pl,
   unroll<C::DB>([&](auto ic) { fp.vB[decltype(ic)::value] = pl.offB[decltype(ic)::value]; });
   fp.a = uniform_ptr(t.a);
   fp.b = uniform_ptr(t.b);
+  fp.astep = pl.astep;
+  fp.bstep = pl.bstep;
   if constexpr (C::F32S) {
     // one fp32 per row and 128-element block: row offsets; the stage adds its
     // block's offset (sstep / sbstep bytes per block)
@@ -490,7 +517,7 @@ __device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, u
   uint32_t ln = (uint32_t)lane;
   asm volatile("" : "+v"(ln));  // recomputed here, not hoisted out of the loop
   const uint32_t wu = (uint32_t)w;
-  const uint8_t* abase = lp.a + s * C::RBA;
+  const uint8_t* abase = lp.a + s * data_off<C>(0, C::RBA, lda);
   unroll<C::DA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     if constexpr (i >= Q0 && i < Q1) {
@@ -498,7 +525,7 @@ __device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, u
       const int r = (int)(o / C::RBA);
       const int c = swz<C::CPA>(r, (int)(o % C::RBA) / 16);
       const int rr = r < lp.mlast ? r : lp.mlast;
-      dma16(abase + (uint32_t)(rr * lda + c * 16), st + C::A_OFF + (i * C::NW + w) * 1024);
+      dma16(abase + (uint32_t)data_off<C>(rr, c * 16, lda), st + C::A_OFF + (i * C::NW + w) * 1024);
     }
   });
   const int blk = s * C::BK / 128;  // the stage's 128-element block
@@ -521,7 +548,7 @@ __device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, u
       dma4(bsb + ro, st + C::BS_OFF + (i * C::NW + w) * 256);
     }
   });
-  const uint8_t* bbase = lp.b + s * C::RBB;
+  const uint8_t* bbase = lp.b + s * data_off<C>(0, C::RBB, ldb);
   unroll<C::DB>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     if constexpr (QB + i >= Q0 && QB + i < Q1) {
@@ -529,7 +556,7 @@ __device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, u
       const int r = (int)(o / C::RBB);
       const int c = swz<C::CPB>(r, (int)(o % C::RBB) / 16);
       const int rr = r < lp.nlast ? r : lp.nlast;
-      dma16(bbase + (uint32_t)(rr * ldb + c * 16), st + C::B_OFF + (i * C::NW + w) * 1024);
+      dma16(bbase + (uint32_t)data_off<C>(rr, c * 16, ldb), st + C::B_OFF + (i * C::NW + w) * 1024);
     }
   });
 }
@@ -541,7 +568,7 @@ template <class C, int PART = -1>
 __device__ __forceinline__ void issue_stage_fast(const FastPlan<C>& fp, int s, uint8_t* st, int w) {
   constexpr bool DO_A = PART != 1, DO_B = PART != 0;
   if constexpr (DO_A) {
-    const uint8_t* base = fp.a + s * C::RBA;
+    const uint8_t* base = fp.a + s * fp.astep;
     unroll<C::DA>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       dma16(base + fp.vA[i], st + C::A_OFF + (i * C::NW + w) * 1024);
@@ -564,7 +591,7 @@ __device__ __forceinline__ void issue_stage_fast(const FastPlan<C>& fp, int s, u
     }
   }
   if constexpr (DO_B) {
-    const uint8_t* base = fp.b + s * C::RBB;
+    const uint8_t* base = fp.b + s * fp.bstep;
     unroll<C::DB>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       dma16(base + fp.vB[i], st + C::B_OFF + (i * C::NW + w) * 1024);
@@ -1131,7 +1158,7 @@ __device__ __forceinline__ void persistent_loop(Src& src, uint8_t* smem, int64_t
                                          });
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (FAST) {
-          bbase = fplan.b + (dummy ? 0 : is) * C::RBB;
+          bbase = fplan.b + (dummy ? 0 : is) * fplan.bstep;
           unroll<C::DB>([&](auto ic) { bvoff[decltype(ic)::value] = fplan.vB[decltype(ic)::value]; });
         } else {
           stage_b_srcs<C>(plan, iops, is, dummy, zero, bsrc);
@@ -1578,8 +1605,8 @@ struct WgradSource {
     // segment start: element bytes (E4M3: 1, E2M1: 1/2); scales, MX
     // block-major (block p0/32, row row0), blockwise block-major too (fp32,
     // block p0/128, row row0)
-    o.a = p.a + (int64_t)q.row0 * p.lda + (C::AFP8 ? q.p0 : q.p0 / 2);
-    o.b = p.b + (int64_t)q.col0 * p.ldb + (C::BFP8 ? q.p0 : q.p0 / 2);
+    o.a = p.a + data_off<C>(q.row0, C::AFP8 ? q.p0 : q.p0 / 2, p.lda);
+    o.b = p.b + data_off<C>(q.col0, C::BFP8 ? q.p0 : q.p0 / 2, p.ldb);
     if constexpr (C::F32S) {
       o.as = p.as + q.p0 / 128 * p.ldas + (int64_t)q.row0 * 4;
       o.bs = p.bs + q.p0 / 128 * p.ldbs + (int64_t)q.col0 * 4;
@@ -1743,13 +1770,14 @@ using CfgA8W = TileCfg<256, 256, 2, 4, 64, 3, kA8A8, 1, 5>;
 using CfgA8 = TileCfg<256, 256, 2, 4, 128, 2, kA8W4, 1, 3>;
 // blockwise FP8: four waves (one per SIMD) each hold a 64x64 accumulator and
 // its per-128 partial; B scale rows are shared by 128 weight rows in the
-// forward, one per row in the weight gradient
+// forward, one per row in the weight gradient (whose column-wise operands
+// are stored in 64-byte K blocks)
 using CfgBlkF = TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 128>;
-using CfgBlkW = TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 1>;
+using CfgBlkW = KBlocked<TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 1>>;
 // blockwise FP8 with power-of-two scales: the a4w4 loop (8 waves, 256x256)
 // with E4M3 on both sides; a 64-deep stage holds 16 KiB of each operand
 using CfgP2F = TileCfg<256, 256, 2, 4, 64, 3, kBlkP2, 1, 5, 128>;
-using CfgP2W = TileCfg<256, 256, 2, 2, 64, 4, kBlkP2, 1, 8, 1>;
+using CfgP2W = KBlocked<TileCfg<256, 256, 2, 2, 64, 4, kBlkP2, 1, 8, 1>>;
 
 template <class C, class K, class P>
 static hipError_t launch_persistent(K kernel, const P& p, int64_t tiles, int num_cus, hipStream_t st) {

@@ -8,8 +8,10 @@
 //   128x128          weights: square blocks; scales f32 [rows/128, cols/128].
 //   1x128 column-wise, segment-padded: the wgrad operands; each expert's rows
 //                    transposed, padded with zeros to a multiple of 128, blocks
-//                    of 128 along the padded length; scales f32 [mpad/128, cols]
-//                    (block-major).
+//                    of 128 along the padded length; codes in 64-byte K blocks,
+//                    u8 [mpad/64, cols, 64] (the weight gradient's DMA reads a
+//                    tile's 64-byte row pieces of one block as one run); scales
+//                    f32 [mpad/128, cols] (block-major).
 //
 // Scale rule and encoder: blk_round.hpp. In power-of-two mode the codes come
 // from gfx950's scaled conversion with the stored scale 2^-t as its operand
@@ -266,7 +268,8 @@ __global__ __launch_bounds__(256) void quant_colwise_1x128_kernel(const uint16_t
   amax = max(max(qmax[0][c], qmax[1][c]), max(qmax[2][c], qmax[3][c]));
   if (c >= ncol) return;
   const BlkScale bs = blk_scale<POW2>(amax);
-  uint8_t* qp = q + (c0 + c) * mpad + p0 + b * 32;
+  // 64-byte K block (p0 + 32 b) / 64 of column c0 + c
+  uint8_t* qp = q + ((p0 + b * 32) / 64 * cols + c0 + c) * 64 + (b & 1) * 32;
   uint32_t o[8];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -385,7 +388,7 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(const uint16_t* _
       o[2 * d] = e.x;
       o[2 * d + 1] = e.y;
     }
-    uint8_t* qp = qc + (c0 + c) * mpad + p0 + b * 32;
+    uint8_t* qp = qc + ((p0 + b * 32) / 64 * cols + c0 + c) * 64 + (b & 1) * 32;
     reinterpret_cast<uint4*>(qp)[0] = make_uint4(o[0], o[1], o[2], o[3]);
     reinterpret_cast<uint4*>(qp)[1] = make_uint4(o[4], o[5], o[6], o[7]);
     if (b == 0) sc[p0 / 128 * cols + c0 + c] = bs.stored;

@@ -37,6 +37,15 @@ def mx_scales_rowmajor(t, rows: int) -> np.ndarray:
     return np.ascontiguousarray(a[:, :rows].T)
 
 
+def kblocked_rows(t) -> np.ndarray:
+    """1x128 column-wise codes are stored in 64-byte blocks along the padded
+    length, u8 [mpad/64, cols, 64]; the oracle keeps rows, [cols, mpad]."""
+    a = host(t)
+    nb, cols, w = a.shape
+    assert w == 64, a.shape
+    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(cols, nb * 64))
+
+
 def host_bf16_f64(t) -> np.ndarray:
     return bf16_bits_to_f64(t.detach().view(torch.int16).cpu().numpy().view(np.uint16))
 

@@ -12,7 +12,7 @@ from oracle import blockwise as ob
 from oracle import grouped as og
 from synth import bf16_normal, f32_normal, fp32_to_bf16_bits, splits_for
 
-from .gpu_util import assert_gemm_close, dev_bf16, dev_f32, have_gpu, host, host_bf16_f64
+from .gpu_util import assert_gemm_close, dev_bf16, dev_f32, have_gpu, host, host_bf16_f64, kblocked_rows
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
 
@@ -107,7 +107,8 @@ def test_quantize_colwise_1x128(pow2, case):
     rq, rs = ob.quantize_colwise_segpad_128(x, splits, pow2=pow2)
     assert mpad == rq.shape[1]
     assert s.shape == (mpad // 128, cols)  # block-major
-    assert np.array_equal(host(q), rq.astype(np.uint8))
+    assert q.shape == (mpad // 64, cols, 64)  # 64-byte K blocks
+    assert np.array_equal(kblocked_rows(q), rq.astype(np.uint8))
     assert np.array_equal(host(s).T.copy().view(np.uint32), rs.astype(np.float32).view(np.uint32))
 
 
@@ -307,7 +308,8 @@ def test_c5_full_size_wgrad_sampled(c5, p2):
         # oracle quantization of the expert's columns, compared with the library's
         rd, rds = ob.quantize_colwise_segpad_128(_bits(dy[r0:r1][:, torch.as_tensor(ns, device="cuda")]), [r1 - r0])
         rx, rxs = ob.quantize_colwise_segpad_128(_bits(a[r0:r1][:, torch.as_tensor(ks, device="cuda")]), [r1 - r0])
-        assert np.array_equal(host(dq[torch.as_tensor(ns, device="cuda")][:, p0:p1]), rd.astype(np.uint8))
+        assert np.array_equal(kblocked_rows(dq[p0 // 64:p1 // 64][:, torch.as_tensor(ns, device="cuda")]),
+                              rd.astype(np.uint8))
         assert np.array_equal(host(xs[p0 // 128:p1 // 128][:, torch.as_tensor(ks, device="cuda")]).T,
                               rxs.astype(np.float32))
         ref = ob.dequantize_1x128(rd, rds) @ ob.dequantize_1x128(rx, rxs).T

@@ -44,10 +44,10 @@ EXPECTED = {
     # MXFP8 weight gradient (DPS 5, general issue) and power-of-two blockwise
     # weight gradient (DPS 6, scalar-base issue), every output mode
     "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi4ELi1ELi5ELi1EEELb0E": [5],
-    # blockwise FP8 weight gradient, power-of-two scales: 4 waves, stage
-    # read-ahead, 4-stage ring, DPS 10, two steps per loop iteration (every
-    # output mode)
-    "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi2ELi64ELi4ELi3ELi1ELi8ELi1EEELb1E": [10, 10],
+    # blockwise FP8 weight gradient, power-of-two scales (operands in 64-byte
+    # K blocks): 4 waves, stage read-ahead, 4-stage ring, DPS 10, two steps
+    # per loop iteration (every output mode)
+    "grouped_wgrad_kernelINS_8KBlockedINS_7TileCfgILi256ELi256ELi2ELi2ELi64ELi4ELi3ELi1ELi8ELi1EEEEELb1E": [10, 10],
 }
 
 
