@@ -287,24 +287,31 @@ def test_c5_full_size_fwd_sampled(c5, p2):
         assert_gemm_close(gpu, ref, what=f"c5 fwd expert {g}")
 
 
+@pytest.mark.parametrize("mode", ["bf16-overwrite", "fp32-accumulate"])
 @pytest.mark.parametrize("p2", [False, True], ids=["general", "pow2"])
-def test_c5_full_size_wgrad_sampled(c5, p2):
+def test_c5_full_size_wgrad_sampled(c5, p2, mode):
     G, M, K, N, sp, a = (c5[k] for k in ("G", "M", "K", "N", "sp", "a"))
     fmt = "fp8_1x128_p2" if p2 else "fp8_1x128"
     gen = torch.Generator(device="cuda").manual_seed(78)
     dy = torch.randn((M, N), generator=gen, device="cuda").to(torch.bfloat16)
     dq, ds, mpad = mxg.quantize_colwise_segpad(dy, sp, fmt)
     xq, xs, _ = mxg.quantize_colwise_segpad(a, sp, fmt)
-    out = torch.empty((G, N, K), dtype=torch.bfloat16, device="cuda")
-    mxg.grouped_wgrad(dq, ds, xq, xs, sp, N, K, mpad, out, accumulate=False, fmt=fmt)
-    torch.cuda.synchronize()
+    acc = mode == "fp32-accumulate"
+    if acc:  # main_grad [G, N, K] fp32 (7.5 GB) accumulated in place
+        out = torch.randn((G, N, K), generator=gen, device="cuda", dtype=torch.float32)
+    else:
+        out = torch.empty((G, N, K), dtype=torch.bfloat16, device="cuda")
     rng = np.random.default_rng(6)
+    picks = [(int(g), rng.choice(N, size=8, replace=False), rng.choice(K, size=8, replace=False))
+             for g in rng.choice(np.nonzero(sp)[0], size=4, replace=False)]
+    before = {g: host(out[g][torch.as_tensor(ns, device="cuda")][:, torch.as_tensor(ks, device="cuda")])
+              for g, ns, ks in picks} if acc else {}
+    mxg.grouped_wgrad(dq, ds, xq, xs, sp, N, K, mpad, out, accumulate=acc, fmt=fmt)
+    torch.cuda.synchronize()
     row_offs, pad_offs = np.concatenate([[0], np.cumsum(sp)]), np.concatenate([[0], np.cumsum((sp + 127) // 128 * 128)])
-    for g in rng.choice(np.nonzero(sp)[0], size=4, replace=False):
+    for g, ns, ks in picks:
         p0, p1 = int(pad_offs[g]), int(pad_offs[g + 1])
         r0, r1 = int(row_offs[g]), int(row_offs[g + 1])
-        ns = rng.choice(N, size=8, replace=False)
-        ks = rng.choice(K, size=8, replace=False)
         # oracle quantization of the expert's columns, compared with the library's
         rd, rds = ob.quantize_colwise_segpad_128(_bits(dy[r0:r1][:, torch.as_tensor(ns, device="cuda")]), [r1 - r0])
         rx, rxs = ob.quantize_colwise_segpad_128(_bits(a[r0:r1][:, torch.as_tensor(ks, device="cuda")]), [r1 - r0])
@@ -313,5 +320,10 @@ def test_c5_full_size_wgrad_sampled(c5, p2):
         assert np.array_equal(host(xs[p0 // 128:p1 // 128][:, torch.as_tensor(ks, device="cuda")]).T,
                               rxs.astype(np.float32))
         ref = ob.dequantize_1x128(rd, rds) @ ob.dequantize_1x128(rx, rxs).T
-        gpu = host_bf16_f64(out[g][torch.as_tensor(ns, device="cuda")][:, torch.as_tensor(ks, device="cuda")])
-        assert_gemm_close(gpu, ref, what=f"c5 wgrad expert {g}")
+        sample = out[g][torch.as_tensor(ns, device="cuda")][:, torch.as_tensor(ks, device="cuda")]
+        if acc:
+            ref = ref + before[g].astype(np.float64)
+            gpu = host(sample).astype(np.float64)
+        else:
+            gpu = host_bf16_f64(sample)
+        assert_gemm_close(gpu, ref, what=f"c5 wgrad {mode} expert {g}")

@@ -274,7 +274,8 @@ def test_fc1_dgrad_full_size_sampled(fc1):
     assert_gemm_close(gdx[np.ix_(rows, kcols)], ref, what="fc1 dgrad")
 
 
-def test_fc1_wgrad_full_size_sampled(fc1):
+@pytest.mark.parametrize("accumulate", [True, False], ids=["accumulate", "overwrite"])
+def test_fc1_wgrad_full_size_sampled(fc1, accumulate):
     K, N, G, sp = fc1["K"], fc1["N"], fc1["G"], fc1["sp"]
     dq, ds, mpad = mxg.quantize_colwise_segpad(dev_bf16(fc1["dy"]), sp, "mxfp4")
     xq, xs, _ = mxg.quantize_colwise_segpad(dev_bf16(fc1["a"]), sp, "mxfp4")
@@ -283,12 +284,16 @@ def test_fc1_wgrad_full_size_sampled(fc1):
     m0 = {}
     rng = np.random.default_rng(12)
     experts = [g for g in range(G) if sp[g] > 0][::5] + [int(np.argmax(sp))]
+    empty = [g for g in range(G) if sp[g] == 0]
     picks = {g: (np.sort(rng.choice(N, 16, replace=False)), np.sort(rng.choice(K, 16, replace=False)))
              for g in experts}
     for g, (ns, ks) in picks.items():
         m0[g] = host(main0[g][np.ix_(ns, ks)]).astype(np.float64)
-    mxg.grouped_wgrad(dq, ds, xq, xs, sp, N, K, mpad, main0, accumulate=True)
+    e0 = {g: host(main0[g][:8, :8]) for g in empty}
+    mxg.grouped_wgrad(dq, ds, xq, xs, sp, N, K, mpad, main0, accumulate=accumulate)
     torch.cuda.synchronize()
+    for g in empty:  # experts without tokens: untouched when accumulating, zero-filled when overwriting
+        assert np.array_equal(host(main0[g][:8, :8]), e0[g] if accumulate else np.zeros((8, 8), np.float32)), g
     offs = fc1["offs"]
     gpu_all, ref_all = [], []
     for g, (ns, ks) in picks.items():
@@ -296,7 +301,7 @@ def test_fc1_wgrad_full_size_sampled(fc1):
         rd, rds = omx.quantize_colwise_segpad(np.ascontiguousarray(fc1["dy"][seg][:, ns]), [sp[g]], "mxfp4")
         rx, rxs = omx.quantize_colwise_segpad(np.ascontiguousarray(fc1["a"][seg][:, ks]), [sp[g]], "mxfp4")
         ref = og.grouped_wgrad(omx.dequantize_rowwise(rd, rds, "mxfp4"), omx.dequantize_rowwise(rx, rxs, "mxfp4"),
-                               [sp[g]], main_grad0=m0[g][None], accumulate=True)[0]
+                               [sp[g]], main_grad0=m0[g][None], accumulate=accumulate)[0]
         gpu_all.append(host(main0[g][np.ix_(ns, ks)]).astype(np.float64))
         ref_all.append(ref)
-    assert_gemm_close(np.stack(gpu_all), np.stack(ref_all), what="fc1 wgrad accumulate")
+    assert_gemm_close(np.stack(gpu_all), np.stack(ref_all), what=f"fc1 wgrad accumulate={accumulate}")
