@@ -208,7 +208,7 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
   const SplitArgs sp = make_splits(m_splits, G);
   if (is_mx(fmt))
     c = hip_status(launch_quant_colwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8,
-                                           mfma, static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), mpad,
+                                           mfma, static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), mpad, cus,
                                            stream),
                    "column-wise quantizer launch");
   else

@@ -99,7 +99,8 @@ hipError_t launch_quant_dual_mx(const uint16_t* x, int64_t rows, int64_t cols, i
                                 bool fp8, bool mfma, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc, int64_t mpad,
                                 int num_cus, hipStream_t st);
 hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
-                                   bool fp8, bool mfma, uint8_t* q, uint8_t* s, int64_t mpad, hipStream_t st);
+                                   bool fp8, bool mfma, uint8_t* q, uint8_t* s, int64_t mpad, int num_cus,
+                                   hipStream_t st);
 
 // MX scales from one layout (mxgg_scale_layout value) into another
 hipError_t launch_relayout_scales(const uint8_t* src, int src_layout, int64_t rows, int64_t blocks, int dst_layout,
