@@ -527,8 +527,9 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
         w, dy = normal((G * N, K), wl["w_std"], seed=SEED_W), normal((M, N), seed=SEED_DY)
         wq, ws = mxg.quantize_rowwise(w, "fp8_128x128_p2")
         del w
-        dq, ds = torch.empty((M, N), **u8), torch.empty((N // 128, M), **f32)  # 1x128 scales block-major
-        tq, ts = torch.empty((G * K, N), **u8), torch.empty((G * K // 128, N // 128), **f32)
+        # blockwise codes in 64-byte K blocks, 1x128 scales block-major
+        dq, ds = torch.empty((N // 64, M, 64), **u8), torch.empty((N // 128, M), **f32)
+        tq, ts = torch.empty((N // 64, G * K, 64), **u8), torch.empty((G * K // 128, N // 128), **f32)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         ops = [
             ("quant_dY_1x128", "quant", lambda: mxg.quantize_rowwise(dy, "fp8_1x128_p2", q=dq, scales=ds)),
@@ -554,8 +555,9 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
         a, w = normal((M, K), seed=SEED_A), normal((G * N, K), wl["w_std"], seed=SEED_W)
         dy = normal((M, N), seed=SEED_DY)
         mpad = mxg.segpad_rows(sp, "fp8_1x128")
-        aq, as_ = torch.empty((M, K), **u8), torch.empty((K // 128, M), **f32)  # 1x128 scales block-major
-        wq, ws = torch.empty((G * N, K), **u8), torch.empty((G * N // 128, K // 128), **f32)
+        # blockwise codes in 64-byte K blocks, 1x128 scales block-major
+        aq, as_ = torch.empty((K // 64, M, 64), **u8), torch.empty((K // 128, M), **f32)
+        wq, ws = torch.empty((K // 64, G * N, 64), **u8), torch.empty((G * N // 128, K // 128), **f32)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         # column-wise 1x128 codes in 64-byte K blocks, scales block-major
         dcq, dcs = torch.empty((mpad // 64, N, 64), **u8), torch.empty((mpad // 128, N), **f32)

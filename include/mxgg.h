@@ -48,6 +48,11 @@
  *                     run.
  *   MXGG_FP8_128x128  E4M3 elements, one fp32 scale per 128x128 block
  *                     (weights).
+ *                     Blockwise E4M3 codes of an operand with L bytes per row
+ *                     are stored in 64-byte blocks along the row, u8 [L/64,
+ *                     rows, 64]: byte j of row r at ((j/64)*rows + r)*64 +
+ *                     j%64, so the 64 bytes a GEMM stage needs from each of a
+ *                     tile's rows are one contiguous run.
  *   MXGG_FP8_1x128_P2, MXGG_FP8_128x128_P2
  *                     The same layouts with every scale a power of two (what
  *                     the quantizers write with MXGG_POW2_SCALES; given to a
@@ -205,7 +210,8 @@ mxgg_status mxgg_mx_scales_relayout(const void* src, mxgg_scale_layout src_layou
  *           MXGG_FP8_1x128: blocks of 128 along cols (cols % 128 == 0).
  *           MXGG_FP8_128x128: 128x128 blocks (rows % 128 == 0, cols % 128 == 0).
  *   flags   MXGG_POW2_SCALES for the blockwise formats (ignored for MX).
- *   q       MXFP4: u8 [rows, cols/2]; otherwise u8 [rows, cols] (E4M3 codes).
+ *   q       MXFP4: u8 [rows, cols/2]; MXFP8: u8 [rows, cols]; blockwise: E4M3
+ *           codes u8 [cols/64, rows, 64] (64-byte blocks along cols).
  *   scales  MX: u8 [cols/32, R4] (block-major, R4 = mxgg_mx_scale_stride(rows)),
  *           or with MXGG_LAYOUT_MFMA u8 [cols/128, R32/32, 64, 2];
  *           FP8_1x128: f32 [cols/128, rows] (block-major);
@@ -283,8 +289,9 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
  * same scale per block ("Add ROCm Triton blockwise FP8 grouped GEMM", weight
  * blocks used in both passes).
  *   w_q, w_s    from mxgg_quantize_rowwise(W as [G*N, K], MXGG_FP8_128x128):
- *               E4M3 [G*N, K] + f32 [G*N/128, K/128].
- *   wt_q, wt_s  written: E4M3 [G*K, N] (expert g's rows [g*K, (g+1)*K)) +
+ *               E4M3 u8 [K/64, G*N, 64] + f32 [G*N/128, K/128].
+ *   wt_q, wt_s  written: E4M3 u8 [N/64, G*K, 64] (the [G*K, N] transpose in
+ *               64-byte blocks along N; expert g's rows [g*K, (g+1)*K)) +
  *               f32 [G*K/128, N/128]. Caller-owned; must not overlap w.
  * N % 128 == 0, K % 128 == 0, N, K < 2^23, G in [1, 512].
  * Errors: NULL, SHAPE, ALIGN, DEVICE, ARCH, HIP.
@@ -300,13 +307,13 @@ mxgg_status mxgg_transpose_128x128(const void* w_q, const void* w_s, int32_t G, 
  * weights; "route te.GroupedLinear through #723; a8w4 fwd-only": the a8w4
  * pair; "Add ROCm Triton blockwise FP8 grouped GEMM": the blockwise pair).
  *   a_q, a_s  A quantized row-wise along K: (MXFP4: u8 [M, K/2] | MXFP8: u8 [M, K])
- *             + u8 [K/32, mxgg_mx_scale_stride(M)]; or MXGG_FP8_1x128: u8 [M, K]
- *             + f32 [K/128, M].
+ *             + u8 [K/32, mxgg_mx_scale_stride(M)]; or MXGG_FP8_1x128: u8
+ *             [K/64, M, 64] + f32 [K/128, M] (M < 2^25).
  *   w_q, w_s  packed expert weights [G*N, K] quantized row-wise along K:
  *             MXFP4 u8 [G*N, K/2] + u8 [K/32, G*N], or with w_fmt =
  *             MXGG_MXFP4 | MXGG_LAYOUT_MFMA the scales u8 [K/128, G*N/32,
- *             64, 2] (K % 128 == 0); or MXGG_FP8_128x128: u8 [G*N, K] + f32
- *             [G*N/128, K/128].
+ *             64, 2] (K % 128 == 0); or MXGG_FP8_128x128: u8 [K/64, G*N, 64]
+ *             + f32 [G*N/128, K/128] (G*N < 2^25).
  *   format pairs (a_fmt, w_fmt): (MXFP4, MXFP4) a4w4, (MXFP8, MXFP4) a8w4,
  *             (FP8_1x128, FP8_128x128) blockwise FP8. a_fmt takes no layout
  *             bits other than block-major.
@@ -337,13 +344,14 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
  *                  dy_s stays block-major.
  *   dy_q, dy_s     dY quantized row-wise along N: MX, u8 [M, N/2] (E2M1) or
  *                  [M, N] (E4M3) + u8 [N/32, mxgg_mx_scale_stride(M)];
- *                  blockwise, E4M3 [M, N] + f32 [N/128, M].
+ *                  blockwise, E4M3 u8 [N/64, M, 64] + f32 [N/128, M] (M < 2^25).
  *   wcol_q, wcol_s MX: W quantized along N with mxgg_quantize_colwise_segpad
  *                  on W as [G*N, K] with splits {N, ..., N}: u8 [K, G*N/2] +
  *                  u8 [G*N/32, K] (expert g owns columns [g*N, (g+1)*N) and
  *                  scale blocks [g*N/32, (g+1)*N/32)).
- *                  Blockwise: W^T from mxgg_transpose_128x128, E4M3
- *                  [G*K, N] + f32 [G*K/128, N/128]. MXGG_FP8_1x128_P2
+ *                  Blockwise: W^T from mxgg_transpose_128x128, E4M3 u8
+ *                  [N/64, G*K, 64] + f32 [G*K/128, N/128] (G*K < 2^25).
+ *                  MXGG_FP8_1x128_P2
  *                  asserts that the scales of BOTH operands (dY's and the
  *                  transposed weights') are powers of two, and the MFMA then
  *                  applies them (a non-power-of-two scale would lose its

@@ -173,16 +173,24 @@ def _layout_shape(layout, rows, blocks):
 
 
 def _q_shape(f, rows, cols):
-    """Quantized data of a [rows, cols] operand packed along cols."""
+    """Codes of a [rows, cols] operand quantized along cols: MX, rows of
+    codes (E2M1 packed two per byte); blockwise E4M3, 64-byte blocks along
+    cols, u8 [cols/64, rows, 64]."""
+    if not _is_mx(f):
+        return (cols // 64, rows, 64)
     return (rows, cols // 2 if (f & 0xFF) == MXFP4 else cols)
 
 
+def _q_rows(q, f):
+    """Row count of a code tensor laid out as _q_shape gives it (a tensor of
+    another rank then fails the shape check that follows)."""
+    if _is_mx(f):
+        return q.shape[0] if q.dim() >= 1 else 0
+    return q.shape[1] if q.dim() >= 2 else 0
+
+
 def _col_q_shape(f, cols, mpad):
-    """Codes of the column-wise segment-padded [cols, mpad] operand: rows of
-    codes, or for 1x128 64-byte blocks along the padded length, u8 [mpad/64,
-    cols, 64]."""
-    if (f & 0xFF) in (FP8_1x128, FP8_1x128_P2):
-        return (mpad // 64, cols, 64)
+    """Codes of the column-wise segment-padded [cols, mpad] operand."""
     return _q_shape(f, cols, mpad)
 
 
@@ -328,8 +336,8 @@ def mxgg_grouped_fwd(a_q, a_s, w_q, w_s, m_splits, N, K, a_fmt="mxfp4", w_fmt="m
     """out[M, N] (bf16) = per-expert A . W_g^T; W packed [G*N, ...]."""
     torch = _torch()
     arr, G = _splits(m_splits)
-    M = a_q.shape[0]
     af, wf = _fmt(a_fmt), _fmt(w_fmt)
+    M = _q_rows(a_q, af)
     _expect(a_q, "a_q", _q_shape(af, M, K), torch.uint8)
     _expect(a_s, "a_s", _row_scale_shape(af, M, K), _sdtype(af))
     _expect(w_q, "w_q", _q_shape(wf, G * N, K), torch.uint8)
@@ -345,15 +353,16 @@ def mxgg_grouped_fwd(a_q, a_s, w_q, w_s, m_splits, N, K, a_fmt="mxfp4", w_fmt="m
 
 def mxgg_transpose_128x128(w_q, w_s, G, N, K, wt_q=None, wt_s=None):
     """128x128-block FP8 weights [G*N, K] (+ f32 [G*N/128, K/128]) transposed
-    to [G*K, N] (+ f32 [G*K/128, N/128]): the input gradient's weights."""
+    to [G*K, N] (+ f32 [G*K/128, N/128]): the input gradient's weights (codes
+    in 64-byte K blocks on both sides)."""
     torch = _torch()
     if wt_q is None:
-        wt_q = torch.empty((G * K, N), dtype=torch.uint8, device=w_q.device)
+        wt_q = torch.empty(_q_shape(FP8_128x128, G * K, N), dtype=torch.uint8, device=w_q.device)
     if wt_s is None:
         wt_s = torch.empty((G * K // 128, N // 128), dtype=torch.float32, device=w_q.device)
-    _expect(w_q, "w_q", (G * N, K), torch.uint8)
+    _expect(w_q, "w_q", _q_shape(FP8_128x128, G * N, K), torch.uint8)
     _expect(w_s, "w_s", (G * N // 128, K // 128), torch.float32)
-    _expect(wt_q, "wt_q", (G * K, N), torch.uint8)
+    _expect(wt_q, "wt_q", _q_shape(FP8_128x128, G * K, N), torch.uint8)
     _expect(wt_s, "wt_s", (G * K // 128, N // 128), torch.float32)
     _check(lib.mxgg_transpose_128x128(_ptr(w_q), _ptr(w_s), G, N, K, _ptr(wt_q), _ptr(wt_s), _stream(w_q)))
     return wt_q, wt_s
@@ -365,8 +374,8 @@ def mxgg_grouped_dgrad(dy_q, dy_s, wcol_q, wcol_s, m_splits, N, K, fmt="mxfp4", 
     with W^T from mxgg_transpose_128x128."""
     torch = _torch()
     arr, G = _splits(m_splits)
-    M = dy_q.shape[0]
     f = _fmt(fmt)
+    M = _q_rows(dy_q, f)
     # layout bits of fmt describe wcol_s; dY's scales are block-major
     _expect(dy_q, "dy_q", _q_shape(f, M, N), torch.uint8)
     _expect(dy_s, "dy_s", _row_scale_shape(f & 0xFF, M, N), _sdtype(f))
@@ -374,7 +383,7 @@ def mxgg_grouped_dgrad(dy_q, dy_s, wcol_q, wcol_s, m_splits, N, K, fmt="mxfp4", 
         _expect(wcol_q, "wcol_q", _q_shape(MXFP4, K, G * N), torch.uint8)
         _expect(wcol_s, "wcol_s", _col_scale_shape(MXFP4 | (f & LAYOUT_MASK), K, G * N), torch.uint8)
     else:                               # transposed 128x128 blocks
-        _expect(wcol_q, "wcol_q", (G * K, N), torch.uint8)
+        _expect(wcol_q, "wcol_q", _q_shape(FP8_128x128, G * K, N), torch.uint8)
         _expect(wcol_s, "wcol_s", (G * K // 128, N // 128), torch.float32)
     if dx is None:
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy_q.device)

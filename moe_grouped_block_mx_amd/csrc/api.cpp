@@ -280,18 +280,18 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
   RowsGemmParams p;
   std::memset(&p, 0, sizeof(p));
   if (a_fmt == MXGG_FP8_1x128) {
-    // E4M3 x E4M3; A scales f32 [K/128, M] (block-major), W scales f32
-    // [G*N/128, K/128]
+    // E4M3 x E4M3 in 64-byte K blocks (A [K/64, M, 64], W [K/64, G*N, 64]);
+    // A scales f32 [K/128, M] (block-major), W scales f32 [G*N/128, K/128]
     p.a = static_cast<const uint8_t*>(a_q);
     p.as = static_cast<const uint8_t*>(a_s);
     p.b = static_cast<const uint8_t*>(w_q);
     p.bs = static_cast<const uint8_t*>(w_s);
     p.c = static_cast<uint16_t*>(out);
-    p.lda = K;
+    p.lda = M * 64;  // bytes per K block
     p.ldas = M * 4;
-    p.ldb = K;
+    p.ldb = (int64_t)G * N * 64;
     p.ldbs = K / 128 * 4;
-    p.b_gstride = N * K;
+    p.b_gstride = N * 64;  // expert g's rows start at g*N in every K block
     p.bs_gstride = N / 128 * (K / 128 * 4);
     p.ldc = N;
     p.n_out = (int32_t)N;
@@ -348,13 +348,14 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
   p.kc = (int32_t)N;
   p.sp = make_splits(m_splits, G);
   if (fmt == MXGG_FP8_1x128) {
-    // dY E4M3 [M, N] + f32 [N/128, M]; W^T E4M3 [G*K, N] + f32 [G*K/128, N/128]
+    // dY E4M3 [N/64, M, 64] + f32 [N/128, M]; W^T E4M3 [N/64, G*K, 64] + f32
+    // [G*K/128, N/128]
     // (the 128x128 blocks of W, transposed: same codes, same scales)
-    p.lda = N;
+    p.lda = M * 64;
     p.ldas = M * 4;
-    p.ldb = N;
+    p.ldb = (int64_t)G * K * 64;
     p.ldbs = N / 128 * 4;
-    p.b_gstride = K * N;
+    p.b_gstride = K * 64;
     p.bs_gstride = K / 128 * (N / 128 * 4);
     c = hip_status(launch_grouped_rows_blk(p, p2, true, cus, stream), "blockwise dgrad launch");
     return c.ok() ? ok() : finish(c);

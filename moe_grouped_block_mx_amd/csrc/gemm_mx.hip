@@ -181,8 +181,8 @@ struct MfmaB : C {
 };
 
 // A configuration whose A and B data are stored in 64-byte blocks along the
-// contraction, u8 [L/64, rows, 64] for rows of L bytes (the blockwise
-// column-wise operands of the weight gradient, segments padded to 128): byte
+// contraction, u8 [L/64, rows, 64] for rows of L bytes (the blockwise E4M3
+// operands: contractions and column-wise segments multiples of 128): byte
 // j of row r sits at (j/64)*ld + r*64 + j%64 with ld = rows*64, so the 64
 // bytes a stage needs from each of a tile's rows form one contiguous run per
 // 64-byte block (one 1 KiB run per DMA instruction instead of 16 row pieces).
@@ -1486,10 +1486,10 @@ struct RowsSource {
     const int col0 = q.nt * C::BN;
     const int nleft = p.n_out - col0;
     TileOps o;
-    o.a = p.a + rw.row0 * p.lda;
+    o.a = p.a + data_off<C>(rw.row0, 0, p.lda);
     // A's scales are block-major ([blocks, rows]: u8, or fp32 for 1x128)
     o.as = p.as + (C::F32S ? rw.row0 * 4 : rw.row0);
-    o.b = p.b + (int64_t)q.g * p.b_gstride + (int64_t)col0 * p.ldb;
+    o.b = p.b + (int64_t)q.g * p.b_gstride + data_off<C>(col0, 0, p.ldb);
     o.bs = p.bs + (int64_t)q.g * p.bs_gstride +
            (C::F32S ? (int64_t)(col0 / C::BDIV) * p.ldbs : C::MFB ? (int64_t)col0 * 4 : (int64_t)col0);
     o.mrows = rw.hi < C::BM ? rw.hi : C::BM;
@@ -1770,13 +1770,13 @@ using CfgA8W = TileCfg<256, 256, 2, 4, 64, 3, kA8A8, 1, 5>;
 using CfgA8 = TileCfg<256, 256, 2, 4, 128, 2, kA8W4, 1, 3>;
 // blockwise FP8: four waves (one per SIMD) each hold a 64x64 accumulator and
 // its per-128 partial; B scale rows are shared by 128 weight rows in the
-// forward, one per row in the weight gradient (whose column-wise operands
-// are stored in 64-byte K blocks)
-using CfgBlkF = TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 128>;
+// forward, one per row in the weight gradient. Every blockwise operand is
+// stored in 64-byte K blocks (KBlocked).
+using CfgBlkF = KBlocked<TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 128>>;
 using CfgBlkW = KBlocked<TileCfg<128, 128, 2, 2, 128, 3, kBlkFp8, 1, 0, 1>>;
 // blockwise FP8 with power-of-two scales: the a4w4 loop (8 waves, 256x256)
 // with E4M3 on both sides; a 64-deep stage holds 16 KiB of each operand
-using CfgP2F = TileCfg<256, 256, 2, 4, 64, 3, kBlkP2, 1, 5, 128>;
+using CfgP2F = KBlocked<TileCfg<256, 256, 2, 4, 64, 3, kBlkP2, 1, 5, 128>>;
 using CfgP2W = KBlocked<TileCfg<256, 256, 2, 2, 64, 4, kBlkP2, 1, 8, 1>>;
 
 template <class C, class K, class P>

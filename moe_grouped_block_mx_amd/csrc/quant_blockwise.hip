@@ -6,6 +6,9 @@
 //                    (block-major, as the GEMM's DMA reads them: a tile's rows
 //                    of one block are contiguous).
 //   128x128          weights: square blocks; scales f32 [rows/128, cols/128].
+// Every blockwise code tensor is stored in 64-byte blocks along its rows,
+// u8 [cols/64, rows, 64] (kblk_off): a GEMM stage's 64 bytes of each of a
+// tile's rows are one contiguous run.
 //   1x128 column-wise, segment-padded: the wgrad operands; each expert's rows
 //                    transposed, padded with zeros to a multiple of 128, blocks
 //                    of 128 along the padded length; codes in 64-byte K blocks,
@@ -30,6 +33,12 @@
 namespace mxgg {
 
 namespace {
+
+// Byte c (along the row) of row r of a code tensor with `rows` rows, in 64-byte
+// K blocks: u8 [cols/64, rows, 64].
+__device__ __forceinline__ int64_t kblk_off(int64_t r, int64_t c, int64_t rows) {
+  return (c >> 6) * rows * 64 + r * 64 + (c & 63);
+}
 
 typedef short v2s __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
@@ -90,10 +99,11 @@ __device__ __forceinline__ uint32_t amax8(const uint32_t (&wd)[4]) {
 // block. One workgroup per block: the 128 rows x 128 bytes are read with
 // 16-byte loads into LDS (dword pitch 33), then each thread transposes 4x4
 // byte squares in registers and writes output rows with 4-byte stores, 32
-// threads per 128-byte output row. HBM-bound: 1 B read and 1 B written per
-// element.
+// threads per 128-byte output row (both sides in 64-byte K blocks: W
+// [K/64, G*N, 64], W^T [N/64, G*K, 64]). HBM-bound: 1 B read and 1 B written
+// per element.
 __global__ __launch_bounds__(256) void transpose_128x128_kernel(const uint8_t* __restrict__ wq,
-                                                                const float* __restrict__ ws, int64_t N,
+                                                                const float* __restrict__ ws, int64_t G, int64_t N,
                                                                 int64_t K, uint8_t* __restrict__ tq,
                                                                 float* __restrict__ ts) {
   __shared__ uint32_t tile[128][33];
@@ -102,17 +112,16 @@ __global__ __launch_bounds__(256) void transpose_128x128_kernel(const uint8_t* _
   const int64_t g = b / (nbs * kbs);
   const int64_t rem = b - g * nbs * kbs;
   const int64_t nb = rem / kbs, kb = rem - nb * kbs;
-  const uint8_t* src = wq + (g * N + nb * 128) * K + kb * 128;
+  const int64_t wrows = G * N, trows = G * K;
   for (int c = threadIdx.x; c < 1024; c += 256) {
     const int r = c >> 3, q = c & 7;
-    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)r * K + q * 16);
+    const uint4 v = *reinterpret_cast<const uint4*>(wq + kblk_off(g * N + nb * 128 + r, kb * 128 + q * 16, wrows));
     tile[r][4 * q] = v.x;
     tile[r][4 * q + 1] = v.y;
     tile[r][4 * q + 2] = v.z;
     tile[r][4 * q + 3] = v.w;
   }
   __syncthreads();
-  uint8_t* dst = tq + (g * K + kb * 128) * N + nb * 128;
   for (int c = threadIdx.x; c < 1024; c += 256) {
     const int kq = c >> 5, nq = c & 31;  // output rows 4kq..4kq+3, bytes 4nq..4nq+3
     uint32_t d[4];
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(256) void transpose_128x128_kernel(const uint8_t* _
     for (int j = 0; j < 4; ++j) {
       const uint32_t o = ((d[0] >> (8 * j)) & 0xffu) | (((d[1] >> (8 * j)) & 0xffu) << 8) |
                          (((d[2] >> (8 * j)) & 0xffu) << 16) | (((d[3] >> (8 * j)) & 0xffu) << 24);
-      *reinterpret_cast<uint32_t*>(dst + (int64_t)(4 * kq + j) * N + 4 * nq) = o;
+      *reinterpret_cast<uint32_t*>(tq + kblk_off(g * K + kb * 128 + 4 * kq + j, nb * 128 + 4 * nq, trows)) = o;
     }
   }
   if (threadIdx.x == 0) ts[(g * kbs + kb) * nbs + nb] = ws[(g * nbs + nb) * kbs + kb];
@@ -142,7 +151,6 @@ __global__ __launch_bounds__(256) void quant_rowwise_1x128_kernel(const uint16_t
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;  // 8-element chunk inside the row
   const bool cvalid = c < cpr;
-  const int64_t qrow = (int64_t)cpr * 8;
   for (int rb = blockIdx.y * (4 * U); rb < rows; rb += gridDim.y * (4 * U)) {
     uint4 v[U];
 #pragma unroll
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(256) void quant_rowwise_1x128_kernel(const uint16_t
       for (int m = 1; m < 16; m <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, m, 64));
       if (!(cvalid && r < rows)) continue;
       const BlkScale bs = blk_scale<POW2>(amax);
-      *reinterpret_cast<uint2*>(q + (int64_t)r * qrow + (int64_t)c * 8) = encode8<POW2>(wd, bs);
+      *reinterpret_cast<uint2*>(q + kblk_off(r, (int64_t)c * 8, rows)) = encode8<POW2>(wd, bs);
       if ((c & 15) == 0) s[(int64_t)(c >> 4) * rows + r] = bs.stored;
     }
   }
@@ -173,8 +181,9 @@ __global__ __launch_bounds__(256) void quant_rowwise_1x128_kernel(const uint16_t
 // four waves through LDS.
 // ---------------------------------------------------------------------------
 template <bool POW2>
-__global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t cols,
-                                                            uint8_t* __restrict__ q, float* __restrict__ s) {
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t rows,
+                                                            int64_t cols, uint8_t* __restrict__ q,
+                                                            float* __restrict__ s) {
   __shared__ uint32_t wmax[4];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
@@ -197,7 +206,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __re
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    *reinterpret_cast<uint2*>(q + (r0 + rr + 16 * i) * cols + c0 + ch * 8) = encode8<POW2>(wd, bs);
+    *reinterpret_cast<uint2*>(q + kblk_off(r0 + rr + 16 * i, c0 + ch * 8, rows)) = encode8<POW2>(wd, bs);
   }
   if (t == 0) s[(int64_t)blockIdx.y * (cols / 128) + blockIdx.x] = bs.stored;
 }
@@ -268,8 +277,7 @@ __global__ __launch_bounds__(256) void quant_colwise_1x128_kernel(const uint16_t
   amax = max(max(qmax[0][c], qmax[1][c]), max(qmax[2][c], qmax[3][c]));
   if (c >= ncol) return;
   const BlkScale bs = blk_scale<POW2>(amax);
-  // 64-byte K block (p0 + 32 b) / 64 of column c0 + c
-  uint8_t* qp = q + ((p0 + b * 32) / 64 * cols + c0 + c) * 64 + (b & 1) * 32;
+  uint8_t* qp = q + kblk_off(c0 + c, p0 + b * 32, cols);
   uint32_t o[8];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(const uint16_t* _
     if (row >= nvalid) continue;
     const BlkScale bs = blk_scale<POW2>(amax);
     const int64_t r = row0 + row;
-    *reinterpret_cast<uint2*>(qr + r * cols + c0 + ch * 8) = encode8<POW2>(wd, bs);
+    *reinterpret_cast<uint2*>(qr + kblk_off(r, c0 + ch * 8, rows)) = encode8<POW2>(wd, bs);
     if (ch == 0) sr[c0 / 128 * rows + r] = bs.stored;
   }
   __syncthreads();
@@ -388,7 +396,7 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(const uint16_t* _
       o[2 * d] = e.x;
       o[2 * d + 1] = e.y;
     }
-    uint8_t* qp = qc + ((p0 + b * 32) / 64 * cols + c0 + c) * 64 + (b & 1) * 32;
+    uint8_t* qp = qc + kblk_off(c0 + c, p0 + b * 32, cols);
     reinterpret_cast<uint4*>(qp)[0] = make_uint4(o[0], o[1], o[2], o[3]);
     reinterpret_cast<uint4*>(qp)[1] = make_uint4(o[4], o[5], o[6], o[7]);
     if (b == 0) sc[p0 / 128 * cols + c0 + c] = bs.stored;
@@ -416,9 +424,9 @@ hipError_t launch_quant_rowwise_blk(const uint16_t* x, int64_t rows, int64_t col
   if (blk128x128) {
     const dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
     if (pow2)
-      hipLaunchKernelGGL(quant_128x128_kernel<true>, grid, dim3(256), 0, st, x, ldx, cols, q, s);
+      hipLaunchKernelGGL(quant_128x128_kernel<true>, grid, dim3(256), 0, st, x, ldx, rows, cols, q, s);
     else
-      hipLaunchKernelGGL(quant_128x128_kernel<false>, grid, dim3(256), 0, st, x, ldx, cols, q, s);
+      hipLaunchKernelGGL(quant_128x128_kernel<false>, grid, dim3(256), 0, st, x, ldx, rows, cols, q, s);
     return hipGetLastError();
   }
   constexpr int U = 4;
@@ -446,7 +454,8 @@ hipError_t launch_transpose_128x128(const uint8_t* wq, const float* ws, int32_t 
                                     float* ts, hipStream_t st) {
   const int64_t blocks = (int64_t)G * (N / 128) * (K / 128);
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_128x128_kernel, dim3((unsigned)blocks), dim3(256), 0, st, wq, ws, N, K, tq, ts);
+  hipLaunchKernelGGL(transpose_128x128_kernel, dim3((unsigned)blocks), dim3(256), 0, st, wq, ws, (int64_t)G, N, K, tq,
+                     ts);
   return hipGetLastError();
 }
 

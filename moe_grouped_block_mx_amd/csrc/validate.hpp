@@ -214,6 +214,10 @@ inline Check validate_quantize_dual(const void* x, int64_t rows, int64_t cols, i
 // operand row stride is kept below 2^23 bytes (tile span < 2^31).
 constexpr int64_t kMaxRowStride = (int64_t)1 << 23;
 
+// Blockwise codes sit in 64-byte K blocks of rows*64 bytes, and a GEMM
+// lane's 32-bit DMA offset spans up to two blocks: rows < 2^25.
+constexpr int64_t kMaxKBlockRows = (int64_t)1 << 25;
+
 inline Check validate_gemm_dims(int64_t M, int64_t N, int64_t K, int blk) {
   if (M < 0 || N <= 0 || K <= 0) return fail(MXGG_ERR_SHAPE, "M=%lld N=%lld K=%lld", M, N, K);
   if (N % blk || K % blk) return fail(MXGG_ERR_SHAPE, "N=%lld and K=%lld must be multiples of %lld", N, K, blk);
@@ -237,6 +241,8 @@ inline Check validate_fwd(const void* a_q, const void* a_s, int a_fmt, const voi
   if (!(a4w4 || a8w4 || blk))
     return fail(MXGG_ERR_FORMAT, "format pair (%lld, %lld) is not supported by the forward", a_fmt, w_fmt);
   MXGG_TRY(validate_gemm_dims(M, N, K, blk ? 128 : 32));
+  if (blk && (M >= kMaxKBlockRows || (int64_t)G * N >= kMaxKBlockRows))
+    return fail(MXGG_ERR_SHAPE, "blockwise: M=%lld and G*N=%lld must stay below 2^25", M, (int64_t)G * N);
   MXGG_TRY(check_splits(m, G, M, "A"));
   if (ws_bytes < ws_need) return fail(MXGG_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes,
                                       (long long)ws_need);
@@ -264,6 +270,8 @@ inline Check validate_dgrad(const void* dy_q, const void* dy_s, const void* wc_q
     return fail(MXGG_ERR_FORMAT, "dgrad supports MXGG_MXFP4, MXGG_MXFP8 and MXGG_FP8_1x128 (got %lld)", fmt);
   const bool blk = fmt == MXGG_FP8_1x128;
   MXGG_TRY(validate_gemm_dims(M, N, K, blk ? 128 : 32));
+  if (blk && (M >= kMaxKBlockRows || (int64_t)G * K >= kMaxKBlockRows))
+    return fail(MXGG_ERR_SHAPE, "blockwise: M=%lld and G*K=%lld must stay below 2^25", M, (int64_t)G * K);
   MXGG_TRY(check_splits(m, G, M, "dY"));
   if (!blk && (int64_t)G * N / 2 >= kMaxRowStride)
     return fail(MXGG_ERR_SHAPE, "G*N=%lld too large (G*N/2 < 2^23)", (int64_t)G * N);

@@ -87,5 +87,7 @@ def test_quantizer_outputs():
         mxg.quantize_dual(x, SPLITS, "mxfp4", q_col=z((K, MPAD), u8))
     with pytest.raises(ValueError, match="q"):
         mxg.quantize_colwise_segpad(x, SPLITS, "mxfp4", q=z((MPAD // 2, K), u8))
-    with pytest.raises(ValueError, match="wt_s"):
-        mxg.transpose_128x128(z((G * 128, 256), u8), z((G, 2), f32), G, 128, 256, wt_s=z((G, 2), f32))
+    with pytest.raises(ValueError, match="wt_s"):   # blockwise codes in 64-byte K blocks: [K/64, G*N, 64]
+        mxg.transpose_128x128(z((256 // 64, G * 128, 64), u8), z((G, 2), f32), G, 128, 256, wt_s=z((G, 2), f32))
+    with pytest.raises(ValueError, match="w_q"):    # rows of codes are refused
+        mxg.transpose_128x128(z((G * 128, 256), u8), z((G, 2), f32), G, 128, 256)

@@ -19,7 +19,7 @@ from oracle import grouped as og
 from oracle import mx as omx
 from synth import bf16_normal, f32_normal, splits_for
 
-from .gpu_util import assert_gemm_close, dev_bf16, dev_f32, have_gpu, host, host_bf16_f64
+from .gpu_util import assert_gemm_close, dev_bf16, dev_f32, have_gpu, host, host_bf16_f64, kblocked_rows
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
 
@@ -109,13 +109,14 @@ def test_transpose_128x128_bit_exact(G, N, K):
     wq, ws = mxg.quantize_rowwise(dev_bf16(w), "fp8_128x128")
     tq, ts = mxg.transpose_128x128(wq, ws, G, N, K)
     torch.cuda.synchronize()
-    q, s = host(wq).reshape(G, N, K), host(ws).reshape(G, N // 128, K // 128)
-    assert np.array_equal(host(tq), q.transpose(0, 2, 1).reshape(G * K, N))
+    # codes in 64-byte K blocks on both sides: compared as rows
+    q, s = kblocked_rows(wq).reshape(G, N, K), host(ws).reshape(G, N // 128, K // 128)
+    assert np.array_equal(kblocked_rows(tq), q.transpose(0, 2, 1).reshape(G * K, N))
     assert np.array_equal(host(ts), s.transpose(0, 2, 1).reshape(G * K // 128, N // 128))
     # and the transposed blocks are the oracle's 128x128 quantization of W^T
     wt = np.ascontiguousarray(w.reshape(G, N, K).transpose(0, 2, 1).reshape(G * K, N))
     rq, rs = ob.quantize_128x128(wt)
-    assert np.array_equal(host(tq), rq.astype(np.uint8))
+    assert np.array_equal(kblocked_rows(tq), rq.astype(np.uint8))
     assert np.array_equal(host(ts), rs.astype(np.float32))
 
 
@@ -146,7 +147,7 @@ def test_dgrad_blockwise(case, fmt):
     torch.cuda.synchronize()
     rd, rds = ob.quantize_1x128(dy, pow2=p2)
     rw, rws = ob.quantize_128x128(w, pow2=p2)
-    assert np.array_equal(host(dq), rd.astype(np.uint8)) and np.array_equal(host(ds).T, rds.astype(np.float32))
+    assert np.array_equal(kblocked_rows(dq), rd.astype(np.uint8)) and np.array_equal(host(ds).T, rds.astype(np.float32))
     W = ob.dequantize_128x128(rw, rws).reshape(G, N, K)
     # dx = dY_g . W_g: the forward's contraction with W_g^T as the weight
     ref = og.grouped_fwd(ob.dequantize_1x128(rd, rds), np.ascontiguousarray(W.transpose(0, 2, 1)), splits)
@@ -281,12 +282,12 @@ def test_blockwise_full_size_dgrad_sampled(p2):
         kcols = kb * 128 + np.sort(rng.choice(128, size=16, replace=False))
         rt = torch.as_tensor(rows, device="cuda")
         rd, rds = ob.quantize_1x128(_bits(dy[rt]))
-        assert np.array_equal(host(dq[rt]), rd.astype(np.uint8))
+        assert np.array_equal(kblocked_rows(dq[:, rt]), rd.astype(np.uint8))
         # the library's transposed codes and scales of the sampled columns,
         # dequantized by the oracle's rule: W^T[k, n] = code * scale[k/128, n/128]
-        ct = host(tq[g * K + torch.as_tensor(kcols, device="cuda")])
+        ct = kblocked_rows(tq[:, g * K + torch.as_tensor(kcols, device="cuda")])
         st = host(ts[g * K // 128 + kb])
-        assert np.array_equal(ct, host(wq[g * N:(g + 1) * N][:, torch.as_tensor(kcols, device="cuda")]).T)
+        assert np.array_equal(ct, kblocked_rows(wq[:, g * N:(g + 1) * N])[:, kcols].T)
         assert np.array_equal(st, host(ws[g * N // 128:(g + 1) * N // 128, kb]))
         Wt = ob.dequantize_1x128(ct, np.broadcast_to(st, (len(kcols), N // 128)))
         ref = ob.dequantize_1x128(rd, rds) @ Wt.T

@@ -50,7 +50,7 @@ def test_quantize_1x128_rowwise(pow2, shape):
     torch.cuda.synchronize()
     rq, rs = ob.quantize_1x128(x, pow2=pow2)
     assert s.shape == (shape[1] // 128, shape[0])  # block-major
-    assert np.array_equal(host(q), rq.astype(np.uint8))
+    assert np.array_equal(kblocked_rows(q), rq.astype(np.uint8))
     assert np.array_equal(host(s).T.copy().view(np.uint32), rs.astype(np.float32).view(np.uint32))
 
 
@@ -60,7 +60,7 @@ def test_quantize_1x128_strided_input():
     q, s = mxg.quantize_rowwise(xt, "fp8_1x128")
     torch.cuda.synchronize()
     rq, rs = ob.quantize_1x128(np.ascontiguousarray(full[:, 128:384]))
-    assert np.array_equal(host(q), rq.astype(np.uint8))
+    assert np.array_equal(kblocked_rows(q), rq.astype(np.uint8))
     assert np.array_equal(host(s).T, rs.astype(np.float32))
 
 
@@ -72,7 +72,7 @@ def test_quantize_128x128(pow2, shape):
     q, s = mxg.quantize_rowwise(dev_bf16(w), "fp8_128x128", flags=POW2 if pow2 else 0)
     torch.cuda.synchronize()
     rq, rs = ob.quantize_128x128(w, pow2=pow2)
-    assert np.array_equal(host(q), rq.astype(np.uint8))
+    assert np.array_equal(kblocked_rows(q), rq.astype(np.uint8))
     assert np.array_equal(host(s).view(np.uint32), rs.astype(np.float32).view(np.uint32))
 
 
@@ -82,7 +82,7 @@ def test_quantize_128x128_all_zero_block():
     q, s = mxg.quantize_rowwise(dev_bf16(w), "fp8_128x128")
     torch.cuda.synchronize()
     rq, rs = ob.quantize_128x128(w)
-    assert np.array_equal(host(q), rq.astype(np.uint8))
+    assert np.array_equal(kblocked_rows(q), rq.astype(np.uint8))
     assert np.array_equal(host(s), rs.astype(np.float32))
 
 
@@ -274,11 +274,11 @@ def test_c5_full_size_fwd_sampled(c5, p2):
         # the sampled activation rows and the sampled weight 128-row block,
         # quantized by the oracle, must equal the library's bytes
         ra, ras = ob.quantize_1x128(_bits(a[torch.as_tensor(rows, device="cuda")]))
-        assert np.array_equal(host(aq[torch.as_tensor(rows, device="cuda")]), ra.astype(np.uint8))
+        assert np.array_equal(kblocked_rows(aq[:, torch.as_tensor(rows, device="cuda")]), ra.astype(np.uint8))
         assert np.array_equal(host(as_[:, torch.as_tensor(rows, device="cuda")]).T, ras.astype(np.float32))
         r0 = g * N + blk * 128
         rw, rws = ob.quantize_128x128(_bits(w[r0:r0 + 128]))
-        assert np.array_equal(host(wq[r0:r0 + 128]), rw.astype(np.uint8))
+        assert np.array_equal(kblocked_rows(wq[:, r0:r0 + 128]), rw.astype(np.uint8))
         assert np.array_equal(host(ws[r0 // 128:r0 // 128 + 1]), rws.astype(np.float32))
         wdeq = ob.dequantize_128x128(rw, rws)[cols - blk * 128]
         ref = ob.dequantize_1x128(ra, ras) @ wdeq.T

@@ -36,11 +36,12 @@ EXPECTED = {
     "grouped_dgrad_kernelINS_5MfmaBINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEELb0E": [5],
     # a4w4 weight gradient: 4 waves, same ring, DPS 10 (every output mode)
     "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi2ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [10],
-    # power-of-two blockwise forward / input gradient: 64-deep stages, 3-stage ring, DPS 6
-    "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEELb1E": [6],
-    "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEELb1E": [6],
-    "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEELb0E": [6],
-    "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEELb0E": [6],
+    # power-of-two blockwise forward / input gradient (operands in 64-byte K
+    # blocks): 64-deep stages, 3-stage ring, DPS 6
+    "grouped_fwd_kernelINS_8KBlockedINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEEEELb1E": [6],
+    "grouped_dgrad_kernelINS_8KBlockedINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEEEELb1E": [6],
+    "grouped_fwd_kernelINS_8KBlockedINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEEEELb0E": [6],
+    "grouped_dgrad_kernelINS_8KBlockedINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi3ELi1ELi5ELi128EEEEELb0E": [6],
     # MXFP8 weight gradient (DPS 5, general issue) and power-of-two blockwise
     # weight gradient (DPS 6, scalar-base issue), every output mode
     "grouped_wgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi64ELi3ELi4ELi1ELi5ELi1EEELb0E": [5],
