@@ -97,11 +97,9 @@ __device__ __forceinline__ uint32_t amax8(const uint32_t (&wd)[4]) {
 // over the weights' rows): the blocks are square, so W^T's 128x128
 // quantization is W's, transposed: the same codes and the same scale per
 // block. One workgroup per block: the 128 rows x 128 bytes are read with
-// 16-byte loads into LDS (dword pitch 33), then each thread transposes 4x4
-// byte squares in registers and writes output rows with 4-byte stores, 32
-// threads per 128-byte output row (both sides in 64-byte K blocks: W
-// [K/64, G*N, 64], W^T [N/64, G*K, 64]). HBM-bound: 1 B read and 1 B written
-// per element.
+// 16-byte loads into LDS (dword pitch 33), then written back transposed with
+// 16-byte stores (both sides in 64-byte K blocks: W [K/64, G*N, 64], W^T
+// [N/64, G*K, 64]). HBM-bound: 1 B read and 1 B written per element.
 __global__ __launch_bounds__(256) void transpose_128x128_kernel(const uint8_t* __restrict__ wq,
                                                                 const float* __restrict__ ws, int64_t G, int64_t N,
                                                                 int64_t K, uint8_t* __restrict__ tq,
@@ -122,17 +120,23 @@ __global__ __launch_bounds__(256) void transpose_128x128_kernel(const uint8_t* _
     tile[r][4 * q + 3] = v.w;
   }
   __syncthreads();
+  // The 128 output rows (k) by 128 bytes (n) are two 64-byte K blocks of
+  // W^T, each one 8 KiB run. Chunk c: block half h = c/512, row k =
+  // (c/4)%128, 16-byte piece qd = c%4, so the 64 chunks of a wave's store are
+  // one contiguous 1 KiB (16 rows); a chunk gathers its 16 bytes from 16 LDS
+  // rows.
   for (int c = threadIdx.x; c < 1024; c += 256) {
-    const int kq = c >> 5, nq = c & 31;  // output rows 4kq..4kq+3, bytes 4nq..4nq+3
-    uint32_t d[4];
+    const int h = c >> 9, k = (c >> 2) & 127, qd = c & 3;
+    const int n0 = h * 64 + qd * 16, sh = 8 * (k & 3);
+    uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = tile[4 * nq + i][kq];  // input row 4nq+i, bytes 4kq..4kq+3
+    for (int m = 0; m < 4; ++m) {
+      o[m] = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t o = ((d[0] >> (8 * j)) & 0xffu) | (((d[1] >> (8 * j)) & 0xffu) << 8) |
-                         (((d[2] >> (8 * j)) & 0xffu) << 16) | (((d[3] >> (8 * j)) & 0xffu) << 24);
-      *reinterpret_cast<uint32_t*>(tq + kblk_off(g * K + kb * 128 + 4 * kq + j, nb * 128 + 4 * nq, trows)) = o;
+      for (int t = 0; t < 4; ++t) o[m] |= ((tile[n0 + 4 * m + t][k >> 2] >> sh) & 0xffu) << (8 * t);
     }
+    *reinterpret_cast<uint4*>(tq + kblk_off(g * K + kb * 128 + k, nb * 128 + n0, trows)) =
+        make_uint4(o[0], o[1], o[2], o[3]);
   }
   if (threadIdx.x == 0) ts[(g * kbs + kb) * nbs + nb] = ws[(g * nbs + nb) * kbs + kb];
 }
