@@ -111,8 +111,10 @@ __global__ __launch_bounds__(256) void transpose_128x128_kernel(const uint8_t* _
   const int64_t rem = b - g * nbs * kbs;
   const int64_t nb = rem / kbs, kb = rem - nb * kbs;
   const int64_t wrows = G * N, trows = G * K;
+  // load chunk c: block half c/512, row (c/4)%128, 16-byte piece c%4 (a
+  // wave's load is 16 consecutive rows of one block: one 1 KiB run)
   for (int c = threadIdx.x; c < 1024; c += 256) {
-    const int r = c >> 3, q = c & 7;
+    const int r = (c >> 2) & 127, q = ((c >> 9) << 2) | (c & 3);
     const uint4 v = *reinterpret_cast<const uint4*>(wq + kblk_off(g * N + nb * 128 + r, kb * 128 + q * 16, wrows));
     tile[r][4 * q] = v.x;
     tile[r][4 * q + 1] = v.y;
