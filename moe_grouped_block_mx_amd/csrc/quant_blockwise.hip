@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) void quant_colwise_1x128_kernel(const uint16_t
 // Identical output to the two single-output kernels (same scale rule and
 // encoder on the same values).
 // ---------------------------------------------------------------------------
-template <bool POW2>
+template <bool POW2, bool ROWS = true>
 __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                int64_t rows, int64_t cols, const SplitArgs sp,
                                                                int64_t mpad,
@@ -362,10 +362,11 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(const uint16_t* _
   for (int i = 0; i < 8; ++i) {
     const int row = rg + 16 * i;
     const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    *reinterpret_cast<uint4*>(tile + row * PITCH + ch * 8) = v[i];
+    if constexpr (!ROWS) continue;
     uint32_t amax = amax8(wd);
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, m, 64));
-    *reinterpret_cast<uint4*>(tile + row * PITCH + ch * 8) = v[i];
     if (row >= nvalid) continue;
     const BlkScale bs = blk_scale<POW2>(amax);
     const int64_t r = row0 + row;
@@ -448,6 +449,16 @@ hipError_t launch_quant_rowwise_blk(const uint16_t* x, int64_t rows, int64_t col
 
 hipError_t launch_quant_colwise_blk(const uint16_t* x, int64_t cols, int64_t ldx, const SplitArgs& sp, bool pow2,
                                     uint8_t* q, float* s, int64_t mpad, hipStream_t st) {
+  if (cols % 128 == 0) {  // the dual kernel without its row-wise output: 128 columns per workgroup
+    const dim3 grid((unsigned)(mpad / 128), (unsigned)(cols / 128));
+    if (pow2)
+      hipLaunchKernelGGL((quant_dual_1x128_kernel<true, false>), grid, dim3(256), 0, st, x, ldx, (int64_t)0, cols,
+                         sp, mpad, nullptr, nullptr, q, s);
+    else
+      hipLaunchKernelGGL((quant_dual_1x128_kernel<false, false>), grid, dim3(256), 0, st, x, ldx, (int64_t)0, cols,
+                         sp, mpad, nullptr, nullptr, q, s);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(mpad / 128), (unsigned)((cols + 63) / 64));
   if (pow2)
     hipLaunchKernelGGL(quant_colwise_1x128_kernel<true>, grid, dim3(256), 0, st, x, ldx, cols, sp, mpad, q, s);

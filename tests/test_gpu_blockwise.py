@@ -91,6 +91,7 @@ COL_CASES = [
     ([128], 96),
     ([0, 0, 7], 160),
     ([129, 1, 255, 0, 40], 32),
+    ([129, 1, 255, 0, 40], 256),         # cols % 128 == 0: 128 columns per workgroup
 ]
 
 
