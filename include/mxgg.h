@@ -158,8 +158,8 @@ typedef enum mxgg_format {
  *     wcol_s (N % 128 == 0). Activation and gradient scales stay block-major
  *     (a_s, dy_s and both weight-gradient operands refuse it with
  *     MXGG_ERR_FORMAT).
- * Blockwise formats take no layout bits (their fp32 scales are row-major by
- * definition); any layout bits on them are MXGG_ERR_FORMAT.
+ * Blockwise formats take no layout bits (their fp32 scales have one layout,
+ * block-major for 1x128); any layout bits on them are MXGG_ERR_FORMAT.
  */
 typedef enum mxgg_scale_layout {
   MXGG_LAYOUT_BLOCK_MAJOR = 0x000,
@@ -167,6 +167,32 @@ typedef enum mxgg_scale_layout {
   MXGG_LAYOUT_MFMA = 0x200
 } mxgg_scale_layout;
 #define MXGG_LAYOUT_MASK 0xF00
+
+/*
+ * MX code layouts, further bits of an MX format argument (beside the scale
+ * layout): fmt = MXGG_MXFP4 | MXGG_KBLOCK_ROWS | MXGG_KBLOCK_COLS. Without
+ * them the codes are plain rows. With them an operand with L code bytes per
+ * row is stored in 64-byte blocks along the row, u8 [L/64, rows, 64]: byte j
+ * of row r at ((j/64)*rows + r)*64 + j%64 (how every blockwise code tensor is
+ * stored). A GEMM stage needs 64 bytes of each of a 256-row tile's rows per
+ * operand (128 E2M1 or 64 E4M3 elements), which are then one contiguous run.
+ *   MXGG_KBLOCK_ROWS  row-wise codes: mxgg_quantize_rowwise's q and the dual
+ *                     quantizer's q_row (cols % 128 == 0); the forward's a_q
+ *                     and w_q, the input gradient's dy_q.
+ *   MXGG_KBLOCK_COLS  column-wise codes along the padded length, u8
+ *                     [mpad_bytes/64, cols, 64]: mxgg_quantize_colwise_segpad's
+ *                     q and the dual quantizer's q_col (every split a multiple
+ *                     of 128, so each expert's segment starts a block); the
+ *                     input gradient's wcol_q.
+ * The forward takes MXGG_KBLOCK_ROWS on a_fmt and w_fmt together or on
+ * neither; the input gradient both bits on fmt or neither; the weight gradient
+ * neither (its MX segments are padded to 32, so a 64-byte stage row would
+ * straddle blocks). A GEMM with K-blocked operands needs rows < 2^25 per
+ * operand. Any other use of the bits is MXGG_ERR_FORMAT.
+ */
+#define MXGG_KBLOCK_ROWS 0x1000
+#define MXGG_KBLOCK_COLS 0x2000
+#define MXGG_KBLOCK_MASK 0x3000
 
 /* flags for the quantizers (blockwise formats only) */
 #define MXGG_POW2_SCALES 1u

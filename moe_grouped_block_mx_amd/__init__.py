@@ -5,7 +5,7 @@ include/mxgg.h); this package is its thin ctypes binding.
 """
 from ._lib import (  # noqa: F401
     FORMATS, FP8_1x128, FP8_128x128, FP8_1x128_P2, FP8_128x128_P2, LAYOUT_BLOCK_MAJOR, LAYOUT_MASK, LAYOUT_MFMA,
-    LAYOUT_ROW_MAJOR,
+    LAYOUT_ROW_MAJOR, KBLOCK_COLS, KBLOCK_MASK, KBLOCK_ROWS,
     LIB_PATH, MAX_EXPERTS, MXFP4, MXFP8, POW2_SCALES,
     MxggError, header_functions, lib,
     mxgg_grouped_dgrad, mxgg_grouped_fwd, mxgg_grouped_wgrad, mxgg_quantize_colwise_segpad, mxgg_quantize_dual,

@@ -24,6 +24,8 @@ POW2_SCALES = 1
 MAX_EXPERTS = 512
 # mxgg_scale_layout: OR-ed into an MX format to state the layout of its scales
 LAYOUT_BLOCK_MAJOR, LAYOUT_ROW_MAJOR, LAYOUT_MFMA, LAYOUT_MASK = 0x000, 0x100, 0x200, 0xF00
+# MX code layouts: row-wise / column-wise codes in 64-byte K blocks
+KBLOCK_ROWS, KBLOCK_COLS, KBLOCK_MASK = 0x1000, 0x2000, 0x3000
 
 STATUS = {
     0: "MXGG_OK", 1: "MXGG_ERR_NULL", 2: "MXGG_ERR_SHAPE", 3: "MXGG_ERR_SPLITS",
@@ -172,26 +174,34 @@ def _layout_shape(layout, rows, blocks):
     return (blocks, mxgg_mx_scale_stride(rows))                   # block-major
 
 
+def _code_bytes(f, n):
+    """Code bytes of n elements (E2M1 packs two per byte)."""
+    return n // 2 if (f & 0xFF) == MXFP4 else n
+
+
 def _q_shape(f, rows, cols):
-    """Codes of a [rows, cols] operand quantized along cols: MX, rows of
-    codes (E2M1 packed two per byte); blockwise E4M3, 64-byte blocks along
-    cols, u8 [cols/64, rows, 64]."""
-    if not _is_mx(f):
-        return (cols // 64, rows, 64)
-    return (rows, cols // 2 if (f & 0xFF) == MXFP4 else cols)
+    """Codes of a [rows, cols] operand quantized along cols: rows of codes,
+    or 64-byte blocks along cols, u8 [bytes per row / 64, rows, 64]
+    (blockwise formats always, MX with KBLOCK_ROWS)."""
+    if not _is_mx(f) or (f & KBLOCK_ROWS):
+        return (_code_bytes(f, cols) // 64, rows, 64)
+    return (rows, _code_bytes(f, cols))
 
 
 def _q_rows(q, f):
     """Row count of a code tensor laid out as _q_shape gives it (a tensor of
     another rank then fails the shape check that follows)."""
-    if _is_mx(f):
+    if _is_mx(f) and not (f & KBLOCK_ROWS):
         return q.shape[0] if q.dim() >= 1 else 0
     return q.shape[1] if q.dim() >= 2 else 0
 
 
 def _col_q_shape(f, cols, mpad):
-    """Codes of the column-wise segment-padded [cols, mpad] operand."""
-    return _q_shape(f, cols, mpad)
+    """Codes of the column-wise segment-padded [cols, mpad] operand: rows, or
+    64-byte blocks along the padded length (blockwise, MX with KBLOCK_COLS)."""
+    if not _is_mx(f) or (f & KBLOCK_COLS):
+        return (_code_bytes(f, mpad) // 64, cols, 64)
+    return (cols, _code_bytes(f, mpad))
 
 
 def _row_scale_shape(f, rows, cols):
@@ -380,7 +390,7 @@ def mxgg_grouped_dgrad(dy_q, dy_s, wcol_q, wcol_s, m_splits, N, K, fmt="mxfp4", 
     _expect(dy_q, "dy_q", _q_shape(f, M, N), torch.uint8)
     _expect(dy_s, "dy_s", _row_scale_shape(f & 0xFF, M, N), _sdtype(f))
     if _is_mx(f):                       # W along N, MXFP4: [K, G*N/2] + [G*N/32, K]
-        _expect(wcol_q, "wcol_q", _q_shape(MXFP4, K, G * N), torch.uint8)
+        _expect(wcol_q, "wcol_q", _col_q_shape(MXFP4 | (f & KBLOCK_COLS), K, G * N), torch.uint8)
         _expect(wcol_s, "wcol_s", _col_scale_shape(MXFP4 | (f & LAYOUT_MASK), K, G * N), torch.uint8)
     else:                               # transposed 128x128 blocks
         _expect(wcol_q, "wcol_q", _q_shape(FP8_128x128, G * K, N), torch.uint8)

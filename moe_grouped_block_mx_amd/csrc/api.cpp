@@ -175,14 +175,14 @@ mxgg_status mxgg_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int
   Check c = validate_quantize_rowwise(x, rows, cols, ldx, (int)fmt, q, scales);
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
-  const bool mfma = is_mfma_layout(fmt);
+  const bool mfma = is_mfma_layout(fmt), kb = kblock_bits(fmt) != 0;
   fmt = (mxgg_format)format_bits(fmt);
   int cus = 0;
   c = device_checks(stream, {{x, "x"}, {q, "q"}, {scales, "scales"}}, &cus);
   if (!c.ok()) return finish(c);
   if (is_mx(fmt))
     c = hip_status(launch_quant_rowwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, fmt == MXGG_MXFP8, mfma,
-                                           static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), cus, stream),
+                                           kb, static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), cus, stream),
                    "row-wise quantizer launch");
   else
     c = hip_status(launch_quant_rowwise_blk(static_cast<const uint16_t*>(x), rows, cols, ldx,
@@ -200,7 +200,7 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
   Check c = validate_quantize_colwise(x, rows, cols, ldx, m_splits, G, (int)fmt, q, scales, mpad);
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
-  const bool mfma = is_mfma_layout(fmt);
+  const bool mfma = is_mfma_layout(fmt), kb = kblock_bits(fmt) != 0;
   fmt = (mxgg_format)format_bits(fmt);
   int cus = 0;
   c = device_checks(stream, {{x, "x"}, {q, "q"}, {scales, "scales"}}, &cus);
@@ -208,8 +208,8 @@ mxgg_status mxgg_quantize_colwise_segpad(const void* x, int64_t rows, int64_t co
   const SplitArgs sp = make_splits(m_splits, G);
   if (is_mx(fmt))
     c = hip_status(launch_quant_colwise_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8,
-                                           mfma, static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), mpad, cus,
-                                           stream),
+                                           mfma, kb, static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales), mpad,
+                                           cus, stream),
                    "column-wise quantizer launch");
   else
     c = hip_status(launch_quant_colwise_blk(static_cast<const uint16_t*>(x), cols, ldx, sp,
@@ -228,6 +228,7 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
   if (!c.ok()) return finish(c);
   if (rows == 0) return ok();
   const bool mfma = is_mfma_layout(fmt);
+  const bool kbr = (fmt & MXGG_KBLOCK_ROWS) != 0, kbc = (fmt & MXGG_KBLOCK_COLS) != 0;
   fmt = (mxgg_format)format_bits(fmt);
   int cus = 0;
   c = device_checks(stream, {{x, "x"}, {q_row, "q_row"}, {s_row, "s_row"}, {q_col, "q_col"}, {s_col, "s_col"}}, &cus);
@@ -235,7 +236,7 @@ mxgg_status mxgg_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_
   const SplitArgs sp = make_splits(m_splits, G);
   if (is_mx(fmt))
     c = hip_status(launch_quant_dual_mx(static_cast<const uint16_t*>(x), rows, cols, ldx, sp, fmt == MXGG_MXFP8, mfma,
-                                        static_cast<uint8_t*>(q_row), static_cast<uint8_t*>(s_row),
+                                        kbr, kbc, static_cast<uint8_t*>(q_row), static_cast<uint8_t*>(s_row),
                                         static_cast<uint8_t*>(q_col), static_cast<uint8_t*>(s_col), mpad, cus,
                                         stream),
                    "dual quantizer launch");
@@ -272,7 +273,8 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
                          mxgg_workspace_size(G));
   if (!c.ok()) return finish(c);
   if (M == 0) return ok();
-  const bool w_mfma = is_mfma_layout(w_fmt);
+  const bool w_mfma = is_mfma_layout(w_fmt), kb = kblock_bits(a_fmt) != 0;
+  a_fmt = (mxgg_format)format_bits(a_fmt);
   w_fmt = (mxgg_format)format_bits(w_fmt);
   int cus = 0;
   c = device_checks(stream, {{a_q, "a_q"}, {a_s, "a_s"}, {w_q, "w_q"}, {w_s, "w_s"}, {out, "out"}}, &cus);
@@ -306,18 +308,19 @@ mxgg_status mxgg_grouped_fwd(const void* a_q, const void* a_s, mxgg_format a_fmt
   p.b = static_cast<const uint8_t*>(w_q);
   p.bs = static_cast<const uint8_t*>(w_s);
   p.c = static_cast<uint16_t*>(out);
-  p.lda = a8 ? K : K / 2;
+  // codes in rows, or in 64-byte K blocks (ld = bytes per block: rows * 64)
+  p.lda = kb ? M * 64 : a8 ? K : K / 2;
   p.ldas = mx_scale_stride(M);    // A scales [K/32, R4(M)]
-  p.ldb = K / 2;
+  p.ldb = kb ? (int64_t)G * N * 64 : K / 2;
   p.ldbs = (int64_t)G * N;        // W scales [K/32, G*N] (MFMA layout: a 128-element
                                   // group is 4 blocks of G*N bytes, N % 32 == 0)
-  p.b_gstride = N * (K / 2);
+  p.b_gstride = kb ? N * 64 : N * (K / 2);
   p.bs_gstride = w_mfma ? N * 4 : N;  // expert g's rows start at g*N (its units at byte g*N*4)
   p.ldc = N;
   p.n_out = (int32_t)N;
   p.kc = (int32_t)K;
   p.sp = make_splits(m_splits, G);
-  c = hip_status(launch_grouped_rows_mx(p, a8, false, w_mfma, cus, stream), "forward launch");
+  c = hip_status(launch_grouped_rows_mx(p, a8, false, w_mfma, kb, cus, stream), "forward launch");
   return c.ok() ? ok() : finish(c);
 }
 
@@ -330,7 +333,7 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
                            mxgg_workspace_size(G));
   if (!c.ok()) return finish(c);
   if (M == 0) return ok();
-  const bool w_mfma = is_mfma_layout(fmt);
+  const bool w_mfma = is_mfma_layout(fmt), kb = kblock_bits(fmt) != 0;
   fmt = (mxgg_format)format_bits(fmt);
   int cus = 0;
   c = device_checks(stream, {{dy_q, "dy_q"}, {dy_s, "dy_s"}, {wcol_q, "wcol_q"}, {wcol_s, "wcol_s"}, {dx, "dx"}},
@@ -361,15 +364,16 @@ mxgg_status mxgg_grouped_dgrad(const void* dy_q, const void* dy_s, const void* w
     return c.ok() ? ok() : finish(c);
   }
   const bool a8 = fmt == MXGG_MXFP8;  // a8w4: dY E4M3, W E2M1
-  p.lda = a8 ? N : N / 2;
+  // codes in rows, or in 64-byte K blocks (ld = bytes per block: rows * 64)
+  p.lda = kb ? M * 64 : a8 ? N : N / 2;
   p.ldas = mx_scale_stride(M);    // dY scales [N/32, R4(M)]
-  p.ldb = (int64_t)G * N / 2;     // W column-wise: [K, G*N/2]
+  p.ldb = kb ? K * 64 : (int64_t)G * N / 2;  // W column-wise: [K, G*N/2] (blocked: [G*N/128, K, 64])
   p.ldbs = K;                     // its scales [G*N/32, K] (MFMA layout: 4 blocks of K
                                   // bytes per 128-element group)
-  p.b_gstride = N / 2;            // expert g owns columns [g*N, (g+1)*N)
+  p.b_gstride = kb ? N / 128 * K * 64 : N / 2;  // expert g owns columns [g*N, (g+1)*N)
   p.bs_gstride = N / 32 * K;      // ... and scale blocks [g*N/32, (g+1)*N/32) (MFMA: the
                                   // same byte offset, groups [g*N/128, (g+1)*N/128))
-  c = hip_status(launch_grouped_rows_mx(p, a8, true, w_mfma, cus, stream), "dgrad launch");
+  c = hip_status(launch_grouped_rows_mx(p, a8, true, w_mfma, kb, cus, stream), "dgrad launch");
   return c.ok() ? ok() : finish(c);
 }
 

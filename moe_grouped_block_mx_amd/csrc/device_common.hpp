@@ -105,4 +105,10 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   }
 }
 
+// Byte c (along the row) of row r of a code tensor with `rows` rows stored in
+// 64-byte K blocks, u8 [bytes per row / 64, rows, 64].
+__device__ __forceinline__ int64_t kblk_off(int64_t r, int64_t c, int64_t rows) {
+  return (c >> 6) * rows * 64 + r * 64 + (c & 63);
+}
+
 }  // namespace mxgg

@@ -107,7 +107,7 @@ struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
   static constexpr int SCHED = SCHED_, BDIV = BDIV_;
   static constexpr bool MFB = false;  // B's MX scales in the MFMA layout (MfmaB)
-  static constexpr bool KBLK = false;  // operand data in 64-byte K blocks (KBlocked)
+  static constexpr bool KBLK_A = false, KBLK_B = false;  // A / B data in 64-byte K blocks (KBlocked)
   static constexpr bool AFP8 = KIND_ != kA4W4, BFP8 = KIND_ == kBlkFp8 || KIND_ == kBlkP2 || KIND_ == kA8A8;
   static constexpr bool BLK = KIND_ == kBlkFp8;                     // per-128 partial promotion
   // fp32 scales, one per 128 elements: A's (1x128) block-major [blocks][rows];
@@ -182,21 +182,24 @@ struct MfmaB : C {
 
 // A configuration whose A and B data are stored in 64-byte blocks along the
 // contraction, u8 [L/64, rows, 64] for rows of L bytes (the blockwise E4M3
-// operands: contractions and column-wise segments multiples of 128): byte
+// operands, and MX operands with the K-block code layout; contractions and
+// segments are then multiples of 128 elements): byte
 // j of row r sits at (j/64)*ld + r*64 + j%64 with ld = rows*64, so the 64
 // bytes a stage needs from each of a tile's rows form one contiguous run per
 // 64-byte block (one 1 KiB run per DMA instruction instead of 16 row pieces).
 template <class C>
 struct KBlocked : C {
-  static constexpr bool KBLK = true;
-  static_assert(C::AFP8 && C::BFP8 && C::RBA % 64 == 0 && C::RBB % 64 == 0, "64-byte K blocks of E4M3 stages");
+  static constexpr bool KBLK_A = true, KBLK_B = true;
+  static_assert(C::RBA % 64 == 0 && C::RBB % 64 == 0, "stages of whole 64-byte K blocks");
 };
 
 // Byte offset of data byte j (along the contraction) of row r: row-major
-// rows of ld bytes, or 64-byte K blocks of ld bytes each (KBLK).
-template <class C>
+// rows of ld bytes, or 64-byte K blocks of ld bytes each (KBLK_A / KBLK_B
+// for operand A / B).
+template <class C, bool ON_B>
 __host__ __device__ constexpr int64_t data_off(int64_t r, int64_t j, int64_t ld) {
-  return C::KBLK ? (j / 64) * ld + r * 64 + j % 64 : r * ld + j;
+  constexpr bool kb = ON_B ? C::KBLK_B : C::KBLK_A;
+  return kb ? (j / 64) * ld + r * 64 + j % 64 : r * ld + j;
 }
 
 // The segment owning item t of a non-decreasing prefix offs[0..n] (offs[0] =
@@ -244,7 +247,7 @@ struct DmaPlan {
   // wave-uniform (A's and B's regions are whole instructions)
   uint32_t sOff[C::F32S ? 1 : C::DSA];
   int sBlk[C::F32S ? 1 : C::DSA];
-  int64_t astep, bstep;  // data bytes from one stage to the next (KBLK: whole blocks)
+  int64_t astep, bstep;  // data bytes from one stage to the next (K blocks: whole blocks)
 };
 constexpr int kNoBlock = 1 << 24;
 
@@ -266,7 +269,7 @@ __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64
     const int r = o / C::RBA;
     const int c = swz<C::CPA>(r, (o % C::RBA) / 16);
     const int rr = r < t.mrows ? r : t.mrows - 1;
-    pl.offA[i] = (uint32_t)data_off<C>(rr, c * 16, lda);
+    pl.offA[i] = (uint32_t)data_off<C, false>(rr, c * 16, lda);
     pl.kA[i] = c * 16;
   });
   unroll<C::DB>([&](auto ic) {
@@ -275,11 +278,11 @@ __device__ __forceinline__ void plan_dma(DmaPlan<C>& pl, const TileOps& t, int64
     const int r = o / C::RBB;
     const int c = swz<C::CPB>(r, (o % C::RBB) / 16);
     const int rr = r < t.nrows ? r : t.nrows - 1;
-    pl.offB[i] = (uint32_t)data_off<C>(rr, c * 16, ldb);
+    pl.offB[i] = (uint32_t)data_off<C, true>(rr, c * 16, ldb);
     pl.kB[i] = c * 16;
   });
-  pl.astep = data_off<C>(0, C::RBA, lda);
-  pl.bstep = data_off<C>(0, C::RBB, ldb);
+  pl.astep = data_off<C, false>(0, C::RBA, lda);
+  pl.bstep = data_off<C, true>(0, C::RBB, ldb);
   // Scales. MX: lane word d of the stage's scale region holds four rows of
   // one block: A's [SB][BM] bytes, then B's [SB][BN], then padding. Rows past
   // the readable scale rows (which only invalid tile rows reach) read the last
@@ -517,7 +520,7 @@ __device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, u
   uint32_t ln = (uint32_t)lane;
   asm volatile("" : "+v"(ln));  // recomputed here, not hoisted out of the loop
   const uint32_t wu = (uint32_t)w;
-  const uint8_t* abase = lp.a + s * data_off<C>(0, C::RBA, lda);
+  const uint8_t* abase = lp.a + s * data_off<C, false>(0, C::RBA, lda);
   unroll<C::DA>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     if constexpr (i >= Q0 && i < Q1) {
@@ -525,7 +528,7 @@ __device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, u
       const int r = (int)(o / C::RBA);
       const int c = swz<C::CPA>(r, (int)(o % C::RBA) / 16);
       const int rr = r < lp.mlast ? r : lp.mlast;
-      dma16(abase + (uint32_t)data_off<C>(rr, c * 16, lda), st + C::A_OFF + (i * C::NW + w) * 1024);
+      dma16(abase + (uint32_t)data_off<C, false>(rr, c * 16, lda), st + C::A_OFF + (i * C::NW + w) * 1024);
     }
   });
   const int blk = s * C::BK / 128;  // the stage's 128-element block
@@ -548,7 +551,7 @@ __device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, u
       dma4(bsb + ro, st + C::BS_OFF + (i * C::NW + w) * 256);
     }
   });
-  const uint8_t* bbase = lp.b + s * data_off<C>(0, C::RBB, ldb);
+  const uint8_t* bbase = lp.b + s * data_off<C, true>(0, C::RBB, ldb);
   unroll<C::DB>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     if constexpr (QB + i >= Q0 && QB + i < Q1) {
@@ -556,7 +559,7 @@ __device__ __forceinline__ void issue_stage_lean(const LeanPlan<C>& lp, int s, u
       const int r = (int)(o / C::RBB);
       const int c = swz<C::CPB>(r, (int)(o % C::RBB) / 16);
       const int rr = r < lp.nlast ? r : lp.nlast;
-      dma16(bbase + (uint32_t)data_off<C>(rr, c * 16, ldb), st + C::B_OFF + (i * C::NW + w) * 1024);
+      dma16(bbase + (uint32_t)data_off<C, true>(rr, c * 16, ldb), st + C::B_OFF + (i * C::NW + w) * 1024);
     }
   });
 }
@@ -1486,10 +1489,10 @@ struct RowsSource {
     const int col0 = q.nt * C::BN;
     const int nleft = p.n_out - col0;
     TileOps o;
-    o.a = p.a + data_off<C>(rw.row0, 0, p.lda);
+    o.a = p.a + data_off<C, false>(rw.row0, 0, p.lda);
     // A's scales are block-major ([blocks, rows]: u8, or fp32 for 1x128)
     o.as = p.as + (C::F32S ? rw.row0 * 4 : rw.row0);
-    o.b = p.b + (int64_t)q.g * p.b_gstride + data_off<C>(col0, 0, p.ldb);
+    o.b = p.b + (int64_t)q.g * p.b_gstride + data_off<C, true>(col0, 0, p.ldb);
     o.bs = p.bs + (int64_t)q.g * p.bs_gstride +
            (C::F32S ? (int64_t)(col0 / C::BDIV) * p.ldbs : C::MFB ? (int64_t)col0 * 4 : (int64_t)col0);
     o.mrows = rw.hi < C::BM ? rw.hi : C::BM;
@@ -1605,8 +1608,8 @@ struct WgradSource {
     // segment start: element bytes (E4M3: 1, E2M1: 1/2); scales, MX
     // block-major (block p0/32, row row0), blockwise block-major too (fp32,
     // block p0/128, row row0)
-    o.a = p.a + data_off<C>(q.row0, C::AFP8 ? q.p0 : q.p0 / 2, p.lda);
-    o.b = p.b + data_off<C>(q.col0, C::BFP8 ? q.p0 : q.p0 / 2, p.ldb);
+    o.a = p.a + data_off<C, false>(q.row0, C::AFP8 ? q.p0 : q.p0 / 2, p.lda);
+    o.b = p.b + data_off<C, true>(q.col0, C::BFP8 ? q.p0 : q.p0 / 2, p.ldb);
     if constexpr (C::F32S) {
       o.as = p.as + q.p0 / 128 * p.ldas + (int64_t)q.row0 * 4;
       o.bs = p.bs + q.p0 / 128 * p.ldbs + (int64_t)q.col0 * 4;
@@ -1817,11 +1820,17 @@ static hipError_t launch_rows(const RowsGemmParams& p, bool dgrad, int num_cus, 
   return launch_rows_as<C, false>(p, dgrad, num_cus, st);
 }
 
-hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, bool mfma_b, int num_cus,
-                                  hipStream_t st) {
+template <class C>
+static hipError_t launch_rows_kb(const RowsGemmParams& p, bool dgrad, bool kblk, int num_cus, hipStream_t st) {
+  return kblk ? launch_rows<KBlocked<C>>(p, dgrad, num_cus, st) : launch_rows<C>(p, dgrad, num_cus, st);
+}
+
+hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, bool mfma_b, bool kblk,
+                                  int num_cus, hipStream_t st) {
   if (mfma_b)
-    return a_fp8 ? launch_rows<MfmaB<CfgA8>>(p, dgrad, num_cus, st) : launch_rows<MfmaB<CfgA4>>(p, dgrad, num_cus, st);
-  return a_fp8 ? launch_rows<CfgA8>(p, dgrad, num_cus, st) : launch_rows<CfgA4>(p, dgrad, num_cus, st);
+    return a_fp8 ? launch_rows_kb<MfmaB<CfgA8>>(p, dgrad, kblk, num_cus, st)
+                 : launch_rows_kb<MfmaB<CfgA4>>(p, dgrad, kblk, num_cus, st);
+  return a_fp8 ? launch_rows_kb<CfgA8>(p, dgrad, kblk, num_cus, st) : launch_rows_kb<CfgA4>(p, dgrad, kblk, num_cus, st);
 }
 
 hipError_t launch_grouped_rows_blk(const RowsGemmParams& p, bool pow2, bool dgrad, int num_cus, hipStream_t st) {

@@ -93,13 +93,15 @@ struct DeviceInfo {
 
 // MX quantizers; mfma: scales in the MFMA layout (column-wise: every split a
 // multiple of 128), else block-major
+// kb / kbr / kbc: the row-wise / column-wise codes in 64-byte K blocks
+// (u8 [bytes per row / 64, rows, 64]), else rows
 hipError_t launch_quant_rowwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool fp8, bool mfma,
-                                   uint8_t* q, uint8_t* s, int num_cus, hipStream_t st);
+                                   bool kb, uint8_t* q, uint8_t* s, int num_cus, hipStream_t st);
 hipError_t launch_quant_dual_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
-                                bool fp8, bool mfma, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc, int64_t mpad,
-                                int num_cus, hipStream_t st);
+                                bool fp8, bool mfma, bool kbr, bool kbc, uint8_t* qr, uint8_t* sr, uint8_t* qc,
+                                uint8_t* sc, int64_t mpad, int num_cus, hipStream_t st);
 hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
-                                   bool fp8, bool mfma, uint8_t* q, uint8_t* s, int64_t mpad, int num_cus,
+                                   bool fp8, bool mfma, bool kbc, uint8_t* q, uint8_t* s, int64_t mpad, int num_cus,
                                    hipStream_t st);
 
 // MX scales from one layout (mxgg_scale_layout value) into another
@@ -108,8 +110,9 @@ hipError_t launch_relayout_scales(const uint8_t* src, int src_layout, int64_t ro
 
 // dgrad selects the input-gradient kernel symbol (same code as the forward's);
 // mfma_b: B's scales in the MFMA layout (bs_gstride then in bytes of it)
-hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, bool mfma_b, int num_cus,
-                                  hipStream_t st);
+// kblk: both operands' codes in 64-byte K blocks (lda / ldb = bytes per block)
+hipError_t launch_grouped_rows_mx(const RowsGemmParams& p, bool a_fp8, bool dgrad, bool mfma_b, bool kblk,
+                                  int num_cus, hipStream_t st);
 // fp8: E4M3 operands on both sides (MXFP8), else E2M1 (MXFP4)
 hipError_t launch_grouped_wgrad_mx(const WgradParams& p, bool fp8, int num_cus, hipStream_t st);
 

@@ -34,12 +34,6 @@ namespace mxgg {
 
 namespace {
 
-// Byte c (along the row) of row r of a code tensor with `rows` rows, in 64-byte
-// K blocks: u8 [cols/64, rows, 64].
-__device__ __forceinline__ int64_t kblk_off(int64_t r, int64_t c, int64_t rows) {
-  return (c >> 6) * rows * 64 + r * 64 + (c & 63);
-}
-
 typedef short v2s __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 

@@ -96,7 +96,7 @@ __device__ __forceinline__ uint2 interleave_bytes(uint32_t a, uint32_t b) {
   return make_uint2(lo, hi);
 }
 
-template <class F, int U, bool MFMA>
+template <class F, int U, bool MFMA, bool KB>
 __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __restrict__ x, int64_t ldx, int rows,
                                                             int cpr, uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ s, int64_t sld) {
@@ -129,10 +129,12 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
       const int e = mx_shared_exp<F>(amax);
       if (!(cvalid && r < rows)) continue;
       const float sc = __uint_as_float(mx_scale_operand_bits(e));
+      const int64_t qb = (int64_t)c * (FP4 ? 4 : 8);  // the chunk's first code byte in the row
+      uint8_t* qp = q + (KB ? kblk_off(r, qb, rows) : (int64_t)r * qrow_bytes + qb);
       if constexpr (FP4)
-        *reinterpret_cast<uint32_t*>(q + (int64_t)r * qrow_bytes + (int64_t)c * 4) = encode8_fp4(wd, sc);
+        *reinterpret_cast<uint32_t*>(qp) = encode8_fp4(wd, sc);
       else
-        *reinterpret_cast<uint2*>(q + (int64_t)r * qrow_bytes + (int64_t)c * 8) = encode8_fp8(wd, e, sc);
+        *reinterpret_cast<uint2*>(qp) = encode8_fp8(wd, e, sc);
       sbytes |= (uint32_t)(e + 127) << (8 * u);
     }
     const int r0 = rb + w * U;
@@ -201,7 +203,7 @@ struct DualCfg {
 // one XCD). The expert scan runs once per workgroup, and the loads of the next
 // tile are issued before the column-wise pass of the current one, so they
 // overlap it. ROWS = false: the column-wise output alone (qr, sr unused).
-template <class F, class D, bool XCD, int ORDER, bool MFMA, bool ROWS = true>
+template <class F, class D, bool XCD, int ORDER, bool MFMA, bool ROWS = true, bool KBR = false, bool KBC = false>
 __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persistent(const uint16_t* __restrict__ x, int64_t ldx,
                                                                     int rows, int64_t cols, const SplitArgs sp,
                                                                     int64_t mpad, uint8_t* __restrict__ qr,
@@ -318,10 +320,12 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
       const int64_t r = blk_row0[par][b] + rin;
       const int e = mx_shared_exp<F>(amax);
       const float sc = __uint_as_float(mx_scale_operand_bits(e));
+      const int64_t qb = FP4 ? c0 / 2 + ch * 4 : c0 + ch * 8;  // first code byte in the row
+      uint8_t* qp = qr + (KBR ? kblk_off(r, qb, rows) : r * (FP4 ? cols / 2 : cols) + qb);
       if constexpr (FP4)
-        *reinterpret_cast<uint32_t*>(qr + r * (cols / 2) + c0 / 2 + ch * 4) = encode8_fp4(wd, sc);
+        *reinterpret_cast<uint32_t*>(qp) = encode8_fp4(wd, sc);
       else
-        *reinterpret_cast<uint2*>(qr + r * cols + c0 + ch * 8) = encode8_fp8(wd, e, sc);
+        *reinterpret_cast<uint2*>(qp) = encode8_fp8(wd, e, sc);
       if ((ch & 3) == 0) {
         const int64_t blk = (c0 + ch * 8) >> 5;
         if constexpr (MFMA) {
@@ -365,7 +369,9 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
           for (int i = 0; i < 16; ++i)
             pairs[i] = j ? (w2[2 * i] >> 16) | (w2[2 * i + 1] & 0xffff0000u)
                          : (w2[2 * i] & 0xffffu) | (w2[2 * i + 1] << 16);
-          encode32_store<FP4>(pairs, e, sc, qc + (c0 + c + j) * qld + (FP4 ? p0 / 2 : p0));
+          encode32_store<FP4>(pairs, e, sc,
+                              qc + (KBC ? kblk_off(c0 + c + j, FP4 ? p0 / 2 : p0, cols)
+                                        : (c0 + c + j) * qld + (FP4 ? p0 / 2 : p0)));
           if constexpr (MFMA)
             sc_[mfma_scale_offset(c0 + c + j, p0 / 32, cols)] = (uint8_t)(e + 127);
           else
@@ -398,7 +404,9 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
           for (int i = 0; i < 16; ++i)  // rows 2i (low) and 2i+1 (high) of column c + j
             pairs[i] = j ? (w2[2 * i] >> 16) | (w2[2 * i + 1] & 0xffff0000u)
                          : (w2[2 * i] & 0xffffu) | (w2[2 * i + 1] << 16);
-          encode32_store<FP4>(pairs, e, sc, qc + (c0 + c + j) * qld + (FP4 ? p0 / 2 : p0));
+          encode32_store<FP4>(pairs, e, sc,
+                              qc + (KBC ? kblk_off(c0 + c + j, FP4 ? p0 / 2 : p0, cols)
+                                        : (c0 + c + j) * qld + (FP4 ? p0 / 2 : p0)));
           if constexpr (MFMA)
             sc_[mfma_scale_offset(c0 + c + j, p0 / 32, cols)] = (uint8_t)(e + 127);
           else
@@ -412,12 +420,12 @@ __global__ __launch_bounds__(D::NT, D::WAVES_PER_SIMD) void quant_dual_mx_persis
   }
 }
 
-template <class D, bool XCD, int ORDER, bool MFMA, bool ROWS = true>
+template <class D, bool XCD, int ORDER, bool MFMA, bool ROWS = true, bool KBR = false, bool KBC = false>
 hipError_t launch_quant_dual_persistent(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                         const SplitArgs& sp, bool fp8, uint8_t* qr, uint8_t* sr, uint8_t* qc,
                                         uint8_t* sc, int64_t mpad, int num_cus, hipStream_t st) {
-  auto kern = fp8 ? quant_dual_mx_persistent<E4M3Fmt, D, XCD, ORDER, MFMA, ROWS>
-                  : quant_dual_mx_persistent<E2M1Fmt, D, XCD, ORDER, MFMA, ROWS>;
+  auto kern = fp8 ? quant_dual_mx_persistent<E4M3Fmt, D, XCD, ORDER, MFMA, ROWS, KBR, KBC>
+                  : quant_dual_mx_persistent<E2M1Fmt, D, XCD, ORDER, MFMA, ROWS, KBR, KBC>;
   const hipError_t e = ensure_dynamic_lds((const void*)kern, D::LDS_BYTES, st);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((mpad + D::TR - 1) / D::TR) * ((cols + D::TC - 1) / D::TC);
@@ -438,7 +446,7 @@ using DualCfgProduct = DualCfg<128, 256, 512, 1, 1, 1>;
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <bool MFMA>
+template <bool MFMA, bool KB>
 static void launch_rowwise_as(const uint16_t* x, int64_t rows, int64_t ldx, int cpr, bool fp8, uint8_t* q,
                               uint8_t* s, int64_t sld, hipStream_t st) {
   constexpr int U = 4;
@@ -446,30 +454,49 @@ static void launch_rowwise_as(const uint16_t* x, int64_t rows, int64_t ldx, int 
   const int64_t gy_need = (row_end + 4 * U - 1) / (4 * U);
   const dim3 grid((unsigned)((cpr + 63) / 64), (unsigned)(gy_need < 65535 ? gy_need : 65535));
   if (fp8)
-    hipLaunchKernelGGL((quant_rowwise_kernel<E4M3Fmt, U, MFMA>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q,
-                       s, sld);
+    hipLaunchKernelGGL((quant_rowwise_kernel<E4M3Fmt, U, MFMA, KB>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr,
+                       q, s, sld);
   else
-    hipLaunchKernelGGL((quant_rowwise_kernel<E2M1Fmt, U, MFMA>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr, q,
-                       s, sld);
+    hipLaunchKernelGGL((quant_rowwise_kernel<E2M1Fmt, U, MFMA, KB>), grid, dim3(256), 0, st, x, ldx, (int)rows, cpr,
+                       q, s, sld);
 }
 
 hipError_t launch_quant_rowwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, bool fp8, bool mfma,
-                                   uint8_t* q, uint8_t* s, int num_cus, hipStream_t st) {
+                                   bool kb, uint8_t* q, uint8_t* s, int num_cus, hipStream_t st) {
   (void)num_cus;
   const int cpr = (int)(cols / 8);
-  if (mfma) launch_rowwise_as<true>(x, rows, ldx, cpr, fp8, q, s, mx_rows32(rows) * 4, st);
-  else launch_rowwise_as<false>(x, rows, ldx, cpr, fp8, q, s, mx_scale_stride(rows), st);
+  const int64_t m32 = mx_rows32(rows) * 4, r4 = mx_scale_stride(rows);
+  if (mfma && kb) launch_rowwise_as<true, true>(x, rows, ldx, cpr, fp8, q, s, m32, st);
+  else if (mfma) launch_rowwise_as<true, false>(x, rows, ldx, cpr, fp8, q, s, m32, st);
+  else if (kb) launch_rowwise_as<false, true>(x, rows, ldx, cpr, fp8, q, s, r4, st);
+  else launch_rowwise_as<false, false>(x, rows, ldx, cpr, fp8, q, s, r4, st);
   return hipGetLastError();
 }
 
+// The dual kernel for each scale layout and code layout of its two outputs.
+template <bool MFMA>
+static hipError_t launch_dual_as(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
+                                 bool fp8, bool kbr, bool kbc, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc,
+                                 int64_t mpad, int num_cus, hipStream_t st) {
+  using D = DualCfgProduct;
+  if (kbr && kbc)
+    return launch_quant_dual_persistent<D, false, 1, MFMA, true, true, true>(x, rows, cols, ldx, sp, fp8, qr, sr, qc,
+                                                                             sc, mpad, num_cus, st);
+  if (kbr)
+    return launch_quant_dual_persistent<D, false, 1, MFMA, true, true, false>(x, rows, cols, ldx, sp, fp8, qr, sr,
+                                                                              qc, sc, mpad, num_cus, st);
+  if (kbc)
+    return launch_quant_dual_persistent<D, false, 1, MFMA, true, false, true>(x, rows, cols, ldx, sp, fp8, qr, sr,
+                                                                              qc, sc, mpad, num_cus, st);
+  return launch_quant_dual_persistent<D, false, 1, MFMA, true, false, false>(x, rows, cols, ldx, sp, fp8, qr, sr, qc,
+                                                                             sc, mpad, num_cus, st);
+}
+
 hipError_t launch_quant_dual_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
-                                bool fp8, bool mfma, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc, int64_t mpad,
-                                int num_cus, hipStream_t st) {
-  if (mfma)
-    return launch_quant_dual_persistent<DualCfgProduct, false, 1, true>(x, rows, cols, ldx, sp, fp8, qr, sr, qc, sc,
-                                                                        mpad, num_cus, st);
-  return launch_quant_dual_persistent<DualCfgProduct, false, 1, false>(x, rows, cols, ldx, sp, fp8, qr, sr, qc, sc,
-                                                                       mpad, num_cus, st);
+                                bool fp8, bool mfma, bool kbr, bool kbc, uint8_t* qr, uint8_t* sr, uint8_t* qc,
+                                uint8_t* sc, int64_t mpad, int num_cus, hipStream_t st) {
+  if (mfma) return launch_dual_as<true>(x, rows, cols, ldx, sp, fp8, kbr, kbc, qr, sr, qc, sc, mpad, num_cus, st);
+  return launch_dual_as<false>(x, rows, cols, ldx, sp, fp8, kbr, kbc, qr, sr, qc, sc, mpad, num_cus, st);
 }
 
 // Column-wise alone: the dual kernel without its row-wise output (one read of
@@ -477,13 +504,20 @@ hipError_t launch_quant_dual_mx(const uint16_t* x, int64_t rows, int64_t cols, i
 // flight). Measured against a one-tile-per-workgroup transpose kernel: fc1 W
 // 300 -> 204 us, X 122 -> 76 us, dY 85 -> 72 us; a8w4 W 1.34 -> 1.14 ms.
 hipError_t launch_quant_colwise_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const SplitArgs& sp,
-                                   bool fp8, bool mfma, uint8_t* q, uint8_t* s, int64_t mpad, int num_cus,
+                                   bool fp8, bool mfma, bool kbc, uint8_t* q, uint8_t* s, int64_t mpad, int num_cus,
                                    hipStream_t st) {
-  if (mfma)
-    return launch_quant_dual_persistent<DualCfgProduct, false, 1, true, false>(x, rows, cols, ldx, sp, fp8, nullptr,
+  using D = DualCfgProduct;
+  if (mfma && kbc)
+    return launch_quant_dual_persistent<D, false, 1, true, false, false, true>(x, rows, cols, ldx, sp, fp8, nullptr,
                                                                               nullptr, q, s, mpad, num_cus, st);
-  return launch_quant_dual_persistent<DualCfgProduct, false, 1, false, false>(x, rows, cols, ldx, sp, fp8, nullptr,
-                                                                             nullptr, q, s, mpad, num_cus, st);
+  if (mfma)
+    return launch_quant_dual_persistent<D, false, 1, true, false>(x, rows, cols, ldx, sp, fp8, nullptr, nullptr, q,
+                                                                  s, mpad, num_cus, st);
+  if (kbc)
+    return launch_quant_dual_persistent<D, false, 1, false, false, false, true>(x, rows, cols, ldx, sp, fp8, nullptr,
+                                                                               nullptr, q, s, mpad, num_cus, st);
+  return launch_quant_dual_persistent<D, false, 1, false, false>(x, rows, cols, ldx, sp, fp8, nullptr, nullptr, q, s,
+                                                                 mpad, num_cus, st);
 }
 
 }  // namespace mxgg

@@ -42,7 +42,8 @@ inline bool valid_format(int f) { return f >= MXGG_MXFP4 && f <= MXGG_FP8_128x12
 // writes it and refuses every other layout by name, so a caller's scales are
 // never read in a layout they are not in.
 inline bool has_layout_bits(int f) { return (f & ~0xFF) != 0; }
-inline int layout_bits(int f) { return f & ~0xFF; }
+inline int layout_bits(int f) { return f & MXGG_LAYOUT_MASK; }   // the scales' layout
+inline int kblock_bits(int f) { return f & MXGG_KBLOCK_MASK; }   // the codes' layout
 inline int format_bits(int f) { return f & 0xFF; }
 inline bool is_mfma_layout(int f) { return layout_bits(f) == MXGG_LAYOUT_MFMA; }
 // The power-of-two blockwise formats share their base format's layout.
@@ -81,11 +82,25 @@ constexpr int64_t kMaxSplit = ((int64_t)1 << 31) - 1;
 
 // Padded row count; callers have checked 0 <= m[g] <= kMaxSplit, so neither
 // the rounding nor the sum (at most 512 terms) can overflow.
-// mfma_ok: the operand's MX scales may be in the MFMA layout.
-inline Check check_layout(int f, const char* what, bool mfma_ok = false) {
+// mfma_ok: the operand's MX scales may be in the MFMA layout; kblock_ok: the
+// code-layout bits the entry point takes for this argument.
+inline Check check_layout(int f, const char* what, bool mfma_ok = false, int kblock_ok = 0) {
   if (!has_layout_bits(f)) return Check{};
   const bool mx = is_mx((mxgg_format)format_bits(f));
-  if (mx && layout_bits(f) == MXGG_LAYOUT_MFMA) {
+  if ((f & ~(0xFF | MXGG_LAYOUT_MASK | MXGG_KBLOCK_MASK)) != 0)
+    return fail(MXGG_ERR_FORMAT, "format 0x%llx: unknown bits", f);
+  if (kblock_bits(f)) {
+    if (!mx || (kblock_bits(f) & ~kblock_ok)) {
+      Check r;
+      r.st = MXGG_ERR_FORMAT;
+      r.msg = std::string(what) + ": these 64-byte K-block code bits are not taken here (MX formats only: "
+              "MXGG_KBLOCK_ROWS for row-wise codes, MXGG_KBLOCK_COLS for column-wise codes)";
+      return r;
+    }
+  }
+  const int lay = layout_bits(f);
+  if (lay == MXGG_LAYOUT_BLOCK_MAJOR) return Check{};
+  if (mx && lay == MXGG_LAYOUT_MFMA) {
     if (mfma_ok) return Check{};
     Check r;
     r.st = MXGG_ERR_FORMAT;
@@ -93,7 +108,7 @@ inline Check check_layout(int f, const char* what, bool mfma_ok = false) {
             "the input gradient's wcol_s); this operand's scales must be block-major";
     return r;
   }
-  if (mx && layout_bits(f) == MXGG_LAYOUT_ROW_MAJOR) {
+  if (mx && lay == MXGG_LAYOUT_ROW_MAJOR) {
     Check r;
     r.st = MXGG_ERR_FORMAT;
     r.msg = std::string(what) + ": row-major MX scales are not accepted (the kernels read block-major or "
@@ -103,12 +118,14 @@ inline Check check_layout(int f, const char* what, bool mfma_ok = false) {
   return fail(MXGG_ERR_FORMAT, "format 0x%llx: unknown layout bits or a layout on a blockwise format", f);
 }
 
-// MFMA-layout column scales: every expert segment starts a 128-element unit.
-inline Check check_mfma_splits(const int64_t* m, int32_t G, const char* what) {
+// MFMA-layout column scales and K-blocked column codes: every expert segment
+// starts a 128-element unit.
+inline Check check_mfma_splits(const int64_t* m, int32_t G, const char* what,
+                               const char* why = "MFMA-layout column scales") {
   for (int32_t g = 0; g < G; ++g)
     if (m[g] % 128) {
       Check r = fail(MXGG_ERR_SPLITS, "m_splits[%lld] = %lld is not a multiple of 128", g, m[g]);
-      r.msg = std::string(what) + ": MFMA-layout column scales need every split a multiple of 128; " + r.msg;
+      r.msg = std::string(what) + ": " + why + " need every split a multiple of 128; " + r.msg;
       return r;
     }
   return Check{};
@@ -145,11 +162,12 @@ inline Check check_ptr(const void* p, bool nonzero, const char* name) {
 
 inline Check validate_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                        const void* q, const void* scales) {
-  MXGG_TRY(check_layout(fmt, "quantize_rowwise", true));
-  const bool mfma = is_mfma_layout(fmt);
+  MXGG_TRY(check_layout(fmt, "quantize_rowwise", true, MXGG_KBLOCK_ROWS));
+  const bool mfma = is_mfma_layout(fmt), kb = kblock_bits(fmt) != 0;
   fmt = format_bits(fmt);
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
   if (mfma && cols % 128) return fail(MXGG_ERR_SHAPE, "cols=%lld: MFMA-layout scales need cols %% 128 == 0", cols);
+  if (kb && cols % 128) return fail(MXGG_ERR_SHAPE, "cols=%lld: K-blocked codes need cols %% 128 == 0", cols);
   if (rows < 0 || cols <= 0) return fail(MXGG_ERR_SHAPE, "rows=%lld cols=%lld", rows, cols);
   const mxgg_format f = (mxgg_format)fmt;
   const int blk = is_mx(f) ? 32 : 128;
@@ -170,8 +188,8 @@ inline Check validate_quantize_rowwise(const void* x, int64_t rows, int64_t cols
 
 inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, const int64_t* m,
                                        int32_t G, int fmt, const void* q, const void* scales, int64_t mpad) {
-  MXGG_TRY(check_layout(fmt, "quantize_colwise", true));
-  const bool mfma = is_mfma_layout(fmt);
+  MXGG_TRY(check_layout(fmt, "quantize_colwise", true, MXGG_KBLOCK_COLS));
+  const bool mfma = is_mfma_layout(fmt), kb = kblock_bits(fmt) != 0;
   fmt = format_bits(fmt);
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
   const mxgg_format f = (mxgg_format)fmt;
@@ -187,6 +205,7 @@ inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols
   if (rows >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SHAPE, "rows=%lld >= 2^31", rows);
   MXGG_TRY(check_splits(m, G, rows, "x"));
   if (mfma) MXGG_TRY(check_mfma_splits(m, G, "quantize_colwise"));
+  if (kb) MXGG_TRY(check_mfma_splits(m, G, "quantize_colwise", "K-blocked column codes"));
   const int64_t need = segpad_rows(m, G, segpad_multiple(f));
   if (mpad != need) return fail(MXGG_ERR_SHAPE, "mpad=%lld but the padded row count is %lld", mpad, need);
   if (mpad >= ((int64_t)1 << 31)) return fail(MXGG_ERR_SHAPE, "mpad=%lld >= 2^31", mpad);
@@ -200,13 +219,14 @@ inline Check validate_quantize_colwise(const void* x, int64_t rows, int64_t cols
 inline Check validate_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, const int64_t* m,
                                     int32_t G, int fmt, const void* q_row, const void* s_row, const void* q_col,
                                     const void* s_col, int64_t mpad) {
-  MXGG_TRY(check_layout(fmt, "quantize_dual", true));
+  MXGG_TRY(check_layout(fmt, "quantize_dual", true, MXGG_KBLOCK_MASK));
   const int f0 = format_bits(fmt);
   if (!valid_format(f0)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
   if (!is_mx((mxgg_format)f0) && f0 != MXGG_FP8_1x128)
     return fail(MXGG_ERR_FORMAT, "the dual quantizer takes MX formats and MXGG_FP8_1x128 (got %lld)", fmt);
-  MXGG_TRY(validate_quantize_rowwise(x, rows, cols, ldx, fmt, q_row, s_row));
-  MXGG_TRY(validate_quantize_colwise(x, rows, cols, ldx, m, G, fmt, q_col, s_col, mpad));
+  // each output takes its own code-layout bit
+  MXGG_TRY(validate_quantize_rowwise(x, rows, cols, ldx, fmt & ~MXGG_KBLOCK_COLS, q_row, s_row));
+  MXGG_TRY(validate_quantize_colwise(x, rows, cols, ldx, m, G, fmt & ~MXGG_KBLOCK_ROWS, q_col, s_col, mpad));
   return Check{};
 }
 
@@ -229,12 +249,19 @@ inline Check validate_gemm_dims(int64_t M, int64_t N, int64_t K, int blk) {
 inline Check validate_fwd(const void* a_q, const void* a_s, int a_fmt, const void* w_q, const void* w_s, int w_fmt,
                           const int64_t* m, int32_t G, int64_t M, int64_t N, int64_t K, const void* out,
                           const void* ws, size_t ws_bytes, size_t ws_need) {
-  MXGG_TRY(check_layout(a_fmt, "fwd A"));
-  MXGG_TRY(check_layout(w_fmt, "fwd W", true));
+  MXGG_TRY(check_layout(a_fmt, "fwd A", false, MXGG_KBLOCK_ROWS));
+  MXGG_TRY(check_layout(w_fmt, "fwd W", true, MXGG_KBLOCK_ROWS));
   const bool w_mfma = is_mfma_layout(w_fmt);
+  const bool kb = kblock_bits(a_fmt) != 0;
+  if (kb != (kblock_bits(w_fmt) != 0))
+    return fail(MXGG_ERR_FORMAT, "fwd: a_fmt and w_fmt carry MXGG_KBLOCK_ROWS together or not at all");
+  a_fmt = format_bits(a_fmt);
   w_fmt = format_bits(w_fmt);
   if (!valid_format(a_fmt) || !valid_format(w_fmt)) return fail(MXGG_ERR_FORMAT, "unknown format");
   if (w_mfma && K % 128) return fail(MXGG_ERR_SHAPE, "K=%lld: MFMA-layout weight scales need K %% 128 == 0", K);
+  if (kb && K % 128) return fail(MXGG_ERR_SHAPE, "K=%lld: K-blocked codes need K %% 128 == 0", K);
+  if (kb && (M >= kMaxKBlockRows || (int64_t)G * N >= kMaxKBlockRows))
+    return fail(MXGG_ERR_SHAPE, "K-blocked codes: M=%lld and G*N=%lld must stay below 2^25", M, (int64_t)G * N);
   const bool a4w4 = a_fmt == MXGG_MXFP4 && w_fmt == MXGG_MXFP4;
   const bool a8w4 = a_fmt == MXGG_MXFP8 && w_fmt == MXGG_MXFP4;
   const bool blk = a_fmt == MXGG_FP8_1x128 && w_fmt == MXGG_FP8_128x128;
@@ -259,11 +286,17 @@ inline Check validate_fwd(const void* a_q, const void* a_s, int a_fmt, const voi
 inline Check validate_dgrad(const void* dy_q, const void* dy_s, const void* wc_q, const void* wc_s, int fmt,
                             const int64_t* m, int32_t G, int64_t M, int64_t N, int64_t K, const void* dx,
                             const void* ws, size_t ws_bytes, size_t ws_need) {
-  MXGG_TRY(check_layout(fmt, "dgrad", true));
+  MXGG_TRY(check_layout(fmt, "dgrad", true, MXGG_KBLOCK_MASK));
   const bool w_mfma = is_mfma_layout(fmt);
+  const int kbits = kblock_bits(fmt);
+  if (kbits != 0 && kbits != MXGG_KBLOCK_MASK)
+    return fail(MXGG_ERR_FORMAT, "dgrad: fmt carries MXGG_KBLOCK_ROWS and MXGG_KBLOCK_COLS together or neither");
   fmt = format_bits(fmt);
   if (!valid_format(fmt)) return fail(MXGG_ERR_FORMAT, "unknown format %lld", fmt);
   if (w_mfma && N % 128) return fail(MXGG_ERR_SHAPE, "N=%lld: MFMA-layout weight scales need N %% 128 == 0", N);
+  if (kbits && N % 128) return fail(MXGG_ERR_SHAPE, "N=%lld: K-blocked codes need N %% 128 == 0", N);
+  if (kbits && (M >= kMaxKBlockRows || K >= kMaxKBlockRows))
+    return fail(MXGG_ERR_SHAPE, "K-blocked codes: M=%lld and K=%lld must stay below 2^25", M, K);
   // fmt is dY's format: MXFP4 (a4w4) or MXFP8 (a8w4) with W column-wise in
   // MXFP4; FP8_1x128 with the transposed 128x128 weight blocks
   if (fmt != MXGG_MXFP4 && fmt != MXGG_MXFP8 && fmt != MXGG_FP8_1x128)

@@ -29,6 +29,11 @@ EXPECTED = {
     "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb1E": [5],
     "grouped_fwd_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [5],
     "grouped_dgrad_kernelINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEELb0E": [5],
+    # the same with both operands' codes in 64-byte K blocks
+    "grouped_fwd_kernelINS_8KBlockedINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEELb1E": [5],
+    "grouped_dgrad_kernelINS_8KBlockedINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEELb1E": [5],
+    "grouped_fwd_kernelINS_8KBlockedINS_5MfmaBINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEEEELb1E": [5],
+    "grouped_dgrad_kernelINS_8KBlockedINS_5MfmaBINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEEEELb1E": [5],
     # the same with the weights' scales in the MFMA layout
     "grouped_fwd_kernelINS_5MfmaBINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEELb1E": [5],
     "grouped_dgrad_kernelINS_5MfmaBINS_7TileCfgILi256ELi256ELi2ELi4ELi128ELi4ELi0ELi1ELi7ELi1EEEEELb1E": [5],
