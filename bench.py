@@ -85,6 +85,11 @@ def parse():
                          "a8w4_bwd: its input and weight gradients; blockwise: the blockwise FP8 forward + "
                          "weight gradient; blockwise_dgrad: the blockwise input gradient")
     ap.add_argument("--copy-only", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--codes", default="auto", choices=["auto", "kblock", "rows"],
+                    help="MX code layout of the forward / input-gradient operands: 64-byte K blocks "
+                         "(MXGG_KBLOCK_ROWS / _COLS) or plain rows; auto: K blocks for the training "
+                         "steps (fc1, a8w4_bwd), rows for the a8w4 forward, whose row-wise quantizer "
+                         "writes rows faster than it saves in the GEMM")
     ap.add_argument("--weight-scales", default="block", choices=["block", "mfma"],
                     help="fc1: the weights' MX scales block-major or in the MFMA layout")
     ap.add_argument("--separate-quant", action="store_true",
@@ -358,7 +363,7 @@ def cpu_baseline(seconds_hint=20.0):
                       f"NumPy fp64 oracle (OpenBLAS {threads} threads, host has {os.cpu_count()} cpus)"}
 
 
-def build_workload(name, dev, separate_quant=False, weight_scales="block"):
+def build_workload(name, dev, separate_quant=False, weight_scales="block", codes="auto"):
     """Device inputs, the op list and the per-op algorithmic work of one step.
 
     Returns dict(ops=[(name, kind, fn)], bytes_alg={op: bytes}, flops={op: flops},
@@ -384,6 +389,15 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
     def fp32_normal(shape, seed=SEED_MAIN_GRAD):
         return torch.randn(shape, generator=gen_for(seed), device=dev, dtype=torch.float32)
 
+    # MX code layout: 64-byte K blocks (u8 [bytes per row / 64, rows, 64]) or rows
+    if codes == "auto":
+        codes = "rows" if name == "a8w4" else "kblock"
+    kr = mxg.KBLOCK_ROWS if codes == "kblock" else 0
+    kc = mxg.KBLOCK_COLS if codes == "kblock" else 0
+
+    def codes_buf(rows, row_bytes, blocked):
+        return torch.empty((row_bytes // 64, rows, 64) if blocked else (rows, row_bytes), **u8)
+
     if name == "fc1":
         wl = WORKLOADS["fc1"]
         G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
@@ -394,40 +408,41 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
         # MX scales are block-major: [blocks of 32 along the contraction, rows
         # rounded up to a multiple of 4]
         R4 = mxg.mx_scale_stride(M)
-        aq, as_ = torch.empty((M, K // 2), **u8), torch.empty((K // 32, R4), **u8)
+        aq, as_ = codes_buf(M, K // 2, kr), torch.empty((K // 32, R4), **u8)
         # the weights' scales block-major, or in the MFMA layout ([K/128,
         # G*N*4] row-wise, [G*N/128, K*4] column-wise)
         lay = mxg.LAYOUT_MFMA if weight_scales == "mfma" else mxg.LAYOUT_BLOCK_MAJOR
         wfmt = mxg.MXFP4 | lay
+        xf, dyf = mxg.MXFP4 | kr, mxg.MXFP4 | kr  # activations: blocked row-wise codes, plain column codes
         ws_shape = (K // 128, G * N * 4) if lay else (K // 32, G * N)
         wcs_shape = (G * N // 128, K * 4) if lay else (G * N // 32, K)
-        wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty(ws_shape, **u8)
+        wq, ws = codes_buf(G * N, K // 2, kr), torch.empty(ws_shape, **u8)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        dq, ds = torch.empty((M, N // 2), **u8), torch.empty((N // 32, R4), **u8)
-        wcq, wcs = torch.empty((K, G * N // 2), **u8), torch.empty(wcs_shape, **u8)
+        dq, ds = codes_buf(M, N // 2, kr), torch.empty((N // 32, R4), **u8)
+        wcq, wcs = codes_buf(K, G * N // 2, kc), torch.empty(wcs_shape, **u8)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         dcq, dcs = torch.empty((N, mpad // 2), **u8), torch.empty((mpad // 32, N), **u8)
         xcq, xcs = torch.empty((K, mpad // 2), **u8), torch.empty((mpad // 32, K), **u8)
         wsp = [N] * G
         dual_ops = [
-            ("quant_X_dual", "quant", lambda: mxg.quantize_dual(a, sp, "mxfp4", q_row=aq, s_row=as_, q_col=xcq,
+            ("quant_X_dual", "quant", lambda: mxg.quantize_dual(a, sp, xf, q_row=aq, s_row=as_, q_col=xcq,
                                                                 s_col=xcs)),
-            ("quant_W_dual", "quant", lambda: mxg.quantize_dual(w, wsp, wfmt, q_row=wq, s_row=ws, q_col=wcq,
-                                                                s_col=wcs)),
-            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, w_fmt=wfmt, out=y)),
-            ("quant_dY_dual", "quant", lambda: mxg.quantize_dual(dy, sp, "mxfp4", q_row=dq, s_row=ds, q_col=dcq,
+            ("quant_W_dual", "quant", lambda: mxg.quantize_dual(w, wsp, wfmt | kr | kc, q_row=wq, s_row=ws,
+                                                                q_col=wcq, s_col=wcs)),
+            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt=xf, w_fmt=wfmt | kr, out=y)),
+            ("quant_dY_dual", "quant", lambda: mxg.quantize_dual(dy, sp, dyf, q_row=dq, s_row=ds, q_col=dcq,
                                                                  s_col=dcs)),
-            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, fmt=wfmt, dx=dx)),
+            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, fmt=wfmt | kr | kc, dx=dx)),
             ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, main_grad,
                                                         accumulate=True)),
         ]
         ops = [
-            ("quant_A_row", "quant", lambda: mxg.quantize_rowwise(a, "mxfp4", q=aq, scales=as_)),
-            ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, wfmt, q=wq, scales=ws)),
-            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, w_fmt=wfmt, out=y)),
-            ("quant_dY_row", "quant", lambda: mxg.quantize_rowwise(dy, "mxfp4", q=dq, scales=ds)),
-            ("quant_W_col", "quant", lambda: mxg.quantize_colwise_segpad(w, [N] * G, wfmt, q=wcq, scales=wcs)),
-            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, fmt=wfmt, dx=dx)),
+            ("quant_A_row", "quant", lambda: mxg.quantize_rowwise(a, xf, q=aq, scales=as_)),
+            ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, wfmt | kr, q=wq, scales=ws)),
+            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt=xf, w_fmt=wfmt | kr, out=y)),
+            ("quant_dY_row", "quant", lambda: mxg.quantize_rowwise(dy, dyf, q=dq, scales=ds)),
+            ("quant_W_col", "quant", lambda: mxg.quantize_colwise_segpad(w, [N] * G, wfmt | kc, q=wcq, scales=wcs)),
+            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, fmt=wfmt | kr | kc, dx=dx)),
             ("quant_dY_col", "quant", lambda: mxg.quantize_colwise_segpad(dy, sp, "mxfp4", q=dcq, scales=dcs)),
             ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "mxfp4", q=xcq, scales=xcs)),
             ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, main_grad,
@@ -450,6 +465,7 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
         config = {"workload": "MoE FC1 a4w4 training step (fwd+dgrad+wgrad with MX quantization)",
                   "quantizers": "separate" if separate_quant else "dual-output",
                   "weight_scales": "MFMA layout" if lay else "block-major",
+                  "codes": "64-byte K blocks (fwd/dgrad operands)" if kr else "rows",
                   "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz,
                   "max_split": int(sp.max()), "mpad": mpad, "routing": "Dirichlet(0.5), 3 zeroed, seed 0"}
         return dict(ops=ops, bytes_alg=bytes_alg, flops={"fwd": 2.0 * M * N * K, "dgrad": 2.0 * M * N * K,
@@ -462,19 +478,20 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
         G, M, K, N = wl["G"], wl["M"], wl["K"], wl["N"]
         sp = splits_for("a8w4")
         a, w = normal((M, K), seed=SEED_A), normal((G * N, K), wl["w_std"], seed=SEED_W)
-        aq, as_ = torch.empty((M, K), **u8), torch.empty((K // 32, mxg.mx_scale_stride(M)), **u8)
-        wq, ws = torch.empty((G * N, K // 2), **u8), torch.empty((K // 32, G * N), **u8)
+        aq, as_ = codes_buf(M, K, kr), torch.empty((K // 32, mxg.mx_scale_stride(M)), **u8)
+        wq, ws = codes_buf(G * N, K // 2, kr), torch.empty((K // 32, G * N), **u8)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        af, wf = mxg.MXFP8 | kr, mxg.MXFP4 | kr
         ops = [
-            ("quant_A_row", "quant", lambda: mxg.quantize_rowwise(a, "mxfp8", q=aq, scales=as_)),
-            ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, "mxfp4", q=wq, scales=ws)),
-            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt="mxfp8", out=y)),
+            ("quant_A_row", "quant", lambda: mxg.quantize_rowwise(a, af, q=aq, scales=as_)),
+            ("quant_W_row", "quant", lambda: mxg.quantize_rowwise(w, wf, q=wq, scales=ws)),
+            ("fwd", "gemm", lambda: mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt=af, w_fmt=wf, out=y)),
         ]
         nz = int((sp > 0).sum())
         bytes_alg = {"quant_A_row": M * K * (2 + 1 + 1 / 32), "quant_W_row": G * N * K * (2 + 0.5 + 1 / 32),
                      "fwd": M * K * (1 + 1 / 32) + nz * N * K * (0.5 + 1 / 32) + M * N * 2}
         config = {"workload": "MoE a8w4 forward (MXFP8 activations x MXFP4 weights, with quantization)",
-                  "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz, "max_split": int(sp.max()),
+                  "codes": "64-byte K blocks" if kr else "rows", "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz, "max_split": int(sp.max()),
                   "routing": "Zipf(1.1), 8 zeroed, seed 0"}
         return dict(ops=ops, bytes_alg=bytes_alg, flops={"fwd": 2.0 * M * N * K}, config=config,
                     peak_tflops=PEAK_FP8_TFLOPS, dtype="mxfp8xmxfp4", hbm_gemms=set(),
@@ -490,16 +507,18 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
         a, w = normal((M, K), seed=SEED_A), normal((G * N, K), wl["w_std"], seed=SEED_W)
         dy, main_grad = normal((M, N), seed=SEED_DY), fp32_normal((G, N, K))
         R4 = mxg.mx_scale_stride(M)
-        dq, ds = torch.empty((M, N), **u8), torch.empty((N // 32, R4), **u8)
+        dq, ds = codes_buf(M, N, kr), torch.empty((N // 32, R4), **u8)
         dcq, dcs = torch.empty((N, mpad), **u8), torch.empty((mpad // 32, N), **u8)
-        wcq, wcs = torch.empty((K, G * N // 2), **u8), torch.empty((G * N // 32, K), **u8)
+        wcq, wcs = codes_buf(K, G * N // 2, kc), torch.empty((G * N // 32, K), **u8)
         xcq, xcs = torch.empty((K, mpad), **u8), torch.empty((mpad // 32, K), **u8)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         ops = [
-            ("quant_dY_dual", "quant", lambda: mxg.quantize_dual(dy, sp, "mxfp8", q_row=dq, s_row=ds, q_col=dcq,
-                                                                 s_col=dcs)),
-            ("quant_W_col", "quant", lambda: mxg.quantize_colwise_segpad(w, [N] * G, "mxfp4", q=wcq, scales=wcs)),
-            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, fmt="mxfp8", dx=dx)),
+            ("quant_dY_dual", "quant", lambda: mxg.quantize_dual(dy, sp, mxg.MXFP8 | kr, q_row=dq, s_row=ds,
+                                                                 q_col=dcq, s_col=dcs)),
+            ("quant_W_col", "quant", lambda: mxg.quantize_colwise_segpad(w, [N] * G, mxg.MXFP4 | kc, q=wcq,
+                                                                         scales=wcs)),
+            ("dgrad", "gemm", lambda: mxg.grouped_dgrad(dq, ds, wcq, wcs, sp, N, K, fmt=mxg.MXFP8 | kr | kc,
+                                                        dx=dx)),
             ("quant_X_col", "quant", lambda: mxg.quantize_colwise_segpad(a, sp, "mxfp8", q=xcq, scales=xcs)),
             ("wgrad", "gemm", lambda: mxg.grouped_wgrad(dcq, dcs, xcq, xcs, sp, N, K, mpad, main_grad,
                                                         accumulate=True, fmt="mxfp8")),
@@ -512,7 +531,7 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block"):
                      "wgrad": mpad * (N + K) * q8 + nz * N * K * 4 * 2}
         config = {"workload": "MoE a8w4 backward (input gradient MXFP8 x MXFP4, weight gradient MXFP8 x MXFP8 "
                               "with fp32 main_grad accumulate, with quantization)",
-                  "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz, "max_split": int(sp.max()),
+                  "codes": "64-byte K blocks (dgrad operands)" if kr else "rows", "experts": G, "rows": M, "K": K, "N": N, "nonempty_experts": nz, "max_split": int(sp.max()),
                   "mpad": mpad, "routing": "Zipf(1.1), 8 zeroed, seed 0"}
         return dict(ops=ops, bytes_alg=bytes_alg, flops={"dgrad": 2.0 * M * N * K, "wgrad": 2.0 * M * N * K},
                     config=config, peak_tflops=PEAK_FP8_TFLOPS, dtype="mxfp8xmxfp4", hbm_gemms={"wgrad"},
@@ -684,7 +703,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    W = build_workload(args.workload, dev, args.separate_quant, args.weight_scales)
+    W = build_workload(args.workload, dev, args.separate_quant, args.weight_scales, args.codes)
     if args.passes != "all":
         keep = {"fwd": {"quant_A_row", "quant_W_row", "quant_X_dual", "quant_W_dual", "fwd"},
                 "dgrad": {"quant_dY_row", "quant_W_col", "quant_dY_dual", "quant_W_dual", "dgrad"},
@@ -730,7 +749,7 @@ def main():
         torch.cuda.empty_cache()
         extra = {}
         for name in EXTRA_WORKLOADS:
-            X = build_workload(name, dev)
+            X = build_workload(name, dev, codes=args.codes)
             t_x, per_x, roof_x = measure(X, args, dev)
             tr_x = read_traffic(roof_x["kernel"], name)
             roof_x["traffic"] = None if tr_x is None else round(tr_x[0] + tr_x[1])

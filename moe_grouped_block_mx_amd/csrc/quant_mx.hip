@@ -87,6 +87,10 @@ __device__ __forceinline__ void encode32_store(const uint32_t (&pairs)[16], int 
 // four rows as two 8-byte runs (K step pairs of fragment lanes r%32 and
 // r%32 + 32); the row groups then run to the 32-row padding, whose scales
 // are 0.
+// K-blocked codes (KB) go through LDS: the workgroup's 16 rows x 64 chunks
+// are staged as [K block][row][64 bytes], so that after one barrier every
+// store instruction writes 1 KiB that is contiguous in the K-blocked layout
+// (the 16 rows of one K block), not 64-byte pieces of rows*64 apart.
 // Grid: x over 64-chunk column groups, y over 4*U-row groups (grid-strided).
 // ---------------------------------------------------------------------------
 // bytes (a0 b0 a1 b1 | a2 b2 a3 b3) of two words
@@ -106,6 +110,10 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
   const bool cvalid = c < cpr;
   const int64_t qrow_bytes = FP4 ? (int64_t)cpr * 4 : (int64_t)cpr * 8;
   static_assert(U == 4, "four rows per thread: one 4-byte scale store");
+  constexpr int BPC = FP4 ? 4 : 8;  // code bytes per 8-element chunk
+  constexpr int CPB = 64 / BPC;     // chunks per 64-byte K block
+  // K-blocked staging: 16 rows x 64 chunks x BPC bytes (64 * BPC uint4)
+  __shared__ uint4 stage[KB ? 64 * BPC : 1];
   // MFMA: sld is the 128-element group stride (padded rows x 4 bytes)
   const int row_end = MFMA ? (int)(sld / 4) : rows;
   for (int rb = blockIdx.y * (4 * U); rb < row_end; rb += gridDim.y * (4 * U)) {
@@ -127,14 +135,24 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
       amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
       amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
       const int e = mx_shared_exp<F>(amax);
-      if (!(cvalid && r < rows)) continue;
       const float sc = __uint_as_float(mx_scale_operand_bits(e));
-      const int64_t qb = (int64_t)c * (FP4 ? 4 : 8);  // the chunk's first code byte in the row
-      uint8_t* qp = q + (KB ? kblk_off(r, qb, rows) : (int64_t)r * qrow_bytes + qb);
-      if constexpr (FP4)
-        *reinterpret_cast<uint32_t*>(qp) = encode8_fp4(wd, sc);
-      else
-        *reinterpret_cast<uint2*>(qp) = encode8_fp8(wd, e, sc);
+      if constexpr (KB) {
+        // every lane stages its codes (rows past the end and chunks past the
+        // row are zeros and never stored); the stores follow the barrier
+        uint8_t* sp = reinterpret_cast<uint8_t*>(stage) + ((lane / CPB) * 16 + w * U + u) * 64 + (lane % CPB) * BPC;
+        if constexpr (FP4)
+          *reinterpret_cast<uint32_t*>(sp) = encode8_fp4(wd, sc);
+        else
+          *reinterpret_cast<uint2*>(sp) = encode8_fp8(wd, e, sc);
+        if (!(cvalid && r < rows)) continue;
+      } else {
+        if (!(cvalid && r < rows)) continue;
+        uint8_t* qp = q + (int64_t)r * qrow_bytes + (int64_t)c * BPC;
+        if constexpr (FP4)
+          *reinterpret_cast<uint32_t*>(qp) = encode8_fp4(wd, sc);
+        else
+          *reinterpret_cast<uint2*>(qp) = encode8_fp8(wd, e, sc);
+      }
       sbytes |= (uint32_t)(e + 127) << (8 * u);
     }
     const int r0 = rb + w * U;
@@ -151,6 +169,21 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint16_t* __re
       // block-major scales [cols/32, sld], sld = rows rounded up to a multiple
       // of 4: the thread's four rows are one aligned word (padding rows get 0)
       if (cvalid && (c & 3) == 0 && r0 < rows) *reinterpret_cast<uint32_t*>(s + (int64_t)(c >> 2) * sld + r0) = sbytes;
+    }
+    if constexpr (KB) {
+      __syncthreads();
+      // the tile's BPC K blocks of 16 rows: 16 bytes per thread and store,
+      // 64 threads (one wave) per K block
+      const int64_t nkb = (int64_t)cpr * BPC / 64;  // K blocks per row
+#pragma unroll
+      for (int i = 0; i < BPC / 4; ++i) {
+        const int p = threadIdx.x + i * 256;
+        const int rl = (p >> 2) & 15, r = rb + rl;
+        const int64_t kbg = (int64_t)blockIdx.x * BPC + (p >> 6);
+        if (kbg < nkb && r < rows)
+          *reinterpret_cast<uint4*>(q + (kbg * rows + r) * 64 + (p & 3) * 16) = stage[p];
+      }
+      __syncthreads();
     }
   }
 }
