@@ -36,6 +36,13 @@ Recipes (activation, weight, gradient formats):
   "blockwise" 1x128 activations / gradients and 128x128 weights, E4M3 with
               power-of-two scales (the input gradient reads the weights'
               blocks transposed).
+When in_features and out_features are multiples of 128, the MX recipes keep
+every row-wise code tensor (activations, output gradients, weights along K)
+and the weights along N in 64-byte K blocks (MXGG_KBLOCK_ROWS /
+MXGG_KBLOCK_COLS: the forward's and the input gradient's operand stages
+become contiguous runs; the results are the same bits); the weight
+gradient's column-wise operands stay in rows. Blockwise codes are always
+K-blocked.
 """
 import torch
 
@@ -46,6 +53,22 @@ RECIPES = {
     "a8w4": dict(act="mxfp8", wgt="mxfp4", grad="mxfp8"),
     "blockwise": dict(act="fp8_1x128_p2", wgt="fp8_128x128_p2", grad="fp8_1x128_p2"),
 }
+
+
+def _formats(recipe, N, K):
+    """The format (with its code-layout bits) of each call of a recipe for a
+    layer of K inputs and N outputs."""
+    r = RECIPES[recipe]
+    if recipe == "blockwise" or K % 128 or N % 128:
+        return dict(act=r["act"], wgt_q=r["wgt"], fwd_w=r["wgt"], grad=r["grad"], dgrad=r["grad"], wgrad=r["grad"])
+    kr, kc = L.KBLOCK_ROWS, L.KBLOCK_COLS
+    act, wgt, grad = L.FORMATS[r["act"]], L.FORMATS[r["wgt"]], L.FORMATS[r["grad"]]
+    return dict(act=act | kr, wgt_q=wgt | kr | kc, fwd_w=wgt | kr, grad=grad | kr, dgrad=grad | kr | kc, wgrad=grad)
+
+
+def _code_rows(q):
+    """Rows of a code tensor: [rows, bytes] or K-blocked [bytes/64, rows, 64]."""
+    return q.shape[1] if q.dim() == 3 else q.shape[0]
 
 
 class _WeightCache:
@@ -63,20 +86,20 @@ class _WeightCache:
             # reuse without checking the version (the caller promises the
             # weight is unchanged); refuse a cache that cannot serve the layer
             if self.fwd is None or self.key[2] != recipe or self.key[0] != weight.data_ptr() \
-                    or self.fwd[0].device != weight.device or self.fwd[0].shape[0] != G * N:
+                    or self.fwd[0].device != weight.device or _code_rows(self.fwd[0]) != G * N:
                 raise RuntimeError("is_first_microbatch=False but no compatible cached weight quantization exists "
                                    "(run a microbatch with is_first_microbatch=True or None first)")
             return self.fwd, self.dgrad
         if is_first_microbatch or key != self.key:
-            r = RECIPES[recipe]
+            f = _formats(recipe, N, K)
             if recipe == "blockwise":
-                q, s = L.mxgg_quantize_rowwise(weight, r["wgt"])
+                q, s = L.mxgg_quantize_rowwise(weight, f["wgt_q"])
                 self.fwd = (q, s)
                 self.dgrad = L.mxgg_transpose_128x128(q, s, G, N, K)
             else:
                 # row-wise along K for the forward, along N (segments of N
                 # rows per expert) for the input gradient, from one read
-                qr, sr, qc, sc, _ = L.mxgg_quantize_dual(weight, [N] * G, r["wgt"])
+                qr, sr, qc, sc, _ = L.mxgg_quantize_dual(weight, [N] * G, f["wgt_q"])
                 self.fwd, self.dgrad = (qr, sr), (qc, sc)
             self.key = key
         return self.fwd, self.dgrad
@@ -96,11 +119,11 @@ class _GroupedLinearFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, weight, m_splits, module, is_first_microbatch, out, dgrad_out):
         G, N, K, recipe = module.num_experts, module.out_features, module.in_features, module.recipe
-        r = RECIPES[recipe]
+        f = _formats(recipe, N, K)
         (wq, ws), wdgrad = module._cache.get(weight, recipe, G, N, K, is_first_microbatch)
         need_wgrad = ctx.needs_input_grad[1]
-        xrow, xcol = _quantize_act(x, m_splits, r["act"], need_wgrad)
-        y = L.mxgg_grouped_fwd(xrow[0], xrow[1], wq, ws, m_splits, N, K, a_fmt=r["act"], w_fmt=r["wgt"], out=out)
+        xrow, xcol = _quantize_act(x, m_splits, f["act"], need_wgrad)
+        y = L.mxgg_grouped_fwd(xrow[0], xrow[1], wq, ws, m_splits, N, K, a_fmt=f["act"], w_fmt=f["fwd_w"], out=out)
         ctx.module, ctx.m_splits, ctx.wdgrad, ctx.xcol = module, m_splits, wdgrad, xcol
         ctx.need_dx = ctx.needs_input_grad[0]
         ctx.dgrad_out = dgrad_out
@@ -112,14 +135,14 @@ class _GroupedLinearFn(torch.autograd.Function):
     def backward(ctx, dy):
         module, m_splits = ctx.module, ctx.m_splits
         G, N, K, recipe = module.num_experts, module.out_features, module.in_features, module.recipe
-        r = RECIPES[recipe]
+        f = _formats(recipe, N, K)
         dy = dy.contiguous()
         need_wgrad = ctx.xcol is not None
-        drow, dcol = _quantize_act(dy, m_splits, r["grad"], need_wgrad)
+        drow, dcol = _quantize_act(dy, m_splits, f["grad"], need_wgrad)
         dx = None
         if ctx.need_dx:
             dx = L.mxgg_grouped_dgrad(drow[0], drow[1], ctx.wdgrad[0], ctx.wdgrad[1], m_splits, N, K,
-                                      fmt=r["grad"], dx=ctx.dgrad_out)
+                                      fmt=f["dgrad"], dx=ctx.dgrad_out)
         if need_wgrad:
             # the accumulation mode is the one in force at this backward
             accumulate = not getattr(module.weight, "overwrite_main_grad", False)
@@ -168,7 +191,7 @@ class GroupedLinear(torch.nn.Module):
     def _run_wgrad(self, job):
         dq, ds, xq, xs, m_splits, mpad, accumulate = job
         L.mxgg_grouped_wgrad(dq, ds, xq, xs, m_splits, self.out_features, self.in_features, mpad,
-                             self.weight.main_grad, accumulate=accumulate, fmt=RECIPES[self.recipe]["grad"])
+                             self.weight.main_grad, accumulate=accumulate, fmt=_formats(self.recipe, self.out_features, self.in_features)["wgrad"])
 
     def backward_dw(self):
         """Launch the delayed weight gradients, oldest first."""

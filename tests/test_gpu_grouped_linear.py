@@ -31,9 +31,10 @@ def _bits(t):
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def _oracle(recipe, x_bits, w_bits, dy_bits, splits):
+def _oracle(recipe, x_bits, w_bits, dy_bits, splits, gnk=(G, N, K)):
     """fp64 forward output, input gradient and weight gradient on the
     oracle's quantized operands of the recipe."""
+    G, N, K = gnk
     r = RECIPES[recipe]
     if recipe == "blockwise":
         X = ob.dequantize_1x128(*ob.quantize_1x128(x_bits))
@@ -74,6 +75,7 @@ def test_forward_backward_match_oracle(recipe):
     y.backward(dev_bf16(dy_bits))
     torch.cuda.synchronize()
     assert layer.weight.grad is None       # accumulated into main_grad instead
+    assert layer._cache.fwd[0].dim() == 3  # K-blocked codes (K and N are multiples of 128)
     ry, rdx, rdw = _oracle(recipe, x_bits, _bits(layer.weight), dy_bits, SPLITS)
     assert_gemm_close(host_bf16_f64(y), ry, what=f"{recipe} forward")
     assert_gemm_close(host_bf16_f64(x.grad), rdx, what=f"{recipe} input gradient")
@@ -176,8 +178,30 @@ def test_preallocated_out_and_dgrad_out_are_written_and_returned():
         layer(x, SPLITS, dgrad_out=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
 
 
-def test_is_first_microbatch_controls_weight_quantization():
-    layer = _layer("a4w4")
+@pytest.mark.parametrize("recipe", ["a4w4", "a8w4"])
+def test_mx_layer_with_features_off_128_keeps_plain_codes(recipe):
+    # K-blocked MX codes need K and N to be multiples of 128; other layers
+    # run on plain rows
+    g, k, n, splits = 3, 160, 96, [40, 0, 57]
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    layer = GroupedLinear(g, k, n, recipe=recipe, weight_std=0.05, generator=gen)
+    m = sum(splits)
+    x_bits = bf16_normal((m, k), 1.0, seed=11)
+    dy_bits = bf16_normal((m, n), 1.0, seed=13)
+    x = dev_bf16(x_bits).requires_grad_(True)
+    y = layer(x, splits)
+    y.backward(dev_bf16(dy_bits))
+    torch.cuda.synchronize()
+    assert layer._cache.fwd[0].dim() == 2
+    ry, rdx, rdw = _oracle(recipe, x_bits, _bits(layer.weight), dy_bits, splits, gnk=(g, n, k))
+    assert_gemm_close(host_bf16_f64(y), ry, what=f"{recipe} forward, K={k} N={n}")
+    assert_gemm_close(host_bf16_f64(x.grad), rdx, what=f"{recipe} input gradient, K={k} N={n}")
+    assert_gemm_close(host(layer.weight.main_grad).astype(np.float64), rdw, what=f"{recipe} weight gradient")
+
+
+@pytest.mark.parametrize("recipe", ["a4w4", "a8w4", "blockwise"])
+def test_is_first_microbatch_controls_weight_quantization(recipe):
+    layer = _layer(recipe)
     M = sum(SPLITS)
     x = dev_bf16(bf16_normal((M, K), 1.0, seed=70))
     with pytest.raises(RuntimeError, match="is_first_microbatch=False"):
@@ -191,5 +215,5 @@ def test_is_first_microbatch_controls_weight_quantization():
     y2 = layer(x, SPLITS, is_first_microbatch=True)           # quantized again
     torch.cuda.synchronize()
     assert layer._cache.fwd[0] is not q0
-    ry = _oracle("a4w4", _bits(x), _bits(layer.weight), bf16_normal((M, N), 1.0, seed=1), SPLITS)[0]
+    ry = _oracle(recipe, _bits(x), _bits(layer.weight), bf16_normal((M, N), 1.0, seed=1), SPLITS)[0]
     assert_gemm_close(host_bf16_f64(y2), ry, what="forward after is_first_microbatch=True")
