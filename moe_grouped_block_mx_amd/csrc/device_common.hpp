@@ -74,14 +74,6 @@ __device__ inline int upper_bound_i32(const int32_t* arr, int n, int32_t val) {
   return lo;
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
 // The i-th 16-byte chunk position after an XOR swizzle of the chunk index by
 // row bits, for the MFMA fragment reads (ds_read_b128: lane l reads row
 // base + l%32, chunk k + l/32, base a multiple of 32). The masks were chosen by

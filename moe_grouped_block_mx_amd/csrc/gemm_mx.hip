@@ -79,9 +79,6 @@ static __device__ __attribute__((aligned(64))) uint32_t g_zero_page[16];
 __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds((const void*)src, (MXGG_LDS void*)lds, 16, 0, 0);
 }
-__device__ __forceinline__ void dma1(const uint8_t* src, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds((const void*)src, (MXGG_LDS void*)lds, 1, 0, 0);
-}
 __device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds((const void*)src, (MXGG_LDS void*)lds, 4, 0, 0);
 }
