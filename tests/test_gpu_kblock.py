@@ -128,6 +128,30 @@ def test_full_size_fc1_forward_and_input_gradient_are_bit_identical():
     assert torch.equal(out[0][1], out[KR | KC][1])
 
 
+def test_full_size_a8w4_forward_and_input_gradient_are_bit_identical():
+    # a8w4 shapes: 128 experts, 65536 routed rows, K = 7168, N = 2048; MXFP8
+    # activations and output gradients, MXFP4 weights
+    from synth import splits_for
+    G, M, K, N = 128, 65536, 7168, 2048
+    sp = [int(v) for v in splits_for("a8w4")]
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    x = torch.randn((M, K), device="cuda", generator=gen).to(torch.bfloat16)
+    w = (torch.randn((G * N, K), device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    dy = torch.randn((M, N), device="cuda", generator=gen).to(torch.bfloat16)
+    out = {}
+    for kb in (0, KR | KC):
+        aq, as_ = mxg.quantize_rowwise(x, mxg.MXFP8 | (kb & KR))
+        dq, ds = mxg.quantize_rowwise(dy, mxg.MXFP8 | (kb & KR))
+        wq, ws, wc, wcs, _ = mxg.quantize_dual(w, [N] * G, mxg.MXFP4 | kb)
+        out[kb] = (mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt=mxg.MXFP8 | (kb & KR),
+                                   w_fmt=mxg.MXFP4 | (kb & KR)),
+                   mxg.grouped_dgrad(dq, ds, wc, wcs, sp, N, K, fmt=mxg.MXFP8 | kb))
+        del aq, as_, dq, ds, wq, ws, wc, wcs
+    torch.cuda.synchronize()
+    assert torch.equal(out[0][0], out[KR | KC][0])
+    assert torch.equal(out[0][1], out[KR | KC][1])
+
+
 def test_k_block_bits_refused_where_the_header_says():
     sp = [128, 128]
     M, N, K = 256, 128, 128
