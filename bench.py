@@ -44,6 +44,7 @@ over GRBM_GUI_ACTIVE x SIMDs), null likewise.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
                        [--workload fc1|a8w4|a8w4_bwd|blockwise|blockwise_dgrad] [--separate-quant]
+                       [--codes auto|kblock|rows] [--weight-scales block|mfma] [--rotate N]
        python bench.py --copy-only            (calibration copy for --pmc runs)
        python bench.py --summarize KERNEL STATS_CSV FETCH_CSV WRITE_CSV
                        COPY_FETCH_CSV COPY_WRITE_CSV   (writes the summary text)
@@ -76,6 +77,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=1,
+                    help="independent copies of every input and output buffer, cycled step by step (3 or more: "
+                         "no step finds the previous step's data in the 256 MB MALL or the L2s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="fc1: skip the a8w4 and blockwise workloads timed beside the headline")
@@ -612,19 +616,25 @@ def build_workload(name, dev, separate_quant=False, weight_scales="block", codes
     raise SystemExit(f"unknown workload {name!r}")
 
 
-def measure(W, args, dev):
+def measure(W, args, dev, sets=None):
     """Warm-up, then `steps` timed steps of the workload's ops between device
     synchronizations, then `steps` more with HIP events around every launch on
-    the stream it is launched on. Returns (seconds per step, per-kernel dict,
-    roofline dict of the kernel with the largest time)."""
+    the stream it is launched on. With `sets` (independent copies of the
+    workload's buffers), step i runs on copy i % len(sets). Returns (seconds
+    per step, per-kernel dict, roofline dict of the kernel with the largest
+    time)."""
     import torch
 
     ops, bytes_alg, flops = W["ops"], W["bytes_alg"], W["flops"]
+    op_sets = [X["ops"] for X in sets] if sets else [ops]
     stream = torch.cuda.current_stream(dev)
     ev = {name: [] for name, _, _ in ops}
+    n_step = [0]
 
     def step(record):
-        for name, _, fn in ops:
+        cur = op_sets[n_step[0] % len(op_sets)]
+        n_step[0] += 1
+        for name, _, fn in cur:
             if record:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -703,14 +713,17 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    W = build_workload(args.workload, dev, args.separate_quant, args.weight_scales, args.codes)
+    Ws = [build_workload(args.workload, dev, args.separate_quant, args.weight_scales, args.codes)
+          for _ in range(args.rotate)]
     if args.passes != "all":
         keep = {"fwd": {"quant_A_row", "quant_W_row", "quant_X_dual", "quant_W_dual", "fwd"},
                 "dgrad": {"quant_dY_row", "quant_W_col", "quant_dY_dual", "quant_W_dual", "dgrad"},
                 "wgrad": {"quant_dY_col", "quant_X_col", "quant_X_dual", "quant_dY_dual", "wgrad"}}[args.passes]
-        W["ops"] = [o for o in W["ops"] if o[0] in keep]
+        for X in Ws:
+            X["ops"] = [o for o in X["ops"] if o[0] in keep]
+    W = Ws[0]
     flops = W["flops"]
-    t_step, per, roof = measure(W, args, dev)
+    t_step, per, roof = measure(W, args, dev, Ws)
     if args.workload == "fc1" and args.passes == "all" and not args.separate_quant:
         for name in per:
             if "TFLOPS" in per[name]:
@@ -724,6 +737,7 @@ def main():
 
     config = dict(W["config"])
     config["passes"] = args.passes
+    config["buffer_sets"] = args.rotate
     out = {
         "metric": W["metric"],
         "value": round(value, 2),
@@ -745,20 +759,22 @@ def main():
     if args.workload == "fc1" and args.passes == "all" and not args.separate_quant and not args.no_extra:
         # the a8w4 forward and the blockwise FP8 forward + weight gradient at
         # their own workload sizes, against the FP8 MFMA peak
-        del W
+        del W, Ws
         torch.cuda.empty_cache()
         extra = {}
         for name in EXTRA_WORKLOADS:
-            X = build_workload(name, dev, codes=args.codes)
-            t_x, per_x, roof_x = measure(X, args, dev)
+            Xs = [build_workload(name, dev, codes=args.codes) for _ in range(args.rotate)]
+            X = Xs[0]
+            t_x, per_x, roof_x = measure(X, args, dev, Xs)
             tr_x = read_traffic(roof_x["kernel"], name)
             roof_x["traffic"] = None if tr_x is None else round(tr_x[0] + tr_x[1])
             fl = sum(X["flops"][n] for n, k, _ in X["ops"] if k == "gemm")
             extra[name] = {"metric": X["metric"], "value": round(fl / t_x / 1e12, 2), "unit": "TFLOPS",
-                           "ms_per_step": round(t_x * 1e3, 4), "dtype": X["dtype"], "config": X["config"],
+                           "ms_per_step": round(t_x * 1e3, 4), "dtype": X["dtype"],
+                           "config": dict(X["config"], buffer_sets=args.rotate),
                            "pct_mfma_peak_step": round(100 * fl / t_x / 1e12 / X["peak_tflops"], 2),
                            "roofline": roof_x, "kernels": per_x}
-            del X
+            del X, Xs
             torch.cuda.empty_cache()
         out["workloads"] = extra
     if not args.no_cpu_baseline and args.workload == "fc1":
