@@ -53,6 +53,24 @@ def test_rowwise_quantizer_writes_k_blocks(fmt, rows, lay):
 
 @pytest.mark.parametrize("lay", [0, MFMA], ids=["block-major", "mfma"])
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_rowwise_k_blocks_past_the_grid_row_limit(fmt, lay):
+    # more than 65535 groups of 16 rows: workgroups loop over row groups, so
+    # the LDS staging of the K blocks runs several times per workgroup
+    rows, cols = 65535 * 16 + 1003, 256
+    f = mxg.FORMATS[fmt] | lay
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    x = torch.randn((rows, cols), device="cuda", generator=gen).to(torch.bfloat16)
+    q0, s0 = mxg.quantize_rowwise(x, f)
+    q1, s1 = mxg.quantize_rowwise(x, f | KR)
+    torch.cuda.synchronize()
+    nb = q0.shape[1] // 64
+    assert q1.shape == (nb, rows, 64)
+    assert torch.equal(q1, q0.reshape(rows, nb, 64).permute(1, 0, 2))
+    assert torch.equal(s0, s1)
+
+
+@pytest.mark.parametrize("lay", [0, MFMA], ids=["block-major", "mfma"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
 @pytest.mark.parametrize("bits", [KC, KR, KR | KC], ids=["cols", "rows", "both"])
 def test_colwise_and_dual_quantizers_write_k_blocks(fmt, bits, lay):
     sp = [128, 0, 256, 384]  # column blocks (and MFMA column scales) need splits % 128
