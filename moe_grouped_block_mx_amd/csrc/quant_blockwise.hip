@@ -143,14 +143,21 @@ __global__ __launch_bounds__(256) void transpose_128x128_kernel(const uint8_t* _
 // 1x128 row-wise. As the MX row-wise kernel: a wave owns 64 consecutive
 // 16-byte chunks of one row (four 128-element blocks, 16 lanes each, amax
 // reduced with four xor-shuffles); each thread keeps U rows' loads in flight.
+// The workgroup's 4*U rows x 512 code bytes (eight 64-byte K blocks) are
+// staged in LDS as [K block][row][64 bytes], so that after a barrier every
+// store instruction writes 1 KiB of contiguous K-blocked codes.
 // ---------------------------------------------------------------------------
 template <bool POW2, int U>
 __global__ __launch_bounds__(256) void quant_rowwise_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                   int rows, int cpr, uint8_t* __restrict__ q,
                                                                   float* __restrict__ s) {
+  static_assert(U == 4, "16 rows per workgroup and iteration: 64 threads per staged K block");
+  __shared__ uint4 stage[8 * 16 * 4];  // [K block][row][4 x 16 bytes]
+  uint2* const st = reinterpret_cast<uint2*>(stage);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;  // 8-element chunk inside the row
   const bool cvalid = c < cpr;
+  const int64_t nkb = cpr / 8;           // K blocks per row (cpr % 16 == 0)
   for (int rb = blockIdx.y * (4 * U); rb < rows; rb += gridDim.y * (4 * U)) {
     uint4 v[U];
 #pragma unroll
@@ -166,11 +173,20 @@ __global__ __launch_bounds__(256) void quant_rowwise_1x128_kernel(const uint16_t
       uint32_t amax = amax8(wd);
 #pragma unroll
       for (int m = 1; m < 16; m <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, m, 64));
-      if (!(cvalid && r < rows)) continue;
       const BlkScale bs = blk_scale<POW2>(amax);
-      *reinterpret_cast<uint2*>(q + kblk_off(r, (int64_t)c * 8, rows)) = encode8<POW2>(wd, bs);
-      if ((c & 15) == 0) s[(int64_t)(c >> 4) * rows + r] = bs.stored;
+      // code bytes 8*lane .. of the tile's row u*4 + w: K block lane/8
+      st[((lane >> 3) * 16 + u * 4 + w) * 8 + (lane & 7)] = encode8<POW2>(wd, bs);
+      if (cvalid && r < rows && (c & 15) == 0) s[(int64_t)(c >> 4) * rows + r] = bs.stored;
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int p = threadIdx.x + 256 * j;
+      const int r = rb + ((p >> 2) & 15);
+      const int64_t kbg = (int64_t)blockIdx.x * 8 + (p >> 6);
+      if (kbg < nkb && r < rows) *reinterpret_cast<uint4*>(q + (kbg * rows + r) * 64 + (p & 3) * 16) = stage[p];
+    }
+    __syncthreads();
   }
 }
 
@@ -178,7 +194,9 @@ __global__ __launch_bounds__(256) void quant_rowwise_1x128_kernel(const uint16_t
 // 128x128 blocks. One workgroup per block: thread t reads rows t/16 + 16 i
 // (i < 8), chunk t%16 (8 elements), i.e. every load instruction covers 16
 // full 256-byte row segments; amax is reduced in the wave, then across the
-// four waves through LDS.
+// four waves through LDS. (Staging the block's codes in LDS so that every
+// store writes 1 KiB of a K block measured equal: the 256-byte row loads set
+// the pace.)
 // ---------------------------------------------------------------------------
 template <bool POW2>
 __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t rows,

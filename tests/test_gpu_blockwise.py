@@ -54,6 +54,24 @@ def test_quantize_1x128_rowwise(pow2, shape):
     assert np.array_equal(host(s).T.copy().view(np.uint32), rs.astype(np.float32).view(np.uint32))
 
 
+@pytest.mark.parametrize("pow2", [True, False])
+def test_quantize_1x128_rowwise_past_the_grid_row_limit(pow2):
+    # more than 65535 groups of 16 rows: workgroups loop over row groups (the
+    # LDS staging of the K-blocked codes runs several times per workgroup);
+    # rows from the first and the last groups against the oracle
+    rows, cols = 65535 * 16 + 1003, 256
+    gen = torch.Generator(device="cuda").manual_seed(19)
+    x = torch.randn((rows, cols), device="cuda", generator=gen).to(torch.bfloat16)
+    q, s = mxg.quantize_rowwise(x, "fp8_1x128", flags=POW2 if pow2 else 0)
+    torch.cuda.synchronize()
+    assert q.shape == (cols // 64, rows, 64) and s.shape == (cols // 128, rows)
+    for sl in (slice(0, 40), slice(65535 * 16 - 8, 65535 * 16 + 40), slice(rows - 40, rows)):
+        xb = host(x[sl].contiguous().view(torch.int16)).view(np.uint16)
+        rq, rs = ob.quantize_1x128(xb, pow2=pow2)
+        assert np.array_equal(kblocked_rows(q[:, sl, :].contiguous()), rq.astype(np.uint8)), sl
+        assert np.array_equal(host(s[:, sl]).T.copy().view(np.uint32), rs.astype(np.float32).view(np.uint32)), sl
+
+
 def test_quantize_1x128_strided_input():
     full = bf16_normal((50, 512), 1.0, seed=12)
     xt = dev_bf16(full)[:, 128:384]
