@@ -83,7 +83,7 @@ def test_quantize_1x128_strided_input():
 
 
 @pytest.mark.parametrize("pow2", [True, False])
-@pytest.mark.parametrize("shape", [(128, 128), (384, 256), (256, 640)])
+@pytest.mark.parametrize("shape", [(128, 128), (384, 256), (256, 640), (256, 512), (384, 1536)])
 def test_quantize_128x128(pow2, shape):
     w = bf16_normal(shape, 0.02, seed=13)
     w[128:134] = _special_rows(shape[1], 6) if shape[0] > 128 else w[128:134]
@@ -94,9 +94,10 @@ def test_quantize_128x128(pow2, shape):
     assert np.array_equal(host(s).view(np.uint32), rs.astype(np.float32).view(np.uint32))
 
 
-def test_quantize_128x128_all_zero_block():
-    w = np.zeros((256, 256), dtype=np.uint16)
-    w[128:, 128:] = bf16_normal((128, 128), 1.0, seed=3)
+@pytest.mark.parametrize("cols", [256, 512])
+def test_quantize_128x128_all_zero_block(cols):
+    w = np.zeros((256, cols), dtype=np.uint16)
+    w[128:, 128:256] = bf16_normal((128, 128), 1.0, seed=3)
     q, s = mxg.quantize_rowwise(dev_bf16(w), "fp8_128x128")
     torch.cuda.synchronize()
     rq, rs = ob.quantize_128x128(w)
