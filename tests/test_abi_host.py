@@ -319,3 +319,52 @@ def test_relayout_validation():
     assert L.mxgg_mx_scales_relayout(P, R, 10, 65535 * 64 + 1, P, B, NULL) == 2
     assert L.mxgg_mx_scales_relayout(NULL, R, 10, 4, P, B, NULL) == 1
     assert L.mxgg_mx_scales_relayout(NULL, R, 0, 4, NULL, B, NULL) == 0     # nothing to do
+
+
+KR, KC = 0x1000, 0x2000           # MXGG_KBLOCK_ROWS, MXGG_KBLOCK_COLS
+VALIDATION = (1, 2, 3, 4, 5, 6)   # NULL, SHAPE, SPLITS, FORMAT, ALIGN, WORKSPACE
+
+
+def test_k_block_bits_validation():
+    # the header's rules for the 64-byte K-block code layouts, checked before
+    # any device call (a call that passes them fails later here: no GPU)
+    def rowwise(fmt, cols=128):
+        return L.mxgg_quantize_rowwise(P, 64, cols, cols, fmt, 0, P, P, NULL)
+    assert rowwise(KR, cols=96) == 2 and "K-blocked" in last()     # cols % 128
+    assert rowwise(KC) == 4 and "K-block" in last()                 # row-wise codes take the rows bit only
+    assert rowwise(2 | KR) == 4                                     # blockwise codes: always K-blocked, no bits
+    assert rowwise(KR) not in VALIDATION and rowwise(1 | KR | 0x200) not in VALIDATION
+
+    def colwise(fmt, m, mpad):
+        return L.mxgg_quantize_colwise_segpad(P, sum(m), 64, 64, splits(*m), len(m), fmt, 0, P, P, mpad, NULL)
+    assert colwise(KC, [100, 156], 288) == 3                        # column blocks need splits % 128
+    assert colwise(KR, [128, 128], 256) == 4                        # column-wise codes take the cols bit only
+    assert colwise(KC, [128, 0, 256], 384) not in VALIDATION
+
+    def dual(fmt, m=(128, 128), mpad=256, cols=128):
+        return L.mxgg_quantize_dual(P, sum(m), cols, cols, splits(*m), len(m), fmt, 0, P, P, P, P, mpad, NULL)
+    assert dual(KR | KC) not in VALIDATION and dual(KR, m=(100, 156), mpad=288) not in VALIDATION
+    assert dual(KC, m=(100, 156), mpad=288) == 3                    # only the column output needs splits % 128
+    assert dual(KR, cols=96) == 2                                   # only the row output needs cols % 128
+
+    m = splits(64, 0, 64)
+    assert fwd(m, 3, 128, K=128, a_fmt=KR, w_fmt=0) == 4 and "together" in last()
+    assert fwd(m, 3, 128, K=96, a_fmt=KR, w_fmt=KR) == 2 and "K-blocked" in last()
+    assert fwd(m, 3, 128, K=128, a_fmt=KC, w_fmt=KC) == 4
+    assert fwd(m, 3, 128, K=128, a_fmt=KR, w_fmt=KR) not in VALIDATION
+    assert fwd(m, 3, 128, K=128, a_fmt=1 | KR, w_fmt=0x200 | KR) not in VALIDATION   # a8w4, MFMA weight scales
+    big = 1 << 25                                                   # a lane's 32-bit DMA offset: rows < 2^25
+    assert fwd(splits(big), 1, big, K=128, a_fmt=KR, w_fmt=KR) == 2 and "2^25" in last()
+    assert fwd(splits(big - 4), 1, big - 4, K=128, a_fmt=KR, w_fmt=KR) not in VALIDATION
+
+    def dgrad(fmt, M=128, N=128, K=64, m=m, G=3):
+        return L.mxgg_grouped_dgrad(P, P, P, P, fmt, m, G, M, N, K, P, NULL, 0, NULL)
+    assert dgrad(KR) == 4 and dgrad(KC) == 4                        # both bits or neither
+    assert dgrad(KR | KC, N=96) == 2                                # N % 128
+    assert dgrad(KR | KC) not in VALIDATION and dgrad(1 | KR | KC | 0x200) not in VALIDATION
+    assert dgrad(KR | KC, M=big, m=splits(big), G=1) == 2 and "2^25" in last()
+    assert dgrad(KR | KC, K=big, M=128, N=128) == 2
+
+    ms = splits(32, 0)
+    assert L.mxgg_grouped_wgrad(P, P, P, P, KR, ms, 2, 64, 64, 32, P, 0, 1, NULL, 0, NULL) == 4
+    assert L.mxgg_grouped_wgrad(P, P, P, P, KC, ms, 2, 64, 64, 32, P, 0, 1, NULL, 0, NULL) == 4
