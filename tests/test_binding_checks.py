@@ -91,3 +91,31 @@ def test_quantizer_outputs():
         mxg.transpose_128x128(z((256 // 64, G * 128, 64), u8), z((G, 2), f32), G, 128, 256, wt_s=z((G, 2), f32))
     with pytest.raises(ValueError, match="w_q"):    # rows of codes are refused
         mxg.transpose_128x128(z((G * 128, 256), u8), z((G, 2), f32), G, 128, 256)
+
+
+def test_k_blocked_mx_code_shapes():
+    # MXGG_KBLOCK_ROWS / _COLS: codes u8 [bytes per row / 64, rows, 64]; a buffer
+    # of the other layout's shape is refused, never read as this one
+    KR, KC = mxg.KBLOCK_ROWS, mxg.KBLOCK_COLS
+    a = fwd_args()
+    blocked_a, blocked_w = z((K // 128, M, 64), u8), z((K // 128, G * N, 64), u8)
+    with pytest.raises(ValueError, match="a_q"):        # rows of codes under the K-block bit
+        mxg.grouped_fwd(a["a_q"], a["a_s"], blocked_w, a["w_s"], SPLITS, N, K, a_fmt=mxg.MXFP4 | KR,
+                        w_fmt=mxg.MXFP4 | KR)
+    with pytest.raises(ValueError, match="w_q"):        # K blocks without the bit
+        mxg.grouped_fwd(a["a_q"], a["a_s"], blocked_w, a["w_s"], SPLITS, N, K)
+    x = z((M, K), bf16)
+    with pytest.raises(ValueError, match="q"):
+        mxg.quantize_rowwise(x, mxg.MXFP4 | KR, q=z((M, K // 2), u8))
+    with pytest.raises(ValueError, match="q"):
+        mxg.quantize_rowwise(x, mxg.MXFP8 | KR, q=z((K // 128, M, 64), u8))   # E4M3: K/64 blocks
+    n2 = 128                                           # the input gradient's K blocks need N % 128
+    dq, ds = z((n2 // 128, M, 64), u8), z((n2 // 32, mxg.mx_scale_stride(M)), u8)
+    wq, ws = z((K, G * n2 // 2), u8), z((G * n2 // 32, K), u8)
+    with pytest.raises(ValueError, match="wcol_q"):    # W along N in rows under MXGG_KBLOCK_COLS
+        mxg.grouped_dgrad(dq, ds, wq, ws, SPLITS, n2, K, fmt=mxg.MXFP4 | KR | KC)
+    with pytest.raises(ValueError, match="dy_q"):      # dY in K blocks without the bits
+        mxg.grouped_dgrad(dq, ds, wq, ws, SPLITS, n2, K)
+    with pytest.raises(ValueError, match="a_q"):       # the right size in the wrong layout
+        mxg.grouped_fwd(blocked_a.reshape(M, K // 2), a["a_s"], blocked_w, a["w_s"], SPLITS, N, K,
+                        a_fmt=mxg.MXFP4 | KR, w_fmt=mxg.MXFP4 | KR)
