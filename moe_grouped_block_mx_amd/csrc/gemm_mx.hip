@@ -1426,11 +1426,15 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&o)[8]) {
 // so an expert's weight tiles are re-read from beyond the XCD's L2 once per
 // kTileGroup row tiles rather than once per 32/Cn. Measured at the fc1
 // shapes: input gradient 342 -> 308 us (Cn = 16), forward and weight
-// gradient unchanged; groups of 2 and 8 were slower.
-constexpr int kTileGroup = 4;
+// gradient unchanged; groups of 2 and 8 were slower. The MX weight gradients
+// (fp32 main_grad read-modify-write) take groups of 5: fc1 670 -> 656 us,
+// MXFP8 at the a8w4 shapes 3.20 -> 3.18 ms (groups of 3 and 6 in between, 12
+// slower than 4); the blockwise one stays at 4.
+constexpr int kTileGroup = 4, kTileGroupMxWgrad = 5;
+template <int GROUP = kTileGroup>
 __device__ __forceinline__ void grouped_tile(int local, int R, int Cn, int& rt, int& ct) {
-  const int r0 = local / (kTileGroup * Cn) * kTileGroup;
-  const int h = R - r0 < kTileGroup ? R - r0 : kTileGroup;
+  const int r0 = local / (GROUP * Cn) * GROUP;
+  const int h = R - r0 < GROUP ? R - r0 : GROUP;
   const int in = local - r0 * Cn;
   ct = in / h;
   rt = r0 + (in - ct * h);
@@ -1593,7 +1597,7 @@ struct WgradSource {
     const int g = order[j];
     const int local = t - tile_offs[j];
     int rt, ct;
-    grouped_tile(local, (p.n_rows + C::BM - 1) / C::BM, tc, rt, ct);
+    grouped_tile<C::F32S ? kTileGroup : kTileGroupMxWgrad>(local, (p.n_rows + C::BM - 1) / C::BM, tc, rt, ct);
     const int64_t p0 = pad_pref[g];
     const Pos q{g, rt * C::BM, ct * C::BN, p0, (int)(pad_pref[g + 1] - p0)};
     if (side) cur = q;
