@@ -170,6 +170,36 @@ def test_full_size_a8w4_forward_and_input_gradient_are_bit_identical():
     assert torch.equal(out[0][1], out[KR | KC][1])
 
 
+def test_k_blocks_with_512_experts_most_empty_and_an_empty_batch():
+    # the largest expert count, 30 % of the experts empty and ragged tiny
+    # segments: forward and input gradient on K-blocked codes equal the plain
+    # layout bit for bit; then an empty batch, which launches nothing
+    rng = np.random.default_rng(21)
+    G, N, K = 512, 128, 256
+    sp = rng.integers(0, 9, size=G)
+    sp[rng.random(G) < 0.3] = 0
+    sp = [int(v) for v in sp]
+    M = sum(sp)
+    x = dev_bf16(bf16_normal((M, K), 1.0, seed=22))
+    w = dev_bf16(bf16_normal((G * N, K), 0.05, seed=23))
+    dy = dev_bf16(bf16_normal((M, N), 1.0, seed=24))
+    out = {}
+    for kb in (0, KR | KC):
+        aq, as_ = mxg.quantize_rowwise(x, mxg.MXFP4 | (kb & KR))
+        dq, ds = mxg.quantize_rowwise(dy, mxg.MXFP4 | (kb & KR))
+        wq, ws, wc, wcs, _ = mxg.quantize_dual(w, [N] * G, mxg.MXFP4 | kb)
+        out[kb] = (mxg.grouped_fwd(aq, as_, wq, ws, sp, N, K, a_fmt=mxg.MXFP4 | (kb & KR),
+                                   w_fmt=mxg.MXFP4 | (kb & KR)),
+                   mxg.grouped_dgrad(dq, ds, wc, wcs, sp, N, K, fmt=mxg.MXFP4 | kb))
+    torch.cuda.synchronize()
+    assert torch.equal(out[0][0], out[KR | KC][0]) and torch.equal(out[0][1], out[KR | KC][1])
+    e = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    eq, es = mxg.quantize_rowwise(e, mxg.MXFP4 | KR)
+    y = mxg.grouped_fwd(eq, es, wq, ws, [0] * G, N, K, a_fmt=mxg.MXFP4 | KR, w_fmt=mxg.MXFP4 | KR)
+    torch.cuda.synchronize()
+    assert eq.shape == (K // 128, 0, 64) and y.shape == (0, N)
+
+
 def test_k_block_bits_refused_where_the_header_says():
     sp = [128, 128]
     M, N, K = 256, 128, 128
